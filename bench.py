@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer hot path on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3|mid|tiny]
+
+A step is one moe_forward of the whole layer (routing, schedule, shared expert, dispatch, routed
+grouped GEMMs with the SwiGLU and scatter epilogues, combine) on one batch of seeded synthetic
+inputs already resident in HBM. W untimed steps, then K steps timed with HIP events on the
+library's stream between two device synchronisations. Prints ONE JSON line.
+
+The default workload is the DeepSeek-V3-shape BF16 forward: T=8192 tokens, D=7168, I=2048,
+256 routed experts top-8 plus one shared expert (I=2048), router logits with a per-expert bias.
+
+`roofline` covers the kernel with the largest device time per step, with its algorithmic bytes
+and FLOPs per launch; `cpu_baseline` times the fp64 CPU oracle on a bounded sample of tokens of
+the same workload (rank 0, one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, TFLOP/s
+PEAK_F32_TFLOPS = 157.3         # fp32 vector
+PEAK_HBM_GBS = 8000.0           # HBM3E, GB/s
+METRIC = 'MoE layer tokens/s (fwd, fwd+bwd) on 1 MI355X; % of MFMA peak'
+
+
+def stage_work(cfg, flags):
+    """Algorithmic FLOPs and HBM bytes per launch of each forward stage."""
+    T, D, I, E, K, Is = cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared
+    n = T * K
+    b = 4 if cfg.dtype == 'f32' else 2
+    fused = bool(flags & 1)
+    w = {}
+    w['route'] = (0.0, T * cfg.E * 4 + T * K * 8)
+    w['schedule'] = (0.0, n * 4 * 3)
+    w['shared'] = (6.0 * T * D * Is, 3 * Is * D * b + 2 * T * D * b + 2 * T * Is * b) if Is else (0.0, 0)
+    w['dispatch'] = (0.0, 0 if fused else T * D * b + n * D * b + n * 4)
+    w['up_gate'] = (4.0 * n * D * I, 2 * E * I * D * b + (T if fused else n) * D * b + n * I * b)
+    w['down'] = (2.0 * n * I * D, E * D * I * b + n * I * b + n * D * b + n * 4)
+    w['combine'] = (0.0, n * D * b + (2 if Is else 1) * T * D * b + n * 4)
+    return w
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument('--gpus', type=int, default=1)
+    ap.add_argument('--steps', type=int, default=50)
+    ap.add_argument('--warmup', type=int, default=10)
+    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny'])
+    ap.add_argument('--chunk-rows', type=int, default=0)
+    ap.add_argument('--flags', type=int, default=0)
+    ap.add_argument('--no-cpu-baseline', action='store_true')
+    ap.add_argument('--cpu-tokens', type=int, default=8, help='tokens in the CPU oracle sample')
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU '
+              'path: the expert-parallel sharding is described in DESIGN.md, not implemented.', file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import mixture_experts_layer_norm_amd as moe
+
+    cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY}[args.workload]
+    torch.cuda.set_device(0)
+    print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
+    L = synth.device_layer(cfg)
+    T, D, K = cfg.T, cfg.D, cfg.K
+    dev = 'cuda'
+    p = moe.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, cfg.dtype, args.chunk_rows, 0, args.flags)
+    dt = L.x.dtype
+    routing_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                     topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
+                     counts=torch.empty((cfg.E,), dtype=torch.int32, device=dev),
+                     offsets=torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev),
+                     perm=torch.empty((T * K,), dtype=torch.int32, device=dev),
+                     inv_perm=torch.empty((T * K,), dtype=torch.int32, device=dev))
+    routing = moe.make_routing(**routing_t)
+    weights = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
+    out = torch.empty((T, D), dtype=dt, device=dev)
+    ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    nst = len(moe.STAGES)
+
+    def step(events=None):
+        if events is None:
+            moe.forward(p, L.x, L.logits, weights, out, routing, ws, stream=stream)
+        else:
+            moe.forward_stages(p, L.x, L.logits, weights, out, routing, ws, events, stream=stream)
+
+    print(f'[bench] warmup {args.warmup}', file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, s in enumerate(moe.STAGES)}
+    print(f'[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); '
+          f'stages {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}', file=sys.stderr, flush=True)
+
+    n = T * K
+    flops = 6.0 * n * cfg.D * cfg.I + 6.0 * T * cfg.D * cfg.I_shared
+    peak = PEAK_F32_TFLOPS if cfg.dtype == 'f32' else PEAK_BF16_TFLOPS
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    work = stage_work(cfg, args.flags)
+    dom = max(stage_ms, key=stage_ms.get)
+    f_dom, b_dom = work[dom]
+    t_dom = stage_ms[dom] * 1e-3
+    t_mfma = f_dom / (peak * 1e12)
+    t_hbm = b_dom / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {'bound': 'mfma', 'achieved': f_dom / t_dom / 1e12, 'peak': peak, 'unit': 'TFLOP/s'}
+    else:
+        roof = {'bound': 'hbm', 'achieved': b_dom / t_dom / 1e9, 'peak': PEAK_HBM_GBS, 'unit': 'GB/s'}
+    roof['frac'] = roof['achieved'] / roof['peak']
+    roof['traffic'] = None
+    roof['kernel'] = {'up_gate': 'gemm_bf16_kernel<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
+                      'down': 'gemm_bf16_kernel<EPI_STORE> (routed W_down + scatter)',
+                      'shared': 'shared expert GEMMs', 'dispatch': 'dispatch_kernel',
+                      'combine': 'combine_bf16_kernel', 'route': 'route_topk_kernel',
+                      'schedule': 'sched_* kernels'}[dom]
+    roof['stage'] = dom
+    roof['avg_ms'] = stage_ms[dom]
+    roof['algorithmic_flops'] = f_dom
+    roof['algorithmic_bytes'] = b_dom
+    roof['mfma_frac'] = f_dom / t_dom / 1e12 / peak
+    roof['hbm_frac'] = b_dom / t_dom / 1e9 / PEAK_HBM_GBS
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, L, args.cpu_tokens)
+
+    line = {
+        'metric': METRIC,
+        'value': T / (ms_per_step * 1e-3),
+        'unit': 'tokens/s',
+        'n_gpus': 1,
+        'steps': args.steps,
+        'warmup': args.warmup,
+        'ms_per_step': ms_per_step,
+        'higher_is_better': True,
+        'scaling': 'weak',
+        'vs_baseline': None,
+        'dtype': 'bf16' if cfg.dtype != 'f32' else 'f32',
+        'data': 'synthetic',
+        'config': {'workload': f'{cfg.name} forward', 'T': T, 'D': cfg.D, 'I': cfg.I, 'E': cfg.E, 'K': K,
+                   'I_shared': cfg.I_shared, 'router': cfg.router, 'chunk_rows': args.chunk_rows,
+                   'flags': args.flags},
+        'tflops': tflops,
+        'mfma_peak_frac': tflops / peak,
+        'stages_ms': stage_ms,
+        'wall_ms_per_step': 1e3 * wall / args.steps,
+        'roofline': roof,
+        'cpu_baseline': cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, L, ntok):
+    """The fp64 oracle on `ntok` sampled tokens of the same layer, on the host cores. The weights
+    of the experts these tokens use are copied to the host before the timed region."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get('num_threads', 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rng = np.random.default_rng(1234)
+    toks = np.sort(rng.choice(cfg.T, ntok, replace=False))
+    lg = L.logits[torch.from_numpy(toks).cuda()].cpu().numpy()
+    xs = L.x[torch.from_numpy(toks).cuda()].float().cpu().numpy()
+    used = sorted(set(oracle.route_topk(lg, cfg.K).ravel().tolist()))
+    print(f'[bench] cpu baseline: {ntok} tokens, {len(used)} experts to host', file=sys.stderr, flush=True)
+    wg = {e: L.w_gate[e].float().cpu().numpy() for e in used}
+    wu = {e: L.w_up[e].float().cpu().numpy() for e in used}
+    wd = {e: L.w_down[e].float().cpu().numpy() for e in used}
+    sh = [t.float().cpu().numpy() if t is not None else None for t in (L.ws_gate, L.ws_up, L.ws_down)]
+    t0 = time.perf_counter()
+    oracle.moe_forward(xs, lg, lambda e: wg[e], lambda e: wu[e], lambda e: wd[e], cfg.K, *sh)
+    dt = time.perf_counter() - t0
+    print(f'[bench] cpu baseline: {dt:.2f} s', file=sys.stderr, flush=True)
+    return {'value': ntok / dt, 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
+            'sample': f'{ntok} random tokens of the same layer (all their routed experts + shared), fp64 numpy, '
+                      f'{len(used)} experts streamed; weights copied to host before timing',
+            'seconds': dt}
+
+
+if __name__ == '__main__':
+    main()

@@ -1,0 +1,229 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) MoE layer library (libmoe.so).
+ *
+ * One DeepSeek-V3-style mixture-of-experts layer on one GPU, as defined by the Cursor blog post
+ * "Mixture-of-Kittens: our open-source MoE megakernel for NVL72s", section "Overlapping
+ * computation and communication in MoE" (notation and MoE layer equation):
+ *
+ *     MoE(x, s) = E_shared(x) + sum_{i in E} g_i E_i(x),      g_i = s_i / sum_{j in E} s_j,
+ *     E_i(x)    = W_down^(i) ( SiLU(W_gate^(i) x) (*) W_up^(i) x ),
+ *
+ * with s = softmax(router logits) over all routed experts and E the top-K routed experts.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Ownership: the caller owns every pointer. Tensor and workspace pointers are device
+ *   pointers (hipMalloc'd memory of the current device); structs are host memory read during
+ *   the call only. The library allocates nothing and keeps no state between calls.
+ * - Asynchrony: a call validates its arguments on the host, then only enqueues kernels on
+ *   `stream`. It never synchronises, never copies device data to the host and never blocks.
+ * - Errors: MOE_OK (0) or a negative moe_status. Argument errors are detected on the host
+ *   before anything is enqueued (no device work happens then). A kernel launch failure returns
+ *   MOE_ERR_HIP. Data errors only the device can see (an expert id out of range in a
+ *   caller-supplied topk_idx) are clamped so that no access goes out of bounds, and set the
+ *   sticky error word at byte offset 0 of the workspace (int32, nonzero = error) without
+ *   faulting; the caller may read it asynchronously after the call.
+ * - Layouts are row-major. Element types: MOE_F32 = float, MOE_BF16 = bfloat16 (uint16 bits),
+ *   MOE_MXFP8 = OCP E4M3 bytes with one E8M0 scale byte per 32 elements along the contraction
+ *   dimension (OCP Microscaling Formats v1.0).
+ * - Determinism: for identical inputs and problem descriptors, every output is bitwise
+ *   identical from run to run, and independent of chunk_rows and of how many workgroups run:
+ *   no floating-point atomics are used and every sum has a fixed order.
+ * - Re-entrancy: calls are re-entrant; concurrent calls need separate workspaces.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, K outside [1, E], ... */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid but not implemented (a size the kernels do not tile) */
+  MOE_ERR_WORKSPACE = -3,     /* workspace null or smaller than moe_workspace_size() */
+  MOE_ERR_MISALIGNED = -4,    /* a tensor pointer not 16-byte aligned */
+  MOE_ERR_HIP = -5            /* a HIP launch error (hipGetLastError after enqueue) */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,     /* fp32 storage and arithmetic */
+  MOE_BF16 = 1,    /* bf16 storage, fp32 accumulation */
+  MOE_MXFP8 = 2    /* routed experts in MXFP8 (E4M3 + E8M0 per 32), shared expert and x in bf16 */
+} moe_dtype;
+
+/* Problem descriptor. T tokens of dimension D; E routed experts of intermediate size I, K per
+ * token; one shared expert of intermediate size I_shared (0 = none).
+ * Size limits: 1 <= K <= min(E, 64); E <= 1024; T*K < 2^31. BF16/MXFP8 need D % 128 == 0 and
+ * I % 128 == 0 (I_shared likewise); MOE_F32 needs D % 4 == 0.
+ * chunk_rows (b): rows of the expert-contiguous routed buffer that one pipeline step carries
+ *   through the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel for
+ *   NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
+ *   values are clamped to [256, T*K] and rounded up to a multiple of 256.
+ * ring_stages: macrobatch ring depth (Notes, section "A ring buffer instead of a host
+ *   round-trip"); 0 selects 3. Ignored when one chunk holds every row.
+ * flags: bitwise OR of MOE_FLAG_* below. */
+typedef struct moe_problem {
+  int32_t T, D, I, E, K, I_shared;
+  int32_t dtype;
+  int32_t chunk_rows;
+  int32_t ring_stages;
+  int32_t flags;
+} moe_problem;
+
+/* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
+#define MOE_FLAG_FUSED_GATHER 0x1
+
+/* Expert weights (device pointers). Routed: w_gate, w_up [E][I][D]; w_down [E][D][I].
+ * Shared: ws_gate, ws_up [I_shared][D]; ws_down [D][I_shared] (always bf16 under MOE_MXFP8).
+ * MXFP8 only: routed weights are E4M3 bytes with scales sc_gate, sc_up [E][I][D/32] and
+ * sc_down [E][D][I/32] (E8M0 bytes), as produced by moe_quantize_mx. */
+typedef struct moe_weights {
+  const void *w_gate, *w_up, *w_down;
+  const void *ws_gate, *ws_up, *ws_down;
+  const uint8_t *sc_gate, *sc_up, *sc_down;
+} moe_weights;
+
+/* Routing state written by the forward and read by the backward (device pointers).
+ * topk_idx [T][K] int32 and topk_w [T][K] float: the K chosen experts per token in descending
+ * logit order (ties to the lower index) and their weights g. counts [E], offsets [E+1]
+ * (exclusive scan of counts), perm [T*K] (slot -> route id t*K+k) and inv_perm [T*K]
+ * (route id -> slot). Slots of expert e are offsets[e] .. offsets[e+1]-1, in route order. */
+typedef struct moe_routing {
+  int32_t *topk_idx;
+  float *topk_w;
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *perm;
+  int32_t *inv_perm;
+} moe_routing;
+
+/* Weight gradients, fp32, same shapes as the weights (shared ones may be NULL when
+ * I_shared == 0). Overwritten, not accumulated; an expert with no rows gets exact zeros. */
+typedef struct moe_grads {
+  float *dw_gate, *dw_up, *dw_down;
+  float *dws_gate, *dws_up, *dws_down;
+} moe_grads;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(int status);
+
+/* Bytes of device workspace that moe_schedule / moe_forward / moe_backward need for `p`
+ * (the largest of the three). Writes *bytes; returns MOE_OK or MOE_ERR_INVALID_ARG.
+ * The first 256 bytes hold the sticky error word (offset 0, int32). */
+int moe_workspace_size(const moe_problem *p, size_t *bytes);
+
+/* Top-K selection and router weights (Blog, "Overlapping computation and communication in
+ * MoE": the router picks the top-k routed experts and weights them with g_i = s_i / sum s_j).
+ * logits [T][E] fp32 -> topk_idx [T][K] int32, topk_w [T][K] fp32. One wavefront per token;
+ * selection compares the fp32 logits (a total order: larger first, lower index on ties,
+ * -0.0 == +0.0, NaN below -inf), g is computed in fp32 as exp(l_k - l_max) / sum. Inputs are
+ * expected to have at least K non-NaN logits per token (otherwise g is NaN). */
+int moe_route_topk(const moe_problem *p, const float *logits, int32_t *topk_idx, float *topk_w,
+                   hipStream_t stream);
+
+/* Device-side histogram + exclusive scan + stable placement: the one-source-rank case of the
+ * pull schedule (Blog, "Scheduling"; sort key from the Notes, section "Pull dispatch, push
+ * combine"). topk_idx [T][K] -> counts [E], offsets [E+1], perm [T*K], inv_perm [T*K], with
+ * the layout documented at moe_routing. Bit-exact and independent of launch shape. No host
+ * synchronisation: counts stay on the device. Needs `ws` of moe_workspace_size bytes. */
+int moe_schedule(const moe_problem *p, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
+                 int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch (the one-GPU analogue of the pull dispatch, Notes "Pull dispatch, push combine"):
+ * x_slot[j - slot_begin] = x[perm[j] / K] for j in [slot_begin, slot_begin + slot_count).
+ * x [T][D] in the activation type (bf16, or f32 under MOE_F32). Under MOE_MXFP8 the rows are
+ * quantised on the way (Notes, "The production details": quantisation fused into dispatch):
+ * x_slot gets E4M3 bytes [slot_count][D] and x_slot_scales E8M0 bytes [slot_count][D/32];
+ * otherwise x_slot_scales must be NULL. */
+int moe_dispatch(const moe_problem *p, const void *x, const int32_t *perm, int64_t slot_begin,
+                 int64_t slot_count, void *x_slot, uint8_t *x_slot_scales, hipStream_t stream);
+
+/* Deterministic combine (Blog, weighted sum after the combine; Notes "The production details"
+ * on determinism): out[t] = shared_out[t] + sum_{k=0}^{K-1} topk_w[t][k] * y_routes[t*K + k],
+ * accumulated in fp32 in exactly that order and rounded once. y_routes [T*K][D] (route order),
+ * shared_out [T][D] or NULL, out [T][D]; activation type (bf16, or f32 under MOE_F32). */
+int moe_combine(const moe_problem *p, const void *y_routes, const void *shared_out,
+                const float *topk_w, void *out, hipStream_t stream);
+
+/* Whole forward: route (moe_route_topk) -> schedule (moe_schedule) -> dispatch into
+ * expert-contiguous ring slots -> grouped up/gate GEMM with the SwiGLU epilogue -> grouped down
+ * GEMM whose epilogue stores row j at route perm[j] -> shared expert -> combine.
+ * x [T][D], logits [T][E] fp32, out [T][D]. `routing` (all six pointers) receives the routing
+ * state for the backward. y_routes [T*K][D] and shared_out [T][D] are optional (NULL: kept in
+ * the workspace); when given they receive the per-route expert outputs and the shared expert
+ * output. */
+int moe_forward(const moe_problem *p, const void *x, const float *logits, const moe_weights *w,
+                void *out, const moe_routing *routing, void *y_routes, void *shared_out,
+                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage boundaries of the forward, for moe_forward_stages. Event i is recorded on `stream`
+ * just before stage i; event MOE_STAGE_COUNT just after the last stage. */
+enum moe_stage {
+  MOE_STAGE_ROUTE = 0,      /* moe_route_topk */
+  MOE_STAGE_SCHEDULE = 1,   /* histogram + scan + placement */
+  MOE_STAGE_SHARED = 2,     /* shared expert (up/gate + SwiGLU, down) */
+  MOE_STAGE_DISPATCH = 3,   /* rows into expert-contiguous slots (skipped under FUSED_GATHER) */
+  MOE_STAGE_UP_GATE = 4,    /* routed grouped GEMM W_gate/W_up + SwiGLU epilogue */
+  MOE_STAGE_DOWN = 5,       /* routed grouped GEMM W_down + scatter epilogue */
+  MOE_STAGE_COMBINE = 6,    /* fixed-order weighted sum */
+  MOE_STAGE_COUNT = 7
+};
+
+/* moe_forward with timing hooks: identical work and outputs; if `stage_events` is not NULL it
+ * holds MOE_STAGE_COUNT + 1 events created by the caller (hipEventCreate), recorded on `stream`
+ * at the stage boundaries above so that hipEventElapsedTime gives per-stage device time. */
+int moe_forward_stages(const moe_problem *p, const void *x, const float *logits,
+                       const moe_weights *w, void *out, const moe_routing *routing,
+                       void *y_routes, void *shared_out, void *ws, size_t ws_bytes,
+                       hipEvent_t *stage_events, hipStream_t stream);
+
+/* Whole backward of the layer (Notes, "Pull dispatch, push combine": reverse-combine and
+ * reverse-dispatch; "A ring buffer instead of a host round-trip": the forward activations are
+ * recomputed, not stored; "The production details": the router gradient as <h, W_down^T dY>).
+ * Inputs: dout [T][D], x [T][D], logits [T][E], weights, and the routing state of the forward.
+ * Outputs: dx [T][D] (activation type), weight gradients (fp32), d_topk_w [T][K] fp32
+ * (gradient w.r.t. g) and d_logits [T][E] fp32 (nullable). Under MOE_BF16 and MOE_F32. */
+int moe_backward(const moe_problem *p, const void *dout, const void *x, const float *logits,
+                 const moe_weights *w, const moe_routing *routing, void *dx, const moe_grads *dw,
+                 float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert-level forward of one expert-parallel rank's share (Blog, "Overlapping computation and
+ * communication in MoE": EP sharding gives each rank a few routed experts plus the shared
+ * expert). Slots arrive already grouped by local expert, as a pull dispatch lands them.
+ * p->E = local experts, p->T = local tokens (rows of the shared expert); K is ignored.
+ * x_slot [slots][D], offsets [E+1] device int32 (expert e owns rows offsets[e]..offsets[e+1]-1,
+ * offsets[E] == slots) -> y_slot [slots][D] = E_e(x_slot) (unweighted; the source applies g).
+ * x_local [T][D] -> shared_out [T][D] (skipped when I_shared == 0). BF16 only. */
+int moe_experts_forward(const moe_problem *p, int64_t slots, const void *x_slot,
+                        const int32_t *offsets, const moe_weights *w, void *y_slot,
+                        const void *x_local, void *shared_out, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Backward of moe_experts_forward where slot j contributes g_slot[j] * E_e(x_slot[j]) against
+ * the upstream gradient dy_slot[j]. Outputs dx_slot [slots][D] (bf16), dg_slot [slots] fp32
+ * (= <dy_slot[j], E_e(x_slot[j])>), routed and shared weight gradients (fp32) and dx_local
+ * [T][D] (bf16, shared expert path with upstream dy_local [T][D]). BF16 only. */
+int moe_experts_backward(const moe_problem *p, int64_t slots, const void *x_slot,
+                         const int32_t *offsets, const float *g_slot, const void *dy_slot,
+                         const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,
+                         const void *x_local, const void *dy_local, void *dx_local,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* MX quantiser (OCP Microscaling v1.0; the Notes' MXFP8, "The production details"): src
+ * [rows][cols] bf16 -> q [rows][cols] E4M3 bytes and scales [rows][cols/32] E8M0 bytes, blocks
+ * of 32 along each row. Scale 2^(floor(log2 amax) - 8) clamped to [2^-127, 2^127]; elements
+ * rounded to nearest-even and saturated to +-448; an all-zero block gets scale byte 127.
+ * cols % 32 == 0. Used offline for the weights, and by dispatch for activations. */
+int moe_quantize_mx(const void *src_bf16, int64_t rows, int32_t cols, uint8_t *q, uint8_t *scales,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,267 @@
+// C ABI entry points: host-side validation, workspace carve-up and kernel orchestration.
+// Every entry point checks its arguments before enqueuing anything and never synchronises.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+
+size_t elt_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int validate_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->T < 1 || p->D < 1 || p->I < 1 || p->E < 1 || p->K < 1 || p->I_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (p->K > p->E) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
+  if (p->E > 1024 || p->K > 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (p->dtype == MOE_F32) {
+    if (p->D % 4) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (p->D % 128 || p->I % 128 || p->I_shared % 128) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+WsLayout ws_layout(const moe_problem& p) {
+  WsLayout L{};
+  const int64_t n = (int64_t)p.T * p.K;
+  const size_t act = elt_bytes(p.dtype);
+  const bool mx = p.dtype == MOE_MXFP8;
+  L.nblk = (n + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
+  L.chunk = n;
+  L.stages = 1;
+  L.ring_rows = n;
+  size_t o = 0;
+  L.err = o; o += 256;
+  L.ctrl = o; o += 4096;
+  L.blk_hist = o; o = align256(o + (size_t)L.nblk * p.E * 4);
+  L.tile_off = o; o = align256(o + (size_t)(p.E + 1) * 4);
+  L.x_slot = o; o = align256(o + (size_t)L.ring_rows * p.D * (mx ? 1 : act));
+  L.x_slot_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.D / 32) : 0));
+  L.h = o; o = align256(o + (size_t)L.ring_rows * p.I * (mx ? 1 : act));
+  L.h_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.I / 32) : 0));
+  L.y_routes = o; o = align256(o + (size_t)n * p.D * act);
+  L.sh_h = o; o = align256(o + (size_t)p.T * p.I_shared * act);
+  L.sh_out = o; o = align256(o + (p.I_shared > 0 ? (size_t)p.T * p.D * act : 0));
+  L.bwd = o;
+  L.total = o;
+  return L;
+}
+
+static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+int moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = ws_layout(*p).total;
+  return MOE_OK;
+}
+
+int moe_route_topk(const moe_problem* p, const float* logits, int32_t* topk_idx, float* topk_w,
+                   hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  return launch_route_topk(logits, topk_idx, topk_w, p->T, p->E, p->K, stream);
+}
+
+static int schedule_into(const moe_problem* p, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv_perm, char* ws, hipStream_t stream) {
+  WsLayout L = ws_layout(*p);
+  return launch_schedule(topk_idx, p->T, p->K, p->E, counts, offsets, perm, inv_perm,
+                         (int32_t*)(ws + L.blk_hist), (int32_t*)(ws + L.tile_off),
+                         (int32_t*)(ws + L.err), stream);
+}
+
+int moe_schedule(const moe_problem* p, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < ws_layout(*p).total) return MOE_ERR_WORKSPACE;
+  return schedule_into(p, topk_idx, counts, offsets, perm, inv_perm, (char*)ws, stream);
+}
+
+int moe_dispatch(const moe_problem* p, const void* x, const int32_t* perm, int64_t slot_begin,
+                 int64_t slot_count, void* x_slot, uint8_t* x_slot_scales, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!x || !perm || !x_slot) return MOE_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)p->T * p->K;
+  if (slot_begin < 0 || slot_count < 0 || slot_begin + slot_count > n) return MOE_ERR_INVALID_ARG;
+  if ((p->dtype == MOE_MXFP8) != (x_slot_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_slot)) return MOE_ERR_MISALIGNED;
+  return launch_dispatch(x, p->dtype, perm, p->K, p->D, slot_begin, slot_count, x_slot, x_slot_scales, stream);
+}
+
+int moe_combine(const moe_problem* p, const void* y_routes, const void* shared_out,
+                const float* topk_w, void* out, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!y_routes || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_routes) || !aligned16(out) || (shared_out && !aligned16(shared_out))) return MOE_ERR_MISALIGNED;
+  return launch_combine(y_routes, shared_out, topk_w, out, p->T, p->K, p->D,
+                        p->dtype == MOE_F32 ? MOE_F32 : MOE_BF16, stream);
+}
+
+int moe_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, uint8_t* q, uint8_t* scales,
+                    hipStream_t stream) {
+  if (!src_bf16 || !q || !scales || rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 32) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(src_bf16) || !aligned16(q)) return MOE_ERR_MISALIGNED;
+  return launch_quantize_mx((const uint16_t*)src_bf16, rows, cols, q, scales, stream);
+}
+
+// Expert FFN over grouped rows: h = SwiGLU(A), y = h W_down^T (optionally scattered).
+static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda, const int32_t* gather,
+                      int gather_div, const void* wg, const void* wu, const void* wd, int D, int I,
+                      int64_t w_stride_up, int64_t w_stride_down, void* h, void* y,
+                      const int32_t* scatter, hipStream_t stream, hipEvent_t mid = nullptr) {
+  GemmArgs g1;
+  g1.A = A; g1.lda = lda; g1.a_gather = gather; g1.a_div = gather_div;
+  g1.B = wg; g1.B2 = wu; g1.ldb = D; g1.b_group_stride = w_stride_up;
+  g1.N = I; g1.K = D; g1.C = h; g1.ldc = I;
+  GemmArgs g2;
+  g2.A = h; g2.lda = I;
+  g2.B = wd; g2.ldb = I; g2.b_group_stride = w_stride_down;
+  g2.N = D; g2.K = I; g2.C = y; g2.ldc = D; g2.c_scatter = scatter;
+  int st;
+  if (dtype == MOE_F32) {
+    g1.c_f32 = 1; g2.c_f32 = 1;
+    st = launch_gemm_f32(g1, grp, EPI_SWIGLU, stream);
+    if (st) return st;
+    if (mid && hipEventRecord(mid, stream) != hipSuccess) return MOE_ERR_HIP;
+    return launch_gemm_f32(g2, grp, EPI_STORE, stream);
+  }
+  st = launch_gemm_bf16(g1, grp, EPI_SWIGLU, stream);
+  if (st) return st;
+  if (mid && hipEventRecord(mid, stream) != hipSuccess) return MOE_ERR_HIP;
+  return launch_gemm_bf16(g2, grp, EPI_STORE, stream);
+}
+
+int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
+                       void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
+                       size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!x || !logits || !w || !out || !r) return MOE_ERR_INVALID_ARG;
+  if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+  if (p->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  WsLayout L = ws_layout(*p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (y_routes && !aligned16(y_routes)) ||
+      (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_MISALIGNED;
+  char* wsb = (char*)ws;
+  const int64_t n = (int64_t)p->T * p->K;
+  const size_t act = elt_bytes(p->dtype);
+  void* yr = y_routes ? y_routes : (void*)(wsb + L.y_routes);
+  void* sho = p->I_shared > 0 ? (shared_out ? shared_out : (void*)(wsb + L.sh_out)) : nullptr;
+
+#define MOE_MARK(i) \
+  do { if (ev && hipEventRecord(ev[i], stream) != hipSuccess) return MOE_ERR_HIP; } while (0)
+  MOE_MARK(MOE_STAGE_ROUTE);
+  st = launch_route_topk(logits, r->topk_idx, r->topk_w, p->T, p->E, p->K, stream);
+  if (st) return st;
+  MOE_MARK(MOE_STAGE_SCHEDULE);
+  st = schedule_into(p, r->topk_idx, r->counts, r->offsets, r->perm, r->inv_perm, wsb, stream);
+  if (st) return st;
+
+  // shared expert first: it does not depend on the schedule
+  MOE_MARK(MOE_STAGE_SHARED);
+  if (p->I_shared > 0) {
+    Grouped gs;
+    gs.M = p->T;
+    st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
+                    0, 0, wsb + L.sh_h, sho, nullptr, stream);
+    if (st) return st;
+  }
+
+  Grouped gr;
+  gr.row_off = r->offsets;
+  gr.tile_off = (const int32_t*)(wsb + L.tile_off);
+  gr.groups = p->E;
+  gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
+  const void* A = x;
+  const int32_t* gather = r->perm;
+  MOE_MARK(MOE_STAGE_DISPATCH);
+  if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
+    st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream);
+    if (st) return st;
+    A = wsb + L.x_slot;
+    gather = nullptr;
+  }
+  MOE_MARK(MOE_STAGE_UP_GATE);
+  st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
+                  (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
+                  ev ? ev[MOE_STAGE_DOWN] : nullptr);
+  if (st) return st;
+  (void)act;
+  MOE_MARK(MOE_STAGE_COMBINE);
+  st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
+  if (st) return st;
+  MOE_MARK(MOE_STAGE_COUNT);
+#undef MOE_MARK
+  return MOE_OK;
+}
+
+int moe_forward(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
+                void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
+                size_t ws_bytes, hipStream_t stream) {
+  return moe_forward_stages(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream);
+}
+
+int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits,
+                 const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* dw,
+                 float* d_topk_w, float* d_logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  (void)dout; (void)x; (void)logits; (void)w; (void)routing; (void)dx; (void)dw; (void)d_topk_w;
+  (void)d_logits; (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                        const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)p; (void)slots; (void)x_slot; (void)offsets; (void)w; (void)y_slot; (void)x_local;
+  (void)shared_out; (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                         const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
+                         float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
+                         void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)p; (void)slots; (void)x_slot; (void)offsets; (void)g_slot; (void)dy_slot; (void)w; (void)dx_slot;
+  (void)dg_slot; (void)dw; (void)x_local; (void)dy_local; (void)dx_local; (void)ws; (void)ws_bytes;
+  (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// Row movement kernels: dispatch into expert-contiguous slots, the fixed-order combine, and the
+// MX quantiser. All are HBM-bound row copies with 16-byte vector accesses.
+//
+// Dispatch is the one-GPU analogue of the pull dispatch (sparsenotes page "Mixture-of-Kittens:
+// MoE Megakernel for NVL72s", section "Pull dispatch, push combine"): the destination slot j
+// reads its source row perm[j] / K. Combine is the source side's weighted sum over the
+// per-route rows y[t*K + k] that the push combine wrote (Cursor blog "Mixture-of-Kittens: our
+// open-source MoE megakernel for NVL72s", section "Scheduling", where one table serves both
+// exchanges), summed in a fixed order with no atomics (sparsenotes page, "The production
+// details", on determinism).
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// OCP MX v1.0 encoding helpers (E4M3 elements, E8M0 block scale, blocks of 32)
+// ---------------------------------------------------------------------------------------------
+// |v| already divided by the block scale -> E4M3 code, round to nearest even, saturate at 448.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a < 448.0f)) return sign | 0x7eu;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    return sign | (uint32_t)rintf(a * 512.0f);   // 8 (== 2^-6) is also the first normal code
+  }
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;   // keep 3 mantissa bits, RNE
+  int code = (int)r - ((127 - 7) << 3);                         // rebias 127 -> 7
+  if (code > 0x7e) code = 0x7e;
+  return sign | (uint32_t)code;
+}
+
+// Block scale exponent for a block whose largest magnitude is amax (> 0):
+// floor(log2 amax) - 8, clamped to [-127, 127]. fp32 subnormals clamp to -127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  int eb = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  int se = eb - 127 - 8;
+  return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// Quantise 32 fp32 values (one block) into 32 codes packed in 8 words; returns the E8M0 byte.
+__device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* packed) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (amax == 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i] = 0u;
+    return 127u;
+  }
+  const int se = mx_shared_exp(amax);
+  const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w |= e4m3_code(v[4 * i + b] * inv) << (8 * b);
+    packed[i] = w;
+  }
+  return (uint32_t)(se + 127);
+}
+
+// ---------------------------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------------------------
+// One wavefront per destination slot; 16-byte chunks.
+__global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__ x,
+                                                       const int32_t* __restrict__ perm, int K,
+                                                       int chunks_per_row, int64_t begin,
+                                                       int64_t count, uint4* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= count) return;
+  const int64_t src = perm[begin + j] / K;
+  const uint4* s = x + src * chunks_per_row;
+  uint4* d = out + j * chunks_per_row;
+  for (int c = lane; c < chunks_per_row; c += 64) d[c] = s[c];
+}
+
+// MXFP8 dispatch: one lane per 32-element block of the row.
+__global__ __launch_bounds__(256) void dispatch_mx_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm, int K,
+                                                          int D, int64_t begin, int64_t count,
+                                                          uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= count) return;
+  const int64_t src = perm[begin + j] / K;
+  const int nb = D / 32;
+  for (int b = lane; b < nb; b += 64) {
+    const uint4* s = reinterpret_cast<const uint4*>(x + src * D + b * 32);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 u = s[c];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+        v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+    uint32_t p[8];
+    sc[j * nb + b] = (uint8_t)mx_block(v, p);
+    uint4* d = reinterpret_cast<uint4*>(q + j * D + b * 32);
+    d[0] = make_uint4(p[0], p[1], p[2], p[3]);
+    d[1] = make_uint4(p[4], p[5], p[6], p[7]);
+  }
+}
+
+int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D, int64_t begin,
+                    int64_t count, void* x_slot, uint8_t* x_slot_sc, hipStream_t s) {
+  if (count <= 0) return MOE_OK;
+  dim3 grid((unsigned)((count + 3) / 4)), block(256);
+  if (dtype == MOE_MXFP8) {
+    hipLaunchKernelGGL(dispatch_mx_kernel, grid, block, 0, s, (const uint16_t*)x, perm, K, D, begin,
+                       count, (uint8_t*)x_slot, x_slot_sc);
+  } else {
+    const int cpr = (int)(D * elt_bytes(dtype) / 16);
+    hipLaunchKernelGGL(dispatch_kernel, grid, block, 0, s, (const uint4*)x, perm, K, cpr, begin,
+                       count, (uint4*)x_slot);
+  }
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// combine: out[t] = shared[t] + sum_k w[t,k] * y[t*K+k], fp32, k ascending, one rounding
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ y,
+                                                           const uint16_t* __restrict__ sh,
+                                                           const float* __restrict__ w,
+                                                           uint16_t* __restrict__ out, int T,
+                                                           int K, int D) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int chunks = D / 8;
+  for (int c = lane; c < chunks; c += 64) {
+    float acc[8];
+    if (sh) {
+      uint4 u = reinterpret_cast<const uint4*>(sh + (size_t)t * D)[c];
+      uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __uint_as_float(q[i] << 16);
+        acc[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int k = 0; k < K; ++k) {
+      const float g = w[(size_t)t * K + k];
+      uint4 u = reinterpret_cast<const uint4*>(y + ((size_t)t * K + k) * D)[c];
+      uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(g, __uint_as_float(q[i] << 16), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(g, __uint_as_float(q[i] & 0xffff0000u), acc[2 * i + 1]);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f2bf(acc[2 * i]) | ((uint32_t)f2bf(acc[2 * i + 1]) << 16);
+    reinterpret_cast<uint4*>(out + (size_t)t * D)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restrict__ y,
+                                                          const float* __restrict__ sh,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ out, int T, int K,
+                                                          int D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * D) return;
+  const int64_t t = i / D, d = i % D;
+  float acc = sh ? sh[i] : 0.f;
+  for (int k = 0; k < K; ++k) acc = fmaf(w[t * K + k], y[(t * K + k) * D + d], acc);
+  out[i] = acc;
+}
+
+int launch_combine(const void* y_routes, const void* shared_out, const float* topk_w, void* out,
+                   int T, int K, int D, int dtype, hipStream_t s) {
+  if (dtype == MOE_F32) {
+    int64_t n = (int64_t)T * D;
+    hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float*)y_routes, (const float*)shared_out, topk_w, (float*)out, T, K, D);
+  } else {
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, (const uint16_t*)y_routes,
+                       (const uint16_t*)shared_out, topk_w, (uint16_t*)out, T, K, D);
+  }
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// MX quantiser for whole matrices (offline weights): one thread per 32-element block
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ src,
+                                                          int64_t nblocks, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ sc) {
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * 256) {
+    const uint4* s = reinterpret_cast<const uint4*>(src + b * 32);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 u = s[c];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+        v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+    uint32_t p[8];
+    sc[b] = (uint8_t)mx_block(v, p);
+    uint4* d = reinterpret_cast<uint4*>(q + b * 32);
+    d[0] = make_uint4(p[0], p[1], p[2], p[3]);
+    d[1] = make_uint4(p[4], p[5], p[6], p[7]);
+  }
+}
+
+int launch_quantize_mx(const uint16_t* src, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
+                       hipStream_t s) {
+  const int64_t nb = rows * (cols / 32);
+  if (nb == 0) return MOE_OK;
+  int64_t grid = (nb + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, nb, q, sc);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -228,3 +228,83 @@ def host_share(cfg: EPShareConfig) -> HostShare:
     su = host_normal(cfg.seed, TID_SUP, (Is, D), 1 / math.sqrt(D), 0, True)
     sd = host_normal(cfg.seed, TID_SDOWN, (D, Is), 1 / math.sqrt(Is), 0, True)
     return HostShare(cfg, counts, x_slot, g, dy, xl, dyl, wg, wu, wd, sg, su, sd)
+
+
+# ----------------------------------------------------------------------------------------------
+# device generator (full-size layers)
+# ----------------------------------------------------------------------------------------------
+def device_seed(cfg_seed: int, tensor_id: int, expert_id: int = 0) -> int:
+    return cfg_seed * 1_000_003 + tensor_id * 4099 + expert_id
+
+
+def device_normal(cfg_seed, tensor_id, shape, std, expert_id=0, dtype=None, device='cuda'):
+    """N(0, std^2) draws from torch's Philox generator on `device`, rounded to `dtype` (RNE)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(cfg_seed, tensor_id, expert_id))
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        v.mul_(std)
+    return v.to(dtype) if dtype is not None else v
+
+
+@dataclasses.dataclass
+class DeviceLayer:
+    """All inputs of one layer as device tensors (bf16 for BF16/MXFP8 configs, fp32 for f32)."""
+    cfg: LayerConfig
+    x: object
+    logits: object        # fp32 [T, E]
+    w_gate: object        # [E, I, D]
+    w_up: object
+    w_down: object        # [E, D, I]
+    ws_gate: object
+    ws_up: object
+    ws_down: object
+
+
+def device_layer(cfg: LayerConfig, device='cuda') -> DeviceLayer:
+    """Full-size inputs generated on the device, expert by expert. Same recipe as host_layer
+    (distributions and router construction), different generator (Philox)."""
+    import torch
+    dt = torch.float32 if cfg.dtype == 'f32' else torch.bfloat16
+    T, D, I, E, Is = cfg.T, cfg.D, cfg.I, cfg.E, cfg.I_shared
+    x = device_normal(cfg.seed, TID_X, (T, D), 1.0, dtype=dt, device=device)
+    if cfg.router == 'zipf_gumbel':
+        g = torch.Generator(device=device)
+        g.manual_seed(device_seed(cfg.seed, TID_GUMBEL))
+        u = torch.rand((T, E), generator=g, device=device, dtype=torch.float64).clamp_(min=1e-300)
+        lp = -cfg.zipf_s * torch.log(torch.arange(1, E + 1, device=device, dtype=torch.float64))
+        logits = (lp[None, :] - torch.log(-torch.log(u))).to(torch.float32)
+    else:
+        wr = device_normal(cfg.seed, TID_WR, (E, D), 1.0 / math.sqrt(D), device=device).double()
+        lg = x.double() @ wr.T
+        if cfg.router == 'gaussian_bias':
+            lg += device_normal(cfg.seed, TID_BIAS, (E,), math.sqrt(cfg.bias_var), device=device).double()[None, :]
+        logits = lg.to(torch.float32)
+        del wr, lg
+    wg = torch.empty((E, I, D), dtype=dt, device=device)
+    wu = torch.empty((E, I, D), dtype=dt, device=device)
+    wd = torch.empty((E, D, I), dtype=dt, device=device)
+    for e in range(E):
+        wg[e] = device_normal(cfg.seed, TID_WGATE, (I, D), 1 / math.sqrt(D), e, dt, device)
+        wu[e] = device_normal(cfg.seed, TID_WUP, (I, D), 1 / math.sqrt(D), e, dt, device)
+        wd[e] = device_normal(cfg.seed, TID_WDOWN, (D, I), 1 / math.sqrt(I), e, dt, device)
+    if Is > 0:
+        sg = device_normal(cfg.seed, TID_SGATE, (Is, D), 1 / math.sqrt(D), 0, dt, device)
+        su = device_normal(cfg.seed, TID_SUP, (Is, D), 1 / math.sqrt(D), 0, dt, device)
+        sd = device_normal(cfg.seed, TID_SDOWN, (D, Is), 1 / math.sqrt(Is), 0, dt, device)
+    else:
+        sg = su = sd = None
+    return DeviceLayer(cfg, x, logits, wg, wu, wd, sg, su, sd)
+
+
+def to_device(L: HostLayer, device='cuda') -> DeviceLayer:
+    """Upload a host layer (exact: host BF16-valued fp32 arrays convert to bf16 without rounding)."""
+    import torch
+    dt = torch.float32 if L.cfg.dtype == 'f32' else torch.bfloat16
+
+    def up(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device=device).to(dt)
+
+    return DeviceLayer(L.cfg, up(L.x), torch.from_numpy(L.logits).to(device), up(L.w_gate), up(L.w_up),
+                       up(L.w_down), up(L.ws_gate), up(L.ws_up), up(L.ws_down))

@@ -1,0 +1,80 @@
+"""The C ABI library loads, exports every entry point include/moe.h declares, and rejects bad
+arguments on the host (no GPU work is done on these paths). CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, 'include', 'moe.h')).read()
+    src = re.sub(r'/\*.*?\*/', '', src, flags=re.S)
+    return sorted(set(re.findall(r'\b(moe_[a-z_0-9]+)\s*\(', src)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ('moe_route_topk', 'moe_schedule', 'moe_dispatch', 'moe_combine', 'moe_forward',
+                 'moe_backward', 'moe_experts_forward', 'moe_experts_backward', 'moe_quantize_mx',
+                 'moe_workspace_size', 'moe_status_string'):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    import mixture_experts_layer_norm_amd as m
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(m.EXPORTED)
+
+
+def test_status_strings():
+    import mixture_experts_layer_norm_amd as m
+    for code, name in m.STATUS.items():
+        assert m.status_string(code) == name
+
+
+def test_workspace_size_and_validation():
+    import mixture_experts_layer_norm_amd as m
+    p = m.problem(8192, 7168, 2048, 256, 8, 2048, 'bf16')
+    n = m.workspace_size(p)
+    assert n > 8192 * 8 * 7168 * 2      # holds at least the per-route outputs
+    bad = [
+        m.problem(0, 128, 64, 8, 2),            # T < 1
+        m.problem(16, 128, 64, 8, 9),           # K > E
+        m.problem(16, 128, 64, 8, 0),           # K < 1
+        m.problem(16, 128, 64, 8, 2, dtype=7),  # unknown dtype
+        m.problem(16, 128, 64, 8, 2, ring_stages=2),
+    ]
+    for p in bad:
+        with pytest.raises(m.MoeError) as ei:
+            m.workspace_size(p)
+        assert ei.value.status == -1
+    for p in (m.problem(16, 100, 128, 8, 2, dtype='bf16'),    # D not a multiple of 128
+              m.problem(16, 128, 64, 2000, 2, dtype='bf16'),  # E > 1024
+              m.problem(16, 128, 64, 100, 65, dtype='bf16')):  # K > 64
+        with pytest.raises(m.MoeError) as ei:
+            m.workspace_size(p)
+        assert ei.value.status == -2
+
+
+def test_entry_points_reject_null_and_small_workspace_without_gpu():
+    """These calls return on the host before any HIP call (no device is present here)."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    p = m.problem(16, 128, 64, 8, 2, 64, 'f32')
+    P = ctypes.byref(p)
+    assert lib.moe_route_topk(P, None, None, None, None) == -1
+    assert lib.moe_schedule(P, 16, 16, 16, 16, 16, None, 0, None) == -3
+    assert lib.moe_schedule(P, 16, 16, 16, 16, 16, 256, 1, None) == -3
+    assert lib.moe_dispatch(P, 16, 16, 0, 10 ** 6, 16, None, None) == -1       # past T*K
+    assert lib.moe_dispatch(P, 16, 16, 0, 4, 16, 16, None) == -1              # scales without MXFP8
+    assert lib.moe_dispatch(P, 8, 16, 0, 4, 16, None, None) == -4             # misaligned x
+    assert lib.moe_combine(P, None, None, None, None, None) == -1
+    assert lib.moe_quantize_mx(16, 4, 48, 16, 16, None) == -2                 # cols % 32
+    w = m.Weights()
+    r = m.Routing()
+    assert lib.moe_forward(P, 16, 16, ctypes.byref(w), 16, ctypes.byref(r), None, None, None, 0, None) == -1

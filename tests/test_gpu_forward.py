@@ -1,0 +1,162 @@
+"""GPU parity of the forward path (dispatch, grouped GEMMs + SwiGLU, down projection with the
+scatter epilogue, shared expert, combine) against the fp64 oracle, plus determinism."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, ForwardRun, assert_close_rms, t2np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope='module')
+def m():
+    import mixture_experts_layer_norm_amd as mod
+    return mod
+
+
+SMALL_BF16 = synth.scaled(synth.DSV3, 'small_bf16_T300_D256_I256_E16_K4', T=300, D=256, I=256, E=16, K=4,
+                          I_shared=256)
+DENSE_F32 = synth.scaled(synth.TINY, 'dense_f32_E1_K1', E=1, K=1)
+DENSE_BF16 = synth.scaled(synth.MID, 'dense_bf16_E1_K1', T=200, D=256, I=128, E=1, K=1, I_shared=128)
+NOSHARED_BF16 = synth.scaled(synth.MID, 'noshared_bf16', T=257, D=384, I=256, E=12, K=3, I_shared=0)
+ONE_TOKEN = synth.scaled(synth.MID, 'one_token_bf16', T=1, D=256, I=128, E=8, K=2, I_shared=128)
+
+
+def oracle_forward(H: synth.HostLayer):
+    return oracle.moe_forward(H.x, H.logits, H.w_gate, H.w_up, H.w_down, H.cfg.K, H.ws_gate, H.ws_up, H.ws_down)
+
+
+def check_forward(m, cfg, flags=0, chunk_rows=0):
+    print(f'[forward] {cfg.name} flags={flags} chunk={chunk_rows}', flush=True)
+    H = synth.host_layer(cfg)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L, flags=flags, chunk_rows=chunk_rows)()
+    torch.cuda.synchronize()
+    out, idx, g, y, sh = oracle_forward(H)
+    tau = TOL[cfg.dtype]
+    bf = cfg.dtype != 'f32'
+    assert np.array_equal(run.topk_idx.cpu().numpy(), idx)
+    assert_close_rms(t2np(run.topk_w), g, TOL['f32'], 'g')
+    # per-route expert outputs in route order (push-combine destinations)
+    assert_close_rms(t2np(run.y_routes), y.reshape(cfg.T * cfg.K, cfg.D), tau, 'y_routes', bf)
+    if cfg.I_shared:
+        assert_close_rms(t2np(run.shared_out), sh, tau, 'shared_out', bf)
+    assert_close_rms(t2np(run.out), out, tau, 'out', bf)
+    return run
+
+
+@pytest.mark.parametrize('cfg', [synth.TINY, DENSE_F32, SMALL_BF16, DENSE_BF16, NOSHARED_BF16, ONE_TOKEN],
+                         ids=lambda c: c.name)
+def test_forward_small(m, cfg):
+    check_forward(m, cfg)
+
+
+def test_forward_tiny_ties(m):
+    """Tie-heavy logits (multiples of 0.25): routing stays bit-exact and the layer matches."""
+    H = synth.host_layer(synth.TINY)
+    H.logits = synth.tie_logits(H.logits)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L)()
+    torch.cuda.synchronize()
+    out, idx, *_ = oracle_forward(H)
+    assert np.array_equal(run.topk_idx.cpu().numpy(), idx)
+    assert_close_rms(t2np(run.out), out, TOL['f32'], 'out')
+
+
+def test_forward_mid(m):
+    check_forward(m, synth.MID)
+
+
+def test_forward_fused_gather_matches_dispatch_bitwise(m):
+    H = synth.host_layer(SMALL_BF16)
+    L = synth.to_device(H)
+    a = ForwardRun(m, L)()
+    b = ForwardRun(m, L, flags=m.MOE_FLAG_FUSED_GATHER)()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out) and torch.equal(a.y_routes, b.y_routes)
+
+
+def test_forward_bitwise_deterministic(m):
+    H = synth.host_layer(SMALL_BF16)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L)
+    ref = run().out.clone()
+    for _ in range(20):
+        run()
+        assert torch.equal(run.out, ref)
+
+
+def test_dispatch_standalone(m):
+    """moe_dispatch copies rows x[perm[j] / K] exactly (perm from the oracle's schedule)."""
+    cfg = SMALL_BF16
+    H = synth.host_layer(cfg)
+    _, _, perm, _ = oracle.schedule(oracle.route_topk(H.logits, cfg.K), cfg.E)
+    p = m.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, cfg.dtype)
+    x = torch.from_numpy(H.x).cuda().to(torch.bfloat16)
+    perm_d = torch.from_numpy(perm).cuda()
+    n = cfg.T * cfg.K
+    for begin, count in [(0, n), (5, n - 5), (n - 1, 1), (17, 0)]:
+        x_slot = torch.empty((max(count, 1), cfg.D), dtype=torch.bfloat16, device='cuda')
+        m.dispatch(p, x, perm_d, begin, count, x_slot)
+        torch.cuda.synchronize()
+        if count:
+            assert np.array_equal(t2np(x_slot[:count]), H.x[perm[begin:begin + count] // cfg.K])
+
+
+@pytest.mark.parametrize('dtype,shared', [('bf16', True), ('bf16', False), ('f32', True)])
+def test_combine_standalone(m, dtype, shared):
+    """moe_combine against the oracle's weighted sum, on seeded per-route rows and weights."""
+    T, K, D = 333, 6, 256
+    bf = dtype == 'bf16'
+    y = synth.host_normal(77, 0, (T * K, D), 1.0, bf16=bf)
+    sh = synth.host_normal(77, 1, (T, D), 1.0, bf16=bf) if shared else None
+    g = synth.host_rng(77, 2).random((T, K), dtype=np.float32)
+    p = m.problem(T, D, 128, 8, K, 128 if shared else 0, dtype)
+    tdt = torch.bfloat16 if bf else torch.float32
+    yd = torch.from_numpy(y).cuda().to(tdt)
+    shd = torch.from_numpy(sh).cuda().to(tdt) if shared else None
+    out = torch.empty((T, D), dtype=tdt, device='cuda')
+    m.combine(p, yd, shd, torch.from_numpy(g).cuda(), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(sh, y, g)
+    assert_close_rms(t2np(out), ref, 1e-5, 'combine', bf)
+    out2 = torch.empty_like(out)
+    m.combine(p, yd, shd, torch.from_numpy(g).cuda(), out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.slow
+def test_forward_dsv3_full_size_sampled(m):
+    """DeepSeek-V3 shape (T=8192, D=7168, I=2048, E=256, K=8, shared I=2048) in the launch
+    configuration the benchmark times; 8 sampled tokens checked against the oracle, routing
+    checked in full."""
+    cfg = synth.DSV3
+    print('[forward] dsv3 full size: generating inputs', flush=True)
+    L = synth.device_layer(cfg)
+    run = ForwardRun(m, L, want_parts=False)()
+    torch.cuda.synchronize()
+    lg = L.logits.cpu().numpy()
+    idx = oracle.route_topk(lg, cfg.K)
+    assert np.array_equal(run.topk_idx.cpu().numpy(), idx)
+    counts, offsets, perm, inv = oracle.schedule(idx, cfg.E)
+    assert np.array_equal(run.perm.cpu().numpy(), perm)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(cfg.T, 8, replace=False))
+    xs = L.x[toks].float().cpu().numpy()
+    # only the experts the sampled tokens use are fetched
+    used = set(idx[toks].ravel().tolist())
+    wg = {e: L.w_gate[e].float().cpu().numpy() for e in used}
+    wu = {e: L.w_up[e].float().cpu().numpy() for e in used}
+    wd = {e: L.w_down[e].float().cpu().numpy() for e in used}
+    print(f'[forward] dsv3 oracle on {len(toks)} tokens, {len(used)} experts', flush=True)
+    out, *_ = oracle.moe_forward(xs, lg[toks], lambda e: wg[e], lambda e: wu[e], lambda e: wd[e], cfg.K,
+                                 L.ws_gate.float().cpu().numpy(), L.ws_up.float().cpu().numpy(),
+                                 L.ws_down.float().cpu().numpy())
+    got = run.out[toks].float().cpu().numpy()
+    assert_close_rms(got, out, TOL['bf16'], 'dsv3 sampled out', True)
