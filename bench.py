@@ -106,6 +106,8 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    for e in [t_start, t_end] + [e for row in evs for e in row]:
+        e.record(stream)          # torch creates the HIP event on first record
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)

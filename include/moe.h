@@ -59,7 +59,9 @@ typedef enum moe_dtype {
 
 /* Problem descriptor. T tokens of dimension D; E routed experts of intermediate size I, K per
  * token; one shared expert of intermediate size I_shared (0 = none).
- * Size limits: 1 <= K <= min(E, 64); E <= 1024; T*K < 2^31. BF16/MXFP8 need D % 128 == 0 and
+ * Size limits: E <= 1024; T*K < 2^31; the routing entry points (route_topk, schedule, forward,
+ * backward) also need K <= min(E, 64) (the expert-level entry points use K only as slots per
+ * token). BF16/MXFP8 need D % 128 == 0 and
  * I % 128 == 0 (I_shared likewise); MOE_F32 needs D % 4 == 0.
  * chunk_rows (b): rows of the expert-contiguous routed buffer that one pipeline step carries
  *   through the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel for
@@ -117,6 +119,10 @@ const char *moe_status_string(int status);
  * (the largest of the three). Writes *bytes; returns MOE_OK or MOE_ERR_INVALID_ARG.
  * The first 256 bytes hold the sticky error word (offset 0, int32). */
 int moe_workspace_size(const moe_problem *p, size_t *bytes);
+
+/* Bytes of device workspace that moe_backward and moe_experts_backward need for `p` (the
+ * expert-level backward takes p->T * p->K as its slot capacity). Same conventions as above. */
+int moe_backward_workspace_size(const moe_problem *p, size_t *bytes);
 
 /* Top-K selection and router weights (Blog, "Overlapping computation and communication in
  * MoE": the router picks the top-k routed experts and weights them with g_i = s_i / sum s_j).
@@ -196,7 +202,9 @@ int moe_backward(const moe_problem *p, const void *dout, const void *x, const fl
 /* Expert-level forward of one expert-parallel rank's share (Blog, "Overlapping computation and
  * communication in MoE": EP sharding gives each rank a few routed experts plus the shared
  * expert). Slots arrive already grouped by local expert, as a pull dispatch lands them.
- * p->E = local experts, p->T = local tokens (rows of the shared expert); K is ignored.
+ * p->E = local experts, p->T = local tokens (rows of the shared expert), p->T * p->K = slot
+ * capacity (slots <= T*K). Offsets outside [0, slots] or decreasing are clamped (error word
+ * set) so that no access leaves the buffers. `ws` holds moe_workspace_size bytes.
  * x_slot [slots][D], offsets [E+1] device int32 (expert e owns rows offsets[e]..offsets[e+1]-1,
  * offsets[E] == slots) -> y_slot [slots][D] = E_e(x_slot) (unweighted; the source applies g).
  * x_local [T][D] -> shared_out [T][D] (skipped when I_shared == 0). BF16 only. */
@@ -208,7 +216,8 @@ int moe_experts_forward(const moe_problem *p, int64_t slots, const void *x_slot,
 /* Backward of moe_experts_forward where slot j contributes g_slot[j] * E_e(x_slot[j]) against
  * the upstream gradient dy_slot[j]. Outputs dx_slot [slots][D] (bf16), dg_slot [slots] fp32
  * (= <dy_slot[j], E_e(x_slot[j])>), routed and shared weight gradients (fp32) and dx_local
- * [T][D] (bf16, shared expert path with upstream dy_local [T][D]). BF16 only. */
+ * [T][D] (bf16, shared expert path with upstream dy_local [T][D]). BF16 only. `ws` holds
+ * moe_backward_workspace_size bytes. */
 int moe_experts_backward(const moe_problem *p, int64_t slots, const void *x_slot,
                          const int32_t *offsets, const float *g_slot, const void *dy_slot,
                          const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,

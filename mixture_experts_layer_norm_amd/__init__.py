@@ -27,7 +27,7 @@ DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
 
 EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_schedule', 'moe_dispatch',
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
-            'moe_quantize_mx', 'moe_forward_stages')
+            'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -64,6 +64,7 @@ _PP = ctypes.POINTER(Problem)
 _sig = {
     'moe_status_string': (ctypes.c_char_p, [ctypes.c_int]),
     'moe_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
+    'moe_backward_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
     'moe_route_topk': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_schedule': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_dispatch': (ctypes.c_int, [_PP, _P, _P, _i64, _i64, _P, _P, _P]),
@@ -118,6 +119,12 @@ def workspace_size(p: Problem) -> int:
     return n.value
 
 
+def backward_workspace_size(p: Problem) -> int:
+    n = _sz(0)
+    _check(_lib.moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)), 'moe_backward_workspace_size')
+    return n.value
+
+
 def route_topk(p, logits, topk_idx, topk_w, stream=None):
     _check(_lib.moe_route_topk(ctypes.byref(p), _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
            'moe_route_topk')
@@ -163,7 +170,10 @@ def forward_stages(p, x, logits, weights: Weights, out, routing: Routing, ws, ev
                    shared_out=None, stream=None):
     """moe_forward with per-stage HIP events: `events` is a sequence of len(STAGES) + 1
     torch.cuda.Event(enable_timing=True) objects, recorded on the library's stream."""
-    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    handles = [e.cuda_event for e in events]
+    if len(handles) != len(STAGES) + 1 or not all(handles):
+        raise ValueError('forward_stages needs len(STAGES) + 1 created events (record each once first)')
+    arr = (ctypes.c_void_p * len(handles))(*handles)
     _check(_lib.moe_forward_stages(ctypes.byref(p), _ptr(x), _ptr(logits), ctypes.byref(weights), _ptr(out),
                                    ctypes.byref(routing), _ptr(y_routes), _ptr(shared_out), _ptr(ws),
                                    ws.numel() * ws.element_size(), arr, _stream(stream)), 'moe_forward_stages')

@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include "common.h"
+#include "pipeline.h"
 
 namespace moe {
 
@@ -10,13 +11,21 @@ size_t elt_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Extra checks of the entry points that route tokens (top-k over the E experts).
+int validate_routing(const moe_problem* p) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (p->K > p->E) return MOE_ERR_INVALID_ARG;
+  if (p->K > 64) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int validate_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   if (p->T < 1 || p->D < 1 || p->I < 1 || p->E < 1 || p->K < 1 || p->I_shared < 0) return MOE_ERR_INVALID_ARG;
-  if (p->K > p->E) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
   if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
-  if (p->E > 1024 || p->K > 64) return MOE_ERR_UNSUPPORTED;
+  if (p->E > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_F32) {
     if (p->D % 4) return MOE_ERR_UNSUPPORTED;
@@ -34,12 +43,28 @@ WsLayout ws_layout(const moe_problem& p) {
   L.nblk = (n + kRouteRowsPerBlock - 1) / kRouteRowsPerBlock;
   L.chunk = n;
   L.stages = 1;
+  L.chunks = 1;
   L.ring_rows = n;
+  L.pipelined = p.chunk_rows > 0 && p.dtype == MOE_BF16 && !(p.flags & MOE_FLAG_FUSED_GATHER);
+  if (L.pipelined) {
+    // b: multiple of 256 rows, at least n/1024 (at most 1024 chunks), at most n rounded up
+    const int64_t nr = (n + 255) / 256 * 256;
+    int64_t b = ((int64_t)p.chunk_rows + 255) / 256 * 256;
+    const int64_t bmin = ((n + 1023) / 1024 + 255) / 256 * 256;
+    b = b < bmin ? bmin : b;
+    b = b > nr ? nr : b;
+    L.chunk = b;
+    L.chunks = (int32_t)((n + b - 1) / b);
+    L.stages = p.ring_stages ? p.ring_stages : 3;
+    L.ring_rows = (int64_t)(L.stages < L.chunks ? L.stages : L.chunks) * b;
+  }
   size_t o = 0;
   L.err = o; o += 256;
   L.ctrl = o; o += 4096;
   L.blk_hist = o; o = align256(o + (size_t)L.nblk * p.E * 4);
   L.tile_off = o; o = align256(o + (size_t)(p.E + 1) * 4);
+  L.grp_clean = o; o = align256(o + (size_t)(p.E + 1) * 4);
+  L.grp_poff = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.x_slot = o; o = align256(o + (size_t)L.ring_rows * p.D * (mx ? 1 : act));
   L.x_slot_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.D / 32) : 0));
   L.h = o; o = align256(o + (size_t)L.ring_rows * p.I * (mx ? 1 : act));
@@ -47,6 +72,9 @@ WsLayout ws_layout(const moe_problem& p) {
   L.y_routes = o; o = align256(o + (size_t)n * p.D * act);
   L.sh_h = o; o = align256(o + (size_t)p.T * p.I_shared * act);
   L.sh_out = o; o = align256(o + (p.I_shared > 0 ? (size_t)p.T * p.D * act : 0));
+  L.pipe_ctile = o; o = align256(o + (L.pipelined ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
+  L.pipe_base = o; o = align256(o + (L.pipelined ? (size_t)(L.chunks + 1) * 4 : 0));
+  L.pipe_ctr = o; o = align256(o + (L.pipelined ? (size_t)(2 + 3 * L.chunks) * 4 : 0));
   L.bwd = o;
   L.total = o;
   return L;
@@ -82,7 +110,7 @@ int moe_workspace_size(const moe_problem* p, size_t* bytes) {
 
 int moe_route_topk(const moe_problem* p, const float* logits, int32_t* topk_idx, float* topk_w,
                    hipStream_t stream) {
-  int st = validate_problem(p);
+  int st = validate_routing(p);
   if (st) return st;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   return launch_route_topk(logits, topk_idx, topk_w, p->T, p->E, p->K, stream);
@@ -98,7 +126,7 @@ static int schedule_into(const moe_problem* p, const int32_t* topk_idx, int32_t*
 
 int moe_schedule(const moe_problem* p, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                  int32_t* perm, int32_t* inv_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = validate_problem(p);
+  int st = validate_routing(p);
   if (st) return st;
   if (!topk_idx || !counts || !offsets || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < ws_layout(*p).total) return MOE_ERR_WORKSPACE;
@@ -165,13 +193,14 @@ static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda,
 int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                        void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
-  int st = validate_problem(p);
+  int st = validate_routing(p);
   if (st) return st;
   if (!x || !logits || !w || !out || !r) return MOE_ERR_INVALID_ARG;
   if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
   if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
-  if (p->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (y_routes && !aligned16(y_routes)) ||
@@ -179,7 +208,6 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
     return MOE_ERR_MISALIGNED;
   char* wsb = (char*)ws;
   const int64_t n = (int64_t)p->T * p->K;
-  const size_t act = elt_bytes(p->dtype);
   void* yr = y_routes ? y_routes : (void*)(wsb + L.y_routes);
   void* sho = p->I_shared > 0 ? (shared_out ? shared_out : (void*)(wsb + L.sh_out)) : nullptr;
 
@@ -194,7 +222,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
 
   // shared expert first: it does not depend on the schedule
   MOE_MARK(MOE_STAGE_SHARED);
-  if (p->I_shared > 0) {
+  if (p->I_shared > 0 && !L.pipelined) {
     Grouped gs;
     gs.M = p->T;
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
@@ -207,21 +235,83 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   gr.tile_off = (const int32_t*)(wsb + L.tile_off);
   gr.groups = p->E;
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
-  const void* A = x;
-  const int32_t* gather = r->perm;
-  MOE_MARK(MOE_STAGE_DISPATCH);
-  if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
-    st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream);
+  if (L.pipelined) {
+    // shared expert, dispatch into the ring, up/gate and down per chunk: one persistent kernel
+    const int64_t b = L.chunk;
+    PipeArgs pa{};
+    pa.T = p->T; pa.D = p->D; pa.I = p->I; pa.E = p->E; pa.K = p->K; pa.Is = p->I_shared;
+    pa.n = (int)n; pa.b = (int)b; pa.C = L.chunks; pa.S = L.stages;
+    pa.ntn1 = p->I / gemm_tile_cols(EPI_SWIGLU);
+    pa.ntn2 = (p->D + gemm_tile_cols(EPI_STORE) - 1) / gemm_tile_cols(EPI_STORE);
+    pa.ntn_s1 = p->I_shared / gemm_tile_cols(EPI_SWIGLU);
+    pa.ntn_s2 = pa.ntn2;
+    pa.sh_mt = (p->T + kGemmBM - 1) / kGemmBM;
+    pa.n_sh1 = p->I_shared > 0 ? pa.sh_mt * pa.ntn_s1 : 0;
+    pa.n_sh2 = p->I_shared > 0 ? pa.sh_mt * pa.ntn_s2 : 0;
+    pa.d_pre = 0;
+    for (int c = 0; c < L.stages && c < L.chunks; ++c) {
+      const int64_t rows = (n - c * b) < b ? (n - c * b) : b;
+      pa.d_pre += (int)((rows + kGemmBM - 1) / kGemmBM);
+    }
+    pa.x = (const uint16_t*)x; pa.perm = r->perm; pa.offsets = r->offsets;
+    pa.wg = (const uint16_t*)w->w_gate; pa.wu = (const uint16_t*)w->w_up; pa.wd = (const uint16_t*)w->w_down;
+    pa.sg = (const uint16_t*)w->ws_gate; pa.su = (const uint16_t*)w->ws_up; pa.sd = (const uint16_t*)w->ws_down;
+    pa.x_ring = (uint16_t*)(wsb + L.x_slot); pa.h_ring = (uint16_t*)(wsb + L.h); pa.y = (uint16_t*)yr;
+    pa.sh_h = (uint16_t*)(wsb + L.sh_h); pa.sh_out = (uint16_t*)sho;
+    pa.ctile = (const int32_t*)(wsb + L.pipe_ctile); pa.chunk_base = (const int32_t*)(wsb + L.pipe_base);
+    pa.ctr = (int32_t*)(wsb + L.pipe_ctr); pa.err = (int32_t*)(wsb + L.err);
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      return MOE_ERR_HIP;
+    st = launch_pipeline(pa, (int32_t*)(wsb + L.pipe_base), ncu, stream);
     if (st) return st;
-    A = wsb + L.x_slot;
-    gather = nullptr;
+    MOE_MARK(MOE_STAGE_DISPATCH);
+    MOE_MARK(MOE_STAGE_UP_GATE);
+    MOE_MARK(MOE_STAGE_DOWN);
+    MOE_MARK(MOE_STAGE_COMBINE);
+    st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
+    if (st) return st;
+    MOE_MARK(MOE_STAGE_COUNT);
+    return MOE_OK;
   }
-  MOE_MARK(MOE_STAGE_UP_GATE);
-  st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
-                  (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
-                  ev ? ev[MOE_STAGE_DOWN] : nullptr);
-  if (st) return st;
-  (void)act;
+  MOE_MARK(MOE_STAGE_DISPATCH);
+  if (mx) {
+    // quantise while dispatching, then the two block-scaled grouped GEMMs (h quantised in the
+    // SwiGLU epilogue)
+    uint8_t* xq = (uint8_t*)(wsb + L.x_slot);
+    uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
+    uint8_t* hq = (uint8_t*)(wsb + L.h);
+    uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
+    st = launch_dispatch(x, MOE_MXFP8, r->perm, p->K, p->D, 0, n, xq, xs, stream);
+    if (st) return st;
+    MOE_MARK(MOE_STAGE_UP_GATE);
+    GemmArgs g1;
+    g1.A = xq; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
+    g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hq; g1.ldc = p->I;
+    st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream);
+    if (st) return st;
+    MOE_MARK(MOE_STAGE_DOWN);
+    GemmArgs g2;
+    g2.A = hq; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
+    g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D; g2.c_scatter = r->perm;
+    st = launch_gemm_mx(g2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream);
+    if (st) return st;
+  } else {
+    const void* A = x;
+    const int32_t* gather = r->perm;
+    if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
+      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream);
+      if (st) return st;
+      A = wsb + L.x_slot;
+      gather = nullptr;
+    }
+    MOE_MARK(MOE_STAGE_UP_GATE);
+    st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
+                    (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
+                    ev ? ev[MOE_STAGE_DOWN] : nullptr);
+    if (st) return st;
+  }
   MOE_MARK(MOE_STAGE_COMBINE);
   st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
   if (st) return st;
@@ -234,34 +324,6 @@ int moe_forward(const moe_problem* p, const void* x, const float* logits, const 
                 void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
   return moe_forward_stages(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream);
-}
-
-int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits,
-                 const moe_weights* w, const moe_routing* routing, void* dx, const moe_grads* dw,
-                 float* d_topk_w, float* d_logits, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = validate_problem(p);
-  if (st) return st;
-  (void)dout; (void)x; (void)logits; (void)w; (void)routing; (void)dx; (void)dw; (void)d_topk_w;
-  (void)d_logits; (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
-}
-
-int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
-                        const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)p; (void)slots; (void)x_slot; (void)offsets; (void)w; (void)y_slot; (void)x_local;
-  (void)shared_out; (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_ERR_UNSUPPORTED;
-}
-
-int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
-                         const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
-                         float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
-                         void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)p; (void)slots; (void)x_slot; (void)offsets; (void)g_slot; (void)dy_slot; (void)w; (void)dx_slot;
-  (void)dg_slot; (void)dw; (void)x_local; (void)dy_local; (void)dx_local; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return MOE_ERR_UNSUPPORTED;
 }
 
 }  // extern "C"

@@ -1,0 +1,302 @@
+// Expert-level forward and the backward pass (host orchestration of the kernels).
+//
+// Backward of E(x) = W_down (SiLU(a) (*) u), a = W_gate x, u = W_up x, for slot rows weighted by
+// g (each slot enters the layer output as g * E(x)), following the sparsenotes page
+// "Mixture-of-Kittens: MoE Megakernel for NVL72s":
+//   * "A ring buffer instead of a host round-trip": forward activations are not kept; a and u
+//     are recomputed (replayed) from the slot rows;
+//   * "The production details": the router-weight gradient dg = <h, dh'> with dh' = W_down^T dy,
+//     so the down-projection output is never recomputed;
+//   * "Pull dispatch, push combine": the backward reverse-combine gathers the output gradient
+//     into slots (dy_slot[j] = dout[perm[j] / K]) and the reverse-dispatch sums each token's
+//     slot gradients back (fixed order, no atomics).
+// Steps per group of rows: weight transposes; replay (a, u in fp32); dgrad-down with the SwiGLU
+// backward in its epilogue (da, du and per-tile <h, dh'> partials); dgrad-up over [da | du] with
+// K = 2I; padded transposes of x, dy, g*h and [da | du]; K-grouped weight-gradient GEMMs.
+// Every GEMM operand that is not an exact input (da, du, g*h) is carried as a pair of bf16 values
+// hi + lo (lo = v - bf16(v)) and contracted in two K passes, so the BF16 MFMA inputs lose ~2^-17
+// relative instead of 2^-9; x, dy and the weights are exact bf16 inputs.
+#include "common.h"
+
+namespace moe {
+
+static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t err, offs, tile_off, poff, offs_s, tile_off_s, poff_s;
+  size_t g_slot, dg_slot, x_slot, dy_slot, dx_slot, dx_sh;
+  size_t act_a, act_u, dau, part, wdT, wguT, xT, dyT, ghT, dauT;
+  size_t s_a, s_u, s_dau, s_part, s_wdT, s_wguT, s_xT, s_dyT, s_hT, s_dauT;
+  size_t total;
+  int64_t n, Spad, Tpad;
+};
+
+// Workspace of the backward for up to n = T*K slot rows (bf16).
+static BwdLayout bwd_layout(const moe_problem& p) {
+  BwdLayout L{};
+  const int64_t n = (int64_t)p.T * p.K, T = p.T, D = p.D, I = p.I, E = p.E, Is = p.I_shared;
+  L.n = n;
+  L.Spad = (n + 64 * E + 63) / 64 * 64;
+  L.Tpad = (T + 127) / 64 * 64;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = al256(o + bytes); return at; };
+  L.err = take(256 + 4096);
+  L.offs = take((E + 1) * 4); L.tile_off = take((E + 1) * 4); L.poff = take((E + 1) * 4);
+  L.offs_s = take(8); L.tile_off_s = take(8); L.poff_s = take(8);
+  L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
+  L.x_slot = take(n * D * 2); L.dy_slot = take(n * D * 2); L.dx_slot = take(n * D * 2);
+  L.dx_sh = take(T * D * 2);
+  // fp32 replay a, u; [da | du | da_lo | du_lo] bf16; transposed padded x, dy, [g*h | lo], [da|du|lo]
+  L.act_a = take(n * I * 4); L.act_u = take(n * I * 4); L.dau = take(n * 4 * I * 2);
+  L.part = take(n * ((I + 127) / 128) * 4);
+  L.wdT = take(E * I * D * 2); L.wguT = take(E * D * 2 * I * 2);
+  L.xT = take(D * L.Spad * 2); L.dyT = take(D * L.Spad * 2); L.ghT = take(2 * I * L.Spad * 2);
+  L.dauT = take(4 * I * L.Spad * 2);
+  if (Is > 0) {
+    L.s_a = take(T * Is * 4); L.s_u = take(T * Is * 4); L.s_dau = take(T * 4 * Is * 2);
+    L.s_part = take(T * ((Is + 127) / 128) * 4);
+    L.s_wdT = take(Is * D * 2); L.s_wguT = take(D * 2 * Is * 2);
+    L.s_xT = take(D * L.Tpad * 2); L.s_dyT = take(D * L.Tpad * 2); L.s_hT = take(2 * Is * L.Tpad * 2);
+    L.s_dauT = take(4 * Is * L.Tpad * 2);
+  }
+  L.total = o;
+  return L;
+}
+
+struct CoreBufs {
+  void *act_a, *act_u, *dau, *wdT, *wguT, *xT, *dyT, *ghT, *dauT;
+  float* part;
+  int64_t Spad;
+};
+
+// Backward of one set of groups (routed experts, or the shared expert as one group).
+// rows: x_rows/dy_rows [n][D] grouped by offs (sanitised, device) with m-tile prefix tile_off
+// and padded offsets poff. g_rows may be null (weight 1). Outputs dx_rows [n][D] bf16, dg_rows
+// [n] fp32 (nullable), dW (fp32).
+static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
+                         const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
+                         const void* wg, const void* wu, const void* wd, void* dx_rows, float* dg_rows,
+                         float* dw_gate, float* dw_up, float* dw_down, const CoreBufs& b, hipStream_t s) {
+  int st;
+  // transposed weights: W_down^T [G][I][D]; [W_gate^T | W_up^T] [G][D][2I]
+  if ((st = launch_transpose_batched(wd, G, D, I, b.wdT, D, (int64_t)I * D, 0, s))) return st;
+  if ((st = launch_transpose_batched(wg, G, I, D, b.wguT, 2 * I, (int64_t)D * 2 * I, 0, s))) return st;
+  if ((st = launch_transpose_batched(wu, G, I, D, b.wguT, 2 * I, (int64_t)D * 2 * I, I, s))) return st;
+
+  Grouped grp;
+  grp.row_off = offs;
+  grp.tile_off = tile_off;
+  grp.groups = G;
+  grp.max_mtiles = (n_cap + kGemmBM - 1) / kGemmBM + G;
+
+  // replay: a = x W_gate^T, u = x W_up^T (kept in fp32)
+  GemmArgs r;
+  r.A = x_rows; r.lda = D; r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
+  r.N = I; r.K = D; r.C = b.act_a; r.C2 = b.act_u; r.ldc = I;
+  if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s))) return st;
+
+  // dgrad-down + SwiGLU backward: dh' = dy W_down; da, du (as bf16 hi/lo pairs); partial <h, dh'>
+  GemmArgs d;
+  d.A = dy_rows; d.lda = D; d.B = b.wdT; d.ldb = D; d.b_group_stride = (int64_t)I * D;
+  d.N = I; d.K = D; d.C = b.dau; d.C2 = (uint16_t*)b.dau + I; d.ldc = 4 * I; d.lo_off = 2 * I;
+  d.ea = (const float*)b.act_a; d.eu = (const float*)b.act_u; d.lde = I;
+  d.row_scale = g_rows; d.row_partial = b.part;
+  if ((st = launch_gemm_bf16(d, grp, EPI_DGRAD, s))) return st;
+  const int ntn_d = (I + gemm_tile_cols(EPI_DGRAD) - 1) / gemm_tile_cols(EPI_DGRAD);
+  if (dg_rows && (st = launch_row_sum(b.part, n_cap, ntn_d, dg_rows, s))) return st;
+
+  // dgrad-up: dx = [da | du] [W_gate^T | W_up^T]^T, high halves then low halves (two K passes)
+  GemmArgs u;
+  u.A = b.dau; u.lda = 4 * I; u.B = b.wguT; u.ldb = 2 * I; u.b_group_stride = (int64_t)D * 2 * I;
+  u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D; u.two_pass = 1; u.a_seg_shift = 2 * I;
+  if ((st = launch_gemm_bf16(u, grp, EPI_STORE, s))) return st;
+
+  // padded transposes for the weight gradients: x and dy exact; g*h and [da|du] as hi/lo rows
+  const int64_t Sp = b.Spad;
+  if ((st = launch_transpose_pad(TR_COPY, x_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.xT, Sp, s))) return st;
+  if ((st = launch_transpose_pad(TR_COPY, dy_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.dyT, Sp, s))) return st;
+  if ((st = launch_transpose_pad(TR_SWIGLU, b.act_a, b.act_u, g_rows, I, I, offs, poff, G, Sp, b.ghT, Sp, s, 1)))
+    return st;
+  if ((st = launch_transpose_pad(TR_COPY, b.dau, nullptr, nullptr, 4 * I, 4 * I, offs, poff, G, Sp, b.dauT, Sp, s)))
+    return st;
+
+  // dW_down[g] = sum_j dy_j (g_j h_j)^T   -> [D][I]  (B = g*h: high rows, then low rows)
+  GemmArgs w1;
+  w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
+  w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I;
+  w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp;
+  if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
+  // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
+  GemmArgs w2;
+  w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
+  w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D;
+  w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp;
+  return launch_gemm_bf16_kgroup(w2, G, s);
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
+  return CoreBufs{ws + L.act_a, ws + L.act_u, ws + L.dau, ws + L.wdT, ws + L.wguT, ws + L.xT, ws + L.dyT,
+                  ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad};
+}
+static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
+  return CoreBufs{ws + L.s_a, ws + L.s_u, ws + L.s_dau, ws + L.s_wdT, ws + L.s_wguT, ws + L.s_xT, ws + L.s_dyT,
+                  ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad};
+}
+
+// one group of T rows for the shared expert: offsets {0, T}
+__global__ void single_group_kernel(int rows, int32_t* offs) {
+  offs[0] = 0;
+  offs[1] = rows;
+}
+
+static int shared_backward(const moe_problem* p, const void* x, const void* dy, const moe_weights* w,
+                           const moe_grads* dw, void* dx, char* wsb, const BwdLayout& L, hipStream_t s) {
+  int32_t* o = (int32_t*)(wsb + L.offs_s);
+  hipLaunchKernelGGL(single_group_kernel, dim3(1), dim3(1), 0, s, p->T, o);
+  MOE_LAUNCH_CHECK();
+  int st = launch_group_prefix(o, 1, p->T, o, (int32_t*)(wsb + L.tile_off_s), (int32_t*)(wsb + L.poff_s),
+                               (int32_t*)(wsb + L.err), s);
+  if (st) return st;
+  return core_backward(1, p->T, p->D, p->I_shared, x, dy, nullptr, o, (int32_t*)(wsb + L.tile_off_s),
+                       (int32_t*)(wsb + L.poff_s), w->ws_gate, w->ws_up, w->ws_down, dx, nullptr, dw->dws_gate,
+                       dw->dws_up, dw->dws_down, shared_bufs(wsb, L), s);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = bwd_layout(*p).total;
+  return MOE_OK;
+}
+
+int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                        const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!x_slot || !offsets || !w || !y_slot || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;
+  if (p->I_shared > 0 && (!x_local || !shared_out || !w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
+  WsLayout L = ws_layout(*p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(x_slot) || !al16(y_slot) || !al16(ws) || (x_local && !al16(x_local)) || (shared_out && !al16(shared_out)))
+    return MOE_ERR_MISALIGNED;
+  char* wsb = (char*)ws;
+  // sanitised offsets + m-tile prefix
+  int32_t* clean = (int32_t*)(wsb + L.grp_clean);
+  int32_t* poff = (int32_t*)(wsb + L.grp_poff);
+  if ((st = launch_group_prefix(offsets, p->E, (int)slots, clean, (int32_t*)(wsb + L.tile_off), poff,
+                                (int32_t*)(wsb + L.err), stream)))
+    return st;
+  Grouped gr;
+  gr.row_off = clean;
+  gr.tile_off = (const int32_t*)(wsb + L.tile_off);
+  gr.groups = p->E;
+  gr.max_mtiles = (slots + kGemmBM - 1) / kGemmBM + p->E;
+  GemmArgs g1;
+  g1.A = x_slot; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
+  g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = wsb + L.h; g1.ldc = p->I;
+  if ((st = launch_gemm_bf16(g1, gr, EPI_SWIGLU, stream))) return st;
+  GemmArgs g2;
+  g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
+  g2.N = p->D; g2.K = p->I; g2.C = y_slot; g2.ldc = p->D;
+  if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream))) return st;
+  if (p->I_shared > 0) {
+    Grouped gs;
+    gs.M = p->T;
+    GemmArgs s1;
+    s1.A = x_local; s1.lda = p->D; s1.B = w->ws_gate; s1.B2 = w->ws_up; s1.ldb = p->D; s1.N = p->I_shared;
+    s1.K = p->D; s1.C = wsb + L.sh_h; s1.ldc = p->I_shared;
+    if ((st = launch_gemm_bf16(s1, gs, EPI_SWIGLU, stream))) return st;
+    GemmArgs s2;
+    s2.A = wsb + L.sh_h; s2.lda = p->I_shared; s2.B = w->ws_down; s2.ldb = p->I_shared; s2.N = p->D;
+    s2.K = p->I_shared; s2.C = shared_out; s2.ldc = p->D;
+    if ((st = launch_gemm_bf16(s2, gs, EPI_STORE, stream))) return st;
+  }
+  return MOE_OK;
+}
+
+int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                         const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
+                         float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
+                         void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
+  if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;
+  if (p->I_shared > 0 && (!x_local || !dy_local || !dx_local || !w->ws_gate || !w->ws_up || !w->ws_down ||
+                          !dw->dws_gate || !dw->dws_up || !dw->dws_down))
+    return MOE_ERR_INVALID_ARG;
+  BwdLayout L = bwd_layout(*p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(x_slot) || !al16(dy_slot) || !al16(dx_slot) || !al16(ws) || (x_local && !al16(x_local)) ||
+      (dy_local && !al16(dy_local)) || (dx_local && !al16(dx_local)))
+    return MOE_ERR_MISALIGNED;
+  char* wsb = (char*)ws;
+  int32_t* offs = (int32_t*)(wsb + L.offs);
+  if ((st = launch_group_prefix(offsets, p->E, (int)slots, offs, (int32_t*)(wsb + L.tile_off),
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream)))
+    return st;
+  if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
+                          (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down, dx_slot, dg_slot, dw->dw_gate,
+                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream)))
+    return st;
+  if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream);
+  return MOE_OK;
+}
+
+int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits, const moe_weights* w,
+                 const moe_routing* r, void* dx, const moe_grads* dw, float* d_topk_w, float* d_logits, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  int st = validate_routing(p);
+  if (st) return st;
+  (void)logits;   // the routing state of the forward carries everything the backward needs
+  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!dout || !x || !w || !r || !dx || !dw || !d_topk_w) return MOE_ERR_INVALID_ARG;
+  if (!r->topk_idx || !r->topk_w || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
+  if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
+  if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down || !dw->dws_gate || !dw->dws_up || !dw->dws_down))
+    return MOE_ERR_INVALID_ARG;
+  BwdLayout L = bwd_layout(*p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!al16(dout) || !al16(x) || !al16(dx) || !al16(ws)) return MOE_ERR_MISALIGNED;
+  char* wsb = (char*)ws;
+  const int64_t n = L.n;
+  // reverse-combine (pull dout into slots), replayed dispatch of x, slot weights
+  if ((st = launch_dispatch(dout, MOE_BF16, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
+  if ((st = launch_dispatch(x, MOE_BF16, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream))) return st;
+  if ((st = launch_gather_f32(r->topk_w, r->perm, n, (float*)(wsb + L.g_slot), stream))) return st;
+  int32_t* offs = (int32_t*)(wsb + L.offs);
+  if ((st = launch_group_prefix(r->offsets, p->E, (int)n, offs, (int32_t*)(wsb + L.tile_off),
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream)))
+    return st;
+  if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+                          (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down,
+                          wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down,
+                          routed_bufs(wsb, L), stream)))
+    return st;
+  if ((st = launch_router_backward((float*)(wsb + L.dg_slot), r->inv_perm, r->topk_idx, r->topk_w, p->T, p->E, p->K,
+                                   d_topk_w, d_logits, stream)))
+    return st;
+  void* dsh = nullptr;
+  if (p->I_shared > 0) {
+    dsh = wsb + L.dx_sh;
+    if ((st = shared_backward(p, x, dout, w, dw, dsh, wsb, L, stream))) return st;
+  }
+  // reverse-dispatch: dx[t] = dx_shared[t] + sum_k dx_slot[inv_perm[t*K + k]]
+  return launch_reverse_dispatch(wsb + L.dx_slot, r->inv_perm, dsh, dx, p->T, p->K, p->D, stream);
+}
+
+}  // extern "C"

@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;   // raw bf16 bits in memory
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
@@ -34,7 +35,7 @@ __device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __ex
 // workspace layout (byte offsets from the workspace base)
 // ---------------------------------------------------------------------------------------------
 constexpr int kRouteRowsPerBlock = 2048;     // schedule: routes per histogram block
-constexpr int kGemmBM = 128;                 // rows per grouped-GEMM m-tile
+constexpr int kGemmBM = 256;                 // rows per grouped-GEMM m-tile
 constexpr int kErrOffset = 0;                // sticky error word (int32)
 
 struct WsLayout {
@@ -42,6 +43,8 @@ struct WsLayout {
   size_t ctrl;             // pipeline counters / flags
   size_t blk_hist;         // [nblk][E] int32
   size_t tile_off;         // [E+1] int32  m-tile prefix for kGemmBM
+  size_t grp_clean;        // [E+1] int32  sanitised caller offsets (expert-level entry)
+  size_t grp_poff;         // [E+1] int32  64-padded offsets
   size_t x_slot;           // dispatched rows
   size_t x_slot_sc;        // MX scales of x_slot
   size_t h;                // gated activation
@@ -51,15 +54,21 @@ struct WsLayout {
   size_t sh_out;           // shared expert output [T][D]
   size_t bwd;              // backward scratch start
   size_t total;
+  size_t pipe_ctile;       // [C][E+1] int32 (chunked pipeline)
+  size_t pipe_base;        // [C+1] int32
+  size_t pipe_ctr;         // [2 + 3C] int32
   int64_t nblk;            // histogram blocks
   int64_t ring_rows;       // rows of x_slot / h held (chunk * stages, or T*K)
   int64_t chunk;           // rows per chunk
   int32_t stages;          // ring stages (1 when one chunk holds everything)
+  int32_t chunks;          // C (1 when one chunk holds everything)
+  bool pipelined;          // chunked persistent pipeline in use
 };
 
 size_t elt_bytes(int dtype);
 WsLayout ws_layout(const moe_problem& p);
 int validate_problem(const moe_problem* p);
+int validate_routing(const moe_problem* p);
 
 // ---------------------------------------------------------------------------------------------
 // launchers (each returns 0 or a moe_status; all enqueue on `s`)
@@ -73,6 +82,21 @@ int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D,
                     int64_t count, void* x_slot, uint8_t* x_slot_sc, hipStream_t s);
 int launch_combine(const void* y_routes, const void* shared_out, const float* topk_w, void* out,
                    int T, int K, int D, int dtype, hipStream_t s);
+int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean, int32_t* tile_off, int32_t* poff,
+                        int32_t* err, hipStream_t s);
+int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
+                         const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
+                         int64_t ldo, hipStream_t s, int split_lo = 0);
+int launch_transpose_batched(const void* in, int B, int R, int C, void* out, int64_t ldo, int64_t out_batch_stride,
+                             int col0, hipStream_t s);
+int launch_row_sum(const float* part, int64_t rows, int ntn, float* out, hipStream_t s);
+int launch_gather_f32(const float* src, const int32_t* idx, int64_t n, float* out, hipStream_t s);
+int launch_router_backward(const float* dg_slot, const int32_t* inv_perm, const int32_t* topk_idx,
+                           const float* topk_w, int T, int E, int K, float* d_topk_w, float* d_logits,
+                           hipStream_t s);
+int launch_reverse_dispatch(const void* dx_slot, const int32_t* inv_perm, const void* dx_shared, void* dx, int T,
+                            int K, int D, hipStream_t s);
+enum { TR_COPY = 0, TR_SCALE = 1, TR_SWIGLU = 2 };   // TR_SWIGLU reads fp32 a and u
 int launch_quantize_mx(const uint16_t* src, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                        hipStream_t s);
 
@@ -87,7 +111,12 @@ struct Grouped {
   int64_t max_mtiles = 0;     // host bound on the number of m-tiles (grid size)
 };
 
-enum Epi { EPI_SWIGLU = 0, EPI_STORE = 1 };
+// EPI_SWIGLU:   h = SiLU(gate) * up                       -> C
+// EPI_STORE:    plain product (optional row scatter)       -> C (bf16 or fp32)
+// EPI_SAVE_AU:  gate pre-activation a -> C, up projection u -> C2 (fp32)
+// EPI_DGRAD:    product dh' = dY W_down; with a, u (ea, eu, fp32) and the row weight g:
+//               da -> C, du -> C2 (bf16) and per-tile partial <h, dh'> -> row_partial
+enum Epi { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_SAVE_AU = 2, EPI_DGRAD = 3 };
 
 struct GemmArgs {
   const void* A = nullptr; int64_t lda = 0;
@@ -99,9 +128,34 @@ struct GemmArgs {
   void* C = nullptr; int64_t ldc = 0;                    // output
   const int32_t* c_scatter = nullptr;                    // output row r -> c_scatter[r]
   int32_t c_f32 = 0;                                     // store fp32 instead of bf16
+  void* C2 = nullptr;                                    // second output (see Epi)
+  // K-grouped mode (weight gradients): group g contracts k in [k_off[g], k_off[g+1]) (multiples
+  // of 64); A is [M][lda], B is [N][ldb] shared by all groups; the fp32 output of group g is
+  // C + g * c_group_stride ([M][ldc]), or C2 + g * c_group_stride for rows >= m_split.
+  const int32_t* k_off = nullptr;
+  int32_t M = 0;
+  int32_t m_split = 0;
+  int64_t c_group_stride = 0;
+  // EPI_DGRAD inputs
+  const float* ea = nullptr;          // a [rows][lde]
+  const float* eu = nullptr;          // u [rows][lde]
+  int64_t lde = 0;
+  const float* row_scale = nullptr;   // g per row
+  float* row_partial = nullptr;       // [rows][N / 256]
+  int64_t lo_off = 0;                 // EPI_DGRAD: also store the low halves (v - bf16(v)) at C + lo_off / C2 + lo_off
+  // second K pass (hi/lo operand splitting): when nonzero, the K range is run twice, the second
+  // time with A and B displaced by these element offsets, accumulating into the same tile
+  int64_t a_seg_shift = 0, b_seg_shift = 0;
+  int32_t two_pass = 0;
 };
 
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
+int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s);
+int gemm_tile_cols(Epi epi);
+struct PipeArgs;
+int launch_pipeline(const PipeArgs& host, int32_t* chunk_base_dev, int ncu, hipStream_t s);
+int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
+                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,277 @@
+// MXFP8 grouped GEMMs on gfx950's block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// The sparsenotes page "Mixture-of-Kittens: MoE Megakernel for NVL72s" ("The production details")
+// runs the routed experts in MXFP8 with activation quantisation fused into dispatch, the grouped
+// GEMMs and the gated activation; the shared expert stays BF16. Operands here are OCP MX v1.0:
+// E4M3 bytes with one E8M0 scale byte per 32 elements along the contraction dimension.
+//
+//   up/gate:  h = SiLU(X W_gate^T) (*) (X W_up^T), quantised to MXFP8 along I in the epilogue
+//   down:     y = h W_down^T (bf16), row j stored at c_scatter[j]
+//
+// Tiling matches the BF16 kernel byte for byte: 256 rows x 256 weight rows, a K step of 128 fp8
+// values (128 bytes per row, LDS rows padded by 16 B), 8 wavefronts of 128 x 64, and two scaled
+// MFMAs (K = 64 each) per K step. Operand layout of the scaled 32x32x64 MFMA (lane l, lane group
+// q = l / 32, row or column l % 32): bytes 0-15 of a lane's 32 hold K block 0 of the instruction
+// and bytes 16-31 K block 1 (32 values each); lane group q supplies K values [16q, 16q+16) of each
+// block and the E8M0 scale of block q. Scales are loaded per lane straight from global memory
+// (4 bytes = the 4 blocks of one row and K step) and the lane's byte is shifted into place.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+constexpr int BM = kGemmBM;   // 256
+constexpr int BKB = 128;      // K step in fp8 elements (= bytes)
+constexpr int PITCH = BKB + 16;
+}  // namespace
+
+__device__ __forceinline__ bool locate_tile_mx(const Grouped& g, int mt, int& grp, int& r0, int& rows) {
+  if (g.row_off) {
+    const int total = g.tile_off[g.groups];
+    if (mt >= total) return false;
+    int lo = 0, hi = g.groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    grp = lo;
+    r0 = g.row_off[lo] + (mt - g.tile_off[lo]) * BM;
+    rows = min(BM, g.row_off[lo + 1] - r0);
+  } else {
+    grp = 0;
+    r0 = mt * BM;
+    if (r0 >= g.M) return false;
+    rows = min(BM, g.M - r0);
+  }
+  return true;
+}
+
+// Quantised E4M3 code of v / 2^se (saturating, RNE); same rule as the dispatch quantiser.
+__device__ __forceinline__ uint32_t e4m3_code_scaled(float v, float inv_scale) {
+  const float s = v * inv_scale;
+  const uint32_t sign = (__float_as_uint(s) >> 24) & 0x80u;
+  const float a = fabsf(s);
+  if (!(a < 448.0f)) return sign | 0x7eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
+  int code = (int)r - ((127 - 7) << 3);
+  if (code > 0x7e) code = 0x7e;
+  return sign | (uint32_t)code;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
+                                                         const uint8_t* __restrict__ b_sc,
+                                                         const uint8_t* __restrict__ b2_sc, int64_t sc_group_stride,
+                                                         uint8_t* __restrict__ h_sc, Grouped g, int ntn) {
+  constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
+  constexpr int MI = WM / 32, NJ = WN / 32;
+  constexpr int A_T = BM * PITCH, B_T = BN * PITCH;
+  constexpr int RPP = 512 / 8;
+  constexpr int AL = BM / RPP, BL = BN / RPP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_T + B_T)];
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int nt = logical % ntn;
+  int grp, r0, rows;
+  if (!locate_tile_mx(g, logical / ntn, grp, r0, rows)) return;
+  const int nk = a.K / BKB;
+  const int kbl = a.K / 32;                      // scale bytes per row
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = tid >> 3, lchunk = tid & 7;
+  const uint8_t* abase = (const uint8_t*)a.A + lchunk * 16;
+  uint32_t aoff[AL];
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int r = r0 + min(lrow + RPP * i, rows - 1);
+    aoff[i] = (uint32_t)((int64_t)r * a.lda);
+  }
+  const uint8_t* bbase[2];
+  bbase[0] = (const uint8_t*)a.B + (int64_t)grp * a.b_group_stride + lchunk * 16;
+  bbase[1] = (EPI == EPI_SWIGLU) ? (const uint8_t*)a.B2 + (int64_t)grp * a.b_group_stride + lchunk * 16 : bbase[0];
+  uint32_t boff[BL];
+  bool bup[BL];
+#pragma unroll
+  for (int i = 0; i < BL; ++i) {
+    const int rr = lrow + RPP * i;
+    int64_t wrow;
+    if (EPI == EPI_SWIGLU) {
+      const int wc = rr / WN, q = (rr % WN) / 32;
+      bup[i] = q >= NJ / 2;
+      wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (bup[i] ? q - NJ / 2 : q) * 32 + (rr & 31);
+    } else {
+      bup[i] = false;
+      wrow = (int64_t)nt * BN + rr;
+    }
+    wrow = wrow < a.N ? wrow : a.N - 1;
+    boff[i] = (uint32_t)(wrow * a.ldb);
+  }
+  // scale rows this lane feeds to the MFMAs: A rows of its row blocks, B rows of its column blocks
+  // scale words are addressed as 32-bit offsets from the scale bases (4 blocks per word)
+  const uint32_t* asb = reinterpret_cast<const uint32_t*>(a_sc);
+  const uint32_t* bsb0 = reinterpret_cast<const uint32_t*>(b_sc + (int64_t)grp * sc_group_stride);
+  const uint32_t* bsb1 = reinterpret_cast<const uint32_t*>((EPI == EPI_SWIGLU ? b2_sc : b_sc) + (int64_t)grp * sc_group_stride);
+  uint32_t asc[MI], bsc[NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = r0 + min(wm * WM + i * 32 + (lane & 31), rows - 1);
+    asc[i] = (uint32_t)((int64_t)r * kbl / 4);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int cc = wn * WN + j * 32 + (lane & 31);   // weight row within the tile
+    int64_t wrow;
+    if (EPI == EPI_SWIGLU) {
+      const bool up = j >= NJ / 2;
+      wrow = (int64_t)nt * (BN / 2) + wn * (WN / 2) + (up ? j - NJ / 2 : j) * 32 + (lane & 31);
+    } else {
+      wrow = (int64_t)nt * BN + cc;
+    }
+    wrow = wrow < a.N ? wrow : a.N - 1;
+    bsc[j] = (uint32_t)(wrow * kbl / 4);
+  }
+  const int q = lane >> 5;
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int wrows = rows - wm * WM;
+
+  u32x4 ra[AL], rb[BL];
+  const int st_off = lrow * PITCH + lchunk * 16;
+#pragma unroll
+  for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + aoff[i]);
+#pragma unroll
+  for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase[bup[i]] + boff[i]);
+#pragma unroll
+  for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(smem + st_off + RPP * i * PITCH) = ra[i];
+#pragma unroll
+  for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(smem + A_T + st_off + RPP * i * PITCH) = rb[i];
+  __syncthreads();
+  const int a_rd = (wm * WM + (lane & 31)) * PITCH + q * 16;
+  const int b_rd = (wn * WN + (lane & 31)) * PITCH + q * 16;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) {
+      const int ko = (kt + 1) * BKB;
+#pragma unroll
+      for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + aoff[i] + ko);
+#pragma unroll
+      for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase[bup[i]] + boff[i] + ko);
+    }
+    uint32_t sa[MI], sbv[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) sa[i] = asb[asc[i] + kt];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sbv[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j] + kt];
+    const uint8_t* As = smem + buf * (A_T + B_T);
+    const uint8_t* Bs = As + A_T;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {            // two K = 64 instructions per K step
+      i32x8 af[MI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint8_t* p = As + a_rd + i * 32 * PITCH + s * 64;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 32);
+        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint8_t* p = Bs + b_rd + j * 32 * PITCH + s * 64;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 32);
+        bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      const int shift = 8 * (2 * s + q);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        if (i * 32 < wrows) {
+          const int sca = (int)((sa[i] >> shift) & 0xffu);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int scb = (int)((sbv[j] >> shift) & 0xffu);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, sca, 0, scb);
+          }
+        }
+      }
+    }
+    if (kt + 1 < nk) {
+      uint8_t* An = smem + (buf ^ 1) * (A_T + B_T);
+#pragma unroll
+      for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(An + st_off + RPP * i * PITCH) = ra[i];
+#pragma unroll
+      for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(An + A_T + st_off + RPP * i * PITCH) = rb[i];
+    }
+    __syncthreads();
+  }
+
+  const int ccol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
+      const bool ok = lr < rows;
+      const int row = r0 + lr;
+      if (EPI == EPI_SWIGLU) {
+        // one 32-column MX block per (row, wavefront): amax over the 32 lanes of this lane group
+        const int64_t col = (int64_t)nt * (BN / 2) + wn * (WN / 2) + ccol;
+        const float h = silu_f(acc[i][0][r]) * acc[i][1][r];
+        float amax = fabsf(h);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        uint32_t code = 0, sbyte = 127;
+        if (amax > 0.f) {
+          int eb = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+          int se = eb - 127 - 8;
+          se = se < -127 ? -127 : (se > 127 ? 127 : se);
+          sbyte = (uint32_t)(se + 127);
+          code = e4m3_code_scaled(h, __uint_as_float((uint32_t)(127 - se) << 23));
+        }
+        if (ok && col < a.N) {
+          ((uint8_t*)a.C)[(int64_t)row * a.ldc + col] = (uint8_t)code;
+          if (ccol == 0) h_sc[(int64_t)row * (a.ldc / 32) + col / 32] = (uint8_t)sbyte;
+        }
+      } else {
+        if (!ok) continue;
+        const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int64_t col = (int64_t)nt * BN + wn * WN + j * 32 + ccol;
+          if (col < a.N) ((uint16_t*)a.C)[orow * a.ldc + col] = f2bf(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+// a_sc / b_sc / b2_sc: E8M0 scales of A [rows][K/32] and of the weights [G][N][K/32].
+int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
+                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s) {
+  const int tcols = (epi == EPI_SWIGLU) ? 128 : 256;
+  const int ntn = (a.N + tcols - 1) / tcols;
+  const int64_t mt = g.row_off ? g.max_mtiles : (g.M + BM - 1) / BM;
+  int64_t nb = mt * ntn;
+  nb = (nb + 7) / 8 * 8;
+  if (nb == 0) return MOE_OK;
+  if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  if (epi == EPI_SWIGLU)
+    hipLaunchKernelGGL(gemm_mx_kernel<EPI_SWIGLU>, dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
+                       sc_group_stride, h_sc, g, ntn);
+  else
+    hipLaunchKernelGGL(gemm_mx_kernel<EPI_STORE>, dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
+                       sc_group_stride, h_sc, g, ntn);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+}  // namespace moe

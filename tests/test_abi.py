@@ -44,7 +44,6 @@ def test_workspace_size_and_validation():
     assert n > 8192 * 8 * 7168 * 2      # holds at least the per-route outputs
     bad = [
         m.problem(0, 128, 64, 8, 2),            # T < 1
-        m.problem(16, 128, 64, 8, 9),           # K > E
         m.problem(16, 128, 64, 8, 0),           # K < 1
         m.problem(16, 128, 64, 8, 2, dtype=7),  # unknown dtype
         m.problem(16, 128, 64, 8, 2, ring_stages=2),
@@ -54,11 +53,15 @@ def test_workspace_size_and_validation():
             m.workspace_size(p)
         assert ei.value.status == -1
     for p in (m.problem(16, 100, 128, 8, 2, dtype='bf16'),    # D not a multiple of 128
-              m.problem(16, 128, 64, 2000, 2, dtype='bf16'),  # E > 1024
-              m.problem(16, 128, 64, 100, 65, dtype='bf16')):  # K > 64
+              m.problem(16, 128, 64, 2000, 2, dtype='bf16')):  # E > 1024
         with pytest.raises(m.MoeError) as ei:
             m.workspace_size(p)
         assert ei.value.status == -2
+    # routing entry points also need K <= min(E, 64); the expert-level ones use K as slots/token
+    lib = m._lib
+    assert lib.moe_route_topk(ctypes.byref(m.problem(16, 128, 128, 8, 9)), 16, 16, 16, None) == -1
+    assert lib.moe_route_topk(ctypes.byref(m.problem(16, 128, 128, 100, 65)), 16, 16, 16, None) == -2
+    assert m.workspace_size(m.problem(7168, 7168, 2048, 4, 8, 2048)) > 0   # 4 local experts, 8 slots/token
 
 
 def test_entry_points_reject_null_and_small_workspace_without_gpu():

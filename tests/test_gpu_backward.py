@@ -1,0 +1,144 @@
+"""GPU parity of the expert-level forward/backward (one expert-parallel rank's share) and of the
+whole-layer backward against the fp64 oracle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, ForwardRun, assert_close_rms, t2np
+
+pytestmark = pytest.mark.gpu
+TAU = TOL['bf16']
+
+
+@pytest.fixture(scope='module')
+def m():
+    import mixture_experts_layer_norm_amd as mod
+    return mod
+
+
+def bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+def share_inputs(cfg, counts):
+    """Seeded share inputs with given per-expert slot counts (sum <= tokens * K)."""
+    S = int(sum(counts))
+    base = synth.host_share(dataclasses.replace(cfg))
+    return base, S
+
+
+SMALL_SHARE = synth.EPShareConfig('small_share_bf16_T100_K5_D256_I256_E3', tokens=100, D=256, I=256, E_local=3, K=5,
+                                  I_shared=128, zipf_s=1.2, seed=41)
+
+
+def run_share(m, H, counts):
+    cfg = H.cfg
+    S = int(sum(counts))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    p = m.problem(cfg.tokens, cfg.D, cfg.I, cfg.E_local, cfg.K, cfg.I_shared, 'bf16')
+    W = m.make_weights(*(bf(a) for a in (H.w_gate, H.w_up, H.w_down, H.ws_gate, H.ws_up, H.ws_down)))
+    keep = [W]
+    dev = {k: bf(getattr(H, k)[:S] if k in ('x_slot', 'dy_slot') else getattr(H, k))
+           for k in ('x_slot', 'dy_slot', 'x_local', 'dy_local', 'w_gate', 'w_up', 'w_down', 'ws_gate', 'ws_up',
+                     'ws_down')}
+    W = m.make_weights(dev['w_gate'], dev['w_up'], dev['w_down'], dev['ws_gate'], dev['ws_up'], dev['ws_down'])
+    off_d = torch.from_numpy(offsets).cuda()
+    g_d = torch.from_numpy(H.g[:S].copy()).cuda()
+    y = torch.empty((S, cfg.D), dtype=torch.bfloat16, device='cuda')
+    sh = torch.empty((cfg.tokens, cfg.D), dtype=torch.bfloat16, device='cuda')
+    ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
+    E, I, D, Is = cfg.E_local, cfg.I, cfg.D, cfg.I_shared
+    dxs = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
+    dg = torch.empty((S,), dtype=torch.float32, device='cuda')
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    G = m.make_grads(**gr)
+    dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
+    wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.experts_backward(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
+                       dev['dy_local'], dxl, wsb)
+    torch.cuda.synchronize()
+    err = int(wsb[:4].view(torch.int32).item())
+    return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, err=err, **gr)
+
+
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242], [0, 0, 500]], ids=['empty_mid', 'ragged', 'one_hot'])
+def test_experts_forward_backward_small(m, counts):
+    print(f'[backward] share counts={counts}', flush=True)
+    H = synth.host_share(SMALL_SHARE)
+    S = int(sum(counts))
+    r = run_share(m, H, counts)
+    assert r['err'] == 0
+    c = np.array(counts)
+    y = oracle.experts_forward(H.x_slot[:S], c, H.w_gate, H.w_up, H.w_down)
+    assert_close_rms(t2np(r['y']), y, TAU, 'y_slot', True)
+    sh = oracle.swiglu_expert(H.x_local, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(r['sh']), sh, TAU, 'shared_out', True)
+    ref = oracle.experts_backward(H.x_slot[:S], c, H.g[:S], H.dy_slot[:S], H.w_gate, H.w_up, H.w_down)
+    assert_close_rms(t2np(r['dx_slot']), ref['dx_slot'], TAU, 'dx_slot', True)
+    assert_close_rms(t2np(r['dg']), ref['dg'], TAU, 'dg')
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        got = t2np(r[k.replace('dW', 'dw')])
+        assert_close_rms(got, ref[k], TAU, k)
+        for e in range(len(counts)):
+            if counts[e] == 0:
+                assert np.all(got[e] == 0), f'{k}[{e}] of an empty expert must be exact zeros'
+    rs = oracle.shared_backward(H.x_local, H.dy_local, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(r['dx_local']), rs['dx'], TAU, 'dx_local', True)
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(r[k.replace('dW', 'dws')]), rs[k], TAU, 'shared ' + k)
+
+
+def test_experts_backward_deterministic(m):
+    H = synth.host_share(SMALL_SHARE)
+    a = run_share(m, H, [300, 0, 157])
+    b = run_share(m, H, [300, 0, 157])
+    for k in ('dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_down', 'dx_local'):
+        assert torch.equal(a[k], b[k]), k
+
+
+LAYER_BWD = synth.scaled(synth.DSV3, 'layer_bwd_bf16_T300_D256_I256_E16_K4', T=300, D=256, I=256, E=16, K=4,
+                         I_shared=128)
+
+
+@pytest.mark.parametrize('cfg', [LAYER_BWD, synth.scaled(LAYER_BWD, 'layer_bwd_noshared', I_shared=0, T=130, K=2)],
+                         ids=lambda c: c.name)
+def test_layer_backward(m, cfg):
+    print(f'[backward] layer {cfg.name}', flush=True)
+    H = synth.host_layer(cfg)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L, want_parts=False)()
+    dout_h = synth.host_dout(cfg, cfg.T)
+    dout = bf(dout_h)
+    E, I, D, Is, T, K = cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.T, cfg.K
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'))
+    if Is:
+        gr.update(dws_gate=torch.empty((Is, D), device='cuda'), dws_up=torch.empty((Is, D), device='cuda'),
+                  dws_down=torch.empty((D, Is), device='cuda'))
+    G = m.make_grads(**gr)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+    m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, wsb)
+    torch.cuda.synchronize()
+    ref = oracle.moe_backward(H.x, H.logits, H.w_gate, H.w_up, H.w_down, K, dout_h, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(dx), ref['dx'], TAU, 'dx', True)
+    assert_close_rms(t2np(dtw), ref['dg'], TAU, 'd_topk_w')
+    assert_close_rms(t2np(dlg), ref['d_logits'], TAU, 'd_logits')
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(gr[k.replace('dW', 'dw')]), ref[k], TAU, k)
+    if Is:
+        for k in ('dWs_gate', 'dWs_up', 'dWs_down'):
+            assert_close_rms(t2np(gr[k.replace('dWs', 'dws')]), ref[k], TAU, k)
+    # off the selected experts d_logits is exactly zero
+    mask = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(mask, ref['idx'].astype(np.int64), True, axis=1)
+    assert np.all(t2np(dlg)[~mask] == 0)

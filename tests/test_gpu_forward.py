@@ -160,3 +160,24 @@ def test_forward_dsv3_full_size_sampled(m):
                                  L.ws_down.float().cpu().numpy())
     got = run.out[toks].float().cpu().numpy()
     assert_close_rms(got, out, TOL['bf16'], 'dsv3 sampled out', True)
+
+
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 3), (256, 4), (768, 5), (1 << 20, 3)])
+def test_pipeline_bitwise_equals_unchunked(m, chunk, stages):
+    """The chunked persistent pipeline (ring of `stages` chunks of `chunk` slots) gives bitwise the
+    same per-route rows, shared output and layer output as the unchunked path: every output tile
+    is one workgroup's fixed-order sum, whatever the chunking."""
+    print(f'[pipeline] chunk={chunk} stages={stages}', flush=True)
+    L = synth.to_device(synth.host_layer(SMALL_BF16))
+    a = ForwardRun(m, L)()
+    b = ForwardRun(m, L, chunk_rows=chunk, ring_stages=stages)()
+    torch.cuda.synchronize()
+    assert int(b.ws[:4].view(torch.int32).item()) == 0
+    assert torch.equal(a.y_routes, b.y_routes)
+    assert torch.equal(a.shared_out, b.shared_out)
+    assert torch.equal(a.out, b.out)
+
+
+def test_pipeline_mid_parity(m):
+    """Chunked pipeline at the mid shape (T=4096, E=128, K=8) against the oracle."""
+    check_forward(m, synth.MID, chunk_rows=512)

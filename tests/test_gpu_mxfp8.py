@@ -1,0 +1,185 @@
+"""GPU parity of the MXFP8 path: the quantiser and the quantising dispatch bit-exact against the
+oracle's OCP MX encoder, and the MXFP8 forward against the oracle run on the same quantised
+values in fp64 (h quantised before the down projection; shared expert in BF16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import TOL, assert_close_rms, mx_choice_allowance, t2np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope='module')
+def m():
+    import mixture_experts_layer_norm_amd as mod
+    return mod
+
+
+def bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+def u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+@pytest.mark.parametrize('rows,cols', [(1, 32), (37, 256), (512, 7168)])
+def test_quantize_mx_bit_exact(m, rows, cols):
+    rng = np.random.default_rng(rows)
+    v = rng.standard_normal((rows, cols)).astype(np.float32) * np.exp(rng.standard_normal((rows, 1)) * 6).astype(np.float32)
+    v[0, :32] = 0.0                                      # an all-zero block
+    if cols >= 64:
+        v[0, 32:64] = 1.0                                # amax an exact power of two
+        v[0, 40] = 1.96875                               # saturates to 448
+    if rows > 1:
+        v[1, :] *= 1e-38                                 # tiny (bf16 subnormal range)
+    v = synth.round_bf16(v)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device='cuda')
+    sc = torch.empty((rows, cols // 32), dtype=torch.uint8, device='cuda')
+    m.quantize_mx(bf(v), q, sc)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(v.astype(np.float64))
+    assert np.array_equal(sc.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+MX_SMALL = synth.scaled(synth.MXFP8, 'small_mxfp8_T300_D256_I256_E16_K4', T=300, D=256, I=256, E=16, K=4,
+                        I_shared=256)
+
+
+def mx_layer(cfg):
+    H = synth.host_layer(cfg)
+    q = {k: oracle.mx_quantize(getattr(H, k).astype(np.float64)) for k in ('w_gate', 'w_up', 'w_down')}
+    return H, q
+
+
+def run_mx_forward(m, H, q):
+    cfg = H.cfg
+    T, K, D, E = cfg.T, cfg.K, cfg.D, cfg.E
+    p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8')
+    tensors = dict(x=bf(H.x), logits=torch.from_numpy(H.logits).cuda(),
+                   wq=[u8(q[k][0]) for k in ('w_gate', 'w_up', 'w_down')],
+                   ws=[bf(H.ws_gate), bf(H.ws_up), bf(H.ws_down)],
+                   sc=[u8(q[k][1]) for k in ('w_gate', 'w_up', 'w_down')])
+    W = m.make_weights(*tensors['wq'], *tensors['ws'], *tensors['sc'])
+    rt = [torch.empty((T, K), dtype=torch.int32, device='cuda'), torch.empty((T, K), dtype=torch.float32, device='cuda'),
+          torch.empty((E,), dtype=torch.int32, device='cuda'), torch.empty((E + 1,), dtype=torch.int32, device='cuda'),
+          torch.empty((T * K,), dtype=torch.int32, device='cuda'), torch.empty((T * K,), dtype=torch.int32, device='cuda')]
+    out = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    yr = torch.empty((T * K, D), dtype=torch.bfloat16, device='cuda')
+    ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.forward(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, y_routes=yr)
+    torch.cuda.synchronize()
+    return out, yr, rt, p, tensors
+
+
+def oracle_mx_forward(x, logits, deq, K, ws_gate, ws_up, ws_down):
+    """Routed experts on MX-dequantised x and weights with h quantised along I; shared in BF16.
+
+    Also returns the per-element allowance for equally correct alternative h decisions (see
+    gpu_util.mx_choice_allowance), propagated through |W_down| to y and through g to out."""
+    x = np.asarray(x, dtype=np.float64)
+    E = np.asarray(logits).shape[1]
+    get = lambda w, e: w(e) if callable(w) else w[e]
+    xq = oracle.mx_roundtrip(x)
+    idx = oracle.route_topk(logits, K)
+    g = oracle.routing_weights(logits, idx)
+    T, D = x.shape
+    y = np.zeros((T, K, D))
+    ya = np.zeros((T, K, D))
+    for e in range(E):
+        t, k = np.nonzero(idx == e)
+        if t.size == 0:
+            continue
+        Xe = xq[t]
+        A = Xe @ np.asarray(get(deq['w_gate'], e)).T
+        U = Xe @ np.asarray(get(deq['w_up'], e)).T
+        Hm = oracle.silu(A) * U
+        Wd = np.asarray(get(deq['w_down'], e))
+        y[t, k] = oracle.mx_roundtrip(Hm) @ Wd.T
+        ya[t, k] = mx_choice_allowance(Hm) @ np.abs(Wd).T
+    sh = oracle.swiglu_expert(x, ws_gate, ws_up, ws_down)
+    out = np.einsum('tk,tkd->td', g, y) + sh
+    out_allow = np.einsum('tk,tkd->td', g, ya)
+    return out, idx, y, ya, out_allow
+
+
+def test_mx_dispatch_bit_exact(m):
+    cfg = MX_SMALL
+    H = synth.host_layer(cfg)
+    idx = oracle.route_topk(H.logits, cfg.K)
+    _, _, perm, _ = oracle.schedule(idx, cfg.E)
+    n = cfg.T * cfg.K
+    p = m.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, 'mxfp8')
+    xq = torch.empty((n, cfg.D), dtype=torch.uint8, device='cuda')
+    xs = torch.empty((n, cfg.D // 32), dtype=torch.uint8, device='cuda')
+    m.dispatch(p, bf(H.x), torch.from_numpy(perm).cuda(), 0, n, xq, xs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(H.x[perm // cfg.K].astype(np.float64))
+    assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
+
+
+def test_mx_forward_small(m):
+    H, q = mx_layer(MX_SMALL)
+    out, yr, rt, *_ = run_mx_forward(m, H, q)
+    deq = {k: oracle.mx_dequantize(*q[k]) for k in q}
+    ref, idx, y, ya, oa = oracle_mx_forward(H.x, H.logits, deq, MX_SMALL.K, H.ws_gate, H.ws_up, H.ws_down)
+    assert np.array_equal(rt[0].cpu().numpy(), idx)
+    D = MX_SMALL.D
+    assert_close_rms(t2np(out), ref, TOL['mxfp8'], 'mx out', True, oa)
+    assert_close_rms(t2np(yr), y.reshape(-1, D), TOL['mxfp8'], 'mx y_routes', True, ya.reshape(-1, D))
+
+
+def test_mx_forward_deterministic(m):
+    H, q = mx_layer(MX_SMALL)
+    a, *_ = run_mx_forward(m, H, q)
+    b, *_ = run_mx_forward(m, H, q)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_mx_forward_full_size_sampled(m):
+    """MXFP8 at T=32768, D=7168, I=2048, E=256, K=8 (Zipf expert popularity): weights quantised on
+    the device, 3 sampled tokens checked against the oracle on its own quantisation of the same
+    weights (the device quantiser is checked bit-exact on those experts first)."""
+    cfg = synth.MXFP8
+    print('[mxfp8] generating full-size inputs', flush=True)
+    L = synth.device_layer(cfg)
+    E, I, D, T, K = cfg.E, cfg.I, cfg.D, cfg.T, cfg.K
+    wq = {k: torch.empty(getattr(L, k).shape, dtype=torch.uint8, device='cuda') for k in ('w_gate', 'w_up', 'w_down')}
+    ws = {k: torch.empty(getattr(L, k).shape[:-1] + (getattr(L, k).shape[-1] // 32,), dtype=torch.uint8, device='cuda')
+          for k in ('w_gate', 'w_up', 'w_down')}
+    for k in wq:
+        m.quantize_mx(getattr(L, k), wq[k], ws[k])
+    p = m.problem(T, D, I, E, K, cfg.I_shared, 'mxfp8')
+    W = m.make_weights(wq['w_gate'], wq['w_up'], wq['w_down'], L.ws_gate, L.ws_up, L.ws_down,
+                       ws['w_gate'], ws['w_up'], ws['w_down'])
+    rt = [torch.empty((T, K), dtype=torch.int32, device='cuda'), torch.empty((T, K), dtype=torch.float32, device='cuda'),
+          torch.empty((E,), dtype=torch.int32, device='cuda'), torch.empty((E + 1,), dtype=torch.int32, device='cuda'),
+          torch.empty((T * K,), dtype=torch.int32, device='cuda'), torch.empty((T * K,), dtype=torch.int32, device='cuda')]
+    out = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    wsp = torch.empty((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.forward(p, L.x, L.logits, W, out, m.make_routing(*rt), wsp)
+    torch.cuda.synchronize()
+    lg = L.logits.cpu().numpy()
+    idx = oracle.route_topk(lg, K)
+    assert np.array_equal(rt[0].cpu().numpy(), idx)
+    toks = np.sort(np.random.default_rng(1).choice(T, 3, replace=False))
+    used = sorted(set(idx[toks].ravel().tolist()))
+    print(f'[mxfp8] oracle on {len(toks)} tokens, {len(used)} experts', flush=True)
+    deq = {}
+    for k in ('w_gate', 'w_up', 'w_down'):
+        deq[k] = {}
+        for e in used:
+            rq, rs = oracle.mx_quantize(getattr(L, k)[e].float().cpu().numpy().astype(np.float64))
+            assert np.array_equal(wq[k][e].cpu().numpy(), rq) and np.array_equal(ws[k][e].cpu().numpy(), rs)
+            deq[k][e] = oracle.mx_dequantize(rq, rs)
+    x = L.x[torch.from_numpy(toks).cuda()].float().cpu().numpy().astype(np.float64)
+    ref, _, _, _, oa = oracle_mx_forward(x, lg[toks], {k: (lambda e, k=k: deq[k][e]) for k in deq}, K,
+                                         L.ws_gate.float().cpu().numpy(), L.ws_up.float().cpu().numpy(),
+                                         L.ws_down.float().cpu().numpy())
+    assert_close_rms(out[torch.from_numpy(toks).cuda()].float().cpu().numpy(), ref, TOL['mxfp8'],
+                     'mx full sampled', True, oa)
