@@ -60,7 +60,9 @@ def main():
     ap.add_argument('--chunk-rows', type=int, default=0)
     ap.add_argument('--flags', type=int, default=0)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--cpu-tokens', type=int, default=8, help='tokens in the CPU oracle sample')
+    ap.add_argument('--cpu-tokens', type=int, default=96, help='tokens in the CPU oracle sample')
+    ap.add_argument('--calib-copy', action='store_true',
+                    help='run one 1 GiB device-to-device copy before the timed region (HBM counter calibration)')
     args = ap.parse_args()
     if args.gpus != 1:
         print(f'bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU '
@@ -98,6 +100,12 @@ def main():
         else:
             moe.forward_stages(p, L.x, L.logits, weights, out, routing, ws, events, stream=stream)
 
+    if args.calib_copy:
+        src = torch.empty((1 << 29,), dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f'[bench] warmup {args.warmup}', file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -66,7 +66,9 @@ typedef enum moe_dtype {
  * chunk_rows (b): rows of the expert-contiguous routed buffer that one pipeline step carries
  *   through the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel for
  *   NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
- *   values are clamped to [256, T*K] and rounded up to a multiple of 256.
+ *   values are rounded up to a multiple of 256 and clamped to [max(256, T*K/1024), T*K]. With
+ *   chunks, dispatched rows and h live in a ring of ring_stages chunk stages (BF16 path; the
+ *   MXFP8 and FUSED_GATHER paths ignore chunk_rows).
  * ring_stages: macrobatch ring depth (Notes, section "A ring buffer instead of a host
  *   round-trip"); 0 selects 3. Ignored when one chunk holds every row.
  * flags: bitwise OR of MOE_FLAG_* below. */
@@ -80,6 +82,12 @@ typedef struct moe_problem {
 
 /* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
 #define MOE_FLAG_FUSED_GATHER 0x1
+/* Tuning: order the grouped GEMM tiles of an expert n-tile major (its m-tiles that share a
+ * weight tile run together) instead of m-tile major. Results are bitwise identical. */
+#define MOE_FLAG_WEIGHT_MAJOR 0x2
+/* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
+ * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
+#define MOE_FLAG_PERSISTENT 0x4
 
 /* Expert weights (device pointers). Routed: w_gate, w_up [E][I][D]; w_down [E][D][I].
  * Shared: ws_gate, ws_up [I_shared][D]; ws_down [D][I_shared] (always bf16 under MOE_MXFP8).

@@ -75,6 +75,7 @@ WsLayout ws_layout(const moe_problem& p) {
   L.pipe_ctile = o; o = align256(o + (L.pipelined ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
   L.pipe_base = o; o = align256(o + (L.pipelined ? (size_t)(L.chunks + 1) * 4 : 0));
   L.pipe_ctr = o; o = align256(o + (L.pipelined ? (size_t)(2 + 3 * L.chunks) * 4 : 0));
+  L.pipe_crow = o; o = align256(o + (L.pipelined ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
   L.bwd = o;
   L.total = o;
   return L;
@@ -201,6 +202,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
   const bool mx = p->dtype == MOE_MXFP8;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
+  if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (y_routes && !aligned16(y_routes)) ||
@@ -222,7 +224,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
 
   // shared expert first: it does not depend on the schedule
   MOE_MARK(MOE_STAGE_SHARED);
-  if (p->I_shared > 0 && !L.pipelined) {
+  if (p->I_shared > 0) {
     Grouped gs;
     gs.M = p->T;
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
@@ -235,38 +237,35 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   gr.tile_off = (const int32_t*)(wsb + L.tile_off);
   gr.groups = p->E;
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
+  gr.weight_major = (p->flags & MOE_FLAG_WEIGHT_MAJOR) ? 1 : 0;
   if (L.pipelined) {
-    // shared expert, dispatch into the ring, up/gate and down per chunk: one persistent kernel
+    // Chunks of b routed slots through a ring of S stages, each carried through dispatch, up/gate
+    // and down before the next; all tile bookkeeping is on the device (no host synchronisation).
     const int64_t b = L.chunk;
-    PipeArgs pa{};
-    pa.T = p->T; pa.D = p->D; pa.I = p->I; pa.E = p->E; pa.K = p->K; pa.Is = p->I_shared;
-    pa.n = (int)n; pa.b = (int)b; pa.C = L.chunks; pa.S = L.stages;
-    pa.ntn1 = p->I / gemm_tile_cols(EPI_SWIGLU);
-    pa.ntn2 = (p->D + gemm_tile_cols(EPI_STORE) - 1) / gemm_tile_cols(EPI_STORE);
-    pa.ntn_s1 = p->I_shared / gemm_tile_cols(EPI_SWIGLU);
-    pa.ntn_s2 = pa.ntn2;
-    pa.sh_mt = (p->T + kGemmBM - 1) / kGemmBM;
-    pa.n_sh1 = p->I_shared > 0 ? pa.sh_mt * pa.ntn_s1 : 0;
-    pa.n_sh2 = p->I_shared > 0 ? pa.sh_mt * pa.ntn_s2 : 0;
-    pa.d_pre = 0;
-    for (int c = 0; c < L.stages && c < L.chunks; ++c) {
-      const int64_t rows = (n - c * b) < b ? (n - c * b) : b;
-      pa.d_pre += (int)((rows + kGemmBM - 1) / kGemmBM);
-    }
-    pa.x = (const uint16_t*)x; pa.perm = r->perm; pa.offsets = r->offsets;
-    pa.wg = (const uint16_t*)w->w_gate; pa.wu = (const uint16_t*)w->w_up; pa.wd = (const uint16_t*)w->w_down;
-    pa.sg = (const uint16_t*)w->ws_gate; pa.su = (const uint16_t*)w->ws_up; pa.sd = (const uint16_t*)w->ws_down;
-    pa.x_ring = (uint16_t*)(wsb + L.x_slot); pa.h_ring = (uint16_t*)(wsb + L.h); pa.y = (uint16_t*)yr;
-    pa.sh_h = (uint16_t*)(wsb + L.sh_h); pa.sh_out = (uint16_t*)sho;
-    pa.ctile = (const int32_t*)(wsb + L.pipe_ctile); pa.chunk_base = (const int32_t*)(wsb + L.pipe_base);
-    pa.ctr = (int32_t*)(wsb + L.pipe_ctr); pa.err = (int32_t*)(wsb + L.err);
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-      return MOE_ERR_HIP;
-    st = launch_pipeline(pa, (int32_t*)(wsb + L.pipe_base), ncu, stream);
+    const int C = L.chunks, S = L.stages;
+    int32_t* ctile = (int32_t*)(wsb + L.pipe_ctile);
+    int32_t* crow = (int32_t*)(wsb + L.pipe_crow);
+    st = launch_chunk_tables(r->offsets, p->E, (int)n, (int)b, C, ctile, crow, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_DISPATCH);
+    uint16_t* xr = (uint16_t*)(wsb + L.x_slot);
+    uint16_t* hr = (uint16_t*)(wsb + L.h);
+    for (int c = 0; c < C; ++c) {
+      const int64_t c0 = c * b, rows = (n - c0) < b ? (n - c0) : b;
+      const int64_t shift = (int64_t)(c % S) * b - c0;            // slot index -> ring row
+      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + (int64_t)(c % S) * b * p->D, nullptr,
+                           stream);
+      if (st) return st;
+      Grouped gc;
+      gc.row_off = crow + (int64_t)c * (p->E + 1);
+      gc.tile_off = ctile + (int64_t)c * (p->E + 1);
+      gc.groups = p->E;
+      gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
+      gc.weight_major = (p->flags & MOE_FLAG_WEIGHT_MAJOR) ? 1 : 0;
+      st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
+                      p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream);
+      if (st) return st;
+    }
     MOE_MARK(MOE_STAGE_UP_GATE);
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_MARK(MOE_STAGE_COMBINE);

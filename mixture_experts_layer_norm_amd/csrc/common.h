@@ -57,6 +57,7 @@ struct WsLayout {
   size_t pipe_ctile;       // [C][E+1] int32 (chunked pipeline)
   size_t pipe_base;        // [C+1] int32
   size_t pipe_ctr;         // [2 + 3C] int32
+  size_t pipe_crow;        // [C][E+1] int32 (chunk row ranges, multi-launch path)
   int64_t nblk;            // histogram blocks
   int64_t ring_rows;       // rows of x_slot / h held (chunk * stages, or T*K)
   int64_t chunk;           // rows per chunk
@@ -109,6 +110,7 @@ struct Grouped {
   int32_t groups = 1;
   int32_t M = 0;              // rows when row_off == nullptr
   int64_t max_mtiles = 0;     // host bound on the number of m-tiles (grid size)
+  int32_t weight_major = 0;   // tile order inside a group: 0 = m-tile major, 1 = n-tile major
 };
 
 // EPI_SWIGLU:   h = SiLU(gate) * up                       -> C
@@ -154,6 +156,8 @@ int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s);
 int gemm_tile_cols(Epi epi);
 struct PipeArgs;
 int launch_pipeline(const PipeArgs& host, int32_t* chunk_base_dev, int ncu, hipStream_t s);
+int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,
+                        hipStream_t s);
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
                    int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);

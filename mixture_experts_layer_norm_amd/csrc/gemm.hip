@@ -46,6 +46,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g
     tc.rows = min(BM, a.M - tc.r0);
     k0 = a.k_off[tc.grp];
     nk = (a.k_off[tc.grp + 1] - k0) / BK;
+  } else if (g.weight_major && g.row_off) {
+    // inside each group: n-tile major, m-tile minor, so the m-tiles that share one weight tile
+    // run side by side and read it from HBM once
+    const int q = logical / ntn;
+    if (q >= g.tile_off[g.groups]) return;
+    int lo = 0, hi = g.groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    const int nmt = g.tile_off[lo + 1] - g.tile_off[lo];
+    const int rem = logical - g.tile_off[lo] * ntn;
+    tc.nt = rem / nmt;
+    tc.grp = lo;
+    tc.r0 = g.row_off[lo] + (rem % nmt) * BM;
+    tc.rows = min(BM, g.row_off[lo + 1] - tc.r0);
+    nk = a.K / BK;
   } else {
     tc.nt = logical % ntn;
     if (!locate_tile(g, logical / ntn, tc)) return;

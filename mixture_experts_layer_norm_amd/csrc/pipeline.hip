@@ -15,7 +15,8 @@
 //   after down(0).
 // An item waits only for items earlier in the sequence (through per-chunk counters with
 // agent-scope release/acquire), so the kernel cannot deadlock even when fewer workgroups are
-// resident than launched; every wait is bounded and sets the sticky error word on expiry.
+// resident than launched; every wait is bounded, sets the sticky error word (bit 4) on expiry,
+// and once that bit is set every other wait returns at once, so the kernel always drains.
 // Each output tile is computed by one workgroup with a fixed summation order, so results are
 // bitwise identical for every chunk size, ring depth and workgroup count.
 #include "gemm_tile.h"
@@ -30,16 +31,25 @@ __device__ __forceinline__ int nd_of(const PipeArgs& p, int c) {
   return (rows + kGemmBM - 1) / kGemmBM;
 }
 
+// Wait until *ctr >= target. Thread 0 polls with relaxed agent-scope loads (an acquire load
+// would invalidate the L2 on every poll and starve the workgroups doing the work), then one
+// acquire fence publishes the producers' data to the whole workgroup. The poll is bounded
+// (about a second); on expiry, or when another wait already expired (bit 4 of the error word),
+// it gives up so that the kernel always drains.
 __device__ __forceinline__ void wait_geq(int32_t* ctr, int target, int32_t* err) {
   if (threadIdx.x == 0) {
     int spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(8);
-      if (++spins > (1 << 26)) {   // seconds: a missing signal is reported instead of hanging
-        atomicOr(err, 4);
-        break;
+      if ((++spins & 255) == 0) {
+        if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 4) break;
+        if (spins > (1 << 20)) {
+          atomicOr(err, 4);
+          break;
+        }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void pipeline_kernel(PipeArgs p) {
 
 // per chunk: m-tiles of every expert's part of the chunk, prefix over experts (one block per chunk)
 __global__ __launch_bounds__(1024) void chunk_tiles_kernel(const int32_t* __restrict__ offsets, int E, int n, int b,
-                                                           int32_t* __restrict__ ctile) {
+                                                           int32_t* __restrict__ ctile, int32_t* __restrict__ crow) {
   __shared__ int sb[1024];
   const int c = blockIdx.x, e = threadIdx.x;
   const int c0 = c * b, c1 = min(n, c0 + b);
@@ -197,6 +207,11 @@ __global__ __launch_bounds__(1024) void chunk_tiles_kernel(const int32_t* __rest
   int32_t* row = ctile + (int64_t)c * (E + 1);
   if (e < E) row[e + 1] = sb[e];
   if (e == 0) row[0] = 0;
+  if (crow) {   // each expert's row range clamped to the chunk (row offsets of the chunk's groups)
+    int32_t* ro = crow + (int64_t)c * (E + 1);
+    if (e < E) ro[e + 1] = min(max(offsets[e + 1], c0), c1);
+    if (e == 0) ro[0] = c0;
+  }
 }
 
 // item blocks of the chunks (prefix over chunks) and zeroed counters (one block)
@@ -224,11 +239,20 @@ __global__ __launch_bounds__(1024) void chunk_base_kernel(PipeArgs p, int32_t* _
 
 int launch_pipeline(const PipeArgs& host, int32_t* chunk_base_dev, int ncu, hipStream_t s) {
   hipLaunchKernelGGL(chunk_tiles_kernel, dim3(host.C), dim3(1024), 0, s, host.offsets, host.E, host.n, host.b,
-                     (int32_t*)host.ctile);
+                     (int32_t*)host.ctile, nullptr);
   MOE_LAUNCH_CHECK();
   hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, host, chunk_base_dev);
   MOE_LAUNCH_CHECK();
   hipLaunchKernelGGL(pipeline_kernel, dim3(ncu), dim3(512), 0, s, host);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+// Chunk tables for the multi-launch chunked path: per chunk, the m-tile prefix over experts
+// (ctile [C][E+1]) and the experts' row ranges clamped to the chunk (crow [C][E+1]).
+int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(chunk_tiles_kernel, dim3(C), dim3(1024), 0, s, offsets, E, n, b, ctile, crow);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -81,3 +81,11 @@ def test_entry_points_reject_null_and_small_workspace_without_gpu():
     w = m.Weights()
     r = m.Routing()
     assert lib.moe_forward(P, 16, 16, ctypes.byref(w), 16, ctypes.byref(r), None, None, None, 0, None) == -1
+    # the persistent chunk kernel is switched off: the flag is refused before any launch
+    pp = m.problem(16, 128, 128, 8, 2, 0, 'bf16', 256, 3, m.MOE_FLAG_PERSISTENT)
+    for f in ('w_gate', 'w_up', 'w_down'):
+        setattr(w, f, 256)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, 256)
+    assert lib.moe_forward(ctypes.byref(pp), 256, 256, ctypes.byref(w), 256, ctypes.byref(r), None, None, 256,
+                           1 << 40, None) == -2

@@ -162,15 +162,11 @@ def test_forward_dsv3_full_size_sampled(m):
     assert_close_rms(got, out, TOL['bf16'], 'dsv3 sampled out', True)
 
 
-@pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 3), (256, 4), (768, 5), (1 << 20, 3)])
-def test_pipeline_bitwise_equals_unchunked(m, chunk, stages):
-    """The chunked persistent pipeline (ring of `stages` chunks of `chunk` slots) gives bitwise the
-    same per-route rows, shared output and layer output as the unchunked path: every output tile
-    is one workgroup's fixed-order sum, whatever the chunking."""
-    print(f'[pipeline] chunk={chunk} stages={stages}', flush=True)
+def chunked_equals_unchunked(m, chunk, stages, flags=0):
+    print(f'[chunked] chunk={chunk} stages={stages} flags={flags}', flush=True)
     L = synth.to_device(synth.host_layer(SMALL_BF16))
     a = ForwardRun(m, L)()
-    b = ForwardRun(m, L, chunk_rows=chunk, ring_stages=stages)()
+    b = ForwardRun(m, L, chunk_rows=chunk, ring_stages=stages, flags=flags)()
     torch.cuda.synchronize()
     assert int(b.ws[:4].view(torch.int32).item()) == 0
     assert torch.equal(a.y_routes, b.y_routes)
@@ -178,6 +174,31 @@ def test_pipeline_bitwise_equals_unchunked(m, chunk, stages):
     assert torch.equal(a.out, b.out)
 
 
-def test_pipeline_mid_parity(m):
-    """Chunked pipeline at the mid shape (T=4096, E=128, K=8) against the oracle."""
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 3), (256, 4), (768, 5), (1 << 20, 3)])
+def test_chunked_ring_bitwise_equals_unchunked(m, chunk, stages):
+    """Chunks of `chunk` routed slots carried through a ring of `stages` chunk buffers give bitwise
+    the same per-route rows, shared output and layer output as the unchunked path: every output
+    tile is one workgroup's fixed-order sum, whatever the chunking."""
+    chunked_equals_unchunked(m, chunk, stages)
+
+
+@pytest.mark.skip(reason='the persistent work-queue chunk kernel hung on MI355X twice (second time after '
+                         'bounding its waits); its cause is not yet shown, so the path is switched off and '
+                         'MOE_FLAG_PERSISTENT returns MOE_ERR_UNSUPPORTED')
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (768, 5)])
+def test_persistent_pipeline_bitwise_equals_unchunked(m, chunk, stages):
+    chunked_equals_unchunked(m, chunk, stages, flags=m.MOE_FLAG_PERSISTENT)
+
+
+def test_chunked_ring_mid_parity(m):
+    """Chunked ring at the mid shape (T=4096, E=128, K=8) against the oracle."""
     check_forward(m, synth.MID, chunk_rows=512)
+
+
+def test_weight_major_tile_order_bitwise(m):
+    """The n-tile-major tile order inside an expert changes only the schedule, not the bits."""
+    L = synth.to_device(synth.host_layer(synth.scaled(SMALL_BF16, 'skewed_small', T=700)))
+    a = ForwardRun(m, L)()
+    b = ForwardRun(m, L, flags=m.MOE_FLAG_WEIGHT_MAJOR)()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, b.out) and torch.equal(a.y_routes, b.y_routes)
