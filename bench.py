@@ -104,6 +104,7 @@ def main():
         src = torch.empty((1 << 29,), dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        torch.neg(src, out=dst)          # an elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
     print(f'[bench] warmup {args.warmup}', file=sys.stderr, flush=True)

@@ -85,6 +85,9 @@ typedef struct moe_problem {
 /* Tuning: order the grouped GEMM tiles of an expert n-tile major (its m-tiles that share a
  * weight tile run together) instead of m-tile major. Results are bitwise identical. */
 #define MOE_FLAG_WEIGHT_MAJOR 0x2
+/* Tile order of the grouped GEMMs: inside each expert, blocks of n n-tiles (1..255), each block
+ * m-tile major (MOE_FLAG_WEIGHT_MAJOR is n = 1). Affects only speed, never the results. */
+#define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
 #define MOE_FLAG_PERSISTENT 0x4

@@ -23,6 +23,11 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_FLAG_FUSED_GATHER = 0x1
 MOE_FLAG_WEIGHT_MAJOR = 0x2
 MOE_FLAG_PERSISTENT = 0x4
+
+
+def MOE_FLAG_TILE_BLOCK(n):
+    """Grouped GEMM tile order: blocks of n n-tiles per expert (speed only)."""
+    return (int(n) & 0xff) << 8
 STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3: 'MOE_ERR_WORKSPACE',
           -4: 'MOE_ERR_MISALIGNED', -5: 'MOE_ERR_HIP'}
 DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}

@@ -83,6 +83,12 @@ WsLayout ws_layout(const moe_problem& p) {
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
+int tile_block_of(uint32_t flags) {
+  if (flags & MOE_FLAG_WEIGHT_MAJOR) return 1;
+  const int nb = (int)((flags >> 8) & 0xff);
+  return nb ? nb : kDefaultTileBlock;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -227,6 +233,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   if (p->I_shared > 0) {
     Grouped gs;
     gs.M = p->T;
+    gs.nblk = tile_block_of(p->flags);
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
                     0, 0, wsb + L.sh_h, sho, nullptr, stream);
     if (st) return st;
@@ -237,7 +244,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   gr.tile_off = (const int32_t*)(wsb + L.tile_off);
   gr.groups = p->E;
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
-  gr.weight_major = (p->flags & MOE_FLAG_WEIGHT_MAJOR) ? 1 : 0;
+  gr.nblk = tile_block_of(p->flags);
   if (L.pipelined) {
     // Chunks of b routed slots through a ring of S stages, each carried through dispatch, up/gate
     // and down before the next; all tile bookkeeping is on the device (no host synchronisation).
@@ -261,7 +268,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
       gc.tile_off = ctile + (int64_t)c * (p->E + 1);
       gc.groups = p->E;
       gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
-      gc.weight_major = (p->flags & MOE_FLAG_WEIGHT_MAJOR) ? 1 : 0;
+      gc.nblk = tile_block_of(p->flags);
       st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
                       p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream);
       if (st) return st;

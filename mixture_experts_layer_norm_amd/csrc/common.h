@@ -68,6 +68,10 @@ struct WsLayout {
 
 size_t elt_bytes(int dtype);
 WsLayout ws_layout(const moe_problem& p);
+// n-tiles per block of the grouped tile order selected by moe_problem::flags (0: m-tile major)
+constexpr int kDefaultTileBlock = 0;
+int tile_block_of(uint32_t flags);
+
 int validate_problem(const moe_problem* p);
 int validate_routing(const moe_problem* p);
 
@@ -110,7 +114,9 @@ struct Grouped {
   int32_t groups = 1;
   int32_t M = 0;              // rows when row_off == nullptr
   int64_t max_mtiles = 0;     // host bound on the number of m-tiles (grid size)
-  int32_t weight_major = 0;   // tile order inside a group: 0 = m-tile major, 1 = n-tile major
+  // Tile order inside a group: blocks of nblk n-tiles; inside a block m-tile major. nblk >= the
+  // n-tile count is plain m-tile major, nblk = 1 n-tile major (0 means m-tile major too).
+  int32_t nblk = 0;
 };
 
 // EPI_SWIGLU:   h = SiLU(gate) * up                       -> C

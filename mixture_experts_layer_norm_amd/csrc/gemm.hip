@@ -19,7 +19,9 @@
 //
 // Workgroup -> tile mapping: tiles are numbered (m-tile major, n-tile minor) and dealt out so
 // that each XCD (workgroups are placed round-robin over the 8 XCDs) gets a contiguous range,
-// which keeps an expert's activation rows and weight tiles in that XCD's L2.
+// which keeps an expert's activation rows and weight tiles in that XCD's L2. The split is over
+// the tiles that exist (read on the device), not over the launched upper bound, so that every
+// XCD gets an equal share even when the routing leaves most of the bound empty.
 #include "gemm_tile.h"
 
 namespace moe {
@@ -31,9 +33,14 @@ namespace moe {
 template <int EPI, bool KG, int WN>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g, int ntn, int mtn) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems];
-  const int nb = gridDim.x;
+  // The grid is an upper bound (grouped tile counts are known only on the device); the valid
+  // tiles are split evenly over the 8 XCDs, each taking a contiguous range of them.
+  const int valid = (KG ? g.groups * mtn : (g.row_off ? g.tile_off[g.groups] : mtn)) * ntn;
+  const int per_xcd = (valid + 7) >> 3;
   const int bid = blockIdx.x;
-  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if ((bid >> 3) >= per_xcd) return;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= valid) return;
   TileCoord tc;
   int k0 = 0, nk;
   if (KG) {
@@ -46,26 +53,35 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g
     tc.rows = min(BM, a.M - tc.r0);
     k0 = a.k_off[tc.grp];
     nk = (a.k_off[tc.grp + 1] - k0) / BK;
-  } else if (g.weight_major && g.row_off) {
-    // inside each group: n-tile major, m-tile minor, so the m-tiles that share one weight tile
-    // run side by side and read it from HBM once
-    const int q = logical / ntn;
-    if (q >= g.tile_off[g.groups]) return;
-    int lo = 0, hi = g.groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    const int nmt = g.tile_off[lo + 1] - g.tile_off[lo];
-    const int rem = logical - g.tile_off[lo] * ntn;
-    tc.nt = rem / nmt;
-    tc.grp = lo;
-    tc.r0 = g.row_off[lo] + (rem % nmt) * BM;
-    tc.rows = min(BM, g.row_off[lo + 1] - tc.r0);
-    nk = a.K / BK;
   } else {
-    tc.nt = logical % ntn;
-    if (!locate_tile(g, logical / ntn, tc)) return;
+    // The tiles of a group occupy logical [tile_off[grp] * ntn, tile_off[grp + 1] * ntn) (dense
+    // mode: one group of mtn m-tiles). Inside a group they run in blocks of nblk n-tiles, each
+    // block m-tile major, so that the tiles running side by side on one XCD share both their
+    // activation rows and their weight rows in L2.
+    int grp = 0, t0 = 0, nmt = mtn;
+    if (g.row_off) {
+      const int q = logical / ntn;
+      int lo = 0, hi = g.groups - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
+      }
+      grp = lo;
+      t0 = g.tile_off[lo];
+      nmt = g.tile_off[lo + 1] - t0;
+    }
+    const int rem = logical - t0 * ntn;
+    const int nbw = (g.nblk > 0 && g.nblk < ntn) ? g.nblk : ntn;
+    const int blk = rem / (nmt * nbw);
+    const int w = min(nbw, ntn - blk * nbw);
+    const int r2 = rem - blk * nmt * nbw;
+    tc.grp = grp;
+    tc.nt = blk * nbw + r2 % w;
+    const int mt = r2 / w;
+    const int rbase = g.row_off ? g.row_off[grp] : 0;
+    const int rend = g.row_off ? g.row_off[grp + 1] : g.M;
+    tc.r0 = rbase + mt * BM;
+    tc.rows = min(BM, rend - tc.r0);
     nk = a.K / BK;
   }
 
@@ -91,12 +107,13 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
   const int64_t nb = grid_blocks(mt, ntn);
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  const int mtn = g.row_off ? 0 : (int)mt;   // dense mode: the exact m-tile count
   dim3 grid((unsigned)nb), block(512);
   switch (epi) {
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN>), grid, block, 0, s, a, g, ntn, 0); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN>), grid, block, 0, s, a, g, ntn, 0); break;
-    case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN>), grid, block, 0, s, a, g, ntn, 0); break;
-    case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN>), grid, block, 0, s, a, g, ntn, 0); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN>), grid, block, 0, s, a, g, ntn, mtn); break;
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

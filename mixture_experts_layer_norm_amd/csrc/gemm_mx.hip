@@ -71,9 +71,13 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   constexpr int RPP = 512 / 8;
   constexpr int AL = BM / RPP, BL = BN / RPP;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_T + B_T)];
-  const int nb = gridDim.x;
+  // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
+  const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
+  const int per_xcd = (valid + 7) >> 3;
   const int bid = blockIdx.x;
-  const int logical = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if ((bid >> 3) >= per_xcd) return;
+  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (logical >= valid) return;
   const int nt = logical % ntn;
   int grp, r0, rows;
   if (!locate_tile_mx(g, logical / ntn, grp, r0, rows)) return;

@@ -1,18 +1,28 @@
 // One workgroup tile of the grouped GEMMs (shared by the standalone kernels and the persistent
 // pipeline). See gemm.hip for the tiling.
+//
+// Operand staging: global_load_lds_dwordx4 copies 16 bytes per lane from HBM straight into LDS
+// (no register staging, no LDS store instructions). One such instruction of a wavefront fills
+// 1 KB of LDS in lane order, i.e. 16 rows of one 32-wide K slice (64 B per row). LDS holds
+// STAGES such slices of the 256 A rows and 256 B rows; loads run STAGES - 1 slices ahead of the
+// MFMAs. Within a row the four 16-byte chunks are stored XOR-swizzled (chunk c of row r at
+// position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3), which makes the fragment reads of 8 or
+// 16 consecutive rows hit distinct banks.
 #pragma once
 #include "common.h"
 
 namespace moe {
 
 namespace gemm_detail {
-constexpr int BM = kGemmBM;   // 256 rows per m-tile
-constexpr int BK = 64;
-constexpr int PITCH = BK + 8; // bf16 per LDS row (16 B of padding)
+constexpr int BM = kGemmBM;                 // 256 rows per m-tile (and 256 B rows per tile)
+constexpr int BK = 32;                      // K elements per stage
+constexpr int STAGES = 4;                   // LDS stages (loads run STAGES - 1 ahead)
+constexpr int ROWB = BK * 2;                // bytes per staged row
+constexpr int STAGE_BYTES = 2 * BM * ROWB;  // A rows, then B rows
 }  // namespace gemm_detail
 
-// LDS of one tile: two buffers of 256 A rows + 256 B rows, PITCH bf16 each
-constexpr int kGemmSmemElems = 2 * (2 * kGemmBM) * (64 + 8);
+// LDS of one tile: STAGES x (256 A rows + 256 B rows) x 64 bytes = 128 KB
+constexpr int kGemmSmemElems = gemm_detail::STAGES * gemm_detail::STAGE_BYTES / 2;
 
 struct TileCoord {
   int grp, r0, rows, nt;
@@ -42,57 +52,118 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
   return true;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt left at maximum)
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// Where this thread's 16-byte chunks come from: per load instruction a row offset (fixed for the
+// tile) and a chunk within the K slice; the K slice is added per stage.
+struct StageSrc {
+  const uint16_t* abase;
+  const uint16_t* bbase[2];
+  uint32_t aoff[2];     // element offsets (row * ld + chunk * 8) of this lane's A loads
+  uint32_t boff[2];     // and B loads
+  bool bup[2];          // B load from the second weight matrix (W_up)
+  int nk1;              // K slices of the first pass; later slices read the second pass
+  int64_t a_shift, b_shift;
+};
+
+// Issues the 4 LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
+// 16 (2 wave + j) .. + 15 and the same B rows, for j = 0, 1.
+__device__ __forceinline__ void stage_issue(const StageSrc& s, int kt, uint8_t* smem, int stage, int wave) {
+  const bool second = kt >= s.nk1;
+  const int ko = (second ? kt - s.nk1 : kt) * BK;
+  const uint16_t* ab = (second ? s.abase + s.a_shift : s.abase) + ko;
+  const int64_t bsh = (second ? s.b_shift : 0) + ko;
+  uint8_t* base = smem + stage * STAGE_BYTES + wave * 2048;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)(ab + s.aoff[j]), (lds_void*)(base + j * 1024), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds((const void*)((s.bup[j] ? s.bbase[1] : s.bbase[0]) + bsh + s.boff[j]),
+                                     (lds_void*)(base + BM * ROWB + j * 1024), 16, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a staged row
+__device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// MFMAs of one K slice from an LDS stage: this wave's MI x NJ 32x32 blocks over two 16-wide
+// K steps, the second step's fragments read while the first multiplies; row blocks with no
+// valid row skip their MFMAs. a_rd / b_rd: byte offsets of this lane's row; sw: its swizzle.
+template <int MI, int NJ>
+__device__ __forceinline__ void mfma_stage(const uint8_t* st, int a_rd, int b_rd, int sw, int half, int wrows,
+                                           f32x16 (&acc)[MI][NJ]) {
+  const uint8_t* As = st + a_rd;
+  const uint8_t* Bs = st + BM * ROWB + b_rd;
+  bf16x8 af[2][MI], bfr[2][NJ];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = ((kk * 2 + half) ^ sw) * 16;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) af[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + c);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bfr[kk][j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + c);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i * 32 < wrows) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Computes one workgroup tile: rows tc.r0 .. tc.r0 + tc.rows - 1 of group tc.grp, n-tile tc.nt,
-// K steps [k0, k0 + 64 nk) (times two with a.two_pass). smem holds 2 x (256 + 256) x 72 bf16.
+// K slices [k0, k0 + 32 nk) (times two with a.two_pass). smem holds kGemmSmemElems bf16.
 template <int EPI, bool KG, int WN>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc, int k0, int nk, int ntn,
                                           uint16_t* smem) {
   constexpr int WAVES_N = 4, WM = 128, BN = WAVES_N * WN;
-  constexpr int NT = 512;
   constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr int A_T = BM * PITCH, B_T = BN * PITCH;
-  constexpr int RPP = NT / 8;                       // rows staged per pass (8 chunks of 16 B per row)
-  constexpr int AL = BM / RPP, BL = BN / RPP;       // 16-byte chunks per thread per K step
+  static_assert(BN == BM, "A and B stages have the same row count");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int lrow = tid >> 3, lchunk = tid & 7;
+  uint8_t* sm = reinterpret_cast<uint8_t*>(smem);
 
-  // element offsets of the rows this thread stages (A rows lrow + RPP i, B rows likewise)
-  const uint16_t* abase0 = (const uint16_t*)a.A + k0 + lchunk * 8;
-  uint32_t aoff[AL];
+  // This lane's loads: row 16 (2 wave + j) + lane / 4 of A and of B, chunk position lane % 4
+  // holding logical chunk (lane % 4) ^ f(row).
+  StageSrc src;
+  src.abase = (const uint16_t*)a.A + k0;
+  src.bbase[0] = (const uint16_t*)a.B + (KG ? 0 : (int64_t)tc.grp * a.b_group_stride) + k0;
+  src.bbase[1] = (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU)
+                     ? (const uint16_t*)a.B2 + (int64_t)tc.grp * a.b_group_stride + k0
+                     : src.bbase[0];
 #pragma unroll
-  for (int i = 0; i < AL; ++i) {
-    const int rr = lrow + RPP * i;
+  for (int j = 0; j < 2; ++j) {
+    const int rr = 16 * (2 * wave + j) + (lane >> 2);
+    const int ch = (lane & 3) ^ chunk_swz(rr);
     const int r = tc.r0 + min(rr, tc.rows - 1);
-    const int64_t src = (!KG && a.a_gather) ? (int64_t)(a.a_gather[r] / a.a_div) : (int64_t)r;
-    aoff[i] = (uint32_t)(src * a.lda);
-  }
-  const uint16_t* bbase0[2];
-  bbase0[0] = (const uint16_t*)a.B + (KG ? 0 : (int64_t)tc.grp * a.b_group_stride) + k0 + lchunk * 8;
-  bbase0[1] = (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU)
-                  ? (const uint16_t*)a.B2 + (int64_t)tc.grp * a.b_group_stride + k0 + lchunk * 8
-                  : bbase0[0];
-  // K step kt < nk1 reads the first pass, kt >= nk1 the second (operands shifted by the split offsets)
-  const int nk1 = nk;
-  if (a.two_pass) nk *= 2;
-  uint32_t boff[BL];
-  bool bup[BL];
-#pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    const int rr = lrow + RPP * i;
+    const int64_t srow = (!KG && a.a_gather) ? (int64_t)(a.a_gather[r] / a.a_div) : (int64_t)r;
+    src.aoff[j] = (uint32_t)(srow * a.lda + ch * 8);
     int64_t wrow;
     if (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU) {
       // per wave column block: NJ/2 blocks of gate rows, then the matching NJ/2 blocks of up rows
-      const int half = rr / WN, q = (rr % WN) / 32;
-      bup[i] = q >= NJ / 2;
-      wrow = (int64_t)tc.nt * (BN / 2) + half * (WN / 2) + (bup[i] ? q - NJ / 2 : q) * 32 + (rr & 31);
+      const int blk = rr / WN, q = (rr % WN) / 32;
+      src.bup[j] = q >= NJ / 2;
+      wrow = (int64_t)tc.nt * (BN / 2) + blk * (WN / 2) + (src.bup[j] ? q - NJ / 2 : q) * 32 + (rr & 31);
     } else {
-      bup[i] = false;
+      src.bup[j] = false;
       wrow = (int64_t)tc.nt * BN + rr;
     }
     wrow = wrow < a.N ? wrow : a.N - 1;          // partial last n-tile: clamp, results unused
-    boff[i] = (uint32_t)(wrow * a.ldb);
+    src.boff[j] = (uint32_t)(wrow * a.ldb + ch * 8);
   }
+  // K slice kt < nk1 reads the first pass, kt >= nk1 the second (operands shifted by the split offsets)
+  src.nk1 = nk;
+  src.a_shift = a.a_seg_shift;
+  src.b_shift = a.b_seg_shift;
+  if (a.two_pass) nk *= 2;
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -104,69 +175,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 
   // row blocks of this wave that hold at least one valid row
   const int wrows = tc.rows - wm * WM;
-  u32x4 ra[AL], rb[BL];
-  const int st_off = lrow * PITCH + lchunk * 8;   // this thread's LDS store offset (+ RPP i rows)
-  if (nk > 0) {
+  const int a_rd = (wm * WM + (lane & 31)) * ROWB;
+  const int b_rd = (wn * WN + (lane & 31)) * ROWB;
+  const int sw = chunk_swz(lane & 31), half = lane >> 5;
+
+  // Stage s of LDS holds K slice kt = s mod STAGES. Before slice kt is read, this thread's loads
+  // of it have landed (vector-memory count: only the slices issued after it may be pending) and
+  // the barrier makes every thread's loads visible; it also ends every wave's reads of the stage
+  // the next issue overwrites (that of slice kt - 1). s_barrier without a fence keeps the later
+  // slices' loads in flight; the empty asm statements stop the compiler moving LDS reads across.
 #pragma unroll
-    for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase0 + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase0[bup[i]] + boff[i]);
-#pragma unroll
-    for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(smem + st_off + RPP * i * PITCH) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(smem + A_T + st_off + RPP * i * PITCH) = rb[i];
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) stage_issue(src, s, sm, s, wave);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(STAGES - 2, nk - 1 - kt);   // slices issued after kt
+    if (ahead >= 2) MOE_WAIT_VMCNT(8);
+    else if (ahead == 1) MOE_WAIT_VMCNT(4);
+    else MOE_WAIT_VMCNT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + STAGES - 1 < nk) stage_issue(src, kt + STAGES - 1, sm, (kt + STAGES - 1) % STAGES, wave);
+    mfma_stage<MI, NJ>(sm + (kt % STAGES) * STAGE_BYTES, a_rd, b_rd, sw, half, wrows, acc);
   }
   __syncthreads();
-  const int a_rd = (wm * WM + (lane & 31)) * PITCH + (lane >> 5) * 8;
-  const int b_rd = (wn * WN + (lane & 31)) * PITCH + (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      const bool second = kt + 1 >= nk1;
-      const int ko = (second ? kt + 1 - nk1 : kt + 1) * BK;
-      const uint16_t* ab = second ? abase0 + a.a_seg_shift : abase0;
-      const int64_t bsh = second ? a.b_seg_shift : 0;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ab + aoff[i] + ko);
-#pragma unroll
-      for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase0[bup[i]] + bsh + boff[i] + ko);
-    }
-    const uint16_t* As = smem + buf * (A_T + B_T);
-    const uint16_t* Bs = As + A_T;
-    bf16x8 af[2][MI], bfr[2][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(As + a_rd + i * 32 * PITCH);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(Bs + b_rd + j * 32 * PITCH);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          af[cur ^ 1][i] = *reinterpret_cast<const bf16x8*>(As + a_rd + i * 32 * PITCH + (kk + 1) * 16);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8*>(Bs + b_rd + j * 32 * PITCH + (kk + 1) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (i * 32 < wrows) {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < nk) {
-      uint16_t* An = smem + (buf ^ 1) * (A_T + B_T);
-#pragma unroll
-      for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(An + st_off + RPP * i * PITCH) = ra[i];
-#pragma unroll
-      for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(An + A_T + st_off + RPP * i * PITCH) = rb[i];
-    }
-    __syncthreads();
-  }
 
   // epilogue. Accumulator slot r of lane l: row (r/4)*8 + (l/32)*4 + r%4, column l%32.
   const int ccol = lane & 31;

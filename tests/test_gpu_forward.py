@@ -195,10 +195,16 @@ def test_chunked_ring_mid_parity(m):
     check_forward(m, synth.MID, chunk_rows=512)
 
 
-def test_weight_major_tile_order_bitwise(m):
-    """The n-tile-major tile order inside an expert changes only the schedule, not the bits."""
-    L = synth.to_device(synth.host_layer(synth.scaled(SMALL_BF16, 'skewed_small', T=700)))
+@pytest.mark.parametrize('order', ['weight_major', 'block1', 'block3', 'block255'])
+def test_tile_order_bitwise(m, order):
+    """The order of the grouped GEMM tiles inside an expert changes only the schedule, not the bits."""
+    flags = {'weight_major': m.MOE_FLAG_WEIGHT_MAJOR, 'block1': m.MOE_FLAG_TILE_BLOCK(1),
+             'block3': m.MOE_FLAG_TILE_BLOCK(3), 'block255': m.MOE_FLAG_TILE_BLOCK(255)}[order]
+    # 4 n-tiles in both GEMMs, about 2 m-tiles per expert
+    L = synth.to_device(synth.host_layer(synth.scaled(SMALL_BF16, 'order_T2000_D1024_I512', T=2000, D=1024,
+                                                      I=512)))
     a = ForwardRun(m, L)()
-    b = ForwardRun(m, L, flags=m.MOE_FLAG_WEIGHT_MAJOR)()
+    b = ForwardRun(m, L, flags=flags)()
     torch.cuda.synchronize()
     assert torch.equal(a.out, b.out) and torch.equal(a.y_routes, b.y_routes)
+    assert torch.equal(a.shared_out, b.shared_out)
