@@ -18,6 +18,7 @@ the same workload (rank 0, one GPU only).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,41 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, TFLOP/s
 PEAK_F32_TFLOPS = 157.3         # fp32 vector
 PEAK_HBM_GBS = 8000.0           # HBM3E, GB/s
 METRIC = 'MoE layer tokens/s (fwd, fwd+bwd) on 1 MI355X; % of MFMA peak'
+
+# HBM traffic of the dominant kernel is read from its rocprofv3 counter summary, and only while the
+# kernel sources are the ones the counters were taken on (hash recorded in the summary).
+GEMM_SOURCES = ('mixture_experts_layer_norm_amd/csrc/gemm_tile.h', 'mixture_experts_layer_norm_amd/csrc/gemm.hip')
+TRAFFIC_SUMMARY = {'up_gate': 'profiles/gemm_swiglu_routed_dsv3_T8192_hbm_traffic.md',
+                   'down': 'profiles/gemm_down_routed_dsv3_T8192_hbm_traffic.md'}
+
+
+def gemm_sources_hash():
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), 'rb') as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage, flags, workload):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) for `stage`, or None when no
+    summary matches the current kernel sources, flags and workload."""
+    rel = TRAFFIC_SUMMARY.get(stage)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    kv = {}
+    with open(os.path.join(ROOT, rel)) as f:
+        for line in f:
+            if line.startswith('- ') and ': ' in line:
+                k, v = line[2:].split(': ', 1)
+                kv[k.strip()] = v.strip().strip('`')
+    try:
+        if (kv.get('sources_sha256_16') != gemm_sources_hash() or int(kv.get('flags', -1)) != flags
+                or kv.get('workload') != workload):
+            return None
+        return float(kv['traffic_bytes_per_launch'])
+    except (KeyError, ValueError):
+        return None
 
 
 def stage_work(cfg, flags):
@@ -60,7 +96,7 @@ def main():
     ap.add_argument('--chunk-rows', type=int, default=0)
     ap.add_argument('--flags', type=int, default=0)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--cpu-tokens', type=int, default=96, help='tokens in the CPU oracle sample')
+    ap.add_argument('--cpu-tokens', type=int, default=160, help='tokens in the CPU oracle sample')
     ap.add_argument('--calib-copy', action='store_true',
                     help='run one 1 GiB device-to-device copy before the timed region (HBM counter calibration)')
     args = ap.parse_args()
@@ -148,7 +184,7 @@ def main():
     else:
         roof = {'bound': 'hbm', 'achieved': b_dom / t_dom / 1e9, 'peak': PEAK_HBM_GBS, 'unit': 'GB/s'}
     roof['frac'] = roof['achieved'] / roof['peak']
-    roof['traffic'] = None
+    roof['traffic'] = measured_traffic(dom, args.flags, cfg.name)
     roof['kernel'] = {'up_gate': 'gemm_bf16_kernel<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
                       'down': 'gemm_bf16_kernel<EPI_STORE> (routed W_down + scatter)',
                       'shared': 'shared expert GEMMs', 'dispatch': 'dispatch_kernel',

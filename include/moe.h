@@ -87,6 +87,9 @@ typedef struct moe_problem {
 #define MOE_FLAG_WEIGHT_MAJOR 0x2
 /* Tile order of the grouped GEMMs: inside each expert, blocks of n n-tiles (1..255), each block
  * m-tile major (MOE_FLAG_WEIGHT_MAJOR is n = 1). Affects only speed, never the results. */
+/* Tuning: run the bf16 grouped GEMMs with 4 wavefronts per workgroup, each owning a 128 x 128
+ * block of the 256 x 256 tile, instead of 8 wavefronts of 128 x 64. Results are bitwise equal. */
+#define MOE_FLAG_GEMM_WAVES4 0x8
 #define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */

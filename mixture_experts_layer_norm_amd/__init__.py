@@ -23,6 +23,7 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_FLAG_FUSED_GATHER = 0x1
 MOE_FLAG_WEIGHT_MAJOR = 0x2
 MOE_FLAG_PERSISTENT = 0x4
+MOE_FLAG_GEMM_WAVES4 = 0x8
 
 
 def MOE_FLAG_TILE_BLOCK(n):

@@ -234,6 +234,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
     Grouped gs;
     gs.M = p->T;
     gs.nblk = tile_block_of(p->flags);
+    gs.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
                     0, 0, wsb + L.sh_h, sho, nullptr, stream);
     if (st) return st;
@@ -245,6 +246,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   gr.groups = p->E;
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
   gr.nblk = tile_block_of(p->flags);
+  gr.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
   if (L.pipelined) {
     // Chunks of b routed slots through a ring of S stages, each carried through dispatch, up/gate
     // and down before the next; all tile bookkeeping is on the device (no host synchronisation).
@@ -269,6 +271,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
       gc.groups = p->E;
       gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
       gc.nblk = tile_block_of(p->flags);
+      gc.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
       st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
                       p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream);
       if (st) return st;

@@ -117,6 +117,7 @@ struct Grouped {
   // Tile order inside a group: blocks of nblk n-tiles; inside a block m-tile major. nblk >= the
   // n-tile count is plain m-tile major, nblk = 1 n-tile major (0 means m-tile major too).
   int32_t nblk = 0;
+  int32_t waves4 = 0;         // bf16 GEMM workgroups of 4 wavefronts x (128 x 128) instead of 8 x (128 x 64)
 };
 
 // EPI_SWIGLU:   h = SiLU(gate) * up                       -> C

@@ -59,29 +59,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Where this thread's 16-byte chunks come from: per load instruction a row offset (fixed for the
 // tile) and a chunk within the K slice; the K slice is added per stage.
+template <int NL>
 struct StageSrc {
   const uint16_t* abase;
   const uint16_t* bbase[2];
-  uint32_t aoff[2];     // element offsets (row * ld + chunk * 8) of this lane's A loads
-  uint32_t boff[2];     // and B loads
-  bool bup[2];          // B load from the second weight matrix (W_up)
+  uint32_t aoff[NL];    // element offsets (row * ld + chunk * 8) of this lane's A loads
+  uint32_t boff[NL];    // and B loads
+  bool bup[NL];         // B load from the second weight matrix (W_up)
   int nk1;              // K slices of the first pass; later slices read the second pass
   int64_t a_shift, b_shift;
 };
 
-// Issues the 4 LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
-// 16 (2 wave + j) .. + 15 and the same B rows, for j = 0, 1.
-__device__ __forceinline__ void stage_issue(const StageSrc& s, int kt, uint8_t* smem, int stage, int wave) {
+// Issues the 2 NL LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
+// 16 (NL wave + j) .. + 15 and the same B rows, for j < NL (NL = 16 / wavefronts).
+template <int NL>
+__device__ __forceinline__ void stage_issue(const StageSrc<NL>& s, int kt, uint8_t* smem, int stage, int wave) {
   const bool second = kt >= s.nk1;
   const int ko = (second ? kt - s.nk1 : kt) * BK;
   const uint16_t* ab = (second ? s.abase + s.a_shift : s.abase) + ko;
   const int64_t bsh = (second ? s.b_shift : 0) + ko;
-  uint8_t* base = smem + stage * STAGE_BYTES + wave * 2048;
+  uint8_t* base = smem + stage * STAGE_BYTES + wave * (NL * 1024);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NL; ++j)
     __builtin_amdgcn_global_load_lds((const void*)(ab + s.aoff[j]), (lds_void*)(base + j * 1024), 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NL; ++j)
     __builtin_amdgcn_global_load_lds((const void*)((s.bup[j] ? s.bbase[1] : s.bbase[0]) + bsh + s.boff[j]),
                                      (lds_void*)(base + BM * ROWB + j * 1024), 16, 0, 0);
 }
@@ -89,59 +91,108 @@ __device__ __forceinline__ void stage_issue(const StageSrc& s, int kt, uint8_t* 
 // XOR swizzle of the 16-byte chunks of a staged row
 __device__ __forceinline__ int chunk_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// MFMAs of one K slice from an LDS stage: this wave's MI x NJ 32x32 blocks over two 16-wide
-// K steps, the second step's fragments read while the first multiplies; row blocks with no
-// valid row skip their MFMAs. a_rd / b_rd: byte offsets of this lane's row; sw: its swizzle.
-template <int MI, int NJ>
-__device__ __forceinline__ void mfma_stage(const uint8_t* st, int a_rd, int b_rd, int sw, int half, int wrows,
-                                           f32x16 (&acc)[MI][NJ]) {
+// Fragments of one K slice for this wave: its first NACT row blocks of A and its NJ column
+// blocks of B, for the two 16-wide K steps of the slice.
+template <int NACT, int NJ>
+struct Frags {
+  bf16x8 a[2][NACT > 0 ? NACT : 1];
+  bf16x8 b[2][NJ];
+};
+
+// Reads the fragments of one LDS stage. a_rd / b_rd: byte offsets of this lane's row; sw: its
+// chunk swizzle; half: which 8 of the 16 K values of an MFMA step the lane supplies.
+template <int NACT, int NJ>
+__device__ __forceinline__ void frag_read(const uint8_t* st, int a_rd, int b_rd, int sw, int half,
+                                          Frags<NACT, NJ>& f) {
   const uint8_t* As = st + a_rd;
   const uint8_t* Bs = st + BM * ROWB + b_rd;
-  bf16x8 af[2][MI], bfr[2][NJ];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int c = ((kk * 2 + half) ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) af[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + c);
+    for (int i = 0; i < NACT; ++i) f.a[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + c);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[kk][j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + c);
+    for (int j = 0; j < NJ; ++j) f.b[kk][j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + c);
   }
+}
+
+// MFMAs of one K slice: NACT x NJ blocks of 32 x 32 over two 16-wide K steps.
+template <int MI, int NJ, int NACT>
+__device__ __forceinline__ void frag_mfma(const Frags<NACT, NJ>& f, f32x16 (&acc)[MI][NJ]) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      if (i * 32 < wrows) {
+    for (int i = 0; i < NACT; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
-      }
-    }
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
+}
+
+// Waits until at most `pending` K slices of this thread's loads are outstanding (2 NL loads each).
+template <int NL>
+__device__ __forceinline__ void wait_slices(int pending) {
+  if (pending >= 2) MOE_WAIT_VMCNT(4 * NL);
+  else if (pending == 1) MOE_WAIT_VMCNT(2 * NL);
+  else MOE_WAIT_VMCNT(0);
+}
+
+// Barrier between K slices: this wave's LDS reads have landed, then all waves meet. No fence, so
+// the later slices' loads stay in flight; the empty asm statements stop the compiler moving LDS
+// accesses across.
+__device__ __forceinline__ void slice_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The K loop of one tile. LDS stage s holds K slice kt with kt = s mod STAGES. In step kt,
+// once slice kt has landed (this thread's loads: only the slices issued after it may be
+// pending) and the barrier has made every thread's loads visible (and ended every wave's reads
+// of slice kt - 1), the stage of slice kt - 1 is refilled with slice kt + STAGES - 1, then the
+// fragments of slice kt are read and multiplied. NACT (active row blocks of this wave) is a
+// compile-time constant so that the loop has no divergent branches around the MFMAs.
+template <int MI, int NJ, int NACT, int NL>
+__device__ __forceinline__ void k_loop(const StageSrc<NL>& src, uint8_t* sm, int nk, int wave, int a_rd,
+                                       int b_rd, int sw, int half, f32x16 (&acc)[MI][NJ]) {
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) stage_issue(src, s, sm, s, wave);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_slices<NL>(min(STAGES - 2, nk - 1 - kt));
+    slice_barrier();
+    if (kt + STAGES - 1 < nk) stage_issue(src, kt + STAGES - 1, sm, (kt + STAGES - 1) % STAGES, wave);
+    Frags<NACT, NJ> f;
+    frag_read<NACT, NJ>(sm + (kt % STAGES) * STAGE_BYTES, a_rd, b_rd, sw, half, f);
+    // every fragment read of the slice ahead of its MFMAs: one LDS latency per slice
+    __builtin_amdgcn_sched_barrier(0);
+    frag_mfma<MI, NJ, NACT>(f, acc);
   }
 }
 
 // Computes one workgroup tile: rows tc.r0 .. tc.r0 + tc.rows - 1 of group tc.grp, n-tile tc.nt,
 // K slices [k0, k0 + 32 nk) (times two with a.two_pass). smem holds kGemmSmemElems bf16.
-template <int EPI, bool KG, int WN>
+template <int EPI, bool KG, int WN, int WAVES_N>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc, int k0, int nk, int ntn,
                                           uint16_t* smem) {
-  constexpr int WAVES_N = 4, WM = 128, BN = WAVES_N * WN;
+  constexpr int WM = 128, BN = WAVES_N * WN;
+  constexpr int NWAVES = 2 * WAVES_N, NL = 16 / NWAVES;   // wavefronts; loads per operand per slice
   constexpr int MI = WM / 32, NJ = WN / 32;
   static_assert(BN == BM, "A and B stages have the same row count");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   uint8_t* sm = reinterpret_cast<uint8_t*>(smem);
 
-  // This lane's loads: row 16 (2 wave + j) + lane / 4 of A and of B, chunk position lane % 4
+  // This lane's loads: row 16 (NL wave + j) + lane / 4 of A and of B, chunk position lane % 4
   // holding logical chunk (lane % 4) ^ f(row).
-  StageSrc src;
+  StageSrc<NL> src;
   src.abase = (const uint16_t*)a.A + k0;
   src.bbase[0] = (const uint16_t*)a.B + (KG ? 0 : (int64_t)tc.grp * a.b_group_stride) + k0;
   src.bbase[1] = (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU)
                      ? (const uint16_t*)a.B2 + (int64_t)tc.grp * a.b_group_stride + k0
                      : src.bbase[0];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rr = 16 * (2 * wave + j) + (lane >> 2);
+  for (int j = 0; j < NL; ++j) {
+    const int rr = 16 * (NL * wave + j) + (lane >> 2);
     const int ch = (lane & 3) ^ chunk_swz(rr);
     const int r = tc.r0 + min(rr, tc.rows - 1);
     const int64_t srow = (!KG && a.a_gather) ? (int64_t)(a.a_gather[r] / a.a_div) : (int64_t)r;
@@ -173,30 +224,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // row blocks of this wave that hold at least one valid row
-  const int wrows = tc.rows - wm * WM;
   const int a_rd = (wm * WM + (lane & 31)) * ROWB;
   const int b_rd = (wn * WN + (lane & 31)) * ROWB;
   const int sw = chunk_swz(lane & 31), half = lane >> 5;
 
-  // Stage s of LDS holds K slice kt = s mod STAGES. Before slice kt is read, this thread's loads
-  // of it have landed (vector-memory count: only the slices issued after it may be pending) and
-  // the barrier makes every thread's loads visible; it also ends every wave's reads of the stage
-  // the next issue overwrites (that of slice kt - 1). s_barrier without a fence keeps the later
-  // slices' loads in flight; the empty asm statements stop the compiler moving LDS reads across.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) stage_issue(src, s, sm, s, wave);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(STAGES - 2, nk - 1 - kt);   // slices issued after kt
-    if (ahead >= 2) MOE_WAIT_VMCNT(8);
-    else if (ahead == 1) MOE_WAIT_VMCNT(4);
-    else MOE_WAIT_VMCNT(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + STAGES - 1 < nk) stage_issue(src, kt + STAGES - 1, sm, (kt + STAGES - 1) % STAGES, wave);
-    mfma_stage<MI, NJ>(sm + (kt % STAGES) * STAGE_BYTES, a_rd, b_rd, sw, half, wrows, acc);
+  static_assert(4 * NL <= 63, "vmcnt range");
+  // wave-uniform count of this wave's row blocks that hold a valid row
+  const int wrows_u = tc.rows - (__builtin_amdgcn_readfirstlane(wave) / WAVES_N) * WM;
+  const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
+  static_assert(MI == 4, "row-block dispatch below assumes 4 row blocks per wave");
+  switch (nact) {
+    case 0: k_loop<MI, NJ, 0, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 1: k_loop<MI, NJ, 1, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 2: k_loop<MI, NJ, 2, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 3: k_loop<MI, NJ, 3, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    default: k_loop<MI, NJ, 4, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
   }
   __syncthreads();
 
