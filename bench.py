@@ -92,7 +92,9 @@ def main():
     ap.add_argument('--gpus', type=int, default=1)
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
-    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny'])
+    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'ep_share'])
+    ap.add_argument('--no-extra', action='store_true',
+                    help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
     ap.add_argument('--flags', type=int, default=0)
     ap.add_argument('--no-cpu-baseline', action='store_true')
@@ -109,6 +111,9 @@ def main():
     import synth
     import mixture_experts_layer_norm_amd as moe
 
+    if args.workload == 'ep_share':
+        print(json.dumps(bench_share(args.steps, args.warmup, args.flags)), flush=True)
+        return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY}[args.workload]
     torch.cuda.set_device(0)
     print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
@@ -200,6 +205,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, L, args.cpu_tokens)
+    extra = None
+    if not args.no_extra and args.workload == 'dsv3':
+        del L, weights, ws, out
+        torch.cuda.empty_cache()
+        extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags)}
 
     line = {
         'metric': METRIC,
@@ -224,7 +234,70 @@ def main():
         'roofline': roof,
         'cpu_baseline': cpu,
     }
+    if extra is not None:
+        line['extra'] = extra
     print(json.dumps(line), flush=True)
+
+
+def bench_share(steps, warmup, flags):
+    """Forward + backward of one expert-parallel rank's share at the DSV3 shape (4 local experts,
+    57,344 slots with Zipf(1.2) loads, shared expert on 7,168 tokens): moe_experts_forward then
+    moe_experts_backward per step, inputs resident in HBM. Returns a result dict."""
+    import torch
+    import synth
+    import mixture_experts_layer_norm_amd as moe
+    cfg = synth.EP_SHARE
+    print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
+    D_ = synth.device_share(cfg)
+    S, E, I, D, Is, T = cfg.slots, cfg.E_local, cfg.I, cfg.D, cfg.I_shared, cfg.tokens
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(D_.counts)]).astype(np.int32)).cuda()
+    p = moe.problem(T, D, I, E, cfg.K, Is, 'bf16', 0, 0, flags)
+    W = moe.make_weights(D_.w_gate, D_.w_up, D_.w_down, D_.ws_gate, D_.ws_up, D_.ws_down)
+    y = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
+    sh = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    dxs = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
+    dg = torch.empty((S,), dtype=torch.float32, device='cuda')
+    gr = [torch.empty(s_, device='cuda') for s_ in ((E, I, D), (E, I, D), (E, D, I), (Is, D), (Is, D), (D, Is))]
+    G = moe.make_grads(*gr)
+    dxl = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    wsb = torch.empty((moe.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        moe.experts_forward(p, S, D_.x_slot, offsets, W, y, D_.x_local, sh, ws, stream=stream)
+
+    def bwd():
+        moe.experts_backward(p, S, D_.x_slot, offsets, D_.g, D_.dy_slot, W, dxs, dg, G, D_.x_local, D_.dy_local,
+                             dxl, wsb, stream=stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in ev]))
+    b_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in ev]))
+    ms = f_ms + b_ms
+    flops_f = 6.0 * S * D * I + 6.0 * T * D * Is
+    flops = 3.0 * flops_f
+    print(f'[bench] ep share: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms', file=sys.stderr, flush=True)
+    return {'workload': f'{cfg.name} forward+backward', 'tokens': T, 'slots': S, 'counts': D_.counts.tolist(),
+            'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms,
+            'value': T / (ms * 1e-3), 'unit': 'tokens/s', 'slots_per_s': S / (ms * 1e-3),
+            'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            'fwd_tflops': flops_f / (f_ms * 1e-3) / 1e12, 'bwd_tflops': 2 * flops_f / (b_ms * 1e-3) / 1e12}
 
 
 def cpu_baseline(cfg, L, ntok):

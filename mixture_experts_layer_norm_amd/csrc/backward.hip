@@ -23,7 +23,7 @@ namespace moe {
 static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t err, offs, tile_off, poff, offs_s, tile_off_s, poff_s;
+  size_t err, offs, tile_off, poff, order, offs_s, tile_off_s, poff_s;
   size_t g_slot, dg_slot, x_slot, dy_slot, dx_slot, dx_sh;
   size_t act_a, act_u, dau, part, wdT, wguT, xT, dyT, ghT, dauT;
   size_t s_a, s_u, s_dau, s_part, s_wdT, s_wguT, s_xT, s_dyT, s_hT, s_dauT;
@@ -42,6 +42,7 @@ static BwdLayout bwd_layout(const moe_problem& p) {
   auto take = [&](size_t bytes) { size_t at = o; o = al256(o + bytes); return at; };
   L.err = take(256 + 4096);
   L.offs = take((E + 1) * 4); L.tile_off = take((E + 1) * 4); L.poff = take((E + 1) * 4);
+  L.order = take(E * 4);
   L.offs_s = take(8); L.tile_off_s = take(8); L.poff_s = take(8);
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
   L.x_slot = take(n * D * 2); L.dy_slot = take(n * D * 2); L.dx_slot = take(n * D * 2);
@@ -67,6 +68,7 @@ struct CoreBufs {
   void *act_a, *act_u, *dau, *wdT, *wguT, *xT, *dyT, *ghT, *dauT;
   float* part;
   int64_t Spad;
+  int32_t* order;   // [G] dealing order of the K-grouped GEMMs (null for one group)
 };
 
 // Backward of one set of groups (routed experts, or the shared expert as one group).
@@ -120,17 +122,20 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   if ((st = launch_transpose_pad(TR_COPY, b.dau, nullptr, nullptr, 4 * I, 4 * I, offs, poff, G, Sp, b.dauT, Sp, s)))
     return st;
 
+  // weight-gradient tiles of the longest groups first
+  if (G > 1 && b.order && (st = launch_group_order(poff, G, b.order, s))) return st;
+  const int32_t* order = G > 1 ? b.order : nullptr;
   // dW_down[g] = sum_j dy_j (g_j h_j)^T   -> [D][I]  (B = g*h: high rows, then low rows)
   GemmArgs w1;
   w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
   w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I;
-  w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp;
+  w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp; w1.k_order = order;
   if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
   // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
   GemmArgs w2;
   w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
   w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D;
-  w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp;
+  w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp; w2.k_order = order;
   return launch_gemm_bf16_kgroup(w2, G, s);
 }
 
@@ -138,11 +143,11 @@ static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
   return CoreBufs{ws + L.act_a, ws + L.act_u, ws + L.dau, ws + L.wdT, ws + L.wguT, ws + L.xT, ws + L.dyT,
-                  ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad};
+                  ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad, (int32_t*)(ws + L.order)};
 }
 static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
   return CoreBufs{ws + L.s_a, ws + L.s_u, ws + L.s_dau, ws + L.s_wdT, ws + L.s_wguT, ws + L.s_xT, ws + L.s_dyT,
-                  ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad};
+                  ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad, nullptr};
 }
 
 // one group of T rows for the shared expert: offsets {0, T}

@@ -87,6 +87,7 @@ int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D,
                     int64_t count, void* x_slot, uint8_t* x_slot_sc, hipStream_t s);
 int launch_combine(const void* y_routes, const void* shared_out, const float* topk_w, void* out,
                    int T, int K, int D, int dtype, hipStream_t s);
+int launch_group_order(const int32_t* poff, int G, int32_t* order, hipStream_t s);
 int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean, int32_t* tile_off, int32_t* poff,
                         int32_t* err, hipStream_t s);
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
@@ -142,6 +143,7 @@ struct GemmArgs {
   // of 64); A is [M][lda], B is [N][ldb] shared by all groups; the fp32 output of group g is
   // C + g * c_group_stride ([M][ldc]), or C2 + g * c_group_stride for rows >= m_split.
   const int32_t* k_off = nullptr;
+  const int32_t* k_order = nullptr;   // groups in dealing order (longest K first); null: 0, 1, ...
   int32_t M = 0;
   int32_t m_split = 0;
   int64_t c_group_stride = 0;

@@ -35,19 +35,23 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
   __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems];
   // The grid is an upper bound (grouped tile counts are known only on the device); the valid
   // tiles are split evenly over the 8 XCDs, each taking a contiguous range of them.
+  // K-grouped tiles differ in length by their group's K extent: they are dealt in launch order
+  // (workgroups start in blockIdx order as CUs free up), groups longest first, so that the
+  // in-order dispatch balances the CUs like a longest-first schedule.
   const int valid = (KG ? g.groups * mtn : (g.row_off ? g.tile_off[g.groups] : mtn)) * ntn;
   const int per_xcd = (valid + 7) >> 3;
   const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
+  if (!KG && (bid >> 3) >= per_xcd) return;
+  const int logical = KG ? bid : (bid & 7) * per_xcd + (bid >> 3);
   if (logical >= valid) return;
   TileCoord tc;
   int k0 = 0, nk;
   if (KG) {
     const int per = mtn * ntn;
-    tc.grp = logical / per;
-    if (tc.grp >= g.groups) return;
-    const int rem = logical - tc.grp * per;
+    const int rank = logical / per;
+    if (rank >= g.groups) return;
+    tc.grp = a.k_order ? a.k_order[rank] : rank;
+    const int rem = logical - rank * per;
     tc.nt = rem % ntn;
     tc.r0 = (rem / ntn) * BM;
     tc.rows = min(BM, a.M - tc.r0);

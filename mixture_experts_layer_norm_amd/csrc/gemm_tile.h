@@ -245,9 +245,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   // epilogue. Accumulator slot r of lane l: row (r/4)*8 + (l/32)*4 + r%4, column l%32.
   const int ccol = lane & 31;
   float* part = reinterpret_cast<float*>(smem);   // EPI_DGRAD: [BM][WAVES_N] partials (LDS is free now)
-#pragma unroll
+  // fully unrolled: the accumulators must be indexed with constants to stay in registers
+#pragma clang loop unroll(full)
   for (int i = 0; i < MI; ++i) {
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int r = 0; r < 16; ++r) {
       const int lr = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       const bool ok = lr < tc.rows;
@@ -300,6 +301,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 #pragma unroll
         for (int off = 16; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
         if (ccol == 0) part[lr * WAVES_N + wn] = p;
+        // bound the loads the scheduler hoists ahead (it would otherwise spill)
+        __builtin_amdgcn_sched_barrier(0);
       } else {
         if (!ok) continue;
         if (KG) {

@@ -54,6 +54,31 @@ __global__ __launch_bounds__(1024) void group_prefix_kernel(const int32_t* __res
   }
 }
 
+// Groups ranked by their K extent (poff[g+1] - poff[g]) in decreasing order, ties to the lower
+// index: order[rank] = group. The K-grouped GEMM deals its tiles in this order, longest first.
+__global__ __launch_bounds__(1024) void group_order_kernel(const int32_t* __restrict__ poff, int G,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int sz[1024];
+  const int t = threadIdx.x;
+  sz[t] = t < G ? poff[t + 1] - poff[t] : -1;
+  __syncthreads();
+  if (t >= G) return;
+  const int mine = sz[t];
+  int rank = 0;
+  for (int u = 0; u < G; ++u) {
+    const int o = sz[u];
+    rank += (o > mine) || (o == mine && u < t);
+  }
+  order[rank] = t;
+}
+
+int launch_group_order(const int32_t* poff, int G, int32_t* order, hipStream_t s) {
+  if (G < 1 || G > 1024) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(group_order_kernel, dim3(1), dim3(1024), 0, s, poff, G, order);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean, int32_t* tile_off, int32_t* poff,
                         int32_t* err, hipStream_t s) {
   hipLaunchKernelGGL(group_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, rows, clean, tile_off, poff, err);
@@ -120,6 +145,47 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   }
 }
 
+// TR_COPY of bf16 rows with 16-byte accesses on both sides: 64 padded columns x 64 features per
+// workgroup; each thread loads 8 consecutive features of a source row and stores 8 consecutive
+// padded columns of one output row. W % 8 == 0, lds % 8 == 0, ldo % 8 == 0.
+__global__ __launch_bounds__(256) void transpose_pad_copy16_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                                   int W, const int32_t* __restrict__ offsets,
+                                                                   const int32_t* __restrict__ poff, int G,
+                                                                   uint16_t* __restrict__ out, int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
+  const int p0 = blockIdx.x * 64;          // padded column block
+  const int c0 = blockIdx.y * 64;          // feature block
+  if (p0 >= poff[G]) return;
+  int lo = 0, hi = G - 1;                  // group holding padded column p0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
+  }
+  const int n = offsets[lo + 1] - offsets[lo];
+  const int jbase = offsets[lo] + (p0 - poff[lo]);
+  const int valid = min(64, n - (p0 - poff[lo]));
+  const int t = threadIdx.x, q = t & 7, rr = t >> 3;   // chunk of 8, row in a pass of 32
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = rr + 32 * pass;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < valid && c0 + q * 8 < W) v = *reinterpret_cast<const u32x4*>(src + (int64_t)(jbase + r) * lds + c0 + q * 8);
+    *reinterpret_cast<u32x4*>(&tile[r][q * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = rr + 32 * pass;            // feature within the block
+    if (c0 + c >= W) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)tile[q * 8 + 2 * k][c] | ((uint32_t)tile[q * 8 + 2 * k + 1][c] << 16);
+    u32x4 o = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(out + (int64_t)(c0 + c) * ldo + p0 + q * 8) = o;
+  }
+}
+
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
                          const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
                          int64_t ldo, hipStream_t s, int split_lo) {
@@ -127,7 +193,11 @@ int launch_transpose_pad(int mode, const void* src, const void* src2, const floa
   const uint16_t* a = (const uint16_t*)src;
   const uint16_t* b = (const uint16_t*)src2;
   uint16_t* o = (uint16_t*)out;
-  if (mode == TR_COPY)
+  const bool v16 = mode == TR_COPY && !split_lo && W % 8 == 0 && lds % 8 == 0 && ldo % 8 == 0 &&
+                   ((uintptr_t)src & 15) == 0 && ((uintptr_t)out & 15) == 0;
+  if (v16)
+    hipLaunchKernelGGL(transpose_pad_copy16_kernel, grid, block, 0, s, a, lds, W, offsets, poff, G, o, ldo);
+  else if (mode == TR_COPY)
     hipLaunchKernelGGL(transpose_pad_kernel<TR_COPY>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo);
   else if (mode == TR_SCALE)
     hipLaunchKernelGGL(transpose_pad_kernel<TR_SCALE>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo);

@@ -308,3 +308,26 @@ def to_device(L: HostLayer, device='cuda') -> DeviceLayer:
 
     return DeviceLayer(L.cfg, up(L.x), torch.from_numpy(L.logits).to(device), up(L.w_gate), up(L.w_up),
                        up(L.w_down), up(L.ws_gate), up(L.ws_up), up(L.ws_down))
+
+
+def device_share(cfg: EPShareConfig, device='cuda') -> HostShare:
+    """Full-size share inputs generated on the device (same recipe as host_share, Philox draws);
+    the fields hold device tensors (bf16, g fp32) and `counts` the host array."""
+    import torch
+    S, D, I, E, Is = cfg.slots, cfg.D, cfg.I, cfg.E_local, cfg.I_shared
+    bf = torch.bfloat16
+    counts = zipf_counts(S, E, cfg.zipf_s)
+    x_slot = device_normal(cfg.seed, TID_XSLOT, (S, D), 1.0, dtype=bf, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(device_seed(cfg.seed, TID_G))
+    g = torch.rand((S,), generator=gen, device=device, dtype=torch.float32)
+    dy = device_normal(cfg.seed, TID_DOUT, (S, D), 1.0, dtype=bf, device=device)
+    xl = device_normal(cfg.seed, TID_XLOCAL, (cfg.tokens, D), 1.0, dtype=bf, device=device)
+    dyl = device_normal(cfg.seed, TID_DYLOCAL, (cfg.tokens, D), 1.0, dtype=bf, device=device)
+    wg = torch.stack([device_normal(cfg.seed, TID_WGATE, (I, D), 1 / math.sqrt(D), e, bf, device) for e in range(E)])
+    wu = torch.stack([device_normal(cfg.seed, TID_WUP, (I, D), 1 / math.sqrt(D), e, bf, device) for e in range(E)])
+    wd = torch.stack([device_normal(cfg.seed, TID_WDOWN, (D, I), 1 / math.sqrt(I), e, bf, device) for e in range(E)])
+    sg = device_normal(cfg.seed, TID_SGATE, (Is, D), 1 / math.sqrt(D), 0, bf, device)
+    su = device_normal(cfg.seed, TID_SUP, (Is, D), 1 / math.sqrt(D), 0, bf, device)
+    sd = device_normal(cfg.seed, TID_SDOWN, (D, Is), 1 / math.sqrt(Is), 0, bf, device)
+    return HostShare(cfg, counts, x_slot, g, dy, xl, dyl, wg, wu, wd, sg, su, sd)

@@ -142,3 +142,87 @@ def test_layer_backward(m, cfg):
     mask = np.zeros((T, E), dtype=bool)
     np.put_along_axis(mask, ref['idx'].astype(np.int64), True, axis=1)
     assert np.all(t2np(dlg)[~mask] == 0)
+
+
+def run_share_device(m, D_):
+    """experts_forward + experts_backward on device-generated share inputs (full size)."""
+    cfg = D_.cfg
+    S, E, I, D, Is = cfg.slots, cfg.E_local, cfg.I, cfg.D, cfg.I_shared
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(D_.counts)]).astype(np.int32)).cuda()
+    p = m.problem(cfg.tokens, D, I, E, cfg.K, Is, 'bf16')
+    W = m.make_weights(D_.w_gate, D_.w_up, D_.w_down, D_.ws_gate, D_.ws_up, D_.ws_down)
+    y = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
+    sh = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
+    ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.experts_forward(p, S, D_.x_slot, offsets, W, y, D_.x_local, sh, ws)
+    dxs = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
+    dg = torch.empty((S,), dtype=torch.float32, device='cuda')
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    G = m.make_grads(**gr)
+    dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
+    wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.experts_backward(p, S, D_.x_slot, offsets, D_.g, D_.dy_slot, W, dxs, dg, G, D_.x_local, D_.dy_local, dxl, wsb)
+    torch.cuda.synchronize()
+    return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, err=int(wsb[:4].view(torch.int32).item()), **gr)
+
+
+def h64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.slow
+def test_ep_share_full_size_sampled(m):
+    """One EP=64 rank's share at the DSV3 shape (4 local experts, Zipf(1.2) loads over 57,344
+    slots, shared expert on 7,168 tokens), forward + backward on the device. Checked against the
+    oracle on samples it can afford: whole slots (y, dx, dg depend on their own slot only), whole
+    shared-expert rows, and single intermediate units i, for which the expert restricted to unit i
+    (rows i of W_gate, W_up and column i of W_down) gives exactly row i of dW_gate, dW_up and
+    column i of dW_down over all of the expert's slots."""
+    cfg = synth.EP_SHARE
+    print('[ep_share] generating full-size share inputs', flush=True)
+    D_ = synth.device_share(cfg)
+    r = run_share_device(m, D_)
+    assert r['err'] == 0
+    off = np.concatenate([[0], np.cumsum(D_.counts)])
+    rng = np.random.default_rng(7)
+    # whole slots, 3 per expert
+    slots = np.concatenate([np.sort(rng.choice(np.arange(off[e], off[e + 1]), 3, replace=False))
+                            for e in range(cfg.E_local)])
+    cnt = np.full(cfg.E_local, 3)
+    idx = torch.from_numpy(slots).cuda()
+    xs, dys, gs = h64(D_.x_slot[idx]), h64(D_.dy_slot[idx]), D_.g[idx].cpu().numpy().astype(np.float64)
+    wg, wu, wd = h64(D_.w_gate), h64(D_.w_up), h64(D_.w_down)
+    print('[ep_share] oracle on sampled slots', flush=True)
+    y = oracle.experts_forward(xs, cnt, wg, wu, wd)
+    assert_close_rms(h64(r['y'][idx]), y, TAU, 'ep y_slot sampled', True)
+    ref = oracle.experts_backward(xs, cnt, gs, dys, wg, wu, wd)
+    assert_close_rms(h64(r['dx_slot'][idx]), ref['dx_slot'], TAU, 'ep dx_slot sampled', True)
+    assert_close_rms(r['dg'][idx].cpu().numpy(), ref['dg'], TAU, 'ep dg sampled')
+    # single units i of the largest and the smallest expert, over all their slots
+    for e in (0, cfg.E_local - 1):
+        a, b = int(off[e]), int(off[e + 1])
+        X, DY = h64(D_.x_slot[a:b]), h64(D_.dy_slot[a:b])
+        G = D_.g[a:b].cpu().numpy().astype(np.float64)
+        for i in rng.choice(cfg.I, 2, replace=False):
+            print(f'[ep_share] oracle on expert {e} unit {i} ({b - a} slots)', flush=True)
+            ru = oracle.experts_backward(X, np.array([b - a]), G, DY, wg[e:e + 1, i:i + 1], wu[e:e + 1, i:i + 1],
+                                         wd[e:e + 1, :, i:i + 1])
+            assert_close_rms(r['dw_gate'][e, i].cpu().numpy(), ru['dW_gate'][0, 0], TAU, f'ep dW_gate[{e},{i}]')
+            assert_close_rms(r['dw_up'][e, i].cpu().numpy(), ru['dW_up'][0, 0], TAU, f'ep dW_up[{e},{i}]')
+            assert_close_rms(r['dw_down'][e, :, i].cpu().numpy(), ru['dW_down'][0, :, 0], TAU, f'ep dW_down[{e},:,{i}]')
+    # shared expert: sampled rows of its output and input gradient, sampled units of its weight gradients
+    rows = np.sort(rng.choice(cfg.tokens, 4, replace=False))
+    ridx = torch.from_numpy(rows).cuda()
+    sg, su, sd = h64(D_.ws_gate), h64(D_.ws_up), h64(D_.ws_down)
+    xl, dyl = h64(D_.x_local), h64(D_.dy_local)
+    assert_close_rms(h64(r['sh'][ridx]), oracle.swiglu_expert(xl[rows], sg, su, sd), TAU, 'ep shared_out sampled',
+                     True)
+    rs = oracle.shared_backward(xl[rows], dyl[rows], sg, su, sd)
+    assert_close_rms(h64(r['dx_local'][ridx]), rs['dx'], TAU, 'ep shared dx sampled', True)
+    for i in rng.choice(cfg.I_shared, 2, replace=False):
+        ru = oracle.shared_backward(xl, dyl, sg[i:i + 1], su[i:i + 1], sd[:, i:i + 1])
+        assert_close_rms(r['dws_gate'][i].cpu().numpy(), ru['dW_gate'][0], TAU, f'ep shared dW_gate[{i}]')
+        assert_close_rms(r['dws_up'][i].cpu().numpy(), ru['dW_up'][0], TAU, f'ep shared dW_up[{i}]')
+        assert_close_rms(r['dws_down'][:, i].cpu().numpy(), ru['dW_down'][:, 0], TAU, f'ep shared dW_down[:,{i}]')
