@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA, TFLOP/s
+PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense FP8 (MX block-scaled) MFMA, TFLOP/s
 PEAK_F32_TFLOPS = 157.3         # fp32 vector
 PEAK_HBM_GBS = 8000.0           # HBM3E, GB/s
 METRIC = 'MoE layer tokens/s (fwd, fwd+bwd) on 1 MI355X; % of MFMA peak'
@@ -77,6 +78,17 @@ def stage_work(cfg, flags):
     b = 4 if cfg.dtype == 'f32' else 2
     fused = bool(flags & 1)
     w = {}
+    if cfg.dtype == 'mxfp8':
+        # routed operands E4M3 (1 byte) + one E8M0 byte per 32; activations in, outputs BF16
+        q = 1 + 1 / 32
+        w['route'] = (0.0, T * cfg.E * 4 + T * K * 8)
+        w['schedule'] = (0.0, n * 4 * 3)
+        w['shared'] = (6.0 * T * D * Is, 3 * Is * D * 2 + 2 * T * D * 2 + 2 * T * Is * 2) if Is else (0.0, 0)
+        w['dispatch'] = (0.0, T * D * 2 + n * D * q + n * 4)
+        w['up_gate'] = (4.0 * n * D * I, 2 * E * I * D * q + n * D * q + n * I * q)
+        w['down'] = (2.0 * n * I * D, E * D * I * q + n * I * q + n * D * 2 + n * 4)
+        w['combine'] = (0.0, n * D * 2 + (2 if Is else 1) * T * D * 2 + n * 4)
+        return w
     w['route'] = (0.0, T * cfg.E * 4 + T * K * 8)
     w['schedule'] = (0.0, n * 4 * 3)
     w['shared'] = (6.0 * T * D * Is, 3 * Is * D * b + 2 * T * D * b + 2 * T * Is * b) if Is else (0.0, 0)
@@ -92,7 +104,7 @@ def main():
     ap.add_argument('--gpus', type=int, default=1)
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
-    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'ep_share'])
+    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'mxfp8', 'ep_share'])
     ap.add_argument('--no-extra', action='store_true',
                     help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
@@ -114,10 +126,21 @@ def main():
     if args.workload == 'ep_share':
         print(json.dumps(bench_share(args.steps, args.warmup, args.flags)), flush=True)
         return
-    cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY}[args.workload]
+    cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
     print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
     L = synth.device_layer(cfg)
+    mx = None
+    if cfg.dtype == 'mxfp8':
+        # routed expert weights quantised on the device (E4M3 + E8M0 per 32 along K); shared stays BF16
+        mx = {}
+        for k in ('w_gate', 'w_up', 'w_down'):
+            wbf = getattr(L, k)
+            q = torch.empty(wbf.shape, dtype=torch.uint8, device='cuda')
+            sc = torch.empty(wbf.shape[:-1] + (wbf.shape[-1] // 32,), dtype=torch.uint8, device='cuda')
+            moe.quantize_mx(wbf, q, sc)
+            mx[k] = (q, sc)
+        torch.cuda.synchronize()
     T, D, K = cfg.T, cfg.D, cfg.K
     dev = 'cuda'
     p = moe.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, cfg.dtype, args.chunk_rows, 0, args.flags)
@@ -129,7 +152,11 @@ def main():
                      perm=torch.empty((T * K,), dtype=torch.int32, device=dev),
                      inv_perm=torch.empty((T * K,), dtype=torch.int32, device=dev))
     routing = moe.make_routing(**routing_t)
-    weights = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
+    if mx is None:
+        weights = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
+    else:
+        weights = moe.make_weights(mx['w_gate'][0], mx['w_up'][0], mx['w_down'][0], L.ws_gate, L.ws_up, L.ws_down,
+                                   mx['w_gate'][1], mx['w_up'][1], mx['w_down'][1])
     out = torch.empty((T, D), dtype=dt, device=dev)
     ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -175,7 +202,7 @@ def main():
 
     n = T * K
     flops = 6.0 * n * cfg.D * cfg.I + 6.0 * T * cfg.D * cfg.I_shared
-    peak = PEAK_F32_TFLOPS if cfg.dtype == 'f32' else PEAK_BF16_TFLOPS
+    peak = {'f32': PEAK_F32_TFLOPS, 'mxfp8': PEAK_MXFP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     work = stage_work(cfg, args.flags)
@@ -190,8 +217,9 @@ def main():
         roof = {'bound': 'hbm', 'achieved': b_dom / t_dom / 1e9, 'peak': PEAK_HBM_GBS, 'unit': 'GB/s'}
     roof['frac'] = roof['achieved'] / roof['peak']
     roof['traffic'] = measured_traffic(dom, args.flags, cfg.name)
-    roof['kernel'] = {'up_gate': 'gemm_bf16_kernel<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
-                      'down': 'gemm_bf16_kernel<EPI_STORE> (routed W_down + scatter)',
+    gk = 'gemm_mx_kernel' if cfg.dtype == 'mxfp8' else 'gemm_bf16_kernel'
+    roof['kernel'] = {'up_gate': f'{gk}<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
+                      'down': f'{gk}<EPI_STORE> (routed W_down + scatter)',
                       'shared': 'shared expert GEMMs', 'dispatch': 'dispatch_kernel',
                       'combine': 'combine_bf16_kernel', 'route': 'route_topk_kernel',
                       'schedule': 'sched_* kernels'}[dom]
@@ -203,7 +231,7 @@ def main():
     roof['hbm_frac'] = b_dom / t_dom / 1e9 / PEAK_HBM_GBS
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg.dtype != 'mxfp8':
         cpu = cpu_baseline(cfg, L, args.cpu_tokens)
     extra = None
     if not args.no_extra and args.workload == 'dsv3':
@@ -222,7 +250,7 @@ def main():
         'higher_is_better': True,
         'scaling': 'weak',
         'vs_baseline': None,
-        'dtype': 'bf16' if cfg.dtype != 'f32' else 'f32',
+        'dtype': {'f32': 'f32', 'mxfp8': 'mxfp8 (e4m3 + e8m0 per 32), bf16 out'}.get(cfg.dtype, 'bf16'),
         'data': 'synthetic',
         'config': {'workload': f'{cfg.name} forward', 'T': T, 'D': cfg.D, 'I': cfg.I, 'E': cfg.E, 'K': K,
                    'I_shared': cfg.I_shared, 'router': cfg.router, 'chunk_rows': args.chunk_rows,
