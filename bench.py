@@ -180,7 +180,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    # timed region: K steps of moe_forward (the shared expert overlaps the routed path on the
+    # library's side stream), bracketed by device synchronisations
+    n_attr = min(args.steps, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(n_attr)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     for e in [t_start, t_end] + [e for row in evs for e in row]:
@@ -189,13 +192,18 @@ def main():
     w0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+    # stage attribution: the same forward with HIP events between its stages (stages in order on the
+    # library's stream, no overlap), outside the timed region
+    for i in range(n_attr):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(n_attr)]))
                 for j, s in enumerate(moe.STAGES)}
     print(f'[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f}); '
           f'stages {json.dumps({k: round(v, 4) for k, v in stage_ms.items()})}', file=sys.stderr, flush=True)
@@ -230,6 +238,11 @@ def main():
     roof['mfma_frac'] = f_dom / t_dom / 1e12 / peak
     roof['hbm_frac'] = b_dom / t_dom / 1e9 / PEAK_HBM_GBS
 
+    pc = standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream) if cfg.dtype == 'bf16' else None
+
+    # per-step spread from the in-order run (sum of its stage events)
+    per_step = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(n_attr)])
+
     cpu = None
     if not args.no_cpu_baseline and cfg.dtype != 'mxfp8':
         cpu = cpu_baseline(cfg, L, args.cpu_tokens)
@@ -258,6 +271,10 @@ def main():
         'tflops': tflops,
         'mfma_peak_frac': tflops / peak,
         'stages_ms': stage_ms,
+        'stages_note': 'stage times from a separate in-order run with HIP events between stages (no overlap)',
+        'stages_sum_ms': float(sum(stage_ms.values())),
+        'in_order_step_ms_p10_p50_p90': [float(np.percentile(per_step, q)) for q in (10, 50, 90)],
+        'permute_combine_standalone': pc,
         'wall_ms_per_step': 1e3 * wall / args.steps,
         'roofline': roof,
         'cpu_baseline': cpu,
@@ -265,6 +282,39 @@ def main():
     if extra is not None:
         line['extra'] = extra
     print(json.dumps(line), flush=True)
+
+
+def standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream, reps=20):
+    """Dispatch and combine timed as standalone kernels on the full-size buffers of the workload
+    (the routing of the last forward), against HBM peak with their algorithmic bytes: dispatch
+    T*D*2 (x read once) + T*K*D*2 (slots written) + 4*T*K; combine T*K*D*2 + 2*T*D*2 + 4*T*K."""
+    import torch
+    T, D, K = cfg.T, cfg.D, cfg.K
+    n = T * K
+    xs = torch.empty((n, D), dtype=torch.bfloat16, device='cuda')
+    ys = torch.empty((n, D), dtype=torch.bfloat16, device='cuda').normal_()
+    sh = torch.empty((T, D), dtype=torch.bfloat16, device='cuda').normal_()
+    res = {}
+    for name, fn, nbytes in (
+            ('dispatch', lambda: moe.dispatch_tokens(p, L.x, routing_t['inv_perm'], xs, stream=stream),
+             T * D * 2 + n * D * 2 + 4 * n),
+            ('dispatch_slot_major', lambda: moe.dispatch(p, L.x, routing_t['perm'], 0, n, xs, stream=stream),
+             T * D * 2 + n * D * 2 + 4 * n),
+            ('combine', lambda: moe.combine(p, ys, sh, routing_t['topk_w'], out, stream=stream),
+             n * D * 2 + 2 * T * D * 2 + 4 * n)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {'ms': ms, 'algorithmic_bytes': nbytes, 'GB_s': nbytes / (ms * 1e-3) / 1e9,
+                     'hbm_frac': nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del xs, ys, sh
+    return res
 
 
 def bench_share(steps, warmup, flags):

@@ -90,6 +90,10 @@ typedef struct moe_problem {
 /* Tuning: run the bf16 grouped GEMMs with 4 wavefronts per workgroup, each owning a 128 x 128
  * block of the 256 x 256 tile, instead of 8 wavefronts of 128 x 64. Results are bitwise equal. */
 #define MOE_FLAG_GEMM_WAVES4 0x8
+/* moe_forward only: run the shared expert on a library-owned side stream (default priority, one
+ * per host thread and device, created on first use) concurrently with the routed path, joined
+ * before the combine. Results are bitwise equal to the in-order forward. */
+#define MOE_FLAG_OVERLAP_SHARED 0x10
 #define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
@@ -163,6 +167,14 @@ int moe_schedule(const moe_problem *p, const int32_t *topk_idx, int32_t *counts,
  * otherwise x_slot_scales must be NULL. */
 int moe_dispatch(const moe_problem *p, const void *x, const int32_t *perm, int64_t slot_begin,
                  int64_t slot_count, void *x_slot, uint8_t *x_slot_scales, hipStream_t stream);
+
+/* The same dispatch over all T*K slots, token-major: each token's row of x is read once and
+ * written to its K slots x_slot[inv_perm[t*K + k]] (inv_perm as produced by moe_schedule, a
+ * bijection onto [0, T*K)). Identical bytes to moe_dispatch over the whole range; this is the
+ * form moe_forward uses when it dispatches all slots at once. BF16 or f32 (MOE_MXFP8 returns
+ * MOE_ERR_UNSUPPORTED: use moe_dispatch). */
+int moe_dispatch_tokens(const moe_problem *p, const void *x, const int32_t *inv_perm, void *x_slot,
+                        hipStream_t stream);
 
 /* Deterministic combine (Blog, weighted sum after the combine; Notes "The production details"
  * on determinism): out[t] = shared_out[t] + sum_{k=0}^{K-1} topk_w[t][k] * y_routes[t*K + k],

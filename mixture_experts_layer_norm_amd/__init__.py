@@ -24,6 +24,7 @@ MOE_FLAG_FUSED_GATHER = 0x1
 MOE_FLAG_WEIGHT_MAJOR = 0x2
 MOE_FLAG_PERSISTENT = 0x4
 MOE_FLAG_GEMM_WAVES4 = 0x8
+MOE_FLAG_OVERLAP_SHARED = 0x10
 
 
 def MOE_FLAG_TILE_BLOCK(n):
@@ -34,6 +35,7 @@ STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3:
 DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
 
 EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_schedule', 'moe_dispatch',
+            'moe_dispatch_tokens',
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
@@ -76,6 +78,7 @@ _sig = {
     'moe_route_topk': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_schedule': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_dispatch': (ctypes.c_int, [_PP, _P, _P, _i64, _i64, _P, _P, _P]),
+    'moe_dispatch_tokens': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_combine': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     'moe_forward': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P, _P,
                                    _P, _sz, _P]),
@@ -147,6 +150,11 @@ def schedule(p, topk_idx, counts, offsets, perm, inv_perm, ws, stream=None):
 def dispatch(p, x, perm, slot_begin, slot_count, x_slot, x_slot_scales=None, stream=None):
     _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(perm), slot_begin, slot_count, _ptr(x_slot),
                              _ptr(x_slot_scales), _stream(stream)), 'moe_dispatch')
+
+
+def dispatch_tokens(p, x, inv_perm, x_slot, stream=None):
+    _check(_lib.moe_dispatch_tokens(ctypes.byref(p), _ptr(x), _ptr(inv_perm), _ptr(x_slot), _stream(stream)),
+           'moe_dispatch_tokens')
 
 
 def combine(p, y_routes, shared_out, topk_w, out, stream=None):

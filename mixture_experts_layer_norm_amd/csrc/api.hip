@@ -152,6 +152,16 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* perm, int64
   return launch_dispatch(x, p->dtype, perm, p->K, p->D, slot_begin, slot_count, x_slot, x_slot_scales, stream);
 }
 
+int moe_dispatch_tokens(const moe_problem* p, const void* x, const int32_t* inv_perm, void* x_slot,
+                        hipStream_t stream) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!x || !inv_perm || !x_slot) return MOE_ERR_INVALID_ARG;
+  if (p->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(x_slot)) return MOE_ERR_MISALIGNED;
+  return launch_dispatch_tokens(x, p->dtype, inv_perm, p->T, p->K, p->D, x_slot, stream);
+}
+
 int moe_combine(const moe_problem* p, const void* y_routes, const void* shared_out,
                 const float* topk_w, void* out, hipStream_t stream) {
   int st = validate_problem(p);
@@ -197,9 +207,51 @@ static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda,
   return launch_gemm_bf16(g2, grp, EPI_STORE, stream);
 }
 
-int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
-                       void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
-                       size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// A library-owned side stream (default priority) per host thread and device, with the two events
+// of a fork/join: moe_forward runs the shared expert on it while the routed path runs on the
+// caller's stream. Created on first use; kept for the life of the process.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+thread_local SideStream t_side[kMaxDevices];
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = t_side[dev];
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) { ss.s = nullptr; return nullptr; }
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+  }
+  return &ss;
+}
+
+// Makes `main` wait for the side stream's work on every exit once armed (also error returns).
+struct Join {
+  hipStream_t main = nullptr;
+  hipEvent_t ev = nullptr;
+  ~Join() { wait(); }
+  int wait() {
+    if (!ev) return MOE_OK;
+    hipEvent_t e = ev;
+    ev = nullptr;
+    return hipStreamWaitEvent(main, e, 0) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+};
+}  // namespace
+
+// The forward. With a side stream (moe_forward) the shared expert runs concurrently with the
+// routed path; without one (moe_forward_stages) everything is in order on `stream`.
+static int forward_impl(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
+                        void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
+                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, SideStream* side) {
   int st = validate_routing(p);
   if (st) return st;
   if (!x || !logits || !w || !out || !r) return MOE_ERR_INVALID_ARG;
@@ -230,13 +282,25 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
 
   // shared expert first: it does not depend on the schedule
   MOE_MARK(MOE_STAGE_SHARED);
+  Join join;
   if (p->I_shared > 0) {
     Grouped gs;
     gs.M = p->T;
     gs.nblk = tile_block_of(p->flags);
     gs.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
+    hipStream_t shs = stream;
+    if (side) {
+      if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+        return MOE_ERR_HIP;
+      shs = side->s;
+    }
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
-                    0, 0, wsb + L.sh_h, sho, nullptr, stream);
+                    0, 0, wsb + L.sh_h, sho, nullptr, shs);
+    if (side) {
+      if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_ERR_HIP;
+      join.main = stream;
+      join.ev = side->join;
+    }
     if (st) return st;
   }
 
@@ -279,6 +343,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
     MOE_MARK(MOE_STAGE_UP_GATE);
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_MARK(MOE_STAGE_COMBINE);
+    if ((st = join.wait())) return st;
     st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_COUNT);
@@ -310,7 +375,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
     const void* A = x;
     const int32_t* gather = r->perm;
     if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
-      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream);
+      st = launch_dispatch_tokens(x, p->dtype, r->inv_perm, p->T, p->K, p->D, wsb + L.x_slot, stream);
       if (st) return st;
       A = wsb + L.x_slot;
       gather = nullptr;
@@ -322,6 +387,7 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
     if (st) return st;
   }
   MOE_MARK(MOE_STAGE_COMBINE);
+  if ((st = join.wait())) return st;
   st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
   if (st) return st;
   MOE_MARK(MOE_STAGE_COUNT);
@@ -329,10 +395,19 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
   return MOE_OK;
 }
 
+extern "C" {
+
 int moe_forward(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                 void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
-  return moe_forward_stages(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream);
+  SideStream* side = (p && p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED)) ? side_stream() : nullptr;
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side);
+}
+
+int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
+                       void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
+                       size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, ev, stream, nullptr);
 }
 
 }  // extern "C"

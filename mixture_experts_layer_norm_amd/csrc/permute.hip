@@ -74,7 +74,16 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const uint4* __restrict__
   const int64_t src = perm[begin + j] / K;
   const uint4* s = x + src * chunks_per_row;
   uint4* d = out + j * chunks_per_row;
-  for (int c = lane; c < chunks_per_row; c += 64) d[c] = s[c];
+  // 8 loads in flight per lane before their stores (a D = 7168 row is 14 chunks per lane)
+  int c = lane;
+  for (; c + 7 * 64 < chunks_per_row; c += 8 * 64) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s[c + u * 64];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) d[c + u * 64] = v[u];
+  }
+  for (; c < chunks_per_row; c += 64) d[c] = s[c];
 }
 
 // MXFP8 dispatch: one lane per 32-element block of the row.
@@ -109,6 +118,44 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(const uint16_t* __rest
   }
 }
 
+// Token-major dispatch of the whole routed range: one wavefront per token reads its row of x once
+// and writes it to the token's K slots inv_perm[t*K + k] (the same bytes as the slot-major gather,
+// with x read from HBM once instead of once per route).
+__global__ __launch_bounds__(256) void dispatch_tokens_kernel(const uint4* __restrict__ x,
+                                                              const int32_t* __restrict__ inv_perm, int T, int K,
+                                                              int chunks_per_row, uint4* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint4* s = x + (int64_t)t * chunks_per_row;
+  const int32_t* slots = inv_perm + (int64_t)t * K;
+  int c = lane;
+  for (; c + 7 * 64 < chunks_per_row; c += 8 * 64) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s[c + u * 64];
+    for (int k = 0; k < K; ++k) {
+      uint4* d = out + (int64_t)slots[k] * chunks_per_row;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) d[c + u * 64] = v[u];
+    }
+  }
+  for (; c < chunks_per_row; c += 64) {
+    const uint4 v = s[c];
+    for (int k = 0; k < K; ++k) out[(int64_t)slots[k] * chunks_per_row + c] = v;
+  }
+}
+
+int launch_dispatch_tokens(const void* x, int dtype, const int32_t* inv_perm, int T, int K, int D, void* x_slot,
+                           hipStream_t s) {
+  if (T <= 0) return MOE_OK;
+  const int cpr = (int)(D * elt_bytes(dtype) / 16);
+  hipLaunchKernelGGL(dispatch_tokens_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, (const uint4*)x,
+                     inv_perm, T, K, cpr, (uint4*)x_slot);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D, int64_t begin,
                     int64_t count, void* x_slot, uint8_t* x_slot_sc, hipStream_t s) {
   if (count <= 0) return MOE_OK;
@@ -128,11 +175,16 @@ int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D,
 // ---------------------------------------------------------------------------------------------
 // combine: out[t] = shared[t] + sum_k w[t,k] * y[t*K+k], fp32, k ascending, one rounding
 // ---------------------------------------------------------------------------------------------
+// One wavefront per token, 8 columns per lane at a time. KC > 0: K = KC known at compile time, so
+// the K row loads of a chunk are issued together; KC = 0: any K. Same sum order either way
+// (shared output first, then k ascending, fp32, one rounding).
+template <int KC>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ y,
                                                            const uint16_t* __restrict__ sh,
                                                            const float* __restrict__ w,
                                                            uint16_t* __restrict__ out, int T,
-                                                           int K, int D) {
+                                                           int K_, int D) {
+  const int K = KC > 0 ? KC : K_;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -151,6 +203,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
+#pragma unroll
     for (int k = 0; k < K; ++k) {
       const float g = w[(size_t)t * K + k];
       uint4 u = reinterpret_cast<const uint4*>(y + ((size_t)t * K + k) * D)[c];
@@ -188,8 +241,17 @@ int launch_combine(const void* y_routes, const void* shared_out, const float* to
     hipLaunchKernelGGL(combine_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (const float*)y_routes, (const float*)shared_out, topk_w, (float*)out, T, K, D);
   } else {
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3((T + 3) / 4), dim3(256), 0, s, (const uint16_t*)y_routes,
-                       (const uint16_t*)shared_out, topk_w, (uint16_t*)out, T, K, D);
+    const dim3 grid((T + 3) / 4), block(256);
+    const uint16_t* yr = (const uint16_t*)y_routes;
+    const uint16_t* sh = (const uint16_t*)shared_out;
+    uint16_t* o = (uint16_t*)out;
+    switch (K) {
+      case 8: hipLaunchKernelGGL(combine_bf16_kernel<8>, grid, block, 0, s, yr, sh, topk_w, o, T, K, D); break;
+      case 6: hipLaunchKernelGGL(combine_bf16_kernel<6>, grid, block, 0, s, yr, sh, topk_w, o, T, K, D); break;
+      case 4: hipLaunchKernelGGL(combine_bf16_kernel<4>, grid, block, 0, s, yr, sh, topk_w, o, T, K, D); break;
+      case 2: hipLaunchKernelGGL(combine_bf16_kernel<2>, grid, block, 0, s, yr, sh, topk_w, o, T, K, D); break;
+      default: hipLaunchKernelGGL(combine_bf16_kernel<0>, grid, block, 0, s, yr, sh, topk_w, o, T, K, D); break;
+    }
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

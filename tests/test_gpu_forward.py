@@ -91,9 +91,11 @@ def test_forward_bitwise_deterministic(m):
         assert torch.equal(run.out, ref)
 
 
-def test_dispatch_standalone(m):
-    """moe_dispatch copies rows x[perm[j] / K] exactly (perm from the oracle's schedule)."""
-    cfg = SMALL_BF16
+@pytest.mark.parametrize('D', [256, 4096, 7168])
+def test_dispatch_standalone(m, D):
+    """moe_dispatch copies rows x[perm[j] / K] exactly (perm from the oracle's schedule); rows of
+    4096 and 7168 columns take the 8-loads-in-flight loop plus its tail."""
+    cfg = synth.scaled(SMALL_BF16, f'dispatch_D{D}', D=D)
     H = synth.host_layer(cfg)
     _, _, perm, _ = oracle.schedule(oracle.route_topk(H.logits, cfg.K), cfg.E)
     p = m.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, cfg.dtype)
@@ -106,17 +108,26 @@ def test_dispatch_standalone(m):
         torch.cuda.synchronize()
         if count:
             assert np.array_equal(t2np(x_slot[:count]), H.x[perm[begin:begin + count] // cfg.K])
+    # token-major form over the whole range: same bytes
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(n, dtype=perm.dtype)
+    x_tok = torch.empty((n, cfg.D), dtype=torch.bfloat16, device='cuda')
+    m.dispatch_tokens(p, x, torch.from_numpy(inv).cuda(), x_tok)
+    torch.cuda.synchronize()
+    assert np.array_equal(t2np(x_tok), H.x[perm // cfg.K])
 
 
-@pytest.mark.parametrize('dtype,shared', [('bf16', True), ('bf16', False), ('f32', True)])
-def test_combine_standalone(m, dtype, shared):
-    """moe_combine against the oracle's weighted sum, on seeded per-route rows and weights."""
-    T, K, D = 333, 6, 256
+@pytest.mark.parametrize('dtype,shared,K,D', [('bf16', True, 6, 256), ('bf16', False, 6, 256), ('f32', True, 6, 256),
+                                             ('bf16', True, 12, 256), ('bf16', True, 8, 4096)])
+def test_combine_standalone(m, dtype, shared, K, D):
+    """moe_combine against the oracle's weighted sum, on seeded per-route rows and weights (K <= 8
+    keeps the weights in registers; K > 8 takes the general loop)."""
+    T = 333
     bf = dtype == 'bf16'
     y = synth.host_normal(77, 0, (T * K, D), 1.0, bf16=bf)
     sh = synth.host_normal(77, 1, (T, D), 1.0, bf16=bf) if shared else None
     g = synth.host_rng(77, 2).random((T, K), dtype=np.float32)
-    p = m.problem(T, D, 128, 8, K, 128 if shared else 0, dtype)
+    p = m.problem(T, D, 128, 16, K, 128 if shared else 0, dtype)
     tdt = torch.bfloat16 if bf else torch.float32
     yd = torch.from_numpy(y).cuda().to(tdt)
     shd = torch.from_numpy(sh).cuda().to(tdt) if shared else None
@@ -211,3 +222,23 @@ def test_tile_order_bitwise(m, order):
     torch.cuda.synchronize()
     assert torch.equal(a.out, b.out) and torch.equal(a.y_routes, b.y_routes)
     assert torch.equal(a.shared_out, b.shared_out)
+
+
+def test_forward_overlapped_shared_equals_in_order(m):
+    """moe_forward with MOE_FLAG_OVERLAP_SHARED runs the shared expert on the library's side stream,
+    concurrently with the routed path; moe_forward_stages runs every stage in order. Both give the same bits, also when the
+    side stream's previous work and the caller's stream interleave over several calls."""
+    L = synth.to_device(synth.host_layer(SMALL_BF16))
+    a = ForwardRun(m, L, flags=m.MOE_FLAG_OVERLAP_SHARED)
+    b = ForwardRun(m, L)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(len(m.STAGES) + 1)]
+    for e in events:
+        e.record()
+    outs = []
+    for _ in range(3):
+        a()
+        m.forward_stages(b.p, L.x, L.logits, b.weights, b.out, b.routing, b.ws, events, b.y_routes, b.shared_out)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out, b.out) and torch.equal(a.shared_out, b.shared_out)
+        outs.append(a.out.clone())
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
