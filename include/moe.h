@@ -94,6 +94,9 @@ typedef struct moe_problem {
  * per host thread and device, created on first use) concurrently with the routed path, joined
  * before the combine. Results are bitwise equal to the in-order forward. */
 #define MOE_FLAG_OVERLAP_SHARED 0x10
+/* Tuning: forward bf16 GEMMs with K slices 32 wide in 4 LDS stages instead of the default 64
+ * wide in 2. Results are bitwise equal. */
+#define MOE_FLAG_GEMM_BK32 0x20
 #define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */

@@ -25,6 +25,7 @@ MOE_FLAG_WEIGHT_MAJOR = 0x2
 MOE_FLAG_PERSISTENT = 0x4
 MOE_FLAG_GEMM_WAVES4 = 0x8
 MOE_FLAG_OVERLAP_SHARED = 0x10
+MOE_FLAG_GEMM_BK32 = 0x20
 
 
 def MOE_FLAG_TILE_BLOCK(n):

@@ -288,6 +288,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     gs.M = p->T;
     gs.nblk = tile_block_of(p->flags);
     gs.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
+    gs.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
     hipStream_t shs = stream;
     if (side) {
       if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
@@ -311,6 +312,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
   gr.nblk = tile_block_of(p->flags);
   gr.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
+  gr.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
   if (L.pipelined) {
     // Chunks of b routed slots through a ring of S stages, each carried through dispatch, up/gate
     // and down before the next; all tile bookkeeping is on the device (no host synchronisation).
@@ -336,6 +338,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
       gc.nblk = tile_block_of(p->flags);
       gc.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
+      gc.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
       st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
                       p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream);
       if (st) return st;

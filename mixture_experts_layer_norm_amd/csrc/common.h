@@ -121,6 +121,7 @@ struct Grouped {
   // n-tile count is plain m-tile major, nblk = 1 n-tile major (0 means m-tile major too).
   int32_t nblk = 0;
   int32_t waves4 = 0;         // bf16 GEMM workgroups of 4 wavefronts x (128 x 128) instead of 8 x (128 x 64)
+  int32_t bk32 = 0;           // bf16 GEMM K slices 32 wide in 4 LDS stages instead of 64 wide in 2
 };
 
 // EPI_SWIGLU:   h = SiLU(gate) * up                       -> C

@@ -30,8 +30,9 @@ namespace moe {
 // wavefront owns a 128 x WN block as (128/32) x (WN/32) v_mfma_f32_32x32x16_bf16 accumulators.
 // Row blocks of 32 that lie past the group's last row skip their MFMAs (a wave-uniform branch),
 // so a sparsely filled tile costs only the streaming of its weight tile.
-template <int EPI, bool KG, int WN, int WAVES_N>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g, int ntn, int mtn) {
+  constexpr int BK = SliceCfg<BKE>::BK;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems];
   // The grid is an upper bound (grouped tile counts are known only on the device); the valid
   // tiles are split evenly over the 8 XCDs, each taking a contiguous range of them.
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
     nk = a.K / BK;
   }
 
-  gemm_tile<EPI, KG, WN, WAVES_N>(a, tc, k0, nk, ntn, smem);
+  gemm_tile<EPI, KG, WN, WAVES_N, BKE>(a, tc, k0, nk, ntn, smem);
 }
 
 static int64_t grid_blocks(int64_t mtiles, int ntn) {
@@ -117,18 +118,27 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
     // 4 wavefronts (2 x 2), each a 128 x 128 block: 256 accumulators per lane, one wave per SIMD
     dim3 block(256);
     switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, 128, 2>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, 128, 2>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, 128, 2>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, 128, 2>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+    }
+  } else if (!g.bk32) {
+    // 64-wide K slices in 2 LDS stages (the default; measured faster than 32 x 4 here)
+    dim3 block(512);
+    switch (epi) {
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
     }
   } else {
     dim3 block(512);
     switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
+      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
     }
   }
   MOE_LAUNCH_CHECK();
@@ -143,7 +153,7 @@ int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s) {
   g.groups = groups;
   const int64_t nb = grid_blocks((int64_t)groups * mtn, ntn);
   if (nb == 0) return MOE_OK;
-  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, true, kWN, 4>), dim3((unsigned)nb), dim3(512), 0, s, a, g, ntn, mtn);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, true, kWN, 4, 64>), dim3((unsigned)nb), dim3(512), 0, s, a, g, ntn, mtn);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -3,11 +3,13 @@
 //
 // Operand staging: global_load_lds_dwordx4 copies 16 bytes per lane from HBM straight into LDS
 // (no register staging, no LDS store instructions). One such instruction of a wavefront fills
-// 1 KB of LDS in lane order, i.e. 16 rows of one 32-wide K slice (64 B per row). LDS holds
-// STAGES such slices of the 256 A rows and 256 B rows; loads run STAGES - 1 slices ahead of the
-// MFMAs. Within a row the four 16-byte chunks are stored XOR-swizzled (chunk c of row r at
-// position c ^ f(r), f(r) = (r >> 2) & 3), which keeps the fragment reads free of LDS bank
-// conflicts.
+// 1 KB of LDS in lane order, i.e. 1024 / ROWB rows of one K slice. Two slice shapes (SliceCfg):
+// 32-wide slices (64 B rows) in 4 LDS stages, loads 3 slices ahead of the MFMAs, or 64-wide
+// slices (128 B rows) in 2 stages, loads 1 slice ahead; both 128 KB of LDS for the 256 A rows
+// and 256 B rows. Within a row the 16-byte chunks are stored XOR-swizzled (chunk c of row r at
+// position c ^ f(r)), with f chosen by measured LDS bank conflicts on gfx950 for this kernel's
+// fragment-read pattern: (r >> 2) & 3 for 64 B rows, (r >> 1) & 7 for 128 B rows (both read
+// conflict-free; e.g. ((r >> 1) ^ (r >> 3)) & 3 or no swizzle do not).
 #pragma once
 #include "common.h"
 
@@ -15,14 +17,26 @@ namespace moe {
 
 namespace gemm_detail {
 constexpr int BM = kGemmBM;                 // 256 rows per m-tile (and 256 B rows per tile)
-constexpr int BK = 32;                      // K elements per stage
-constexpr int STAGES = 4;                   // LDS stages (loads run STAGES - 1 ahead)
-constexpr int ROWB = BK * 2;                // bytes per staged row
-constexpr int STAGE_BYTES = 2 * BM * ROWB;  // A rows, then B rows
+
+// Shape of one staged K slice: BKE bf16 per row.
+template <int BKE>
+struct SliceCfg {
+  static_assert(BKE == 32 || BKE == 64, "32- or 64-wide K slices");
+  static constexpr int BK = BKE;                      // K elements per slice
+  static constexpr int STAGES = BKE == 32 ? 4 : 2;    // LDS stages (loads run STAGES - 1 ahead)
+  static constexpr int ROWB = BKE * 2;                // bytes per staged row
+  static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;             // rows filled by one wavefront load
+  static constexpr int KSTEPS = BKE / 16;             // MFMA K steps per slice
+  static constexpr int STAGE_BYTES = 2 * BM * ROWB;   // A rows, then B rows
+  __device__ static __forceinline__ int swz(int row) { return BKE == 32 ? (row >> 2) & 3 : (row >> 1) & 7; }
+};
+constexpr int BK = 32;                      // default slice width (K multiples the callers use)
 }  // namespace gemm_detail
 
-// LDS of one tile: STAGES x (256 A rows + 256 B rows) x 64 bytes = 128 KB
-constexpr int kGemmSmemElems = gemm_detail::STAGES * gemm_detail::STAGE_BYTES / 2;
+// LDS of one tile: 128 KB for either slice shape
+constexpr int kGemmSmemElems = 4 * gemm_detail::SliceCfg<32>::STAGE_BYTES / 2;
+static_assert(4 * gemm_detail::SliceCfg<32>::STAGE_BYTES == 2 * gemm_detail::SliceCfg<64>::STAGE_BYTES, "");
 
 struct TileCoord {
   int grp, r0, rows, nt;
@@ -71,58 +85,56 @@ struct StageSrc {
 };
 
 // Issues the 2 NL LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
-// 16 (NL wave + j) .. + 15 and the same B rows, for j < NL (NL = 16 / wavefronts).
-template <int NL>
+// RPI (NL wave + j) .. + RPI - 1 and the same B rows, for j < NL.
+template <int NL, int BKE>
 __device__ __forceinline__ void stage_issue(const StageSrc<NL>& s, int kt, uint8_t* smem, int stage, int wave) {
+  using C = SliceCfg<BKE>;
   const bool second = kt >= s.nk1;
-  const int ko = (second ? kt - s.nk1 : kt) * BK;
+  const int ko = (second ? kt - s.nk1 : kt) * C::BK;
   const uint16_t* ab = (second ? s.abase + s.a_shift : s.abase) + ko;
   const int64_t bsh = (second ? s.b_shift : 0) + ko;
-  uint8_t* base = smem + stage * STAGE_BYTES + wave * (NL * 1024);
+  uint8_t* base = smem + stage * C::STAGE_BYTES + wave * (NL * 1024);
 #pragma unroll
   for (int j = 0; j < NL; ++j)
     __builtin_amdgcn_global_load_lds((const void*)(ab + s.aoff[j]), (lds_void*)(base + j * 1024), 16, 0, 0);
 #pragma unroll
   for (int j = 0; j < NL; ++j)
     __builtin_amdgcn_global_load_lds((const void*)((s.bup[j] ? s.bbase[1] : s.bbase[0]) + bsh + s.boff[j]),
-                                     (lds_void*)(base + BM * ROWB + j * 1024), 16, 0, 0);
+                                     (lds_void*)(base + BM * C::ROWB + j * 1024), 16, 0, 0);
 }
 
-// XOR swizzle of the 16-byte chunks of a staged row. Chosen by measurement on gfx950 (LDS bank
-// conflict counter over this kernel's fragment-read pattern): (r >> 2) & 3 reads conflict-free,
-// where ((r >> 1) ^ (r >> 3)) & 3 or no swizzle do not.
-__device__ __forceinline__ int chunk_swz(int row) { return (row >> 2) & 3; }
 
 // Fragments of one K slice for this wave: its first NACT row blocks of A and its NJ column
 // blocks of B, for the two 16-wide K steps of the slice.
-template <int NACT, int NJ>
+template <int NACT, int NJ, int KS>
 struct Frags {
-  bf16x8 a[2][NACT > 0 ? NACT : 1];
-  bf16x8 b[2][NJ];
+  bf16x8 a[KS][NACT > 0 ? NACT : 1];
+  bf16x8 b[KS][NJ];
 };
 
 // Reads the fragments of one LDS stage. a_rd / b_rd: byte offsets of this lane's row; sw: its
 // chunk swizzle; half: which 8 of the 16 K values of an MFMA step the lane supplies.
-template <int NACT, int NJ>
+template <int NACT, int NJ, int BKE>
 __device__ __forceinline__ void frag_read(const uint8_t* st, int a_rd, int b_rd, int sw, int half,
-                                          Frags<NACT, NJ>& f) {
+                                          Frags<NACT, NJ, SliceCfg<BKE>::KSTEPS>& f) {
+  using C = SliceCfg<BKE>;
   const uint8_t* As = st + a_rd;
-  const uint8_t* Bs = st + BM * ROWB + b_rd;
+  const uint8_t* Bs = st + BM * C::ROWB + b_rd;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
     const int c = ((kk * 2 + half) ^ sw) * 16;
 #pragma unroll
-    for (int i = 0; i < NACT; ++i) f.a[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * ROWB + c);
+    for (int i = 0; i < NACT; ++i) f.a[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * C::ROWB + c);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) f.b[kk][j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * ROWB + c);
+    for (int j = 0; j < NJ; ++j) f.b[kk][j] = *reinterpret_cast<const bf16x8*>(Bs + j * 32 * C::ROWB + c);
   }
 }
 
-// MFMAs of one K slice: NACT x NJ blocks of 32 x 32 over two 16-wide K steps.
-template <int MI, int NJ, int NACT>
-__device__ __forceinline__ void frag_mfma(const Frags<NACT, NJ>& f, f32x16 (&acc)[MI][NJ]) {
+// MFMAs of one K slice: NACT x NJ blocks of 32 x 32 over the slice's 16-wide K steps.
+template <int MI, int NJ, int NACT, int KS>
+__device__ __forceinline__ void frag_mfma(const Frags<NACT, NJ, KS>& f, f32x16 (&acc)[MI][NJ]) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
     for (int i = 0; i < NACT; ++i)
 #pragma unroll
@@ -154,38 +166,41 @@ __device__ __forceinline__ void slice_barrier() {
 // of slice kt - 1), the stage of slice kt - 1 is refilled with slice kt + STAGES - 1, then the
 // fragments of slice kt are read and multiplied. NACT (active row blocks of this wave) is a
 // compile-time constant so that the loop has no divergent branches around the MFMAs.
-template <int MI, int NJ, int NACT, int NL>
+template <int MI, int NJ, int NACT, int NL, int BKE>
 __device__ __forceinline__ void k_loop(const StageSrc<NL>& src, uint8_t* sm, int nk, int wave, int a_rd,
                                        int b_rd, int sw, int half, f32x16 (&acc)[MI][NJ]) {
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) stage_issue(src, s, sm, s, wave);
+  using C = SliceCfg<BKE>;
+  constexpr int ST = C::STAGES;
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) stage_issue<NL, BKE>(src, s, sm, s, wave);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_slices<NL>(min(STAGES - 2, nk - 1 - kt));
+    wait_slices<NL>(min(ST - 2, nk - 1 - kt));
     slice_barrier();
-    if (kt + STAGES - 1 < nk) stage_issue(src, kt + STAGES - 1, sm, (kt + STAGES - 1) % STAGES, wave);
-    Frags<NACT, NJ> f;
-    frag_read<NACT, NJ>(sm + (kt % STAGES) * STAGE_BYTES, a_rd, b_rd, sw, half, f);
+    if (kt + ST - 1 < nk) stage_issue<NL, BKE>(src, kt + ST - 1, sm, (kt + ST - 1) % ST, wave);
+    Frags<NACT, NJ, C::KSTEPS> f;
+    frag_read<NACT, NJ, BKE>(sm + (kt % ST) * C::STAGE_BYTES, a_rd, b_rd, sw, half, f);
     // every fragment read of the slice ahead of its MFMAs: one LDS latency per slice
     __builtin_amdgcn_sched_barrier(0);
-    frag_mfma<MI, NJ, NACT>(f, acc);
+    frag_mfma<MI, NJ, NACT, C::KSTEPS>(f, acc);
   }
 }
 
 // Computes one workgroup tile: rows tc.r0 .. tc.r0 + tc.rows - 1 of group tc.grp, n-tile tc.nt,
 // K slices [k0, k0 + 32 nk) (times two with a.two_pass). smem holds kGemmSmemElems bf16.
-template <int EPI, bool KG, int WN, int WAVES_N>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc, int k0, int nk, int ntn,
                                           uint16_t* smem) {
+  using C = SliceCfg<BKE>;
   constexpr int WM = 128, BN = WAVES_N * WN;
-  constexpr int NWAVES = 2 * WAVES_N, NL = 16 / NWAVES;   // wavefronts; loads per operand per slice
+  constexpr int NWAVES = 2 * WAVES_N, NL = BM / (C::RPI * NWAVES);   // wavefronts; loads per operand per slice
   constexpr int MI = WM / 32, NJ = WN / 32;
   static_assert(BN == BM, "A and B stages have the same row count");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   uint8_t* sm = reinterpret_cast<uint8_t*>(smem);
 
-  // This lane's loads: row 16 (NL wave + j) + lane / 4 of A and of B, chunk position lane % 4
-  // holding logical chunk (lane % 4) ^ f(row).
+  // This lane's loads: row RPI (NL wave + j) + lane / CPR of A and of B, chunk position lane % CPR
+  // holding logical chunk (lane % CPR) ^ f(row).
   StageSrc<NL> src;
   src.abase = (const uint16_t*)a.A + k0;
   src.bbase[0] = (const uint16_t*)a.B + (KG ? 0 : (int64_t)tc.grp * a.b_group_stride) + k0;
@@ -194,8 +209,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
                      : src.bbase[0];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    const int rr = 16 * (NL * wave + j) + (lane >> 2);
-    const int ch = (lane & 3) ^ chunk_swz(rr);
+    const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;
+    const int ch = (lane % C::CPR) ^ C::swz(rr);
     const int r = tc.r0 + min(rr, tc.rows - 1);
     const int64_t srow = (!KG && a.a_gather) ? (int64_t)(a.a_gather[r] / a.a_div) : (int64_t)r;
     src.aoff[j] = (uint32_t)(srow * a.lda + ch * 8);
@@ -226,9 +241,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int a_rd = (wm * WM + (lane & 31)) * ROWB;
-  const int b_rd = (wn * WN + (lane & 31)) * ROWB;
-  const int sw = chunk_swz(lane & 31), half = lane >> 5;
+  const int a_rd = (wm * WM + (lane & 31)) * C::ROWB;
+  const int b_rd = (wn * WN + (lane & 31)) * C::ROWB;
+  const int sw = C::swz(lane & 31), half = lane >> 5;
 
   static_assert(4 * NL <= 63, "vmcnt range");
   // wave-uniform count of this wave's row blocks that hold a valid row
@@ -236,11 +251,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
   static_assert(MI == 4, "row-block dispatch below assumes 4 row blocks per wave");
   switch (nact) {
-    case 0: k_loop<MI, NJ, 0, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 1: k_loop<MI, NJ, 1, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 2: k_loop<MI, NJ, 2, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 3: k_loop<MI, NJ, 3, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    default: k_loop<MI, NJ, 4, NL>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 0: k_loop<MI, NJ, 0, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 1: k_loop<MI, NJ, 1, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 2: k_loop<MI, NJ, 2, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 3: k_loop<MI, NJ, 3, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    default: k_loop<MI, NJ, 4, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
   }
   __syncthreads();
 

@@ -126,13 +126,13 @@ __global__ __launch_bounds__(512, 1) void pipeline_kernel(PipeArgs p) {
       if (kind == 0) {
         a.A = p.x; a.lda = p.D; a.B = p.sg; a.B2 = p.su; a.ldb = p.D; a.N = p.Is; a.K = p.D;
         a.C = p.sh_h; a.ldc = p.Is;
-        gemm_tile<EPI_SWIGLU, false, 64, 4>(a, tc, 0, p.D / BK, ntn, smem);
+        gemm_tile<EPI_SWIGLU, false, 64, 4, 32>(a, tc, 0, p.D / BK, ntn, smem);
         signal_done(sh1cnt);
       } else {
         wait_geq(sh1cnt, p.n_sh1, p.err);
         a.A = p.sh_h; a.lda = p.Is; a.B = p.sd; a.ldb = p.Is; a.N = p.D; a.K = p.Is; a.C = p.sh_out;
         a.ldc = p.D;
-        gemm_tile<EPI_STORE, false, 64, 4>(a, tc, 0, p.Is / BK, ntn, smem);
+        gemm_tile<EPI_STORE, false, 64, 4, 32>(a, tc, 0, p.Is / BK, ntn, smem);
         __syncthreads();
       }
     } else if (kind == 2) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(512, 1) void pipeline_kernel(PipeArgs p) {
       GemmArgs a;
       a.A = p.x_ring + ring0 * p.D; a.lda = p.D; a.B = p.wg; a.B2 = p.wu; a.ldb = p.D;
       a.b_group_stride = (int64_t)p.I * p.D; a.N = p.I; a.K = p.D; a.C = p.h_ring + ring0 * p.I; a.ldc = p.I;
-      gemm_tile<EPI_SWIGLU, false, 64, 4>(a, tc, 0, p.D / BK, p.ntn1, smem);
+      gemm_tile<EPI_SWIGLU, false, 64, 4, 32>(a, tc, 0, p.D / BK, p.ntn1, smem);
       signal_done(g1cnt + c);
     } else {
       // down tile of chunk c, rows scattered to their route ids
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(512, 1) void pipeline_kernel(PipeArgs p) {
       GemmArgs a;
       a.A = p.h_ring + ring0 * p.I; a.lda = p.I; a.B = p.wd; a.ldb = p.I; a.b_group_stride = (int64_t)p.D * p.I;
       a.N = p.D; a.K = p.I; a.C = p.y; a.ldc = p.D; a.c_scatter = p.perm;
-      gemm_tile<EPI_STORE, false, 64, 4>(a, tc, 0, p.I / BK, p.ntn2, smem);
+      gemm_tile<EPI_STORE, false, 64, 4, 32>(a, tc, 0, p.I / BK, p.ntn2, smem);
       signal_done(g2cnt + c);
     }
   }

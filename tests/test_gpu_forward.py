@@ -206,14 +206,16 @@ def test_chunked_ring_mid_parity(m):
     check_forward(m, synth.MID, chunk_rows=512)
 
 
-@pytest.mark.parametrize('order', ['weight_major', 'block1', 'block3', 'block255', 'waves4', 'waves4_block2'])
+@pytest.mark.parametrize('order', ['weight_major', 'block1', 'block3', 'block255', 'waves4', 'waves4_block2', 'bk32',
+                                   'bk32_block2'])
 def test_tile_order_bitwise(m, order):
     """The order of the grouped GEMM tiles inside an expert and the wavefront layout of a tile
     change only the schedule, not the bits."""
     flags = {'weight_major': m.MOE_FLAG_WEIGHT_MAJOR, 'block1': m.MOE_FLAG_TILE_BLOCK(1),
              'block3': m.MOE_FLAG_TILE_BLOCK(3), 'block255': m.MOE_FLAG_TILE_BLOCK(255),
              'waves4': m.MOE_FLAG_GEMM_WAVES4,
-             'waves4_block2': m.MOE_FLAG_GEMM_WAVES4 | m.MOE_FLAG_TILE_BLOCK(2)}[order]
+             'waves4_block2': m.MOE_FLAG_GEMM_WAVES4 | m.MOE_FLAG_TILE_BLOCK(2), 'bk32': m.MOE_FLAG_GEMM_BK32,
+             'bk32_block2': m.MOE_FLAG_GEMM_BK32 | m.MOE_FLAG_TILE_BLOCK(2)}[order]
     # 4 n-tiles in both GEMMs, about 2 m-tiles per expert
     L = synth.to_device(synth.host_layer(synth.scaled(SMALL_BF16, 'order_T2000_D1024_I512', T=2000, D=1024,
                                                       I=512)))
