@@ -8,22 +8,18 @@
 //   up/gate:  h = SiLU(X W_gate^T) (*) (X W_up^T), quantised to MXFP8 along I in the epilogue
 //   down:     y = h W_down^T (bf16), row j stored at c_scatter[j]
 //
-// Tiling matches the BF16 kernel byte for byte: 256 rows x 256 weight rows, a K step of 128 fp8
-// values (128 bytes per row, LDS rows padded by 16 B), 8 wavefronts of 128 x 64, and two scaled
-// MFMAs (K = 64 each) per K step. Operand layout of the scaled 32x32x64 MFMA (lane l, lane group
-// q = l / 32, row or column l % 32): bytes 0-15 of a lane's 32 hold K block 0 of the instruction
-// and bytes 16-31 K block 1 (32 values each); lane group q supplies K values [16q, 16q+16) of each
-// block and the E8M0 scale of block q. Scales are loaded per lane straight from global memory
-// (4 bytes = the 4 blocks of one row and K step) and the lane's byte is shifted into place.
-#include "common.h"
+// Tiling matches the BF16 kernel byte for byte: 256 rows x 256 weight rows, 8 wavefronts of
+// 128 x 64, and the same LDS staging (gemm_tile.h): a K slice of 128 fp8 values is a 128-byte row,
+// copied from HBM straight into LDS (global_load_lds_dwordx4), 2 stages, chunks swizzled by
+// (r >> 1) & 7; two scaled MFMAs (K = 64 each) per slice. Operand layout of the scaled 32x32x64
+// MFMA (lane l, lane group q = l / 32, row or column l % 32): bytes 0-15 of a lane's 32 hold K
+// block 0 of the instruction and bytes 16-31 K block 1 (32 values each); lane group q supplies K
+// values [16q, 16q+16) of each block and the E8M0 scale of block q. Scale words (4 bytes = the 4
+// blocks of one row and slice) are loaded per lane from global memory with the slice's copy, and
+// the lane's byte is shifted into place.
+#include "gemm_tile.h"
 
 namespace moe {
-
-namespace {
-constexpr int BM = kGemmBM;   // 256
-constexpr int BKB = 128;      // K step in fp8 elements (= bytes)
-constexpr int PITCH = BKB + 16;
-}  // namespace
 
 __device__ __forceinline__ bool locate_tile_mx(const Grouped& g, int mt, int& grp, int& r0, int& rows) {
   if (g.row_off) {
@@ -60,17 +56,81 @@ __device__ __forceinline__ uint32_t e4m3_code_scaled(float v, float inv_scale) {
   return sign | (uint32_t)code;
 }
 
+// The K loop of an MX tile: 2 LDS stages; in step kt, once slice kt and its scale words have
+// landed and the barrier has made every thread's copies visible, slice kt + 1 and its scale words
+// are issued and the two scaled MFMAs of slice kt run for this wave's first NACT row blocks.
+template <int EPI, int NACT, int NL>
+__device__ __forceinline__ void mx_k_loop(const StageSrc<NL>& src, uint8_t* sm, int nk, int wave, int a_rd,
+                                          int b_rd, int sw, int q, const uint32_t* asb, const uint32_t* bsb0,
+                                          const uint32_t* bsb1, const uint32_t (&asc)[4], const uint32_t (&bsc)[2],
+                                          f32x16 (&acc)[4][2]) {
+  using C = SliceCfg<64>;
+  constexpr int MI = 4, NJ = 2;
+  uint32_t san[MI], sbn[NJ];
+  stage_issue<NL, 64>(src, 0, sm, 0, wave);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) san[i] = asb[asc[i]];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) sbn[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j]];
+  for (int kt = 0; kt < nk; ++kt) {
+    MOE_WAIT_VMCNT(0);
+    slice_barrier();
+    uint32_t sa[MI], sb[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) sa[i] = san[i];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sb[j] = sbn[j];
+    if (kt + 1 < nk) {
+      stage_issue<NL, 64>(src, kt + 1, sm, (kt + 1) & 1, wave);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) san[i] = asb[asc[i] + kt + 1];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sbn[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j] + kt + 1];
+    }
+    const uint8_t* As = sm + (kt & 1) * C::STAGE_BYTES + a_rd;
+    const uint8_t* Bs = sm + (kt & 1) * C::STAGE_BYTES + BM * C::ROWB + b_rd;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int clo = ((4 * s + q) ^ sw) * 16, chi = ((4 * s + 2 + q) ^ sw) * 16;
+      i32x8 af[NACT > 0 ? NACT : 1], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < NACT; ++i) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(As + i * 32 * C::ROWB + clo);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(As + i * 32 * C::ROWB + chi);
+        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(Bs + j * 32 * C::ROWB + clo);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(Bs + j * 32 * C::ROWB + chi);
+        bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int shift = 8 * (2 * s + q);
+#pragma unroll
+      for (int i = 0; i < NACT; ++i) {
+        const int sca = (int)((sa[i] >> shift) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int scb = (int)((sb[j] >> shift) & 0xffu);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, sca, 0, scb);
+        }
+      }
+    }
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
                                                          const uint8_t* __restrict__ b_sc,
                                                          const uint8_t* __restrict__ b2_sc, int64_t sc_group_stride,
                                                          uint8_t* __restrict__ h_sc, Grouped g, int ntn) {
+  using C = SliceCfg<64>;
   constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
   constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr int A_T = BM * PITCH, B_T = BN * PITCH;
-  constexpr int RPP = 512 / 8;
-  constexpr int AL = BM / RPP, BL = BN / RPP;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_T + B_T)];
+  constexpr int NL = BM / (C::RPI * 8);   // loads per operand per slice per wavefront
+  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kGemmSmemElems];
+  uint8_t* sm = reinterpret_cast<uint8_t*>(smem_u16);
   // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
   const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
   const int per_xcd = (valid + 7) >> 3;
@@ -81,38 +141,37 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   const int nt = logical % ntn;
   int grp, r0, rows;
   if (!locate_tile_mx(g, logical / ntn, grp, r0, rows)) return;
-  const int nk = a.K / BKB;
+  const int nk = a.K / 128;                      // 128-wide K slices
   const int kbl = a.K / 32;                      // scale bytes per row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const uint8_t* abase = (const uint8_t*)a.A + lchunk * 16;
-  uint32_t aoff[AL];
+  // Copies as 16-bit units (2 fp8 each): row offsets in units of lda / 2.
+  StageSrc<NL> src;
+  src.abase = (const uint16_t*)a.A;
+  src.bbase[0] = (const uint16_t*)((const uint8_t*)a.B + (int64_t)grp * a.b_group_stride);
+  src.bbase[1] = (EPI == EPI_SWIGLU) ? (const uint16_t*)((const uint8_t*)a.B2 + (int64_t)grp * a.b_group_stride)
+                                     : src.bbase[0];
+  src.nk1 = nk;
+  src.a_shift = 0;
+  src.b_shift = 0;
 #pragma unroll
-  for (int i = 0; i < AL; ++i) {
-    const int r = r0 + min(lrow + RPP * i, rows - 1);
-    aoff[i] = (uint32_t)((int64_t)r * a.lda);
-  }
-  const uint8_t* bbase[2];
-  bbase[0] = (const uint8_t*)a.B + (int64_t)grp * a.b_group_stride + lchunk * 16;
-  bbase[1] = (EPI == EPI_SWIGLU) ? (const uint8_t*)a.B2 + (int64_t)grp * a.b_group_stride + lchunk * 16 : bbase[0];
-  uint32_t boff[BL];
-  bool bup[BL];
-#pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    const int rr = lrow + RPP * i;
+  for (int j = 0; j < NL; ++j) {
+    const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;
+    const int ch = (lane % C::CPR) ^ C::swz(rr);
+    const int r = r0 + min(rr, rows - 1);
+    src.aoff[j] = (uint32_t)((int64_t)r * (a.lda / 2) + ch * 8);
     int64_t wrow;
     if (EPI == EPI_SWIGLU) {
-      const int wc = rr / WN, q = (rr % WN) / 32;
-      bup[i] = q >= NJ / 2;
-      wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (bup[i] ? q - NJ / 2 : q) * 32 + (rr & 31);
+      const int wc = rr / WN, qq = (rr % WN) / 32;
+      src.bup[j] = qq >= NJ / 2;
+      wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (src.bup[j] ? qq - NJ / 2 : qq) * 32 + (rr & 31);
     } else {
-      bup[i] = false;
+      src.bup[j] = false;
       wrow = (int64_t)nt * BN + rr;
     }
     wrow = wrow < a.N ? wrow : a.N - 1;
-    boff[i] = (uint32_t)(wrow * a.ldb);
+    src.boff[j] = (uint32_t)(wrow * (a.ldb / 2) + ch * 8);
   }
   // scale rows this lane feeds to the MFMAs: A rows of its row blocks, B rows of its column blocks
   // scale words are addressed as 32-bit offsets from the scale bases (4 blocks per word)
@@ -147,81 +206,24 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int wrows = rows - wm * WM;
 
-  u32x4 ra[AL], rb[BL];
-  const int st_off = lrow * PITCH + lchunk * 16;
-#pragma unroll
-  for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + aoff[i]);
-#pragma unroll
-  for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase[bup[i]] + boff[i]);
-#pragma unroll
-  for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(smem + st_off + RPP * i * PITCH) = ra[i];
-#pragma unroll
-  for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(smem + A_T + st_off + RPP * i * PITCH) = rb[i];
-  __syncthreads();
-  const int a_rd = (wm * WM + (lane & 31)) * PITCH + q * 16;
-  const int b_rd = (wn * WN + (lane & 31)) * PITCH + q * 16;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      const int ko = (kt + 1) * BKB;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase + aoff[i] + ko);
-#pragma unroll
-      for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase[bup[i]] + boff[i] + ko);
-    }
-    uint32_t sa[MI], sbv[NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sa[i] = asb[asc[i] + kt];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sbv[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j] + kt];
-    const uint8_t* As = smem + buf * (A_T + B_T);
-    const uint8_t* Bs = As + A_T;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {            // two K = 64 instructions per K step
-      i32x8 af[MI], bfr[NJ];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const uint8_t* p = As + a_rd + i * 32 * PITCH + s * 64;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 32);
-        af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint8_t* p = Bs + b_rd + j * 32 * PITCH + s * 64;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 32);
-        bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      }
-      const int shift = 8 * (2 * s + q);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        if (i * 32 < wrows) {
-          const int sca = (int)((sa[i] >> shift) & 0xffu);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int scb = (int)((sbv[j] >> shift) & 0xffu);
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], acc[i][j], 0, 0, 0, sca, 0, scb);
-          }
-        }
-      }
-    }
-    if (kt + 1 < nk) {
-      uint8_t* An = smem + (buf ^ 1) * (A_T + B_T);
-#pragma unroll
-      for (int i = 0; i < AL; ++i) *reinterpret_cast<u32x4*>(An + st_off + RPP * i * PITCH) = ra[i];
-#pragma unroll
-      for (int i = 0; i < BL; ++i) *reinterpret_cast<u32x4*>(An + A_T + st_off + RPP * i * PITCH) = rb[i];
-    }
-    __syncthreads();
+  const int a_rd = (wm * WM + (lane & 31)) * C::ROWB;
+  const int b_rd = (wn * WN + (lane & 31)) * C::ROWB;
+  const int sw = C::swz(lane & 31);
+  const int wrows_u = rows - (__builtin_amdgcn_readfirstlane(wave) / WAVES_N) * WM;
+  const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
+  switch (nact) {
+    case 0: mx_k_loop<EPI, 0, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
+    case 1: mx_k_loop<EPI, 1, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
+    case 2: mx_k_loop<EPI, 2, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
+    case 3: mx_k_loop<EPI, 3, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
+    default: mx_k_loop<EPI, 4, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
   }
 
   const int ccol = lane & 31;
-#pragma unroll
+#pragma clang loop unroll(full)
   for (int i = 0; i < MI; ++i) {
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int r = 0; r < 16; ++r) {
       const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
       const bool ok = lr < rows;
