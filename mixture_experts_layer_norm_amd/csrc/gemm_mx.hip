@@ -56,37 +56,36 @@ __device__ __forceinline__ uint32_t e4m3_code_scaled(float v, float inv_scale) {
   return sign | (uint32_t)code;
 }
 
-// The K loop of an MX tile: 2 LDS stages; in step kt, once slice kt and its scale words have
+// The K loop of an MX tile: 2 LDS stages. In step kt, once slice kt and its scale words have
 // landed and the barrier has made every thread's copies visible, slice kt + 1 and its scale words
-// are issued and the two scaled MFMAs of slice kt run for this wave's first NACT row blocks.
+// are issued and the two scaled MFMAs of slice kt run for this wave's first NACT row blocks. The
+// scale words of a slice (one 32-bit word = 4 blocks per tile row, A rows then B rows) are copied
+// into LDS too: wavefront w copies the words of 64 tile rows, one 4-byte load per lane.
 template <int EPI, int NACT, int NL>
-__device__ __forceinline__ void mx_k_loop(const StageSrc<NL>& src, uint8_t* sm, int nk, int wave, int a_rd,
-                                          int b_rd, int sw, int q, const uint32_t* asb, const uint32_t* bsb0,
-                                          const uint32_t* bsb1, const uint32_t (&asc)[4], const uint32_t (&bsc)[2],
-                                          f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void mx_k_loop(const StageSrc<NL>& src, uint8_t* sm, uint32_t* scl, int nk, int wave,
+                                          int a_rd, int b_rd, int sw, int q, const uint32_t* sc_src, int a_srow,
+                                          int b_srow, f32x16 (&acc)[4][2]) {
   using C = SliceCfg<64>;
   constexpr int MI = 4, NJ = 2;
-  uint32_t san[MI], sbn[NJ];
+  // this wave's scale-word copy: words sc_src[kt] of its row into scl[stage][64 wave + lane]
+  auto issue_scales = [&](int kt, int stage) __attribute__((always_inline)) {
+    __builtin_amdgcn_global_load_lds((const void*)(sc_src + kt), (lds_void*)(scl + stage * 512 + 64 * wave), 4, 0, 0);
+  };
   stage_issue<NL, 64>(src, 0, sm, 0, wave);
-#pragma unroll
-  for (int i = 0; i < MI; ++i) san[i] = asb[asc[i]];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) sbn[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j]];
+  issue_scales(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     MOE_WAIT_VMCNT(0);
     slice_barrier();
-    uint32_t sa[MI], sb[NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) sa[i] = san[i];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sb[j] = sbn[j];
     if (kt + 1 < nk) {
       stage_issue<NL, 64>(src, kt + 1, sm, (kt + 1) & 1, wave);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) san[i] = asb[asc[i] + kt + 1];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) sbn[j] = (EPI == EPI_SWIGLU && j >= NJ / 2 ? bsb1 : bsb0)[bsc[j] + kt + 1];
+      issue_scales(kt + 1, (kt + 1) & 1);
     }
+    const uint32_t* scs = scl + (kt & 1) * 512;
+    uint32_t sa[MI], sb[NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) sa[i] = scs[a_srow + i * 32];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sb[j] = scs[256 + b_srow + j * 32];
     const uint8_t* As = sm + (kt & 1) * C::STAGE_BYTES + a_rd;
     const uint8_t* Bs = sm + (kt & 1) * C::STAGE_BYTES + BM * C::ROWB + b_rd;
 #pragma unroll
@@ -173,29 +172,29 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
     wrow = wrow < a.N ? wrow : a.N - 1;
     src.boff[j] = (uint32_t)(wrow * (a.ldb / 2) + ch * 8);
   }
-  // scale rows this lane feeds to the MFMAs: A rows of its row blocks, B rows of its column blocks
-  // scale words are addressed as 32-bit offsets from the scale bases (4 blocks per word)
-  const uint32_t* asb = reinterpret_cast<const uint32_t*>(a_sc);
-  const uint32_t* bsb0 = reinterpret_cast<const uint32_t*>(b_sc + (int64_t)grp * sc_group_stride);
-  const uint32_t* bsb1 = reinterpret_cast<const uint32_t*>((EPI == EPI_SWIGLU ? b2_sc : b_sc) + (int64_t)grp * sc_group_stride);
-  uint32_t asc[MI], bsc[NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int r = r0 + min(wm * WM + i * 32 + (lane & 31), rows - 1);
-    asc[i] = (uint32_t)((int64_t)r * kbl / 4);
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int cc = wn * WN + j * 32 + (lane & 31);   // weight row within the tile
-    int64_t wrow;
-    if (EPI == EPI_SWIGLU) {
-      const bool up = j >= NJ / 2;
-      wrow = (int64_t)nt * (BN / 2) + wn * (WN / 2) + (up ? j - NJ / 2 : j) * 32 + (lane & 31);
+  // Scale words: wavefront w < 4 copies those of A tile rows 64 w + lane, w >= 4 those of B tile
+  // rows 64 (w - 4) + lane (in the B tile's row order), one 32-bit word (4 blocks) per slice.
+  __shared__ __attribute__((aligned(16))) uint32_t scl[2 * 512];
+  const uint32_t* sc_src;
+  {
+    const int tr = 64 * (wave & 3) + lane;   // tile row whose words this lane copies
+    if (wave < 4) {
+      const int r = r0 + min(tr, rows - 1);
+      sc_src = reinterpret_cast<const uint32_t*>(a_sc) + (int64_t)r * kbl / 4;
     } else {
-      wrow = (int64_t)nt * BN + cc;
+      int64_t wrow;
+      bool up = false;
+      if (EPI == EPI_SWIGLU) {
+        const int wc = tr / WN, qq = (tr % WN) / 32;
+        up = qq >= NJ / 2;
+        wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (up ? qq - NJ / 2 : qq) * 32 + (tr & 31);
+      } else {
+        wrow = (int64_t)nt * BN + tr;
+      }
+      wrow = wrow < a.N ? wrow : a.N - 1;
+      const uint8_t* base = (up ? b2_sc : b_sc) + (int64_t)grp * sc_group_stride;
+      sc_src = reinterpret_cast<const uint32_t*>(base) + wrow * kbl / 4;
     }
-    wrow = wrow < a.N ? wrow : a.N - 1;
-    bsc[j] = (uint32_t)(wrow * kbl / 4);
   }
   const int q = lane >> 5;
 
@@ -210,14 +209,15 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   const int a_rd = (wm * WM + (lane & 31)) * C::ROWB;
   const int b_rd = (wn * WN + (lane & 31)) * C::ROWB;
   const int sw = C::swz(lane & 31);
+  const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);   // tile rows of this lane's scales
   const int wrows_u = rows - (__builtin_amdgcn_readfirstlane(wave) / WAVES_N) * WM;
   const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
   switch (nact) {
-    case 0: mx_k_loop<EPI, 0, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
-    case 1: mx_k_loop<EPI, 1, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
-    case 2: mx_k_loop<EPI, 2, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
-    case 3: mx_k_loop<EPI, 3, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
-    default: mx_k_loop<EPI, 4, NL>(src, sm, nk, wave, a_rd, b_rd, sw, q, asb, bsb0, bsb1, asc, bsc, acc); break;
+    case 0: mx_k_loop<EPI, 0, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
+    case 1: mx_k_loop<EPI, 1, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
+    case 2: mx_k_loop<EPI, 2, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
+    case 3: mx_k_loop<EPI, 3, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
+    default: mx_k_loop<EPI, 4, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
   }
 
   const int ccol = lane & 31;
