@@ -154,6 +154,10 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   src.nk1 = nk;
   src.a_shift = 0;
   src.b_shift = 0;
+  {
+    const int left = __builtin_amdgcn_readfirstlane(rows) - C::RPI * NL * __builtin_amdgcn_readfirstlane(wave);
+    src.na = left <= 0 ? 0 : min(NL, (left + C::RPI - 1) / C::RPI);
+  }
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;

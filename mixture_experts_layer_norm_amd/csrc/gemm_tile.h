@@ -82,6 +82,7 @@ struct StageSrc {
   bool bup[NL];         // B load from the second weight matrix (W_up)
   int nk1;              // K slices of the first pass; later slices read the second pass
   int64_t a_shift, b_shift;
+  int na;               // A loads issued per slice (2-stage slices skip loads of rows past the tile's end)
 };
 
 // Issues the 2 NL LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
@@ -95,8 +96,12 @@ __device__ __forceinline__ void stage_issue(const StageSrc<NL>& s, int kt, uint8
   const int64_t bsh = (second ? s.b_shift : 0) + ko;
   uint8_t* base = smem + stage * C::STAGE_BYTES + wave * (NL * 1024);
 #pragma unroll
-  for (int j = 0; j < NL; ++j)
+  for (int j = 0; j < NL; ++j) {
+    // With 2 stages every wait drains all loads (vmcnt 0), so the count per slice may vary.
+    // The skipped rows hold stale LDS; they feed only accumulator rows the epilogue drops.
+    if (C::STAGES == 2 && j >= s.na) break;
     __builtin_amdgcn_global_load_lds((const void*)(ab + s.aoff[j]), (lds_void*)(base + j * 1024), 16, 0, 0);
+  }
 #pragma unroll
   for (int j = 0; j < NL; ++j)
     __builtin_amdgcn_global_load_lds((const void*)((s.bup[j] ? s.bbase[1] : s.bbase[0]) + bsh + s.boff[j]),
@@ -229,6 +234,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   }
   // K slice kt < nk1 reads the first pass, kt >= nk1 the second (operands shifted by the split offsets)
   src.nk1 = nk;
+  {
+    // wave-uniform: A loads j of this wave start at row RPI (NL wave + j)
+    const int left = __builtin_amdgcn_readfirstlane(tc.rows) - C::RPI * NL * __builtin_amdgcn_readfirstlane(wave);
+    src.na = left <= 0 ? 0 : min(NL, (left + C::RPI - 1) / C::RPI);
+  }
   src.a_shift = a.a_seg_shift;
   src.b_shift = a.b_seg_shift;
   if (a.two_pass) nk *= 2;
