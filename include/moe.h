@@ -171,13 +171,14 @@ int moe_schedule(const moe_problem *p, const int32_t *topk_idx, int32_t *counts,
 int moe_dispatch(const moe_problem *p, const void *x, const int32_t *perm, int64_t slot_begin,
                  int64_t slot_count, void *x_slot, uint8_t *x_slot_scales, hipStream_t stream);
 
-/* The same dispatch over all T*K slots, token-major: each token's row of x is read once and
- * written to its K slots x_slot[inv_perm[t*K + k]] (inv_perm as produced by moe_schedule, a
- * bijection onto [0, T*K)). Identical bytes to moe_dispatch over the whole range; this is the
- * form moe_forward uses when it dispatches all slots at once. BF16 or f32 (MOE_MXFP8 returns
- * MOE_ERR_UNSUPPORTED: use moe_dispatch). */
+/* The same dispatch over all T*K slots, token-major: each token's row of x is read once (and
+ * under MOE_MXFP8 quantised once) and written to its K slots x_slot[inv_perm[t*K + k]]
+ * (inv_perm as produced by moe_schedule, a bijection onto [0, T*K)). Identical bytes to
+ * moe_dispatch over the whole range; this is the form moe_forward uses when it dispatches all
+ * slots at once. x_slot_scales: E8M0 bytes [T*K][D/32] under MOE_MXFP8, NULL otherwise
+ * (MOE_ERR_INVALID_ARG if that does not hold). */
 int moe_dispatch_tokens(const moe_problem *p, const void *x, const int32_t *inv_perm, void *x_slot,
-                        hipStream_t stream);
+                        uint8_t *x_slot_scales, hipStream_t stream);
 
 /* Deterministic combine (Blog, weighted sum after the combine; Notes "The production details"
  * on determinism): out[t] = shared_out[t] + sum_{k=0}^{K-1} topk_w[t][k] * y_routes[t*K + k],

@@ -79,7 +79,7 @@ _sig = {
     'moe_route_topk': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_schedule': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_dispatch': (ctypes.c_int, [_PP, _P, _P, _i64, _i64, _P, _P, _P]),
-    'moe_dispatch_tokens': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
+    'moe_dispatch_tokens': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     'moe_combine': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     'moe_forward': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P, _P,
                                    _P, _sz, _P]),
@@ -153,9 +153,9 @@ def dispatch(p, x, perm, slot_begin, slot_count, x_slot, x_slot_scales=None, str
                              _ptr(x_slot_scales), _stream(stream)), 'moe_dispatch')
 
 
-def dispatch_tokens(p, x, inv_perm, x_slot, stream=None):
-    _check(_lib.moe_dispatch_tokens(ctypes.byref(p), _ptr(x), _ptr(inv_perm), _ptr(x_slot), _stream(stream)),
-           'moe_dispatch_tokens')
+def dispatch_tokens(p, x, inv_perm, x_slot, x_slot_scales=None, stream=None):
+    _check(_lib.moe_dispatch_tokens(ctypes.byref(p), _ptr(x), _ptr(inv_perm), _ptr(x_slot), _ptr(x_slot_scales),
+                                    _stream(stream)), 'moe_dispatch_tokens')
 
 
 def combine(p, y_routes, shared_out, topk_w, out, stream=None):

@@ -153,13 +153,13 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* perm, int64
 }
 
 int moe_dispatch_tokens(const moe_problem* p, const void* x, const int32_t* inv_perm, void* x_slot,
-                        hipStream_t stream) {
+                        uint8_t* x_slot_scales, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
   if (!x || !inv_perm || !x_slot) return MOE_ERR_INVALID_ARG;
-  if (p->dtype == MOE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if ((p->dtype == MOE_MXFP8) != (x_slot_scales != nullptr)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(x_slot)) return MOE_ERR_MISALIGNED;
-  return launch_dispatch_tokens(x, p->dtype, inv_perm, p->T, p->K, p->D, x_slot, stream);
+  return launch_dispatch_tokens(x, p->dtype, inv_perm, p->T, p->K, p->D, x_slot, x_slot_scales, stream);
 }
 
 int moe_combine(const moe_problem* p, const void* y_routes, const void* shared_out,
@@ -360,7 +360,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
     uint8_t* hq = (uint8_t*)(wsb + L.h);
     uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
-    st = launch_dispatch(x, MOE_MXFP8, r->perm, p->K, p->D, 0, n, xq, xs, stream);
+    st = launch_dispatch_tokens(x, MOE_MXFP8, r->inv_perm, p->T, p->K, p->D, xq, xs, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_UP_GATE);
     GemmArgs g1;
@@ -378,7 +378,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     const void* A = x;
     const int32_t* gather = r->perm;
     if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
-      st = launch_dispatch_tokens(x, p->dtype, r->inv_perm, p->T, p->K, p->D, wsb + L.x_slot, stream);
+      st = launch_dispatch_tokens(x, p->dtype, r->inv_perm, p->T, p->K, p->D, wsb + L.x_slot, nullptr, stream);
       if (st) return st;
       A = wsb + L.x_slot;
       gather = nullptr;

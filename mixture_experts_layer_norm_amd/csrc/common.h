@@ -84,7 +84,7 @@ int launch_schedule(const int32_t* idx, int T, int K, int E, int32_t* counts, in
                     int32_t* err, hipStream_t s);
 
 int launch_dispatch_tokens(const void* x, int dtype, const int32_t* inv_perm, int T, int K, int D, void* x_slot,
-                           hipStream_t s);
+                           uint8_t* x_slot_sc, hipStream_t s);
 int launch_dispatch(const void* x, int dtype, const int32_t* perm, int K, int D, int64_t begin,
                     int64_t count, void* x_slot, uint8_t* x_slot_sc, hipStream_t s);
 int launch_combine(const void* y_routes, const void* shared_out, const float* topk_w, void* out,

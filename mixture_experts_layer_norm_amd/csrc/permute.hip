@@ -146,12 +146,55 @@ __global__ __launch_bounds__(256) void dispatch_tokens_kernel(const uint4* __res
   }
 }
 
+// Token-major MXFP8 dispatch: one wavefront per token quantises each 32-wide block of its row
+// once and writes the codes and the scale byte to the token's K slots.
+__global__ __launch_bounds__(256) void dispatch_tokens_mx_kernel(const uint16_t* __restrict__ x,
+                                                                 const int32_t* __restrict__ inv_perm, int T,
+                                                                 int K, int D, uint8_t* __restrict__ q,
+                                                                 uint8_t* __restrict__ sc) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* slots = inv_perm + (int64_t)t * K;
+  const int nb = D / 32;
+  for (int b = lane; b < nb; b += 64) {
+    const uint4* s = reinterpret_cast<const uint4*>(x + (int64_t)t * D + b * 32);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 u = s[c];
+      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+        v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+    uint32_t p[8];
+    const uint8_t e = (uint8_t)mx_block(v, p);
+    const uint4 lo = make_uint4(p[0], p[1], p[2], p[3]), hi = make_uint4(p[4], p[5], p[6], p[7]);
+    for (int k = 0; k < K; ++k) {
+      const int64_t j = slots[k];
+      sc[j * nb + b] = e;
+      uint4* d = reinterpret_cast<uint4*>(q + j * D + b * 32);
+      d[0] = lo;
+      d[1] = hi;
+    }
+  }
+}
+
 int launch_dispatch_tokens(const void* x, int dtype, const int32_t* inv_perm, int T, int K, int D, void* x_slot,
-                           hipStream_t s) {
+                           uint8_t* x_slot_sc, hipStream_t s) {
   if (T <= 0) return MOE_OK;
-  const int cpr = (int)(D * elt_bytes(dtype) / 16);
-  hipLaunchKernelGGL(dispatch_tokens_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, (const uint4*)x,
-                     inv_perm, T, K, cpr, (uint4*)x_slot);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (dtype == MOE_MXFP8) {
+    hipLaunchKernelGGL(dispatch_tokens_mx_kernel, grid, block, 0, s, (const uint16_t*)x, inv_perm, T, K, D,
+                       (uint8_t*)x_slot, x_slot_sc);
+  } else {
+    const int cpr = (int)(D * elt_bytes(dtype) / 16);
+    hipLaunchKernelGGL(dispatch_tokens_kernel, grid, block, 0, s, (const uint4*)x, inv_perm, T, K, cpr,
+                       (uint4*)x_slot);
+  }
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -77,8 +77,11 @@ def test_entry_points_reject_null_and_small_workspace_without_gpu():
     assert lib.moe_dispatch(P, 16, 16, 0, 4, 16, 16, None) == -1              # scales without MXFP8
     assert lib.moe_dispatch(P, 8, 16, 0, 4, 16, None, None) == -4             # misaligned x
     assert lib.moe_combine(P, None, None, None, None, None) == -1
-    assert lib.moe_dispatch_tokens(P, 16, None, 16, None) == -1
-    assert lib.moe_dispatch_tokens(P, 8, 16, 16, None) == -4             # misaligned x
+    assert lib.moe_dispatch_tokens(P, 16, None, 16, None, None) == -1
+    assert lib.moe_dispatch_tokens(P, 16, 16, 16, 16, None) == -1        # scales without MXFP8
+    assert lib.moe_dispatch_tokens(P, 8, 16, 16, None, None) == -4      # misaligned x
+    pm = m.problem(16, 128, 128, 8, 2, 128, 'mxfp8')
+    assert lib.moe_dispatch_tokens(ctypes.byref(pm), 16, 16, 16, None, None) == -1   # MXFP8 needs scales
     assert lib.moe_quantize_mx(16, 4, 48, 16, 16, None) == -2                 # cols % 32
     w = m.Weights()
     r = m.Routing()

@@ -111,7 +111,7 @@ def test_mx_dispatch_bit_exact(m):
     cfg = MX_SMALL
     H = synth.host_layer(cfg)
     idx = oracle.route_topk(H.logits, cfg.K)
-    _, _, perm, _ = oracle.schedule(idx, cfg.E)
+    _, _, perm, inv = oracle.schedule(idx, cfg.E)
     n = cfg.T * cfg.K
     p = m.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, 'mxfp8')
     xq = torch.empty((n, cfg.D), dtype=torch.uint8, device='cuda')
@@ -119,6 +119,32 @@ def test_mx_dispatch_bit_exact(m):
     m.dispatch(p, bf(H.x), torch.from_numpy(perm).cuda(), 0, n, xq, xs)
     torch.cuda.synchronize()
     rq, rs = oracle.mx_quantize(H.x[perm // cfg.K].astype(np.float64))
+    assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
+    # token-major form (the one the forward uses): same bytes
+    xq.fill_(0xAA)
+    xs.fill_(0xAA)
+    m.dispatch_tokens(p, bf(H.x), torch.from_numpy(inv).cuda(), xq, xs)
+    torch.cuda.synchronize()
+    assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize('T,D', [(37, 7168), (64, 2176)])
+def test_mx_dispatch_tokens_wide_rows(m, T, D):
+    """Token-major MXFP8 dispatch on rows of 224 and 68 blocks (more blocks than lanes, ragged),
+    block magnitudes spread over 2^-20 .. 2^19 so the scale bytes vary."""
+    K, E = 3, 8
+    rng = np.random.default_rng(11)
+    mag = np.exp2(rng.integers(-20, 20, (T, D // 32))).repeat(32, axis=1)
+    x = synth.round_bf16(rng.standard_normal((T, D)) * mag)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    _, _, perm, inv = oracle.schedule(idx, E)
+    n = T * K
+    p = m.problem(T, D, 128, E, K, 0, 'mxfp8')
+    xq = torch.full((n, D), 0xAA, dtype=torch.uint8, device='cuda')
+    xs = torch.full((n, D // 32), 0xAA, dtype=torch.uint8, device='cuda')
+    m.dispatch_tokens(p, bf(x), torch.from_numpy(inv).cuda(), xq, xs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.mx_quantize(x[perm // K].astype(np.float64))
     assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
 
 
