@@ -225,16 +225,20 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   }
 
   const int ccol = lane & 31;
+  const int tid512 = threadIdx.x;
+  __syncthreads();   // every wavefront is done with the staged slices: LDS holds the output tile now
+  if (EPI == EPI_SWIGLU) {
+    // E4M3 h tile (256 rows x 128 bytes) through LDS, then 16-byte stores (4 per thread instead of
+    // 64 single bytes). Chunk c of row r at c ^ (2 ((r >> 2) & 3)): rows r and r + 4 of one LDS
+    // write instruction fall on different banks. The E8M0 bytes go straight out.
 #pragma clang loop unroll(full)
-  for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MI; ++i)
 #pragma clang loop unroll(full)
-    for (int r = 0; r < 16; ++r) {
-      const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
-      const bool ok = lr < rows;
-      const int row = r0 + lr;
-      if (EPI == EPI_SWIGLU) {
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
+        const int row = r0 + lr;
         // one 32-column MX block per (row, wavefront): amax over the 32 lanes of this lane group
-        const int64_t col = (int64_t)nt * (BN / 2) + wn * (WN / 2) + ccol;
+        const int c = wn * (WN / 2) + ccol;
         const float h = silu_f(acc[i][0][r]) * acc[i][1][r];
         float amax = fabsf(h);
 #pragma unroll
@@ -247,19 +251,46 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
           sbyte = (uint32_t)(se + 127);
           code = e4m3_code_scaled(h, __uint_as_float((uint32_t)(127 - se) << 23));
         }
-        if (ok && col < a.N) {
-          ((uint8_t*)a.C)[(int64_t)row * a.ldc + col] = (uint8_t)code;
-          if (ccol == 0) h_sc[(int64_t)row * (a.ldc / 32) + col / 32] = (uint8_t)sbyte;
-        }
-      } else {
-        if (!ok) continue;
-        const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
+        sm[lr * 128 + (((c >> 4) ^ (((lr >> 2) & 3) << 1)) << 4) + (c & 15)] = (uint8_t)code;
+        const int64_t col = (int64_t)nt * (BN / 2) + c;
+        if (ccol == 0 && lr < rows && col < a.N) h_sc[(int64_t)row * (a.ldc / 32) + col / 32] = (uint8_t)sbyte;
+      }
+    __syncthreads();
+#pragma unroll 4
+    for (int qq = tid512; qq < BM * 8; qq += 512) {
+      const int lr = qq >> 3, c = qq & 7;
+      if (lr >= rows) break;
+      const int64_t col = (int64_t)nt * (BN / 2) + c * 16;
+      if (col >= a.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 128 + ((c ^ (((lr >> 2) & 3) << 1)) << 4));
+      *reinterpret_cast<uint4*>((uint8_t*)a.C + (int64_t)(r0 + lr) * a.ldc + col) = v;
+    }
+  } else {
+    // BF16 output tile through LDS (512-byte rows, chunk c of row r at c ^ (4 ((r >> 2) & 3))),
+    // then 16-byte stores to the (scattered) output rows
+#pragma clang loop unroll(full)
+    for (int i = 0; i < MI; ++i)
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
+        const int sw4 = ((lr >> 2) & 3) << 2;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int64_t col = (int64_t)nt * BN + wn * WN + j * 32 + ccol;
-          if (col < a.N) ((uint16_t*)a.C)[orow * a.ldc + col] = f2bf(acc[i][j][r]);
+          const int c = wn * WN + j * 32 + ccol;
+          *reinterpret_cast<uint16_t*>(sm + lr * 512 + (((c >> 3) ^ sw4) << 4) + (c & 7) * 2) = f2bf(acc[i][j][r]);
         }
       }
+    __syncthreads();
+#pragma unroll 4
+    for (int qq = tid512; qq < BM * 32; qq += 512) {
+      const int lr = qq >> 5, c = qq & 31;
+      if (lr >= rows) break;
+      const int64_t col = (int64_t)nt * BN + c * 8;
+      if (col >= a.N) continue;
+      const int row = r0 + lr;
+      const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
+      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *reinterpret_cast<uint4*>((uint16_t*)a.C + orow * a.ldc + col) = v;
     }
   }
 }
@@ -274,6 +305,9 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
   nb = (nb + 7) / 8 * 8;
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  // the epilogue writes whole 16-byte chunks of output rows
+  const int64_t rowb = (epi == EPI_SWIGLU) ? 1 : 2;
+  if ((reinterpret_cast<uintptr_t>(a.C) | (a.ldc * rowb) | (a.N * rowb)) & 15) return MOE_ERR_MISALIGNED;
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL(gemm_mx_kernel<EPI_SWIGLU>, dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
                        sc_group_stride, h_sc, g, ntn);

@@ -271,6 +271,67 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 
   // epilogue. Accumulator slot r of lane l: row (r/4)*8 + (l/32)*4 + r%4, column l%32.
   const int ccol = lane & 31;
+  if (EPI == EPI_STORE && !KG && !a.c_f32 && ((reinterpret_cast<uintptr_t>(a.C) | (a.ldc * 2) | (a.N * 2)) & 15) == 0) {
+    // BF16 tile through LDS (free now), then whole 16-byte chunks to the output rows (16-byte
+    // aligned rows and N a multiple of 8): 16 stores per thread instead of 128 two-byte ones. Chunk c of tile row r sits at c ^ (4 ((r >> 2) & 3))
+    // so the two rows one store instruction writes (r and r + 4) use different banks.
+    static_assert(BN * 2 == 512, "one tile row is 32 chunks of 16 bytes");
+#pragma clang loop unroll(full)
+    for (int i = 0; i < MI; ++i)
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int sw4 = ((lr >> 2) & 3) << 2;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int c = wn * WN + j * 32 + ccol;
+          *reinterpret_cast<uint16_t*>(sm + lr * 512 + (((c >> 3) ^ sw4) << 4) + (c & 7) * 2) = f2bf(acc[i][j][r]);
+        }
+      }
+    __syncthreads();
+    constexpr int NT = NWAVES * 64;
+#pragma unroll 4
+    for (int q = tid; q < BM * 32; q += NT) {
+      const int lr = q >> 5, c = q & 31;
+      if (lr >= tc.rows) break;           // rows grow with q
+      const int64_t col = (int64_t)tc.nt * BN + c * 8;
+      if (col >= a.N) continue;
+      const int row = tc.r0 + lr;
+      const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
+      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *reinterpret_cast<uint4*>((uint16_t*)a.C + orow * a.ldc + col) = v;
+    }
+    return;
+  }
+  if (EPI == EPI_SWIGLU && !a.c_f32 && ((reinterpret_cast<uintptr_t>(a.C) | (a.ldc * 2) | (a.N * 2)) & 15) == 0) {
+    // h tile (BM x BN/2 BF16, 256-byte rows) through LDS the same way, 8 chunk stores per thread
+    static_assert(BN == 256, "h tile rows are 16 chunks of 16 bytes");
+#pragma clang loop unroll(full)
+    for (int i = 0; i < MI; ++i)
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int sw4 = ((lr >> 2) & 3) << 2;
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+          const int c = wn * (WN / 2) + j * 32 + ccol;
+          const float h = silu_f(acc[i][j][r]) * acc[i][j + NJ / 2][r];
+          *reinterpret_cast<uint16_t*>(sm + lr * 256 + (((c >> 3) ^ sw4) << 4) + (c & 7) * 2) = f2bf(h);
+        }
+      }
+    __syncthreads();
+    constexpr int NT = NWAVES * 64;
+#pragma unroll 4
+    for (int q = tid; q < BM * 16; q += NT) {
+      const int lr = q >> 4, c = q & 15;
+      if (lr >= tc.rows) break;
+      const int64_t col = (int64_t)tc.nt * (BN / 2) + c * 8;
+      if (col >= a.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 256 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *reinterpret_cast<uint4*>((uint16_t*)a.C + (int64_t)(tc.r0 + lr) * a.ldc + col) = v;
+    }
+    return;
+  }
   float* part = reinterpret_cast<float*>(smem);   // EPI_DGRAD: [BM][WAVES_N] partials (LDS is free now)
   // fully unrolled: the accumulators must be indexed with constants to stay in registers
 #pragma clang loop unroll(full)
