@@ -82,11 +82,13 @@ typedef struct moe_problem {
 
 /* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
 #define MOE_FLAG_FUSED_GATHER 0x1
-/* Tuning: order the grouped GEMM tiles of an expert n-tile major (its m-tiles that share a
- * weight tile run together) instead of m-tile major. Results are bitwise identical. */
+/* Tuning: order the GEMM tiles of each expert n-tile major (all m-tiles that share a weight tile
+ * run together) instead of the default (pairs of m-tiles, n-tile major inside a pair, which lets
+ * both the weight and the activation tiles be reused from the L2). Results are bitwise identical. */
 #define MOE_FLAG_WEIGHT_MAJOR 0x2
-/* Tile order of the grouped GEMMs: inside each expert, blocks of n n-tiles (1..255), each block
- * m-tile major (MOE_FLAG_WEIGHT_MAJOR is n = 1). Affects only speed, never the results. */
+/* Tile order of the GEMMs: inside each expert, blocks of n n-tiles (1..255), each block m-tile
+ * major (n = 1 is MOE_FLAG_WEIGHT_MAJOR; n >= the n-tile count is plain m-tile major). Affects
+ * only speed, never the results. */
 /* Tuning: run the bf16 grouped GEMMs with 4 wavefronts per workgroup, each owning a 128 x 128
  * block of the 256 x 256 tile, instead of 8 wavefronts of 128 x 64. Results are bitwise equal. */
 #define MOE_FLAG_GEMM_WAVES4 0x8

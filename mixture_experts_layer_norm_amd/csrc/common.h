@@ -68,7 +68,8 @@ struct WsLayout {
 
 size_t elt_bytes(int dtype);
 WsLayout ws_layout(const moe_problem& p);
-// n-tiles per block of the grouped tile order selected by moe_problem::flags (0: m-tile major)
+// n-tiles per block of the grouped tile order selected by moe_problem::flags (0: the default
+// order, pairs of m-tiles, n-tile major inside a pair)
 constexpr int kDefaultTileBlock = 0;
 int tile_block_of(uint32_t flags);
 
@@ -117,8 +118,9 @@ struct Grouped {
   int32_t groups = 1;
   int32_t M = 0;              // rows when row_off == nullptr
   int64_t max_mtiles = 0;     // host bound on the number of m-tiles (grid size)
-  // Tile order inside a group: blocks of nblk n-tiles; inside a block m-tile major. nblk >= the
-  // n-tile count is plain m-tile major, nblk = 1 n-tile major (0 means m-tile major too).
+  // Tile order inside a group: blocks of nblk n-tiles, inside a block m-tile major (nblk >= the
+  // n-tile count: plain m-tile major, 1: n-tile major). 0 selects the default: pairs of m-tiles,
+  // n-tile major inside a pair.
   int32_t nblk = 0;
   int32_t waves4 = 0;         // bf16 GEMM workgroups of 4 wavefronts x (128 x 128) instead of 8 x (128 x 64)
   int32_t bk32 = 0;           // bf16 GEMM K slices 32 wide in 4 LDS stages instead of 64 wide in 2

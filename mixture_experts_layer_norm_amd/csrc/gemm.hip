@@ -17,8 +17,9 @@
 // accumulator slot and the epilogue needs no data exchange. 256-row m-tiles read each expert's
 // weights once for up to 256 routed rows; row blocks past an expert's last row skip their MFMAs.
 //
-// Workgroup -> tile mapping: tiles are numbered (m-tile major, n-tile minor) and dealt out so
-// that each XCD (workgroups are placed round-robin over the 8 XCDs) gets a contiguous range,
+// Workgroup -> tile mapping: tiles are numbered group by group (inside a group in pairs of
+// m-tiles, n-tile major inside a pair, see decode_grouped_tile) and dealt out so that each XCD (workgroups are
+// placed round-robin over the 8 XCDs) gets a contiguous range,
 // which keeps an expert's activation rows and weight tiles in that XCD's L2. The split is over
 // the tiles that exist (read on the device), not over the launched upper bound, so that every
 // XCD gets an equal share even when the routing leaves most of the bound empty.
@@ -59,34 +60,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
     k0 = a.k_off[tc.grp];
     nk = (a.k_off[tc.grp + 1] - k0) / BK;
   } else {
-    // The tiles of a group occupy logical [tile_off[grp] * ntn, tile_off[grp + 1] * ntn) (dense
-    // mode: one group of mtn m-tiles). Inside a group they run in blocks of nblk n-tiles, each
-    // block m-tile major, so that the tiles running side by side on one XCD share both their
-    // activation rows and their weight rows in L2.
-    int grp = 0, t0 = 0, nmt = mtn;
-    if (g.row_off) {
-      const int q = logical / ntn;
-      int lo = 0, hi = g.groups - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
-      }
-      grp = lo;
-      t0 = g.tile_off[lo];
-      nmt = g.tile_off[lo + 1] - t0;
-    }
-    const int rem = logical - t0 * ntn;
-    const int nbw = (g.nblk > 0 && g.nblk < ntn) ? g.nblk : ntn;
-    const int blk = rem / (nmt * nbw);
-    const int w = min(nbw, ntn - blk * nbw);
-    const int r2 = rem - blk * nmt * nbw;
-    tc.grp = grp;
-    tc.nt = blk * nbw + r2 % w;
-    const int mt = r2 / w;
-    const int rbase = g.row_off ? g.row_off[grp] : 0;
-    const int rend = g.row_off ? g.row_off[grp + 1] : g.M;
-    tc.r0 = rbase + mt * BM;
-    tc.rows = min(BM, rend - tc.r0);
+    if (!decode_grouped_tile(g, logical, ntn, mtn, tc)) return;
     nk = a.K / BK;
   }
 

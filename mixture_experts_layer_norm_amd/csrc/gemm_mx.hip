@@ -15,32 +15,11 @@
 // MFMA (lane l, lane group q = l / 32, row or column l % 32): bytes 0-15 of a lane's 32 hold K
 // block 0 of the instruction and bytes 16-31 K block 1 (32 values each); lane group q supplies K
 // values [16q, 16q+16) of each block and the E8M0 scale of block q. Scale words (4 bytes = the 4
-// blocks of one row and slice) are loaded per lane from global memory with the slice's copy, and
-// the lane's byte is shifted into place.
+// blocks of one row and slice) are copied into LDS beside the slice (one 4-byte LDS-direct load
+// per wavefront), and each lane shifts its byte into place.
 #include "gemm_tile.h"
 
 namespace moe {
-
-__device__ __forceinline__ bool locate_tile_mx(const Grouped& g, int mt, int& grp, int& r0, int& rows) {
-  if (g.row_off) {
-    const int total = g.tile_off[g.groups];
-    if (mt >= total) return false;
-    int lo = 0, hi = g.groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
-    }
-    grp = lo;
-    r0 = g.row_off[lo] + (mt - g.tile_off[lo]) * BM;
-    rows = min(BM, g.row_off[lo + 1] - r0);
-  } else {
-    grp = 0;
-    r0 = mt * BM;
-    if (r0 >= g.M) return false;
-    rows = min(BM, g.M - r0);
-  }
-  return true;
-}
 
 // Quantised E4M3 code of v / 2^se (saturating, RNE); same rule as the dispatch quantiser.
 __device__ __forceinline__ uint32_t e4m3_code_scaled(float v, float inv_scale) {
@@ -137,9 +116,9 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   if ((bid >> 3) >= per_xcd) return;
   const int logical = (bid & 7) * per_xcd + (bid >> 3);
   if (logical >= valid) return;
-  const int nt = logical % ntn;
-  int grp, r0, rows;
-  if (!locate_tile_mx(g, logical / ntn, grp, r0, rows)) return;
+  TileCoord tc;
+  if (!decode_grouped_tile(g, logical, ntn, (g.M + BM - 1) / BM, tc)) return;
+  const int nt = tc.nt, grp = tc.grp, r0 = tc.r0, rows = tc.rows;
   const int nk = a.K / 128;                      // 128-wide K slices
   const int kbl = a.K / 32;                      // scale bytes per row
 

@@ -44,6 +44,15 @@ struct TileCoord {
 
 using namespace gemm_detail;
 
+// Rows per m-tile of a group of n rows cut into m = ceil(n / BM) m-tiles: the rows are shared out
+// evenly (in multiples of 32) instead of m - 1 full tiles and a remainder. The m-tiles of one group
+// stream the same weight rows; with equal row counts they advance at the same rate, so the
+// copies that run side by side stay close enough in K for the second read of each weight slice
+// to hit the L2. ceil(n / (32 m)) * 32 <= BM, and (m - 1) times it stays below n: no tile is empty.
+__device__ __forceinline__ int group_tile_rows(int n, int m) {
+  return m <= 1 ? BM : ((n + 32 * m - 1) / (32 * m)) * 32;
+}
+
 // Find the (group, first row, valid rows) of m-tile mt; false when mt is past the last tile.
 __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord& tc) {
   if (g.row_off) {
@@ -55,8 +64,9 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
       if (g.tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     tc.grp = lo;
-    tc.r0 = g.row_off[lo] + (mt - g.tile_off[lo]) * BM;
-    tc.rows = min(BM, g.row_off[lo + 1] - tc.r0);
+    const int per = group_tile_rows(g.row_off[lo + 1] - g.row_off[lo], g.tile_off[lo + 1] - g.tile_off[lo]);
+    tc.r0 = g.row_off[lo] + (mt - g.tile_off[lo]) * per;
+    tc.rows = min(per, g.row_off[lo + 1] - tc.r0);
   } else {
     tc.grp = 0;
     tc.r0 = mt * BM;
@@ -64,6 +74,54 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
     tc.rows = min(BM, g.M - tc.r0);
   }
   return true;
+}
+
+// Tile `logical` of a grouped (or dense) GEMM with ntn n-tiles per group (dense: one group of mtn
+// m-tiles). The tiles of group grp occupy logical [tile_off[grp] * ntn, tile_off[grp + 1] * ntn).
+// Workgroups start in launch order as CUs free up, so on one XCD tiles d apart in that order
+// start about d / 32 of a tile's run time apart: only tiles a position or two apart still read a
+// K slice the other has just brought into the L2. Default order (g.nblk = 0): pairs of m-tiles,
+// n-tile major inside a pair, i.e. (m0,n0) (m1,n0) (m0,n1) (m1,n1) ... then (m2,n0) (m3,n0) ...
+// Both the weight tile (shared by the pair) and each activation tile (every second tile) are
+// reused from the L2, so an expert fetches about 9 operand tiles per m-tile instead of the
+// 17 of plain m-tile major order. g.nblk = n > 0: blocks of n n-tiles, m-tile major inside a
+// block (n >= ntn: plain m-tile major; n = 1: n-tile major over all the group's m-tiles).
+__device__ __forceinline__ bool decode_grouped_tile(const Grouped& g, int logical, int ntn, int mtn, TileCoord& tc) {
+  int grp = 0, t0 = 0, nmt = mtn;
+  if (g.row_off) {
+    const int q = logical / ntn;
+    int lo = 0, hi = g.groups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    grp = lo;
+    t0 = g.tile_off[lo];
+    nmt = g.tile_off[lo + 1] - t0;
+  }
+  const int rem = logical - t0 * ntn;
+  int mt;
+  tc.grp = grp;
+  if (g.nblk > 0) {
+    const int nbw = min(g.nblk, ntn);
+    const int blk = rem / (nmt * nbw);
+    const int w = min(nbw, ntn - blk * nbw);
+    const int r2 = rem - blk * nmt * nbw;
+    tc.nt = blk * nbw + r2 % w;
+    mt = r2 / w;
+  } else {
+    const int pair = rem / (2 * ntn);
+    const int h = min(2, nmt - 2 * pair);
+    const int r2 = rem - pair * 2 * ntn;
+    tc.nt = r2 / h;
+    mt = 2 * pair + r2 % h;
+  }
+  const int rbase = g.row_off ? g.row_off[grp] : 0;
+  const int rend = g.row_off ? g.row_off[grp + 1] : g.M;
+  const int per = g.row_off ? group_tile_rows(rend - rbase, nmt) : BM;
+  tc.r0 = rbase + mt * per;
+  tc.rows = min(per, rend - tc.r0);
+  return tc.rows > 0;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
