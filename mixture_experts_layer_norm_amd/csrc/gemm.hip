@@ -34,7 +34,8 @@ namespace moe {
 template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g, int ntn, int mtn) {
   constexpr int BK = SliceCfg<BKE>::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems];
+  // EPI_DGRAD keeps its [BM][WAVES_N] fp32 row partials past the 128 KB of operand staging
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems + (EPI == EPI_DGRAD ? 2 * BM * WAVES_N : 0)];
   // The grid is an upper bound (grouped tile counts are known only on the device); the valid
   // tiles are split evenly over the 8 XCDs, each taking a contiguous range of them.
   // K-grouped tiles differ in length by their group's K extent: they are dealt in launch order

@@ -390,6 +390,106 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
     }
     return;
   }
+  if (EPI == EPI_DGRAD && a.lo_off % 8 == 0 &&
+      ((reinterpret_cast<uintptr_t>(a.ea) | reinterpret_cast<uintptr_t>(a.eu) | reinterpret_cast<uintptr_t>(a.C) |
+        reinterpret_cast<uintptr_t>(a.C2) | (a.lde * 4) | (a.ldc * 2) | (a.N * 2)) & 15) == 0) {
+    // SwiGLU backward through LDS, in 4 rounds of 64 tile rows (row block i of both wavefront
+    // rows). Per round: a and u (fp32) of those rows are copied into LDS with 16-byte loads; each
+    // lane reads its elements, computes da, du and their low halves, and writes the four BF16
+    // values back into the 8 bytes it read; then whole 16-byte chunks of each output row go out.
+    // Same arithmetic and the same partial-sum order as the element-wise epilogue below. The row
+    // partials <h, dh'> sit past the 128 KB of staging (the kernel allocates them for DGRAD).
+    float* part = reinterpret_cast<float*>(smem + kGemmSmemElems);   // [BM][WAVES_N]
+    uint8_t* la = sm;                 // a: 64 rows x 1 KB (256 fp32), chunk c of row r at c ^ (8 ((r >> 2) & 1))
+    uint8_t* lu = sm + 65536;         // u: the same
+    constexpr int NT = NWAVES * 64;
+#pragma clang loop unroll(full)
+    for (int i = 0; i < MI; ++i) {
+      if (i > 0) __syncthreads();     // the previous round's stores have read their chunks
+      // LDS-direct copies, one 1 KB row per wavefront instruction: lane l fills position l of the
+      // row, i.e. chunk l ^ swizzle (columns past N are left out)
+#pragma unroll
+      for (int t = 0; t < 64 / NWAVES; ++t) {
+        const int rl = __builtin_amdgcn_readfirstlane(wave) * (64 / NWAVES) + t;
+        const int lr = (rl >> 5) * WM + i * 32 + (rl & 31);
+        const int c = lane ^ (((rl >> 2) & 1) << 3);
+        const int64_t col = (int64_t)tc.nt * BN + c * 4;
+        if (lr < tc.rows && col < a.N) {
+          const int64_t ge = (int64_t)(tc.r0 + lr) * a.lde + col;
+          __builtin_amdgcn_global_load_lds((const void*)(a.ea + ge), (lds_void*)(la + rl * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(a.eu + ge), (lds_void*)(lu + rl * 1024), 16, 0, 0);
+        }
+      }
+      MOE_WAIT_VMCNT(0);
+      __syncthreads();
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int rsub = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int rl = wm * 32 + rsub, lr = wm * WM + i * 32 + rsub;
+        const bool ok = lr < tc.rows;
+        const int row = tc.r0 + lr;
+        const float gj = (ok && a.row_scale) ? a.row_scale[row] : 1.f;
+        float p = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int cl = wn * WN + j * 32 + ccol;
+          const int pos = rl * 1024 + (((cl >> 2) ^ (((rl >> 2) & 1) << 3)) << 4) + (cl & 3) * 4;
+          const float av = *reinterpret_cast<const float*>(la + pos);
+          const float uv = *reinterpret_cast<const float*>(lu + pos);
+          const float sg = sigmoid_f(av);
+          const float sl = av * sg;
+          const float dhp = acc[i][j][r];
+          if (ok && (int64_t)tc.nt * BN + cl < a.N) p = fmaf(sl * uv, dhp, p);
+          const float dh = gj * dhp;
+          const float da = dh * uv * sg * (1.f + av * (1.f - sg));
+          const float du = dh * sl;
+          const uint16_t dah = f2bf(da), duh = f2bf(du);
+          *reinterpret_cast<uint32_t*>(la + pos) = (uint32_t)dah | ((uint32_t)duh << 16);
+          *reinterpret_cast<uint32_t*>(lu + pos) =
+              (uint32_t)f2bf(da - bf2f(dah)) | ((uint32_t)f2bf(du - bf2f(duh)) << 16);
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) p += __shfl_xor(p, off, 64);
+        if (ccol == 0) part[lr * WAVES_N + wn] = p;
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int q = tid; q < 64 * 32; q += NT) {
+        const int rl = q >> 5, g8 = q & 31;
+        const int lr = (rl >> 5) * WM + i * 32 + (rl & 31);
+        const int64_t col = (int64_t)tc.nt * BN + g8 * 8;
+        if (lr >= tc.rows || col >= a.N) continue;
+        const int sw = ((rl >> 2) & 1) << 3;
+        const int p0 = rl * 1024 + (((2 * g8) ^ sw) << 4), p1 = rl * 1024 + (((2 * g8 + 1) ^ sw) << 4);
+        const uint4 h0 = *reinterpret_cast<const uint4*>(la + p0), h1 = *reinterpret_cast<const uint4*>(la + p1);
+        const int64_t o = (int64_t)(tc.r0 + lr) * a.ldc + col;
+        // element e of the 8 holds (da | du << 16): the low halves are da, the high halves du
+        *reinterpret_cast<uint4*>((uint16_t*)a.C + o) =
+            make_uint4((h0.x & 0xffffu) | (h0.y << 16), (h0.z & 0xffffu) | (h0.w << 16),
+                       (h1.x & 0xffffu) | (h1.y << 16), (h1.z & 0xffffu) | (h1.w << 16));
+        *reinterpret_cast<uint4*>((uint16_t*)a.C2 + o) =
+            make_uint4((h0.x >> 16) | (h0.y & 0xffff0000u), (h0.z >> 16) | (h0.w & 0xffff0000u),
+                       (h1.x >> 16) | (h1.y & 0xffff0000u), (h1.z >> 16) | (h1.w & 0xffff0000u));
+        if (a.lo_off) {
+          const uint4 l0 = *reinterpret_cast<const uint4*>(lu + p0), l1 = *reinterpret_cast<const uint4*>(lu + p1);
+          *reinterpret_cast<uint4*>((uint16_t*)a.C + o + a.lo_off) =
+              make_uint4((l0.x & 0xffffu) | (l0.y << 16), (l0.z & 0xffffu) | (l0.w << 16),
+                         (l1.x & 0xffffu) | (l1.y << 16), (l1.z & 0xffffu) | (l1.w << 16));
+          *reinterpret_cast<uint4*>((uint16_t*)a.C2 + o + a.lo_off) =
+              make_uint4((l0.x >> 16) | (l0.y & 0xffff0000u), (l0.z >> 16) | (l0.w & 0xffff0000u),
+                         (l1.x >> 16) | (l1.y & 0xffff0000u), (l1.z >> 16) | (l1.w & 0xffff0000u));
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < tc.rows) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES_N; ++w) sum += part[tid * WAVES_N + w];
+      a.row_partial[(int64_t)(tc.r0 + tid) * ntn + tc.nt] = sum;
+    }
+    return;
+  }
   float* part = reinterpret_cast<float*>(smem);   // EPI_DGRAD: [BM][WAVES_N] partials (LDS is free now)
   // fully unrolled: the accumulators must be indexed with constants to stay in registers
 #pragma clang loop unroll(full)
