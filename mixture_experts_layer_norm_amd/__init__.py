@@ -17,6 +17,11 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f'{LIB_PATH} is missing: build it with `python mixture_experts_layer_norm_amd/build.py` '
                       '(the library has no fallback path)')
 
+# torch first: libmoe.so's libamdhip64.so.7 then resolves to the HIP runtime torch has loaded.
+# Loaded the other way round, the process would hold two HIP runtimes and torch's device
+# pointers and streams would be invalid in the library (every launch fails).
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2

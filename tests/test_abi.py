@@ -94,3 +94,17 @@ def test_entry_points_reject_null_and_small_workspace_without_gpu():
         setattr(r, f, 256)
     assert lib.moe_forward(ctypes.byref(pp), 256, 256, ctypes.byref(w), 256, ctypes.byref(r), None, None, 256,
                            1 << 40, None) == -2
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the binding before torch must not load a second HIP runtime into the process
+    (torch's device pointers would be invalid in the library)."""
+    import subprocess
+    import sys
+    code = ('import re, mixture_experts_layer_norm_amd, torch\n'
+            'maps = open("/proc/self/maps").read()\n'
+            'print(len(set(re.findall(r"\\S*/libamdhip64\\S*", maps))))\n')
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, '-c', code], capture_output=True, text=True, cwd=root, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == '1', r.stdout
