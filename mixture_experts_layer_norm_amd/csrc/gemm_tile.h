@@ -390,41 +390,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
     }
     return;
   }
-  if (EPI == EPI_SAVE_AU && ((reinterpret_cast<uintptr_t>(a.C) | reinterpret_cast<uintptr_t>(a.C2) | (a.ldc * 4) |
-                              (a.N * 4)) & 15) == 0) {
-    // fp32 a and u tiles (256 rows x 128 columns each, 512-byte rows) through LDS one after the
-    // other, then 16-byte chunk stores; chunk c of row r at c ^ (8 ((r >> 2) & 1))
-    static_assert(BN == 256, "a/u tile rows are 32 chunks of 16 bytes");
-    constexpr int NT = NWAVES * 64;
-#pragma clang loop unroll(full)
-    for (int m = 0; m < 2; ++m) {
-      if (m) __syncthreads();
-#pragma clang loop unroll(full)
-      for (int i = 0; i < MI; ++i)
-#pragma clang loop unroll(full)
-        for (int r = 0; r < 16; ++r) {
-          const int lr = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int sw = ((lr >> 2) & 1) << 3;
-#pragma unroll
-          for (int j = 0; j < NJ / 2; ++j) {
-            const int c = wn * (WN / 2) + j * 32 + ccol;
-            *reinterpret_cast<float*>(sm + lr * 512 + (((c >> 2) ^ sw) << 4) + (c & 3) * 4) = acc[i][j + m * (NJ / 2)][r];
-          }
-        }
-      __syncthreads();
-      float* dst = (float*)(m ? a.C2 : a.C);
-#pragma unroll 4
-      for (int q = tid; q < BM * 32; q += NT) {
-        const int lr = q >> 5, c = q & 31;
-        if (lr >= tc.rows) break;
-        const int64_t col = (int64_t)tc.nt * (BN / 2) + c * 4;
-        if (col >= a.N) continue;
-        *reinterpret_cast<float4*>(dst + (int64_t)(tc.r0 + lr) * a.ldc + col) =
-            *reinterpret_cast<const float4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 1) << 3)) << 4));
-      }
-    }
-    return;
-  }
   if (EPI == EPI_DGRAD && a.lo_off % 8 == 0 &&
       ((reinterpret_cast<uintptr_t>(a.ea) | reinterpret_cast<uintptr_t>(a.eu) | reinterpret_cast<uintptr_t>(a.C) |
         reinterpret_cast<uintptr_t>(a.C2) | (a.lde * 4) | (a.ldc * 2) | (a.N * 2)) & 15) == 0) {
