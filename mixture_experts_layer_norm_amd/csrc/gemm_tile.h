@@ -76,6 +76,23 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
   return true;
 }
 
+// Largest g < groups with off[g] <= q (off non-decreasing, off[0] = 0, groups <= 4096): the
+// group of m-tile q. Two rounds of 64 loads across the wavefront and a ballot each, instead of a
+// binary search whose ~log2(groups) dependent loads would sit in front of every tile's first
+// K slice. Wave-uniform result.
+__device__ __forceinline__ int find_group(const int32_t* __restrict__ off, int groups, int q) {
+  const int lane = threadIdx.x & 63;
+  const int step = (groups + 63) >> 6;
+  const int i1 = lane * step;
+  const bool p1 = i1 < groups && off[i1] <= q;
+  const uint64_t m1 = __ballot(p1);                       // lanes 0 .. L1 (lane 0 always: off[0] = 0)
+  const int base = (63 - __builtin_clzll(m1)) * step;
+  const int i2 = base + lane;
+  const bool p2 = lane < step && i2 < groups && off[i2] <= q;
+  const uint64_t m2 = __ballot(p2);
+  return base + (63 - __builtin_clzll(m2));
+}
+
 // Tile `logical` of a grouped (or dense) GEMM with ntn n-tiles per group (dense: one group of mtn
 // m-tiles). The tiles of group grp occupy logical [tile_off[grp] * ntn, tile_off[grp + 1] * ntn).
 // Workgroups start in launch order as CUs free up, so on one XCD tiles d apart in that order
@@ -89,15 +106,9 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
 __device__ __forceinline__ bool decode_grouped_tile(const Grouped& g, int logical, int ntn, int mtn, TileCoord& tc) {
   int grp = 0, t0 = 0, nmt = mtn;
   if (g.row_off) {
-    const int q = logical / ntn;
-    int lo = 0, hi = g.groups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.tile_off[mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    grp = lo;
-    t0 = g.tile_off[lo];
-    nmt = g.tile_off[lo + 1] - t0;
+    grp = find_group(g.tile_off, g.groups, logical / ntn);
+    t0 = g.tile_off[grp];
+    nmt = g.tile_off[grp + 1] - t0;
   }
   const int rem = logical - t0 * ntn;
   int mt;
