@@ -107,7 +107,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int NL = BM / (C::RPI * 8);   // loads per operand per slice per wavefront
-  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kGemmSmemElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kGemmSmemElems + 2048];
   uint8_t* sm = reinterpret_cast<uint8_t*>(smem_u16);
   // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
   const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   }
   // Scale words: wavefront w < 4 copies those of A tile rows 64 w + lane, w >= 4 those of B tile
   // rows 64 (w - 4) + lane (in the B tile's row order), one 32-bit word (4 blocks) per slice.
-  __shared__ __attribute__((aligned(16))) uint32_t scl[2 * 512];
+  uint32_t* scl = reinterpret_cast<uint32_t*>(sm + 2 * C::STAGE_BYTES);   // 2 x 512 scale words past the stages
   const uint32_t* sc_src;
   {
     const int tr = 64 * (wave & 3) + lane;   // tile row whose words this lane copies
