@@ -250,7 +250,8 @@ def main():
     if not args.no_extra and args.workload == 'dsv3':
         del L, weights, ws, out
         torch.cuda.empty_cache()
-        extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags)}
+        extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
+                 'pull_schedule_ep8': bench_pull_schedule(moe, stream)}
 
     line = {
         'metric': METRIC,
@@ -315,6 +316,44 @@ def standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream, reps=20):
                      'hbm_frac': nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del xs, ys, sh
     return res
+
+
+def bench_pull_schedule(moe, stream, R=8, N=8192, K=8, L=32, reps=20):
+    """The R > 1 pull-dispatch schedule (moe_pull_schedule) at the DSV3 routing shape sharded over
+    R = 8 ranks: routing [8][8192][8] over E = 256 experts (Gumbel-top-k on a mild Zipf
+    popularity), rank 0's table of 32 local experts. Three launches; reported per call."""
+    import torch
+    E = R * L
+    g = torch.Generator(device='cuda')
+    g.manual_seed(4242)
+    lp = -0.8 * torch.log(torch.arange(1, E + 1, device='cuda', dtype=torch.float32))
+    u = torch.rand((R, N, E), generator=g, device='cuda').clamp_(min=1e-30)
+    routing = torch.topk(lp - torch.log(-torch.log(u)), K, dim=2).indices.to(torch.int32).contiguous()
+    del u
+    n = R * N * K
+    dev = 'cuda'
+    counts = torch.empty((L,), dtype=torch.int32, device=dev)
+    src = torch.empty((L, R), dtype=torch.int32, device=dev)
+    offs = torch.empty((L + 1,), dtype=torch.int32, device=dev)
+    phs = torch.empty((n,), dtype=torch.int32, device=dev)
+    phi = torch.empty((n,), dtype=torch.int32, device=dev)
+    pos = torch.empty((n,), dtype=torch.int32, device=dev)
+    ws = torch.zeros((moe.pull_schedule_workspace_size(R, N, K, L),), dtype=torch.uint8, device=dev)
+
+    def fn():
+        moe.pull_schedule(routing, 0, L, counts, src, offs, phs, phi, ws, route_pos=pos, stream=stream)
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pulled = int(offs[L].item())
+    return {'workload': f'pull schedule R={R} N={N} K={K} L={L} (rank 0)', 'ms': ms, 'routes': n,
+            'routes_pulled': pulled, 'routes_per_s': n / (ms * 1e-3)}
 
 
 def bench_share(steps, warmup, flags):

@@ -164,6 +164,29 @@ int moe_route_topk(const moe_problem *p, const float *logits, int32_t *topk_idx,
 int moe_schedule(const moe_problem *p, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                  int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Pull-dispatch schedule of rank `rank` among R source ranks (Blog, "Scheduling"; region order
+ * from the Notes, "Pull dispatch, push combine"). routing [R][N][K] int32 (device): global expert
+ * of route k of token i on source rank r, in [0, R*L); rank c owns experts [c*L, (c+1)*L).
+ * Outputs (device): counts [L] routes per local expert, src_counts [L][R] routes per (local
+ * expert, source rank), offsets [L+1] exclusive scan of counts (offsets[L] = routes this rank
+ * pulls), and for slot p < offsets[L] the source of the route it holds: phi_src[p] (source rank)
+ * and phi_idx[p] (i*K + k on that rank). Inside the region of expert l the routes are ordered by
+ * (ordinal, source rank), the ordinal being the number of earlier routes (in (i, k) order) from
+ * the same source rank to l; so slot offsets[l] + q holds, for q < sum_r min(M[l][r], o + 1),
+ * ordinal o's routes in source-rank order. route_pos [R*N*K] (nullable) receives each route's
+ * slot, or -1 for routes owned by another rank. phi_src / phi_idx must hold R*N*K entries (the
+ * worst case). Bit-exact and independent of launch shape; no host synchronisation. At R = 1 this
+ * is moe_schedule's permutation (phi_idx = perm). Expert ids outside [0, R*L) set bit 0 of the
+ * sticky error word (the first int32 of `ws`, never cleared by the library) and count as expert
+ * 0. Needs `ws` of moe_pull_schedule_workspace_size bytes. Returns MOE_ERR_UNSUPPORTED when
+ * R*L > 1024 or R*N*K >= 2^31. */
+int moe_pull_schedule(int32_t R, int32_t N, int32_t K, int32_t L, int32_t rank, const int32_t *routing,
+                      int32_t *counts, int32_t *src_counts, int32_t *offsets, int32_t *phi_src,
+                      int32_t *phi_idx, int32_t *route_pos, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace moe_pull_schedule needs for (R, N, K, L). */
+int moe_pull_schedule_workspace_size(int32_t R, int32_t N, int32_t K, int32_t L, size_t *bytes);
+
 /* Dispatch (the one-GPU analogue of the pull dispatch, Notes "Pull dispatch, push combine"):
  * x_slot[j - slot_begin] = x[perm[j] / K] for j in [slot_begin, slot_begin + slot_count).
  * x [T][D] in the activation type (bf16, or f32 under MOE_F32). Under MOE_MXFP8 the rows are

@@ -43,7 +43,8 @@ DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
 EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_schedule', 'moe_dispatch',
             'moe_dispatch_tokens',
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
-            'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size')
+            'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
+            'moe_pull_schedule_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -94,6 +95,8 @@ _sig = {
     'moe_experts_backward': (ctypes.c_int, [_PP, _i64, _P, _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                                             ctypes.POINTER(Grads), _P, _P, _P, _P, _sz, _P]),
     'moe_quantize_mx': (ctypes.c_int, [_P, _i64, _i32, _P, _P, _P]),
+    'moe_pull_schedule': (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    'moe_pull_schedule_workspace_size': (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     'moe_forward_stages': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P,
                                           _P, _P, _sz, _P, _P]),
 }
@@ -227,3 +230,17 @@ def quantize_mx(src_bf16, q, scales, stream=None):
     rows = src_bf16.numel() // cols
     _check(_lib.moe_quantize_mx(_ptr(src_bf16), rows, cols, _ptr(q), _ptr(scales), _stream(stream)),
            'moe_quantize_mx')
+
+
+def pull_schedule_workspace_size(R: int, N: int, K: int, L: int) -> int:
+    n = _sz(0)
+    _check(_lib.moe_pull_schedule_workspace_size(R, N, K, L, ctypes.byref(n)), 'moe_pull_schedule_workspace_size')
+    return n.value
+
+
+def pull_schedule(routing, rank, L, counts, src_counts, offsets, phi_src, phi_idx, ws, route_pos=None, stream=None):
+    """routing: int32 [R, N, K] device tensor of global expert ids."""
+    R, N, K = routing.shape
+    _check(_lib.moe_pull_schedule(R, N, K, L, rank, _ptr(routing), _ptr(counts), _ptr(src_counts), _ptr(offsets),
+                                  _ptr(phi_src), _ptr(phi_idx), _ptr(route_pos), _ptr(ws), ws.numel(),
+                                  _stream(stream)), 'moe_pull_schedule')

@@ -83,6 +83,16 @@ def test_entry_points_reject_null_and_small_workspace_without_gpu():
     pm = m.problem(16, 128, 128, 8, 2, 128, 'mxfp8')
     assert lib.moe_dispatch_tokens(ctypes.byref(pm), 16, 16, 16, None, None) == -1   # MXFP8 needs scales
     assert lib.moe_quantize_mx(16, 4, 48, 16, 16, None) == -2                 # cols % 32
+    # pull schedule: R, rank, R*L limit, null pointers, workspace size
+    nb = ctypes.c_size_t(0)
+    assert lib.moe_pull_schedule_workspace_size(8, 64, 8, 32, ctypes.byref(nb)) == 0 and nb.value > 256
+    assert lib.moe_pull_schedule_workspace_size(8, 64, 8, 32, None) == -1
+    a = (16,) * 7
+    assert lib.moe_pull_schedule(0, 64, 8, 4, 0, *a, 16, 1 << 20, None) == -1          # R < 1
+    assert lib.moe_pull_schedule(4, 64, 8, 4, 4, *a, 16, 1 << 20, None) == -1          # rank >= R
+    assert lib.moe_pull_schedule(64, 64, 8, 32, 0, *a, 16, 1 << 20, None) == -2        # R*L > 1024
+    assert lib.moe_pull_schedule(4, 64, 8, 4, 0, None, *a[1:], 16, 1 << 20, None) == -1
+    assert lib.moe_pull_schedule(4, 64, 8, 4, 0, *a, 16, 8, None) == -3                # workspace too small
     w = m.Weights()
     r = m.Routing()
     assert lib.moe_forward(P, 16, 16, ctypes.byref(w), 16, ctypes.byref(r), None, None, None, 0, None) == -1
