@@ -248,10 +248,11 @@ def main():
         cpu = cpu_baseline(cfg, L, args.cpu_tokens)
     extra = None
     if not args.no_extra and args.workload == 'dsv3':
+        rg = bench_route_gemm(moe, cfg, L.x, stream)
         del L, weights, ws, out
         torch.cuda.empty_cache()
         extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
-                 'pull_schedule_ep8': bench_pull_schedule(moe, stream)}
+                 'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 
     line = {
         'metric': METRIC,
@@ -316,6 +317,35 @@ def standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream, reps=20):
                      'hbm_frac': nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del xs, ys, sh
     return res
+
+
+def bench_route_gemm(moe, cfg, x, stream, reps=20):
+    """moe_route_gemm at the workload's shape: router GEMM (x [T][D] BF16 times a random
+    w_router [E][D]) split along D, plus the top-K; 2*T*D*E FLOP."""
+    import torch
+    T, D, E, K = cfg.T, cfg.D, cfg.E, cfg.K
+    g = torch.Generator(device='cuda')
+    g.manual_seed(77)
+    w = (torch.randn((E, D), generator=g, device='cuda') / D ** 0.5).to(torch.bfloat16)
+    p = moe.problem(T, D, cfg.I, E, K, 0, 'bf16')
+    lg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    idx = torch.empty((T, K), dtype=torch.int32, device='cuda')
+    gw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    ws = torch.empty((moe.route_gemm_workspace_size(p),), dtype=torch.uint8, device='cuda')
+
+    def fn():
+        moe.route_gemm(p, x, w, lg, idx, gw, ws, stream=stream)
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * T * D * E
+    return {'workload': f'router GEMM + top-{K}, T={T} D={D} E={E}', 'ms': ms, 'tflops': flops / (ms * 1e-3) / 1e12}
 
 
 def bench_pull_schedule(moe, stream, R=8, N=8192, K=8, L=32, reps=20):

@@ -156,6 +156,20 @@ int moe_backward_workspace_size(const moe_problem *p, size_t *bytes);
 int moe_route_topk(const moe_problem *p, const float *logits, int32_t *topk_idx, float *topk_w,
                    hipStream_t stream);
 
+/* Router GEMM fused with the top-K selection (the logits of the Blog's "Overlapping computation
+ * and communication in MoE" computed in the library): logits[t][e] = sum_d x[t][d] w_router[e][d]
+ * from BF16 x [T][D] and w_router [E][D] with fp32 accumulation, split along D into K-groups
+ * whose fp32 partial products are summed in group order (deterministic), then moe_route_topk's
+ * selection and weights on those logits. logits [T][E] fp32 receives them (nullable);
+ * topk_idx [T][K], topk_w [T][K] as moe_route_topk. BF16 problems only (MOE_ERR_UNSUPPORTED for
+ * MOE_F32; under MOE_MXFP8 x is the BF16 input). x and w_router 16-byte aligned. Needs `ws` of
+ * moe_route_gemm_workspace_size bytes (the split-K partials). */
+int moe_route_gemm(const moe_problem *p, const void *x, const void *w_router, float *logits,
+                   int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace moe_route_gemm needs for `p`. */
+int moe_route_gemm_workspace_size(const moe_problem *p, size_t *bytes);
+
 /* Device-side histogram + exclusive scan + stable placement: the one-source-rank case of the
  * pull schedule (Blog, "Scheduling"; sort key from the Notes, section "Pull dispatch, push
  * combine"). topk_idx [T][K] -> counts [E], offsets [E+1], perm [T*K], inv_perm [T*K], with

@@ -44,7 +44,7 @@ EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_sc
             'moe_dispatch_tokens',
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
-            'moe_pull_schedule_workspace_size')
+            'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -95,6 +95,8 @@ _sig = {
     'moe_experts_backward': (ctypes.c_int, [_PP, _i64, _P, _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                                             ctypes.POINTER(Grads), _P, _P, _P, _P, _sz, _P]),
     'moe_quantize_mx': (ctypes.c_int, [_P, _i64, _i32, _P, _P, _P]),
+    'moe_route_gemm': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    'moe_route_gemm_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
     'moe_pull_schedule': (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_pull_schedule_workspace_size': (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     'moe_forward_stages': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P,
@@ -244,3 +246,14 @@ def pull_schedule(routing, rank, L, counts, src_counts, offsets, phi_src, phi_id
     _check(_lib.moe_pull_schedule(R, N, K, L, rank, _ptr(routing), _ptr(counts), _ptr(src_counts), _ptr(offsets),
                                   _ptr(phi_src), _ptr(phi_idx), _ptr(route_pos), _ptr(ws), ws.numel(),
                                   _stream(stream)), 'moe_pull_schedule')
+
+
+def route_gemm_workspace_size(p: Problem) -> int:
+    n = _sz(0)
+    _check(_lib.moe_route_gemm_workspace_size(ctypes.byref(p), ctypes.byref(n)), 'moe_route_gemm_workspace_size')
+    return n.value
+
+
+def route_gemm(p, x, w_router, logits, topk_idx, topk_w, ws, stream=None):
+    _check(_lib.moe_route_gemm(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
+                               _ptr(ws), ws.numel(), _stream(stream)), 'moe_route_gemm')

@@ -2,6 +2,8 @@
 // Every entry point checks its arguments before enqueuing anything and never synchronises.
 #include <string.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "pipeline.h"
 
@@ -121,6 +123,71 @@ int moe_route_topk(const moe_problem* p, const float* logits, int32_t* topk_idx,
   if (st) return st;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   return launch_route_topk(logits, topk_idx, topk_w, p->T, p->E, p->K, stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+// Router GEMM split along D into S K-groups so that the T/256 x E/256 output tiles fill the
+// chip: about 256 workgroups, at least one 64-wide K slice per group, at most 16 groups.
+struct RouteGemmWs {
+  int S;
+  size_t err, k_off, part, total;
+};
+
+static RouteGemmWs route_gemm_ws(const moe_problem& p) {
+  RouteGemmWs w{};
+  const int mtn = (p.T + kGemmBM - 1) / kGemmBM, ntn = (p.E + 255) / 256, nkt = p.D / 64;
+  const int want = (256 + mtn * ntn - 1) / (mtn * ntn);
+  w.S = std::max(1, std::min(want, std::min(16, nkt)));
+  w.err = 0;
+  w.k_off = 256;
+  w.part = 512;
+  w.total = w.part + (((size_t)w.S * p.T * p.E * 4 + 255) / 256) * 256;
+  return w;
+}
+
+__global__ void route_k_off_kernel(int S, int nkt, int32_t* k_off) {
+  const int g = threadIdx.x;
+  if (g <= S) k_off[g] = (int)(((int64_t)g * nkt / S) * 64);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_route_gemm_workspace_size(const moe_problem* p, size_t* bytes) {
+  int st = validate_routing(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  *bytes = route_gemm_ws(*p).total;
+  return MOE_OK;
+}
+
+int moe_route_gemm(const moe_problem* p, const void* x, const void* w_router, float* logits, int32_t* topk_idx,
+                   float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = validate_routing(p);
+  if (st) return st;
+  if (p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (!x || !w_router || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_MISALIGNED;
+  const RouteGemmWs W = route_gemm_ws(*p);
+  if (!ws || ws_bytes < W.total) return MOE_ERR_WORKSPACE;
+  char* wsb = (char*)ws;
+  int32_t* k_off = (int32_t*)(wsb + W.k_off);
+  float* part = (float*)(wsb + W.part);
+  hipLaunchKernelGGL(route_k_off_kernel, dim3(1), dim3(64), 0, stream, W.S, p->D / 64, k_off);
+  MOE_LAUNCH_CHECK();
+  // partial logits: part[s][t][e] = sum over k in group s of x[t][k] w_router[e][k] (fp32)
+  GemmArgs g;
+  g.A = x; g.lda = p->D; g.B = w_router; g.ldb = p->D;
+  g.M = p->T; g.N = p->E; g.K = p->D;
+  g.C = part; g.ldc = p->E; g.c_group_stride = (int64_t)p->T * p->E;
+  g.k_off = k_off;
+  if ((st = launch_gemm_bf16_kgroup(g, W.S, stream))) return st;
+  return launch_route_topk_partials(part, W.S, (int64_t)p->T * p->E, logits, topk_idx, topk_w, p->T, p->E, p->K,
+                                    stream);
 }
 
 static int schedule_into(const moe_problem* p, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,

@@ -80,6 +80,8 @@ int validate_routing(const moe_problem* p);
 // launchers (each returns 0 or a moe_status; all enqueue on `s`)
 // ---------------------------------------------------------------------------------------------
 int launch_route_topk(const float* logits, int32_t* idx, float* w, int T, int E, int K, hipStream_t s);
+int launch_route_topk_partials(const float* part, int S, int64_t part_stride, float* logits, int32_t* idx, float* w,
+                               int T, int E, int K, hipStream_t s);
 int launch_schedule(const int32_t* idx, int T, int K, int E, int32_t* counts, int32_t* offsets,
                     int32_t* perm, int32_t* inv_perm, int32_t* blk_hist, int32_t* tile_off,
                     int32_t* err, hipStream_t s);

@@ -38,23 +38,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// One wavefront per token. NV = logits per lane (E <= 64 * NV).
+// Top-K of one token from its keys (key = (value order << 32) | ~e: the max picks the larger
+// value, then the lower index), then g_k = exp(v_k - v_0) / sum_j exp(v_j - v_0). One wavefront.
 template <int NV>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
-                                                         int32_t* __restrict__ idx,
-                                                         float* __restrict__ wout, int T, int E,
-                                                         int K) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    int e = lane + 64 * j;
-    // key = (value order << 32) | (~e): the max picks the larger value, then the lower index.
-    key[j] = (e < E) ? (((uint64_t)order_key(row[e]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
-  }
+__device__ __forceinline__ void topk_from_keys(uint64_t (&key)[NV], int K, int lane, int32_t* __restrict__ idx_row,
+                                               float* __restrict__ w_row) {
   int my_e = 0;
   float my_v = 0.f;
   float vmax = 0.f;
@@ -71,15 +59,81 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     if (k == 0) vmax = v;
     if (lane == k) { my_e = e; my_v = v; }
   }
-  // g_k = exp(v_k - v_0) / sum_j exp(v_j - v_0); lane k holds choice k (K <= 64)
+  // lane k holds choice k (K <= 64)
   float z = (lane < K) ? expf(my_v - vmax) : 0.f;
   float s = z;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
   if (lane < K) {
-    idx[(size_t)t * K + lane] = my_e;
-    wout[(size_t)t * K + lane] = z / s;
+    idx_row[lane] = my_e;
+    w_row[lane] = z / s;
   }
+}
+
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  return ((uint64_t)order_key(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+// One wavefront per token. NV = logits per lane (E <= 64 * NV).
+template <int NV>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                         int32_t* __restrict__ idx,
+                                                         float* __restrict__ wout, int T, int E,
+                                                         int K) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  uint64_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = (e < E) ? route_key(row[e], e) : 0ull;
+  }
+  topk_from_keys<NV>(key, K, lane, idx + (size_t)t * K, wout + (size_t)t * K);
+}
+
+// The same from S split-K partial products of the router GEMM: logit = sum over s of part[s]
+// (s ascending, fp32), also stored to logits when it is not null.
+template <int NV>
+__global__ __launch_bounds__(256) void route_topk_partials_kernel(const float* __restrict__ part, int S,
+                                                                  int64_t part_stride, float* __restrict__ logits,
+                                                                  int32_t* __restrict__ idx, float* __restrict__ wout,
+                                                                  int T, int E, int K) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  uint64_t key[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = 0ull;
+    if (e < E) {
+      const float* p = part + (size_t)t * E + e;
+      float v = p[0];
+      for (int q = 1; q < S; ++q) v += p[q * part_stride];
+      if (logits) logits[(size_t)t * E + e] = v;
+      key[j] = route_key(v, e);
+    }
+  }
+  topk_from_keys<NV>(key, K, lane, idx + (size_t)t * K, wout + (size_t)t * K);
+}
+
+int launch_route_topk_partials(const float* part, int S, int64_t part_stride, float* logits, int32_t* idx, float* w,
+                               int T, int E, int K, hipStream_t s) {
+  dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(route_topk_partials_kernel<1>, grid, block, 0, s, part, S, part_stride, logits, idx, w, T, E, K);
+  else if (E <= 128)
+    hipLaunchKernelGGL(route_topk_partials_kernel<2>, grid, block, 0, s, part, S, part_stride, logits, idx, w, T, E, K);
+  else if (E <= 256)
+    hipLaunchKernelGGL(route_topk_partials_kernel<4>, grid, block, 0, s, part, S, part_stride, logits, idx, w, T, E, K);
+  else if (E <= 512)
+    hipLaunchKernelGGL(route_topk_partials_kernel<8>, grid, block, 0, s, part, S, part_stride, logits, idx, w, T, E, K);
+  else
+    hipLaunchKernelGGL(route_topk_partials_kernel<16>, grid, block, 0, s, part, S, part_stride, logits, idx, w, T, E, K);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 int launch_route_topk(const float* logits, int32_t* idx, float* w, int T, int E, int K, hipStream_t s) {

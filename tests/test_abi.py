@@ -83,6 +83,12 @@ def test_entry_points_reject_null_and_small_workspace_without_gpu():
     pm = m.problem(16, 128, 128, 8, 2, 128, 'mxfp8')
     assert lib.moe_dispatch_tokens(ctypes.byref(pm), 16, 16, 16, None, None) == -1   # MXFP8 needs scales
     assert lib.moe_quantize_mx(16, 4, 48, 16, 16, None) == -2                 # cols % 32
+    # fused router: fp32 refused, null pointers, workspace size
+    pb = m.problem(16, 128, 128, 8, 2, 128, 'bf16')
+    assert lib.moe_route_gemm(P, 16, 16, 16, 16, 16, 16, 1 << 30, None) == -2            # MOE_F32
+    assert lib.moe_route_gemm(ctypes.byref(pb), None, 16, 16, 16, 16, 16, 1 << 30, None) == -1
+    assert lib.moe_route_gemm(ctypes.byref(pb), 16, 16, 16, 16, 16, 16, 8, None) == -3   # workspace
+    assert lib.moe_route_gemm_workspace_size(ctypes.byref(pb), None) == -1
     # pull schedule: R, rank, R*L limit, null pointers, workspace size
     nb = ctypes.c_size_t(0)
     assert lib.moe_pull_schedule_workspace_size(8, 64, 8, 32, ctypes.byref(nb)) == 0 and nb.value > 256
