@@ -316,3 +316,105 @@ def shared_backward(x, dy, ws_gate, ws_up, ws_down):
     dX, a, b, c, _, _ = _expert_backward(np.asarray(x, dtype=np.float64), np.asarray(dy, dtype=np.float64),
                                          ws_gate, ws_up, ws_down)
     return dict(dx=dX, dW_gate=a, dW_up=b, dW_down=c)
+
+
+# ----------------------------------------------------------------------------------------------
+# MXFP8 expert-level forward and backward
+# ----------------------------------------------------------------------------------------------
+# The Notes ("The production details") run the routed experts in MXFP8 in training, forward and
+# backward, without saying which operand is quantised along which axis. Reading taken here: every
+# grouped GEMM quantises both of its operands along its own contraction dimension (OCP MX blocks of
+# 32); activations are quantised from their high-precision values (bf16 inputs, the fp32 replay
+# a, u, h and the fp32 SwiGLU backward); the weights exist only as the forward's MX tensors, so
+# the backward re-quantises their dequantised values along its contraction axis. Along the slot
+# axis (weight gradients) the blocks start at each expert's first slot, the last one zero-padded.
+def mx_along(v, axis, quantize=True):
+    """MX round trip of v [n, m] along `axis` (0: down each column, 1: along each row). Blocks of
+    32 from index 0; a short last block is padded with zeros, which changes no block maximum."""
+    v = np.asarray(v, dtype=np.float64)
+    if not quantize:
+        return v
+    from .mx import mx_roundtrip, MX_BLOCK
+    w = v if axis == 1 else v.T
+    n = w.shape[1]
+    pad = (-n) % MX_BLOCK
+    if pad:
+        w = np.concatenate([w, np.zeros((w.shape[0], pad))], axis=1)
+    r = mx_roundtrip(w)[:, :n]
+    return r if axis == 1 else r.T
+
+
+def _mx_weights(wq, sc):
+    from .mx import mx_dequantize
+    return mx_dequantize(np.asarray(wq, dtype=np.uint8), np.asarray(sc, dtype=np.uint8))
+
+
+def experts_forward_mx(x_slot, counts, wq_gate, sc_gate, wq_up, sc_up, wq_down, sc_down, quantize=True):
+    """MXFP8 experts on slot rows (one expert-parallel rank's share): x quantised along D, the
+    gated activation h along I before the down projection; weights are the MX tensors
+    [E, I, D] (gate, up; blocks along D) and [E, D, I] (down; blocks along I). Unweighted outputs
+    per slot. quantize=False skips the activation round trips (the fp64 path on the same weights)."""
+    x_slot = np.asarray(x_slot, dtype=np.float64)
+    Wg, Wu, Wd = _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up), _mx_weights(wq_down, sc_down)
+    y = np.zeros_like(x_slot)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    for e in range(len(counts)):
+        a, b = off[e], off[e + 1]
+        if b <= a:
+            continue
+        Xq = mx_along(x_slot[a:b], 1, quantize)
+        H = silu(Xq @ Wg[e].T) * (Xq @ Wu[e].T)
+        y[a:b] = mx_along(H, 1, quantize) @ Wd[e].T
+    return y
+
+
+def experts_backward_mx(x_slot, counts, g, dy_slot, wq_gate, sc_gate, wq_up, sc_up, wq_down, sc_down,
+                        quantize=True):
+    """Backward of experts_forward_mx with router weights g per slot (each slot enters the loss as
+    g_j E_e(x_j) against dy_slot[j]), every GEMM in MXFP8 as read above:
+
+        replay     a = Q_D(x) W_gate^T,  u = Q_D(x) W_up^T,  h = SiLU(a) u
+        dgrad-down dh' = Q_D(dy) Q_D(W_down)                  (W_down [D, I] quantised down D)
+        dg         <h, dh'>                                    (fp64 here, fp32 on the device)
+        SwiGLU     dh = g dh',  da = dh u sig(a)(1 + a(1 - sig(a))),  du = dh SiLU(a)
+        dgrad-up   dx = Q_I(da) Q_I(W_gate) + Q_I(du) Q_I(W_up)    (W [I, D] quantised down I)
+        wgrad      dW_down = Q_n(g dy)^T Q_n(h),  dW_gate = Q_n(da)^T Q_n(x),  dW_up = Q_n(du)^T Q_n(x)
+
+    with Q_n blocks along the expert's slots. quantize=False makes every Q the identity, which is
+    experts_backward on the dequantised weights."""
+    x_slot = np.asarray(x_slot, dtype=np.float64)
+    dy_slot = np.asarray(dy_slot, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    Wg, Wu, Wd = _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up), _mx_weights(wq_down, sc_down)
+    S, D = x_slot.shape
+    E = len(counts)
+    I = Wg.shape[1]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    q = lambda v, ax: mx_along(v, ax, quantize)
+    dx = np.zeros((S, D))
+    dg = np.zeros(S)
+    dWg = np.zeros((E, I, D))
+    dWu = np.zeros((E, I, D))
+    dWd = np.zeros((E, D, I))
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        if b <= a:
+            continue
+        X, dy, ge = x_slot[a:b], dy_slot[a:b], g[a:b, None]
+        Xq = q(X, 1)
+        A = Xq @ Wg[e].T
+        U = Xq @ Wu[e].T
+        sg = sigmoid(A)
+        Sa = A * sg
+        H = Sa * U
+        dhp = q(dy, 1) @ q(Wd[e], 0)
+        dg[a:b] = np.einsum('ni,ni->n', H, dhp)
+        dh = ge * dhp
+        dA = dh * U * sg * (1.0 + A * (1.0 - sg))
+        dU = dh * Sa
+        dx[a:b] = q(dA, 1) @ q(Wg[e], 0) + q(dU, 1) @ q(Wu[e], 0)
+        dWd[e] = q(ge * dy, 0).T @ q(H, 0)
+        Xn = q(X, 0)
+        dWg[e] = q(dA, 0).T @ Xn
+        dWu[e] = q(dU, 0).T @ Xn
+    return dict(dx_slot=dx, dg=dg, dW_gate=dWg, dW_up=dWu, dW_down=dWd)
