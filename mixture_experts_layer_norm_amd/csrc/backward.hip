@@ -27,6 +27,9 @@ struct BwdLayout {
   size_t g_slot, dg_slot, x_slot, dy_slot, dx_slot, dx_sh;
   size_t act_a, act_u, dau, part, wdT, wguT, xT, dyT, ghT, dauT;
   size_t s_a, s_u, s_dau, s_part, s_wdT, s_wguT, s_xT, s_dyT, s_hT, s_dauT;
+  // MXFP8 routed experts: E4M3 codes (q) and E8M0 scales (s) of every backward GEMM operand
+  size_t mq_x, ms_x, mq_dy, ms_dy, m_dhp, m_h, m_daf, mq_dau, ms_dau, mq_wdT, ms_wdT, mq_wguT, ms_wguT;
+  size_t mq_xT, ms_xT, mq_gdyT, ms_gdyT, mq_hT, ms_hT, mq_dauT, ms_dauT;
   size_t total;
   int64_t n, Spad, Tpad;
 };
@@ -47,12 +50,27 @@ static BwdLayout bwd_layout(const moe_problem& p) {
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
   L.x_slot = take(n * D * 2); L.dy_slot = take(n * D * 2); L.dx_slot = take(n * D * 2);
   L.dx_sh = take(T * D * 2);
-  // fp32 replay a, u; [da | du | da_lo | du_lo] bf16; transposed padded x, dy, [g*h | lo], [da|du|lo]
-  L.act_a = take(n * I * 4); L.act_u = take(n * I * 4); L.dau = take(n * 4 * I * 2);
-  L.part = take(n * ((I + 127) / 128) * 4);
-  L.wdT = take(E * I * D * 2); L.wguT = take(E * D * 2 * I * 2);
-  L.xT = take(D * L.Spad * 2); L.dyT = take(D * L.Spad * 2); L.ghT = take(2 * I * L.Spad * 2);
-  L.dauT = take(4 * I * L.Spad * 2);
+  L.act_a = take(n * I * 4); L.act_u = take(n * I * 4);
+  if (p.dtype == MOE_MXFP8) {
+    // rows quantised along D; dgrad-down output and h, [da | du] in fp32; [da | du] along I;
+    // weights re-quantised transposed; slot-axis operands [features][Spad], experts 128-aligned
+    L.Spad = (n + 128 * E + 127) / 128 * 128;
+    const int64_t S = L.Spad;
+    L.mq_x = take(n * D); L.ms_x = take(n * D / 32); L.mq_dy = take(n * D); L.ms_dy = take(n * D / 32);
+    L.m_dhp = take(n * I * 4); L.m_h = take(n * I * 4); L.m_daf = take(n * 2 * I * 4);
+    L.mq_dau = take(n * 2 * I); L.ms_dau = take(n * 2 * I / 32);
+    L.mq_wdT = take(E * I * D); L.ms_wdT = take(E * I * D / 32);
+    L.mq_wguT = take(E * D * 2 * I); L.ms_wguT = take(E * D * 2 * I / 32);
+    L.mq_xT = take(D * S); L.ms_xT = take(D * S / 32); L.mq_gdyT = take(D * S); L.ms_gdyT = take(D * S / 32);
+    L.mq_hT = take(I * S); L.ms_hT = take(I * S / 32); L.mq_dauT = take(2 * I * S); L.ms_dauT = take(2 * I * S / 32);
+  } else {
+    // [da | du | da_lo | du_lo] bf16; transposed padded x, dy, [g*h | lo], [da|du|lo]
+    L.dau = take(n * 4 * I * 2);
+    L.part = take(n * ((I + 127) / 128) * 4);
+    L.wdT = take(E * I * D * 2); L.wguT = take(E * D * 2 * I * 2);
+    L.xT = take(D * L.Spad * 2); L.dyT = take(D * L.Spad * 2); L.ghT = take(2 * I * L.Spad * 2);
+    L.dauT = take(4 * I * L.Spad * 2);
+  }
   if (Is > 0) {
     L.s_a = take(T * Is * 4); L.s_u = take(T * Is * 4); L.s_dau = take(T * 4 * Is * 2);
     L.s_part = take(T * ((Is + 127) / 128) * 4);
@@ -139,6 +157,77 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   return launch_gemm_bf16_kgroup(w2, G, s);
 }
 
+// MXFP8 backward of the routed groups (the shared expert stays BF16). Weights are the forward's
+// MX tensors: W_gate, W_up [G][I][D] and W_down [G][D][I] with scales along their last axis.
+// Every GEMM takes both operands quantised along its own contraction dimension (blocks of 32):
+//   replay     a, u (fp32)   = Q_D(x) W_gate^T, Q_D(x) W_up^T
+//   dgrad-down dh' (fp32)    = Q_D(dy) Q_D(W_down^T)
+//   SwiGLU     da, du, h (fp32), Q_I([da | du]), dg = <h, dh'>
+//   dgrad-up   dx (bf16)     = Q_I([da | du]) Q_I([W_gate^T | W_up^T])^T
+//   wgrad      dW_down = Q_n(g dy)^T Q_n(h), [dW_gate; dW_up] = Q_n([da | du])^T Q_n(x)
+// with Q_n along each group's slots (poff: offsets padded to 128, one MX K slice).
+static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
+                            const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
+                            const moe_weights* w, void* dx_rows, float* dg_rows, float* dw_gate, float* dw_up,
+                            float* dw_down, char* ws, const BwdLayout& L, hipStream_t s) {
+  int st;
+  auto B = [&](size_t off) { return (uint8_t*)(ws + off); };
+  auto F = [&](size_t off) { return (float*)(ws + off); };
+  const int64_t S = L.Spad, ID = (int64_t)I * D;
+  // weights re-quantised along the backward contraction axis
+  if ((st = launch_mx_requant_t((const uint8_t*)w->w_down, w->sc_down, G, D, I, B(L.mq_wdT), B(L.ms_wdT), D, 0, ID, ID / 32, s))) return st;
+  if ((st = launch_mx_requant_t((const uint8_t*)w->w_gate, w->sc_gate, G, I, D, B(L.mq_wguT), B(L.ms_wguT), 2 * I, 0, 2 * ID, 2 * ID / 32, s)))
+    return st;
+  if ((st = launch_mx_requant_t((const uint8_t*)w->w_up, w->sc_up, G, I, D, B(L.mq_wguT), B(L.ms_wguT), 2 * I, I, 2 * ID, 2 * ID / 32, s)))
+    return st;
+  // slot rows quantised along D
+  if ((st = launch_quantize_mx((const uint16_t*)x_rows, n_cap, D, B(L.mq_x), B(L.ms_x), s))) return st;
+  if ((st = launch_quantize_mx((const uint16_t*)dy_rows, n_cap, D, B(L.mq_dy), B(L.ms_dy), s))) return st;
+
+  Grouped grp;
+  grp.row_off = offs;
+  grp.tile_off = tile_off;
+  grp.groups = G;
+  grp.max_mtiles = (n_cap + kGemmBM - 1) / kGemmBM + G;
+  GemmArgs r;   // replay
+  r.A = B(L.mq_x); r.lda = D; r.B = w->w_gate; r.B2 = w->w_up; r.ldb = D; r.b_group_stride = ID;
+  r.N = I; r.K = D; r.C = F(L.act_a); r.C2 = F(L.act_u); r.ldc = I;
+  if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s))) return st;
+  GemmArgs d;   // dgrad-down
+  d.A = B(L.mq_dy); d.lda = D; d.B = B(L.mq_wdT); d.ldb = D; d.b_group_stride = ID;
+  d.N = I; d.K = D; d.C = F(L.m_dhp); d.ldc = I; d.c_f32 = 1;
+  if ((st = launch_gemm_mx(d, B(L.ms_dy), B(L.ms_wdT), nullptr, ID / 32, nullptr, grp, EPI_STORE, s))) return st;
+  if ((st = launch_mx_swiglu_bwd(F(L.act_a), F(L.act_u), F(L.m_dhp), g_rows, n_cap, I, F(L.m_h), F(L.m_daf),
+                                 B(L.mq_dau), B(L.ms_dau), dg_rows, s)))
+    return st;
+  GemmArgs u;   // dgrad-up, K = 2I
+  u.A = B(L.mq_dau); u.lda = 2 * I; u.B = B(L.mq_wguT); u.ldb = 2 * I; u.b_group_stride = 2 * ID;
+  u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
+  if ((st = launch_gemm_mx(u, B(L.ms_dau), B(L.ms_wguT), nullptr, 2 * ID / 32, nullptr, grp, EPI_STORE, s))) return st;
+
+  // slot-axis operands of the weight gradients
+  if ((st = launch_mx_quant_t(MXT_BF16, x_rows, nullptr, nullptr, D, D, offs, poff, G, S, B(L.mq_xT), B(L.ms_xT), S, s)))
+    return st;
+  if ((st = launch_mx_quant_t(MXT_BF16_SCALED, dy_rows, nullptr, g_rows, D, D, offs, poff, G, S, B(L.mq_gdyT),
+                              B(L.ms_gdyT), S, s)))
+    return st;
+  if ((st = launch_mx_quant_t(MXT_F32, F(L.m_h), nullptr, nullptr, I, I, offs, poff, G, S, B(L.mq_hT), B(L.ms_hT), S, s)))
+    return st;
+  if ((st = launch_mx_quant_t(MXT_F32, F(L.m_daf), nullptr, nullptr, 2 * I, 2 * I, offs, poff, G, S, B(L.mq_dauT),
+                              B(L.ms_dauT), S, s)))
+    return st;
+  int32_t* order = G > 1 ? (int32_t*)(ws + L.order) : nullptr;
+  if (order && (st = launch_group_order(poff, G, order, s))) return st;
+  GemmArgs w1;  // dW_down [G][D][I]
+  w1.A = B(L.mq_gdyT); w1.lda = S; w1.B = B(L.mq_hT); w1.ldb = S; w1.k_off = poff; w1.k_order = order;
+  w1.M = D; w1.N = I; w1.C = dw_down; w1.ldc = I; w1.c_group_stride = ID;
+  if ((st = launch_gemm_mx_kgroup(w1, B(L.ms_gdyT), B(L.ms_hT), G, s))) return st;
+  GemmArgs w2;  // [dW_gate; dW_up] [G][I][D] each
+  w2.A = B(L.mq_dauT); w2.lda = S; w2.B = B(L.mq_xT); w2.ldb = S; w2.k_off = poff; w2.k_order = order;
+  w2.M = 2 * I; w2.N = D; w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = ID;
+  return launch_gemm_mx_kgroup(w2, B(L.ms_dauT), B(L.ms_xT), G, s);
+}
+
 static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
@@ -188,8 +277,10 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
                         void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
-  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
   if (!x_slot || !offsets || !w || !y_slot || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;
   if (p->I_shared > 0 && (!x_local || !shared_out || !w->ws_gate || !w->ws_up || !w->ws_down)) return MOE_ERR_INVALID_ARG;
   WsLayout L = ws_layout(*p);
@@ -208,6 +299,25 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   gr.tile_off = (const int32_t*)(wsb + L.tile_off);
   gr.groups = p->E;
   gr.max_mtiles = (slots + kGemmBM - 1) / kGemmBM + p->E;
+  if (mx) {
+    // slot rows quantised along D, then the forward's two block-scaled GEMMs (h quantised along I
+    // in the SwiGLU epilogue)
+    uint8_t* xq = (uint8_t*)(wsb + L.x_slot);
+    uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
+    uint8_t* hq = (uint8_t*)(wsb + L.h);
+    uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
+    if ((st = launch_quantize_mx((const uint16_t*)x_slot, slots, p->D, xq, xs, stream))) return st;
+    GemmArgs m1;
+    m1.A = xq; m1.lda = p->D; m1.B = w->w_gate; m1.B2 = w->w_up; m1.ldb = p->D;
+    m1.b_group_stride = (int64_t)p->I * p->D; m1.N = p->I; m1.K = p->D; m1.C = hq; m1.ldc = p->I;
+    if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream)))
+      return st;
+    GemmArgs m2;
+    m2.A = hq; m2.lda = p->I; m2.B = w->w_down; m2.ldb = p->I; m2.b_group_stride = (int64_t)p->D * p->I;
+    m2.N = p->D; m2.K = p->I; m2.C = y_slot; m2.ldc = p->D;
+    if ((st = launch_gemm_mx(m2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream)))
+      return st;
+  } else {
   GemmArgs g1;
   g1.A = x_slot; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
   g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = wsb + L.h; g1.ldc = p->I;
@@ -216,6 +326,7 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
   g2.N = p->D; g2.K = p->I; g2.C = y_slot; g2.ldc = p->D;
   if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream))) return st;
+  }
   if (p->I_shared > 0) {
     Grouped gs;
     gs.M = p->T;
@@ -237,9 +348,11 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
                          void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
-  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
   if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
+  if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;
   if (p->I_shared > 0 && (!x_local || !dy_local || !dx_local || !w->ws_gate || !w->ws_up || !w->ws_down ||
                           !dw->dws_gate || !dw->dws_up || !dw->dws_down))
@@ -252,12 +365,18 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
   char* wsb = (char*)ws;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(offsets, p->E, (int)slots, offs, (int32_t*)(wsb + L.tile_off),
-                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream)))
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
     return st;
-  if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
+  if (mx) {
+    if ((st = core_backward_mx(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
+                               (int32_t*)(wsb + L.poff), w, dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, wsb,
+                               L, stream)))
+      return st;
+  } else if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
                           (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down, dx_slot, dg_slot, dw->dw_gate,
-                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream)))
+                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream))) {
     return st;
+  }
   if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream);
   return MOE_OK;
 }

@@ -94,7 +94,7 @@ int launch_combine(const void* y_routes, const void* shared_out, const float* to
                    int T, int K, int D, int dtype, hipStream_t s);
 int launch_group_order(const int32_t* poff, int G, int32_t* order, hipStream_t s);
 int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean, int32_t* tile_off, int32_t* poff,
-                        int32_t* err, hipStream_t s);
+                        int32_t* err, hipStream_t s, int pad = 64);
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
                          const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
                          int64_t ldo, hipStream_t s, int split_lo = 0);
@@ -110,6 +110,15 @@ int launch_reverse_dispatch(const void* dx_slot, const int32_t* inv_perm, const 
 enum { TR_COPY = 0, TR_SCALE = 1, TR_SWIGLU = 2 };   // TR_SWIGLU reads fp32 a and u
 int launch_quantize_mx(const uint16_t* src, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                        hipStream_t s);
+// MXFP8 backward operands (mx_backward.hip)
+enum { MXT_BF16 = 0, MXT_BF16_SCALED = 1, MXT_F32 = 2, MXT_SWIGLU = 3 };
+int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, int C, uint8_t* out, uint8_t* osc,
+                        int64_t ldo, int64_t col0, int64_t out_bstride, int64_t osc_bstride, hipStream_t s);
+int launch_mx_quant_t(int mode, const void* src, const float* src2, const float* rscale, int64_t lds, int W,
+                      const int32_t* offs, const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc,
+                      int64_t ldo, hipStream_t s);
+int launch_mx_swiglu_bwd(const float* a, const float* u, const float* dhp, const float* g, int64_t n, int I, float* hf,
+                         float* daf, uint8_t* dq, uint8_t* dsc, float* dg, hipStream_t s);
 
 // grouped GEMM descriptor. The rows of group g are row_off[g] .. row_off[g+1]-1 of A (after the
 // optional gather); m-tiles of kGemmBM rows are numbered by tile_off (prefix over groups). With
@@ -176,6 +185,10 @@ int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int3
                         hipStream_t s);
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
                    int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s);
+// K-grouped MXFP8 weight gradients: A [M][lda] and B [N][ldb] E4M3 along K with scales
+// [M][lda / 32], [N][ldb / 32]; group g contracts k in [k_off[g], k_off[g+1]) (multiples of 128);
+// fp32 output as launch_gemm_bf16_kgroup.
+int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 
 }  // namespace moe

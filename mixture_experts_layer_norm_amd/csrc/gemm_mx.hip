@@ -98,7 +98,9 @@ __device__ __forceinline__ void mx_k_loop(const StageSrc<NL>& src, uint8_t* sm, 
   }
 }
 
-template <int EPI>
+// KG (weight gradients): tile `blockIdx.x` in launch order is n-tile fastest, then m-tile, then
+// group (groups in k_order, longest K first); group grp contracts k in [k_off[grp], k_off[grp+1]).
+template <int EPI, bool KG>
 __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
                                                          const uint8_t* __restrict__ b_sc,
                                                          const uint8_t* __restrict__ b2_sc, int64_t sc_group_stride,
@@ -107,29 +109,46 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int NL = BM / (C::RPI * 8);   // loads per operand per slice per wavefront
+  constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU;   // gate and up rows in one tile
   __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kGemmSmemElems + 2048];
   uint8_t* sm = reinterpret_cast<uint8_t*>(smem_u16);
-  // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
-  const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
-  const int per_xcd = (valid + 7) >> 3;
-  const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int logical = (bid & 7) * per_xcd + (bid >> 3);
-  if (logical >= valid) return;
-  TileCoord tc;
-  if (!decode_grouped_tile(g, logical, ntn, (g.M + BM - 1) / BM, tc)) return;
-  const int nt = tc.nt, grp = tc.grp, r0 = tc.r0, rows = tc.rows;
-  const int nk = a.K / 128;                      // 128-wide K slices
-  const int kbl = a.K / 32;                      // scale bytes per row
+  int nt, grp, r0, rows, nk, k0 = 0;
+  int64_t kbl;                                   // scale bytes per A / B row
+  if (KG) {
+    const int mtn = (a.M + BM - 1) / BM;
+    const int logical = blockIdx.x;
+    if (logical >= g.groups * mtn * ntn) return;
+    const int gi = logical / (mtn * ntn), rem = logical - gi * mtn * ntn;
+    grp = a.k_order ? a.k_order[gi] : gi;
+    const int mt = rem / ntn;
+    nt = rem - mt * ntn;
+    r0 = mt * BM;
+    rows = min(BM, a.M - r0);
+    k0 = a.k_off[grp];
+    nk = (a.k_off[grp + 1] - k0) / 128;
+    kbl = a.lda / 32;
+  } else {
+    // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
+    const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
+    const int per_xcd = (valid + 7) >> 3;
+    const int bid = blockIdx.x;
+    if ((bid >> 3) >= per_xcd) return;
+    const int logical = (bid & 7) * per_xcd + (bid >> 3);
+    if (logical >= valid) return;
+    TileCoord tc;
+    if (!decode_grouped_tile(g, logical, ntn, (g.M + BM - 1) / BM, tc)) return;
+    nt = tc.nt; grp = tc.grp; r0 = tc.r0; rows = tc.rows;
+    nk = a.K / 128;                              // 128-wide K slices
+    kbl = a.K / 32;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // Copies as 16-bit units (2 fp8 each): row offsets in units of lda / 2.
   StageSrc<NL> src;
-  src.abase = (const uint16_t*)a.A;
-  src.bbase[0] = (const uint16_t*)((const uint8_t*)a.B + (int64_t)grp * a.b_group_stride);
-  src.bbase[1] = (EPI == EPI_SWIGLU) ? (const uint16_t*)((const uint8_t*)a.B2 + (int64_t)grp * a.b_group_stride)
-                                     : src.bbase[0];
+  src.abase = (const uint16_t*)((const uint8_t*)a.A + k0);
+  src.bbase[0] = (const uint16_t*)((const uint8_t*)a.B + (KG ? 0 : (int64_t)grp * a.b_group_stride) + k0);
+  src.bbase[1] = PAIRED ? (const uint16_t*)((const uint8_t*)a.B2 + (int64_t)grp * a.b_group_stride) : src.bbase[0];
   src.nk1 = nk;
   src.a_shift = 0;
   src.b_shift = 0;
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
     const int r = r0 + min(rr, rows - 1);
     src.aoff[j] = (uint32_t)((int64_t)r * (a.lda / 2) + ch * 8);
     int64_t wrow;
-    if (EPI == EPI_SWIGLU) {
+    if (PAIRED) {
       const int wc = rr / WN, qq = (rr % WN) / 32;
       src.bup[j] = qq >= NJ / 2;
       wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (src.bup[j] ? qq - NJ / 2 : qq) * 32 + (rr & 31);
@@ -163,11 +182,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
     const int tr = 64 * (wave & 3) + lane;   // tile row whose words this lane copies
     if (wave < 4) {
       const int r = r0 + min(tr, rows - 1);
-      sc_src = reinterpret_cast<const uint32_t*>(a_sc) + (int64_t)r * kbl / 4;
+      sc_src = reinterpret_cast<const uint32_t*>(a_sc + (int64_t)r * kbl + k0 / 32);
     } else {
       int64_t wrow;
       bool up = false;
-      if (EPI == EPI_SWIGLU) {
+      if (PAIRED) {
         const int wc = tr / WN, qq = (tr % WN) / 32;
         up = qq >= NJ / 2;
         wrow = (int64_t)nt * (BN / 2) + wc * (WN / 2) + (up ? qq - NJ / 2 : qq) * 32 + (tr & 31);
@@ -175,8 +194,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
         wrow = (int64_t)nt * BN + tr;
       }
       wrow = wrow < a.N ? wrow : a.N - 1;
-      const uint8_t* base = (up ? b2_sc : b_sc) + (int64_t)grp * sc_group_stride;
-      sc_src = reinterpret_cast<const uint32_t*>(base) + wrow * kbl / 4;
+      const uint8_t* base = (up ? b2_sc : b_sc) + (KG ? 0 : (int64_t)grp * sc_group_stride);
+      sc_src = reinterpret_cast<const uint32_t*>(base + wrow * (KG ? (int64_t)(a.ldb / 32) : kbl) + k0 / 32);
     }
   }
   const int q = lane >> 5;
@@ -195,7 +214,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   const int a_srow = wm * WM + (lane & 31), b_srow = wn * WN + (lane & 31);   // tile rows of this lane's scales
   const int wrows_u = rows - (__builtin_amdgcn_readfirstlane(wave) / WAVES_N) * WM;
   const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
-  switch (nact) {
+  if (nk > 0) switch (nact) {
     case 0: mx_k_loop<EPI, 0, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
     case 1: mx_k_loop<EPI, 1, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
     case 2: mx_k_loop<EPI, 2, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
@@ -205,6 +224,41 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
 
   const int ccol = lane & 31;
   const int tid512 = threadIdx.x;
+  if (KG || EPI == EPI_SAVE_AU || (EPI == EPI_STORE && a.c_f32)) {
+    // fp32 outputs, element stores (the 32 lanes of a lane group cover 32 consecutive columns).
+    // Accumulator slot r of lane l: tile row (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
+#pragma clang loop unroll(full)
+    for (int i = 0; i < MI; ++i)
+#pragma clang loop unroll(full)
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + (r >> 2) * 8 + q * 4 + (r & 3);
+        if (lr >= rows) continue;
+        const int64_t row = r0 + lr;
+        if (EPI == EPI_SAVE_AU && !KG) {
+          const int64_t col = (int64_t)nt * (BN / 2) + wn * (WN / 2) + ccol;
+          if (col < a.N) {
+            ((float*)a.C)[row * a.ldc + col] = acc[i][0][r];
+            ((float*)a.C2)[row * a.ldc + col] = acc[i][1][r];
+          }
+        } else {
+          float* out = (float*)a.C;
+          int64_t orow = row;
+          if (KG) {
+            if (a.m_split > 0 && row >= a.m_split) {
+              out = (float*)a.C2;
+              orow = row - a.m_split;
+            }
+            out += (int64_t)grp * a.c_group_stride;
+          }
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int64_t col = (int64_t)nt * BN + wn * WN + j * 32 + ccol;
+            if (col < a.N) out[orow * a.ldc + col] = acc[i][j][r];
+          }
+        }
+      }
+    return;
+  }
   __syncthreads();   // every wavefront is done with the staged slices: LDS holds the output tile now
   if (EPI == EPI_SWIGLU) {
     // E4M3 h tile (256 rows x 128 bytes) through LDS, then 16-byte stores (4 per thread instead of
@@ -277,22 +331,43 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
 // a_sc / b_sc / b2_sc: E8M0 scales of A [rows][K/32] and of the weights [G][N][K/32].
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
                    int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s) {
-  const int tcols = (epi == EPI_SWIGLU) ? 128 : 256;
+  if (epi != EPI_SWIGLU && epi != EPI_STORE && epi != EPI_SAVE_AU) return MOE_ERR_UNSUPPORTED;
+  const bool paired = epi == EPI_SWIGLU || epi == EPI_SAVE_AU;
+  const int tcols = paired ? 128 : 256;
   const int ntn = (a.N + tcols - 1) / tcols;
   const int64_t mt = g.row_off ? g.max_mtiles : (g.M + BM - 1) / BM;
   int64_t nb = mt * ntn;
   nb = (nb + 7) / 8 * 8;
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  // the epilogue writes whole 16-byte chunks of output rows
-  const int64_t rowb = (epi == EPI_SWIGLU) ? 1 : 2;
+  // the bf16 / E4M3 epilogues write whole 16-byte chunks of output rows; fp32 ones single words
+  const int64_t rowb = epi == EPI_SWIGLU ? 1 : (epi == EPI_SAVE_AU || a.c_f32) ? 4 : 2;
   if ((reinterpret_cast<uintptr_t>(a.C) | (a.ldc * rowb) | (a.N * rowb)) & 15) return MOE_ERR_MISALIGNED;
   if (epi == EPI_SWIGLU)
-    hipLaunchKernelGGL(gemm_mx_kernel<EPI_SWIGLU>, dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
+    hipLaunchKernelGGL((gemm_mx_kernel<EPI_SWIGLU, false>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
+                       sc_group_stride, h_sc, g, ntn);
+  else if (epi == EPI_SAVE_AU)
+    hipLaunchKernelGGL((gemm_mx_kernel<EPI_SAVE_AU, false>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
                        sc_group_stride, h_sc, g, ntn);
   else
-    hipLaunchKernelGGL(gemm_mx_kernel<EPI_STORE>, dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
+    hipLaunchKernelGGL((gemm_mx_kernel<EPI_STORE, false>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
                        sc_group_stride, h_sc, g, ntn);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
+int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s) {
+  if (groups <= 0 || a.M <= 0 || a.N <= 0) return MOE_OK;
+  if ((a.lda | a.ldb) % 128 || a.ldc % 4 || (reinterpret_cast<uintptr_t>(a.C) & 15) ||
+      (a.C2 && (reinterpret_cast<uintptr_t>(a.C2) & 15)))
+    return MOE_ERR_MISALIGNED;
+  const int ntn = (a.N + BM - 1) / BM, mtn = (a.M + BM - 1) / BM;
+  const int64_t nb = (int64_t)groups * mtn * ntn;
+  if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  Grouped g;
+  g.groups = groups;
+  hipLaunchKernelGGL((gemm_mx_kernel<EPI_STORE, true>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b_sc,
+                     (int64_t)0, (uint8_t*)nullptr, g, ntn);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -9,56 +9,9 @@
 // exchanges), summed in a fixed order with no atomics (sparsenotes page, "The production
 // details", on determinism).
 #include "common.h"
+#include "mx_codec.h"
 
 namespace moe {
-
-// ---------------------------------------------------------------------------------------------
-// OCP MX v1.0 encoding helpers (E4M3 elements, E8M0 block scale, blocks of 32)
-// ---------------------------------------------------------------------------------------------
-// |v| already divided by the block scale -> E4M3 code, round to nearest even, saturate at 448.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (!(a < 448.0f)) return sign | 0x7eu;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
-    return sign | (uint32_t)rintf(a * 512.0f);   // 8 (== 2^-6) is also the first normal code
-  }
-  const uint32_t ua = __float_as_uint(a);
-  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;   // keep 3 mantissa bits, RNE
-  int code = (int)r - ((127 - 7) << 3);                         // rebias 127 -> 7
-  if (code > 0x7e) code = 0x7e;
-  return sign | (uint32_t)code;
-}
-
-// Block scale exponent for a block whose largest magnitude is amax (> 0):
-// floor(log2 amax) - 8, clamped to [-127, 127]. fp32 subnormals clamp to -127.
-__device__ __forceinline__ int mx_shared_exp(float amax) {
-  int eb = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-  int se = eb - 127 - 8;
-  return se < -127 ? -127 : (se > 127 ? 127 : se);
-}
-
-// Quantise 32 fp32 values (one block) into 32 codes packed in 8 words; returns the E8M0 byte.
-__device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* packed) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  if (amax == 0.f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed[i] = 0u;
-    return 127u;
-  }
-  const int se = mx_shared_exp(amax);
-  const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) w |= e4m3_code(v[4 * i + b] * inv) << (8 * b);
-    packed[i] = w;
-  }
-  return (uint32_t)(se + 127);
-}
 
 // ---------------------------------------------------------------------------------------------
 // dispatch

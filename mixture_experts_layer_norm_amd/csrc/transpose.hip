@@ -11,10 +11,11 @@ namespace moe {
 
 // Group bookkeeping from caller row offsets: a sanitised copy (offsets[0] taken as 0, every
 // offset clamped to [previous, rows], so no later kernel can index past the buffers; a change
-// sets the sticky error word), the m-tile prefix (kGemmBM rows) and the 64-padded offsets.
+// sets the sticky error word), the m-tile prefix (kGemmBM rows) and the offsets padded to a
+// multiple of `pad` (64 for the bf16 weight gradients, 128 for the MXFP8 ones).
 __global__ __launch_bounds__(1024) void group_prefix_kernel(const int32_t* __restrict__ offsets, int G, int rows,
                                                             int32_t* __restrict__ clean, int32_t* __restrict__ tile_off,
-                                                            int32_t* __restrict__ poff, int32_t* err) {
+                                                            int32_t* __restrict__ poff, int32_t* err, int pad) {
   __shared__ int sv[1024], sa[1024], sb[1024];
   const int t = threadIdx.x;
   const int raw = t < G ? offsets[t + 1] : 0;
@@ -32,7 +33,7 @@ __global__ __launch_bounds__(1024) void group_prefix_kernel(const int32_t* __res
   if (t < G && (v != raw || (t == 0 && offsets[0] != 0))) atomicOr(err, 2);
   const int n = t < G ? v - prev : 0;
   sa[t] = t < G ? (n + kGemmBM - 1) / kGemmBM : 0;
-  sb[t] = t < G ? (n + 63) / 64 * 64 : 0;
+  sb[t] = t < G ? (n + pad - 1) / pad * pad : 0;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
     const int a = t >= off ? sa[t - off] : 0;
@@ -80,8 +81,8 @@ int launch_group_order(const int32_t* poff, int G, int32_t* order, hipStream_t s
 }
 
 int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean, int32_t* tile_off, int32_t* poff,
-                        int32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(group_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, rows, clean, tile_off, poff, err);
+                        int32_t* err, hipStream_t s, int pad) {
+  hipLaunchKernelGGL(group_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, rows, clean, tile_off, poff, err, pad);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -354,8 +354,13 @@ def experts_forward_mx(x_slot, counts, wq_gate, sc_gate, wq_up, sc_up, wq_down, 
     gated activation h along I before the down projection; weights are the MX tensors
     [E, I, D] (gate, up; blocks along D) and [E, D, I] (down; blocks along I). Unweighted outputs
     per slot. quantize=False skips the activation round trips (the fp64 path on the same weights)."""
+    return experts_forward_mx_w(x_slot, counts, _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up),
+                                _mx_weights(wq_down, sc_down), quantize)
+
+
+def experts_forward_mx_w(x_slot, counts, Wg, Wu, Wd, quantize=True):
+    """experts_forward_mx on already dequantised MX weights Wg, Wu [E, I, D], Wd [E, D, I]."""
     x_slot = np.asarray(x_slot, dtype=np.float64)
-    Wg, Wu, Wd = _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up), _mx_weights(wq_down, sc_down)
     y = np.zeros_like(x_slot)
     off = np.concatenate([[0], np.cumsum(counts)])
     for e in range(len(counts)):
@@ -382,15 +387,26 @@ def experts_backward_mx(x_slot, counts, g, dy_slot, wq_gate, sc_gate, wq_up, sc_
 
     with Q_n blocks along the expert's slots. quantize=False makes every Q the identity, which is
     experts_backward on the dequantised weights."""
+    return experts_backward_mx_w(x_slot, counts, g, dy_slot, _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up),
+                                 _mx_weights(wq_down, sc_down), quantize)
+
+
+def experts_backward_mx_w(x_slot, counts, g, dy_slot, Wg, Wu, Wd, quantize=True, return_parts=False):
+    """experts_backward_mx on already dequantised MX weights Wg, Wu [E, I, D], Wd [E, D, I]. Row i
+    of dW_gate / dW_up and column i of dW_down depend only on rows i of Wg, Wu and column i of Wd
+    (every quantisation they meet runs down a single column), so they can be had from the
+    restriction to that unit. return_parts adds, per expert, the unquantised operands that are
+    computed rather than given (h, da, du, g dy) under 'parts'."""
     x_slot = np.asarray(x_slot, dtype=np.float64)
     dy_slot = np.asarray(dy_slot, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
-    Wg, Wu, Wd = _mx_weights(wq_gate, sc_gate), _mx_weights(wq_up, sc_up), _mx_weights(wq_down, sc_down)
+    Wg, Wu, Wd = (np.asarray(w, dtype=np.float64) for w in (Wg, Wu, Wd))
     S, D = x_slot.shape
     E = len(counts)
     I = Wg.shape[1]
     off = np.concatenate([[0], np.cumsum(counts)])
     q = lambda v, ax: mx_along(v, ax, quantize)
+    parts = {}
     dx = np.zeros((S, D))
     dg = np.zeros(S)
     dWg = np.zeros((E, I, D))
@@ -417,4 +433,9 @@ def experts_backward_mx(x_slot, counts, g, dy_slot, wq_gate, sc_gate, wq_up, sc_
         Xn = q(X, 0)
         dWg[e] = q(dA, 0).T @ Xn
         dWu[e] = q(dU, 0).T @ Xn
-    return dict(dx_slot=dx, dg=dg, dW_gate=dWg, dW_up=dWu, dW_down=dWd)
+        if return_parts:
+            parts[e] = dict(H=H, dA=dA, dU=dU, gdy=ge * dy)
+    res = dict(dx_slot=dx, dg=dg, dW_gate=dWg, dW_up=dWu, dW_down=dWd)
+    if return_parts:
+        res['parts'] = parts
+    return res

@@ -81,3 +81,17 @@ def test_backward_mx_close_to_fp64_and_zero_for_empty_expert():
         assert 1e-4 < rel < 0.15, (k, rel)      # quantised, but only by the E4M3 rounding
     for k in ('dW_gate', 'dW_up', 'dW_down'):
         assert np.all(got[k][1] == 0)
+
+
+def test_backward_mx_unit_restriction():
+    """Row i of dW_gate / dW_up and column i of dW_down from the expert restricted to unit i (rows
+    i of W_gate, W_up, column i of W_down) equal those of the whole expert: every quantisation on
+    their path runs down a single column. The full-size GPU test samples units this way."""
+    x, dy, g, counts, wg, wu, wd = _share(3, S=45, counts=(45,))
+    Wg, Wu, Wd = (oracle.mx_dequantize(*w) for w in (wg, wu, wd))
+    full = oracle.experts_backward_mx_w(x, counts, g, dy, Wg, Wu, Wd)
+    for i in (0, 7, 31):
+        ru = oracle.experts_backward_mx_w(x, counts, g, dy, Wg[:, i:i + 1], Wu[:, i:i + 1], Wd[:, :, i:i + 1])
+        np.testing.assert_allclose(ru['dW_gate'][0, 0], full['dW_gate'][0, i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(ru['dW_up'][0, 0], full['dW_up'][0, i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(ru['dW_down'][0, :, 0], full['dW_down'][0, :, i], rtol=1e-12, atol=1e-12)
