@@ -104,7 +104,7 @@ def main():
     ap.add_argument('--gpus', type=int, default=1)
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
-    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'mxfp8', 'ep_share'])
+    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'mxfp8', 'ep_share', 'ep_share_mxfp8'])
     ap.add_argument('--no-extra', action='store_true',
                     help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
@@ -123,8 +123,9 @@ def main():
     import synth
     import mixture_experts_layer_norm_amd as moe
 
-    if args.workload == 'ep_share':
-        print(json.dumps(bench_share(args.steps, args.warmup, args.flags)), flush=True)
+    if args.workload in ('ep_share', 'ep_share_mxfp8'):
+        dt = 'mxfp8' if args.workload == 'ep_share_mxfp8' else 'bf16'
+        print(json.dumps(bench_share(args.steps, args.warmup, args.flags, dt)), flush=True)
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
@@ -252,6 +253,7 @@ def main():
         del L, weights, ws, out
         torch.cuda.empty_cache()
         extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
+                 'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 
     line = {
@@ -386,20 +388,31 @@ def bench_pull_schedule(moe, stream, R=8, N=8192, K=8, L=32, reps=20):
             'routes_pulled': pulled, 'routes_per_s': n / (ms * 1e-3)}
 
 
-def bench_share(steps, warmup, flags):
+def bench_share(steps, warmup, flags, dtype='bf16'):
     """Forward + backward of one expert-parallel rank's share at the DSV3 shape (4 local experts,
     57,344 slots with Zipf(1.2) loads, shared expert on 7,168 tokens): moe_experts_forward then
-    moe_experts_backward per step, inputs resident in HBM. Returns a result dict."""
+    moe_experts_backward per step, inputs resident in HBM. dtype 'mxfp8': the routed experts in
+    MXFP8 forward and backward (weights quantised on the device beforehand, untimed), the shared
+    expert in BF16. Returns a result dict."""
     import torch
     import synth
     import mixture_experts_layer_norm_amd as moe
     cfg = synth.EP_SHARE
-    print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
+    print(f'[bench] generating {cfg.name} on the device ({dtype})', file=sys.stderr, flush=True)
     D_ = synth.device_share(cfg)
     S, E, I, D, Is, T = cfg.slots, cfg.E_local, cfg.I, cfg.D, cfg.I_shared, cfg.tokens
     offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(D_.counts)]).astype(np.int32)).cuda()
-    p = moe.problem(T, D, I, E, cfg.K, Is, 'bf16', 0, 0, flags)
-    W = moe.make_weights(D_.w_gate, D_.w_up, D_.w_down, D_.ws_gate, D_.ws_up, D_.ws_down)
+    p = moe.problem(T, D, I, E, cfg.K, Is, dtype, 0, 0, flags)
+    if dtype == 'mxfp8':
+        wq, wsc = [], []
+        for k in ('w_gate', 'w_up', 'w_down'):
+            wbf = getattr(D_, k)
+            wq.append(torch.empty(wbf.shape, dtype=torch.uint8, device='cuda'))
+            wsc.append(torch.empty(wbf.shape[:-1] + (wbf.shape[-1] // 32,), dtype=torch.uint8, device='cuda'))
+            moe.quantize_mx(wbf, wq[-1], wsc[-1])
+        W = moe.make_weights(*wq, D_.ws_gate, D_.ws_up, D_.ws_down, *wsc)
+    else:
+        W = moe.make_weights(D_.w_gate, D_.w_up, D_.w_down, D_.ws_gate, D_.ws_up, D_.ws_down)
     y = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
     sh = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
     ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device='cuda')
@@ -439,11 +452,15 @@ def bench_share(steps, warmup, flags):
     ms = f_ms + b_ms
     flops_f = 6.0 * S * D * I + 6.0 * T * D * Is
     flops = 3.0 * flops_f
-    print(f'[bench] ep share: fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms', file=sys.stderr, flush=True)
-    return {'workload': f'{cfg.name} forward+backward', 'tokens': T, 'slots': S, 'counts': D_.counts.tolist(),
-            'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms,
+    print(f'[bench] ep share ({dtype}): fwd {f_ms:.3f} ms, bwd {b_ms:.3f} ms', file=sys.stderr, flush=True)
+    # MXFP8: routed FLOPs priced at the MXFP8 peak, shared-expert FLOPs at the BF16 peak
+    t_peak = (3.0 * 6.0 * S * D * I / (PEAK_MXFP8_TFLOPS if dtype == 'mxfp8' else PEAK_BF16_TFLOPS)
+              + 3.0 * 6.0 * T * D * Is / PEAK_BF16_TFLOPS) / 1e12
+    name = cfg.name.replace('bf16', dtype) if dtype != 'bf16' else cfg.name
+    return {'workload': f'{name} forward+backward', 'dtype': dtype, 'tokens': T, 'slots': S,
+            'counts': D_.counts.tolist(), 'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms,
             'value': T / (ms * 1e-3), 'unit': 'tokens/s', 'slots_per_s': S / (ms * 1e-3),
-            'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': t_peak / (ms * 1e-3),
             'fwd_tflops': flops_f / (f_ms * 1e-3) / 1e12, 'bwd_tflops': 2 * flops_f / (b_ms * 1e-3) / 1e12}
 
 

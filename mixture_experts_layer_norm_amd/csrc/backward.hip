@@ -387,8 +387,10 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   int st = validate_routing(p);
   if (st) return st;
   (void)logits;   // the routing state of the forward carries everything the backward needs
-  if (p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8;
+  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
   if (!dout || !x || !w || !r || !dx || !dw || !d_topk_w) return MOE_ERR_INVALID_ARG;
+  if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (!r->topk_idx || !r->topk_w || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
   if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down || !dw->dws_gate || !dw->dws_up || !dw->dws_down))
@@ -404,13 +406,19 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   if ((st = launch_gather_f32(r->topk_w, r->perm, n, (float*)(wsb + L.g_slot), stream))) return st;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(r->offsets, p->E, (int)n, offs, (int32_t*)(wsb + L.tile_off),
-                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream)))
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
     return st;
-  if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
-                          (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down,
-                          wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down,
-                          routed_bufs(wsb, L), stream)))
+  if (mx) {
+    if ((st = core_backward_mx(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+                               (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
+                               (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream)))
+      return st;
+  } else if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+                                 (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up,
+                                 w->w_down, wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up,
+                                 dw->dw_down, routed_bufs(wsb, L), stream))) {
     return st;
+  }
   if ((st = launch_router_backward((float*)(wsb + L.dg_slot), r->inv_perm, r->topk_idx, r->topk_w, p->T, p->E, p->K,
                                    d_topk_w, d_logits, stream)))
     return st;

@@ -92,7 +92,7 @@ def allow_along(V, axis):
     return a if axis == 1 else a.T
 
 
-def backward_allowance(ref, x, counts, Wg, Wu, Wd, units=None):
+def backward_allowance(ref, x, counts, Wg, Wu, Wd, units=None, Xn=None):
     """Per-element allowance on dx_slot and the weight gradients for equally correct quantisation
     decisions on the operands the device computes in fp32 (da, du along I for dgrad-up; da, du,
     h and g dy along the slots for the weight gradients). units: restrict to one unit (the unit
@@ -102,10 +102,10 @@ def backward_allowance(ref, x, counts, Wg, Wu, Wd, units=None):
     mq = oracle.mx_along
     for e, P in ref['parts'].items():
         a, b = off[e], off[e + 1]
-        Xn = np.abs(mq(x[a:b], 0))
+        Xa = np.abs(mq(x[a:b], 0)) if Xn is None else np.abs(Xn)
         aA, aU = allow_along(P['dA'], 0), allow_along(P['dU'], 0)
-        al['dW_gate'][e] = aA.T @ Xn
-        al['dW_up'][e] = aU.T @ Xn
+        al['dW_gate'][e] = aA.T @ Xa
+        al['dW_up'][e] = aU.T @ Xa
         al['dW_down'][e] = allow_along(P['gdy'], 0).T @ np.abs(mq(P['H'], 0)) + \
             np.abs(mq(P['gdy'], 0)).T @ allow_along(P['H'], 0)
         if units is None:
@@ -164,7 +164,9 @@ def test_mx_ep_share_full_size_sampled(m):
     over 57,344 slots): weights quantised on the device and checked bit-exact against the oracle's
     encoder, then whole sampled slots (y, dx_slot, dg) and single intermediate units i of the
     largest and smallest expert (row i of dW_gate / dW_up, column i of dW_down over all the
-    expert's slots) against the oracle."""
+    expert's slots) against the oracle. The unit checks use the two smaller experts (8,109 and
+    5,741 slots, 64 and 45 K slices of the K-grouped GEMM): the oracle's quantisation of a whole
+    expert's x along both axes is the slow part of this test on the host."""
     cfg = synth.EP_SHARE
     print('[mx ep_share] generating full-size share inputs', flush=True)
     D_ = synth.device_share(cfg)
@@ -213,18 +215,68 @@ def test_mx_ep_share_full_size_sampled(m):
     al = backward_allowance(ref, xs, cnt, Wg, Wu, Wd)
     assert_close_rms(h64(dxs[idx]), ref['dx_slot'], TAU, 'mx ep dx_slot sampled', True, al['dx_slot'])
     assert_close_rms(dg[idx].cpu().numpy(), ref['dg'], TAU, 'mx ep dg sampled')
-    for e in (0, E - 1):
+    for e in (E - 2, E - 1):
         a, b = int(off[e]), int(off[e + 1])
         X, DY = h64(D_.x_slot[a:b]), h64(D_.dy_slot[a:b])
         Ge = D_.g[a:b].cpu().numpy().astype(np.float64)
-        for i in rng.choice(I, 2, replace=False):
+        Xn = oracle.mx_along(X, 0)
+        for i in rng.choice(I, 1, replace=False):
             print(f'[mx ep_share] oracle on expert {e} unit {i} ({b - a} slots)', flush=True)
             ru = oracle.experts_backward_mx_w(X, np.array([b - a]), Ge, DY, Wg[e:e + 1, i:i + 1], Wu[e:e + 1, i:i + 1],
                                               Wd[e:e + 1, :, i:i + 1], return_parts=True)
-            au = backward_allowance(ru, X, np.array([b - a]), None, None, None, units=True)
+            au = backward_allowance(ru, X, np.array([b - a]), None, None, None, units=True, Xn=Xn)
             assert_close_rms(gr['dw_gate'][e, i].cpu().numpy(), ru['dW_gate'][0, 0], TAU, f'mx ep dW_gate[{e},{i}]',
                              False, au['dW_gate'][0, 0])
             assert_close_rms(gr['dw_up'][e, i].cpu().numpy(), ru['dW_up'][0, 0], TAU, f'mx ep dW_up[{e},{i}]', False,
                              au['dW_up'][0, 0])
             assert_close_rms(gr['dw_down'][e, :, i].cpu().numpy(), ru['dW_down'][0, :, 0], TAU,
                              f'mx ep dW_down[{e},:,{i}]', False, au['dW_down'][0, :, 0])
+
+
+def test_mx_layer_backward(m):
+    """Whole-layer moe_backward in MXFP8 after the MXFP8 forward: the oracle's expert backward on
+    the dispatched slots (schedule of the oracle's own routing), reverse-dispatched and summed with
+    the BF16 shared expert's input gradient; router gradients from dg."""
+    from test_gpu_mxfp8 import MX_SMALL, mx_layer, run_mx_forward
+    cfg = MX_SMALL
+    print(f'[mx backward] layer {cfg.name}', flush=True)
+    H, q = mx_layer(cfg)
+    out, yr, rt, p, tensors = run_mx_forward(m, H, q)
+    T, K, D, E, I, Is = cfg.T, cfg.K, cfg.D, cfg.E, cfg.I, cfg.I_shared
+    dout_h = synth.host_dout(cfg, T)
+    W = m.make_weights(*tensors['wq'], *tensors['ws'], *tensors['sc'])
+    gr = dict(dw_gate=torch.full((E, I, D), float('nan'), device='cuda'),
+              dw_up=torch.full((E, I, D), float('nan'), device='cuda'),
+              dw_down=torch.full((E, D, I), float('nan'), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+    m.backward(p, bf(dout_h), tensors['x'], tensors['logits'], W, m.make_routing(*rt), dx, m.make_grads(**gr), dtw,
+               dlg, wsb)
+    torch.cuda.synchronize()
+    assert int(wsb[:4].view(torch.int32).item()) == 0
+    idx = oracle.route_topk(H.logits, K)
+    g = oracle.routing_weights(H.logits, idx)
+    counts, _, perm, inv = oracle.schedule(idx, E)
+    x64, d64 = H.x.astype(np.float64), dout_h.astype(np.float64)
+    Wg, Wu, Wd = (oracle.mx_dequantize(*q[k]) for k in ('w_gate', 'w_up', 'w_down'))
+    xs, dys, gs = x64[perm // K], d64[perm // K], g.ravel()[perm]
+    ref = oracle.experts_backward_mx_w(xs, counts, gs, dys, Wg, Wu, Wd, return_parts=True)
+    al = backward_allowance(ref, xs, counts, Wg, Wu, Wd)
+    rs = oracle.shared_backward(x64, d64, H.ws_gate, H.ws_up, H.ws_down)
+    dx_ref = ref['dx_slot'][inv].reshape(T, K, D).sum(axis=1) + rs['dx']
+    dx_al = al['dx_slot'][inv].reshape(T, K, D).sum(axis=1)
+    assert_close_rms(t2np(dx), dx_ref, TAU, 'mx layer dx', True, dx_al)
+    dg = ref['dg'][inv].reshape(T, K)
+    assert_close_rms(t2np(dtw), dg, TAU, 'mx layer d_topk_w')
+    dl = oracle.d_logits_from_dg(g, idx, dg, E)
+    assert_close_rms(t2np(dlg), dl, TAU, 'mx layer d_logits')
+    mask = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(mask, idx.astype(np.int64), True, axis=1)
+    assert np.all(t2np(dlg)[~mask] == 0)
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(gr[k.replace('dW', 'dw')]), ref[k], TAU, 'mx layer ' + k, False, al[k])
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(gr[k.replace('dW', 'dws')]), rs[k], TOL['bf16'], 'mx layer shared ' + k)
