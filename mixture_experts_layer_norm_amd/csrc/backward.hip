@@ -28,7 +28,7 @@ struct BwdLayout {
   size_t act_a, act_u, dau, part, wdT, wguT, xT, dyT, ghT, dauT;
   size_t s_a, s_u, s_dau, s_part, s_wdT, s_wguT, s_xT, s_dyT, s_hT, s_dauT;
   // MXFP8 routed experts: E4M3 codes (q) and E8M0 scales (s) of every backward GEMM operand
-  size_t mq_x, ms_x, mq_dy, ms_dy, m_dhp, m_h, m_daf, mq_dau, ms_dau, mq_wdT, ms_wdT, mq_wguT, ms_wguT;
+  size_t mq_x, ms_x, mq_dy, ms_dy, m_dhp, mq_dau, ms_dau, mq_wdT, ms_wdT, mq_wguT, ms_wguT;
   size_t mq_xT, ms_xT, mq_gdyT, ms_gdyT, mq_hT, ms_hT, mq_dauT, ms_dauT;
   size_t total;
   int64_t n, Spad, Tpad;
@@ -57,7 +57,7 @@ static BwdLayout bwd_layout(const moe_problem& p) {
     L.Spad = (n + 128 * E + 127) / 128 * 128;
     const int64_t S = L.Spad;
     L.mq_x = take(n * D); L.ms_x = take(n * D / 32); L.mq_dy = take(n * D); L.ms_dy = take(n * D / 32);
-    L.m_dhp = take(n * I * 4); L.m_h = take(n * I * 4); L.m_daf = take(n * 2 * I * 4);
+    L.m_dhp = take(n * I * 4); L.part = take(n * ((I + 255) / 256) * 4);
     L.mq_dau = take(n * 2 * I); L.ms_dau = take(n * 2 * I / 32);
     L.mq_wdT = take(E * I * D); L.ms_wdT = take(E * I * D / 32);
     L.mq_wguT = take(E * D * 2 * I); L.ms_wguT = take(E * D * 2 * I / 32);
@@ -162,7 +162,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
 // Every GEMM takes both operands quantised along its own contraction dimension (blocks of 32):
 //   replay     a, u (fp32)   = Q_D(x) W_gate^T, Q_D(x) W_up^T
 //   dgrad-down dh' (fp32)    = Q_D(dy) Q_D(W_down^T)
-//   SwiGLU     da, du, h (fp32), Q_I([da | du]), dg = <h, dh'>
+//   SwiGLU     da, du, h (fp32, registers only): Q_I([da | du]), Q_n(h), Q_n([da | du]), dg = <h, dh'>
 //   dgrad-up   dx (bf16)     = Q_I([da | du]) Q_I([W_gate^T | W_up^T])^T
 //   wgrad      dW_down = Q_n(g dy)^T Q_n(h), [dW_gate; dW_up] = Q_n([da | du])^T Q_n(x)
 // with Q_n along each group's slots (poff: offsets padded to 128, one MX K slice).
@@ -197,9 +197,12 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   d.A = B(L.mq_dy); d.lda = D; d.B = B(L.mq_wdT); d.ldb = D; d.b_group_stride = ID;
   d.N = I; d.K = D; d.C = F(L.m_dhp); d.ldc = I; d.c_f32 = 1;
   if ((st = launch_gemm_mx(d, B(L.ms_dy), B(L.ms_wdT), nullptr, ID / 32, nullptr, grp, EPI_STORE, s))) return st;
-  if ((st = launch_mx_swiglu_bwd(F(L.act_a), F(L.act_u), F(L.m_dhp), g_rows, n_cap, I, F(L.m_h), F(L.m_daf),
-                                 B(L.mq_dau), B(L.ms_dau), dg_rows, s)))
+  // SwiGLU backward: [da | du] quantised along I (dgrad-up), h and [da | du] along the slots
+  // (weight gradients), dg from per-tile partial sums
+  if ((st = launch_mx_swiglu_bwd_t(F(L.act_a), F(L.act_u), F(L.m_dhp), g_rows, I, offs, poff, G, S, B(L.mq_dau),
+                                   B(L.ms_dau), B(L.mq_hT), B(L.ms_hT), B(L.mq_dauT), B(L.ms_dauT), S, F(L.part), s)))
     return st;
+  if ((st = launch_row_sum(F(L.part), n_cap, (I + 255) / 256, dg_rows, s))) return st;
   GemmArgs u;   // dgrad-up, K = 2I
   u.A = B(L.mq_dau); u.lda = 2 * I; u.B = B(L.mq_wguT); u.ldb = 2 * I; u.b_group_stride = 2 * ID;
   u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
@@ -210,11 +213,6 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
     return st;
   if ((st = launch_mx_quant_t(MXT_BF16_SCALED, dy_rows, nullptr, g_rows, D, D, offs, poff, G, S, B(L.mq_gdyT),
                               B(L.ms_gdyT), S, s)))
-    return st;
-  if ((st = launch_mx_quant_t(MXT_F32, F(L.m_h), nullptr, nullptr, I, I, offs, poff, G, S, B(L.mq_hT), B(L.ms_hT), S, s)))
-    return st;
-  if ((st = launch_mx_quant_t(MXT_F32, F(L.m_daf), nullptr, nullptr, 2 * I, 2 * I, offs, poff, G, S, B(L.mq_dauT),
-                              B(L.ms_dauT), S, s)))
     return st;
   int32_t* order = G > 1 ? (int32_t*)(ws + L.order) : nullptr;
   if (order && (st = launch_group_order(poff, G, order, s))) return st;

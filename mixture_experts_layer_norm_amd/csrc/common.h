@@ -117,8 +117,9 @@ int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, in
 int launch_mx_quant_t(int mode, const void* src, const float* src2, const float* rscale, int64_t lds, int W,
                       const int32_t* offs, const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc,
                       int64_t ldo, hipStream_t s);
-int launch_mx_swiglu_bwd(const float* a, const float* u, const float* dhp, const float* g, int64_t n, int I, float* hf,
-                         float* daf, uint8_t* dq, uint8_t* dsc, float* dg, hipStream_t s);
+int launch_mx_swiglu_bwd_t(const float* a, const float* u, const float* dhp, const float* g, int I, const int32_t* offs,
+                           const int32_t* poff, int G, int64_t max_padded, uint8_t* dq, uint8_t* dsc, uint8_t* hq,
+                           uint8_t* hsc, uint8_t* daq, uint8_t* dasc, int64_t ldo, float* part, hipStream_t s);
 
 // grouped GEMM descriptor. The rows of group g are row_off[g] .. row_off[g+1]-1 of A (after the
 // optional gather); m-tiles of kGemmBM rows are numbered by tile_off (prefix over groups). With

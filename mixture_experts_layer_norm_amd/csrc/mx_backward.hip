@@ -9,14 +9,32 @@
 //   * mx_quant_t_kernel: an activation of the slot rows, grouped by expert, transposed and
 //     quantised along the slots: [cols][padded slots], each expert's slots starting at a multiple
 //     of 128 (one K slice of the MX GEMM), the padding zeros. Blocks start at the expert's first
-//     slot. Sources: x, g * dy, h = SiLU(a) u, or [da | du];
-//   * mx_swiglu_bwd_kernel: the SwiGLU backward of one slot row from the replayed a, u and the
-//     dgrad-down output dh' (all fp32): da, du (fp32, and quantised along I for dgrad-up), h
-//     (fp32) and the router-weight gradient dg = <h, dh'> summed in a fixed order.
+//     slot. Sources: x and g * dy (bf16; fp32 sources and h = SiLU(a) u are supported too);
+//   * mx_swiglu_bwd_t_kernel: the SwiGLU backward on a tile of 32 slots x 256 units from the
+//     replayed a, u and the dgrad-down output dh' (all fp32): da, du quantised along I for
+//     dgrad-up, and h, da, du quantised along the slots (the weight-gradient operands) from
+//     registers, so neither h nor [da | du] goes through HBM in fp32; the router-weight gradient
+//     dg = <h, dh'> as per-tile partial sums in a fixed order.
 #include "common.h"
 #include "mx_codec.h"
 
 namespace moe {
+
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD b % 8), each with its
+// own L2. The transposing kernels write each 128-byte line of an output row in 32-byte pieces
+// from neighbouring slot blocks; taking the tiles XCD-contiguously (XCD x takes tiles
+// [x per, (x + 1) per), slot block fastest) keeps the pieces of a line in one L2 so they leave it
+// as one line. Returns false for padding workgroups.
+__device__ __forceinline__ bool xcd_tile(int nsb, int ntiles, int& sb, int& ct) {
+  const int per = (ntiles + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (logical >= ntiles) return false;
+  sb = logical % nsb;
+  ct = logical / nsb;
+  return true;
+}
+
+static inline unsigned xcd_grid(int64_t ntiles) { return (unsigned)((ntiles + 7) / 8 * 8); }
 
 // Column pass shared by both transposing quantisers: tile[32][256] fp32 in LDS holds 32
 // consecutive rows of the source block; thread c quantises column c0 + c (32 values down the
@@ -63,7 +81,7 @@ __global__ __launch_bounds__(256) void mx_requant_t_kernel(const uint8_t* __rest
                     osc + (int64_t)g * osc_bstride + (int64_t)c * (ldo / 32) + (col0 + r0) / 32);
 }
 
-// grid (max padded slots / 32, ceil(W / 256)), 256 threads. Slot block [p0, p0 + 32) lies in the
+// (max padded slots / 32) x ceil(W / 256) tiles (xcd_tile), 256 threads. Slot block [p0, p0 + 32) lies in the
 // group g with poff[g] <= p0 < poff[g + 1]; its source rows are offs[g] + p0 - poff[g] + i while
 // below offs[g + 1] (zeros past it). Output row c (source column) at q + c * ldo + p0, scales at
 // sc + c * (ldo / 32) + p0 / 32.
@@ -71,10 +89,12 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(int mode, const void* _
                                                          const float* __restrict__ rscale, int64_t lds, int W,
                                                          const int32_t* __restrict__ offs, const int32_t* __restrict__ poff,
                                                          int G, uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
-                                                         int64_t ldo) {
+                                                         int64_t ldo, int nsb, int ntiles) {
   __shared__ float tile[32][257];
   const int tid = threadIdx.x;
-  const int p0 = blockIdx.x * 32, c0 = blockIdx.y * 256;
+  int sb, ct;
+  if (!xcd_tile(nsb, ntiles, sb, ct)) return;
+  const int p0 = sb * 32, c0 = ct * 256;
   if (p0 >= poff[G]) return;
   int lo = 0, hi = G - 1;   // last group with poff[g] <= p0 (empty groups have poff[g] == poff[g + 1])
   while (lo < hi) {
@@ -126,60 +146,129 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(int mode, const void* _
   if (c < W) quantise_column(tile, tid, q + (int64_t)c * ldo + p0, sc + (int64_t)c * (ldo / 32) + p0 / 32);
 }
 
-// One wavefront per slot row j < n: lane l takes the 32-element blocks b = l, l + 64, ... of the
-// I columns. da, du -> daf [n][2I] (fp32) and, quantised per block along I, dq [n][2I] codes +
-// dsc [n][2I / 32] (du blocks after the I / 32 da blocks); h -> hf [n][I]; dg[j] = <h, dh'>
-// (per-lane sums in column order, then a fixed butterfly across the wavefront).
-__global__ __launch_bounds__(256) void mx_swiglu_bwd_kernel(const float* __restrict__ a, const float* __restrict__ u,
-                                                            const float* __restrict__ dhp, const float* __restrict__ g,
-                                                            int64_t n, int I, float* __restrict__ hf,
-                                                            float* __restrict__ daf, uint8_t* __restrict__ dq,
-                                                            uint8_t* __restrict__ dsc, float* __restrict__ dg) {
-  const int lane = threadIdx.x & 63;
-  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= n) return;
-  const float gj = g[j];
-  const int nb = I / 32;
-  float part = 0.f;
-  for (int b = lane; b < nb; b += 64) {
-    const int64_t e0 = j * I + b * 32;
-    float da[32], du[32];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(a + e0 + 4 * c);
-      const f32x4 uv = *reinterpret_cast<const f32x4*>(u + e0 + 4 * c);
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(dhp + e0 + 4 * c);
-      f32x4 hv;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x = av[k], s = sigmoid_f(x), sa = x * s;
-        hv[k] = sa * uv[k];
-        part = fmaf(hv[k], pv[k], part);
-        const float dh = gj * pv[k];
-        da[4 * c + k] = dh * uv[k] * s * (1.f + x * (1.f - s));
-        du[4 * c + k] = dh * sa;
-      }
-      *reinterpret_cast<f32x4*>(hf + e0 + 4 * c) = hv;
-    }
-    const int64_t d0 = j * 2 * I + b * 32;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      *reinterpret_cast<f32x4*>(daf + d0 + 4 * c) = f32x4{da[4 * c], da[4 * c + 1], da[4 * c + 2], da[4 * c + 3]};
-      *reinterpret_cast<f32x4*>(daf + d0 + I + 4 * c) = f32x4{du[4 * c], du[4 * c + 1], du[4 * c + 2], du[4 * c + 3]};
-    }
-    uint32_t p[8];
-    dsc[j * (2 * nb) + b] = (uint8_t)mx_block(da, p);
-    u32x4* qd = reinterpret_cast<u32x4*>(dq + d0);
-    qd[0] = u32x4{p[0], p[1], p[2], p[3]};
-    qd[1] = u32x4{p[4], p[5], p[6], p[7]};
-    dsc[j * (2 * nb) + nb + b] = (uint8_t)mx_block(du, p);
-    qd = reinterpret_cast<u32x4*>(dq + d0 + I);
-    qd[0] = u32x4{p[0], p[1], p[2], p[3]};
-    qd[1] = u32x4{p[4], p[5], p[6], p[7]};
+// (max padded slots / 32) x ceil(I / 256) tiles (xcd_tile), 256 threads; thread t owns unit c = 256 ct + t of
+// the 32 slots [p0, p0 + 32) of one group (rows as in mx_quant_t_kernel, zeros past the group's
+// end). Per valid row: da, du quantised along I (32-unit blocks = 32-lane groups, amax by
+// shuffles), staged in LDS and written as 16-byte chunks into dq [n][2I] and the scale bytes into
+// dsc [n][2I / 32] (du after da); per unit: the 32 values of h, da, du down the
+// slots quantised into hq / daq (rows c and I + c of [2I][ldo]) with their scales; per row and
+// unit tile: part[r][ct] = sum over the tile's units of h dh' (wavefront butterflies, then the four
+// wavefronts in order).
+__global__ __launch_bounds__(256) void mx_swiglu_bwd_t_kernel(const float* __restrict__ a, const float* __restrict__ u,
+                                                              const float* __restrict__ dhp, const float* __restrict__ g,
+                                                              int I, const int32_t* __restrict__ offs,
+                                                              const int32_t* __restrict__ poff, int G,
+                                                              uint8_t* __restrict__ dq, uint8_t* __restrict__ dsc,
+                                                              uint8_t* __restrict__ hq, uint8_t* __restrict__ hsc,
+                                                              uint8_t* __restrict__ daq, uint8_t* __restrict__ dasc,
+                                                              int64_t ldo, float* __restrict__ part, int ntn, int nsb,
+                                                              int ntiles) {
+  __shared__ float wsum[4][32];
+  __shared__ __attribute__((aligned(16))) uint8_t rowq[32][512];   // row-quantised da | du codes of the tile
+  __shared__ uint8_t rows_sc[32][16];                               // and their scale bytes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int sb, ct;
+  if (!xcd_tile(nsb, ntiles, sb, ct)) return;
+  const int p0 = sb * 32;
+  if (p0 >= poff[G]) return;
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
   }
+  const int64_t rbase = (int64_t)offs[lo] + (p0 - poff[lo]);
+  const int64_t rend = offs[lo + 1];
+  const int c = ct * 256 + tid;
+  const bool cv = c < I;                 // whole 32-lane groups agree (I % 32 == 0)
+  const int nb = I / 32;
+  float hv[32], dav[32], duv[32];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  if (lane == 0) dg[j] = part;
+  for (int i = 0; i < 32; ++i) {
+    const int64_t r = rbase + i;
+    const bool rv = r < rend;            // uniform across the workgroup
+    float h = 0.f, da = 0.f, du = 0.f, pr = 0.f;
+    if (rv && cv) {
+      const float x = a[r * I + c], uu = u[r * I + c], p = dhp[r * I + c];
+      const float sg = sigmoid_f(x), sa = x * sg;
+      h = sa * uu;
+      pr = h * p;
+      const float dh = g[r] * p;
+      da = dh * uu * sg * (1.f + x * (1.f - sg));
+      du = dh * sa;
+    }
+    hv[i] = h;
+    dav[i] = da;
+    duv[i] = du;
+    if (rv) {
+      // row quantisation along I: the 32 lanes of this lane group hold one block of da and of du
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float v = half ? du : da;
+        float amax = fabsf(v);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        uint32_t code = 0, sbyte = 127;
+        if (amax > 0.f) {
+          const int se = mx_shared_exp(amax);
+          sbyte = (uint32_t)(se + 127);
+          code = e4m3_code(v * __uint_as_float((uint32_t)(127 - se) << 23));
+        }
+        rowq[i][half * 256 + tid] = (uint8_t)code;
+        if ((lane & 31) == 0) rows_sc[i][half * 8 + tid / 32] = (uint8_t)sbyte;
+      }
+      float s = pr;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) wsum[wave][i] = s;
+    }
+  }
+  if (cv) {
+    uint32_t pk[8];
+    u32x4* d;
+    hsc[(int64_t)c * (ldo / 32) + p0 / 32] = (uint8_t)mx_block(hv, pk);
+    d = reinterpret_cast<u32x4*>(hq + (int64_t)c * ldo + p0);
+    d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    d[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    dasc[(int64_t)c * (ldo / 32) + p0 / 32] = (uint8_t)mx_block(dav, pk);
+    d = reinterpret_cast<u32x4*>(daq + (int64_t)c * ldo + p0);
+    d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    d[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    dasc[(int64_t)(I + c) * (ldo / 32) + p0 / 32] = (uint8_t)mx_block(duv, pk);
+    d = reinterpret_cast<u32x4*>(daq + (int64_t)(I + c) * ldo + p0);
+    d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    d[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+  }
+  __syncthreads();
+  if (tid < 32 && rbase + tid < rend)
+    part[(rbase + tid) * ntn + ct] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+  // row-quantised codes: 16-byte chunks of the valid rows (32 rows x 2 halves x 16 chunks)
+  const int cw = min(256, I - ct * 256);   // units of this tile (a multiple of 32)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int qd = tid + 256 * k, i = qd >> 5, half = (qd >> 4) & 1, ch = qd & 15;
+    const int64_t r = rbase + i;
+    if (r < rend && ch * 16 < cw)
+      *reinterpret_cast<u32x4*>(dq + r * 2 * I + half * I + ct * 256 + ch * 16) =
+          *reinterpret_cast<const u32x4*>(&rowq[i][half * 256 + ch * 16]);
+  }
+  if (tid < 64) {
+    const int i = tid >> 1, half = tid & 1;
+    const int64_t r = rbase + i;
+    if (r < rend)
+      for (int b = 0; b < cw / 32; ++b) dsc[r * 2 * nb + half * nb + ct * 8 + b] = rows_sc[i][half * 8 + b];
+  }
+}
+
+int launch_mx_swiglu_bwd_t(const float* a, const float* u, const float* dhp, const float* g, int I, const int32_t* offs,
+                           const int32_t* poff, int G, int64_t max_padded, uint8_t* dq, uint8_t* dsc, uint8_t* hq,
+                           uint8_t* hsc, uint8_t* daq, uint8_t* dasc, int64_t ldo, float* part, hipStream_t s) {
+  if (max_padded <= 0) return MOE_OK;
+  if (I % 32 || max_padded % 32 || ldo % 128) return MOE_ERR_UNSUPPORTED;
+  const int ntn = (I + 255) / 256, nsb = (int)(max_padded / 32), ntiles = nsb * ntn;
+  hipLaunchKernelGGL(mx_swiglu_bwd_t_kernel, dim3(xcd_grid(ntiles)), dim3(256), 0, s, a, u, dhp, g, I, offs, poff, G, dq,
+                     dsc, hq, hsc, daq, dasc, ldo, part, ntn, nsb, ntiles);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, int C, uint8_t* out, uint8_t* osc,
@@ -197,18 +286,9 @@ int launch_mx_quant_t(int mode, const void* src, const float* src2, const float*
                       int64_t ldo, hipStream_t s) {
   if (max_padded <= 0 || W <= 0) return MOE_OK;
   if (max_padded % 32 || ldo % 128 || W % 8 || lds % 8) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_quant_t_kernel, dim3((unsigned)(max_padded / 32), (W + 255) / 256), dim3(256), 0, s, mode, src,
-                     src2, rscale, lds, W, offs, poff, G, q, sc, ldo);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
-}
-
-int launch_mx_swiglu_bwd(const float* a, const float* u, const float* dhp, const float* g, int64_t n, int I, float* hf,
-                         float* daf, uint8_t* dq, uint8_t* dsc, float* dg, hipStream_t s) {
-  if (n <= 0) return MOE_OK;
-  if (I % 32) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mx_swiglu_bwd_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, a, u, dhp, g, n, I, hf, daf,
-                     dq, dsc, dg);
+  const int nsb = (int)(max_padded / 32), ntiles = nsb * ((W + 255) / 256);
+  hipLaunchKernelGGL(mx_quant_t_kernel, dim3(xcd_grid(ntiles)), dim3(256), 0, s, mode, src, src2, rscale, lds, W, offs,
+                     poff, G, q, sc, ldo, nsb, ntiles);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }
