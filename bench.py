@@ -240,6 +240,7 @@ def main():
     roof['hbm_frac'] = b_dom / t_dom / 1e9 / PEAK_HBM_GBS
 
     pc = standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream) if cfg.dtype == 'bf16' else None
+    yl = second_stream_latency(step, stream) if (not args.no_extra and args.workload == 'dsv3') else None
 
     # per-step spread from the in-order run (sum of its stage events)
     per_step = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(n_attr)])
@@ -252,7 +253,8 @@ def main():
         rg = bench_route_gemm(moe, cfg, L.x, stream)
         del L, weights, ws, out
         torch.cuda.empty_cache()
-        extra = {'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
+        extra = {'second_stream_latency': yl,
+                 'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
                  'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 
@@ -462,6 +464,48 @@ def bench_share(steps, warmup, flags, dtype='bf16'):
             'value': T / (ms * 1e-3), 'unit': 'tokens/s', 'slots_per_s': S / (ms * 1e-3),
             'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': t_peak / (ms * 1e-3),
             'fwd_tflops': flops_f / (f_ms * 1e-3) / 1e12, 'bwd_tflops': 2 * flops_f / (b_ms * 1e-3) / 1e12}
+
+
+def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10):
+    """Latency of a small kernel (an in-place add over 4 MB) enqueued on a second default-priority
+    stream while moe_forward runs on the library's stream, `delay` ms after the forward was
+    enqueued. The forward's GEMMs are one tile per workgroup, so the dispatcher can hand a CU to
+    the other stream at every tile boundary; no yield flag is involved. Probes that did not start
+    inside the forward are dropped."""
+    import torch
+    other = torch.cuda.Stream()
+    small = torch.zeros(1 << 20, device='cuda')
+
+    def probe():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(other)
+        with torch.cuda.stream(other):
+            small.add_(1.0)
+        e1.record(other)
+        return e0, e1
+
+    alone = []
+    for _ in range(trials):
+        e0, e1 = probe()
+        torch.cuda.synchronize()
+        alone.append(e0.elapsed_time(e1) * 1e3)
+    res = {'probe': 'in-place add over 1M fp32 on a second default-priority stream',
+           'alone_us_median': float(np.median(alone))}
+    for d in delays_ms:
+        lat = []
+        for _ in range(trials):
+            fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            fa.record(stream)
+            step()
+            fb.record(stream)
+            time.sleep(d / 1e3)
+            e0, e1 = probe()
+            torch.cuda.synchronize()
+            if fa.elapsed_time(e0) > 0 and e0.elapsed_time(fb) > 0:
+                lat.append(e0.elapsed_time(e1) * 1e3)
+        res[f'after_{d:g}ms'] = ({'probes': len(lat), 'median_us': float(np.median(lat)),
+                                  'max_us': float(np.max(lat))} if lat else {'probes': 0})
+    return res
 
 
 def cpu_baseline(cfg, L, ntok):
