@@ -180,9 +180,14 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
     return st;
   if ((st = launch_mx_requant_t((const uint8_t*)w->w_up, w->sc_up, G, I, D, B(L.mq_wguT), B(L.ms_wguT), 2 * I, I, 2 * ID, 2 * ID / 32, s)))
     return st;
-  // slot rows quantised along D
-  if ((st = launch_quantize_mx((const uint16_t*)x_rows, n_cap, D, B(L.mq_x), B(L.ms_x), s))) return st;
-  if ((st = launch_quantize_mx((const uint16_t*)dy_rows, n_cap, D, B(L.mq_dy), B(L.ms_dy), s))) return st;
+  // x and dy: along D (dgrad operands) and, in the same pass, x and g dy along the slots
+  // (weight-gradient operands)
+  if ((st = launch_mx_quant_t((const uint16_t*)x_rows, nullptr, D, D, offs, poff, G, S, B(L.mq_xT), B(L.ms_xT), S,
+                              B(L.mq_x), B(L.ms_x), s)))
+    return st;
+  if ((st = launch_mx_quant_t((const uint16_t*)dy_rows, g_rows, D, D, offs, poff, G, S, B(L.mq_gdyT), B(L.ms_gdyT), S,
+                              B(L.mq_dy), B(L.ms_dy), s)))
+    return st;
 
   Grouped grp;
   grp.row_off = offs;
@@ -208,12 +213,6 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
   if ((st = launch_gemm_mx(u, B(L.ms_dau), B(L.ms_wguT), nullptr, 2 * ID / 32, nullptr, grp, EPI_STORE, s))) return st;
 
-  // slot-axis operands of the weight gradients
-  if ((st = launch_mx_quant_t(MXT_BF16, x_rows, nullptr, nullptr, D, D, offs, poff, G, S, B(L.mq_xT), B(L.ms_xT), S, s)))
-    return st;
-  if ((st = launch_mx_quant_t(MXT_BF16_SCALED, dy_rows, nullptr, g_rows, D, D, offs, poff, G, S, B(L.mq_gdyT),
-                              B(L.ms_gdyT), S, s)))
-    return st;
   int32_t* order = G > 1 ? (int32_t*)(ws + L.order) : nullptr;
   if (order && (st = launch_group_order(poff, G, order, s))) return st;
   GemmArgs w1;  // dW_down [G][D][I]

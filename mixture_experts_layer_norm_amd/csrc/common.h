@@ -111,12 +111,11 @@ enum { TR_COPY = 0, TR_SCALE = 1, TR_SWIGLU = 2 };   // TR_SWIGLU reads fp32 a a
 int launch_quantize_mx(const uint16_t* src, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                        hipStream_t s);
 // MXFP8 backward operands (mx_backward.hip)
-enum { MXT_BF16 = 0, MXT_BF16_SCALED = 1, MXT_F32 = 2, MXT_SWIGLU = 3 };
 int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, int C, uint8_t* out, uint8_t* osc,
                         int64_t ldo, int64_t col0, int64_t out_bstride, int64_t osc_bstride, hipStream_t s);
-int launch_mx_quant_t(int mode, const void* src, const float* src2, const float* rscale, int64_t lds, int W,
-                      const int32_t* offs, const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc,
-                      int64_t ldo, hipStream_t s);
+int launch_mx_quant_t(const uint16_t* src, const float* rscale, int64_t lds, int W, const int32_t* offs,
+                      const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc, int64_t ldo, uint8_t* rq,
+                      uint8_t* rsc, hipStream_t s);
 int launch_mx_swiglu_bwd_t(const float* a, const float* u, const float* dhp, const float* g, int I, const int32_t* offs,
                            const int32_t* poff, int G, int64_t max_padded, uint8_t* dq, uint8_t* dsc, uint8_t* hq,
                            uint8_t* hsc, uint8_t* daq, uint8_t* dasc, int64_t ldo, float* part, hipStream_t s);

@@ -18,22 +18,9 @@
 // blocks of one row and slice) are copied into LDS beside the slice (one 4-byte LDS-direct load
 // per wavefront), and each lane shifts its byte into place.
 #include "gemm_tile.h"
+#include "mx_codec.h"
 
 namespace moe {
-
-// Quantised E4M3 code of v / 2^se (saturating, RNE); same rule as the dispatch quantiser.
-__device__ __forceinline__ uint32_t e4m3_code_scaled(float v, float inv_scale) {
-  const float s = v * inv_scale;
-  const uint32_t sign = (__float_as_uint(s) >> 24) & 0x80u;
-  const float a = fabsf(s);
-  if (!(a < 448.0f)) return sign | 0x7eu;
-  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
-  const uint32_t ua = __float_as_uint(a);
-  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
-  int code = (int)r - ((127 - 7) << 3);
-  if (code > 0x7e) code = 0x7e;
-  return sign | (uint32_t)code;
-}
 
 // The K loop of an MX tile: 2 LDS stages. In step kt, once slice kt and its scale words have
 // landed and the barrier has made every thread's copies visible, slice kt + 1 and its scale words
@@ -282,7 +269,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
           int se = eb - 127 - 8;
           se = se < -127 ? -127 : (se > 127 ? 127 : se);
           sbyte = (uint32_t)(se + 127);
-          code = e4m3_code_scaled(h, __uint_as_float((uint32_t)(127 - se) << 23));
+          code = e4m3_code(h * __uint_as_float((uint32_t)(127 - se) << 23));
         }
         sm[lr * 128 + (((c >> 4) ^ (((lr >> 2) & 3) << 1)) << 4) + (c & 15)] = (uint8_t)code;
         const int64_t col = (int64_t)nt * (BN / 2) + c;

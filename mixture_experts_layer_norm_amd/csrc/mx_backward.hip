@@ -6,10 +6,11 @@
 //   * mx_requant_t_kernel: a forward MX weight [R][C] (blocks along C) dequantised and quantised
 //     again along R into its transpose [C][R] (W_down along D for dgrad-down, W_gate / W_up
 //     along I for dgrad-up);
-//   * mx_quant_t_kernel: an activation of the slot rows, grouped by expert, transposed and
-//     quantised along the slots: [cols][padded slots], each expert's slots starting at a multiple
-//     of 128 (one K slice of the MX GEMM), the padding zeros. Blocks start at the expert's first
-//     slot. Sources: x and g * dy (bf16; fp32 sources and h = SiLU(a) u are supported too);
+//   * mx_quant_t_kernel: a bf16 activation of the slot rows (x, or dy scaled by g), grouped by
+//     expert, transposed and quantised along the slots: [cols][padded slots], each expert's slots
+//     starting at a multiple of 128 (one K slice of the MX GEMM), the padding zeros, blocks from
+//     the expert's first slot; in the same pass the unscaled rows quantised along the features
+//     (the dgrad operands Q_D(x), Q_D(dy)), so each is read once;
 //   * mx_swiglu_bwd_t_kernel: the SwiGLU backward on a tile of 32 slots x 256 units from the
 //     replayed a, u and the dgrad-down output dh' (all fp32): da, du quantised along I for
 //     dgrad-up, and h, da, du quantised along the slots (the weight-gradient operands) from
@@ -81,20 +82,27 @@ __global__ __launch_bounds__(256) void mx_requant_t_kernel(const uint8_t* __rest
                     osc + (int64_t)g * osc_bstride + (int64_t)c * (ldo / 32) + (col0 + r0) / 32);
 }
 
-// (max padded slots / 32) x ceil(W / 256) tiles (xcd_tile), 256 threads. Slot block [p0, p0 + 32) lies in the
-// group g with poff[g] <= p0 < poff[g + 1]; its source rows are offs[g] + p0 - poff[g] + i while
-// below offs[g + 1] (zeros past it). Output row c (source column) at q + c * ldo + p0, scales at
-// sc + c * (ldo / 32) + p0 / 32.
-__global__ __launch_bounds__(256) void mx_quant_t_kernel(int mode, const void* __restrict__ src, const float* __restrict__ src2,
-                                                         const float* __restrict__ rscale, int64_t lds, int W,
-                                                         const int32_t* __restrict__ offs, const int32_t* __restrict__ poff,
-                                                         int G, uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
-                                                         int64_t ldo, int nsb, int ntiles) {
-  __shared__ float tile[32][257];
+// (max padded slots / 128) x ceil(W / 64) tiles (xcd_tile), 256 threads: a bf16 source block of
+// 128 padded slot positions (one group's: poff is 128-aligned) x 64 features. Rows are
+// offs[g] + p - poff[g] while below offs[g + 1]; past that the block holds zeros. Outputs:
+//   * along the slots: feature c's 32-slot blocks -> q + c * ldo + p (codes) and
+//     sc + c * (ldo / 32) + p / 32 (scales); with rscale the values are rscale[row] * src; four
+//     neighbouring threads write one 128-byte line of an output row;
+//   * along the features (rq != nullptr): each valid row's two 32-feature blocks -> rq + row * W +
+//     c0 (codes) and rsc + row * (W / 32) + c0 / 32 (scales), from the unscaled source.
+// The fp32 tile row r sits at r * 65 + (r / 32) * 8, so the four slot blocks a column read touches
+// fall on different banks.
+__global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ src, const float* __restrict__ rscale,
+                                                         int64_t lds, int W, const int32_t* __restrict__ offs,
+                                                         const int32_t* __restrict__ poff, int G, uint8_t* __restrict__ q,
+                                                         uint8_t* __restrict__ sc, int64_t ldo, uint8_t* __restrict__ rq,
+                                                         uint8_t* __restrict__ rsc, int nsb, int ntiles) {
+  __shared__ float tile[128 * 65 + 32];
+  __shared__ float rs[128];   // row scales of the block (1 without rscale or past the group's end)
   const int tid = threadIdx.x;
   int sb, ct;
   if (!xcd_tile(nsb, ntiles, sb, ct)) return;
-  const int p0 = sb * 32, c0 = ct * 256;
+  const int p0 = sb * 128, c0 = ct * 64;
   if (p0 >= poff[G]) return;
   int lo = 0, hi = G - 1;   // last group with poff[g] <= p0 (empty groups have poff[g] == poff[g + 1])
   while (lo < hi) {
@@ -103,47 +111,50 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(int mode, const void* _
   }
   const int64_t rbase = (int64_t)offs[lo] + (p0 - poff[lo]);
   const int64_t rend = offs[lo + 1];
-  if (mode == MXT_F32 || mode == MXT_SWIGLU) {
-    // 32 rows x 64 chunks of 4 floats, 8 per thread
+  auto at = [](int r, int c) { return r * 65 + (r >> 5) * 8 + c; };
+  if (tid < 128) rs[tid] = (rscale && rbase + tid < rend) ? rscale[rbase + tid] : 1.f;
+  // 128 rows x 8 chunks of 8 bf16, 4 per thread
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int qd = tid + 256 * k, i = qd >> 6, cc = (qd & 63) * 4;
-      const int64_t r = rbase + i;
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (r < rend && c0 + cc < W) {
-        v = *reinterpret_cast<const f32x4*>((const float*)src + r * lds + c0 + cc);
-        if (mode == MXT_SWIGLU) {
-          const f32x4 u = *reinterpret_cast<const f32x4*>(src2 + r * lds + c0 + cc);
+  for (int k = 0; k < 4; ++k) {
+    const int qd = tid + 256 * k, i = qd >> 3, cc = (qd & 7) * 8;
+    const int64_t r = rbase + i;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (r < rend && c0 + cc < W) w = *reinterpret_cast<const u32x4*>(src + r * lds + c0 + cc);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) v[b] = silu_f(v[b]) * u[b];
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tile[i][cc + b] = v[b];
-    }
-  } else {
-    // bf16: 32 rows x 32 chunks of 8, 4 per thread; MXT_BF16_SCALED multiplies by rscale[row]
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int qd = tid + 256 * k, i = qd >> 5, cc = (qd & 31) * 8;
-      const int64_t r = rbase + i;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (r < rend && c0 + cc < W) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>((const uint16_t*)src + r * lds + c0 + cc);
-        const float f = mode == MXT_BF16_SCALED ? rscale[r] : 1.f;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          v[2 * b] = __uint_as_float(w[b] << 16) * f;
-          v[2 * b + 1] = __uint_as_float(w[b] & 0xffff0000u) * f;
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < 8; ++b) tile[i][cc + b] = v[b];
+    for (int b = 0; b < 4; ++b) {
+      tile[at(i, cc + 2 * b)] = __uint_as_float(w[b] << 16);
+      tile[at(i, cc + 2 * b + 1)] = __uint_as_float(w[b] & 0xffff0000u);
     }
   }
   __syncthreads();
-  const int c = c0 + tid;
-  if (c < W) quantise_column(tile, tid, q + (int64_t)c * ldo + p0, sc + (int64_t)c * (ldo / 32) + p0 / 32);
+  uint32_t pk[8];
+  if (rq) {
+    // along the features: row i, block b (unscaled source)
+    const int i = tid >> 1, b = tid & 1;
+    const int64_t r = rbase + i;
+    if (r < rend && c0 + 32 * b < W) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = tile[at(i, 32 * b + j)];
+      rsc[r * (W / 32) + c0 / 32 + b] = (uint8_t)mx_block(v, pk);
+      u32x4* d = reinterpret_cast<u32x4*>(rq + r * W + c0 + 32 * b);
+      d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      d[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    }
+  }
+  {
+    // along the slots: feature c, slot block k
+    const int c = tid >> 2, k = tid & 3;
+    if (c0 + c < W) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = tile[at(32 * k + j, c)] * rs[32 * k + j];
+      sc[(int64_t)(c0 + c) * (ldo / 32) + (p0 >> 5) + k] = (uint8_t)mx_block(v, pk);
+      u32x4* d = reinterpret_cast<u32x4*>(q + (int64_t)(c0 + c) * ldo + p0 + 32 * k);
+      d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      d[1] = u32x4{pk[4], pk[5], pk[6], pk[7]};
+    }
+  }
 }
 
 // (max padded slots / 32) x ceil(I / 256) tiles (xcd_tile), 256 threads; thread t owns unit c = 256 ct + t of
@@ -281,14 +292,14 @@ int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, in
   return MOE_OK;
 }
 
-int launch_mx_quant_t(int mode, const void* src, const float* src2, const float* rscale, int64_t lds, int W,
-                      const int32_t* offs, const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc,
-                      int64_t ldo, hipStream_t s) {
+int launch_mx_quant_t(const uint16_t* src, const float* rscale, int64_t lds, int W, const int32_t* offs,
+                      const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc, int64_t ldo, uint8_t* rq,
+                      uint8_t* rsc, hipStream_t s) {
   if (max_padded <= 0 || W <= 0) return MOE_OK;
-  if (max_padded % 32 || ldo % 128 || W % 8 || lds % 8) return MOE_ERR_UNSUPPORTED;
-  const int nsb = (int)(max_padded / 32), ntiles = nsb * ((W + 255) / 256);
-  hipLaunchKernelGGL(mx_quant_t_kernel, dim3(xcd_grid(ntiles)), dim3(256), 0, s, mode, src, src2, rscale, lds, W, offs,
-                     poff, G, q, sc, ldo, nsb, ntiles);
+  if (max_padded % 128 || ldo % 128 || W % 32 || lds % 8) return MOE_ERR_UNSUPPORTED;
+  const int nsb = (int)(max_padded / 128), ntiles = nsb * ((W + 63) / 64);
+  hipLaunchKernelGGL(mx_quant_t_kernel, dim3(xcd_grid(ntiles)), dim3(256), 0, s, src, rscale, lds, W, offs, poff, G, q,
+                     sc, ldo, rq, rsc, nsb, ntiles);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -1,24 +1,27 @@
 // OCP Microscaling v1.0 encoding on the device (E4M3 elements, E8M0 block scale, blocks of 32):
 // the MXFP8 format the sparsenotes page "Mixture-of-Kittens: MoE Megakernel for NVL72s" names in
-// "The production details". Shared by the dispatch quantiser and the MXFP8 backward kernels.
+// "The production details". Shared by the dispatch quantiser, the MXFP8 GEMM's SwiGLU epilogue
+// and the MXFP8 backward kernels.
 #pragma once
 #include "common.h"
 
 namespace moe {
 
-// |v| already divided by the block scale -> E4M3 code, round to nearest even, saturate at 448.
+// |v| already divided by the block scale -> E4M3 code, round to nearest even, saturate at 448
+// (NaN and infinities saturate too). Branch-free: both candidate codes are formed and one is
+// selected, so a wavefront quantising a block takes no divergent branches.
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
   const float a = fabsf(v);
-  if (!(a < 448.0f)) return sign | 0x7eu;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
-    return sign | (uint32_t)rintf(a * 512.0f);   // 8 (== 2^-6) is also the first normal code
-  }
   const uint32_t ua = __float_as_uint(a);
-  uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;   // keep 3 mantissa bits, RNE
-  int code = (int)r - ((127 - 7) << 3);                         // rebias 127 -> 7
-  if (code > 0x7e) code = 0x7e;
-  return sign | (uint32_t)code;
+  // normal range (a >= 2^-6): keep 3 mantissa bits, round to nearest even, rebias 127 -> 7, cap
+  // at 0x7e (448); a >= 2^-6 gives r >= 121 << 3, so the subtraction does not wrap there
+  const uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
+  const uint32_t cn = min(r - ((127u - 7u) << 3), 0x7eu);
+  // below 2^-6: multiples of 2^-9 (8, i.e. 2^-6 itself, is also the first normal code)
+  const uint32_t cs = (uint32_t)rintf(fminf(a, 0.015625f) * 512.0f);
+  const uint32_t c = a < 0.015625f ? cs : cn;
+  return sign | (a < 448.0f ? c : 0x7eu);
 }
 
 // Block scale exponent for a block whose largest magnitude is amax (> 0):
