@@ -90,14 +90,16 @@ __global__ __launch_bounds__(256) void mx_requant_t_kernel(const uint8_t* __rest
 //     neighbouring threads write one 128-byte line of an output row;
 //   * along the features (rq != nullptr): each valid row's two 32-feature blocks -> rq + row * W +
 //     c0 (codes) and rsc + row * (W / 32) + c0 / 32 (scales), from the unscaled source.
-// The fp32 tile row r sits at r * 65 + (r / 32) * 8, so the four slot blocks a column read touches
-// fall on different banks.
+// The tile stays bf16 in LDS (18.5 KB, so 8 workgroups share a CU and their loads overlap): row r
+// at halfword r * 72 + (r / 32) * 16, which puts the four 32-slot blocks a column read touches on
+// different banks.
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ src, const float* __restrict__ rscale,
                                                          int64_t lds, int W, const int32_t* __restrict__ offs,
                                                          const int32_t* __restrict__ poff, int G, uint8_t* __restrict__ q,
                                                          uint8_t* __restrict__ sc, int64_t ldo, uint8_t* __restrict__ rq,
                                                          uint8_t* __restrict__ rsc, int nsb, int ntiles) {
-  __shared__ float tile[128 * 65 + 32];
+  constexpr int P = 72;       // halfwords per tile row (64 + 8)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * P + 64];
   __shared__ float rs[128];   // row scales of the block (1 without rscale or past the group's end)
   const int tid = threadIdx.x;
   int sb, ct;
@@ -111,20 +113,16 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   }
   const int64_t rbase = (int64_t)offs[lo] + (p0 - poff[lo]);
   const int64_t rend = offs[lo + 1];
-  auto at = [](int r, int c) { return r * 65 + (r >> 5) * 8 + c; };
+  auto at = [](int r, int c) { return r * P + (r >> 5) * 16 + c; };
   if (tid < 128) rs[tid] = (rscale && rbase + tid < rend) ? rscale[rbase + tid] : 1.f;
-  // 128 rows x 8 chunks of 8 bf16, 4 per thread
+  // 128 rows x 8 chunks of 8 bf16, 4 per thread, stored as 16-byte LDS writes
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int qd = tid + 256 * k, i = qd >> 3, cc = (qd & 7) * 8;
     const int64_t r = rbase + i;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (r < rend && c0 + cc < W) w = *reinterpret_cast<const u32x4*>(src + r * lds + c0 + cc);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      tile[at(i, cc + 2 * b)] = __uint_as_float(w[b] << 16);
-      tile[at(i, cc + 2 * b + 1)] = __uint_as_float(w[b] & 0xffff0000u);
-    }
+    *reinterpret_cast<u32x4*>(&tile[at(i, cc)]) = w;
   }
   __syncthreads();
   uint32_t pk[8];
@@ -135,7 +133,14 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     if (r < rend && c0 + 32 * b < W) {
       float v[32];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = tile[at(i, 32 * b + j)];
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&tile[at(i, 32 * b + 8 * j)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * j + 2 * e] = __uint_as_float(w[e] << 16);
+          v[8 * j + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
       rsc[r * (W / 32) + c0 / 32 + b] = (uint8_t)mx_block(v, pk);
       u32x4* d = reinterpret_cast<u32x4*>(rq + r * W + c0 + 32 * b);
       d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
@@ -148,7 +153,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     if (c0 + c < W) {
       float v[32];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = tile[at(32 * k + j, c)] * rs[32 * k + j];
+      for (int j = 0; j < 32; ++j)
+        v[j] = __uint_as_float((uint32_t)tile[at(32 * k + j, c)] << 16) * rs[32 * k + j];
       sc[(int64_t)(c0 + c) * (ldo / 32) + (p0 >> 5) + k] = (uint8_t)mx_block(v, pk);
       u32x4* d = reinterpret_cast<u32x4*>(q + (int64_t)(c0 + c) * ldo + p0 + 32 * k);
       d[0] = u32x4{pk[0], pk[1], pk[2], pk[3]};
