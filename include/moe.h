@@ -262,10 +262,10 @@ int moe_forward_stages(const moe_problem *p, const void *x, const float *logits,
  * reverse-dispatch; "A ring buffer instead of a host round-trip": the forward activations are
  * recomputed, not stored; "The production details": the router gradient as <h, W_down^T dY>).
  * Inputs: dout [T][D], x [T][D], logits [T][E], weights, and the routing state of the forward.
- * Outputs: dx [T][D] (BF16), weight gradients (fp32), d_topk_w [T][K] fp32 (gradient w.r.t.
- * g) and d_logits [T][E] fp32 (nullable). MOE_BF16, or MOE_MXFP8 with the forward's MX weights
- * (routed experts as in moe_experts_backward; the shared expert in BF16). MOE_F32 returns
- * MOE_ERR_UNSUPPORTED. */
+ * Outputs: dx [T][D] (activation type: BF16, fp32 under MOE_F32), weight gradients (fp32),
+ * d_topk_w [T][K] fp32 (gradient w.r.t. g) and d_logits [T][E] fp32 (nullable). MOE_BF16;
+ * MOE_MXFP8 with the forward's MX weights (routed experts as in moe_experts_backward; the shared
+ * expert in BF16); MOE_F32 with every operand fp32 (plain FMA GEMMs, for small problems). */
 int moe_backward(const moe_problem *p, const void *dout, const void *x, const float *logits,
                  const moe_weights *w, const moe_routing *routing, void *dx, const moe_grads *dw,
                  float *d_topk_w, float *d_logits, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -278,7 +278,8 @@ int moe_backward(const moe_problem *p, const void *dout, const void *x, const fl
  * set) so that no access leaves the buffers. `ws` holds moe_workspace_size bytes.
  * x_slot [slots][D], offsets [E+1] device int32 (expert e owns rows offsets[e]..offsets[e+1]-1,
  * offsets[E] == slots) -> y_slot [slots][D] = E_e(x_slot) (unweighted; the source applies g).
- * x_local [T][D] -> shared_out [T][D] (skipped when I_shared == 0). MOE_BF16, or MOE_MXFP8:
+ * x_local [T][D] -> shared_out [T][D] (skipped when I_shared == 0). MOE_BF16, MOE_F32 (fp32
+ * tensors and weights, plain FMA GEMMs), or MOE_MXFP8:
  * x_slot stays BF16 and is quantised along D inside the call, the routed weights are the MX
  * tensors of moe_weights (E4M3 + E8M0 scales per 32 along their last axis), h is quantised
  * along I before the down projection, and the shared expert runs in BF16. */
@@ -290,7 +291,7 @@ int moe_experts_forward(const moe_problem *p, int64_t slots, const void *x_slot,
 /* Backward of moe_experts_forward where slot j contributes g_slot[j] * E_e(x_slot[j]) against
  * the upstream gradient dy_slot[j]. Outputs dx_slot [slots][D] (bf16), dg_slot [slots] fp32
  * (= <dy_slot[j], E_e(x_slot[j])>), routed and shared weight gradients (fp32) and dx_local
- * [T][D] (bf16, shared expert path with upstream dy_local [T][D]). `ws` holds
+ * [T][D] (bf16, fp32 under MOE_F32; shared expert path with upstream dy_local [T][D]). `ws` holds
  * moe_backward_workspace_size bytes (which depend on p->dtype).
  * MOE_MXFP8 (sparsenotes page "Mixture-of-Kittens: MoE Megakernel for NVL72s", "The production
  * details": the routed experts train in MXFP8): every routed GEMM takes both operands quantised

@@ -30,6 +30,8 @@ struct BwdLayout {
   // MXFP8 routed experts: E4M3 codes (q) and E8M0 scales (s) of every backward GEMM operand
   size_t mq_x, ms_x, mq_dy, ms_dy, m_dhp, mq_dau, ms_dau, mq_wdT, ms_wdT, mq_wguT, ms_wguT;
   size_t mq_xT, ms_xT, mq_gdyT, ms_gdyT, mq_hT, ms_hT, mq_dauT, ms_dauT;
+  // fp32: dh', h, da, du of the routed rows and of the shared expert's rows
+  size_t f_dh, f_h, f_da, f_du, sf_dh, sf_h, sf_da, sf_du;
   size_t total;
   int64_t n, Spad, Tpad;
 };
@@ -47,10 +49,20 @@ static BwdLayout bwd_layout(const moe_problem& p) {
   L.offs = take((E + 1) * 4); L.tile_off = take((E + 1) * 4); L.poff = take((E + 1) * 4);
   L.order = take(E * 4);
   L.offs_s = take(8); L.tile_off_s = take(8); L.poff_s = take(8);
+  const int64_t eb = p.dtype == MOE_F32 ? 4 : 2;   // bytes per activation element
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
-  L.x_slot = take(n * D * 2); L.dy_slot = take(n * D * 2); L.dx_slot = take(n * D * 2);
-  L.dx_sh = take(T * D * 2);
+  L.x_slot = take(n * D * eb); L.dy_slot = take(n * D * eb); L.dx_slot = take(n * D * eb);
+  L.dx_sh = take(T * D * eb);
   L.act_a = take(n * I * 4); L.act_u = take(n * I * 4);
+  if (p.dtype == MOE_F32) {
+    L.f_dh = take(n * I * 4); L.f_h = take(n * I * 4); L.f_da = take(n * I * 4); L.f_du = take(n * I * 4);
+    if (Is > 0) {
+      L.s_a = take(T * Is * 4); L.s_u = take(T * Is * 4);
+      L.sf_dh = take(T * Is * 4); L.sf_h = take(T * Is * 4); L.sf_da = take(T * Is * 4); L.sf_du = take(T * Is * 4);
+    }
+    L.total = o;
+    return L;
+  }
   if (p.dtype == MOE_MXFP8) {
     // rows quantised along D; dgrad-down output and h, [da | du] in fp32; [da | du] along I;
     // weights re-quantised transposed; slot-axis operands [features][Spad], experts 128-aligned
@@ -225,6 +237,13 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   return launch_gemm_mx_kgroup(w2, B(L.ms_dauT), B(L.ms_xT), G, s);
 }
 
+int core_backward_f32(int G, int64_t n_cap, int64_t max_rows, int D, int I, const float* x_rows, const float* dy_rows,
+                      const float* g_rows, const int32_t* offs, const float* wg, const float* wu, const float* wd,
+                      float* dx_rows, float* dg_rows, float* dw_gate, float* dw_up, float* dw_down, float* sa, float* su,
+                      float* sdh, float* sh, float* sda, float* sdu, hipStream_t s);
+int launch_reverse_dispatch_f32(const float* dx_slot, const int32_t* inv_perm, const float* dx_shared, float* dx, int T,
+                                int K, int D, hipStream_t s);
+
 static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
@@ -247,6 +266,13 @@ static int shared_backward(const moe_problem* p, const void* x, const void* dy, 
   int32_t* o = (int32_t*)(wsb + L.offs_s);
   hipLaunchKernelGGL(single_group_kernel, dim3(1), dim3(1), 0, s, p->T, o);
   MOE_LAUNCH_CHECK();
+  if (p->dtype == MOE_F32) {
+    auto F = [&](size_t off) { return (float*)(wsb + off); };
+    return core_backward_f32(1, p->T, p->T, p->D, p->I_shared, (const float*)x, (const float*)dy, nullptr, o,
+                             (const float*)w->ws_gate, (const float*)w->ws_up, (const float*)w->ws_down, (float*)dx,
+                             nullptr, dw->dws_gate, dw->dws_up, dw->dws_down, F(L.s_a), F(L.s_u), F(L.sf_dh), F(L.sf_h),
+                             F(L.sf_da), F(L.sf_du), s);
+  }
   int st = launch_group_prefix(o, 1, p->T, o, (int32_t*)(wsb + L.tile_off_s), (int32_t*)(wsb + L.poff_s),
                                (int32_t*)(wsb + L.err), s);
   if (st) return st;
@@ -275,7 +301,8 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   int st = validate_problem(p);
   if (st) return st;
   const bool mx = p->dtype == MOE_MXFP8;
-  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
+  // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
+  auto gemm = p->dtype == MOE_F32 ? launch_gemm_f32 : launch_gemm_bf16;
   if (!x_slot || !offsets || !w || !y_slot || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;
@@ -318,11 +345,11 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   GemmArgs g1;
   g1.A = x_slot; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
   g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = wsb + L.h; g1.ldc = p->I;
-  if ((st = launch_gemm_bf16(g1, gr, EPI_SWIGLU, stream))) return st;
+  if ((st = gemm(g1, gr, EPI_SWIGLU, stream))) return st;
   GemmArgs g2;
   g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
   g2.N = p->D; g2.K = p->I; g2.C = y_slot; g2.ldc = p->D;
-  if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream))) return st;
+  if ((st = gemm(g2, gr, EPI_STORE, stream))) return st;
   }
   if (p->I_shared > 0) {
     Grouped gs;
@@ -330,11 +357,11 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
     GemmArgs s1;
     s1.A = x_local; s1.lda = p->D; s1.B = w->ws_gate; s1.B2 = w->ws_up; s1.ldb = p->D; s1.N = p->I_shared;
     s1.K = p->D; s1.C = wsb + L.sh_h; s1.ldc = p->I_shared;
-    if ((st = launch_gemm_bf16(s1, gs, EPI_SWIGLU, stream))) return st;
+    if ((st = gemm(s1, gs, EPI_SWIGLU, stream))) return st;
     GemmArgs s2;
     s2.A = wsb + L.sh_h; s2.lda = p->I_shared; s2.B = w->ws_down; s2.ldb = p->I_shared; s2.N = p->D;
     s2.K = p->I_shared; s2.C = shared_out; s2.ldc = p->D;
-    if ((st = launch_gemm_bf16(s2, gs, EPI_STORE, stream))) return st;
+    if ((st = gemm(s2, gs, EPI_STORE, stream))) return st;
   }
   return MOE_OK;
 }
@@ -345,8 +372,7 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
                          void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
-  const bool mx = p->dtype == MOE_MXFP8;
-  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
@@ -364,7 +390,14 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
   if ((st = launch_group_prefix(offsets, p->E, (int)slots, offs, (int32_t*)(wsb + L.tile_off),
                                 (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
     return st;
-  if (mx) {
+  if (f32) {
+    auto F = [&](size_t off) { return (float*)(wsb + off); };
+    if ((st = core_backward_f32(p->E, slots, slots, p->D, p->I, (const float*)x_slot, (const float*)dy_slot, g_slot,
+                                offs, (const float*)w->w_gate, (const float*)w->w_up, (const float*)w->w_down,
+                                (float*)dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, F(L.act_a), F(L.act_u),
+                                F(L.f_dh), F(L.f_h), F(L.f_da), F(L.f_du), stream)))
+      return st;
+  } else if (mx) {
     if ((st = core_backward_mx(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
                                (int32_t*)(wsb + L.poff), w, dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, wsb,
                                L, stream)))
@@ -384,8 +417,7 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   int st = validate_routing(p);
   if (st) return st;
   (void)logits;   // the routing state of the forward carries everything the backward needs
-  const bool mx = p->dtype == MOE_MXFP8;
-  if (p->dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
+  const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!dout || !x || !w || !r || !dx || !dw || !d_topk_w) return MOE_ERR_INVALID_ARG;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (!r->topk_idx || !r->topk_w || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
@@ -398,14 +430,22 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   char* wsb = (char*)ws;
   const int64_t n = L.n;
   // reverse-combine (pull dout into slots), replayed dispatch of x, slot weights
-  if ((st = launch_dispatch(dout, MOE_BF16, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
-  if ((st = launch_dispatch(x, MOE_BF16, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream))) return st;
+  const int adt = f32 ? MOE_F32 : MOE_BF16;   // activations stay bf16 under MXFP8 until quantised
+  if ((st = launch_dispatch(dout, adt, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
+  if ((st = launch_dispatch(x, adt, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream))) return st;
   if ((st = launch_gather_f32(r->topk_w, r->perm, n, (float*)(wsb + L.g_slot), stream))) return st;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(r->offsets, p->E, (int)n, offs, (int32_t*)(wsb + L.tile_off),
                                 (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
     return st;
-  if (mx) {
+  if (f32) {
+    auto F = [&](size_t off) { return (float*)(wsb + off); };
+    if ((st = core_backward_f32(p->E, n, n, p->D, p->I, F(L.x_slot), F(L.dy_slot), F(L.g_slot), offs,
+                                (const float*)w->w_gate, (const float*)w->w_up, (const float*)w->w_down, F(L.dx_slot),
+                                F(L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, F(L.act_a), F(L.act_u), F(L.f_dh),
+                                F(L.f_h), F(L.f_da), F(L.f_du), stream)))
+      return st;
+  } else if (mx) {
     if ((st = core_backward_mx(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
                                (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
                                (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream)))
@@ -425,6 +465,9 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
     if ((st = shared_backward(p, x, dout, w, dw, dsh, wsb, L, stream))) return st;
   }
   // reverse-dispatch: dx[t] = dx_shared[t] + sum_k dx_slot[inv_perm[t*K + k]]
+  if (f32)
+    return launch_reverse_dispatch_f32((const float*)(wsb + L.dx_slot), r->inv_perm, (const float*)dsh, (float*)dx,
+                                       p->T, p->K, p->D, stream);
   return launch_reverse_dispatch(wsb + L.dx_slot, r->inv_perm, dsh, dx, p->T, p->K, p->D, stream);
 }
 

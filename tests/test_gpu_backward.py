@@ -226,3 +226,98 @@ def test_ep_share_full_size_sampled(m):
         assert_close_rms(r['dws_gate'][i].cpu().numpy(), ru['dW_gate'][0], TAU, f'ep shared dW_gate[{i}]')
         assert_close_rms(r['dws_up'][i].cpu().numpy(), ru['dW_up'][0], TAU, f'ep shared dW_up[{i}]')
         assert_close_rms(r['dws_down'][:, i].cpu().numpy(), ru['dW_down'][:, 0], TAU, f'ep shared dW_down[:,{i}]')
+
+
+def test_layer_backward_f32_tiny(m):
+    """Whole-layer backward on the tiny fp32 configuration (T=256, D=128, I=64, 8 experts top-2 +
+    shared): every gradient within 1e-4 RMS of the fp64 oracle, zero d_logits off the selection."""
+    cfg = synth.TINY
+    print(f'[backward] layer {cfg.name}', flush=True)
+    H = synth.host_layer(cfg)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L, want_parts=False)()
+    dout_h = synth.host_dout(cfg, cfg.T)
+    dout = torch.from_numpy(np.ascontiguousarray(dout_h, dtype=np.float32)).cuda()
+    E, I, D, Is, T, K = cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.T, cfg.K
+    gr = dict(dw_gate=torch.full((E, I, D), float('nan'), device='cuda'),
+              dw_up=torch.full((E, I, D), float('nan'), device='cuda'),
+              dw_down=torch.full((E, D, I), float('nan'), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    dx = torch.empty((T, D), dtype=torch.float32, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+    m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, m.make_grads(**gr), dtw, dlg, wsb)
+    torch.cuda.synchronize()
+    assert int(wsb[:4].view(torch.int32).item()) == 0
+    tau = TOL['f32']
+    ref = oracle.moe_backward(H.x, H.logits, H.w_gate, H.w_up, H.w_down, K, dout_h, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(dx), ref['dx'], tau, 'f32 dx')
+    assert_close_rms(t2np(dtw), ref['dg'], tau, 'f32 d_topk_w')
+    assert_close_rms(t2np(dlg), ref['d_logits'], tau, 'f32 d_logits')
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(gr[k.replace('dW', 'dw')]), ref[k], tau, 'f32 ' + k)
+    for k in ('dWs_gate', 'dWs_up', 'dWs_down'):
+        assert_close_rms(t2np(gr[k.replace('dWs', 'dws')]), ref[k], tau, 'f32 ' + k)
+    mask = np.zeros((T, E), dtype=bool)
+    np.put_along_axis(mask, ref['idx'].astype(np.int64), True, axis=1)
+    assert np.all(t2np(dlg)[~mask] == 0)
+
+
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242]], ids=['empty_mid', 'ragged'])
+def test_experts_forward_backward_f32(m, counts):
+    """Expert-level forward + backward in fp32 on the small share (1e-4 RMS against fp64),
+    exact zeros for an empty expert's weight gradients, bitwise repeatable."""
+    H = synth.host_share(SMALL_SHARE)
+    cfg = H.cfg
+    S = int(sum(counts))
+    E, I, D, Is = cfg.E_local, cfg.I, cfg.D, cfg.I_shared
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    p = m.problem(cfg.tokens, D, I, E, cfg.K, Is, 'f32')
+    wts = [f(getattr(H, k)) for k in ('w_gate', 'w_up', 'w_down', 'ws_gate', 'ws_up', 'ws_down')]
+    W = m.make_weights(*wts)   # the binding keeps raw pointers: wts must outlive every call
+    off_d = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    xs, dys, xl, dyl = f(H.x_slot[:S]), f(H.dy_slot[:S]), f(H.x_local), f(H.dy_local)
+    g_d = torch.from_numpy(H.g[:S].copy()).cuda()
+
+    def run():
+        y = torch.empty((S, D), device='cuda')
+        sh = torch.empty((cfg.tokens, D), device='cuda')
+        ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+        m.experts_forward(p, S, xs, off_d, W, y, xl, sh, ws)
+        dxs = torch.empty((S, D), device='cuda')
+        dg = torch.empty((S,), device='cuda')
+        gr = dict(dw_gate=torch.full((E, I, D), float('nan'), device='cuda'),
+                  dw_up=torch.full((E, I, D), float('nan'), device='cuda'),
+                  dw_down=torch.full((E, D, I), float('nan'), device='cuda'),
+                  dws_gate=torch.empty((Is, D), device='cuda'), dws_up=torch.empty((Is, D), device='cuda'),
+                  dws_down=torch.empty((D, Is), device='cuda'))
+        dxl = torch.empty((cfg.tokens, D), device='cuda')
+        wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+        m.experts_backward(p, S, xs, off_d, g_d, dys, W, dxs, dg, m.make_grads(**gr), xl, dyl, dxl, wsb)
+        torch.cuda.synchronize()
+        assert int(wsb[:4].view(torch.int32).item()) == 0
+        return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, **gr)
+
+    print(f'[backward] f32 share counts={counts}', flush=True)
+    r = run()
+    tau = TOL['f32']
+    c = np.array(counts)
+    assert_close_rms(t2np(r['y']), oracle.experts_forward(H.x_slot[:S], c, H.w_gate, H.w_up, H.w_down), tau, 'f32 y')
+    assert_close_rms(t2np(r['sh']), oracle.swiglu_expert(H.x_local, H.ws_gate, H.ws_up, H.ws_down), tau, 'f32 sh')
+    ref = oracle.experts_backward(H.x_slot[:S], c, H.g[:S], H.dy_slot[:S], H.w_gate, H.w_up, H.w_down)
+    assert_close_rms(t2np(r['dx_slot']), ref['dx_slot'], tau, 'f32 dx_slot')
+    assert_close_rms(t2np(r['dg']), ref['dg'], tau, 'f32 dg')
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        got = t2np(r[k.replace('dW', 'dw')])
+        assert_close_rms(got, ref[k], tau, 'f32 ' + k)
+        for e in range(len(counts)):
+            if counts[e] == 0:
+                assert np.all(got[e] == 0), f'{k}[{e}] of an empty expert must be exact zeros'
+    rs = oracle.shared_backward(H.x_local, H.dy_local, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(r['dx_local']), rs['dx'], tau, 'f32 shared dx')
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(r[k.replace('dW', 'dws')]), rs[k], tau, 'f32 shared ' + k)
+    r2 = run()
+    for k in ('dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dx_local'):
+        assert torch.equal(r[k], r2[k]), k
