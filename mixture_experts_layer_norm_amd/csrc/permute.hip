@@ -104,7 +104,10 @@ __global__ __launch_bounds__(256) void dispatch_tokens_kernel(const uint4* __res
 }
 
 // Token-major MXFP8 dispatch: one wavefront per token quantises each 32-wide block of its row
-// once and writes the codes (nontemporal stores, as above) and the scale byte to the token's K slots.
+// once and writes the codes and the scale byte to the token's K slots. Ordinary stores here: a
+// lane writes its 32-byte block as two 16-byte halves, so each store instruction leaves gaps in
+// the lines that nontemporal stores would send out unmerged (measured 0.59 -> 0.80 ms at
+// T = 32768 with them).
 __global__ __launch_bounds__(256) void dispatch_tokens_mx_kernel(const uint16_t* __restrict__ x,
                                                                  const int32_t* __restrict__ inv_perm, int T,
                                                                  int K, int D, uint8_t* __restrict__ q,
@@ -134,8 +137,8 @@ __global__ __launch_bounds__(256) void dispatch_tokens_mx_kernel(const uint16_t*
       const int64_t j = slots[k];
       sc[j * nb + b] = e;
       u32x4* d = reinterpret_cast<u32x4*>(q + j * D + b * 32);
-      __builtin_nontemporal_store(lo, d);
-      __builtin_nontemporal_store(hi, d + 1);
+      d[0] = lo;
+      d[1] = hi;
     }
   }
 }
