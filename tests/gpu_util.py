@@ -71,6 +71,17 @@ def assert_close_rms(got, ref, tau, what='', stored_bf16=False, allowance=None):
     return ratio
 
 
+def frac_beyond(got, ref, tau, stored_bf16=False):
+    """Share of elements with |got - ref| > tau * RMS(ref) (+ half a BF16 ulp of ref for a tensor
+    stored as BF16), with no allowance for alternative quantisation decisions. Genuine decision
+    flips touch few elements; a wrong axis, a dropped term or a transposed operand moves most."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    bound = tau * rms + (half_ulp_bf16(ref) if stored_bf16 else 0.0)
+    return float(np.mean(np.abs(got - ref) > bound)) if ref.size else 0.0
+
+
 def t2np(t):
     return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype != torch.int32 else t.cpu().numpy()
 

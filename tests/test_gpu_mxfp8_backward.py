@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, assert_close_rms, mx_choice_allowance, t2np
+from gpu_util import TOL, assert_close_rms, frac_beyond, mx_choice_allowance, t2np
 
 pytestmark = pytest.mark.gpu
 TAU = TOL['mxfp8']
@@ -138,6 +138,12 @@ def test_mx_experts_forward_backward_small(m, counts):
         for e in range(len(counts)):
             if counts[e] == 0:
                 assert np.all(got[e] == 0), f'{k}[{e}] of an empty expert must be exact zeros'
+    # without any allowance, only a small share of elements may sit beyond tau * RMS
+    fr = {'dx_slot': frac_beyond(t2np(r['dx_slot']), ref['dx_slot'], TAU, True)}
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        fr[k] = frac_beyond(t2np(r[k.replace('dW', 'dw')]), ref[k], TAU)
+    print('  share beyond tau*RMS without allowance:', {k: f'{v:.2e}' for k, v in fr.items()}, flush=True)
+    assert max(fr.values()) < 0.005, fr
     # the shared expert stays BF16
     rs = oracle.shared_backward(H.x_local, H.dy_local, H.ws_gate, H.ws_up, H.ws_down)
     assert_close_rms(t2np(r['dx_local']), rs['dx'], TOL['bf16'], 'shared dx_local', True)
@@ -278,5 +284,10 @@ def test_mx_layer_backward(m):
     assert np.all(t2np(dlg)[~mask] == 0)
     for k in ('dW_gate', 'dW_up', 'dW_down'):
         assert_close_rms(t2np(gr[k.replace('dW', 'dw')]), ref[k], TAU, 'mx layer ' + k, False, al[k])
+    fr = {'dx': frac_beyond(t2np(dx), dx_ref, TAU, True)}
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        fr[k] = frac_beyond(t2np(gr[k.replace('dW', 'dw')]), ref[k], TAU)
+    print('  share beyond tau*RMS without allowance:', {k: f'{v:.2e}' for k, v in fr.items()}, flush=True)
+    assert max(fr.values()) < 0.005, fr
     for k in ('dW_gate', 'dW_up', 'dW_down'):
         assert_close_rms(t2np(gr[k.replace('dW', 'dws')]), rs[k], TOL['bf16'], 'mx layer shared ' + k)
