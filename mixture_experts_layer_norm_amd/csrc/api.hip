@@ -4,6 +4,8 @@
 
 #include <algorithm>
 
+#include <vector>
+
 #include "common.h"
 #include "pipeline.h"
 
@@ -280,9 +282,26 @@ namespace {
 // A library-owned side stream (default priority) per host thread and device, with the two events
 // of a fork/join: moe_forward runs the shared expert on it while the routed path runs on the
 // caller's stream. Created on first use; kept for the life of the process.
+// It also carries the dispatch stream of the chunked ring and a pool of events, grown once and
+// reused by every later call: disp[c] marks chunk c dispatched, ug[c] its up/gate done.
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t ds = nullptr;                 // dispatch stream of the chunked ring
+  hipEvent_t ring_fork = nullptr;
+  std::vector<hipEvent_t> disp, ug;
+  bool ensure_ring(int C) {
+    if (!ds && hipStreamCreateWithFlags(&ds, hipStreamNonBlocking) != hipSuccess) { ds = nullptr; return false; }
+    if (!ring_fork && hipEventCreateWithFlags(&ring_fork, hipEventDisableTiming) != hipSuccess) { ring_fork = nullptr; return false; }
+    while ((int)disp.size() < C) {
+      hipEvent_t a = nullptr, b = nullptr;
+      if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess) return false;
+      if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) { hipEventDestroy(a); return false; }
+      disp.push_back(a);
+      ug.push_back(b);
+    }
+    return true;
+  }
 };
 constexpr int kMaxDevices = 64;
 thread_local SideStream t_side[kMaxDevices];
@@ -357,14 +376,15 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     gs.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
     gs.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
     hipStream_t shs = stream;
-    if (side) {
+    const bool overlap = side && (p->flags & MOE_FLAG_OVERLAP_SHARED);
+    if (overlap) {
       if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
         return MOE_ERR_HIP;
       shs = side->s;
     }
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
                     0, 0, wsb + L.sh_h, sho, nullptr, shs);
-    if (side) {
+    if (overlap) {
       if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_ERR_HIP;
       join.main = stream;
       join.ev = side->join;
@@ -392,12 +412,25 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     MOE_MARK(MOE_STAGE_DISPATCH);
     uint16_t* xr = (uint16_t*)(wsb + L.x_slot);
     uint16_t* hr = (uint16_t*)(wsb + L.h);
+    // With the library's streams (moe_forward) dispatch runs ahead on its own stream: chunk c is
+    // dispatched once chunk c - S's up/gate has read ring stage c % S (event ug[c - S]), and the
+    // compute stream starts chunk c once it is dispatched (event disp[c]). Without them
+    // (moe_forward_stages) everything stays in order on `stream`.
+    const bool ahead = side && side->ensure_ring(C);
+    hipStream_t dstream = ahead ? side->ds : stream;
+    if (ahead && (hipEventRecord(side->ring_fork, stream) != hipSuccess ||
+                  hipStreamWaitEvent(side->ds, side->ring_fork, 0) != hipSuccess))
+      return MOE_ERR_HIP;
     for (int c = 0; c < C; ++c) {
       const int64_t c0 = c * b, rows = (n - c0) < b ? (n - c0) : b;
       const int64_t shift = (int64_t)(c % S) * b - c0;            // slot index -> ring row
+      if (ahead && c >= S && hipStreamWaitEvent(dstream, side->ug[c - S], 0) != hipSuccess) return MOE_ERR_HIP;
       st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + (int64_t)(c % S) * b * p->D, nullptr,
-                           stream);
+                           dstream);
       if (st) return st;
+      if (ahead && (hipEventRecord(side->disp[c], dstream) != hipSuccess ||
+                    hipStreamWaitEvent(stream, side->disp[c], 0) != hipSuccess))
+        return MOE_ERR_HIP;
       Grouped gc;
       gc.row_off = crow + (int64_t)c * (p->E + 1);
       gc.tile_off = ctile + (int64_t)c * (p->E + 1);
@@ -407,7 +440,8 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       gc.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
       gc.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
       st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
-                      p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream);
+                      p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream,
+                      ahead ? side->ug[c] : nullptr);
       if (st) return st;
     }
     MOE_MARK(MOE_STAGE_UP_GATE);
@@ -470,7 +504,10 @@ extern "C" {
 int moe_forward(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                 void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
-  SideStream* side = (p && p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED)) ? side_stream() : nullptr;
+  // the library's side streams: the shared expert's (MOE_FLAG_OVERLAP_SHARED) and the chunked
+  // ring's dispatch stream (chunk_rows > 0)
+  const bool want_side = p && ((p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED)) || p->chunk_rows > 0);
+  SideStream* side = want_side ? side_stream() : nullptr;
   return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side);
 }
 
