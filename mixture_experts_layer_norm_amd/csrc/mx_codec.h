@@ -7,21 +7,21 @@
 
 namespace moe {
 
-// |v| already divided by the block scale -> E4M3 code, round to nearest even, saturate at 448
-// (NaN and infinities saturate too). Branch-free: both candidate codes are formed and one is
-// selected, so a wavefront quantising a block takes no divergent branches.
+// Values already divided by the block scale -> E4M3 codes, round to nearest even (subnormals
+// included), saturating at +-448: the clamp (v_med3) then gfx950's packed conversion to OCP E4M3
+// (v_cvt_pk_fp8_f32), 2.5 instructions per value where a software encoder took about 15. Four
+// values packed little-endian (value i in byte i). A NaN input gives an unspecified code.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi), __builtin_amdgcn_fmed3f(b, lo, hi), 0,
+                                          false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi), __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  const uint32_t ua = __float_as_uint(a);
-  // normal range (a >= 2^-6): keep 3 mantissa bits, round to nearest even, rebias 127 -> 7, cap
-  // at 0x7e (448); a >= 2^-6 gives r >= 121 << 3, so the subtraction does not wrap there
-  const uint32_t r = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
-  const uint32_t cn = min(r - ((127u - 7u) << 3), 0x7eu);
-  // below 2^-6: multiples of 2^-9 (8, i.e. 2^-6 itself, is also the first normal code)
-  const uint32_t cs = (uint32_t)rintf(fminf(a, 0.015625f) * 512.0f);
-  const uint32_t c = a < 0.015625f ? cs : cn;
-  return sign | (a < 448.0f ? c : 0x7eu);
+  const float c = __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xffu;
 }
 
 // Block scale exponent for a block whose largest magnitude is amax (> 0):
@@ -45,12 +45,8 @@ __device__ __forceinline__ uint32_t mx_block(const float* v, uint32_t* packed) {
   const int se = mx_shared_exp(amax);
   const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) w |= e4m3_code(v[4 * i + b] * inv) << (8 * b);
-    packed[i] = w;
-  }
+  for (int i = 0; i < 8; ++i)
+    packed[i] = e4m3_pack4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
   return (uint32_t)(se + 127);
 }
 
