@@ -104,10 +104,10 @@ __global__ __launch_bounds__(256) void dispatch_tokens_kernel(const uint4* __res
 }
 
 // Token-major MXFP8 dispatch: one wavefront per token quantises each 32-wide block of its row
-// once and writes the codes and the scale byte to the token's K slots. Ordinary stores here: a
-// lane writes its 32-byte block as two 16-byte halves, so each store instruction leaves gaps in
-// the lines that nontemporal stores would send out unmerged (measured 0.59 -> 0.80 ms at
-// T = 32768 with them).
+// once and writes the codes and the scale byte to the token's K slots. The codes are exchanged
+// across lanes first so that every store instruction covers 1 KB of whole lines: stored as each
+// lane's own two 16-byte halves, nontemporal stores left gaps in every line and were slower
+// (0.59 -> 0.80 ms at T = 32768).
 __global__ __launch_bounds__(256) void dispatch_tokens_mx_kernel(const uint16_t* __restrict__ x,
                                                                  const int32_t* __restrict__ inv_perm, int T,
                                                                  int K, int D, uint8_t* __restrict__ q,
@@ -117,28 +117,48 @@ __global__ __launch_bounds__(256) void dispatch_tokens_mx_kernel(const uint16_t*
   if (t >= T) return;
   const int32_t* slots = inv_perm + (int64_t)t * K;
   const int nb = D / 32;
-  for (int b = lane; b < nb; b += 64) {
-    const uint4* s = reinterpret_cast<const uint4*>(x + (int64_t)t * D + b * 32);
-    float v[32];
+  for (int base = 0; base < nb; base += 64) {
+    // lane quantises block b = base + lane
+    const int b = base + lane;
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    uint8_t e = 127;
+    if (b < nb) {
+      const uint4* s = reinterpret_cast<const uint4*>(x + (int64_t)t * D + b * 32);
+      float v[32];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 u = s[c];
-      uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      for (int c = 0; c < 4; ++c) {
+        uint4 u = s[c];
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
-        v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        for (int i = 0; i < 4; ++i) {
+          v[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+          v[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
       }
+      uint32_t p[8];
+      e = (uint8_t)mx_block(v, p);
+      lo = u32x4{p[0], p[1], p[2], p[3]};
+      hi = u32x4{p[4], p[5], p[6], p[7]};
     }
-    uint32_t p[8];
-    const uint8_t e = (uint8_t)mx_block(v, p);
-    const u32x4 lo = {p[0], p[1], p[2], p[3]}, hi = {p[4], p[5], p[6], p[7]};
+    // Lane l then stores 16-byte chunk l of the 64 blocks' 2 KB of codes (block base + l / 2,
+    // half l % 2) and chunk 64 + l (block base + 32 + l / 2), so each store instruction writes
+    // 1 KB of whole lines and nontemporal stores can be used.
+    const int s0 = lane >> 1, s1 = 32 + (lane >> 1);
+    u32x4 c0, c1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t l0 = __shfl(lo[i], s0, 64), h0 = __shfl(hi[i], s0, 64);
+      const uint32_t l1 = __shfl(lo[i], s1, 64), h1 = __shfl(hi[i], s1, 64);
+      c0[i] = (lane & 1) ? h0 : l0;
+      c1[i] = (lane & 1) ? h1 : l1;
+    }
+    const bool v0 = base + s0 < nb, v1 = base + s1 < nb;
     for (int k = 0; k < K; ++k) {
       const int64_t j = slots[k];
-      sc[j * nb + b] = e;
-      u32x4* d = reinterpret_cast<u32x4*>(q + j * D + b * 32);
-      d[0] = lo;
-      d[1] = hi;
+      if (b < nb) sc[j * nb + b] = e;
+      u32x4* d = reinterpret_cast<u32x4*>(q + j * D + (int64_t)base * 32);
+      if (v0) __builtin_nontemporal_store(c0, d + lane);
+      if (v1) __builtin_nontemporal_store(c1, d + 64 + lane);
     }
   }
 }
