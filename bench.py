@@ -255,6 +255,7 @@ def main():
         torch.cuda.empty_cache()
         extra = {'second_stream_latency': yl,
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
+                 'ep_share_fwd_bwd_dgrad_one_pass': bench_share(max(5, args.steps // 5), 2, args.flags | 0x40),
                  'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 
@@ -459,7 +460,7 @@ def bench_share(steps, warmup, flags, dtype='bf16'):
     t_peak = (3.0 * 6.0 * S * D * I / (PEAK_MXFP8_TFLOPS if dtype == 'mxfp8' else PEAK_BF16_TFLOPS)
               + 3.0 * 6.0 * T * D * Is / PEAK_BF16_TFLOPS) / 1e12
     name = cfg.name.replace('bf16', dtype) if dtype != 'bf16' else cfg.name
-    return {'workload': f'{name} forward+backward', 'dtype': dtype, 'tokens': T, 'slots': S,
+    return {'workload': f'{name} forward+backward', 'dtype': dtype, 'flags': flags, 'tokens': T, 'slots': S,
             'counts': D_.counts.tolist(), 'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms,
             'value': T / (ms * 1e-3), 'unit': 'tokens/s', 'slots_per_s': S / (ms * 1e-3),
             'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': t_peak / (ms * 1e-3),

@@ -13,9 +13,13 @@
 // Steps per group of rows: weight transposes; replay (a, u in fp32); dgrad-down with the SwiGLU
 // backward in its epilogue (da, du and per-tile <h, dh'> partials); dgrad-up over [da | du] with
 // K = 2I; padded transposes of x, dy, g*h and [da | du]; K-grouped weight-gradient GEMMs.
-// Every GEMM operand that is not an exact input (da, du, g*h) is carried as a pair of bf16 values
-// hi + lo (lo = v - bf16(v)) and contracted in two K passes, so the BF16 MFMA inputs lose ~2^-17
-// relative instead of 2^-9; x, dy and the weights are exact bf16 inputs.
+// The weight-gradient operands that are not exact inputs (da, du, g*h) are carried as pairs of
+// bf16 values hi + lo (lo = v - bf16(v)) and contracted in two K passes, so they lose ~2^-17
+// relative instead of 2^-9: a weight gradient of an expert with a single slot is an outer
+// product, and its largest elements would carry the whole 2^-9 rounding. dgrad-up does the same
+// by default; with MOE_FLAG_BWD_DGRAD_ONE_PASS it contracts the bf16 da, du alone (every dx
+// element sums 2I products with independent roundings, so the error stays within the BF16 bound;
+// one K pass instead of two). x, dy and the weights are exact bf16 inputs.
 #include "common.h"
 
 namespace moe {
@@ -108,7 +112,8 @@ struct CoreBufs {
 static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
                          const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                          const void* wg, const void* wu, const void* wd, void* dx_rows, float* dg_rows,
-                         float* dw_gate, float* dw_up, float* dw_down, const CoreBufs& b, hipStream_t s) {
+                         float* dw_gate, float* dw_up, float* dw_down, const CoreBufs& b, hipStream_t s,
+                         bool dgrad_one_pass) {
   int st;
   // transposed weights: W_down^T [G][I][D]; [W_gate^T | W_up^T] [G][D][2I]
   if ((st = launch_transpose_batched(wd, G, D, I, b.wdT, D, (int64_t)I * D, 0, s))) return st;
@@ -137,10 +142,11 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   const int ntn_d = (I + gemm_tile_cols(EPI_DGRAD) - 1) / gemm_tile_cols(EPI_DGRAD);
   if (dg_rows && (st = launch_row_sum(b.part, n_cap, ntn_d, dg_rows, s))) return st;
 
-  // dgrad-up: dx = [da | du] [W_gate^T | W_up^T]^T, high halves then low halves (two K passes)
+  // dgrad-up: dx = [da | du] [W_gate^T | W_up^T]^T
   GemmArgs u;
   u.A = b.dau; u.lda = 4 * I; u.B = b.wguT; u.ldb = 2 * I; u.b_group_stride = (int64_t)D * 2 * I;
-  u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D; u.two_pass = 1; u.a_seg_shift = 2 * I;
+  u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
+  if (!dgrad_one_pass) { u.two_pass = 1; u.a_seg_shift = 2 * I; }   // high halves, then low halves
   if ((st = launch_gemm_bf16(u, grp, EPI_STORE, s))) return st;
 
   // padded transposes for the weight gradients: x and dy exact; g*h and [da|du] as hi/lo rows
@@ -278,7 +284,8 @@ static int shared_backward(const moe_problem* p, const void* x, const void* dy, 
   if (st) return st;
   return core_backward(1, p->T, p->D, p->I_shared, x, dy, nullptr, o, (int32_t*)(wsb + L.tile_off_s),
                        (int32_t*)(wsb + L.poff_s), w->ws_gate, w->ws_up, w->ws_down, dx, nullptr, dw->dws_gate,
-                       dw->dws_up, dw->dws_down, shared_bufs(wsb, L), s);
+                       dw->dws_up, dw->dws_down, shared_bufs(wsb, L), s,
+                       (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0);
 }
 
 }  // namespace moe
@@ -404,7 +411,8 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
       return st;
   } else if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
                           (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down, dx_slot, dg_slot, dw->dw_gate,
-                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream))) {
+                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream,
+                          (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0))) {
     return st;
   }
   if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream);
@@ -453,7 +461,8 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   } else if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
                                  (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up,
                                  w->w_down, wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up,
-                                 dw->dw_down, routed_bufs(wsb, L), stream))) {
+                                 dw->dw_down, routed_bufs(wsb, L), stream,
+                          (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0))) {
     return st;
   }
   if ((st = launch_router_backward((float*)(wsb + L.dg_slot), r->inv_perm, r->topk_idx, r->topk_w, p->T, p->E, p->K,

@@ -67,7 +67,8 @@ def assert_close_rms(got, ref, tau, what='', stored_bf16=False, allowance=None):
     assert not bad.any(), (f'{what}: {int(bad.sum())} elements out of bound; worst |d| = {d.flat[i]:.3e} at ref '
                            f'{ref.flat[i]:.3e} (tau*RMS = {tau * rms:.3e})')
     ratio = float(d.max() / rms) if rms else 0.0
-    print(f'  {what}: max|d|/RMS = {ratio:.2e} (tau {tau:g})', flush=True)
+    used = float(np.max(d / bound))
+    print(f'  {what}: max|d|/RMS = {ratio:.2e} (tau {tau:g}); worst element at {used:.2f} of its bound', flush=True)
     return ratio
 
 

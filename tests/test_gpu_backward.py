@@ -35,11 +35,11 @@ SMALL_SHARE = synth.EPShareConfig('small_share_bf16_T100_K5_D256_I256_E3', token
                                   I_shared=128, zipf_s=1.2, seed=41)
 
 
-def run_share(m, H, counts):
+def run_share(m, H, counts, flags=0):
     cfg = H.cfg
     S = int(sum(counts))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    p = m.problem(cfg.tokens, cfg.D, cfg.I, cfg.E_local, cfg.K, cfg.I_shared, 'bf16')
+    p = m.problem(cfg.tokens, cfg.D, cfg.I, cfg.E_local, cfg.K, cfg.I_shared, 'bf16', flags=flags)
     W = m.make_weights(*(bf(a) for a in (H.w_gate, H.w_up, H.w_down, H.ws_gate, H.ws_up, H.ws_down)))
     keep = [W]
     dev = {k: bf(getattr(H, k)[:S] if k in ('x_slot', 'dy_slot') else getattr(H, k))
@@ -321,3 +321,22 @@ def test_experts_forward_backward_f32(m, counts):
     r2 = run()
     for k in ('dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dx_local'):
         assert torch.equal(r[k], r2[k]), k
+
+
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242]], ids=['empty_mid', 'ragged'])
+def test_experts_backward_dgrad_one_pass(m, counts):
+    """MOE_FLAG_BWD_DGRAD_ONE_PASS: dgrad-up over the bf16 da, du in one K pass. dx_slot and
+    dx_local stay within the BF16 bound; the other outputs are computed as without the flag."""
+    print(f'[backward] one-pass dgrad-up, share counts={counts}', flush=True)
+    H = synth.host_share(SMALL_SHARE)
+    S = int(sum(counts))
+    r = run_share(m, H, counts, flags=m.MOE_FLAG_BWD_DGRAD_ONE_PASS)
+    assert r['err'] == 0
+    c = np.array(counts)
+    ref = oracle.experts_backward(H.x_slot[:S], c, H.g[:S], H.dy_slot[:S], H.w_gate, H.w_up, H.w_down)
+    assert_close_rms(t2np(r['dx_slot']), ref['dx_slot'], TAU, 'one-pass dx_slot', True)
+    rs = oracle.shared_backward(H.x_local, H.dy_local, H.ws_gate, H.ws_up, H.ws_down)
+    assert_close_rms(t2np(r['dx_local']), rs['dx'], TAU, 'one-pass dx_local', True)
+    base = run_share(m, H, counts)
+    for k in ('dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_down'):
+        assert torch.equal(r[k], base[k]), k
