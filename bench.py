@@ -256,6 +256,8 @@ def main():
         extra = {'second_stream_latency': yl,
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
                  'ep_share_fwd_bwd_dgrad_one_pass': bench_share(max(5, args.steps // 5), 2, args.flags | 0x40),
+                 'ep_share_fwd_bwd_one_pass_lo_mxfp8': bench_share(max(5, args.steps // 5), 2,
+                                                                  args.flags | 0x40 | 0x80),
                  'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 

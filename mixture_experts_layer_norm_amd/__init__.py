@@ -32,6 +32,7 @@ MOE_FLAG_GEMM_WAVES4 = 0x8
 MOE_FLAG_OVERLAP_SHARED = 0x10
 MOE_FLAG_GEMM_BK32 = 0x20
 MOE_FLAG_BWD_DGRAD_ONE_PASS = 0x40
+MOE_FLAG_BWD_WGRAD_LO_MXFP8 = 0x80
 
 
 def MOE_FLAG_TILE_BLOCK(n):

@@ -36,17 +36,34 @@ struct BwdLayout {
   size_t mq_xT, ms_xT, mq_gdyT, ms_gdyT, mq_hT, ms_hT, mq_dauT, ms_dauT;
   // fp32: dh', h, da, du of the routed rows and of the shared expert's rows
   size_t f_dh, f_h, f_da, f_du, sf_dh, sf_h, sf_da, sf_du;
+  // BF16: the weight gradients' second K pass in MXFP8 (low halves and the exact operands, all
+  // quantised along the slots), routed and shared
+  size_t lq_dau, ls_dau, lq_gh, ls_gh, lq_x, ls_x, lq_dy, ls_dy;
+  size_t slq_dau, sls_dau, slq_gh, sls_gh, slq_x, sls_x, slq_dy, sls_dy;
   size_t total;
   int64_t n, Spad, Tpad;
+  int pad, pad_s;          // group alignment of the slot axis: routed, shared
+  bool lo_mx, lo_mx_s;     // BF16 weight gradients' low-half pass in MXFP8: routed, shared
 };
+
+// Under MOE_FLAG_BWD_WGRAD_LO_MXFP8 the BF16 weight gradients take their low-half pass in MXFP8
+// (a second, accumulating pass over the fp32 dW), where a group's K is long enough on average to
+// repay reading and writing dW once more.
+static bool wgrad_lo_mx(const moe_problem& p, int64_t rows, int64_t groups) {
+  return (p.flags & MOE_FLAG_BWD_WGRAD_LO_MXFP8) && rows >= 4096 * groups;
+}
 
 // Workspace of the backward for up to n = T*K slot rows (bf16).
 static BwdLayout bwd_layout(const moe_problem& p) {
   BwdLayout L{};
   const int64_t n = (int64_t)p.T * p.K, T = p.T, D = p.D, I = p.I, E = p.E, Is = p.I_shared;
   L.n = n;
-  L.Spad = (n + 64 * E + 63) / 64 * 64;
-  L.Tpad = (T + 127) / 64 * 64;
+  L.lo_mx = p.dtype == MOE_BF16 && wgrad_lo_mx(p, n, E);
+  L.lo_mx_s = p.dtype != MOE_F32 && Is > 0 && wgrad_lo_mx(p, T, 1);   // the shared expert is BF16 under MXFP8
+  L.pad = p.dtype == MOE_MXFP8 || L.lo_mx ? 128 : 64;               // 128: one MX K slice
+  L.pad_s = L.lo_mx_s ? 128 : 64;
+  L.Spad = (n + L.pad * E + L.pad - 1) / L.pad * L.pad;
+  L.Tpad = L.lo_mx_s ? (T + 127) / 128 * 128 : (T + 127) / 64 * 64;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = al256(o + bytes); return at; };
   L.err = take(256 + 4096);
@@ -70,7 +87,6 @@ static BwdLayout bwd_layout(const moe_problem& p) {
   if (p.dtype == MOE_MXFP8) {
     // rows quantised along D; dgrad-down output and h, [da | du] in fp32; [da | du] along I;
     // weights re-quantised transposed; slot-axis operands [features][Spad], experts 128-aligned
-    L.Spad = (n + 128 * E + 127) / 128 * 128;
     const int64_t S = L.Spad;
     L.mq_x = take(n * D); L.ms_x = take(n * D / 32); L.mq_dy = take(n * D); L.ms_dy = take(n * D / 32);
     L.m_dhp = take(n * I * 4); L.part = take(n * ((I + 255) / 256) * 4);
@@ -86,6 +102,11 @@ static BwdLayout bwd_layout(const moe_problem& p) {
     L.wdT = take(E * I * D * 2); L.wguT = take(E * D * 2 * I * 2);
     L.xT = take(D * L.Spad * 2); L.dyT = take(D * L.Spad * 2); L.ghT = take(2 * I * L.Spad * 2);
     L.dauT = take(4 * I * L.Spad * 2);
+    const int64_t S = L.Spad;
+    if (L.lo_mx) {
+      L.lq_dau = take(2 * I * S); L.ls_dau = take(2 * I * S / 32); L.lq_gh = take(I * S); L.ls_gh = take(I * S / 32);
+      L.lq_x = take(D * S); L.ls_x = take(D * S / 32); L.lq_dy = take(D * S); L.ls_dy = take(D * S / 32);
+    }
   }
   if (Is > 0) {
     L.s_a = take(T * Is * 4); L.s_u = take(T * Is * 4); L.s_dau = take(T * 4 * Is * 2);
@@ -93,6 +114,12 @@ static BwdLayout bwd_layout(const moe_problem& p) {
     L.s_wdT = take(Is * D * 2); L.s_wguT = take(D * 2 * Is * 2);
     L.s_xT = take(D * L.Tpad * 2); L.s_dyT = take(D * L.Tpad * 2); L.s_hT = take(2 * Is * L.Tpad * 2);
     L.s_dauT = take(4 * Is * L.Tpad * 2);
+    const int64_t S = L.Tpad;
+    if (L.lo_mx_s) {
+      L.slq_dau = take(2 * Is * S); L.sls_dau = take(2 * Is * S / 32); L.slq_gh = take(Is * S);
+      L.sls_gh = take(Is * S / 32); L.slq_x = take(D * S); L.sls_x = take(D * S / 32); L.slq_dy = take(D * S);
+      L.sls_dy = take(D * S / 32);
+    }
   }
   L.total = o;
   return L;
@@ -103,6 +130,9 @@ struct CoreBufs {
   float* part;
   int64_t Spad;
   int32_t* order;   // [G] dealing order of the K-grouped GEMMs (null for one group)
+  // MXFP8 codes and scales of the weight gradients' second pass: [da | du] and g*h low halves,
+  // x and dy, each [features][Spad] along the slots (all null: both passes in BF16)
+  uint8_t *q_dau, *s_dau, *q_gh, *s_gh, *q_x, *s_x, *q_dy, *s_dy;
 };
 
 // Backward of one set of groups (routed experts, or the shared expert as one group).
@@ -161,18 +191,44 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   // weight-gradient tiles of the longest groups first
   if (G > 1 && b.order && (st = launch_group_order(poff, G, b.order, s))) return st;
   const int32_t* order = G > 1 ? b.order : nullptr;
-  // dW_down[g] = sum_j dy_j (g_j h_j)^T   -> [D][I]  (B = g*h: high rows, then low rows)
+  if (!b.q_dy) {
+    // both halves in one K loop: B = g*h high rows then low rows; A = [da; du] high rows then low
+    GemmArgs w1;   // dW_down[g] = sum_j dy_j (g_j h_j)^T   -> [D][I]
+    w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
+    w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I;
+    w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp; w1.k_order = order;
+    if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
+    GemmArgs w2;   // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
+    w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
+    w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D;
+    w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp; w2.k_order = order;
+    return launch_gemm_bf16_kgroup(w2, G, s);
+  }
+  // MOE_FLAG_BWD_WGRAD_LO_MXFP8 on long groups: the high halves in BF16, then the low halves in
+  // MXFP8 added into the same fp32 outputs. A low half is below 2^-8 of its value, so the E4M3 rounding of the second pass (its
+  // operands quantised along the slots) costs about 2^-12 relative, with half the bytes and twice
+  // the MFMA rate of a second BF16 pass.
+  if ((st = launch_quantize_mx((const uint16_t*)b.dyT, D, (int)Sp, b.q_dy, b.s_dy, s))) return st;
+  if ((st = launch_quantize_mx((const uint16_t*)b.xT, D, (int)Sp, b.q_x, b.s_x, s))) return st;
+  if ((st = launch_quantize_mx((const uint16_t*)b.ghT + (int64_t)I * Sp, I, (int)Sp, b.q_gh, b.s_gh, s))) return st;
+  if ((st = launch_quantize_mx((const uint16_t*)b.dauT + (int64_t)2 * I * Sp, 2 * I, (int)Sp, b.q_dau, b.s_dau, s)))
+    return st;
+  // dW_down[g] = sum_j dy_j (g_j h_j)^T   -> [D][I]
   GemmArgs w1;
   w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
-  w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I;
-  w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp; w1.k_order = order;
+  w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I; w1.k_order = order;
   if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
+  GemmArgs m1 = w1;
+  m1.A = b.q_dy; m1.B = b.q_gh; m1.c_accumulate = 1;
+  if ((st = launch_gemm_mx_kgroup(m1, b.s_dy, b.s_gh, G, s))) return st;
   // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
   GemmArgs w2;
   w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
-  w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D;
-  w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp; w2.k_order = order;
-  return launch_gemm_bf16_kgroup(w2, G, s);
+  w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D; w2.k_order = order;
+  if ((st = launch_gemm_bf16_kgroup(w2, G, s))) return st;
+  GemmArgs m2 = w2;
+  m2.A = b.q_dau; m2.B = b.q_x; m2.c_accumulate = 1;
+  return launch_gemm_mx_kgroup(m2, b.s_dau, b.s_x, G, s);
 }
 
 // MXFP8 backward of the routed groups (the shared expert stays BF16). Weights are the forward's
@@ -253,12 +309,17 @@ int launch_reverse_dispatch_f32(const float* dx_slot, const int32_t* inv_perm, c
 static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
+  auto u = [&](size_t o) { return L.lo_mx ? (uint8_t*)(ws + o) : nullptr; };
   return CoreBufs{ws + L.act_a, ws + L.act_u, ws + L.dau, ws + L.wdT, ws + L.wguT, ws + L.xT, ws + L.dyT,
-                  ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad, (int32_t*)(ws + L.order)};
+                  ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad, (int32_t*)(ws + L.order),
+                  u(L.lq_dau), u(L.ls_dau), u(L.lq_gh), u(L.ls_gh), u(L.lq_x), u(L.ls_x), u(L.lq_dy), u(L.ls_dy)};
 }
 static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
+  auto u = [&](size_t o) { return L.lo_mx_s ? (uint8_t*)(ws + o) : nullptr; };
   return CoreBufs{ws + L.s_a, ws + L.s_u, ws + L.s_dau, ws + L.s_wdT, ws + L.s_wguT, ws + L.s_xT, ws + L.s_dyT,
-                  ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad, nullptr};
+                  ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad, nullptr,
+                  u(L.slq_dau), u(L.sls_dau), u(L.slq_gh), u(L.sls_gh), u(L.slq_x), u(L.sls_x), u(L.slq_dy),
+                  u(L.sls_dy)};
 }
 
 // one group of T rows for the shared expert: offsets {0, T}
@@ -280,7 +341,7 @@ static int shared_backward(const moe_problem* p, const void* x, const void* dy, 
                              F(L.sf_da), F(L.sf_du), s);
   }
   int st = launch_group_prefix(o, 1, p->T, o, (int32_t*)(wsb + L.tile_off_s), (int32_t*)(wsb + L.poff_s),
-                               (int32_t*)(wsb + L.err), s);
+                               (int32_t*)(wsb + L.err), s, L.pad_s);
   if (st) return st;
   return core_backward(1, p->T, p->D, p->I_shared, x, dy, nullptr, o, (int32_t*)(wsb + L.tile_off_s),
                        (int32_t*)(wsb + L.poff_s), w->ws_gate, w->ws_up, w->ws_down, dx, nullptr, dw->dws_gate,
@@ -395,7 +456,7 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
   char* wsb = (char*)ws;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(offsets, p->E, (int)slots, offs, (int32_t*)(wsb + L.tile_off),
-                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, L.pad)))
     return st;
   if (f32) {
     auto F = [&](size_t off) { return (float*)(wsb + off); };
@@ -444,7 +505,7 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
   if ((st = launch_gather_f32(r->topk_w, r->perm, n, (float*)(wsb + L.g_slot), stream))) return st;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(r->offsets, p->E, (int)n, offs, (int32_t*)(wsb + L.tile_off),
-                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, mx ? 128 : 64)))
+                                (int32_t*)(wsb + L.poff), (int32_t*)(wsb + L.err), stream, L.pad)))
     return st;
   if (f32) {
     auto F = [&](size_t off) { return (float*)(wsb + off); };

@@ -174,6 +174,7 @@ struct GemmArgs {
   // time with A and B displaced by these element offsets, accumulating into the same tile
   int64_t a_seg_shift = 0, b_seg_shift = 0;
   int32_t two_pass = 0;
+  int32_t c_accumulate = 0;           // fp32 outputs of the MXFP8 GEMM: C += product
 };
 
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);

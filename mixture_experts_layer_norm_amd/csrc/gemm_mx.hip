@@ -240,7 +240,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int64_t col = (int64_t)nt * BN + wn * WN + j * 32 + ccol;
-            if (col < a.N) out[orow * a.ldc + col] = acc[i][j][r];
+            if (col < a.N) out[orow * a.ldc + col] = acc[i][j][r] + (a.c_accumulate ? out[orow * a.ldc + col] : 0.f);
           }
         }
       }

@@ -68,12 +68,37 @@ def run_share(m, H, counts, flags=0):
     return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, err=err, **gr)
 
 
+# Groups of 4096+ slots on average: with MOE_FLAG_BWD_WGRAD_LO_MXFP8 the weight gradients'
+# low-half pass runs in MXFP8 (routed and shared expert), as it does on the full-size share.
+LONG_SHARE = synth.EPShareConfig('long_share_bf16_T4096_K3_D256_I256_E3', tokens=4096, D=256, I=256, E_local=3, K=3,
+                                 I_shared=128, zipf_s=1.2, seed=43)
+
+
 @pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242], [0, 0, 500]], ids=['empty_mid', 'ragged', 'one_hot'])
 def test_experts_forward_backward_small(m, counts):
-    print(f'[backward] share counts={counts}', flush=True)
+    check_share(m, SMALL_SHARE, counts)
+
+
+@pytest.mark.parametrize('lo_mx', [False, True], ids=['bf16', 'lo_mxfp8'])
+@pytest.mark.parametrize('counts', [[6000, 0, 4321], [1, 7003, 5284]], ids=['empty_mid', 'ragged'])
+def test_experts_forward_backward_long_groups(m, counts, lo_mx):
+    check_share(m, LONG_SHARE, counts, m.MOE_FLAG_BWD_WGRAD_LO_MXFP8 if lo_mx else 0)
+
+
+def test_wgrad_lo_mxfp8_short_groups_unchanged(m):
+    """On groups shorter than 4096 rows on average the flag leaves every output bitwise unchanged."""
     H = synth.host_share(SMALL_SHARE)
+    a = run_share(m, H, [300, 0, 157], flags=m.MOE_FLAG_BWD_WGRAD_LO_MXFP8)
+    b = run_share(m, H, [300, 0, 157])
+    for k in ('dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_gate', 'dws_up', 'dws_down', 'dx_local'):
+        assert torch.equal(a[k], b[k]), k
+
+
+def check_share(m, cfg, counts, flags=0):
+    print(f'[backward] share {cfg.name} counts={counts} flags={flags:#x}', flush=True)
+    H = synth.host_share(cfg)
     S = int(sum(counts))
-    r = run_share(m, H, counts)
+    r = run_share(m, H, counts, flags)
     assert r['err'] == 0
     c = np.array(counts)
     y = oracle.experts_forward(H.x_slot[:S], c, H.w_gate, H.w_up, H.w_down)
