@@ -132,13 +132,19 @@ LAYER_BWD = synth.scaled(synth.DSV3, 'layer_bwd_bf16_T300_D256_I256_E16_K4', T=3
                          I_shared=128)
 
 
-@pytest.mark.parametrize('cfg', [LAYER_BWD, synth.scaled(LAYER_BWD, 'layer_bwd_noshared', I_shared=0, T=130, K=2)],
-                         ids=lambda c: c.name)
-def test_layer_backward(m, cfg):
-    print(f'[backward] layer {cfg.name}', flush=True)
+# Three experts over 6144 tokens x 2 routes: groups long enough for MOE_FLAG_BWD_WGRAD_LO_MXFP8
+# (routed and shared expert) on the whole-layer backward.
+LAYER_LONG = synth.scaled(LAYER_BWD, 'layer_bwd_long_T6144_E3_K2', T=6144, E=3, K=2)
+
+
+@pytest.mark.parametrize('cfg,flags', [(LAYER_BWD, 0), (synth.scaled(LAYER_BWD, 'layer_bwd_noshared', I_shared=0, T=130,
+                                                                     K=2), 0), (LAYER_LONG, 0x80)],
+                         ids=['layer_bwd', 'noshared', 'long_lo_mxfp8'])
+def test_layer_backward(m, cfg, flags):
+    print(f'[backward] layer {cfg.name} flags={flags:#x}', flush=True)
     H = synth.host_layer(cfg)
     L = synth.to_device(H)
-    run = ForwardRun(m, L, want_parts=False)()
+    run = ForwardRun(m, L, flags=flags, want_parts=False)()
     dout_h = synth.host_dout(cfg, cfg.T)
     dout = bf(dout_h)
     E, I, D, Is, T, K = cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.T, cfg.K

@@ -33,12 +33,12 @@ SMALL = synth.EPShareConfig('small_share_mxfp8_T100_K5_D256_I256_E3', tokens=100
                             I_shared=128, zipf_s=1.2, seed=43)
 
 
-def run_share_mx(m, H, q, counts, dev_w=None):
+def run_share_mx(m, H, q, counts, dev_w=None, flags=0):
     """experts_forward + experts_backward in MXFP8 on host share inputs; q: MX bytes of the weights."""
     cfg = H.cfg
     S = int(sum(counts))
     E, I, D, Is = cfg.E_local, cfg.I, cfg.D, cfg.I_shared
-    p = m.problem(cfg.tokens, D, I, E, cfg.K, Is, 'mxfp8')
+    p = m.problem(cfg.tokens, D, I, E, cfg.K, Is, 'mxfp8', flags=flags)
     dev = dict(x_slot=bf(H.x_slot[:S]), dy_slot=bf(H.dy_slot[:S]), x_local=bf(H.x_local), dy_local=bf(H.dy_local),
                ws=[bf(H.ws_gate), bf(H.ws_up), bf(H.ws_down)],
                wq=[u8(q[k][0]) for k in ('w_gate', 'w_up', 'w_down')],
@@ -158,6 +158,24 @@ def test_mx_experts_backward_deterministic(m):
     b = run_share_mx(m, H, q, [300, 0, 157])
     for k in ('y', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_down', 'dx_local'):
         assert torch.equal(a[k], b[k]), k
+
+
+def test_mx_shared_expert_wgrad_lo_mxfp8(m):
+    """MOE_FLAG_BWD_WGRAD_LO_MXFP8 under MOE_MXFP8 with 4096 local tokens: the BF16 shared
+    expert's weight gradients take their low-half pass in MXFP8 and stay within the BF16 bar; the
+    routed experts (short groups here) are bitwise as without the flag."""
+    cfg = dataclasses.replace(SMALL, name='share_mxfp8_T4096_K1_D256_I256_E3', tokens=4096, K=1)
+    H = synth.host_share(cfg)
+    q = {k: oracle.mx_quantize(getattr(H, k).astype(np.float64)) for k in ('w_gate', 'w_up', 'w_down')}
+    counts = [300, 0, 157]
+    r = run_share_mx(m, H, q, counts, flags=m.MOE_FLAG_BWD_WGRAD_LO_MXFP8)
+    base = run_share_mx(m, H, q, counts)
+    assert r['err'] == 0
+    for k in ('y', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dx_local'):
+        assert torch.equal(r[k], base[k]), k
+    rs = oracle.shared_backward(H.x_local, H.dy_local, H.ws_gate, H.ws_up, H.ws_down)
+    for k in ('dW_gate', 'dW_up', 'dW_down'):
+        assert_close_rms(t2np(r[k.replace('dW', 'dws')]), rs[k], TOL['bf16'], 'shared lo-MXFP8 ' + k)
 
 
 def h64(t):
