@@ -111,7 +111,9 @@ typedef struct moe_problem {
  * least 4096 rows (routed: T*K >= 4096 E; shared expert: T >= 4096, also under MOE_MXFP8), since
  * it reads and writes dW once more; otherwise the flag changes nothing. The low halves keep
  * about 4 significant bits, so dW carries about 2^-13 relative error per product: measured max
- * |d| of dW at 7e-4 RMS against 2e-5 with both passes in BF16 (both far inside tau = 2e-2). */
+ * |d| of dW at 7e-4 RMS against 2e-5 with both passes in BF16 (both far inside tau = 2e-2).
+ * moe_backward_workspace_size grows by the quantised operands, (3 I + 2 D) * 33/32 bytes per
+ * padded slot (routed) and (3 I_shared + 2 D) * 33/32 per padded token (shared), where taken. */
 #define MOE_FLAG_BWD_WGRAD_LO_MXFP8 0x80
 #define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
