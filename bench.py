@@ -255,6 +255,8 @@ def main():
         torch.cuda.empty_cache()
         extra = {'second_stream_latency': yl,
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
+                 'ep_share_fwd_bwd_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
+                                                                  keep=True),
                  'ep_share_fwd_bwd_dgrad_one_pass': bench_share(max(5, args.steps // 5), 2, args.flags | 0x40),
                  'ep_share_fwd_bwd_one_pass_lo_mxfp8': bench_share(max(5, args.steps // 5), 2,
                                                                   args.flags | 0x40 | 0x80),
@@ -393,12 +395,13 @@ def bench_pull_schedule(moe, stream, R=8, N=8192, K=8, L=32, reps=20):
             'routes_pulled': pulled, 'routes_per_s': n / (ms * 1e-3)}
 
 
-def bench_share(steps, warmup, flags, dtype='bf16'):
+def bench_share(steps, warmup, flags, dtype='bf16', keep=False):
     """Forward + backward of one expert-parallel rank's share at the DSV3 shape (4 local experts,
     57,344 slots with Zipf(1.2) loads, shared expert on 7,168 tokens): moe_experts_forward then
     moe_experts_backward per step, inputs resident in HBM. dtype 'mxfp8': the routed experts in
     MXFP8 forward and backward (weights quantised on the device beforehand, untimed), the shared
-    expert in BF16. Returns a result dict."""
+    expert in BF16. keep: the forward hands a, u (fp32) to the backward, which skips its replay
+    (moe_experts_forward_keep / moe_experts_backward_kept). Returns a result dict."""
     import torch
     import synth
     import mixture_experts_layer_norm_amd as moe
@@ -429,12 +432,21 @@ def bench_share(steps, warmup, flags, dtype='bf16'):
     wsb = torch.empty((moe.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
     stream = torch.cuda.current_stream()
 
+    act = [torch.empty((S, I), device='cuda') for _ in range(2)] if keep else None
+
     def fwd():
-        moe.experts_forward(p, S, D_.x_slot, offsets, W, y, D_.x_local, sh, ws, stream=stream)
+        if keep:
+            moe.experts_forward_keep(p, S, D_.x_slot, offsets, W, y, D_.x_local, sh, *act, ws, stream=stream)
+        else:
+            moe.experts_forward(p, S, D_.x_slot, offsets, W, y, D_.x_local, sh, ws, stream=stream)
 
     def bwd():
-        moe.experts_backward(p, S, D_.x_slot, offsets, D_.g, D_.dy_slot, W, dxs, dg, G, D_.x_local, D_.dy_local,
-                             dxl, wsb, stream=stream)
+        if keep:
+            moe.experts_backward_kept(p, S, D_.x_slot, offsets, D_.g, D_.dy_slot, W, dxs, dg, G, D_.x_local,
+                                      D_.dy_local, dxl, *act, wsb, stream=stream)
+        else:
+            moe.experts_backward(p, S, D_.x_slot, offsets, D_.g, D_.dy_slot, W, dxs, dg, G, D_.x_local,
+                                 D_.dy_local, dxl, wsb, stream=stream)
 
     for _ in range(warmup):
         fwd()
@@ -462,7 +474,7 @@ def bench_share(steps, warmup, flags, dtype='bf16'):
     t_peak = (3.0 * 6.0 * S * D * I / (PEAK_MXFP8_TFLOPS if dtype == 'mxfp8' else PEAK_BF16_TFLOPS)
               + 3.0 * 6.0 * T * D * Is / PEAK_BF16_TFLOPS) / 1e12
     name = cfg.name.replace('bf16', dtype) if dtype != 'bf16' else cfg.name
-    return {'workload': f'{name} forward+backward', 'dtype': dtype, 'flags': flags, 'tokens': T, 'slots': S,
+    return {'workload': f'{name} forward+backward', 'dtype': dtype, 'flags': flags, 'keep_activations': keep, 'tokens': T, 'slots': S,
             'counts': D_.counts.tolist(), 'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms,
             'value': T / (ms * 1e-3), 'unit': 'tokens/s', 'slots_per_s': S / (ms * 1e-3),
             'tflops': flops / (ms * 1e-3) / 1e12, 'mfma_peak_frac': t_peak / (ms * 1e-3),

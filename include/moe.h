@@ -323,6 +323,30 @@ int moe_experts_backward(const moe_problem *p, int64_t slots, const void *x_slot
                          const void *x_local, const void *dy_local, void *dx_local,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_experts_forward that also hands the routed experts' pre-activations to the caller, so
+ * that moe_experts_backward_kept can skip its replay of them. act_a, act_u: [slots][I] fp32
+ * device buffers (16-byte aligned, I % 4 == 0) that receive a = x_slot W_gate^T and
+ * u = x_slot W_up^T with the backward replay's own GEMM, bitwise; h = SiLU(a) u is then formed
+ * from them with the fused epilogue's arithmetic, so y_slot and shared_out are bitwise those of
+ * moe_experts_forward. The replay the pages describe (sparsenotes page "Mixture-of-Kittens: MoE
+ * Megakernel for NVL72s", "The production details") recomputes a, u; on one GPU that is pure
+ * extra work, and 2 * slots * I * 4 bytes of HBM buy it back. MOE_BF16 only (otherwise
+ * MOE_ERR_UNSUPPORTED); null act_a or act_u: MOE_ERR_INVALID_ARG. */
+int moe_experts_forward_keep(const moe_problem *p, int64_t slots, const void *x_slot,
+                             const int32_t *offsets, const moe_weights *w, void *y_slot,
+                             const void *x_local, void *shared_out, float *act_a, float *act_u,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_experts_backward reading the routed a, u that moe_experts_forward_keep wrote for the same
+ * x_slot, offsets and weights, instead of replaying them; every output is bitwise that of
+ * moe_experts_backward. The shared expert still replays its own (T rows). MOE_BF16 only. */
+int moe_experts_backward_kept(const moe_problem *p, int64_t slots, const void *x_slot,
+                              const int32_t *offsets, const float *g_slot, const void *dy_slot,
+                              const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,
+                              const void *x_local, const void *dy_local, void *dx_local,
+                              const float *act_a, const float *act_u, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* MX quantiser (OCP Microscaling v1.0; the Notes' MXFP8, "The production details"): src
  * [rows][cols] bf16 -> q [rows][cols] E4M3 bytes and scales [rows][cols/32] E8M0 bytes, blocks
  * of 32 along each row. Scale 2^(floor(log2 amax) - 8) clamped to [2^-127, 2^127]; elements

@@ -20,6 +20,8 @@
 // by default; with MOE_FLAG_BWD_DGRAD_ONE_PASS it contracts the bf16 da, du alone (every dx
 // element sums 2I products with independent roundings, so the error stays within the BF16 bound;
 // one K pass instead of two). x, dy and the weights are exact bf16 inputs.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
@@ -143,7 +145,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
                          const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                          const void* wg, const void* wu, const void* wd, void* dx_rows, float* dg_rows,
                          float* dw_gate, float* dw_up, float* dw_down, const CoreBufs& b, hipStream_t s,
-                         bool dgrad_one_pass) {
+                         bool dgrad_one_pass, bool replay = true) {
   int st;
   // transposed weights: W_down^T [G][I][D]; [W_gate^T | W_up^T] [G][D][2I]
   if ((st = launch_transpose_batched(wd, G, D, I, b.wdT, D, (int64_t)I * D, 0, s))) return st;
@@ -156,11 +158,13 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   grp.groups = G;
   grp.max_mtiles = (n_cap + kGemmBM - 1) / kGemmBM + G;
 
-  // replay: a = x W_gate^T, u = x W_up^T (kept in fp32)
-  GemmArgs r;
-  r.A = x_rows; r.lda = D; r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
-  r.N = I; r.K = D; r.C = b.act_a; r.C2 = b.act_u; r.ldc = I;
-  if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s))) return st;
+  // replay: a = x W_gate^T, u = x W_up^T (kept in fp32); skipped when the forward kept them
+  if (replay) {
+    GemmArgs r;
+    r.A = x_rows; r.lda = D; r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
+    r.N = I; r.K = D; r.C = b.act_a; r.C2 = b.act_u; r.ldc = I;
+    if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s))) return st;
+  }
 
   // dgrad-down + SwiGLU backward: dh' = dy W_down; da, du (as bf16 hi/lo pairs); partial <h, dh'>
   GemmArgs d;
@@ -363,11 +367,31 @@ int moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
-                        const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
-                        void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace moe {
+
+// h = bf16(SiLU(a) u) from the kept fp32 a, u: the arithmetic of the SwiGLU GEMM epilogue, so h
+// (and y) are bitwise those of the fused path.
+__global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* __restrict__ a, const float* __restrict__ u,
+                                                          int64_t n4, uint16_t* __restrict__ h) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 va = reinterpret_cast<const float4*>(a)[i], vu = reinterpret_cast<const float4*>(u)[i];
+    const uint32_t lo = (uint32_t)f2bf(silu_f(va.x) * vu.x) | ((uint32_t)f2bf(silu_f(va.y) * vu.y) << 16);
+    const uint32_t hi = (uint32_t)f2bf(silu_f(va.z) * vu.z) | ((uint32_t)f2bf(silu_f(va.w) * vu.w) << 16);
+    reinterpret_cast<uint2*>(h)[i] = make_uint2(lo, hi);
+  }
+}
+
+static int experts_forward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                                const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
+                                float* act_a, float* act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
+  const bool keep = act_a || act_u;
+  if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (keep && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (keep && (!al16(act_a) || !al16(act_u) || p->I % 4)) return MOE_ERR_MISALIGNED;
   const bool mx = p->dtype == MOE_MXFP8;
   // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
   auto gemm = p->dtype == MOE_F32 ? launch_gemm_f32 : launch_gemm_bf16;
@@ -413,7 +437,19 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   GemmArgs g1;
   g1.A = x_slot; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
   g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = wsb + L.h; g1.ldc = p->I;
-  if ((st = gemm(g1, gr, EPI_SWIGLU, stream))) return st;
+  if (keep) {
+    // a, u to the caller in fp32 (the backward's replay GEMM), then h from them
+    g1.C = act_a; g1.C2 = act_u;
+    if ((st = gemm(g1, gr, EPI_SAVE_AU, stream))) return st;
+    const int64_t n4 = slots * p->I / 4;
+    if (n4 > 0) {
+      const unsigned nb = (unsigned)std::min<int64_t>((n4 + 255) / 256, 16384);
+      hipLaunchKernelGGL(swiglu_rows_kernel, dim3(nb), dim3(256), 0, stream, act_a, act_u, n4, (uint16_t*)(wsb + L.h));
+      MOE_LAUNCH_CHECK();
+    }
+  } else if ((st = gemm(g1, gr, EPI_SWIGLU, stream))) {
+    return st;
+  }
   GemmArgs g2;
   g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
   g2.N = p->D; g2.K = p->I; g2.C = y_slot; g2.ldc = p->D;
@@ -434,12 +470,16 @@ int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot,
   return MOE_OK;
 }
 
-int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
-                         const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
-                         float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
-                         void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
+static int experts_backward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                                 const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
+                                 float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
+                                 void* dx_local, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
+  const bool kept = act_a || act_u;
+  if (kept && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (kept && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
@@ -470,14 +510,57 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
                                (int32_t*)(wsb + L.poff), w, dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, wsb,
                                L, stream)))
       return st;
-  } else if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
-                          (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down, dx_slot, dg_slot, dw->dw_gate,
-                          dw->dw_up, dw->dw_down, routed_bufs(wsb, L), stream,
-                          (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0))) {
-    return st;
+  } else {
+    CoreBufs cb = routed_bufs(wsb, L);
+    if (kept) {
+      cb.act_a = const_cast<float*>(act_a);   // read only from here on
+      cb.act_u = const_cast<float*>(act_u);
+    }
+    if ((st = core_backward(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
+                            (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down, dx_slot, dg_slot, dw->dw_gate,
+                            dw->dw_up, dw->dw_down, cb, stream, (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0,
+                            !kept)))
+      return st;
   }
   if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream);
   return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                        const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, nullptr, nullptr, ws,
+                              ws_bytes, stream);
+}
+
+int moe_experts_forward_keep(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                             const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
+                             float* act_a, float* act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
+  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, act_a, act_u, ws,
+                              ws_bytes, stream);
+}
+
+int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                         const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
+                         float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
+                         void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return experts_backward_impl(p, slots, x_slot, offsets, g_slot, dy_slot, w, dx_slot, dg_slot, dw, x_local,
+                               dy_local, dx_local, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_experts_backward_kept(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
+                              const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
+                              float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
+                              void* dx_local, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
+  return experts_backward_impl(p, slots, x_slot, offsets, g_slot, dy_slot, w, dx_slot, dg_slot, dw, x_local,
+                               dy_local, dx_local, act_a, act_u, ws, ws_bytes, stream);
 }
 
 int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits, const moe_weights* w,

@@ -35,7 +35,7 @@ SMALL_SHARE = synth.EPShareConfig('small_share_bf16_T100_K5_D256_I256_E3', token
                                   I_shared=128, zipf_s=1.2, seed=41)
 
 
-def run_share(m, H, counts, flags=0):
+def run_share(m, H, counts, flags=0, keep=False):
     cfg = H.cfg
     S = int(sum(counts))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -51,8 +51,12 @@ def run_share(m, H, counts, flags=0):
     y = torch.empty((S, cfg.D), dtype=torch.bfloat16, device='cuda')
     sh = torch.empty((cfg.tokens, cfg.D), dtype=torch.bfloat16, device='cuda')
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
-    m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
     E, I, D, Is = cfg.E_local, cfg.I, cfg.D, cfg.I_shared
+    if keep:
+        act = [torch.full((S, I), float('nan'), device='cuda') for _ in range(2)]
+        m.experts_forward_keep(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, *act, ws)
+    else:
+        m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
     dxs = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
     dg = torch.empty((S,), dtype=torch.float32, device='cuda')
     gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
@@ -61,8 +65,12 @@ def run_share(m, H, counts, flags=0):
     G = m.make_grads(**gr)
     dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
     wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
-    m.experts_backward(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
-                       dev['dy_local'], dxl, wsb)
+    if keep:
+        m.experts_backward_kept(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
+                                dev['dy_local'], dxl, *act, wsb)
+    else:
+        m.experts_backward(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
+                           dev['dy_local'], dxl, wsb)
     torch.cuda.synchronize()
     err = int(wsb[:4].view(torch.int32).item())
     return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, err=err, **gr)
@@ -83,6 +91,19 @@ def test_experts_forward_backward_small(m, counts):
 @pytest.mark.parametrize('counts', [[6000, 0, 4321], [1, 7003, 5284]], ids=['empty_mid', 'ragged'])
 def test_experts_forward_backward_long_groups(m, counts, lo_mx):
     check_share(m, LONG_SHARE, counts, m.MOE_FLAG_BWD_WGRAD_LO_MXFP8 if lo_mx else 0)
+
+
+@pytest.mark.parametrize('flags', [0, 0x40], ids=['default', 'one_pass'])
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242], [0, 0, 500]], ids=['empty_mid', 'ragged', 'one_hot'])
+def test_experts_keep_activations_bitwise(m, counts, flags):
+    """moe_experts_forward_keep + moe_experts_backward_kept: a, u handed from the forward to the
+    backward instead of replayed; every output bitwise that of the replaying pair."""
+    H = synth.host_share(SMALL_SHARE)
+    a = run_share(m, H, counts, flags, keep=True)
+    b = run_share(m, H, counts, flags)
+    assert a['err'] == 0
+    for k in ('y', 'sh', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_gate', 'dws_up', 'dws_down', 'dx_local'):
+        assert torch.equal(a[k], b[k]), k
 
 
 def test_wgrad_lo_mxfp8_short_groups_unchanged(m):
