@@ -261,6 +261,8 @@ def main():
                  'ep_share_fwd_bwd_one_pass_lo_mxfp8': bench_share(max(5, args.steps // 5), 2,
                                                                   args.flags | 0x40 | 0x80),
                  'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
+                 'ep_share_fwd_bwd_mxfp8_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
+                                                                        'mxfp8', keep=True),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
 
     line = {

@@ -330,8 +330,9 @@ int moe_experts_backward(const moe_problem *p, int64_t slots, const void *x_slot
  * from them with the fused epilogue's arithmetic, so y_slot and shared_out are bitwise those of
  * moe_experts_forward. The replay the pages describe (sparsenotes page "Mixture-of-Kittens: MoE
  * Megakernel for NVL72s", "The production details") recomputes a, u; on one GPU that is pure
- * extra work, and 2 * slots * I * 4 bytes of HBM buy it back. MOE_BF16 only (otherwise
- * MOE_ERR_UNSUPPORTED); null act_a or act_u: MOE_ERR_INVALID_ARG. */
+ * extra work, and 2 * slots * I * 4 bytes of HBM buy it back. MOE_BF16 and MOE_MXFP8 (a, u
+ * from the block-scaled GEMM over Q_D(x_slot), h quantised along I from them as the fused
+ * epilogue does); MOE_F32: MOE_ERR_UNSUPPORTED; null act_a or act_u: MOE_ERR_INVALID_ARG. */
 int moe_experts_forward_keep(const moe_problem *p, int64_t slots, const void *x_slot,
                              const int32_t *offsets, const moe_weights *w, void *y_slot,
                              const void *x_local, void *shared_out, float *act_a, float *act_u,
@@ -339,7 +340,8 @@ int moe_experts_forward_keep(const moe_problem *p, int64_t slots, const void *x_
 
 /* moe_experts_backward reading the routed a, u that moe_experts_forward_keep wrote for the same
  * x_slot, offsets and weights, instead of replaying them; every output is bitwise that of
- * moe_experts_backward. The shared expert still replays its own (T rows). MOE_BF16 only. */
+ * moe_experts_backward. The shared expert still replays its own (T rows). MOE_BF16 and
+ * MOE_MXFP8 (the a, u of moe_experts_forward_keep under the same dtype). */
 int moe_experts_backward_kept(const moe_problem *p, int64_t slots, const void *x_slot,
                               const int32_t *offsets, const float *g_slot, const void *dy_slot,
                               const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,

@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "mx_codec.h"
 
 namespace moe {
 
@@ -247,10 +248,16 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
 static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
                             const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                             const moe_weights* w, void* dx_rows, float* dg_rows, float* dw_gate, float* dw_up,
-                            float* dw_down, char* ws, const BwdLayout& L, hipStream_t s) {
+                            float* dw_down, char* ws, const BwdLayout& L, hipStream_t s,
+                            const float* kept_a = nullptr, const float* kept_u = nullptr) {
   int st;
   auto B = [&](size_t off) { return (uint8_t*)(ws + off); };
-  auto F = [&](size_t off) { return (float*)(ws + off); };
+  // a, u: the forward's (kept) or replayed into the workspace
+  auto F = [&](size_t off) {
+    if (kept_a && off == L.act_a) return const_cast<float*>(kept_a);
+    if (kept_a && off == L.act_u) return const_cast<float*>(kept_u);
+    return (float*)(ws + off);
+  };
   const int64_t S = L.Spad, ID = (int64_t)I * D;
   // weights re-quantised along the backward contraction axis
   if ((st = launch_mx_requant_t((const uint8_t*)w->w_down, w->sc_down, G, D, I, B(L.mq_wdT), B(L.ms_wdT), D, 0, ID, ID / 32, s))) return st;
@@ -272,10 +279,12 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   grp.tile_off = tile_off;
   grp.groups = G;
   grp.max_mtiles = (n_cap + kGemmBM - 1) / kGemmBM + G;
-  GemmArgs r;   // replay
-  r.A = B(L.mq_x); r.lda = D; r.B = w->w_gate; r.B2 = w->w_up; r.ldb = D; r.b_group_stride = ID;
-  r.N = I; r.K = D; r.C = F(L.act_a); r.C2 = F(L.act_u); r.ldc = I;
-  if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s))) return st;
+  if (!kept_a) {
+    GemmArgs r;   // replay
+    r.A = B(L.mq_x); r.lda = D; r.B = w->w_gate; r.B2 = w->w_up; r.ldb = D; r.b_group_stride = ID;
+    r.N = I; r.K = D; r.C = F(L.act_a); r.C2 = F(L.act_u); r.ldc = I;
+    if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s))) return st;
+  }
   GemmArgs d;   // dgrad-down
   d.A = B(L.mq_dy); d.lda = D; d.B = B(L.mq_wdT); d.ldb = D; d.b_group_stride = ID;
   d.N = I; d.K = D; d.C = F(L.m_dhp); d.ldc = I; d.c_f32 = 1;
@@ -383,6 +392,32 @@ __global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* __restric
   }
 }
 
+// The same from the kept a, u under MXFP8: h = SiLU(a) u in fp32, quantised along I in blocks of
+// 32 (E4M3 codes, E8M0 scales) exactly as the MXFP8 SwiGLU GEMM epilogue does. One thread per
+// block; blocks are row-major over [rows][I / 32].
+__global__ __launch_bounds__(256) void swiglu_rows_mx_kernel(const float* __restrict__ a, const float* __restrict__ u,
+                                                             int64_t nblk, uint8_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sc) {
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * 256) {
+    const float4* pa = reinterpret_cast<const float4*>(a + b * 32);
+    const float4* pu = reinterpret_cast<const float4*>(u + b * 32);
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 va = pa[k], vu = pu[k];
+      v[4 * k] = silu_f(va.x) * vu.x;
+      v[4 * k + 1] = silu_f(va.y) * vu.y;
+      v[4 * k + 2] = silu_f(va.z) * vu.z;
+      v[4 * k + 3] = silu_f(va.w) * vu.w;
+    }
+    uint32_t p[8];
+    sc[b] = (uint8_t)mx_block(v, p);
+    u32x4* d = reinterpret_cast<u32x4*>(q + b * 32);
+    d[0] = u32x4{p[0], p[1], p[2], p[3]};
+    d[1] = u32x4{p[4], p[5], p[6], p[7]};
+  }
+}
+
 static int experts_forward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                                 const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
                                 float* act_a, float* act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -390,7 +425,7 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
   if (st) return st;
   const bool keep = act_a || act_u;
   if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
-  if (keep && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (keep && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (keep && (!al16(act_a) || !al16(act_u) || p->I % 4)) return MOE_ERR_MISALIGNED;
   const bool mx = p->dtype == MOE_MXFP8;
   // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
@@ -426,8 +461,22 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
     GemmArgs m1;
     m1.A = xq; m1.lda = p->D; m1.B = w->w_gate; m1.B2 = w->w_up; m1.ldb = p->D;
     m1.b_group_stride = (int64_t)p->I * p->D; m1.N = p->I; m1.K = p->D; m1.C = hq; m1.ldc = p->I;
-    if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream)))
+    if (keep) {
+      // a, u to the caller in fp32 (the backward's replay GEMM), then h quantised from them
+      m1.C = act_a; m1.C2 = act_u;
+      if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), nullptr, gr, EPI_SAVE_AU,
+                               stream)))
+        return st;
+      const int64_t nblk = slots * (p->I / 32);
+      if (nblk > 0) {
+        const unsigned nb = (unsigned)std::min<int64_t>((nblk + 255) / 256, 16384);
+        hipLaunchKernelGGL(swiglu_rows_mx_kernel, dim3(nb), dim3(256), 0, stream, act_a, act_u, nblk, hq, hs);
+        MOE_LAUNCH_CHECK();
+      }
+    } else if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU,
+                                    stream))) {
       return st;
+    }
     GemmArgs m2;
     m2.A = hq; m2.lda = p->I; m2.B = w->w_down; m2.ldb = p->I; m2.b_group_stride = (int64_t)p->D * p->I;
     m2.N = p->D; m2.K = p->I; m2.C = y_slot; m2.ldc = p->D;
@@ -479,7 +528,7 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
   if (st) return st;
   const bool kept = act_a || act_u;
   if (kept && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
-  if (kept && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (kept && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
@@ -508,7 +557,7 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
   } else if (mx) {
     if ((st = core_backward_mx(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
                                (int32_t*)(wsb + L.poff), w, dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, wsb,
-                               L, stream)))
+                               L, stream, act_a, act_u)))
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);

@@ -128,12 +128,12 @@ def test_one_hip_runtime_whatever_the_import_order():
 
 def test_keep_activation_entry_points_reject_without_gpu():
     """moe_experts_forward_keep / moe_experts_backward_kept check on the host, before any HIP
-    call: both activation buffers are required, and only MOE_BF16 is supported."""
+    call: both activation buffers are required, and MOE_F32 is not supported."""
     import mixture_experts_layer_norm_amd as m
     lib = m._lib
     W, G = m.Weights(), m.Grads()
     fake = 1 << 20   # never dereferenced: every call below returns before touching memory
-    for dt, acts, code in (('bf16', (fake, None), -1), ('f32', (fake, fake), -2), ('mxfp8', (fake, fake), -2)):
+    for dt, acts, code in (('bf16', (fake, None), -1), ('mxfp8', (None, fake), -1), ('f32', (fake, fake), -2)):
         p = m.problem(100, 256, 256, 3, 5, 128, dt)
         assert lib.moe_experts_forward_keep(ctypes.byref(p), 0, fake, fake, ctypes.byref(W), fake, fake, fake,
                                             *acts, fake, 1 << 40, None) == code, dt

@@ -33,7 +33,7 @@ SMALL = synth.EPShareConfig('small_share_mxfp8_T100_K5_D256_I256_E3', tokens=100
                             I_shared=128, zipf_s=1.2, seed=43)
 
 
-def run_share_mx(m, H, q, counts, dev_w=None, flags=0):
+def run_share_mx(m, H, q, counts, dev_w=None, flags=0, keep=False):
     """experts_forward + experts_backward in MXFP8 on host share inputs; q: MX bytes of the weights."""
     cfg = H.cfg
     S = int(sum(counts))
@@ -49,7 +49,11 @@ def run_share_mx(m, H, q, counts, dev_w=None, flags=0):
     y = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
     sh = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
-    m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
+    if keep:
+        act = [torch.full((S, I), float('nan'), device='cuda') for _ in range(2)]
+        m.experts_forward_keep(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, *act, ws)
+    else:
+        m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
     dxs = torch.empty((S, D), dtype=torch.bfloat16, device='cuda')
     dg = torch.empty((S,), dtype=torch.float32, device='cuda')
     gr = dict(dw_gate=torch.full((E, I, D), float('nan'), device='cuda'),
@@ -60,8 +64,12 @@ def run_share_mx(m, H, q, counts, dev_w=None, flags=0):
     dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
     wsb = torch.full((m.backward_workspace_size(p),), 0x7f, dtype=torch.uint8, device='cuda')
     wsb[:4].zero_()
-    m.experts_backward(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
-                       dev['dy_local'], dxl, wsb)
+    if keep:
+        m.experts_backward_kept(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
+                                dev['dy_local'], dxl, *act, wsb)
+    else:
+        m.experts_backward(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
+                           dev['dy_local'], dxl, wsb)
     torch.cuda.synchronize()
     err = int(wsb[:4].view(torch.int32).item())
     return dict(y=y, sh=sh, dx_slot=dxs, dg=dg, dx_local=dxl, err=err, **gr)
@@ -157,6 +165,21 @@ def test_mx_experts_backward_deterministic(m):
     a = run_share_mx(m, H, q, [300, 0, 157])
     b = run_share_mx(m, H, q, [300, 0, 157])
     for k in ('y', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_down', 'dx_local'):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242], [129, 128, 127]],
+                         ids=['empty_mid', 'ragged_single', 'around_128'])
+def test_mx_experts_keep_activations_bitwise(m, counts):
+    """moe_experts_forward_keep + moe_experts_backward_kept under MXFP8: a, u from the forward's
+    block-scaled GEMM, h quantised from them outside the GEMM; every output bitwise that of the
+    fused forward and the replaying backward."""
+    H = synth.host_share(SMALL)
+    q = {k: oracle.mx_quantize(getattr(H, k).astype(np.float64)) for k in ('w_gate', 'w_up', 'w_down')}
+    a = run_share_mx(m, H, q, counts, keep=True)
+    b = run_share_mx(m, H, q, counts)
+    assert a['err'] == 0
+    for k in ('y', 'sh', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_gate', 'dws_up', 'dws_down', 'dx_local'):
         assert torch.equal(a[k], b[k]), k
 
 
