@@ -402,8 +402,8 @@ def bench_share(steps, warmup, flags, dtype='bf16', keep=False):
     57,344 slots with Zipf(1.2) loads, shared expert on 7,168 tokens): moe_experts_forward then
     moe_experts_backward per step, inputs resident in HBM. dtype 'mxfp8': the routed experts in
     MXFP8 forward and backward (weights quantised on the device beforehand, untimed), the shared
-    expert in BF16. keep: the forward hands a, u (fp32) to the backward, which skips its replay
-    (moe_experts_forward_keep / moe_experts_backward_kept). Returns a result dict."""
+    expert in BF16. keep: the forward hands a, u (fp32, routed and shared expert) to the backward,
+    which skips its replays (moe_experts_forward_keep / moe_experts_backward_kept). Returns a result dict."""
     import torch
     import synth
     import mixture_experts_layer_norm_amd as moe
@@ -434,7 +434,7 @@ def bench_share(steps, warmup, flags, dtype='bf16', keep=False):
     wsb = torch.empty((moe.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
     stream = torch.cuda.current_stream()
 
-    act = [torch.empty((S, I), device='cuda') for _ in range(2)] if keep else None
+    act = [torch.empty(shp, device='cuda') for shp in ((S, I), (S, I), (T, Is), (T, Is))] if keep else None
 
     def fwd():
         if keep:

@@ -332,22 +332,27 @@ int moe_experts_backward(const moe_problem *p, int64_t slots, const void *x_slot
  * Megakernel for NVL72s", "The production details") recomputes a, u; on one GPU that is pure
  * extra work, and 2 * slots * I * 4 bytes of HBM buy it back. MOE_BF16 and MOE_MXFP8 (a, u
  * from the block-scaled GEMM over Q_D(x_slot), h quantised along I from them as the fused
- * epilogue does); MOE_F32: MOE_ERR_UNSUPPORTED; null act_a or act_u: MOE_ERR_INVALID_ARG. */
+ * epilogue does); MOE_F32: MOE_ERR_UNSUPPORTED; null act_a or act_u: MOE_ERR_INVALID_ARG.
+ * shared_act_a, shared_act_u: the same for the shared expert, [T][I_shared] fp32 (BF16 GEMM under
+ * both dtypes), or both null to let the backward replay the shared expert; ignored when
+ * I_shared == 0; only one of the two given: MOE_ERR_INVALID_ARG. */
 int moe_experts_forward_keep(const moe_problem *p, int64_t slots, const void *x_slot,
                              const int32_t *offsets, const moe_weights *w, void *y_slot,
                              const void *x_local, void *shared_out, float *act_a, float *act_u,
-                             void *ws, size_t ws_bytes, hipStream_t stream);
+                             float *shared_act_a, float *shared_act_u, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* moe_experts_backward reading the routed a, u that moe_experts_forward_keep wrote for the same
  * x_slot, offsets and weights, instead of replaying them; every output is bitwise that of
- * moe_experts_backward. The shared expert still replays its own (T rows). MOE_BF16 and
- * MOE_MXFP8 (the a, u of moe_experts_forward_keep under the same dtype). */
+ * moe_experts_backward. The shared expert reads shared_act_a, shared_act_u when given (both
+ * or neither), and replays its own otherwise. MOE_BF16 and MOE_MXFP8 (the buffers of
+ * moe_experts_forward_keep under the same dtype). */
 int moe_experts_backward_kept(const moe_problem *p, int64_t slots, const void *x_slot,
                               const int32_t *offsets, const float *g_slot, const void *dy_slot,
                               const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,
                               const void *x_local, const void *dy_local, void *dx_local,
-                              const float *act_a, const float *act_u, void *ws, size_t ws_bytes,
-                              hipStream_t stream);
+                              const float *act_a, const float *act_u, const float *shared_act_a,
+                              const float *shared_act_u, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* MX quantiser (OCP Microscaling v1.0; the Notes' MXFP8, "The production details"): src
  * [rows][cols] bf16 -> q [rows][cols] E4M3 bytes and scales [rows][cols/32] E8M0 bytes, blocks

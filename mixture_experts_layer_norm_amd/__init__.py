@@ -98,9 +98,9 @@ _sig = {
     'moe_experts_backward': (ctypes.c_int, [_PP, _i64, _P, _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                                             ctypes.POINTER(Grads), _P, _P, _P, _P, _sz, _P]),
     'moe_experts_forward_keep': (ctypes.c_int, [_PP, _i64, _P, _P, ctypes.POINTER(Weights), _P, _P, _P, _P, _P, _P,
-                                                _sz, _P]),
+                                                _P, _P, _sz, _P]),
     'moe_experts_backward_kept': (ctypes.c_int, [_PP, _i64, _P, _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
-                                                 ctypes.POINTER(Grads), _P, _P, _P, _P, _P, _P, _sz, _P]),
+                                                 ctypes.POINTER(Grads), _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_quantize_mx': (ctypes.c_int, [_P, _i64, _i32, _P, _P, _P]),
     'moe_route_gemm': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_route_gemm_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
@@ -234,21 +234,23 @@ def experts_backward(p, slots, x_slot, offsets, g_slot, dy_slot, weights: Weight
                                      ws.numel() * ws.element_size(), _stream(stream)), 'moe_experts_backward')
 
 
-def experts_forward_keep(p, slots, x_slot, offsets, weights: Weights, y_slot, x_local, shared_out, act_a, act_u, ws,
-                         stream=None):
+def experts_forward_keep(p, slots, x_slot, offsets, weights: Weights, y_slot, x_local, shared_out, act_a, act_u,
+                         shared_act_a, shared_act_u, ws, stream=None):
     _check(_lib.moe_experts_forward_keep(ctypes.byref(p), slots, _ptr(x_slot), _ptr(offsets), ctypes.byref(weights),
                                          _ptr(y_slot), _ptr(x_local), _ptr(shared_out), _ptr(act_a), _ptr(act_u),
-                                         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           'moe_experts_forward_keep')
+                                         _ptr(shared_act_a), _ptr(shared_act_u), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream)), 'moe_experts_forward_keep')
 
 
 def experts_backward_kept(p, slots, x_slot, offsets, g_slot, dy_slot, weights: Weights, dx_slot, dg_slot,
-                          grads: Grads, x_local, dy_local, dx_local, act_a, act_u, ws, stream=None):
+                          grads: Grads, x_local, dy_local, dx_local, act_a, act_u, shared_act_a, shared_act_u, ws,
+                          stream=None):
     _check(_lib.moe_experts_backward_kept(ctypes.byref(p), slots, _ptr(x_slot), _ptr(offsets), _ptr(g_slot),
                                           _ptr(dy_slot), ctypes.byref(weights), _ptr(dx_slot), _ptr(dg_slot),
                                           ctypes.byref(grads), _ptr(x_local), _ptr(dy_local), _ptr(dx_local),
-                                          _ptr(act_a), _ptr(act_u), _ptr(ws), ws.numel() * ws.element_size(),
-                                          _stream(stream)), 'moe_experts_backward_kept')
+                                          _ptr(act_a), _ptr(act_u), _ptr(shared_act_a), _ptr(shared_act_u), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           'moe_experts_backward_kept')
 
 
 def quantize_mx(src_bf16, q, scales, stream=None):

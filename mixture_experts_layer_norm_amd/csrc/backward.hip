@@ -342,7 +342,8 @@ __global__ void single_group_kernel(int rows, int32_t* offs) {
 }
 
 static int shared_backward(const moe_problem* p, const void* x, const void* dy, const moe_weights* w,
-                           const moe_grads* dw, void* dx, char* wsb, const BwdLayout& L, hipStream_t s) {
+                           const moe_grads* dw, void* dx, char* wsb, const BwdLayout& L, hipStream_t s,
+                           const float* kept_a = nullptr, const float* kept_u = nullptr) {
   int32_t* o = (int32_t*)(wsb + L.offs_s);
   hipLaunchKernelGGL(single_group_kernel, dim3(1), dim3(1), 0, s, p->T, o);
   MOE_LAUNCH_CHECK();
@@ -356,10 +357,14 @@ static int shared_backward(const moe_problem* p, const void* x, const void* dy, 
   int st = launch_group_prefix(o, 1, p->T, o, (int32_t*)(wsb + L.tile_off_s), (int32_t*)(wsb + L.poff_s),
                                (int32_t*)(wsb + L.err), s, L.pad_s);
   if (st) return st;
+  CoreBufs cb = shared_bufs(wsb, L);
+  if (kept_a) {
+    cb.act_a = const_cast<float*>(kept_a);   // read only from here on
+    cb.act_u = const_cast<float*>(kept_u);
+  }
   return core_backward(1, p->T, p->D, p->I_shared, x, dy, nullptr, o, (int32_t*)(wsb + L.tile_off_s),
                        (int32_t*)(wsb + L.poff_s), w->ws_gate, w->ws_up, w->ws_down, dx, nullptr, dw->dws_gate,
-                       dw->dws_up, dw->dws_down, shared_bufs(wsb, L), s,
-                       (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0);
+                       dw->dws_up, dw->dws_down, cb, s, (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0, !kept_a);
 }
 
 }  // namespace moe
@@ -420,13 +425,17 @@ __global__ __launch_bounds__(256) void swiglu_rows_mx_kernel(const float* __rest
 
 static int experts_forward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                                 const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
-                                float* act_a, float* act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                float* act_a, float* act_u, float* sact_a, float* sact_u, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
   const bool keep = act_a || act_u;
   if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (!sact_a != !sact_u || (sact_a && !keep)) return MOE_ERR_INVALID_ARG;
   if (keep && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (p->I_shared == 0) sact_a = sact_u = nullptr;
   if (keep && (!al16(act_a) || !al16(act_u) || p->I % 4)) return MOE_ERR_MISALIGNED;
+  if (sact_a && (!al16(sact_a) || !al16(sact_u) || p->I_shared % 4)) return MOE_ERR_MISALIGNED;
   const bool mx = p->dtype == MOE_MXFP8;
   // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
   auto gemm = p->dtype == MOE_F32 ? launch_gemm_f32 : launch_gemm_bf16;
@@ -510,7 +519,18 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
     GemmArgs s1;
     s1.A = x_local; s1.lda = p->D; s1.B = w->ws_gate; s1.B2 = w->ws_up; s1.ldb = p->D; s1.N = p->I_shared;
     s1.K = p->D; s1.C = wsb + L.sh_h; s1.ldc = p->I_shared;
-    if ((st = gemm(s1, gs, EPI_SWIGLU, stream))) return st;
+    if (sact_a) {
+      // the shared expert's a, u to the caller as well, h from them (BF16 even under MXFP8)
+      s1.C = sact_a; s1.C2 = sact_u;
+      if ((st = launch_gemm_bf16(s1, gs, EPI_SAVE_AU, stream))) return st;
+      const int64_t n4 = (int64_t)p->T * p->I_shared / 4;
+      const unsigned nb = (unsigned)std::min<int64_t>((n4 + 255) / 256, 16384);
+      hipLaunchKernelGGL(swiglu_rows_kernel, dim3(nb), dim3(256), 0, stream, sact_a, sact_u, n4,
+                         (uint16_t*)(wsb + L.sh_h));
+      MOE_LAUNCH_CHECK();
+    } else if ((st = gemm(s1, gs, EPI_SWIGLU, stream))) {
+      return st;
+    }
     GemmArgs s2;
     s2.A = wsb + L.sh_h; s2.lda = p->I_shared; s2.B = w->ws_down; s2.ldb = p->I_shared; s2.N = p->D;
     s2.K = p->I_shared; s2.C = shared_out; s2.ldc = p->D;
@@ -522,13 +542,15 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
 static int experts_backward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                                  const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
                                  float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
-                                 void* dx_local, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+                                 void* dx_local, const float* act_a, const float* act_u, const float* sact_a,
+                                 const float* sact_u, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
   const bool kept = act_a || act_u;
   if (kept && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (!sact_a != !sact_u || (sact_a && !kept)) return MOE_ERR_INVALID_ARG;
   if (kept && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (p->I_shared == 0) sact_a = sact_u = nullptr;
   const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!x_slot || !offsets || !g_slot || !dy_slot || !w || !dx_slot || !dg_slot || !dw) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
@@ -571,7 +593,7 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
                             !kept)))
       return st;
   }
-  if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream);
+  if (p->I_shared > 0) return shared_backward(p, x_local, dy_local, w, dw, dx_local, wsb, L, stream, sact_a, sact_u);
   return MOE_OK;
 }
 
@@ -582,16 +604,17 @@ extern "C" {
 int moe_experts_forward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                         const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
                         void* ws, size_t ws_bytes, hipStream_t stream) {
-  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, nullptr, nullptr, ws,
-                              ws_bytes, stream);
+  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, nullptr, nullptr, nullptr,
+                              nullptr, ws, ws_bytes, stream);
 }
 
 int moe_experts_forward_keep(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                              const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
-                             float* act_a, float* act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
+                             float* act_a, float* act_u, float* shared_act_a, float* shared_act_u, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
-  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, act_a, act_u, ws,
-                              ws_bytes, stream);
+  return experts_forward_impl(p, slots, x_slot, offsets, w, y_slot, x_local, shared_out, act_a, act_u, shared_act_a,
+                              shared_act_u, ws, ws_bytes, stream);
 }
 
 int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
@@ -599,17 +622,17 @@ int moe_experts_backward(const moe_problem* p, int64_t slots, const void* x_slot
                          float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
                          void* dx_local, void* ws, size_t ws_bytes, hipStream_t stream) {
   return experts_backward_impl(p, slots, x_slot, offsets, g_slot, dy_slot, w, dx_slot, dg_slot, dw, x_local,
-                               dy_local, dx_local, nullptr, nullptr, ws, ws_bytes, stream);
+                               dy_local, dx_local, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 int moe_experts_backward_kept(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                               const float* g_slot, const void* dy_slot, const moe_weights* w, void* dx_slot,
                               float* dg_slot, const moe_grads* dw, const void* x_local, const void* dy_local,
-                              void* dx_local, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
+                              void* dx_local, const float* act_a, const float* act_u, const float* shared_act_a,
+                              const float* shared_act_u, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
   return experts_backward_impl(p, slots, x_slot, offsets, g_slot, dy_slot, w, dx_slot, dg_slot, dw, x_local,
-                               dy_local, dx_local, act_a, act_u, ws, ws_bytes, stream);
+                               dy_local, dx_local, act_a, act_u, shared_act_a, shared_act_u, ws, ws_bytes, stream);
 }
 
 int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits, const moe_weights* w,

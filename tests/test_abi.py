@@ -133,9 +133,12 @@ def test_keep_activation_entry_points_reject_without_gpu():
     lib = m._lib
     W, G = m.Weights(), m.Grads()
     fake = 1 << 20   # never dereferenced: every call below returns before touching memory
-    for dt, acts, code in (('bf16', (fake, None), -1), ('mxfp8', (None, fake), -1), ('f32', (fake, fake), -2)):
+    cases = (('bf16', (fake, None, None, None), -1), ('mxfp8', (None, fake, None, None), -1),
+             ('bf16', (fake, fake, fake, None), -1), ('f32', (fake, fake, None, None), -2))
+    for dt, acts, code in cases:
         p = m.problem(100, 256, 256, 3, 5, 128, dt)
         assert lib.moe_experts_forward_keep(ctypes.byref(p), 0, fake, fake, ctypes.byref(W), fake, fake, fake,
-                                            *acts, fake, 1 << 40, None) == code, dt
+                                            *acts, fake, 1 << 40, None) == code, (dt, acts)
         assert lib.moe_experts_backward_kept(ctypes.byref(p), 0, fake, fake, fake, fake, ctypes.byref(W), fake, fake,
-                                             ctypes.byref(G), fake, fake, fake, *acts, fake, 1 << 40, None) == code, dt
+                                             ctypes.byref(G), fake, fake, fake, *acts, fake, 1 << 40,
+                                             None) == code, (dt, acts)

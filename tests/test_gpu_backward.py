@@ -35,7 +35,7 @@ SMALL_SHARE = synth.EPShareConfig('small_share_bf16_T100_K5_D256_I256_E3', token
                                   I_shared=128, zipf_s=1.2, seed=41)
 
 
-def run_share(m, H, counts, flags=0, keep=False):
+def run_share(m, H, counts, flags=0, keep=False, keep_shared=True):
     cfg = H.cfg
     S = int(sum(counts))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -54,6 +54,7 @@ def run_share(m, H, counts, flags=0, keep=False):
     E, I, D, Is = cfg.E_local, cfg.I, cfg.D, cfg.I_shared
     if keep:
         act = [torch.full((S, I), float('nan'), device='cuda') for _ in range(2)]
+        act += [torch.full((cfg.tokens, Is), float('nan'), device='cuda') if keep_shared else None for _ in range(2)]
         m.experts_forward_keep(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, *act, ws)
     else:
         m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
@@ -93,13 +94,15 @@ def test_experts_forward_backward_long_groups(m, counts, lo_mx):
     check_share(m, LONG_SHARE, counts, m.MOE_FLAG_BWD_WGRAD_LO_MXFP8 if lo_mx else 0)
 
 
+@pytest.mark.parametrize('keep_shared', [True, False], ids=['shared_kept', 'shared_replayed'])
 @pytest.mark.parametrize('flags', [0, 0x40], ids=['default', 'one_pass'])
 @pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242], [0, 0, 500]], ids=['empty_mid', 'ragged', 'one_hot'])
-def test_experts_keep_activations_bitwise(m, counts, flags):
+def test_experts_keep_activations_bitwise(m, counts, flags, keep_shared):
     """moe_experts_forward_keep + moe_experts_backward_kept: a, u handed from the forward to the
-    backward instead of replayed; every output bitwise that of the replaying pair."""
+    backward instead of replayed (routed, and the shared expert's too or not); every output
+    bitwise that of the replaying pair."""
     H = synth.host_share(SMALL_SHARE)
-    a = run_share(m, H, counts, flags, keep=True)
+    a = run_share(m, H, counts, flags, keep=True, keep_shared=keep_shared)
     b = run_share(m, H, counts, flags)
     assert a['err'] == 0
     for k in ('y', 'sh', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_gate', 'dws_up', 'dws_down', 'dx_local'):

@@ -51,6 +51,7 @@ def run_share_mx(m, H, q, counts, dev_w=None, flags=0, keep=False):
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
     if keep:
         act = [torch.full((S, I), float('nan'), device='cuda') for _ in range(2)]
+        act += [torch.full((cfg.tokens, Is), float('nan'), device='cuda') for _ in range(2)]
         m.experts_forward_keep(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, *act, ws)
     else:
         m.experts_forward(p, S, dev['x_slot'], off_d, W, y, dev['x_local'], sh, ws)
