@@ -260,6 +260,8 @@ def main():
                  'ep_share_fwd_bwd_dgrad_one_pass': bench_share(max(5, args.steps // 5), 2, args.flags | 0x40),
                  'ep_share_fwd_bwd_one_pass_lo_mxfp8': bench_share(max(5, args.steps // 5), 2,
                                                                   args.flags | 0x40 | 0x80),
+                 'ep_share_fwd_bwd_keep_one_pass_lo_mxfp8': bench_share(max(5, args.steps // 5), 2,
+                                                                       args.flags | 0x40 | 0x80, keep=True),
                  'ep_share_fwd_bwd_mxfp8': bench_share(max(5, args.steps // 5), 2, args.flags, 'mxfp8'),
                  'ep_share_fwd_bwd_mxfp8_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
                                                                         'mxfp8', keep=True),
