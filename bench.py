@@ -109,6 +109,8 @@ def main():
                     help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
     ap.add_argument('--flags', type=int, default=0)
+    ap.add_argument('--keep-activations', action='store_true',
+                    help='ep_share workloads: hand a, u from the forward to the backward instead of replaying')
     ap.add_argument('--no-cpu-baseline', action='store_true')
     ap.add_argument('--cpu-tokens', type=int, default=160, help='tokens in the CPU oracle sample')
     ap.add_argument('--calib-copy', action='store_true',
@@ -125,7 +127,7 @@ def main():
 
     if args.workload in ('ep_share', 'ep_share_mxfp8'):
         dt = 'mxfp8' if args.workload == 'ep_share_mxfp8' else 'bf16'
-        print(json.dumps(bench_share(args.steps, args.warmup, args.flags, dt)), flush=True)
+        print(json.dumps(bench_share(args.steps, args.warmup, args.flags, dt, keep=args.keep_activations)), flush=True)
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)

@@ -252,12 +252,10 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
                             const float* kept_a = nullptr, const float* kept_u = nullptr) {
   int st;
   auto B = [&](size_t off) { return (uint8_t*)(ws + off); };
-  // a, u: the forward's (kept) or replayed into the workspace
-  auto F = [&](size_t off) {
-    if (kept_a && off == L.act_a) return const_cast<float*>(kept_a);
-    if (kept_a && off == L.act_u) return const_cast<float*>(kept_u);
-    return (float*)(ws + off);
-  };
+  auto F = [&](size_t off) { return (float*)(ws + off); };
+  // a, u: the forward's (kept, read only) or replayed into the workspace
+  float* act_a = kept_a ? const_cast<float*>(kept_a) : F(L.act_a);
+  float* act_u = kept_a ? const_cast<float*>(kept_u) : F(L.act_u);
   const int64_t S = L.Spad, ID = (int64_t)I * D;
   // weights re-quantised along the backward contraction axis
   if ((st = launch_mx_requant_t((const uint8_t*)w->w_down, w->sc_down, G, D, I, B(L.mq_wdT), B(L.ms_wdT), D, 0, ID, ID / 32, s))) return st;
@@ -282,7 +280,7 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   if (!kept_a) {
     GemmArgs r;   // replay
     r.A = B(L.mq_x); r.lda = D; r.B = w->w_gate; r.B2 = w->w_up; r.ldb = D; r.b_group_stride = ID;
-    r.N = I; r.K = D; r.C = F(L.act_a); r.C2 = F(L.act_u); r.ldc = I;
+    r.N = I; r.K = D; r.C = act_a; r.C2 = act_u; r.ldc = I;
     if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s))) return st;
   }
   GemmArgs d;   // dgrad-down
@@ -291,7 +289,7 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   if ((st = launch_gemm_mx(d, B(L.ms_dy), B(L.ms_wdT), nullptr, ID / 32, nullptr, grp, EPI_STORE, s))) return st;
   // SwiGLU backward: [da | du] quantised along I (dgrad-up), h and [da | du] along the slots
   // (weight gradients), dg from per-tile partial sums
-  if ((st = launch_mx_swiglu_bwd_t(F(L.act_a), F(L.act_u), F(L.m_dhp), g_rows, I, offs, poff, G, S, B(L.mq_dau),
+  if ((st = launch_mx_swiglu_bwd_t(act_a, act_u, F(L.m_dhp), g_rows, I, offs, poff, G, S, B(L.mq_dau),
                                    B(L.ms_dau), B(L.mq_hT), B(L.ms_hT), B(L.mq_dauT), B(L.ms_dauT), S, F(L.part), s)))
     return st;
   if ((st = launch_row_sum(F(L.part), n_cap, (I + 255) / 256, dg_rows, s))) return st;
