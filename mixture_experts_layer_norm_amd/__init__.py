@@ -45,7 +45,7 @@ DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
 EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_schedule', 'moe_dispatch',
             'moe_dispatch_tokens',
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
-            'moe_experts_forward_keep', 'moe_experts_backward_kept',
+            'moe_experts_forward_keep', 'moe_experts_backward_kept', 'moe_forward_keep', 'moe_backward_kept',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
             'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
@@ -94,6 +94,10 @@ _sig = {
                                    _P, _sz, _P]),
     'moe_backward': (ctypes.c_int, [_PP, _P, _P, _P, ctypes.POINTER(Weights), ctypes.POINTER(Routing), _P,
                                     ctypes.POINTER(Grads), _P, _P, _P, _sz, _P]),
+    'moe_forward_keep': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P, _P,
+                                        _P, _P, _P, _sz, _P]),
+    'moe_backward_kept': (ctypes.c_int, [_PP, _P, _P, _P, ctypes.POINTER(Weights), ctypes.POINTER(Routing), _P,
+                                         ctypes.POINTER(Grads), _P, _P, _P, _P, _P, _sz, _P]),
     'moe_experts_forward': (ctypes.c_int, [_PP, _i64, _P, _P, ctypes.POINTER(Weights), _P, _P, _P, _P, _sz, _P]),
     'moe_experts_backward': (ctypes.c_int, [_PP, _i64, _P, _P, _P, _P, ctypes.POINTER(Weights), _P, _P,
                                             ctypes.POINTER(Grads), _P, _P, _P, _P, _sz, _P]),
@@ -218,6 +222,21 @@ def backward(p, dout, x, logits, weights: Weights, routing: Routing, dx, grads: 
     _check(_lib.moe_backward(ctypes.byref(p), _ptr(dout), _ptr(x), _ptr(logits), ctypes.byref(weights),
                              ctypes.byref(routing), _ptr(dx), ctypes.byref(grads), _ptr(d_topk_w), _ptr(d_logits),
                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), 'moe_backward')
+
+
+def forward_keep(p, x, logits, weights: Weights, out, routing: Routing, act_a, act_u, ws, y_routes=None,
+                 shared_out=None, stream=None):
+    _check(_lib.moe_forward_keep(ctypes.byref(p), _ptr(x), _ptr(logits), ctypes.byref(weights), _ptr(out),
+                                 ctypes.byref(routing), _ptr(y_routes), _ptr(shared_out), _ptr(act_a), _ptr(act_u),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), 'moe_forward_keep')
+
+
+def backward_kept(p, dout, x, logits, weights: Weights, routing: Routing, dx, grads: Grads, d_topk_w, d_logits,
+                  act_a, act_u, ws, stream=None):
+    _check(_lib.moe_backward_kept(ctypes.byref(p), _ptr(dout), _ptr(x), _ptr(logits), ctypes.byref(weights),
+                                  ctypes.byref(routing), _ptr(dx), ctypes.byref(grads), _ptr(d_topk_w),
+                                  _ptr(d_logits), _ptr(act_a), _ptr(act_u), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), 'moe_backward_kept')
 
 
 def experts_forward(p, slots, x_slot, offsets, weights: Weights, y_slot, x_local, shared_out, ws, stream=None):

@@ -337,9 +337,14 @@ struct Join {
 // routed path; without one (moe_forward_stages) everything is in order on `stream`.
 static int forward_impl(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                         void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
-                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, SideStream* side) {
+                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, SideStream* side,
+                        float* act_a = nullptr, float* act_u = nullptr) {
   int st = validate_routing(p);
   if (st) return st;
+  const bool keep = act_a || act_u;
+  if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (keep && (p->dtype != MOE_BF16 || p->chunk_rows > 0)) return MOE_ERR_UNSUPPORTED;
+  if (keep && (!aligned16(act_a) || !aligned16(act_u))) return MOE_ERR_MISALIGNED;
   if (!x || !logits || !w || !out || !r) return MOE_ERR_INVALID_ARG;
   if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
@@ -485,10 +490,24 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       gather = nullptr;
     }
     MOE_MARK(MOE_STAGE_UP_GATE);
-    st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
-                    (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
-                    ev ? ev[MOE_STAGE_DOWN] : nullptr);
-    if (st) return st;
+    if (keep) {
+      // a, u to the caller in fp32 (the backward's replay GEMM, in slot order), h from them, then down
+      GemmArgs g1;
+      g1.A = A; g1.lda = p->D; g1.a_gather = gather; g1.a_div = p->K;
+      g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D; g1.b_group_stride = (int64_t)p->I * p->D;
+      g1.N = p->I; g1.K = p->D; g1.C = act_a; g1.C2 = act_u; g1.ldc = p->I;
+      if ((st = launch_gemm_bf16(g1, gr, EPI_SAVE_AU, stream))) return st;
+      if ((st = launch_swiglu_rows(act_a, act_u, n * p->I / 4, (uint16_t*)(wsb + L.h), stream))) return st;
+      GemmArgs g2;
+      g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
+      g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D; g2.c_scatter = r->perm;
+      if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream))) return st;
+    } else {
+      st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
+                      (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
+                      ev ? ev[MOE_STAGE_DOWN] : nullptr);
+      if (st) return st;
+    }
   }
   MOE_MARK(MOE_STAGE_COMBINE);
   if ((st = join.wait())) return st;
@@ -509,6 +528,16 @@ int moe_forward(const moe_problem* p, const void* x, const float* logits, const 
   const bool want_side = p && ((p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED)) || p->chunk_rows > 0);
   SideStream* side = want_side ? side_stream() : nullptr;
   return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side);
+}
+
+int moe_forward_keep(const moe_problem* p, const void* x, const float* logits, const moe_weights* w, void* out,
+                     const moe_routing* r, void* y_routes, void* shared_out, float* act_a, float* act_u, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
+  const bool want_side = p && p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED);
+  SideStream* side = want_side ? side_stream() : nullptr;
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side, act_a,
+                      act_u);
 }
 
 int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,

@@ -395,6 +395,14 @@ __global__ __launch_bounds__(256) void swiglu_rows_kernel(const float* __restric
   }
 }
 
+int launch_swiglu_rows(const float* a, const float* u, int64_t n4, uint16_t* h, hipStream_t s) {
+  if (n4 <= 0) return MOE_OK;
+  const unsigned nb = (unsigned)std::min<int64_t>((n4 + 255) / 256, 16384);
+  hipLaunchKernelGGL(swiglu_rows_kernel, dim3(nb), dim3(256), 0, s, a, u, n4, h);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 // The same from the kept a, u under MXFP8: h = SiLU(a) u in fp32, quantised along I in blocks of
 // 32 (E4M3 codes, E8M0 scales) exactly as the MXFP8 SwiGLU GEMM epilogue does. One thread per
 // block; blocks are row-major over [rows][I / 32].
@@ -633,11 +641,15 @@ int moe_experts_backward_kept(const moe_problem* p, int64_t slots, const void* x
                                dy_local, dx_local, act_a, act_u, shared_act_a, shared_act_u, ws, ws_bytes, stream);
 }
 
-int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits, const moe_weights* w,
-                 const moe_routing* r, void* dx, const moe_grads* dw, float* d_topk_w, float* d_logits, void* ws,
-                 size_t ws_bytes, hipStream_t stream) {
+static int backward_impl(const moe_problem* p, const void* dout, const void* x, const float* logits,
+                         const moe_weights* w, const moe_routing* r, void* dx, const moe_grads* dw, float* d_topk_w,
+                         float* d_logits, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   int st = validate_routing(p);
   if (st) return st;
+  const bool kept = act_a || act_u;
+  if (kept && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
+  if (kept && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   (void)logits;   // the routing state of the forward carries everything the backward needs
   const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!dout || !x || !w || !r || !dx || !dw || !d_topk_w) return MOE_ERR_INVALID_ARG;
@@ -672,12 +684,17 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
                                (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
                                (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream)))
       return st;
-  } else if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
-                                 (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up,
-                                 w->w_down, wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up,
-                                 dw->dw_down, routed_bufs(wsb, L), stream,
-                          (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0))) {
-    return st;
+  } else {
+    CoreBufs cb = routed_bufs(wsb, L);
+    if (kept) {
+      cb.act_a = const_cast<float*>(act_a);   // read only from here on
+      cb.act_u = const_cast<float*>(act_u);
+    }
+    if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+                            (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down,
+                            wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, cb,
+                            stream, (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0, !kept)))
+      return st;
   }
   if ((st = launch_router_backward((float*)(wsb + L.dg_slot), r->inv_perm, r->topk_idx, r->topk_w, p->T, p->E, p->K,
                                    d_topk_w, d_logits, stream)))
@@ -692,6 +709,20 @@ int moe_backward(const moe_problem* p, const void* dout, const void* x, const fl
     return launch_reverse_dispatch_f32((const float*)(wsb + L.dx_slot), r->inv_perm, (const float*)dsh, (float*)dx,
                                        p->T, p->K, p->D, stream);
   return launch_reverse_dispatch(wsb + L.dx_slot, r->inv_perm, dsh, dx, p->T, p->K, p->D, stream);
+}
+
+int moe_backward(const moe_problem* p, const void* dout, const void* x, const float* logits, const moe_weights* w,
+                 const moe_routing* r, void* dx, const moe_grads* dw, float* d_topk_w, float* d_logits, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  return backward_impl(p, dout, x, logits, w, r, dx, dw, d_topk_w, d_logits, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int moe_backward_kept(const moe_problem* p, const void* dout, const void* x, const float* logits,
+                      const moe_weights* w, const moe_routing* r, void* dx, const moe_grads* dw, float* d_topk_w,
+                      float* d_logits, const float* act_a, const float* act_u, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
+  return backward_impl(p, dout, x, logits, w, r, dx, dw, d_topk_w, d_logits, act_a, act_u, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -189,6 +189,8 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
 // K-grouped MXFP8 weight gradients: A [M][lda] and B [N][ldb] E4M3 along K with scales
 // [M][lda / 32], [N][ldb / 32]; group g contracts k in [k_off[g], k_off[g+1]) (multiples of 128);
 // fp32 output as launch_gemm_bf16_kgroup.
+// h [n4 * 4] bf16 = SiLU(a) u from fp32 a, u, with the SwiGLU GEMM epilogue's arithmetic.
+int launch_swiglu_rows(const float* a, const float* u, int64_t n4, uint16_t* h, hipStream_t s);
 int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 

@@ -395,3 +395,39 @@ def test_experts_backward_dgrad_one_pass(m, counts):
     base = run_share(m, H, counts)
     for k in ('dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_down'):
         assert torch.equal(r[k], base[k]), k
+
+
+@pytest.mark.parametrize('flags', [0, 0x1, 0x40], ids=['dispatched', 'fused_gather', 'one_pass'])
+def test_layer_keep_activations_bitwise(m, flags):
+    """moe_forward_keep + moe_backward_kept: the routed a, u handed from the layer forward to the
+    layer backward instead of replayed; every output bitwise that of moe_forward + moe_backward."""
+    cfg = LAYER_BWD
+    print(f'[backward] layer keep {cfg.name} flags={flags:#x}', flush=True)
+    H = synth.host_layer(cfg)
+    L = synth.to_device(H)
+    E, I, D, Is, T, K = cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.T, cfg.K
+    dout = bf(synth.host_dout(cfg, T))
+    res = []
+    for keep in (False, True):
+        run = ForwardRun(m, L, flags=flags, want_parts=False)
+        act = [torch.full((T * K, I), float('nan'), device='cuda') for _ in range(2)]
+        if keep:
+            m.forward_keep(run.p, L.x, L.logits, run.weights, run.out, run.routing, *act, run.ws)
+        else:
+            run()
+        gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+                  dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+                  dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+        G = m.make_grads(**gr)
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+        dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+        dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+        wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+        if keep:
+            m.backward_kept(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, *act, wsb)
+        else:
+            m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, wsb)
+        torch.cuda.synchronize()
+        res.append(dict(out=run.out.clone(), perm=run.perm.clone(), dx=dx, dtw=dtw, dlg=dlg, **gr))
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k
