@@ -67,3 +67,51 @@ def test_forward_and_backward_graph_replay_bitwise(m):
         for name, a, b in zip(['out', 'topk_idx', 'perm', 'dx', 'd_topk_w', 'd_logits'] + list(gr), outs(), ref):
             assert torch.equal(a, b), f'replay {rep}: {name} differs from the eager result'
     del g
+
+
+def test_keep_activations_graph_replay_bitwise(m):
+    """moe_forward_keep + moe_backward_kept captured into one graph: replays bitwise equal to the
+    eager run, the kept a, u buffers poisoned before every replay."""
+    print(f'[graph] keep {CFG.name}', flush=True)
+    H = synth.host_layer(CFG)
+    L = synth.to_device(H)
+    run = ForwardRun(m, L, want_parts=False)
+    E, I, D, Is, T, K = CFG.E, CFG.I, CFG.D, CFG.I_shared, CFG.T, CFG.K
+    dout = torch.from_numpy(np.ascontiguousarray(synth.host_dout(CFG, T), dtype=np.float32)).cuda().to(torch.bfloat16)
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    G = m.make_grads(**gr)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    act = [torch.empty((T * K, I), device='cuda') for _ in range(2)]
+    wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+
+    def step():
+        m.forward_keep(run.p, L.x, L.logits, run.weights, run.out, run.routing, *act, run.ws)
+        m.backward_kept(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, *act, wsb)
+
+    outs = lambda: [run.out, dx, dtw, dlg] + act + list(gr.values())
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs():
+            t.fill_(float('nan'))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs(), ref)):
+            assert torch.equal(a, b), f'replay {rep}: output {i} differs from the eager result'
+    del g
