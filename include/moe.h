@@ -291,15 +291,16 @@ int moe_backward(const moe_problem *p, const void *dout, const void *x, const fl
  * in the schedule's slot order, with the backward replay's own GEMM; h is formed from them with
  * the fused epilogue's arithmetic, so every output is bitwise that of moe_forward. The pages'
  * replay (sparsenotes page "Mixture-of-Kittens: MoE Megakernel for NVL72s", "The production
- * details") recomputes a, u; on one GPU 2 T K I 4 bytes of HBM buy that GEMM back. MOE_BF16 with
- * chunk_rows == 0 only (otherwise MOE_ERR_UNSUPPORTED); null act_a or act_u: MOE_ERR_INVALID_ARG. */
+ * details") recomputes a, u; on one GPU 2 T K I 4 bytes of HBM buy that GEMM back. MOE_BF16 and
+ * MOE_MXFP8 (a, u of the block-scaled GEMM; h quantised along I from them as the epilogue does)
+ * with chunk_rows == 0 (otherwise MOE_ERR_UNSUPPORTED); null act_a or act_u: MOE_ERR_INVALID_ARG. */
 int moe_forward_keep(const moe_problem *p, const void *x, const float *logits, const moe_weights *w,
                      void *out, const moe_routing *routing, void *y_routes, void *shared_out,
                      float *act_a, float *act_u, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_backward reading the routed a, u that moe_forward_keep wrote for the same x, routing and
  * weights instead of replaying them; every output bitwise that of moe_backward. The shared expert
- * replays its own. MOE_BF16 only. */
+ * replays its own. MOE_BF16 and MOE_MXFP8. */
 int moe_backward_kept(const moe_problem *p, const void *dout, const void *x, const float *logits,
                       const moe_weights *w, const moe_routing *routing, void *dx, const moe_grads *dw,
                       float *d_topk_w, float *d_logits, const float *act_a, const float *act_u,

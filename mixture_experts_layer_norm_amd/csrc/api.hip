@@ -343,7 +343,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   if (st) return st;
   const bool keep = act_a || act_u;
   if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
-  if (keep && (p->dtype != MOE_BF16 || p->chunk_rows > 0)) return MOE_ERR_UNSUPPORTED;
+  if (keep && (p->dtype == MOE_F32 || p->chunk_rows > 0)) return MOE_ERR_UNSUPPORTED;
   if (keep && (!aligned16(act_a) || !aligned16(act_u))) return MOE_ERR_MISALIGNED;
   if (!x || !logits || !w || !out || !r) return MOE_ERR_INVALID_ARG;
   if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm) return MOE_ERR_INVALID_ARG;
@@ -472,7 +472,15 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     GemmArgs g1;
     g1.A = xq; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
     g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hq; g1.ldc = p->I;
-    st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream);
+    if (keep) {
+      // a, u to the caller in fp32 (the backward's replay GEMM), h quantised from them
+      g1.C = act_a; g1.C2 = act_u;
+      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), nullptr, gr, EPI_SAVE_AU, stream);
+      if (st) return st;
+      st = launch_swiglu_rows_mx(act_a, act_u, n * (p->I / 32), hq, hs, stream);
+    } else {
+      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream);
+    }
     if (st) return st;
     MOE_MARK(MOE_STAGE_DOWN);
     GemmArgs g2;

@@ -429,6 +429,14 @@ __global__ __launch_bounds__(256) void swiglu_rows_mx_kernel(const float* __rest
   }
 }
 
+int launch_swiglu_rows_mx(const float* a, const float* u, int64_t nblk, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  if (nblk <= 0) return MOE_OK;
+  const unsigned nb = (unsigned)std::min<int64_t>((nblk + 255) / 256, 16384);
+  hipLaunchKernelGGL(swiglu_rows_mx_kernel, dim3(nb), dim3(256), 0, s, a, u, nblk, q, sc);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
+}
+
 static int experts_forward_impl(const moe_problem* p, int64_t slots, const void* x_slot, const int32_t* offsets,
                                 const moe_weights* w, void* y_slot, const void* x_local, void* shared_out,
                                 float* act_a, float* act_u, float* sact_a, float* sact_u, void* ws,
@@ -649,7 +657,7 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
   if (st) return st;
   const bool kept = act_a || act_u;
   if (kept && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
-  if (kept && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (kept && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   (void)logits;   // the routing state of the forward carries everything the backward needs
   const bool mx = p->dtype == MOE_MXFP8, f32 = p->dtype == MOE_F32;
   if (!dout || !x || !w || !r || !dx || !dw || !d_topk_w) return MOE_ERR_INVALID_ARG;
@@ -682,7 +690,8 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
   } else if (mx) {
     if ((st = core_backward_mx(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
                                (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
-                               (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream)))
+                               (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream,
+                               act_a, act_u)))
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);

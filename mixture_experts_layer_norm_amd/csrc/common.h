@@ -191,6 +191,9 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
 // fp32 output as launch_gemm_bf16_kgroup.
 // h [n4 * 4] bf16 = SiLU(a) u from fp32 a, u, with the SwiGLU GEMM epilogue's arithmetic.
 int launch_swiglu_rows(const float* a, const float* u, int64_t n4, uint16_t* h, hipStream_t s);
+// The same under MXFP8: nblk blocks of 32 along I -> E4M3 codes q and E8M0 scales sc, as the
+// MXFP8 SwiGLU GEMM epilogue quantises h.
+int launch_swiglu_rows_mx(const float* a, const float* u, int64_t nblk, uint8_t* q, uint8_t* sc, hipStream_t s);
 int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 

@@ -56,7 +56,8 @@ def mx_layer(cfg):
     return H, q
 
 
-def run_mx_forward(m, H, q):
+def run_mx_forward(m, H, q, act=None):
+    """moe_forward in MXFP8; with act = [a, u] buffers, moe_forward_keep."""
     cfg = H.cfg
     T, K, D, E = cfg.T, cfg.K, cfg.D, cfg.E
     p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8')
@@ -71,7 +72,10 @@ def run_mx_forward(m, H, q):
     out = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
     yr = torch.empty((T * K, D), dtype=torch.bfloat16, device='cuda')
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
-    m.forward(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, y_routes=yr)
+    if act is None:
+        m.forward(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, y_routes=yr)
+    else:
+        m.forward_keep(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), *act, ws, y_routes=yr)
     torch.cuda.synchronize()
     return out, yr, rt, p, tensors
 
