@@ -439,3 +439,47 @@ def experts_backward_mx_w(x_slot, counts, g, dy_slot, Wg, Wu, Wd, quantize=True,
     if return_parts:
         res['parts'] = parts
     return res
+
+
+def moe_forward_mx(x, logits, w_gate, w_up, w_down, K, ws_gate=None, ws_up=None, ws_down=None, quantize=True,
+                   return_h=False):
+    """The whole layer with the routed experts in MXFP8 (Notes, "The production details": activation
+    quantisation fused into dispatch, the grouped GEMMs and the gated activation; the shared expert
+    stays in BF16).
+
+    Routing and combine are those of moe_forward (Blog, MoE layer equation). Each routed slot carries
+    its token's row of x quantised along D (dispatch copies and quantises token rows, so a slot's
+    blocks are its token's); the gated activation h of a slot is quantised along I before the down
+    projection. w_gate, w_up [E, I, D] and w_down [E, D, I] are the dequantised MX weights (arrays,
+    or callables e -> array to stream them); the shared expert works on the unquantised x with its
+    own (BF16-valued) weights. quantize=False skips both activation round trips, which is moe_forward
+    on the same weights.
+
+    Returns (out [T, D], idx [T, K], g [T, K], y [T, K, D] per-route outputs, shared [T, D] or None);
+    with return_h also a dict e -> (t, k, H) of each expert's unquantised gated activation rows (the
+    values whose quantisation decisions the device takes in fp32)."""
+    x = np.asarray(x, dtype=np.float64)
+    T, D = x.shape
+    E = np.asarray(logits).shape[1]
+    idx = route_topk(logits, K)
+    g = routing_weights(logits, idx)
+    xq = mx_along(x, 1, quantize)
+    get = lambda w, e: w(e) if callable(w) else w[e]
+    y = np.zeros((T, K, D))
+    hs = {}
+    for e in range(E):
+        t, k = np.nonzero(idx == e)
+        if t.size == 0:
+            continue
+        Xe = xq[t]
+        H = silu(Xe @ np.asarray(get(w_gate, e), dtype=np.float64).T) * (Xe @ np.asarray(get(w_up, e), dtype=np.float64).T)
+        y[t, k] = mx_along(H, 1, quantize) @ np.asarray(get(w_down, e), dtype=np.float64).T
+        if return_h:
+            hs[e] = (t, k, H)
+    out = np.einsum('tk,tkd->td', g, y)
+    sh = None
+    if ws_gate is not None:
+        sh = swiglu_expert(x, ws_gate, ws_up, ws_down)
+        out = out + sh
+    res = (out, idx, g, y, sh)
+    return res + (hs,) if return_h else res

@@ -242,10 +242,13 @@ def test_ep_share_full_size_sampled(m):
     assert r['err'] == 0
     off = np.concatenate([[0], np.cumsum(D_.counts)])
     rng = np.random.default_rng(7)
-    # whole slots, 3 per expert
-    slots = np.concatenate([np.sort(rng.choice(np.arange(off[e], off[e + 1]), 3, replace=False))
+    # whole slots, 16 per expert: its first and last slot and 14 drawn at random
+    slots = np.concatenate([np.unique(np.concatenate([[off[e], off[e + 1] - 1],
+                                                      rng.choice(np.arange(off[e] + 1, off[e + 1] - 1), 14,
+                                                                 replace=False)]))
                             for e in range(cfg.E_local)])
-    cnt = np.full(cfg.E_local, 3)
+    cnt = np.full(cfg.E_local, 16)
+    assert slots.size == 16 * cfg.E_local
     idx = torch.from_numpy(slots).cuda()
     xs, dys, gs = h64(D_.x_slot[idx]), h64(D_.dy_slot[idx]), D_.g[idx].cpu().numpy().astype(np.float64)
     wg, wu, wd = h64(D_.w_gate), h64(D_.w_up), h64(D_.w_down)
@@ -255,12 +258,13 @@ def test_ep_share_full_size_sampled(m):
     ref = oracle.experts_backward(xs, cnt, gs, dys, wg, wu, wd)
     assert_close_rms(h64(r['dx_slot'][idx]), ref['dx_slot'], TAU, 'ep dx_slot sampled', True)
     assert_close_rms(r['dg'][idx].cpu().numpy(), ref['dg'], TAU, 'ep dg sampled')
-    # single units i of the largest and the smallest expert, over all their slots
-    for e in (0, cfg.E_local - 1):
+    # single units i of every expert, over all its slots: units at both edges of the first and
+    # last 128-column tile of h and four drawn at random
+    for e in range(cfg.E_local):
         a, b = int(off[e]), int(off[e + 1])
         X, DY = h64(D_.x_slot[a:b]), h64(D_.dy_slot[a:b])
         G = D_.g[a:b].cpu().numpy().astype(np.float64)
-        for i in rng.choice(cfg.I, 2, replace=False):
+        for i in np.concatenate([[0, 127, 128, cfg.I - 1], rng.choice(np.arange(129, cfg.I - 1), 4, replace=False)]):
             print(f'[ep_share] oracle on expert {e} unit {i} ({b - a} slots)', flush=True)
             ru = oracle.experts_backward(X, np.array([b - a]), G, DY, wg[e:e + 1, i:i + 1], wu[e:e + 1, i:i + 1],
                                          wd[e:e + 1, :, i:i + 1])

@@ -145,31 +145,44 @@ def test_combine_standalone(m, dtype, shared, K, D):
 @pytest.mark.slow
 def test_forward_dsv3_full_size_sampled(m):
     """DeepSeek-V3 shape (T=8192, D=7168, I=2048, E=256, K=8, shared I=2048) in the launch
-    configuration the benchmark times; 8 sampled tokens checked against the oracle, routing
-    checked in full."""
+    configuration the benchmark times. Routing and schedule checked in full; against the oracle:
+    the layer output of 256 sampled tokens, and the per-route expert outputs y of two whole
+    experts, the hottest one (its rows span several m-tiles, the last one partial) and the
+    smallest non-empty one."""
     cfg = synth.DSV3
     print('[forward] dsv3 full size: generating inputs', flush=True)
     L = synth.device_layer(cfg)
-    run = ForwardRun(m, L, want_parts=False)()
+    run = ForwardRun(m, L, want_parts=True)()
     torch.cuda.synchronize()
     lg = L.logits.cpu().numpy()
     idx = oracle.route_topk(lg, cfg.K)
     assert np.array_equal(run.topk_idx.cpu().numpy(), idx)
     counts, offsets, perm, inv = oracle.schedule(idx, cfg.E)
     assert np.array_equal(run.perm.cpu().numpy(), perm)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(cfg.T, 8, replace=False))
-    xs = L.x[toks].float().cpu().numpy()
-    # only the experts the sampled tokens use are fetched
-    used = set(idx[toks].ravel().tolist())
-    wg = {e: L.w_gate[e].float().cpu().numpy() for e in used}
-    wu = {e: L.w_up[e].float().cpu().numpy() for e in used}
-    wd = {e: L.w_down[e].float().cpu().numpy() for e in used}
-    print(f'[forward] dsv3 oracle on {len(toks)} tokens, {len(used)} experts', flush=True)
-    out, *_ = oracle.moe_forward(xs, lg[toks], lambda e: wg[e], lambda e: wu[e], lambda e: wd[e], cfg.K,
-                                 L.ws_gate.float().cpu().numpy(), L.ws_up.float().cpu().numpy(),
-                                 L.ws_down.float().cpu().numpy())
-    got = run.out[toks].float().cpu().numpy()
+    cache = {}
+
+    def weights(e):
+        if e not in cache:
+            cache.clear()       # one expert at a time: the oracle visits experts in order
+            cache[e] = tuple(w[e].float().cpu().numpy() for w in (L.w_gate, L.w_up, L.w_down))
+        return cache[e]
+
+    # whole experts: every route of the hottest and of the smallest non-empty expert
+    nz = np.nonzero(counts)[0]
+    for e in (int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])):
+        routes = perm[offsets[e]:offsets[e + 1]]
+        print(f'[forward] dsv3 y_routes of expert {e} ({routes.size} routes)', flush=True)
+        xs = L.x[torch.from_numpy(routes // cfg.K).cuda()].float().cpu().numpy()
+        ref = oracle.swiglu_expert(xs, *weights(e))
+        got = run.y_routes[torch.from_numpy(routes).cuda()].float().cpu().numpy()
+        assert_close_rms(got, ref, TOL['bf16'], f'dsv3 y_routes expert {e}', True)
+    toks = np.sort(np.random.default_rng(0).choice(cfg.T, 256, replace=False))
+    xs = L.x[torch.from_numpy(toks).cuda()].float().cpu().numpy()
+    print(f'[forward] dsv3 oracle on {len(toks)} tokens, {len(set(idx[toks].ravel().tolist()))} experts', flush=True)
+    out, *_ = oracle.moe_forward(xs, lg[toks], lambda e: weights(e)[0], lambda e: weights(e)[1],
+                                 lambda e: weights(e)[2], cfg.K, L.ws_gate.float().cpu().numpy(),
+                                 L.ws_up.float().cpu().numpy(), L.ws_down.float().cpu().numpy())
+    got = run.out[torch.from_numpy(toks).cuda()].float().cpu().numpy()
     assert_close_rms(got, out, TOL['bf16'], 'dsv3 sampled out', True)
 
 
