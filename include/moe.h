@@ -63,15 +63,19 @@ typedef enum moe_dtype {
  * backward) also need K <= min(E, 64) (the expert-level entry points use K only as slots per
  * token). BF16/MXFP8 need D % 128 == 0 and
  * I % 128 == 0 (I_shared likewise); MOE_F32 needs D % 4 == 0.
- * chunk_rows (b): rows of the expert-contiguous routed buffer that one pipeline step carries
- *   through the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel for
- *   NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
+ * chunk_rows (b): rows of the expert-contiguous routed buffer that one chunk carries through
+ *   dispatch and the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel
+ *   for NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
  *   values are rounded up to a multiple of 256 and clamped to [max(256, T*K/1024), T*K]. With
- *   chunks, dispatched rows and h live in a ring of ring_stages chunk stages (BF16 path; the
- *   MXFP8 and FUSED_GATHER paths ignore chunk_rows).
+ *   chunks, the dispatched rows and h live in a ring of ring_stages chunk stages (BF16 and
+ *   MXFP8). moe_forward / moe_forward_stages return MOE_ERR_UNSUPPORTED for chunk_rows > 0 under
+ *   MOE_F32 or MOE_FLAG_FUSED_GATHER (no dispatched copies to hold), as do moe_forward_keep and
+ *   the expert-level forwards (their slots are not dispatched through a ring). The backward entry
+ *   points do not chunk: they accept the forward's problem descriptor and ignore chunk_rows and
+ *   ring_stages.
  * ring_stages: macrobatch ring depth (Notes, section "A ring buffer instead of a host
  *   round-trip"); 0 selects 3. Ignored when one chunk holds every row.
- * flags: bitwise OR of MOE_FLAG_* below. */
+ * flags: bitwise OR of MOE_FLAG_* below; any other bit is MOE_ERR_INVALID_ARG. */
 typedef struct moe_problem {
   int32_t T, D, I, E, K, I_shared;
   int32_t dtype;
@@ -82,23 +86,8 @@ typedef struct moe_problem {
 
 /* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
 #define MOE_FLAG_FUSED_GATHER 0x1
-/* Tuning: order the GEMM tiles of each expert n-tile major (all m-tiles that share a weight tile
- * run together) instead of the default (pairs of m-tiles, n-tile major inside a pair, which lets
- * both the weight and the activation tiles be reused from the L2). Results are bitwise identical. */
-#define MOE_FLAG_WEIGHT_MAJOR 0x2
-/* Tile order of the GEMMs: inside each expert, blocks of n n-tiles (1..255), each block m-tile
- * major (n = 1 is MOE_FLAG_WEIGHT_MAJOR; n >= the n-tile count is plain m-tile major). Affects
- * only speed, never the results. */
-/* Tuning: run the bf16 grouped GEMMs with 4 wavefronts per workgroup, each owning a 128 x 128
- * block of the 256 x 256 tile, instead of 8 wavefronts of 128 x 64. Results are bitwise equal. */
-#define MOE_FLAG_GEMM_WAVES4 0x8
-/* moe_forward only: run the shared expert on a library-owned side stream (default priority, one
- * per host thread and device, created on first use) concurrently with the routed path, joined
- * before the combine. Results are bitwise equal to the in-order forward. */
-#define MOE_FLAG_OVERLAP_SHARED 0x10
-/* Tuning: forward bf16 GEMMs with K slices 32 wide in 4 LDS stages instead of the default 64
- * wide in 2. Results are bitwise equal. */
-#define MOE_FLAG_GEMM_BK32 0x20
+/* Bits 0x2, 0x8, 0x10, 0x20 and 0xff00 are reserved (they selected tuning variants that measured
+ * no faster and were removed); a problem that sets one is rejected. */
 /* moe_backward / moe_experts_backward under MOE_BF16: contract dgrad-up (dx = [da | du] [W_gate |
  * W_up]) over the bf16 da, du in one K pass instead of over their hi + lo halves in two. Each dx
  * element sums 2I products whose roundings are independent; measured max |d| of dx reaches
@@ -115,7 +104,6 @@ typedef struct moe_problem {
  * moe_backward_workspace_size grows by the quantised operands, (3 I + 2 D) * 33/32 bytes per
  * padded slot (routed) and (3 I_shared + 2 D) * 33/32 per padded token (shared), where taken. */
 #define MOE_FLAG_BWD_WGRAD_LO_MXFP8 0x80
-#define MOE_FLAG_TILE_BLOCK(n) (((uint32_t)(n) & 0xffu) << 8)
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
 #define MOE_FLAG_PERSISTENT 0x4
@@ -162,6 +150,12 @@ int moe_workspace_size(const moe_problem *p, size_t *bytes);
 /* Bytes of device workspace that moe_backward and moe_experts_backward need for `p` (the
  * expert-level backward takes p->T * p->K as its slot capacity). Same conventions as above. */
 int moe_backward_workspace_size(const moe_problem *p, size_t *bytes);
+
+/* Bytes of device workspace that moe_backward_kept and moe_experts_backward_kept need for `p`:
+ * the above less the 2 * T * K * I * 4 bytes the replay of the routed a, u would fill (the caller
+ * holds them). The replaying backwards refuse a workspace of only this size (MOE_ERR_WORKSPACE).
+ * MOE_F32: MOE_ERR_UNSUPPORTED (no kept path). */
+int moe_backward_kept_workspace_size(const moe_problem *p, size_t *bytes);
 
 /* Top-K selection and router weights (Blog, "Overlapping computation and communication in
  * MoE": the router picks the top-k routed experts and weights them with g_i = s_i / sum s_j).
@@ -300,7 +294,9 @@ int moe_forward_keep(const moe_problem *p, const void *x, const float *logits, c
 
 /* moe_backward reading the routed a, u that moe_forward_keep wrote for the same x, routing and
  * weights instead of replaying them; every output bitwise that of moe_backward. The shared expert
- * replays its own. MOE_BF16 and MOE_MXFP8. */
+ * replays its own. MOE_BF16 and MOE_MXFP8 (MOE_F32: MOE_ERR_UNSUPPORTED); act_a, act_u non-null
+ * (MOE_ERR_INVALID_ARG) and 16-byte aligned (MOE_ERR_MISALIGNED). `ws` holds
+ * moe_backward_kept_workspace_size bytes. */
 int moe_backward_kept(const moe_problem *p, const void *dout, const void *x, const float *logits,
                       const moe_weights *w, const moe_routing *routing, void *dx, const moe_grads *dw,
                       float *d_topk_w, float *d_logits, const float *act_a, const float *act_u,
@@ -366,7 +362,8 @@ int moe_experts_forward_keep(const moe_problem *p, int64_t slots, const void *x_
  * x_slot, offsets and weights, instead of replaying them; every output is bitwise that of
  * moe_experts_backward. The shared expert reads shared_act_a, shared_act_u when given (both
  * or neither), and replays its own otherwise. MOE_BF16 and MOE_MXFP8 (the buffers of
- * moe_experts_forward_keep under the same dtype). */
+ * moe_experts_forward_keep under the same dtype); act buffers 16-byte aligned with I % 4 == 0
+ * (MOE_ERR_MISALIGNED). `ws` holds moe_backward_kept_workspace_size bytes. */
 int moe_experts_backward_kept(const moe_problem *p, int64_t slots, const void *x_slot,
                               const int32_t *offsets, const float *g_slot, const void *dy_slot,
                               const moe_weights *w, void *dx_slot, float *dg_slot, const moe_grads *dw,

@@ -26,18 +26,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_FLAG_FUSED_GATHER = 0x1
-MOE_FLAG_WEIGHT_MAJOR = 0x2
 MOE_FLAG_PERSISTENT = 0x4
-MOE_FLAG_GEMM_WAVES4 = 0x8
-MOE_FLAG_OVERLAP_SHARED = 0x10
-MOE_FLAG_GEMM_BK32 = 0x20
 MOE_FLAG_BWD_DGRAD_ONE_PASS = 0x40
 MOE_FLAG_BWD_WGRAD_LO_MXFP8 = 0x80
-
-
-def MOE_FLAG_TILE_BLOCK(n):
-    """Grouped GEMM tile order: blocks of n n-tiles per expert (speed only)."""
-    return (int(n) & 0xff) << 8
 STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3: 'MOE_ERR_WORKSPACE',
           -4: 'MOE_ERR_MISALIGNED', -5: 'MOE_ERR_HIP'}
 DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
@@ -47,7 +38,8 @@ EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_sc
             'moe_combine', 'moe_forward', 'moe_backward', 'moe_experts_forward', 'moe_experts_backward',
             'moe_experts_forward_keep', 'moe_experts_backward_kept', 'moe_forward_keep', 'moe_backward_kept',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
-            'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size')
+            'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size',
+            'moe_backward_kept_workspace_size')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -85,6 +77,7 @@ _sig = {
     'moe_status_string': (ctypes.c_char_p, [ctypes.c_int]),
     'moe_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
     'moe_backward_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
+    'moe_backward_kept_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
     'moe_route_topk': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_schedule': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_dispatch': (ctypes.c_int, [_PP, _P, _P, _i64, _i64, _P, _P, _P]),
@@ -155,6 +148,12 @@ def workspace_size(p: Problem) -> int:
 def backward_workspace_size(p: Problem) -> int:
     n = _sz(0)
     _check(_lib.moe_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)), 'moe_backward_workspace_size')
+    return n.value
+
+
+def backward_kept_workspace_size(p: Problem) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.moe_backward_kept_workspace_size(ctypes.byref(p), ctypes.byref(n)), 'moe_backward_kept_workspace_size')
     return n.value
 
 

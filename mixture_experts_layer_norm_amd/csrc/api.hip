@@ -4,16 +4,16 @@
 
 #include <algorithm>
 
-#include <vector>
-
 #include "common.h"
-#include "pipeline.h"
 
 namespace moe {
 
 size_t elt_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static constexpr uint32_t kKnownFlags = MOE_FLAG_FUSED_GATHER | MOE_FLAG_PERSISTENT | MOE_FLAG_BWD_DGRAD_ONE_PASS |
+                                        MOE_FLAG_BWD_WGRAD_LO_MXFP8;
 
 // Extra checks of the entry points that route tokens (top-k over the E experts).
 int validate_routing(const moe_problem* p) {
@@ -29,6 +29,7 @@ int validate_problem(const moe_problem* p) {
   if (p->T < 1 || p->D < 1 || p->I < 1 || p->E < 1 || p->K < 1 || p->I_shared < 0) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
   if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
+  if ((uint32_t)p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
   if (p->E > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_F32) {
@@ -49,8 +50,8 @@ WsLayout ws_layout(const moe_problem& p) {
   L.stages = 1;
   L.chunks = 1;
   L.ring_rows = n;
-  L.pipelined = p.chunk_rows > 0 && p.dtype == MOE_BF16 && !(p.flags & MOE_FLAG_FUSED_GATHER);
-  if (L.pipelined) {
+  L.chunked = p.chunk_rows > 0 && (p.dtype == MOE_BF16 || p.dtype == MOE_MXFP8);
+  if (L.chunked) {
     // b: multiple of 256 rows, at least n/1024 (at most 1024 chunks), at most n rounded up
     const int64_t nr = (n + 255) / 256 * 256;
     int64_t b = ((int64_t)p.chunk_rows + 255) / 256 * 256;
@@ -76,22 +77,14 @@ WsLayout ws_layout(const moe_problem& p) {
   L.y_routes = o; o = align256(o + (size_t)n * p.D * act);
   L.sh_h = o; o = align256(o + (size_t)p.T * p.I_shared * act);
   L.sh_out = o; o = align256(o + (p.I_shared > 0 ? (size_t)p.T * p.D * act : 0));
-  L.pipe_ctile = o; o = align256(o + (L.pipelined ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
-  L.pipe_base = o; o = align256(o + (L.pipelined ? (size_t)(L.chunks + 1) * 4 : 0));
-  L.pipe_ctr = o; o = align256(o + (L.pipelined ? (size_t)(2 + 3 * L.chunks) * 4 : 0));
-  L.pipe_crow = o; o = align256(o + (L.pipelined ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
+  L.chunk_tiles = o; o = align256(o + (L.chunked ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
+  L.chunk_rowoff = o; o = align256(o + (L.chunked ? (size_t)L.chunks * (p.E + 1) * 4 : 0));
   L.bwd = o;
   L.total = o;
   return L;
 }
 
 static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
-
-int tile_block_of(uint32_t flags) {
-  if (flags & MOE_FLAG_WEIGHT_MAJOR) return 1;
-  const int nb = (int)((flags >> 8) & 0xff);
-  return nb ? nb : kDefaultTileBlock;
-}
 
 }  // namespace moe
 
@@ -278,67 +271,11 @@ static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda,
 
 }  // extern "C"
 
-namespace {
-// A library-owned side stream (default priority) per host thread and device, with the two events
-// of a fork/join: moe_forward runs the shared expert on it while the routed path runs on the
-// caller's stream. Created on first use; kept for the life of the process.
-// It also carries the dispatch stream of the chunked ring and a pool of events, grown once and
-// reused by every later call: disp[c] marks chunk c dispatched, ug[c] its up/gate done.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  hipStream_t ds = nullptr;                 // dispatch stream of the chunked ring
-  hipEvent_t ring_fork = nullptr;
-  std::vector<hipEvent_t> disp, ug;
-  bool ensure_ring(int C) {
-    if (!ds && hipStreamCreateWithFlags(&ds, hipStreamNonBlocking) != hipSuccess) { ds = nullptr; return false; }
-    if (!ring_fork && hipEventCreateWithFlags(&ring_fork, hipEventDisableTiming) != hipSuccess) { ring_fork = nullptr; return false; }
-    while ((int)disp.size() < C) {
-      hipEvent_t a = nullptr, b = nullptr;
-      if (hipEventCreateWithFlags(&a, hipEventDisableTiming) != hipSuccess) return false;
-      if (hipEventCreateWithFlags(&b, hipEventDisableTiming) != hipSuccess) { hipEventDestroy(a); return false; }
-      disp.push_back(a);
-      ug.push_back(b);
-    }
-    return true;
-  }
-};
-constexpr int kMaxDevices = 64;
-thread_local SideStream t_side[kMaxDevices];
-
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = t_side[dev];
-  if (!ss.s) {
-    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) { ss.s = nullptr; return nullptr; }
-    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-  }
-  return &ss;
-}
-
-// Makes `main` wait for the side stream's work on every exit once armed (also error returns).
-struct Join {
-  hipStream_t main = nullptr;
-  hipEvent_t ev = nullptr;
-  ~Join() { wait(); }
-  int wait() {
-    if (!ev) return MOE_OK;
-    hipEvent_t e = ev;
-    ev = nullptr;
-    return hipStreamWaitEvent(main, e, 0) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-  }
-};
-}  // namespace
-
-// The forward. With a side stream (moe_forward) the shared expert runs concurrently with the
-// routed path; without one (moe_forward_stages) everything is in order on `stream`.
+// The forward, in order on `stream`. `ev` (moe_forward_stages) marks the stage boundaries.
 static int forward_impl(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                         void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
-                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, SideStream* side,
-                        float* act_a = nullptr, float* act_u = nullptr) {
+                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, float* act_a = nullptr,
+                        float* act_u = nullptr) {
   int st = validate_routing(p);
   if (st) return st;
   const bool keep = act_a || act_u;
@@ -352,6 +289,8 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   const bool mx = p->dtype == MOE_MXFP8;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
+  // the chunked ring holds dispatched copies; with the gather fused into GEMM1 there are none
+  if (p->chunk_rows > 0 && ((p->flags & MOE_FLAG_FUSED_GATHER) || p->dtype == MOE_F32)) return MOE_ERR_UNSUPPORTED;
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (y_routes && !aligned16(y_routes)) ||
@@ -373,27 +312,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
 
   // shared expert first: it does not depend on the schedule
   MOE_MARK(MOE_STAGE_SHARED);
-  Join join;
   if (p->I_shared > 0) {
     Grouped gs;
     gs.M = p->T;
-    gs.nblk = tile_block_of(p->flags);
-    gs.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
-    gs.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
-    hipStream_t shs = stream;
-    const bool overlap = side && (p->flags & MOE_FLAG_OVERLAP_SHARED);
-    if (overlap) {
-      if (hipEventRecord(side->fork, stream) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
-        return MOE_ERR_HIP;
-      shs = side->s;
-    }
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
-                    0, 0, wsb + L.sh_h, sho, nullptr, shs);
-    if (overlap) {
-      if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_ERR_HIP;
-      join.main = stream;
-      join.ev = side->join;
-    }
+                    0, 0, wsb + L.sh_h, sho, nullptr, stream);
     if (st) return st;
   }
 
@@ -402,57 +325,58 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   gr.tile_off = (const int32_t*)(wsb + L.tile_off);
   gr.groups = p->E;
   gr.max_mtiles = (n + kGemmBM - 1) / kGemmBM + p->E;
-  gr.nblk = tile_block_of(p->flags);
-  gr.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
-  gr.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
-  if (L.pipelined) {
+  if (L.chunked) {
     // Chunks of b routed slots through a ring of S stages, each carried through dispatch, up/gate
-    // and down before the next; all tile bookkeeping is on the device (no host synchronisation).
+    // and down before the next (the Notes' "Granularity as a tunable" and "A ring buffer instead
+    // of a host round-trip"); all tile bookkeeping is on the device (no host synchronisation).
+    // Slot j of chunk c lives in ring row (c % S) b + (j - c b): each chunk's operands are
+    // addressed through a base pointer displaced by (c % S) b - c b rows, so the kernels index
+    // them by slot as in the unchunked path and every output tile is the same workgroup sum.
     const int64_t b = L.chunk;
     const int C = L.chunks, S = L.stages;
-    int32_t* ctile = (int32_t*)(wsb + L.pipe_ctile);
-    int32_t* crow = (int32_t*)(wsb + L.pipe_crow);
+    int32_t* ctile = (int32_t*)(wsb + L.chunk_tiles);
+    int32_t* crow = (int32_t*)(wsb + L.chunk_rowoff);
     st = launch_chunk_tables(r->offsets, p->E, (int)n, (int)b, C, ctile, crow, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_DISPATCH);
-    uint16_t* xr = (uint16_t*)(wsb + L.x_slot);
-    uint16_t* hr = (uint16_t*)(wsb + L.h);
-    // With the library's streams (moe_forward) dispatch runs ahead on its own stream: chunk c is
-    // dispatched once chunk c - S's up/gate has read ring stage c % S (event ug[c - S]), and the
-    // compute stream starts chunk c once it is dispatched (event disp[c]). Without them
-    // (moe_forward_stages) everything stays in order on `stream`.
-    const bool ahead = side && side->ensure_ring(C);
-    hipStream_t dstream = ahead ? side->ds : stream;
-    if (ahead && (hipEventRecord(side->ring_fork, stream) != hipSuccess ||
-                  hipStreamWaitEvent(side->ds, side->ring_fork, 0) != hipSuccess))
-      return MOE_ERR_HIP;
+    const int64_t xrow = mx ? p->D : (int64_t)p->D * 2, hrow = mx ? p->I : (int64_t)p->I * 2;   // bytes per row
+    uint8_t* xr = (uint8_t*)(wsb + L.x_slot);
+    uint8_t* hr = (uint8_t*)(wsb + L.h);
+    uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
+    uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
     for (int c = 0; c < C; ++c) {
       const int64_t c0 = c * b, rows = (n - c0) < b ? (n - c0) : b;
-      const int64_t shift = (int64_t)(c % S) * b - c0;            // slot index -> ring row
-      if (ahead && c >= S && hipStreamWaitEvent(dstream, side->ug[c - S], 0) != hipSuccess) return MOE_ERR_HIP;
-      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + (int64_t)(c % S) * b * p->D, nullptr,
-                           dstream);
+      const int64_t stage = (int64_t)(c % S) * b, shift = stage - c0;   // slot index -> ring row
+      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + stage * xrow,
+                           mx ? xs + stage * (p->D / 32) : nullptr, stream);
       if (st) return st;
-      if (ahead && (hipEventRecord(side->disp[c], dstream) != hipSuccess ||
-                    hipStreamWaitEvent(stream, side->disp[c], 0) != hipSuccess))
-        return MOE_ERR_HIP;
       Grouped gc;
       gc.row_off = crow + (int64_t)c * (p->E + 1);
       gc.tile_off = ctile + (int64_t)c * (p->E + 1);
       gc.groups = p->E;
       gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
-      gc.nblk = tile_block_of(p->flags);
-      gc.waves4 = (p->flags & MOE_FLAG_GEMM_WAVES4) ? 1 : 0;
-      gc.bk32 = (p->flags & MOE_FLAG_GEMM_BK32) ? 1 : 0;
-      st = expert_ffn(p->dtype, gc, xr + shift * p->D, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
-                      p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * p->I, yr, r->perm, stream,
-                      ahead ? side->ug[c] : nullptr);
+      if (mx) {
+        GemmArgs g1;
+        g1.A = xr + shift * xrow; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
+        g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hr + shift * hrow; g1.ldc = p->I;
+        st = launch_gemm_mx(g1, xs + shift * (p->D / 32), w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32),
+                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, stream);
+        if (st) return st;
+        GemmArgs g2;
+        g2.A = hr + shift * hrow; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I;
+        g2.b_group_stride = (int64_t)p->D * p->I; g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D;
+        g2.c_scatter = r->perm;
+        st = launch_gemm_mx(g2, hs + shift * (p->I / 32), w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr,
+                            gc, EPI_STORE, stream);
+      } else {
+        st = expert_ffn(p->dtype, gc, xr + shift * xrow, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
+                        p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, stream);
+      }
       if (st) return st;
     }
     MOE_MARK(MOE_STAGE_UP_GATE);
     MOE_MARK(MOE_STAGE_DOWN);
     MOE_MARK(MOE_STAGE_COMBINE);
-    if ((st = join.wait())) return st;
     st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_COUNT);
@@ -518,7 +442,6 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     }
   }
   MOE_MARK(MOE_STAGE_COMBINE);
-  if ((st = join.wait())) return st;
   st = launch_combine(yr, sho, r->topk_w, out, p->T, p->K, p->D, p->dtype, stream);
   if (st) return st;
   MOE_MARK(MOE_STAGE_COUNT);
@@ -531,27 +454,20 @@ extern "C" {
 int moe_forward(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                 void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                 size_t ws_bytes, hipStream_t stream) {
-  // the library's side streams: the shared expert's (MOE_FLAG_OVERLAP_SHARED) and the chunked
-  // ring's dispatch stream (chunk_rows > 0)
-  const bool want_side = p && ((p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED)) || p->chunk_rows > 0);
-  SideStream* side = want_side ? side_stream() : nullptr;
-  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side);
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream);
 }
 
 int moe_forward_keep(const moe_problem* p, const void* x, const float* logits, const moe_weights* w, void* out,
                      const moe_routing* r, void* y_routes, void* shared_out, float* act_a, float* act_u, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
   if (!act_a || !act_u) return MOE_ERR_INVALID_ARG;
-  const bool want_side = p && p->I_shared > 0 && (p->flags & MOE_FLAG_OVERLAP_SHARED);
-  SideStream* side = want_side ? side_stream() : nullptr;
-  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, side, act_a,
-                      act_u);
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, act_a, act_u);
 }
 
 int moe_forward_stages(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                        void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
-  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, ev, stream, nullptr);
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, ev, stream);
 }
 
 }  // extern "C"

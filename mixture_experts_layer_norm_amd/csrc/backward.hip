@@ -3,8 +3,9 @@
 // Backward of E(x) = W_down (SiLU(a) (*) u), a = W_gate x, u = W_up x, for slot rows weighted by
 // g (each slot enters the layer output as g * E(x)), following the sparsenotes page
 // "Mixture-of-Kittens: MoE Megakernel for NVL72s":
-//   * "A ring buffer instead of a host round-trip": forward activations are not kept; a and u
-//     are recomputed (replayed) from the slot rows;
+//   * "A ring buffer instead of a host round-trip": a and u are recomputed (replayed) from the
+//     slot rows, unless the caller hands in the forward's kept fp32 a, u (the *_kept entry points,
+//     filled by the *_keep forwards), which skips the replay GEMM;
 //   * "The production details": the router-weight gradient dg = <h, dh'> with dh' = W_down^T dy,
 //     so the down-projection output is never recomputed;
 //   * "Pull dispatch, push combine": the backward reverse-combine gathers the output gradient
@@ -56,8 +57,9 @@ static bool wgrad_lo_mx(const moe_problem& p, int64_t rows, int64_t groups) {
   return (p.flags & MOE_FLAG_BWD_WGRAD_LO_MXFP8) && rows >= 4096 * groups;
 }
 
-// Workspace of the backward for up to n = T*K slot rows (bf16).
-static BwdLayout bwd_layout(const moe_problem& p) {
+// Workspace of the backward for up to n = T*K slot rows (bf16). kept: the caller hands in the
+// routed a, u (the *_kept entry points), so no room is reserved for replaying them.
+static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
   BwdLayout L{};
   const int64_t n = (int64_t)p.T * p.K, T = p.T, D = p.D, I = p.I, E = p.E, Is = p.I_shared;
   L.n = n;
@@ -77,7 +79,8 @@ static BwdLayout bwd_layout(const moe_problem& p) {
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
   L.x_slot = take(n * D * eb); L.dy_slot = take(n * D * eb); L.dx_slot = take(n * D * eb);
   L.dx_sh = take(T * D * eb);
-  L.act_a = take(n * I * 4); L.act_u = take(n * I * 4);
+  // replayed a, u; left out when the caller keeps them (offsets then unused)
+  L.act_a = take(kept ? 0 : n * I * 4); L.act_u = take(kept ? 0 : n * I * 4);
   if (p.dtype == MOE_F32) {
     L.f_dh = take(n * I * 4); L.f_h = take(n * I * 4); L.f_da = take(n * I * 4); L.f_du = take(n * I * 4);
     if (Is > 0) {
@@ -379,6 +382,15 @@ int moe_backward_workspace_size(const moe_problem* p, size_t* bytes) {
   return MOE_OK;
 }
 
+int moe_backward_kept_workspace_size(const moe_problem* p, size_t* bytes) {
+  int st = validate_problem(p);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  if (p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(*p, true).total;
+  return MOE_OK;
+}
+
 }  // extern "C"
 
 namespace moe {
@@ -443,6 +455,9 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
                                 size_t ws_bytes, hipStream_t stream) {
   int st = validate_problem(p);
   if (st) return st;
+  // the slots arrive dispatched: nothing to carry through a ring (its layout would also be too
+  // small for all slots)
+  if (p->chunk_rows > 0) return MOE_ERR_UNSUPPORTED;
   const bool keep = act_a || act_u;
   if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
   if (!sact_a != !sact_u || (sact_a && !keep)) return MOE_ERR_INVALID_ARG;
@@ -573,11 +588,13 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
   if (p->I_shared > 0 && (!x_local || !dy_local || !dx_local || !w->ws_gate || !w->ws_up || !w->ws_down ||
                           !dw->dws_gate || !dw->dws_up || !dw->dws_down))
     return MOE_ERR_INVALID_ARG;
-  BwdLayout L = bwd_layout(*p);
+  BwdLayout L = bwd_layout(*p, kept);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!al16(x_slot) || !al16(dy_slot) || !al16(dx_slot) || !al16(ws) || (x_local && !al16(x_local)) ||
       (dy_local && !al16(dy_local)) || (dx_local && !al16(dx_local)))
     return MOE_ERR_MISALIGNED;
+  if (kept && (!al16(act_a) || !al16(act_u) || p->I % 4)) return MOE_ERR_MISALIGNED;
+  if (sact_a && (!al16(sact_a) || !al16(sact_u) || p->I_shared % 4)) return MOE_ERR_MISALIGNED;
   char* wsb = (char*)ws;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(offsets, p->E, (int)slots, offs, (int32_t*)(wsb + L.tile_off),
@@ -666,9 +683,10 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
   if (!w->w_gate || !w->w_up || !w->w_down || !dw->dw_gate || !dw->dw_up || !dw->dw_down) return MOE_ERR_INVALID_ARG;
   if (p->I_shared > 0 && (!w->ws_gate || !w->ws_up || !w->ws_down || !dw->dws_gate || !dw->dws_up || !dw->dws_down))
     return MOE_ERR_INVALID_ARG;
-  BwdLayout L = bwd_layout(*p);
+  BwdLayout L = bwd_layout(*p, kept);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!al16(dout) || !al16(x) || !al16(dx) || !al16(ws)) return MOE_ERR_MISALIGNED;
+  if (kept && (!al16(act_a) || !al16(act_u))) return MOE_ERR_MISALIGNED;
   char* wsb = (char*)ws;
   const int64_t n = L.n;
   // reverse-combine (pull dout into slots), replayed dispatch of x, slot weights

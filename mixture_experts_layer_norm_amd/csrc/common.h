@@ -40,7 +40,7 @@ constexpr int kErrOffset = 0;                // sticky error word (int32)
 
 struct WsLayout {
   size_t err;              // int32 error word
-  size_t ctrl;             // pipeline counters / flags
+  size_t ctrl;             // reserved control words
   size_t blk_hist;         // [nblk][E] int32
   size_t tile_off;         // [E+1] int32  m-tile prefix for kGemmBM
   size_t grp_clean;        // [E+1] int32  sanitised caller offsets (expert-level entry)
@@ -54,24 +54,18 @@ struct WsLayout {
   size_t sh_out;           // shared expert output [T][D]
   size_t bwd;              // backward scratch start
   size_t total;
-  size_t pipe_ctile;       // [C][E+1] int32 (chunked pipeline)
-  size_t pipe_base;        // [C+1] int32
-  size_t pipe_ctr;         // [2 + 3C] int32
-  size_t pipe_crow;        // [C][E+1] int32 (chunk row ranges, multi-launch path)
+  size_t chunk_tiles;      // [C][E+1] int32 m-tile prefix of each chunk over experts
+  size_t chunk_rowoff;     // [C][E+1] int32 experts' row ranges clamped to each chunk
   int64_t nblk;            // histogram blocks
   int64_t ring_rows;       // rows of x_slot / h held (chunk * stages, or T*K)
   int64_t chunk;           // rows per chunk
   int32_t stages;          // ring stages (1 when one chunk holds everything)
   int32_t chunks;          // C (1 when one chunk holds everything)
-  bool pipelined;          // chunked persistent pipeline in use
+  bool chunked;            // chunk_rows selects the chunked ring
 };
 
 size_t elt_bytes(int dtype);
 WsLayout ws_layout(const moe_problem& p);
-// n-tiles per block of the grouped tile order selected by moe_problem::flags (0: the default
-// order, pairs of m-tiles, n-tile major inside a pair)
-constexpr int kDefaultTileBlock = 0;
-int tile_block_of(uint32_t flags);
 
 int validate_problem(const moe_problem* p);
 int validate_routing(const moe_problem* p);
@@ -129,12 +123,6 @@ struct Grouped {
   int32_t groups = 1;
   int32_t M = 0;              // rows when row_off == nullptr
   int64_t max_mtiles = 0;     // host bound on the number of m-tiles (grid size)
-  // Tile order inside a group: blocks of nblk n-tiles, inside a block m-tile major (nblk >= the
-  // n-tile count: plain m-tile major, 1: n-tile major). 0 selects the default: pairs of m-tiles,
-  // n-tile major inside a pair.
-  int32_t nblk = 0;
-  int32_t waves4 = 0;         // bf16 GEMM workgroups of 4 wavefronts x (128 x 128) instead of 8 x (128 x 64)
-  int32_t bk32 = 0;           // bf16 GEMM K slices 32 wide in 4 LDS stages instead of 64 wide in 2
 };
 
 // EPI_SWIGLU:   h = SiLU(gate) * up                       -> C
@@ -180,8 +168,6 @@ struct GemmArgs {
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s);
 int gemm_tile_cols(Epi epi);
-struct PipeArgs;
-int launch_pipeline(const PipeArgs& host, int32_t* chunk_base_dev, int ncu, hipStream_t s);
 int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,
                         hipStream_t s);
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
@@ -189,12 +175,12 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
 // K-grouped MXFP8 weight gradients: A [M][lda] and B [N][ldb] E4M3 along K with scales
 // [M][lda / 32], [N][ldb / 32]; group g contracts k in [k_off[g], k_off[g+1]) (multiples of 128);
 // fp32 output as launch_gemm_bf16_kgroup.
+int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
 // h [n4 * 4] bf16 = SiLU(a) u from fp32 a, u, with the SwiGLU GEMM epilogue's arithmetic.
 int launch_swiglu_rows(const float* a, const float* u, int64_t n4, uint16_t* h, hipStream_t s);
 // The same under MXFP8: nblk blocks of 32 along I -> E4M3 codes q and E8M0 scales sc, as the
 // MXFP8 SwiGLU GEMM epilogue quantises h.
 int launch_swiglu_rows_mx(const float* a, const float* u, int64_t nblk, uint8_t* q, uint8_t* sc, hipStream_t s);
-int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
 int launch_gemm_f32(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
 
 }  // namespace moe

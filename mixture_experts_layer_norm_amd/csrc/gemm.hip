@@ -9,20 +9,21 @@
 // weights [N][K]), the layout MFMA fragments want.
 //
 // Tiling (bf16): 512 threads = 8 wavefronts in a 2 x 4 grid, workgroup tile 256 rows x 256 weight
-// rows, K step 64, LDS double-buffered (2 x 72 KB, rows padded by 16 B so that the fragment
-// reads of 32 rows hit distinct bank groups), fragments double-buffered in registers. Each
-// wavefront owns a 128 x 64 block of the product as 4 x 2 v_mfma_f32_32x32x16_bf16
-// accumulators (fp32). For SwiGLU the weight tile interleaves 32 gate rows and the 32 up rows of
+// rows, K slices 64 wide staged into LDS by LDS-direct loads (two 64 KB stages, the next slice
+// loading while the current one multiplies; 16-byte chunks XOR-swizzled within each row, see
+// gemm_tile.h). Each wavefront owns a 128 x 64 block of the product as 4 x 2
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32), reading its fragments straight from the
+// swizzled LDS rows. For SwiGLU the weight tile interleaves 32 gate rows and the 32 up rows of
 // the same h columns, so a lane holds the gate and up value of the same (row, column) in the same
 // accumulator slot and the epilogue needs no data exchange. 256-row m-tiles read each expert's
 // weights once for up to 256 routed rows; row blocks past an expert's last row skip their MFMAs.
 //
 // Workgroup -> tile mapping: tiles are numbered group by group (inside a group in pairs of
-// m-tiles, n-tile major inside a pair, see decode_grouped_tile) and dealt out so that each XCD (workgroups are
-// placed round-robin over the 8 XCDs) gets a contiguous range,
-// which keeps an expert's activation rows and weight tiles in that XCD's L2. The split is over
-// the tiles that exist (read on the device), not over the launched upper bound, so that every
-// XCD gets an equal share even when the routing leaves most of the bound empty.
+// m-tiles, n-tile major inside a pair, see decode_grouped_tile) and dealt out so that each XCD
+// (workgroups are placed round-robin over the 8 XCDs) gets a contiguous range, which keeps an
+// expert's activation rows and weight tiles in that XCD's L2. The split is over the tiles that
+// exist (read on the device), not over the launched upper bound, so that every XCD gets an
+// equal share even when the routing leaves most of the bound empty.
 #include "gemm_tile.h"
 
 namespace moe {
@@ -88,33 +89,12 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   const int mtn = g.row_off ? 0 : (int)mt;   // dense mode: the exact m-tile count
-  dim3 grid((unsigned)nb);
-  if (g.waves4) {
-    // 4 wavefronts (2 x 2), each a 128 x 128 block: 256 accumulators per lane, one wave per SIMD
-    dim3 block(256);
-    switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, 128, 2, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-    }
-  } else if (!g.bk32) {
-    // 64-wide K slices in 2 LDS stages (the default; measured faster than 32 x 4 here)
-    dim3 block(512);
-    switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
-    }
-  } else {
-    dim3 block(512);
-    switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 32>), grid, block, 0, s, a, g, ntn, mtn); break;
-    }
+  dim3 grid((unsigned)nb), block(512);
+  switch (epi) {
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
+    case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
   }
   MOE_LAUNCH_CHECK();
   return MOE_OK;

@@ -1,15 +1,13 @@
-// One workgroup tile of the grouped GEMMs (shared by the standalone kernels and the persistent
-// pipeline). See gemm.hip for the tiling.
+// One workgroup tile of the bf16 grouped GEMMs (and the operand staging the MXFP8 GEMM shares).
+// See gemm.hip for the tiling.
 //
 // Operand staging: global_load_lds_dwordx4 copies 16 bytes per lane from HBM straight into LDS
 // (no register staging, no LDS store instructions). One such instruction of a wavefront fills
-// 1 KB of LDS in lane order, i.e. 1024 / ROWB rows of one K slice. Two slice shapes (SliceCfg):
-// 32-wide slices (64 B rows) in 4 LDS stages, loads 3 slices ahead of the MFMAs, or 64-wide
-// slices (128 B rows) in 2 stages, loads 1 slice ahead; both 128 KB of LDS for the 256 A rows
-// and 256 B rows. Within a row the 16-byte chunks are stored XOR-swizzled (chunk c of row r at
-// position c ^ f(r)), with f chosen by measured LDS bank conflicts on gfx950 for this kernel's
-// fragment-read pattern: (r >> 2) & 3 for 64 B rows, (r >> 1) & 7 for 128 B rows (both read
-// conflict-free; e.g. ((r >> 1) ^ (r >> 3)) & 3 or no swizzle do not).
+// 1 KB of LDS in lane order, i.e. 8 rows of one 64-wide K slice (128 B rows). Two LDS stages of
+// 256 A rows and 256 B rows (128 KB); the next slice loads while the current one multiplies.
+// Within a row the 16-byte chunks are stored XOR-swizzled (chunk c of row r at position
+// c ^ ((r >> 1) & 7)), chosen by measured LDS bank conflicts on gfx950 for this kernel's
+// fragment-read pattern (it reads conflict-free; e.g. r & 7 or no swizzle do not).
 #pragma once
 #include "common.h"
 
@@ -21,22 +19,20 @@ constexpr int BM = kGemmBM;                 // 256 rows per m-tile (and 256 B ro
 // Shape of one staged K slice: BKE bf16 per row.
 template <int BKE>
 struct SliceCfg {
-  static_assert(BKE == 32 || BKE == 64, "32- or 64-wide K slices");
+  static_assert(BKE == 64, "64-wide K slices");
   static constexpr int BK = BKE;                      // K elements per slice
-  static constexpr int STAGES = BKE == 32 ? 4 : 2;    // LDS stages (loads run STAGES - 1 ahead)
+  static constexpr int STAGES = 2;                    // LDS stages (loads run one slice ahead)
   static constexpr int ROWB = BKE * 2;                // bytes per staged row
   static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;             // rows filled by one wavefront load
   static constexpr int KSTEPS = BKE / 16;             // MFMA K steps per slice
   static constexpr int STAGE_BYTES = 2 * BM * ROWB;   // A rows, then B rows
-  __device__ static __forceinline__ int swz(int row) { return BKE == 32 ? (row >> 2) & 3 : (row >> 1) & 7; }
+  __device__ static __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 };
-constexpr int BK = 32;                      // default slice width (K multiples the callers use)
 }  // namespace gemm_detail
 
-// LDS of one tile: 128 KB for either slice shape
-constexpr int kGemmSmemElems = 4 * gemm_detail::SliceCfg<32>::STAGE_BYTES / 2;
-static_assert(4 * gemm_detail::SliceCfg<32>::STAGE_BYTES == 2 * gemm_detail::SliceCfg<64>::STAGE_BYTES, "");
+// LDS of one tile: two 64 KB stages
+constexpr int kGemmSmemElems = 2 * gemm_detail::SliceCfg<64>::STAGE_BYTES / 2;
 
 struct TileCoord {
   int grp, r0, rows, nt;
@@ -97,12 +93,10 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ off, int g
 // m-tiles). The tiles of group grp occupy logical [tile_off[grp] * ntn, tile_off[grp + 1] * ntn).
 // Workgroups start in launch order as CUs free up, so on one XCD tiles d apart in that order
 // start about d / 32 of a tile's run time apart: only tiles a position or two apart still read a
-// K slice the other has just brought into the L2. Default order (g.nblk = 0): pairs of m-tiles,
-// n-tile major inside a pair, i.e. (m0,n0) (m1,n0) (m0,n1) (m1,n1) ... then (m2,n0) (m3,n0) ...
-// Both the weight tile (shared by the pair) and each activation tile (every second tile) are
-// reused from the L2, so an expert fetches about 9 operand tiles per m-tile instead of the
-// 17 of plain m-tile major order. g.nblk = n > 0: blocks of n n-tiles, m-tile major inside a
-// block (n >= ntn: plain m-tile major; n = 1: n-tile major over all the group's m-tiles).
+// K slice the other has just brought into the L2. Order: pairs of m-tiles, n-tile major inside a
+// pair, i.e. (m0,n0) (m1,n0) (m0,n1) (m1,n1) ... then (m2,n0) (m3,n0) ... Both the weight tile
+// (shared by the pair) and each activation tile (every second tile) are reused from the L2, so an
+// expert fetches about 9 operand tiles per m-tile instead of the 17 of plain m-tile major order.
 __device__ __forceinline__ bool decode_grouped_tile(const Grouped& g, int logical, int ntn, int mtn, TileCoord& tc) {
   int grp = 0, t0 = 0, nmt = mtn;
   if (g.row_off) {
@@ -111,22 +105,12 @@ __device__ __forceinline__ bool decode_grouped_tile(const Grouped& g, int logica
     nmt = g.tile_off[grp + 1] - t0;
   }
   const int rem = logical - t0 * ntn;
-  int mt;
   tc.grp = grp;
-  if (g.nblk > 0) {
-    const int nbw = min(g.nblk, ntn);
-    const int blk = rem / (nmt * nbw);
-    const int w = min(nbw, ntn - blk * nbw);
-    const int r2 = rem - blk * nmt * nbw;
-    tc.nt = blk * nbw + r2 % w;
-    mt = r2 / w;
-  } else {
-    const int pair = rem / (2 * ntn);
-    const int h = min(2, nmt - 2 * pair);
-    const int r2 = rem - pair * 2 * ntn;
-    tc.nt = r2 / h;
-    mt = 2 * pair + r2 % h;
-  }
+  const int pair = rem / (2 * ntn);
+  const int h = min(2, nmt - 2 * pair);
+  const int r2 = rem - pair * 2 * ntn;
+  tc.nt = r2 / h;
+  const int mt = 2 * pair + r2 % h;
   const int rbase = g.row_off ? g.row_off[grp] : 0;
   const int rend = g.row_off ? g.row_off[grp + 1] : g.M;
   const int per = g.row_off ? group_tile_rows(rend - rbase, nmt) : BM;

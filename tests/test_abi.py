@@ -142,3 +142,81 @@ def test_keep_activation_entry_points_reject_without_gpu():
         assert lib.moe_experts_backward_kept(ctypes.byref(p), 0, fake, fake, fake, fake, ctypes.byref(W), fake, fake,
                                              ctypes.byref(G), fake, fake, fake, *acts, fake, 1 << 40,
                                              None) == code, (dt, acts)
+
+
+def test_removed_flag_bits_and_chunk_refusals_without_gpu():
+    """Flag bits the library does not define are refused; chunk_rows is refused where no ring can
+    hold the rows (fp32, the gather fused into GEMM1, the expert-level forward, the keep forward)
+    instead of being ignored. Every call returns before any HIP call."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    n = ctypes.c_size_t()
+    for bit in (0x2, 0x8, 0x10, 0x20, 0x100, 0x8000, 0x10000):
+        p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, bit)
+        assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1, hex(bit)
+    fake = 1 << 20
+    w, r = m.Weights(), m.Routing()
+    for f in ('w_gate', 'w_up', 'w_down', 'sc_gate', 'sc_up', 'sc_down'):
+        setattr(w, f, fake)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, fake)
+    for dt, flags in (('bf16', m.MOE_FLAG_FUSED_GATHER), ('f32', 0)):
+        p = m.problem(64, 128, 128, 8, 2, 0, dt, 256, 3, flags)
+        assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
+                               1 << 40, None) == -2, (dt, flags)
+    for dt in ('bf16', 'mxfp8', 'f32'):
+        p = m.problem(64, 128, 128, 8, 2, 0, dt, 512, 3)
+        assert lib.moe_experts_forward(ctypes.byref(p), 64, fake, fake, ctypes.byref(w), fake, None, None, fake,
+                                       1 << 40, None) == -2, dt
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 512, 3)
+    assert lib.moe_forward_keep(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None,
+                                fake, fake, fake, 1 << 40, None) == -2
+
+
+def test_layer_keep_entry_points_reject_without_gpu():
+    """moe_forward_keep / moe_backward_kept: F32 unsupported, both buffers required, both 16-byte
+    aligned; checked on the host before any launch."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    fake = 1 << 20
+    w, r, g = m.Weights(), m.Routing(), m.Grads()
+    for f in ('w_gate', 'w_up', 'w_down', 'sc_gate', 'sc_up', 'sc_down'):
+        setattr(w, f, fake)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, fake)
+    for f in ('dw_gate', 'dw_up', 'dw_down'):
+        setattr(g, f, fake)
+    cases = (('bf16', (fake, None), -1), ('mxfp8', (None, fake), -1), ('f32', (fake, fake), -2),
+             ('bf16', (fake + 4, fake), -4), ('mxfp8', (fake, fake + 8), -4))
+    for dt, acts, code in cases:
+        p = m.problem(64, 128, 128, 8, 2, 0, dt)
+        assert lib.moe_forward_keep(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None,
+                                    *acts, fake, 1 << 40, None) == code, ('fwd', dt, acts)
+        assert lib.moe_backward_kept(ctypes.byref(p), fake, fake, fake, ctypes.byref(w), ctypes.byref(r), fake,
+                                     ctypes.byref(g), fake, None, *acts, fake, 1 << 40, None) == code, ('bwd', dt, acts)
+
+
+def test_kept_backward_workspace_is_smaller_and_refused_by_the_replay():
+    """moe_backward_kept_workspace_size leaves out the replayed a, u (2 T K I 4 bytes); the
+    replaying backwards refuse a workspace of only that size (MOE_ERR_WORKSPACE, before any launch)."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    fake = 1 << 20
+    w, r, g = m.Weights(), m.Routing(), m.Grads()
+    for f in ('w_gate', 'w_up', 'w_down', 'sc_gate', 'sc_up', 'sc_down'):
+        setattr(w, f, fake)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, fake)
+    for f in ('dw_gate', 'dw_up', 'dw_down'):
+        setattr(g, f, fake)
+    for dt in ('bf16', 'mxfp8'):
+        p = m.problem(300, 256, 384, 16, 4, 0, dt)
+        full, kept = m.backward_workspace_size(p), m.backward_kept_workspace_size(p)
+        assert 0 <= full - kept - 2 * 300 * 4 * 384 * 4 <= 512, (dt, full, kept)
+        assert lib.moe_backward(ctypes.byref(p), fake, fake, fake, ctypes.byref(w), ctypes.byref(r), fake,
+                                ctypes.byref(g), fake, None, fake, kept, None) == -3, dt
+        assert lib.moe_experts_backward(ctypes.byref(p), 1200, fake, fake, fake, fake, ctypes.byref(w), fake, fake,
+                                        ctypes.byref(g), None, None, None, fake, kept, None) == -3, dt
+    n = ctypes.c_size_t()
+    assert lib.moe_backward_kept_workspace_size(ctypes.byref(m.problem(300, 256, 384, 16, 4, 0, 'f32')),
+                                                ctypes.byref(n)) == -2

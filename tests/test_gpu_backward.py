@@ -65,7 +65,9 @@ def run_share(m, H, counts, flags=0, keep=False, keep_shared=True):
               dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
     G = m.make_grads(**gr)
     dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
-    wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+    # the kept backward runs in exactly the smaller workspace that leaves out the replay's a, u
+    wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(p),),
+                      dtype=torch.uint8, device='cuda')
     if keep:
         m.experts_backward_kept(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
                                 dev['dy_local'], dxl, *act, wsb)
@@ -426,7 +428,8 @@ def test_layer_keep_activations_bitwise(m, flags):
         dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
         dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
         dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
-        wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+        wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(run.p),),
+                          dtype=torch.uint8, device='cuda')
         if keep:
             m.backward_kept(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, *act, wsb)
         else:

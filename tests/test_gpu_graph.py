@@ -86,7 +86,7 @@ def test_keep_activations_graph_replay_bitwise(m):
     dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
     dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
     act = [torch.empty((T * K, I), device='cuda') for _ in range(2)]
-    wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+    wsb = torch.zeros((m.backward_kept_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
 
     def step():
         m.forward_keep(run.p, L.x, L.logits, run.weights, run.out, run.routing, *act, run.ws)

@@ -56,11 +56,11 @@ def mx_layer(cfg):
     return H, q
 
 
-def run_mx_forward(m, H, q, act=None):
+def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0):
     """moe_forward in MXFP8; with act = [a, u] buffers, moe_forward_keep."""
     cfg = H.cfg
     T, K, D, E = cfg.T, cfg.K, cfg.D, cfg.E
-    p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8')
+    p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8', chunk_rows, ring_stages)
     tensors = dict(x=bf(H.x), logits=torch.from_numpy(H.logits).cuda(),
                    wq=[u8(q[k][0]) for k in ('w_gate', 'w_up', 'w_down')],
                    ws=[bf(H.ws_gate), bf(H.ws_up), bf(H.ws_down)],
@@ -153,6 +153,16 @@ def test_mx_forward_small(m):
         fb = frac_beyond(got, want, TOL['mxfp8'], True)
         print(f'  mx {name}: share beyond tau*RMS without allowance = {fb:.2e}', flush=True)
         assert fb < MAX_FRAC_BEYOND, (name, fb)
+
+
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 4), (768, 5), (1 << 20, 3)])
+def test_mx_chunked_ring_bitwise_equals_unchunked(m, chunk, stages):
+    """The MXFP8 forward through the chunked ring (dispatch quantises each chunk into ring stage
+    c mod S, the two block-scaled GEMMs read it there) gives the unchunked path's bits."""
+    H, q = mx_layer(MX_SMALL)
+    a, ya, *_ = run_mx_forward(m, H, q)
+    b, yb, _, p, _ = run_mx_forward(m, H, q, chunk_rows=chunk, ring_stages=stages)
+    assert torch.equal(a, b) and torch.equal(ya, yb)
 
 
 def test_mx_forward_deterministic(m):

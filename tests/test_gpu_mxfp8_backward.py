@@ -63,7 +63,8 @@ def run_share_mx(m, H, q, counts, dev_w=None, flags=0, keep=False):
               dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
     G = m.make_grads(**gr)
     dxl = torch.empty((cfg.tokens, D), dtype=torch.bfloat16, device='cuda')
-    wsb = torch.full((m.backward_workspace_size(p),), 0x7f, dtype=torch.uint8, device='cuda')
+    wsb = torch.full(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(p),), 0x7f,
+                     dtype=torch.uint8, device='cuda')
     wsb[:4].zero_()
     if keep:
         m.experts_backward_kept(p, S, dev['x_slot'], off_d, g_d, dev['dy_slot'], W, dxs, dg, G, dev['x_local'],
@@ -355,7 +356,8 @@ def test_mx_layer_keep_activations_bitwise(m):
         dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
         dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
         dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
-        wsb = torch.zeros((m.backward_workspace_size(p),), dtype=torch.uint8, device='cuda')
+        wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(p),),
+                          dtype=torch.uint8, device='cuda')
         args = (p, dout, tensors['x'], tensors['logits'], W, m.make_routing(*rt), dx, m.make_grads(**gr), dtw, dlg)
         if keep:
             m.backward_kept(*args, *act, wsb)
