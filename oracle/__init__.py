@@ -24,7 +24,7 @@ from .moe import (  # noqa: F401
     swiglu_expert, moe_forward, moe_backward, d_logits_from_dg,
     experts_forward, experts_backward, shared_backward, combine,
     mx_along, experts_forward_mx, experts_backward_mx, experts_forward_mx_w, experts_backward_mx_w,
-    moe_forward_mx,
+    moe_forward_mx, router_logits, router_backward,
 )
 from .mx import (  # noqa: F401
     e4m3_round, e4m3_encode, e4m3_decode, mx_quantize, mx_dequantize, mx_roundtrip, E4M3_MAX,

@@ -266,6 +266,20 @@ def moe_backward(x, logits, w_gate, w_up, w_down, K, dout, ws_gate=None, ws_up=N
     return res
 
 
+def router_logits(x, w_router):
+    """Router projection: logits[t, e] = <x[t], W_r[e]> with W_r [E, D] (the router of the Blog's
+    "Overlapping computation and communication in MoE", whose softmax gives the weights s)."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
+
+
+def router_backward(x, w_router, d_logits):
+    """Backward of router_logits given the gradient w.r.t. the logits [T, E] (d_logits_from_dg):
+    dW_r = d_logits^T x [E, D] and the router's share of the input gradient dx = d_logits W_r
+    [T, D], to be added to the experts' (the logits are linear in both x and W_r)."""
+    dl = np.asarray(d_logits, dtype=np.float64)
+    return dl.T @ np.asarray(x, dtype=np.float64), dl @ np.asarray(w_router, dtype=np.float64)
+
+
 # ----------------------------------------------------------------------------------------------
 # expert-level entry (slots already grouped by expert: one expert-parallel rank's share)
 # ----------------------------------------------------------------------------------------------
