@@ -188,6 +188,20 @@ int moe_route_gemm_workspace_size(const moe_problem *p, size_t *bytes);
 int moe_schedule(const moe_problem *p, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                  int32_t *perm, int32_t *inv_perm, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_schedule for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same outputs, bit for bit, with no
+ * workspace argument. Its scratch (per-block histograms and the m-tile prefix) is a static device
+ * array of 2 MiB + 8 KiB that each GPU holds from the first call until the process ends; the
+ * first call on a device also looks up that array's address there (the library's only
+ * host-side state, kept per device). Sizes beyond the array -- ceil(T*K / 2048) * E > 2^19,
+ * e.g. more than 2^20 routes with E = 1024 or 2^22 with E = 256 -- return MOE_ERR_UNSUPPORTED
+ * before anything is enqueued. error_word: a caller-owned device int32 that receives the sticky
+ * error bits moe_schedule puts at workspace offset 0 (bit 0: an expert id out of range, counted
+ * as expert 0); never cleared by the library. Calls that overlap on one GPU share the array and
+ * race: serialise them (one stream, or an event between streams). */
+int moe_schedule_noalloc(const moe_problem *p, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
+                         int32_t *perm, int32_t *inv_perm, int32_t *error_word, hipStream_t stream);
+
 /* Pull-dispatch schedule of rank `rank` among R source ranks (Blog, "Scheduling"; region order
  * from the Notes, "Pull dispatch, push combine"). routing [R][N][K] int32 (device): global expert
  * of route k of token i on source rank r, in [0, R*L); rank c owns experts [c*L, (c+1)*L).

@@ -39,7 +39,7 @@ EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_sc
             'moe_experts_forward_keep', 'moe_experts_backward_kept', 'moe_forward_keep', 'moe_backward_kept',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
             'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size',
-            'moe_backward_kept_workspace_size')
+            'moe_backward_kept_workspace_size', 'moe_schedule_noalloc')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -80,6 +80,7 @@ _sig = {
     'moe_backward_kept_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(_sz)]),
     'moe_route_topk': (ctypes.c_int, [_PP, _P, _P, _P, _P]),
     'moe_schedule': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    'moe_schedule_noalloc': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P]),
     'moe_dispatch': (ctypes.c_int, [_PP, _P, _P, _i64, _i64, _P, _P, _P]),
     'moe_dispatch_tokens': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     'moe_combine': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
@@ -166,6 +167,11 @@ def schedule(p, topk_idx, counts, offsets, perm, inv_perm, ws, stream=None):
     _check(_lib.moe_schedule(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
                              _ptr(inv_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            'moe_schedule')
+
+
+def schedule_noalloc(p, topk_idx, counts, offsets, perm, inv_perm, error_word, stream=None):
+    _check(_lib.moe_schedule_noalloc(ctypes.byref(p), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
+                                     _ptr(inv_perm), _ptr(error_word), _stream(stream)), 'moe_schedule_noalloc')
 
 
 def dispatch(p, x, perm, slot_begin, slot_count, x_slot, x_slot_scales=None, stream=None):

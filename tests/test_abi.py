@@ -220,3 +220,17 @@ def test_kept_backward_workspace_is_smaller_and_refused_by_the_replay():
     n = ctypes.c_size_t()
     assert lib.moe_backward_kept_workspace_size(ctypes.byref(m.problem(300, 256, 384, 16, 4, 0, 'f32')),
                                                 ctypes.byref(n)) == -2
+
+
+def test_schedule_noalloc_rejects_without_gpu():
+    """moe_schedule_noalloc validates on the host before touching the device: null outputs or a
+    null error word are INVALID_ARG; a routing whose histograms exceed the static scratch
+    (ceil(T*K / 2048) * E > 2^19) is UNSUPPORTED."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    fake = 1 << 20
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16')
+    assert lib.moe_schedule_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, None, None) == -1
+    assert lib.moe_schedule_noalloc(ctypes.byref(p), None, fake, fake, fake, fake, fake, None) == -1
+    big = m.problem(1 << 18, 128, 128, 1024, 8, 0, 'bf16')        # 2^21 routes, 1024 experts
+    assert lib.moe_schedule_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None) == -2
