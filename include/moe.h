@@ -180,6 +180,18 @@ int moe_route_gemm(const moe_problem *p, const void *x, const void *w_router, fl
 /* Bytes of device workspace moe_route_gemm needs for `p`. */
 int moe_route_gemm_workspace_size(const moe_problem *p, size_t *bytes);
 
+/* Backward of moe_route_gemm's projection logits = x W_r^T (the router of the Blog's
+ * "Overlapping computation and communication in MoE"; the router-gradient step of the Notes'
+ * "The production details" continued through the projection): from d_logits [T][E] fp32 (as
+ * moe_backward writes it), dw_router [E][D] fp32 = d_logits^T x (overwritten) and, when dx is
+ * not NULL, dx [T][D] (BF16, the experts' input gradient from moe_backward) += d_logits W_r,
+ * summed in fp32 onto the stored value and rounded once. x [T][D], w_router [E][D] BF16.
+ * Products are exact in fp32; each output is one thread's fp32 sum in ascending token (dw) or
+ * expert (dx) order: deterministic. BF16 and MXFP8 problems (x is BF16 under both);
+ * MOE_F32: MOE_ERR_UNSUPPORTED. No workspace. */
+int moe_route_gemm_backward(const moe_problem *p, const void *x, const void *w_router, const float *d_logits,
+                            float *dw_router, void *dx, hipStream_t stream);
+
 /* Device-side histogram + exclusive scan + stable placement: the one-source-rank case of the
  * pull schedule (Blog, "Scheduling"; sort key from the Notes, section "Pull dispatch, push
  * combine"). topk_idx [T][K] -> counts [E], offsets [E+1], perm [T*K], inv_perm [T*K], with

@@ -39,7 +39,7 @@ EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_sc
             'moe_experts_forward_keep', 'moe_experts_backward_kept', 'moe_forward_keep', 'moe_backward_kept',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
             'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size',
-            'moe_backward_kept_workspace_size', 'moe_schedule_noalloc')
+            'moe_backward_kept_workspace_size', 'moe_schedule_noalloc', 'moe_route_gemm_backward')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -102,6 +102,7 @@ _sig = {
     'moe_quantize_mx': (ctypes.c_int, [_P, _i64, _i32, _P, _P, _P]),
     'moe_route_gemm': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_route_gemm_workspace_size': (ctypes.c_int, [_PP, ctypes.POINTER(ctypes.c_size_t)]),
+    'moe_route_gemm_backward': (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
     'moe_pull_schedule': (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
     'moe_pull_schedule_workspace_size': (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     'moe_forward_stages': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P,
@@ -307,3 +308,8 @@ def route_gemm_workspace_size(p: Problem) -> int:
 def route_gemm(p, x, w_router, logits, topk_idx, topk_w, ws, stream=None):
     _check(_lib.moe_route_gemm(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(topk_idx), _ptr(topk_w),
                                _ptr(ws), ws.numel(), _stream(stream)), 'moe_route_gemm')
+
+
+def route_gemm_backward(p, x, w_router, d_logits, dw_router, dx=None, stream=None):
+    _check(_lib.moe_route_gemm_backward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(d_logits), _ptr(dw_router),
+                                        _ptr(dx), _stream(stream)), 'moe_route_gemm_backward')
