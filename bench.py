@@ -127,41 +127,16 @@ def main():
 
     if args.workload in ('ep_share', 'ep_share_mxfp8'):
         dt = 'mxfp8' if args.workload == 'ep_share_mxfp8' else 'bf16'
+        if args.calib_copy:
+            calib_copy()
         print(json.dumps(bench_share(args.steps, args.warmup, args.flags, dt, keep=args.keep_activations)), flush=True)
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
-    print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
-    L = synth.device_layer(cfg)
-    mx = None
-    if cfg.dtype == 'mxfp8':
-        # routed expert weights quantised on the device (E4M3 + E8M0 per 32 along K); shared stays BF16
-        mx = {}
-        for k in ('w_gate', 'w_up', 'w_down'):
-            wbf = getattr(L, k)
-            q = torch.empty(wbf.shape, dtype=torch.uint8, device='cuda')
-            sc = torch.empty(wbf.shape[:-1] + (wbf.shape[-1] // 32,), dtype=torch.uint8, device='cuda')
-            moe.quantize_mx(wbf, q, sc)
-            mx[k] = (q, sc)
-        torch.cuda.synchronize()
+    F = make_forward(cfg, args.chunk_rows, args.flags)
+    L, p, weights, routing_t, routing, out, ws = F['L'], F['p'], F['weights'], F['routing_t'], F['routing'], F['out'], F['ws']
     T, D, K = cfg.T, cfg.D, cfg.K
     dev = 'cuda'
-    p = moe.problem(cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared, cfg.dtype, args.chunk_rows, 0, args.flags)
-    dt = L.x.dtype
-    routing_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
-                     topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
-                     counts=torch.empty((cfg.E,), dtype=torch.int32, device=dev),
-                     offsets=torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev),
-                     perm=torch.empty((T * K,), dtype=torch.int32, device=dev),
-                     inv_perm=torch.empty((T * K,), dtype=torch.int32, device=dev))
-    routing = moe.make_routing(**routing_t)
-    if mx is None:
-        weights = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
-    else:
-        weights = moe.make_weights(mx['w_gate'][0], mx['w_up'][0], mx['w_down'][0], L.ws_gate, L.ws_up, L.ws_down,
-                                   mx['w_gate'][1], mx['w_up'][1], mx['w_down'][1])
-    out = torch.empty((T, D), dtype=dt, device=dev)
-    ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     nst = len(moe.STAGES)
 
@@ -172,19 +147,14 @@ def main():
             moe.forward_stages(p, L.x, L.logits, weights, out, routing, ws, events, stream=stream)
 
     if args.calib_copy:
-        src = torch.empty((1 << 29,), dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.neg(src, out=dst)          # an elementwise kernel: reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy()
     print(f'[bench] warmup {args.warmup}', file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps of moe_forward (the shared expert overlaps the routed path on the
-    # library's side stream), bracketed by device synchronisations
+    # timed region: K steps of moe_forward (every stage in order on this stream), bracketed by
+    # device synchronisations
     n_attr = min(args.steps, 20)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(n_attr)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -253,9 +223,14 @@ def main():
     extra = None
     if not args.no_extra and args.workload == 'dsv3':
         rg = bench_route_gemm(moe, cfg, L.x, stream)
-        del L, weights, ws, out
+        del weights, ws, out, F
         torch.cuda.empty_cache()
-        extra = {'second_stream_latency': yl,
+        layer = {'layer_fwd_bwd': layer_fwd_bwd_leg(cfg, L, keep=False),
+                 'layer_fwd_bwd_keep_activations': layer_fwd_bwd_leg(cfg, L, keep=True)}
+        del L
+        torch.cuda.empty_cache()
+        extra = {'second_stream_latency': yl, **layer,
+                 'mid_forward': forward_leg(synth.MID, 20), 'mxfp8_forward': forward_leg(synth.MXFP8, 5),
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
                  'ep_share_fwd_bwd_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
                                                                   keep=True),
@@ -268,6 +243,8 @@ def main():
                  'ep_share_fwd_bwd_mxfp8_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
                                                                         'mxfp8', keep=True),
                  'pull_schedule_ep8': bench_pull_schedule(moe, stream), 'route_gemm': rg}
+        if not args.no_cpu_baseline:
+            extra['cpu_baselines'] = cpu_oracle_extra(moe)
 
     line = {
         'metric': METRIC,
@@ -529,16 +506,47 @@ def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10):
     return res
 
 
+def host_info():
+    """What the CPU oracle runs on: CPU model, the cores this process may use, and the BLAS numpy
+    calls (vendor, version and thread count as threadpoolctl reports them)."""
+    model = 'unknown'
+    try:
+        with open('/proc/cpuinfo') as f:
+            for line in f:
+                if line.startswith('model name'):
+                    model = line.split(':', 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get('user_api') == 'blas':
+                blas.append({k: i.get(k) for k in ('internal_api', 'version', 'num_threads', 'threading_layer')})
+    except Exception:  # pragma: no cover
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {'cpu_model': model, 'cores_available': cores, 'blas': blas}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get('num_threads', 1) for i in threadpool_info() if i.get('user_api') == 'blas'), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
 def cpu_baseline(cfg, L, ntok):
     """The fp64 oracle on `ntok` sampled tokens of the same layer, on the host cores. The weights
     of the experts these tokens use are copied to the host before the timed region."""
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get('num_threads', 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads = blas_threads()
     rng = np.random.default_rng(1234)
     toks = np.sort(rng.choice(cfg.T, ntok, replace=False))
     lg = L.logits[torch.from_numpy(toks).cuda()].cpu().numpy()
@@ -556,7 +564,252 @@ def cpu_baseline(cfg, L, ntok):
     return {'value': ntok / dt, 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
             'sample': f'{ntok} random tokens of the same layer (all their routed experts + shared), fp64 numpy, '
                       f'{len(used)} experts streamed; weights copied to host before timing',
-            'seconds': dt}
+            'seconds': dt, 'host': host_info()}
+
+
+def calib_copy():
+    """One elementwise kernel that reads exactly 1 GiB and writes exactly 1 GiB (torch.neg over 2^29
+    int16): the yardstick the HBM traffic counters (FETCH_SIZE, WRITE_SIZE) are scaled by."""
+    import torch
+    src = torch.empty((1 << 29,), dtype=torch.int16, device='cuda')
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def make_forward(cfg, chunk_rows=0, flags=0):
+    """Inputs of one moe_forward of configuration `cfg` generated on the device (seeded), with the
+    routing state, output and workspace buffers; under MXFP8 the routed weights quantised on the
+    device (E4M3 + E8M0 per 32 along K; the shared expert stays BF16)."""
+    import torch
+    import synth
+    import mixture_experts_layer_norm_amd as moe
+    print(f'[bench] generating {cfg.name} on the device', file=sys.stderr, flush=True)
+    L = synth.device_layer(cfg)
+    T, D, K, E = cfg.T, cfg.D, cfg.K, cfg.E
+    dev = 'cuda'
+    mx = None
+    if cfg.dtype == 'mxfp8':
+        mx = {}
+        for k in ('w_gate', 'w_up', 'w_down'):
+            wbf = getattr(L, k)
+            q = torch.empty(wbf.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(wbf.shape[:-1] + (wbf.shape[-1] // 32,), dtype=torch.uint8, device=dev)
+            moe.quantize_mx(wbf, q, sc)
+            mx[k] = (q, sc)
+        torch.cuda.synchronize()
+    p = moe.problem(T, D, cfg.I, E, K, cfg.I_shared, cfg.dtype, chunk_rows, 0, flags)
+    routing_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
+                     topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
+                     counts=torch.empty((E,), dtype=torch.int32, device=dev),
+                     offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                     perm=torch.empty((T * K,), dtype=torch.int32, device=dev),
+                     inv_perm=torch.empty((T * K,), dtype=torch.int32, device=dev))
+    if mx is None:
+        weights = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
+    else:
+        weights = moe.make_weights(mx['w_gate'][0], mx['w_up'][0], mx['w_down'][0], L.ws_gate, L.ws_up, L.ws_down,
+                                   mx['w_gate'][1], mx['w_up'][1], mx['w_down'][1])
+    return dict(L=L, p=p, mx=mx, weights=weights, routing_t=routing_t, routing=moe.make_routing(**routing_t),
+                out=torch.empty((T, D), dtype=L.x.dtype, device=dev),
+                ws=torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device=dev))
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Mean device time of fn() over `steps` calls after `warmup`, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def forward_leg(cfg, steps, warmup=3):
+    """moe_forward of another configuration, timed like the headline (device time per step, inputs
+    resident in HBM): mid BF16 at T=4096 and MXFP8 at T=32768."""
+    import torch
+    import mixture_experts_layer_norm_amd as moe
+    F = make_forward(cfg)
+    stream = torch.cuda.current_stream()
+    ms = time_calls(lambda: moe.forward(F['p'], F['L'].x, F['L'].logits, F['weights'], F['out'], F['routing'],
+                                        F['ws'], stream=stream), steps, warmup, stream)
+    T, D, I, Is, n = cfg.T, cfg.D, cfg.I, cfg.I_shared, cfg.T * cfg.K
+    routed, shared = 6.0 * n * D * I, 6.0 * T * D * Is
+    if cfg.dtype == 'mxfp8':
+        t_peak = routed / (PEAK_MXFP8_TFLOPS * 1e12) + shared / (PEAK_BF16_TFLOPS * 1e12)
+    else:
+        t_peak = (routed + shared) / (PEAK_BF16_TFLOPS * 1e12)
+    del F
+    torch.cuda.empty_cache()
+    return {'workload': f'{cfg.name} forward', 'steps': steps, 'ms_per_step': ms, 'value': T / (ms * 1e-3),
+            'unit': 'tokens/s', 'tflops': (routed + shared) / (ms * 1e-3) / 1e12,
+            'mfma_peak_frac': t_peak / (ms * 1e-3),
+            'peak_note': 'MXFP8: routed FLOPs at 5.0 PF, shared-expert FLOPs at 2.5 PF' if cfg.dtype == 'mxfp8'
+            else 'BF16 at 2.5 PF'}
+
+
+def layer_fwd_bwd_leg(cfg, L, keep, steps=5, warmup=2):
+    """The whole layer forward + backward at `cfg` (moe_forward + moe_backward, or with keep
+    moe_forward_keep + moe_backward_kept, which hand the routed a, u in fp32 to the backward instead
+    of replaying them); the forward and backward device times per step and TFLOP/s counting the
+    backward as twice the forward's FLOPs."""
+    import torch
+    import mixture_experts_layer_norm_amd as moe
+    T, D, I, E, K, Is = cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared
+    dev = 'cuda'
+    p = moe.problem(T, D, I, E, K, Is, cfg.dtype)
+    rt = [torch.empty((T, K), dtype=torch.int32, device=dev), torch.empty((T, K), dtype=torch.float32, device=dev),
+          torch.empty((E,), dtype=torch.int32, device=dev), torch.empty((E + 1,), dtype=torch.int32, device=dev),
+          torch.empty((T * K,), dtype=torch.int32, device=dev), torch.empty((T * K,), dtype=torch.int32, device=dev)]
+    R = moe.make_routing(*rt)
+    W = moe.make_weights(L.w_gate, L.w_up, L.w_down, L.ws_gate, L.ws_up, L.ws_down)
+    out = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    dout = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+    gr = [torch.empty(s_, device=dev) for s_ in ((E, I, D), (E, I, D), (E, D, I), (Is, D), (Is, D), (D, Is))]
+    G = moe.make_grads(*gr)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    dtw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dlg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    wsb = torch.empty(((moe.backward_kept_workspace_size if keep else moe.backward_workspace_size)(p),),
+                      dtype=torch.uint8, device=dev)
+    act = [torch.empty((T * K, I), device=dev) for _ in range(2)] if keep else None
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        if keep:
+            moe.forward_keep(p, L.x, L.logits, W, out, R, *act, ws, stream=stream)
+        else:
+            moe.forward(p, L.x, L.logits, W, out, R, ws, stream=stream)
+
+    def bwd():
+        if keep:
+            moe.backward_kept(p, dout, L.x, L.logits, W, R, dx, G, dtw, dlg, *act, wsb, stream=stream)
+        else:
+            moe.backward(p, dout, L.x, L.logits, W, R, dx, G, dtw, dlg, wsb, stream=stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in ev]))
+    b_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in ev]))
+    flops_f = 6.0 * T * K * D * I + 6.0 * T * D * Is
+    ms = f_ms + b_ms
+    del ws, wsb, act, gr, G
+    torch.cuda.empty_cache()
+    return {'workload': f'{cfg.name} forward+backward' + (' (a, u kept)' if keep else ' (a, u replayed)'),
+            'steps': steps, 'ms_per_step': ms, 'fwd_ms': f_ms, 'bwd_ms': b_ms, 'value': T / (ms * 1e-3),
+            'unit': 'tokens/s', 'tflops': 3.0 * flops_f / (ms * 1e-3) / 1e12,
+            'mfma_peak_frac': 3.0 * flops_f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def cpu_oracle_extra(moe_mod):
+    """The fp64 CPU oracle timed on the other configurations, each on a bounded sample (a few
+    seconds of host work): the whole mid layer forward; one EP=64 rank's share forward+backward on
+    128 slots per expert and 64 shared-expert tokens; the MXFP8 forward on 32 tokens whose experts
+    lie in the smallest popular set (the weights' MX quantisation, offline in the recipe, is done by
+    the oracle's encoder before the timed region)."""
+    import torch
+    import oracle
+    import synth
+    res = {}
+    threads = blas_threads()
+    # mid, whole layer
+    L = synth.device_layer(synth.MID)
+    h = lambda t: t.float().cpu().numpy() if t is not None else None
+    x, lg = h(L.x), L.logits.cpu().numpy()
+    w = [h(L.w_gate), h(L.w_up), h(L.w_down)]
+    sh = [h(L.ws_gate), h(L.ws_up), h(L.ws_down)]
+    del L
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, lg, *w, synth.MID.K, *sh)
+    dt = time.perf_counter() - t0
+    res['mid_forward'] = {'value': synth.MID.T / dt, 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
+                          'sample': f'the whole {synth.MID.name} forward (all {synth.MID.T} tokens)', 'seconds': dt}
+    del x, lg, w, sh
+    # EP share, forward + backward on sampled slots
+    cfg = synth.EP_SHARE
+    D_ = synth.device_share(cfg)
+    off = np.concatenate([[0], np.cumsum(D_.counts)])
+    rng = np.random.default_rng(5)
+    slots = np.concatenate([np.sort(rng.choice(np.arange(off[e], off[e + 1]), 128, replace=False))
+                            for e in range(cfg.E_local)])
+    rows = np.sort(rng.choice(cfg.tokens, 64, replace=False))
+    si, ri = torch.from_numpy(slots).cuda(), torch.from_numpy(rows).cuda()
+    xs, dys, gs = h(D_.x_slot[si]), h(D_.dy_slot[si]), D_.g[si].cpu().numpy().astype(np.float64)
+    wg, wu, wd = h(D_.w_gate), h(D_.w_up), h(D_.w_down)
+    xl, dyl = h(D_.x_local[ri]), h(D_.dy_local[ri])
+    sg, su, sd = h(D_.ws_gate), h(D_.ws_up), h(D_.ws_down)
+    del D_
+    torch.cuda.empty_cache()
+    cnt = np.full(cfg.E_local, 128)
+    t0 = time.perf_counter()
+    oracle.experts_forward(xs, cnt, wg, wu, wd)
+    oracle.experts_backward(xs, cnt, gs, dys, wg, wu, wd)
+    oracle.swiglu_expert(xl, sg, su, sd)
+    oracle.shared_backward(xl, dyl, sg, su, sd)
+    dt = time.perf_counter() - t0
+    res['ep_share_fwd_bwd'] = {'value': 64 / dt, 'unit': 'tokens/s', 'slots_per_s': slots.size / dt,
+                               'cores': threads, 'kind': 'oracle',
+                               'sample': f'{cfg.name}: 128 slots per expert ({slots.size} slots, the routed work of 64 '
+                                         f'tokens at the share\'s {cfg.slots // cfg.tokens} slots per token) and 64 '
+                                         f'local tokens through the shared expert, forward+backward; value counts '
+                                         f'those 64 tokens', 'seconds': dt}
+    del xs, dys, gs, wg, wu, wd, xl, dyl, sg, su, sd
+    # MXFP8 forward on tokens that use few experts
+    cfg = synth.MXFP8
+    L = synth.device_layer(cfg)
+    lgm = L.logits.cpu().numpy()
+    idx = oracle.route_topk(lgm, cfg.K)
+    top, has0 = idx.max(axis=1), (idx == 0).any(axis=1)
+    toks = None
+    for M in range(cfg.K, cfg.E + 1):
+        cand = np.nonzero((top < M) & has0)[0]
+        if cand.size >= 32:
+            toks = np.sort(cand[:32])
+            break
+    used = sorted(set(idx[toks].ravel().tolist()))
+    ti = torch.from_numpy(toks).cuda()
+    xm = h(L.x[ti])
+    raw = {(k, e): getattr(L, k)[e].float().cpu().numpy() for k in ('w_gate', 'w_up', 'w_down') for e in used}
+    shm = [h(L.ws_gate), h(L.ws_up), h(L.ws_down)]
+    del L
+    torch.cuda.empty_cache()
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as pool:
+        deq = dict(zip(raw.keys(), pool.map(lambda a: oracle.mx_dequantize(*oracle.mx_quantize(a.astype(np.float64))),
+                                            raw.values())))
+    del raw
+    t0 = time.perf_counter()
+    oracle.moe_forward_mx(xm, lgm[toks], lambda e: deq[('w_gate', e)], lambda e: deq[('w_up', e)],
+                          lambda e: deq[('w_down', e)], cfg.K, *shm)
+    dt = time.perf_counter() - t0
+    res['mxfp8_forward'] = {'value': toks.size / dt, 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
+                            'sample': f'{toks.size} tokens of {cfg.name} routed among its {len(used)} most popular '
+                                      f'experts (x and h quantised in the timed region, weights before it)',
+                            'seconds': dt}
+    res['host'] = host_info()
+    return res
 
 
 if __name__ == '__main__':
