@@ -337,7 +337,28 @@ def bench_route_gemm(moe, cfg, x, stream, reps=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flops = 2.0 * T * D * E
-    return {'workload': f'router GEMM + top-{K}, T={T} D={D} E={E}', 'ms': ms, 'tflops': flops / (ms * 1e-3) / 1e12}
+    res = {'workload': f'router GEMM + top-{K}, T={T} D={D} E={E}', 'ms': ms, 'tflops': flops / (ms * 1e-3) / 1e12}
+    # its backward: dW_r = d_logits^T x and dx += d_logits W_r (fp32 FMA, 4*T*D*E FLOP), with
+    # d_logits nonzero on each token's K chosen experts as the layer backward writes it
+    dl = torch.zeros((T, E), dtype=torch.float32, device='cuda')
+    dl.scatter_(1, idx.long(), torch.randn((T, K), generator=g, device='cuda'))
+    dw = torch.empty((E, D), dtype=torch.float32, device='cuda')
+    dx = torch.zeros((T, D), dtype=torch.bfloat16, device='cuda')
+
+    def fb():
+        moe.route_gemm_backward(p, x, w, dl, dw, dx, stream=stream)
+    for _ in range(2):
+        fb()
+    e0.record(stream)
+    for _ in range(reps // 2):
+        fb()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mb = e0.elapsed_time(e1) / (reps // 2)
+    res['backward'] = {'ms': mb, 'tflops': 2 * flops / (mb * 1e-3) / 1e12,
+                       'fp32_peak_frac': 2 * flops / (mb * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
+                       'note': 'dW_r = d_logits^T x and dx += d_logits W_r, fp32 FMA; fraction of the 157.3 TFLOP/s fp32 peak'}
+    return res
 
 
 def bench_pull_schedule(moe, stream, R=8, N=8192, K=8, L=32, reps=20):

@@ -14,7 +14,9 @@
  * ---------------------------------------
  * - Ownership: the caller owns every pointer. Tensor and workspace pointers are device
  *   pointers (hipMalloc'd memory of the current device); structs are host memory read during
- *   the call only. The library allocates nothing and keeps no state between calls.
+ *   the call only. The library allocates nothing, creates no streams or events, and keeps no
+ *   state between calls, except that moe_schedule_noalloc keeps, per device, the address of its
+ *   static scratch array.
  * - Asynchrony: a call validates its arguments on the host, then only enqueues kernels on
  *   `stream`. It never synchronises, never copies device data to the host and never blocks.
  * - Errors: MOE_OK (0) or a negative moe_status. Argument errors are detected on the host
