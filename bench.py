@@ -18,6 +18,7 @@ the same workload (rank 0, one GPU only).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -48,6 +49,18 @@ def gemm_sources_hash():
         with open(os.path.join(ROOT, rel), 'rb') as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def routed_gemm_kernel(cfg, ntn, flags):
+    """Which kernel the library launches for a routed BF16 GEMM with ntn n-tiles: the persistent
+    one where the launch's upper bound of tiles is at least 12 per workgroup (one workgroup per CU),
+    or with MOE_FLAG_PERSISTENT_GEMM; the per-tile one otherwise (the library's own rule)."""
+    import torch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    mt = (cfg.T * cfg.K + 255) // 256 + cfg.E
+    nb = (mt * ntn + 7) // 8 * 8
+    nw = min(max(ncu, 8) // 8 * 8, nb)
+    return 'gemm_bf16_persistent_kernel' if (flags & 0x10000) or nb >= 12 * nw else 'gemm_bf16_kernel'
 
 
 def measured_traffic(stage, flags, workload):
@@ -198,9 +211,13 @@ def main():
         roof = {'bound': 'hbm', 'achieved': b_dom / t_dom / 1e9, 'peak': PEAK_HBM_GBS, 'unit': 'GB/s'}
     roof['frac'] = roof['achieved'] / roof['peak']
     roof['traffic'] = measured_traffic(dom, args.flags, cfg.name)
-    gk = 'gemm_mx_kernel' if cfg.dtype == 'mxfp8' else 'gemm_bf16_kernel'
-    roof['kernel'] = {'up_gate': f'{gk}<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
-                      'down': f'{gk}<EPI_STORE> (routed W_down + scatter)',
+    gk = {'mxfp8': 'gemm_mx_kernel', 'f32': 'gemm_f32_kernel'}.get(cfg.dtype, 'gemm_bf16_kernel')
+    gku = gkd = gk
+    if cfg.dtype == 'bf16' and not args.chunk_rows:
+        gku = routed_gemm_kernel(cfg, cfg.I // 128, args.flags)
+        gkd = routed_gemm_kernel(cfg, (cfg.D + 255) // 256, args.flags)
+    roof['kernel'] = {'up_gate': f'{gku}<EPI_SWIGLU> (routed W_gate/W_up + SwiGLU)',
+                      'down': f'{gkd}<EPI_STORE> (routed W_down + scatter)',
                       'shared': 'shared expert GEMMs', 'dispatch': 'dispatch_kernel',
                       'combine': 'combine_bf16_kernel', 'route': 'route_topk_kernel',
                       'schedule': 'sched_* kernels'}[dom]
@@ -212,7 +229,18 @@ def main():
     roof['hbm_frac'] = b_dom / t_dom / 1e9 / PEAK_HBM_GBS
 
     pc = standalone_permute_combine(moe, p, cfg, L, routing_t, out, stream) if cfg.dtype == 'bf16' else None
-    yl = second_stream_latency(step, stream) if (not args.no_extra and args.workload == 'dsv3') else None
+    yl = None
+    if not args.no_extra and args.workload == 'dsv3':
+        # the same forward with persistent GEMMs that honour the workgroup budget word
+        pb = moe.problem(T, D, cfg.I, cfg.E, K, cfg.I_shared, cfg.dtype, args.chunk_rows, 0,
+                         args.flags | moe.MOE_FLAG_PERSISTENT_GEMM | moe.MOE_FLAG_CU_BUDGET)
+        wsb = torch.zeros((moe.workspace_size(pb),), dtype=torch.uint8, device=dev)
+        word = wsb[moe.MOE_WS_CU_BUDGET_OFFSET:moe.MOE_WS_CU_BUDGET_OFFSET + 4].view(torch.int32)
+
+        def step_b():
+            moe.forward(pb, L.x, L.logits, weights, out, routing, wsb, stream=stream)
+        yl = second_stream_latency(step, stream, budget=(step_b, word, 224))
+        del wsb
 
     # per-step spread from the in-order run (sum of its stage events)
     per_step = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(n_attr)])
@@ -485,20 +513,25 @@ def bench_share(steps, warmup, flags, dtype='bf16', keep=False):
             'fwd_tflops': flops_f / (f_ms * 1e-3) / 1e12, 'bwd_tflops': 2 * flops_f / (b_ms * 1e-3) / 1e12}
 
 
-def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10):
+def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10, budget=None):
     """Latency of a small kernel (an in-place add over 4 MB) enqueued on a second default-priority
     stream while moe_forward runs on the library's stream, `delay` ms after the forward was
-    enqueued. The forward's GEMMs are one tile per workgroup, so the dispatcher can hand a CU to
-    the other stream at every tile boundary; no yield flag is involved. Probes that did not start
-    inside the forward are dropped."""
+    enqueued. Probes that did not start inside the forward are dropped.
+    budget = (step_b, word, value): the forward `step_b` runs with MOE_FLAG_PERSISTENT_GEMM |
+    MOE_FLAG_CU_BUDGET, and the second stream first copies `value` into its workgroup budget word
+    `word` (a host-to-device copy, which needs no CU), then runs the probe; the latency counts from
+    the copy. Workgroups at or above `value` end after their current tile and leave their CUs to
+    the probe; the word is reset to 0 after each trial."""
     import torch
     other = torch.cuda.Stream()
     small = torch.zeros(1 << 20, device='cuda')
 
-    def probe():
+    def probe(pre=None):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(other)
         with torch.cuda.stream(other):
+            if pre is not None:
+                pre()
             small.add_(1.0)
         e1.record(other)
         return e0, e1
@@ -510,21 +543,66 @@ def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10):
         alone.append(e0.elapsed_time(e1) * 1e3)
     res = {'probe': 'in-place add over 1M fp32 on a second default-priority stream',
            'alone_us_median': float(np.median(alone))}
-    for d in delays_ms:
-        lat = []
-        for _ in range(trials):
-            fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            fa.record(stream)
-            step()
-            fb.record(stream)
-            time.sleep(d / 1e3)
-            e0, e1 = probe()
+
+    def sweep(run, pre, reset):
+        out = {}
+        for d in delays_ms:
+            lat = []
+            for _ in range(trials):
+                fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                fa.record(stream)
+                run()
+                fb.record(stream)
+                time.sleep(d / 1e3)
+                e0, e1 = probe(pre)
+                torch.cuda.synchronize()
+                if reset is not None:
+                    reset()
+                if fa.elapsed_time(e0) > 0 and e0.elapsed_time(fb) > 0:
+                    lat.append(e0.elapsed_time(e1) * 1e3)
+            out[f'after_{d:g}ms'] = ({'probes': len(lat), 'median_us': float(np.median(lat)),
+                                      'max_us': float(np.max(lat))} if lat else {'probes': 0})
+        return out
+
+    res.update(sweep(step, None, None))
+    if budget is not None:
+        step_b, word, value = budget
+
+        def reset():
+            word.fill_(0)
             torch.cuda.synchronize()
-            if fa.elapsed_time(e0) > 0 and e0.elapsed_time(fb) > 0:
-                lat.append(e0.elapsed_time(e1) * 1e3)
-        res[f'after_{d:g}ms'] = ({'probes': len(lat), 'median_us': float(np.median(lat)),
-                                  'max_us': float(np.max(lat))} if lat else {'probes': 0})
+        # budget set before the forward: its GEMMs use `value` workgroups, the rest stay free
+        reset()
+        word.fill_(value)
+        torch.cuda.synchronize()
+        res['cu_budget_preset'] = {'value': value, 'note': 'persistent GEMMs with MOE_FLAG_CU_BUDGET, budget set '
+                                                           'before the forward', **sweep(step_b, None, None)}
+        reset()
+        # budget lowered while the forward runs, by a stream write-value operation on the second
+        # stream (executed by the command processor, needs no CU)
+        hip = hip_runtime()
+        if hip is not None:
+            def pre():
+                hip.hipStreamWriteValue32(ctypes.c_void_p(other.cuda_stream), ctypes.c_void_p(word.data_ptr()),
+                                          ctypes.c_uint32(value), ctypes.c_uint(0))
+            res['cu_budget_dynamic'] = {'value': value, 'note': 'budget written by hipStreamWriteValue32 on the '
+                                                                'second stream; latency from that write to the end '
+                                                                'of the probe', **sweep(step_b, pre, reset)}
     return res
+
+
+def hip_runtime():
+    """The HIP runtime library this process has loaded (torch's), through ctypes, or None."""
+    try:
+        with open('/proc/self/maps') as f:
+            paths = {line.split()[-1] for line in f if 'libamdhip64' in line}
+        if not paths:
+            return None
+        lib = ctypes.CDLL(sorted(paths)[0])
+        lib.hipStreamWriteValue32.restype = ctypes.c_int
+        return lib
+    except OSError:
+        return None
 
 
 def host_info():

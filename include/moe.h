@@ -89,7 +89,7 @@ typedef struct moe_problem {
 /* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
 #define MOE_FLAG_FUSED_GATHER 0x1
 /* Bits 0x2, 0x8, 0x10, 0x20 and 0xff00 are reserved (they selected tuning variants that measured
- * no faster and were removed); a problem that sets one is rejected. */
+ * no faster and were removed); a problem that sets one, or any bit not defined here, is rejected. */
 /* moe_backward / moe_experts_backward under MOE_BF16: contract dgrad-up (dx = [da | du] [W_gate |
  * W_up]) over the bf16 da, du in one K pass instead of over their hi + lo halves in two. Each dx
  * element sums 2I products whose roundings are independent; measured max |d| of dx reaches
@@ -109,6 +109,34 @@ typedef struct moe_problem {
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
 #define MOE_FLAG_PERSISTENT 0x4
+/* Persistent grouped GEMMs (MOE_BF16; the sparsenotes page "Mixture-of-Kittens: MoE Megakernel for
+ * NVL72s", sections "Granularity as a tunable" and "The production details"): the up/gate and down
+ * GEMMs of the forward entry points (moe_forward, moe_forward_stages, moe_forward_keep, and the
+ * expert-level moe_experts_forward, moe_experts_forward_keep; routed and shared expert) can run as
+ * persistent kernels, one workgroup per CU taking 256 x 256 tiles from ticket counters kept in
+ * the first 256 bytes of the workspace, instead of one workgroup per tile. Without this flag a
+ * GEMM runs persistent where it has at least 12 tiles per workgroup (e.g. the routed GEMMs at
+ * T = 8192, 256 experts, K = 8), per tile otherwise; with it, always. Each tile is computed by one
+ * workgroup in the same order either way, so every output is bitwise the same. Workgroups never
+ * wait for each other. MOE_F32 and MOE_MXFP8 with the flag: MOE_ERR_UNSUPPORTED. The backward
+ * entry points accept the flag and ignore it. */
+#define MOE_FLAG_PERSISTENT_GEMM 0x10000
+/* With MOE_FLAG_PERSISTENT_GEMM (alone: MOE_ERR_INVALID_ARG): between tiles, the persistent GEMMs
+ * read the int32 workgroup budget at byte offset MOE_WS_CU_BUDGET_OFFSET of the workspace. While
+ * it holds v > 0, workgroups with index >= v take no further tile and end after their current
+ * one, handing their CUs to other work on the GPU (the Notes' "The production details": the
+ * kernel yields processors to a higher-priority stream); the workgroups below v take every
+ * remaining tile, so the outputs are unchanged. v <= 0: no limit. The caller owns the word: it
+ * must initialise it before the call (the workspace is otherwise uninitialised); the library only
+ * reads it. Set before the call, it partitions the GPU: the persistent GEMMs use v workgroups and
+ * leave the other CUs to other streams (e.g. collectives). It may also be changed while the call
+ * runs, and takes effect at each workgroup's next tile boundary; but a copy or stream write-value
+ * enqueued on another stream can itself wait for a free CU before it lands, so a write meant to
+ * free CUs quickly belongs before the call. With this flag every forward GEMM runs persistent
+ * (MOE_FLAG_PERSISTENT_GEMM); the other kernels (routing, dispatch, combine) are short, run one
+ * workgroup per block, and do not read the word. */
+#define MOE_FLAG_CU_BUDGET 0x20000
+#define MOE_WS_CU_BUDGET_OFFSET 4
 
 /* Expert weights (device pointers). Routed: w_gate, w_up [E][I][D]; w_down [E][D][I].
  * Shared: ws_gate, ws_up [I_shared][D]; ws_down [D][I_shared] (always bf16 under MOE_MXFP8).

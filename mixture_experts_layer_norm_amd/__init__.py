@@ -29,6 +29,9 @@ MOE_FLAG_FUSED_GATHER = 0x1
 MOE_FLAG_PERSISTENT = 0x4
 MOE_FLAG_BWD_DGRAD_ONE_PASS = 0x40
 MOE_FLAG_BWD_WGRAD_LO_MXFP8 = 0x80
+MOE_FLAG_PERSISTENT_GEMM = 0x10000
+MOE_FLAG_CU_BUDGET = 0x20000
+MOE_WS_CU_BUDGET_OFFSET = 4
 STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3: 'MOE_ERR_WORKSPACE',
           -4: 'MOE_ERR_MISALIGNED', -5: 'MOE_ERR_HIP'}
 DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}

@@ -13,7 +13,7 @@ size_t elt_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static constexpr uint32_t kKnownFlags = MOE_FLAG_FUSED_GATHER | MOE_FLAG_PERSISTENT | MOE_FLAG_BWD_DGRAD_ONE_PASS |
-                                        MOE_FLAG_BWD_WGRAD_LO_MXFP8;
+                                        MOE_FLAG_BWD_WGRAD_LO_MXFP8 | MOE_FLAG_PERSISTENT_GEMM | MOE_FLAG_CU_BUDGET;
 
 // Extra checks of the entry points that route tokens (top-k over the E experts).
 int validate_routing(const moe_problem* p) {
@@ -30,6 +30,7 @@ int validate_problem(const moe_problem* p) {
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16 && p->dtype != MOE_MXFP8) return MOE_ERR_INVALID_ARG;
   if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
   if ((uint32_t)p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
+  if ((p->flags & MOE_FLAG_CU_BUDGET) && !(p->flags & MOE_FLAG_PERSISTENT_GEMM)) return MOE_ERR_INVALID_ARG;
   if (p->E > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_F32) {
@@ -246,7 +247,8 @@ int moe_quantize_mx(const void* src_bf16, int64_t rows, int32_t cols, uint8_t* q
 static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda, const int32_t* gather,
                       int gather_div, const void* wg, const void* wu, const void* wd, int D, int I,
                       int64_t w_stride_up, int64_t w_stride_down, void* h, void* y,
-                      const int32_t* scatter, hipStream_t stream, hipEvent_t mid = nullptr) {
+                      const int32_t* scatter, hipStream_t stream, hipEvent_t mid = nullptr,
+                      const Persist* pc = nullptr) {
   GemmArgs g1;
   g1.A = A; g1.lda = lda; g1.a_gather = gather; g1.a_div = gather_div;
   g1.B = wg; g1.B2 = wu; g1.ldb = D; g1.b_group_stride = w_stride_up;
@@ -263,10 +265,10 @@ static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda,
     if (mid && hipEventRecord(mid, stream) != hipSuccess) return MOE_ERR_HIP;
     return launch_gemm_f32(g2, grp, EPI_STORE, stream);
   }
-  st = launch_gemm_bf16(g1, grp, EPI_SWIGLU, stream);
+  st = launch_gemm_bf16(g1, grp, EPI_SWIGLU, stream, pc);
   if (st) return st;
   if (mid && hipEventRecord(mid, stream) != hipSuccess) return MOE_ERR_HIP;
-  return launch_gemm_bf16(g2, grp, EPI_STORE, stream);
+  return launch_gemm_bf16(g2, grp, EPI_STORE, stream, pc);
 }
 
 }  // extern "C"
@@ -289,6 +291,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   const bool mx = p->dtype == MOE_MXFP8;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
+  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // the chunked ring holds dispatched copies; with the gather fused into GEMM1 there are none
   if (p->chunk_rows > 0 && ((p->flags & MOE_FLAG_FUSED_GATHER) || p->dtype == MOE_F32)) return MOE_ERR_UNSUPPORTED;
   WsLayout L = ws_layout(*p);
@@ -300,6 +303,16 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   const int64_t n = (int64_t)p->T * p->K;
   void* yr = y_routes ? y_routes : (void*)(wsb + L.y_routes);
   void* sho = p->I_shared > 0 ? (shared_out ? shared_out : (void*)(wsb + L.sh_out)) : nullptr;
+  // persistent GEMMs (BF16): ticket counters and the workgroup budget word in the error word's
+  // block; taken where a launch has enough tiles per workgroup, always with the flag
+  Persist pcs;
+  const Persist* pc = nullptr;
+  if (p->dtype == MOE_BF16) {
+    pcs.tickets = (int32_t*)(wsb + L.err + kTicketsOffset);
+    pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
+    pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)(wsb + L.err + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+    pc = &pcs;
+  }
 
 #define MOE_MARK(i) \
   do { if (ev && hipEventRecord(ev[i], stream) != hipSuccess) return MOE_ERR_HIP; } while (0)
@@ -316,7 +329,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     Grouped gs;
     gs.M = p->T;
     st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
-                    0, 0, wsb + L.sh_h, sho, nullptr, stream);
+                    0, 0, wsb + L.sh_h, sho, nullptr, stream, nullptr, pc);
     if (st) return st;
   }
 
@@ -370,7 +383,8 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
                             gc, EPI_STORE, stream);
       } else {
         st = expert_ffn(p->dtype, gc, xr + shift * xrow, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
-                        p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, stream);
+                        p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, stream,
+                        nullptr, pc);
       }
       if (st) return st;
     }
@@ -433,11 +447,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       GemmArgs g2;
       g2.A = wsb + L.h; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
       g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D; g2.c_scatter = r->perm;
-      if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream))) return st;
+      if ((st = launch_gemm_bf16(g2, gr, EPI_STORE, stream, pc))) return st;
     } else {
       st = expert_ffn(p->dtype, gr, A, p->D, gather, p->K, w->w_gate, w->w_up, w->w_down, p->D, p->I,
                       (int64_t)p->I * p->D, (int64_t)p->D * p->I, wsb + L.h, yr, r->perm, stream,
-                      ev ? ev[MOE_STAGE_DOWN] : nullptr);
+                      ev ? ev[MOE_STAGE_DOWN] : nullptr, pc);
       if (st) return st;
     }
   }

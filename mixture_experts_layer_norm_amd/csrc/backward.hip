@@ -467,7 +467,21 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
   if (sact_a && (!al16(sact_a) || !al16(sact_u) || p->I_shared % 4)) return MOE_ERR_MISALIGNED;
   const bool mx = p->dtype == MOE_MXFP8;
   // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
-  auto gemm = p->dtype == MOE_F32 ? launch_gemm_f32 : launch_gemm_bf16;
+  const bool f32 = p->dtype == MOE_F32;
+  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // BF16: the up/gate and down GEMMs run persistent where they have enough tiles per workgroup
+  // (always with MOE_FLAG_PERSISTENT_GEMM), their ticket counters in the workspace's first block
+  Persist pcs;
+  const Persist* pc = nullptr;
+  if (p->dtype == MOE_BF16 && ws) {
+    pcs.tickets = (int32_t*)((char*)ws + kTicketsOffset);
+    pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
+    pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)((char*)ws + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+    pc = &pcs;
+  }
+  auto gemm = [f32, pc](const GemmArgs& a, const Grouped& g, Epi e, hipStream_t s) {
+    return f32 ? launch_gemm_f32(a, g, e, s) : launch_gemm_bf16(a, g, e, s, pc);
+  };
   if (!x_slot || !offsets || !w || !y_slot || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (slots < 0 || slots > (int64_t)p->T * p->K) return MOE_ERR_INVALID_ARG;

@@ -37,6 +37,9 @@ __device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __ex
 constexpr int kRouteRowsPerBlock = 2048;     // schedule: routes per histogram block
 constexpr int kGemmBM = 256;                 // rows per grouped-GEMM m-tile
 constexpr int kErrOffset = 0;                // sticky error word (int32)
+// Byte offset, inside the error word's 256-byte block at the start of the forward workspace, of the
+// persistent GEMMs' 8 ticket counters (the workgroup budget word sits at MOE_WS_CU_BUDGET_OFFSET).
+constexpr size_t kTicketsOffset = 64;
 
 struct WsLayout {
   size_t err;              // int32 error word
@@ -165,7 +168,18 @@ struct GemmArgs {
   int32_t c_accumulate = 0;           // fp32 outputs of the MXFP8 GEMM: C += product
 };
 
-int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s);
+// Persistent launch of the forward grouped GEMMs (gemm.hip): tickets, 8 int32 counters in device
+// memory (zeroed by the launch); budget, the workgroup budget word (nullable, read only); force:
+// always persistent, otherwise only where the launch holds at least kPersistMinTilesPerWg tiles
+// per workgroup (its upper bound of tiles, known on the host).
+struct Persist {
+  int32_t* tickets = nullptr;
+  const int32_t* budget = nullptr;
+  bool force = false;
+};
+constexpr int kPersistMinTilesPerWg = 12;
+// pc: run EPI_SWIGLU / EPI_STORE as the persistent kernel (other epilogues ignore it).
+int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s, const Persist* pc = nullptr);
 int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s);
 int gemm_tile_cols(Epi epi);
 int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,

@@ -78,7 +78,8 @@ __device__ __forceinline__ bool locate_tile(const Grouped& g, int mt, TileCoord&
 // binary search whose ~log2(groups) dependent loads would sit in front of every tile's first
 // K slice. Wave-uniform result.
 __device__ __forceinline__ int find_group(const int32_t* __restrict__ off, int groups, int q) {
-  const int lane = threadIdx.x & 63;
+  // lane id from the lane count, so that no caller keeps the thread index register live for it
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int step = (groups + 63) >> 6;
   const int i1 = lane * step;
   const bool p1 = i1 < groups && off[i1] <= q;
@@ -257,13 +258,17 @@ __device__ __forceinline__ void k_loop(const StageSrc<NL>& src, uint8_t* sm, int
 // K slices [k0, k0 + 32 nk) (times two with a.two_pass). smem holds kGemmSmemElems bf16.
 template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc, int k0, int nk, int ntn,
-                                          uint16_t* smem) {
+                                          uint16_t* smem, int tid_in = -1) {
   using C = SliceCfg<BKE>;
   constexpr int WM = 128, BN = WAVES_N * WN;
   constexpr int NWAVES = 2 * WAVES_N, NL = BM / (C::RPI * NWAVES);   // wavefronts; loads per operand per slice
   constexpr int MI = WM / 32, NJ = WN / 32;
   static_assert(BN == BM, "A and B stages have the same row count");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // tid_in: the thread index as the caller holds it (a persistent caller passes one the compiler
+  // cannot see as loop-invariant, so that the tile's lane-dependent addresses are not hoisted out
+  // of its tile loop and kept live across the K loop)
+  const int tid = tid_in >= 0 ? tid_in : (int)threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: per-wave bases stay in SGPRs
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   uint8_t* sm = reinterpret_cast<uint8_t*>(smem);
 

@@ -151,7 +151,7 @@ def test_removed_flag_bits_and_chunk_refusals_without_gpu():
     import mixture_experts_layer_norm_amd as m
     lib = m._lib
     n = ctypes.c_size_t()
-    for bit in (0x2, 0x8, 0x10, 0x20, 0x100, 0x8000, 0x10000):
+    for bit in (0x2, 0x8, 0x10, 0x20, 0x100, 0x8000, 0x40000):
         p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, bit)
         assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1, hex(bit)
     fake = 1 << 20
@@ -171,6 +171,32 @@ def test_removed_flag_bits_and_chunk_refusals_without_gpu():
     p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 512, 3)
     assert lib.moe_forward_keep(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None,
                                 fake, fake, fake, 1 << 40, None) == -2
+
+
+def test_persistent_gemm_flags_without_gpu():
+    """MOE_FLAG_CU_BUDGET needs MOE_FLAG_PERSISTENT_GEMM (invalid alone); the persistent GEMMs are
+    BF16 only (MOE_F32, MOE_MXFP8: unsupported); checked on the host before any launch. The
+    budget word sits inside the first 256 bytes of the forward workspace, with the error word."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    n = ctypes.c_size_t()
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_CU_BUDGET)
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET)
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value >= 256
+    assert 4 <= m.MOE_WS_CU_BUDGET_OFFSET and m.MOE_WS_CU_BUDGET_OFFSET + 4 <= 64
+    fake = 1 << 20
+    w, r = m.Weights(), m.Routing()
+    for f in ('w_gate', 'w_up', 'w_down', 'sc_gate', 'sc_up', 'sc_down'):
+        setattr(w, f, fake)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, fake)
+    for dt in ('f32', 'mxfp8'):
+        p = m.problem(64, 128, 128, 8, 2, 0, dt, 0, 0, m.MOE_FLAG_PERSISTENT_GEMM)
+        assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
+                               1 << 40, None) == -2, dt
+        assert lib.moe_experts_forward(ctypes.byref(p), 64, fake, fake, ctypes.byref(w), fake, None, None, fake,
+                                       1 << 40, None) == -2, dt
 
 
 def test_layer_keep_entry_points_reject_without_gpu():
