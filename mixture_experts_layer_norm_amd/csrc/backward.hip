@@ -139,6 +139,7 @@ struct CoreBufs {
   // MXFP8 codes and scales of the weight gradients' second pass: [da | du] and g*h low halves,
   // x and dy, each [features][Spad] along the slots (all null: both passes in BF16)
   uint8_t *q_dau, *s_dau, *q_gh, *s_gh, *q_x, *s_x, *q_dy, *s_dy;
+  const Persist* pc = nullptr;   // persistent GEMM control (BF16), see launch_gemm_bf16
 };
 
 // Backward of one set of groups (routed experts, or the shared expert as one group).
@@ -167,7 +168,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
     GemmArgs r;
     r.A = x_rows; r.lda = D; r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
     r.N = I; r.K = D; r.C = b.act_a; r.C2 = b.act_u; r.ldc = I;
-    if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s))) return st;
+    if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s, b.pc))) return st;
   }
 
   // dgrad-down + SwiGLU backward: dh' = dy W_down; da, du (as bf16 hi/lo pairs); partial <h, dh'>
@@ -176,7 +177,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   d.N = I; d.K = D; d.C = b.dau; d.C2 = (uint16_t*)b.dau + I; d.ldc = 4 * I; d.lo_off = 2 * I;
   d.ea = (const float*)b.act_a; d.eu = (const float*)b.act_u; d.lde = I;
   d.row_scale = g_rows; d.row_partial = b.part;
-  if ((st = launch_gemm_bf16(d, grp, EPI_DGRAD, s))) return st;
+  if ((st = launch_gemm_bf16(d, grp, EPI_DGRAD, s, b.pc))) return st;
   const int ntn_d = (I + gemm_tile_cols(EPI_DGRAD) - 1) / gemm_tile_cols(EPI_DGRAD);
   if (dg_rows && (st = launch_row_sum(b.part, n_cap, ntn_d, dg_rows, s))) return st;
 
@@ -185,7 +186,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   u.A = b.dau; u.lda = 4 * I; u.B = b.wguT; u.ldb = 2 * I; u.b_group_stride = (int64_t)D * 2 * I;
   u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
   if (!dgrad_one_pass) { u.two_pass = 1; u.a_seg_shift = 2 * I; }   // high halves, then low halves
-  if ((st = launch_gemm_bf16(u, grp, EPI_STORE, s))) return st;
+  if ((st = launch_gemm_bf16(u, grp, EPI_STORE, s, b.pc))) return st;
 
   // padded transposes for the weight gradients: x and dy exact; g*h and [da|du] as hi/lo rows
   const int64_t Sp = b.Spad;
@@ -205,12 +206,12 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
     w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
     w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I;
     w1.two_pass = 1; w1.b_seg_shift = (int64_t)I * Sp; w1.k_order = order;
-    if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
+    if ((st = launch_gemm_bf16_kgroup(w1, G, s, b.pc))) return st;
     GemmArgs w2;   // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
     w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
     w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D;
     w2.two_pass = 1; w2.a_seg_shift = (int64_t)2 * I * Sp; w2.k_order = order;
-    return launch_gemm_bf16_kgroup(w2, G, s);
+    return launch_gemm_bf16_kgroup(w2, G, s, b.pc);
   }
   // MOE_FLAG_BWD_WGRAD_LO_MXFP8 on long groups: the high halves in BF16, then the low halves in
   // MXFP8 added into the same fp32 outputs. A low half is below 2^-8 of its value, so the E4M3 rounding of the second pass (its
@@ -225,7 +226,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   GemmArgs w1;
   w1.A = b.dyT; w1.lda = Sp; w1.B = b.ghT; w1.ldb = Sp; w1.k_off = poff; w1.M = D; w1.N = I;
   w1.C = dw_down; w1.ldc = I; w1.c_group_stride = (int64_t)D * I; w1.k_order = order;
-  if ((st = launch_gemm_bf16_kgroup(w1, G, s))) return st;
+  if ((st = launch_gemm_bf16_kgroup(w1, G, s, b.pc))) return st;
   GemmArgs m1 = w1;
   m1.A = b.q_dy; m1.B = b.q_gh; m1.c_accumulate = 1;
   if ((st = launch_gemm_mx_kgroup(m1, b.s_dy, b.s_gh, G, s))) return st;
@@ -233,7 +234,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   GemmArgs w2;
   w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
   w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = (int64_t)I * D; w2.k_order = order;
-  if ((st = launch_gemm_bf16_kgroup(w2, G, s))) return st;
+  if ((st = launch_gemm_bf16_kgroup(w2, G, s, b.pc))) return st;
   GemmArgs m2 = w2;
   m2.A = b.q_dau; m2.B = b.q_x; m2.c_accumulate = 1;
   return launch_gemm_mx_kgroup(m2, b.s_dau, b.s_x, G, s);
@@ -336,6 +337,16 @@ static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
                   u(L.sls_dy)};
 }
 
+// Persistent GEMM control of a backward call (BF16 GEMMs): the ticket counters and the budget word
+// sit in the first block of the backward workspace, as in the forward's.
+static Persist bwd_persist(const moe_problem* p, char* wsb, const BwdLayout& L) {
+  Persist pc;
+  pc.tickets = (int32_t*)(wsb + L.err + kTicketsOffset);
+  pc.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
+  pc.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)(wsb + L.err + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+  return pc;
+}
+
 // one group of T rows for the shared expert: offsets {0, T}
 __global__ void single_group_kernel(int rows, int32_t* offs) {
   offs[0] = 0;
@@ -359,6 +370,8 @@ static int shared_backward(const moe_problem* p, const void* x, const void* dy, 
                                (int32_t*)(wsb + L.err), s, L.pad_s);
   if (st) return st;
   CoreBufs cb = shared_bufs(wsb, L);
+  const Persist pc = bwd_persist(p, wsb, L);
+  cb.pc = &pc;
   if (kept_a) {
     cb.act_a = const_cast<float*>(kept_a);   // read only from here on
     cb.act_u = const_cast<float*>(kept_u);
@@ -628,6 +641,8 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);
+    const Persist pc = bwd_persist(p, wsb, L);
+    cb.pc = &pc;
     if (kept) {
       cb.act_a = const_cast<float*>(act_a);   // read only from here on
       cb.act_u = const_cast<float*>(act_u);
@@ -727,6 +742,8 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);
+    const Persist pc = bwd_persist(p, wsb, L);
+    cb.pc = &pc;
     if (kept) {
       cb.act_a = const_cast<float*>(act_a);   // read only from here on
       cb.act_u = const_cast<float*>(act_u);

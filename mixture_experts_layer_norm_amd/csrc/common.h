@@ -178,9 +178,9 @@ struct Persist {
   bool force = false;
 };
 constexpr int kPersistMinTilesPerWg = 12;
-// pc: run EPI_SWIGLU / EPI_STORE as the persistent kernel (other epilogues ignore it).
+// pc: may run as the persistent kernel (see Persist).
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s, const Persist* pc = nullptr);
-int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s);
+int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s, const Persist* pc = nullptr);
 int gemm_tile_cols(Epi epi);
 int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,
                         hipStream_t s);

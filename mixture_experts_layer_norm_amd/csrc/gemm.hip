@@ -69,12 +69,13 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
   gemm_tile<EPI, KG, WN, WAVES_N, BKE>(a, tc, k0, nk, ntn, smem);
 }
 
-// Persistent form of the forward grouped GEMMs (up/gate + SwiGLU, down + scatter): one workgroup
-// per CU loops over tiles instead of one workgroup per tile. The tiles and their order are those
-// of gemm_bf16_kernel (the same contiguous range per XCD), but a workgroup takes them from a
-// ticket counter per XCD range, starting with its own XCD's range (workgroups are placed
-// round-robin over the 8 XCDs) and moving on to the other ranges once that one is used up, so
-// the XCDs that finish early take over the rest. Workgroups never wait for one another: the only
+// Persistent form of the grouped GEMMs (every epilogue; grouped, dense and K-grouped tiles): one
+// workgroup per CU loops over tiles instead of one workgroup per tile. The tiles and their order
+// are those of gemm_bf16_kernel, but a workgroup takes them from ticket counters: for grouped and
+// dense tiles one per XCD range, starting with its own XCD's range (workgroups are placed
+// round-robin over the 8 XCDs) and moving on to the other ranges once that one is used up, so the
+// XCDs that finish early take over the rest; for K-grouped tiles one counter over the dealing
+// order (longest groups first). Workgroups never wait for one another: the only
 // shared state is the counters, and each tile is computed by exactly one workgroup with the
 // same summation order as the per-tile launch, so the results are bitwise those of
 // gemm_bf16_kernel whatever the grid and the timing.
@@ -83,26 +84,30 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
 // persistent kernel hands processors back to another stream's work). While it holds v > 0,
 // workgroups with index >= v take no further tile and exit once their current tile is done;
 // the others go on until every tile is taken. The library reads the word and never writes it.
-template <int EPI, int WN, int WAVES_N, int BKE>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(GemmArgs a, Grouped g, int ntn,
                                                                                   int mtn, int32_t* tickets,
                                                                                   const int32_t* budget) {
-  static_assert(EPI == EPI_SWIGLU || EPI == EPI_STORE, "forward epilogues only");
+  static_assert(!(KG && EPI != EPI_STORE), "K-grouped tiles store fp32 weight gradients");
   constexpr int BK = SliceCfg<BKE>::BK;
-  // The two control words live past the operand staging in the same LDS array: as separate
-  // __shared__ objects their presence made the compiler guard every fragment read with a wait for
-  // all outstanding LDS-direct copies (it could not tell them apart), which serialised each K
-  // slice's loads with its MFMAs.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems + 8];
-  int& s_next = *reinterpret_cast<int*>(smem + kGemmSmemElems);
-  int& s_probe = *reinterpret_cast<int*>(smem + kGemmSmemElems + 2);
-  const int valid = (g.row_off ? g.tile_off[g.groups] : mtn) * ntn;
-  const int per_xcd = (valid + 7) >> 3;
-  const int home = blockIdx.x & 7;
+  // The two control words live past the operand staging (and EPI_DGRAD's row partials) in the
+  // same LDS array: as separate __shared__ objects their presence made the compiler guard every
+  // fragment read with a wait for all outstanding LDS-direct copies (it could not tell them
+  // apart), which serialised each K slice's loads with its MFMAs.
+  constexpr int kExtra = EPI == EPI_DGRAD ? 2 * BM * WAVES_N : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems + kExtra + 8];
+  int& s_next = *reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra);
+  int& s_probe = *reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra + 2);
+  // K-grouped: every (group, m-tile, n-tile) in launch order (longest groups first), one counter;
+  // grouped / dense: the XCD ranges of gemm_bf16_kernel, one counter each
+  const int valid = KG ? g.groups * mtn * ntn : (g.row_off ? g.tile_off[g.groups] : mtn) * ntn;
+  const int per_xcd = KG ? valid : (valid + 7) >> 3;
+  const int nrange = KG ? 1 : 8;
+  const int home = KG ? 0 : (int)(blockIdx.x & 7);
   // The loop keeps no per-lane value live across a tile (the tile itself uses the whole register
   // budget): the thread index is rebuilt per tile from the lane count and the wavefront's scalar
-  // index, and thread 0's position in the XCD ranges (home, home + 1, ... found used up) is kept
-  // in LDS.
+  // index, and thread 0's position in the ranges (home, home + 1, ... found used up) is kept in
+  // LDS.
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   auto thread_index = [&]() -> int {
     int t = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
     }
     int probe = s_probe;
     int got = -1;
-    for (; probe < 8; ++probe) {
+    for (; probe < nrange; ++probe) {
       const int x = (home + probe) & 7;
       const int lo = x * per_xcd, cnt = min(per_xcd, valid - lo);
       if (cnt <= 0) continue;
@@ -139,13 +144,29 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
     // A per-tile copy of the arguments the tile reads, opaque like the thread index, so that
     // nothing the tile derives from them is hoisted out of the loop and held across the K loop.
     GemmArgs la = a;
-    asm volatile("" : "+s"(la.A), "+s"(la.B), "+s"(la.B2), "+s"(la.C), "+s"(la.a_gather), "+s"(la.c_scatter));
+    asm volatile("" : "+s"(la.A), "+s"(la.B), "+s"(la.B2), "+s"(la.C), "+s"(la.C2), "+s"(la.a_gather),
+                 "+s"(la.c_scatter));
     asm volatile("" : "+s"(la.lda), "+s"(la.ldb), "+s"(la.ldc), "+s"(la.b_group_stride), "+s"(la.a_seg_shift),
                  "+s"(la.b_seg_shift));
     asm volatile("" : "+s"(la.N), "+s"(la.K), "+s"(la.a_div), "+s"(la.c_f32), "+s"(la.two_pass));
     TileCoord tc;
-    if (decode_grouped_tile(g, cur, ntn, mtn, tc))
-      gemm_tile<EPI, false, WN, WAVES_N, BKE>(la, tc, 0, la.K / BK, ntn, smem, thread_index());
+    int k0 = 0, nk = la.K / BK;
+    bool ok = true;
+    if (KG) {
+      // as gemm_bf16_kernel: tile `cur` of the groups in dealing order
+      const int per = mtn * ntn;
+      const int rank = cur / per;
+      tc.grp = la.k_order ? la.k_order[rank] : rank;
+      const int rem = cur - rank * per;
+      tc.nt = rem % ntn;
+      tc.r0 = (rem / ntn) * BM;
+      tc.rows = min(BM, la.M - tc.r0);
+      k0 = la.k_off[tc.grp];
+      nk = (la.k_off[tc.grp + 1] - k0) / BK;
+    } else {
+      ok = decode_grouped_tile(g, cur, ntn, mtn, tc);
+    }
+    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE>(la, tc, k0, nk, ntn, smem, thread_index());
     // every thread is past its read of s_next (the tile's barriers) and, after the barrier
     // below, past the epilogue's LDS reads that the next tile's copies overwrite
     if (thread_index() == 0) s_next = take();
@@ -173,6 +194,26 @@ constexpr int kTileCols = 4 * kWN;
 
 int gemm_tile_cols(Epi epi) { return (epi == EPI_SWIGLU || epi == EPI_SAVE_AU) ? kTileCols / 2 : kTileCols; }
 
+// Grid of the persistent form for a launch of at most nb tiles, or nw = 0 for the per-tile form:
+// one workgroup per CU (a multiple of 8, so that every XCD holds the same number), at most one
+// per possible tile, taken when forced or when the launch has at least kPersistMinTilesPerWg
+// tiles per workgroup. Measured on the DSV3 forward (T=8192, 256 experts: at most 32 and 56
+// tiles per workgroup) the persistent form is 5% faster than the per-tile launch, and on one
+// expert-parallel rank's share (14 and 25) faster too; at the mid shape (6 and 8) 3% slower, the
+// counters' zeroing launch and each tile's ticket costing more than the workgroup launches they
+// replace.
+static int persistent_grid(int64_t nb, const Persist* pc, int64_t& nw) {
+  nw = 0;
+  if (!pc || !pc->tickets) return MOE_OK;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOE_ERR_HIP;
+  int64_t w = (int64_t)(ncu > 8 ? ncu : 8) / 8 * 8;
+  if (w > nb) w = nb;
+  if (pc->force || nb >= (int64_t)kPersistMinTilesPerWg * w) nw = w;
+  return MOE_OK;
+}
+
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s, const Persist* pc) {
   const int tcols = gemm_tile_cols(epi);
   const int ntn = (a.N + tcols - 1) / tcols;
@@ -181,32 +222,21 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   const int mtn = g.row_off ? 0 : (int)mt;   // dense mode: the exact m-tile count
-  if (pc && pc->tickets && (epi == EPI_SWIGLU || epi == EPI_STORE)) {
-    // one workgroup per CU (a multiple of 8, so that every XCD holds the same number), at most
-    // one per possible tile
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return MOE_ERR_HIP;
-    int64_t nw = (int64_t)(ncu > 8 ? ncu : 8) / 8 * 8;
-    if (nw > nb) nw = nb;
-    // Unforced, only launches with at least kPersistMinTilesPerWg tiles per workgroup (upper
-    // bound) run persistent. Measured on the DSV3 forward (T=8192, 256 experts: at most 32 and 56
-    // tiles per workgroup) the persistent form is 5% faster than the per-tile launch, and on one
-    // expert-parallel rank's share (14 and 25) faster too; at the mid shape (6 and 8) 3% slower,
-    // the counters' zeroing launch and each tile's ticket costing more than the workgroup
-    // launches they replace.
-    if (pc->force || nb >= (int64_t)kPersistMinTilesPerWg * nw) {
-      hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
-      MOE_LAUNCH_CHECK();
-      if (epi == EPI_SWIGLU)
-        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, kWN, 4, 64>), dim3((unsigned)nw), dim3(512), 0, s,
-                           a, g, ntn, mtn, pc->tickets, pc->budget);
-      else
-        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, kWN, 4, 64>), dim3((unsigned)nw), dim3(512), 0, s,
-                           a, g, ntn, mtn, pc->tickets, pc->budget);
-      MOE_LAUNCH_CHECK();
-      return MOE_OK;
+  int64_t nw = 0;
+  int st;
+  if ((st = persistent_grid(nb, pc, nw))) return st;
+  if (nw > 0) {
+    hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
+    MOE_LAUNCH_CHECK();
+    const dim3 pg((unsigned)nw), pb(512);
+    switch (epi) {
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
     }
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
   }
   dim3 grid((unsigned)nb), block(512);
   switch (epi) {
@@ -221,12 +251,23 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
 
 // Weight-gradient GEMM: for each group, C_g[M][N] = sum over k in the group's range of
 // A[m][k] * B[n][k], written once (fp32), with no split-K and no atomics.
-int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s) {
+int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s, const Persist* pc) {
   const int ntn = (a.N + kTileCols - 1) / kTileCols, mtn = (a.M + BM - 1) / BM;
   Grouped g;
   g.groups = groups;
   const int64_t nb = grid_blocks((int64_t)groups * mtn, ntn);
   if (nb == 0) return MOE_OK;
+  int64_t nw = 0;
+  int st;
+  if ((st = persistent_grid(nb, pc, nw))) return st;
+  if (nw > 0) {
+    hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
+    MOE_LAUNCH_CHECK();
+    hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, true, kWN, 4, 64>), dim3((unsigned)nw), dim3(512), 0, s,
+                       a, g, ntn, mtn, pc->tickets, pc->budget);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, true, kWN, 4, 64>), dim3((unsigned)nb), dim3(512), 0, s, a, g, ntn, mtn);
   MOE_LAUNCH_CHECK();
   return MOE_OK;

@@ -169,3 +169,34 @@ def test_persistent_gemm_experts_forward(m, budget):
         assert int(ws[:4].view(torch.int32).item()) == 0
         outs.append((y, sh))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize('cfg,budget', [(SMALL_BF16, None), (SMALL_BF16, 3), (NOSHARED_BF16, None)],
+                         ids=['small', 'small_budget3', 'noshared'])
+def test_persistent_gemm_layer_backward(m, cfg, budget):
+    """moe_backward with forced persistent GEMMs (replay, dgrad-down with the SwiGLU backward,
+    dgrad-up, K-grouped weight gradients; routed and shared): every gradient equals the per-tile
+    backward's bit for bit, also with a budget of 3 workgroups."""
+    print(f'[persistent] layer backward {cfg.name} budget={budget}', flush=True)
+    L = synth.to_device(synth.host_layer(cfg))
+    T, D, I, E, K, Is = cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared
+    rng = np.random.default_rng(3)
+    dout = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).cuda().to(torch.bfloat16)
+    res = []
+    for flags in (0, m.MOE_FLAG_PERSISTENT_GEMM | (m.MOE_FLAG_CU_BUDGET if budget else 0)):
+        run = ForwardRun(m, L, flags=flags)()
+        shapes = ((E, I, D), (E, I, D), (E, D, I)) + (((Is, D), (Is, D), (D, Is)) if Is else ())
+        gr = [torch.full(sh, float('nan'), device='cuda') for sh in shapes]
+        G = m.make_grads(*gr)
+        dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+        dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+        dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+        wsb = torch.zeros((m.backward_workspace_size(run.p),), dtype=torch.uint8, device='cuda')
+        if budget:
+            wsb[m.MOE_WS_CU_BUDGET_OFFSET:m.MOE_WS_CU_BUDGET_OFFSET + 4].view(torch.int32).fill_(budget)
+        m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, wsb)
+        torch.cuda.synchronize()
+        assert int(wsb[:4].view(torch.int32).item()) == 0
+        res.append([dx, dtw, dlg] + gr)
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
