@@ -118,11 +118,14 @@ typedef struct moe_problem {
  * GEMM runs persistent where it has at least 12 tiles per workgroup (e.g. the routed GEMMs at
  * T = 8192, 256 experts, K = 8), per tile otherwise; with it, always. Each tile is computed by one
  * workgroup in the same order either way, so every output is bitwise the same. Workgroups never
- * wait for each other. MOE_F32 and MOE_MXFP8 with the flag: MOE_ERR_UNSUPPORTED. The backward
- * entry points accept the flag and ignore it. */
+ * wait for each other. MOE_F32 and MOE_MXFP8 forwards with the flag: MOE_ERR_UNSUPPORTED. The
+ * backward entry points apply the same rule to their BF16 GEMMs (replay, dgrad-down, dgrad-up,
+ * K-grouped weight gradients; under MOE_MXFP8 the shared expert's), with the counters in their own
+ * workspace's first 256 bytes. */
 #define MOE_FLAG_PERSISTENT_GEMM 0x10000
 /* With MOE_FLAG_PERSISTENT_GEMM (alone: MOE_ERR_INVALID_ARG): between tiles, the persistent GEMMs
- * read the int32 workgroup budget at byte offset MOE_WS_CU_BUDGET_OFFSET of the workspace. While
+ * read the int32 workgroup budget at byte offset MOE_WS_CU_BUDGET_OFFSET of the workspace the call
+ * is given (forward or backward workspace). While
  * it holds v > 0, workgroups with index >= v take no further tile and end after their current
  * one, handing their CUs to other work on the GPU (the Notes' "The production details": the
  * kernel yields processors to a higher-priority stream); the workgroups below v take every
