@@ -164,6 +164,11 @@ struct GemmArgs {
   // second K pass (hi/lo operand splitting): when nonzero, the K range is run twice, the second
   // time with A and B displaced by these element offsets, accumulating into the same tile
   int64_t a_seg_shift = 0, b_seg_shift = 0;
+  // B stored k-major ([K][N] rows, N contiguous; bf16 grouped GEMMs with EPI_STORE / EPI_DGRAD):
+  // the weights as they are, read through transposing LDS reads instead of a transposed copy.
+  // K rows >= b_split (when nonzero) come from B2, row k - b_split.
+  int32_t b_kmajor = 0;
+  int32_t b_split = 0;
   int32_t two_pass = 0;
   int32_t c_accumulate = 0;           // fp32 outputs of the MXFP8 GEMM: C += product
 };

@@ -32,7 +32,7 @@ namespace moe {
 // wavefront owns a 128 x WN block as (128/32) x (WN/32) v_mfma_f32_32x32x16_bf16 accumulators.
 // Row blocks of 32 that lie past the group's last row skip their MFMAs (a wave-uniform branch),
 // so a sparsely filled tile costs only the streaming of its weight tile.
-template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE, bool BT = false>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a, Grouped g, int ntn, int mtn) {
   constexpr int BK = SliceCfg<BKE>::BK;
   // EPI_DGRAD keeps its [BM][WAVES_N] fp32 row partials past the 128 KB of operand staging
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
     nk = a.K / BK;
   }
 
-  gemm_tile<EPI, KG, WN, WAVES_N, BKE>(a, tc, k0, nk, ntn, smem);
+  gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(a, tc, k0, nk, ntn, smem);
 }
 
 // Persistent form of the grouped GEMMs (every epilogue; grouped, dense and K-grouped tiles): one
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
 // persistent kernel hands processors back to another stream's work). While it holds v > 0,
 // workgroups with index >= v take no further tile and exit once their current tile is done;
 // the others go on until every tile is taken. The library reads the word and never writes it.
-template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE, bool BT = false>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(GemmArgs a, Grouped g, int ntn,
                                                                                   int mtn, int32_t* tickets,
                                                                                   const int32_t* budget) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
                  "+s"(la.c_scatter));
     asm volatile("" : "+s"(la.lda), "+s"(la.ldb), "+s"(la.ldc), "+s"(la.b_group_stride), "+s"(la.a_seg_shift),
                  "+s"(la.b_seg_shift));
-    asm volatile("" : "+s"(la.N), "+s"(la.K), "+s"(la.a_div), "+s"(la.c_f32), "+s"(la.two_pass));
+    asm volatile("" : "+s"(la.N), "+s"(la.K), "+s"(la.a_div), "+s"(la.c_f32), "+s"(la.two_pass), "+s"(la.b_split));
     TileCoord tc;
     int k0 = 0, nk = la.K / BK;
     bool ok = true;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
     } else {
       ok = decode_grouped_tile(g, cur, ntn, mtn, tc);
     }
-    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE>(la, tc, k0, nk, ntn, smem, thread_index());
+    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(la, tc, k0, nk, ntn, smem, thread_index());
     // every thread is past its read of s_next (the tile's barriers) and, after the barrier
     // below, past the epilogue's LDS reads that the next tile's copies overwrite
     if (thread_index() == 0) s_next = take();
@@ -222,6 +222,9 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
   if (nb == 0) return MOE_OK;
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   const int mtn = g.row_off ? 0 : (int)mt;   // dense mode: the exact m-tile count
+  if (a.b_kmajor && ((epi != EPI_STORE && epi != EPI_DGRAD) || a.N % 8 || a.ldb % 8 || a.b_seg_shift ||
+                     a.K % 64 || (a.b_split && (a.b_split % 64 || !a.B2))))
+    return MOE_ERR_UNSUPPORTED;
   int64_t nw = 0;
   int st;
   if ((st = persistent_grid(nb, pc, nw))) return st;
@@ -229,16 +232,31 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
     hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
     MOE_LAUNCH_CHECK();
     const dim3 pg((unsigned)nw), pb(512);
-    switch (epi) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-      case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-      case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-      case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+    if (a.b_kmajor) {
+      if (epi == EPI_STORE)
+        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget);
+      else
+        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget);
+    } else {
+      switch (epi) {
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+        case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+        case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+        case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+      }
     }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
   dim3 grid((unsigned)nb), block(512);
+  if (a.b_kmajor) {
+    if (epi == EPI_STORE)
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 64, true>), grid, block, 0, s, a, g, ntn, mtn);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI_DGRAD, false, kWN, 4, 64, true>), grid, block, 0, s, a, g, ntn, mtn);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   switch (epi) {
     case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_SWIGLU, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;
     case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_kernel<EPI_STORE, false, kWN, 4, 64>), grid, block, 0, s, a, g, ntn, mtn); break;

@@ -139,17 +139,39 @@ struct StageSrc {
   int64_t a_shift, b_shift;
   int na;               // A loads issued per slice (2-stage slices skip loads of rows past the tile's end)
   bool b_nt = false;    // weight loads carry the non-temporal cache policy
+  int64_t bk_stride = 0;   // k-major B: elements per K row
+  int b_split = 0;         // k-major B: K rows >= b_split come from bbase[1]
 };
+
+// k-major B tile in LDS: 64 K rows of the tile's 256 N columns (512 bytes per row), 16-byte chunk c
+// of row k stored at position c ^ bt_swz(k), so that one transposing fragment read (4 rows x 16
+// columns per 16 lanes, rows 8 apart for the other half-wave) uses every bank at most twice.
+__device__ __forceinline__ int bt_swz(int k) { return 4 * (k & 3); }
 
 // Issues the 2 NL LDS-direct loads of this thread for K slice kt into LDS stage `stage`: A rows
 // RPI (NL wave + j) .. + RPI - 1 and the same B rows, for j < NL.
-template <int NL, int BKE>
+template <int NL, int BKE, bool BT = false>
 __device__ __forceinline__ void stage_issue(const StageSrc<NL>& s, int kt, uint8_t* smem, int stage, int wave) {
   using C = SliceCfg<BKE>;
   const bool second = kt >= s.nk1;
   const int ko = (second ? kt - s.nk1 : kt) * C::BK;
   const uint16_t* ab = (second ? s.abase + s.a_shift : s.abase) + ko;
   const int64_t bsh = (second ? s.b_shift : 0) + ko;
+  if (BT) {
+    // k-major B: K rows ko .. ko + 63 (from the second matrix past b_split), 2 rows per load
+    uint8_t* base = smem + stage * C::STAGE_BYTES + wave * (NL * 1024);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      if (C::STAGES == 2 && j >= s.na) break;
+      __builtin_amdgcn_global_load_lds((const void*)(ab + s.aoff[j]), (lds_void*)(base + j * 1024), 16, 0, 0);
+    }
+    const bool up = s.b_split && ko >= s.b_split;
+    const uint16_t* bk = up ? s.bbase[1] + (int64_t)(ko - s.b_split) * s.bk_stride : s.bbase[0] + (int64_t)ko * s.bk_stride;
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(bk + s.boff[j]), (lds_void*)(base + BM * C::ROWB + j * 1024), 16, 0, 0);
+    return;
+  }
   uint8_t* base = smem + stage * C::STAGE_BYTES + wave * (NL * 1024);
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
@@ -199,6 +221,33 @@ __device__ __forceinline__ void frag_read(const uint8_t* st, int a_rd, int b_rd,
   }
 }
 
+// The same with a k-major B tile: each B fragment (8 consecutive K of one N column) is two
+// transposing reads (ds_read_b64_tr_b16: within each 16 lanes, lane i receives element i, i + 16,
+// i + 32, i + 48 of the 64 the 16 lanes read, so lanes 4 j + b reading 4 columns 4 b .. 4 b + 3
+// of K row j deliver to lane i the 4 K values of column i). b_tr[j]: this lane's byte offset for
+// column block j at K step 0; K step kk adds 16 kk rows, the second read 4 more.
+template <int NACT, int NJ, int BKE>
+__device__ __forceinline__ void frag_read_bt(const uint8_t* st, int a_rd, const int (&b_tr)[NJ], int sw, int half,
+                                             Frags<NACT, NJ, SliceCfg<BKE>::KSTEPS>& f) {
+  using C = SliceCfg<BKE>;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const uint8_t* As = st + a_rd;
+  const uint8_t* Bs = st + BM * C::ROWB;
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    const int c = ((kk * 2 + half) ^ sw) * 16;
+#pragma unroll
+    for (int i = 0; i < NACT; ++i) f.a[kk][i] = *reinterpret_cast<const bf16x8*>(As + i * 32 * C::ROWB + c);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint8_t* p = Bs + b_tr[j] + kk * 16 * 512;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p + 4 * 512));
+      f.b[kk][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
 // MFMAs of one K slice: NACT x NJ blocks of 32 x 32 over the slice's 16-wide K steps.
 template <int MI, int NJ, int NACT, int KS>
 __device__ __forceinline__ void frag_mfma(const Frags<NACT, NJ, KS>& f, f32x16 (&acc)[MI][NJ]) {
@@ -235,19 +284,28 @@ __device__ __forceinline__ void slice_barrier() {
 // of slice kt - 1), the stage of slice kt - 1 is refilled with slice kt + STAGES - 1, then the
 // fragments of slice kt are read and multiplied. NACT (active row blocks of this wave) is a
 // compile-time constant so that the loop has no divergent branches around the MFMAs.
-template <int MI, int NJ, int NACT, int NL, int BKE>
+template <int MI, int NJ, int NACT, int NL, int BKE, bool BT = false>
 __device__ __forceinline__ void k_loop(const StageSrc<NL>& src, uint8_t* sm, int nk, int wave, int a_rd,
-                                       int b_rd, int sw, int half, f32x16 (&acc)[MI][NJ]) {
+                                       int b_rd, int sw, int half, f32x16 (&acc)[MI][NJ], const int (&b_tr)[NJ]) {
   using C = SliceCfg<BKE>;
   constexpr int ST = C::STAGES;
   for (int s = 0; s < ST - 1; ++s)
-    if (s < nk) stage_issue<NL, BKE>(src, s, sm, s, wave);
+    if (s < nk) stage_issue<NL, BKE, BT>(src, s, sm, s, wave);
   for (int kt = 0; kt < nk; ++kt) {
     wait_slices<NL>(min(ST - 2, nk - 1 - kt));
     slice_barrier();
-    if (kt + ST - 1 < nk) stage_issue<NL, BKE>(src, kt + ST - 1, sm, (kt + ST - 1) % ST, wave);
+    if (!BT && kt + ST - 1 < nk) stage_issue<NL, BKE>(src, kt + ST - 1, sm, (kt + ST - 1) % ST, wave);
     Frags<NACT, NJ, C::KSTEPS> f;
-    frag_read<NACT, NJ, BKE>(sm + (kt % ST) * C::STAGE_BYTES, a_rd, b_rd, sw, half, f);
+    if (BT) {
+      // The transposing reads carry no alias information, so the compiler would make them wait
+      // for every outstanding LDS-direct copy, the next slice's included: the next slice's
+      // copies are issued after them instead (they still run under this slice's MFMAs).
+      frag_read_bt<NACT, NJ, BKE>(sm + (kt % ST) * C::STAGE_BYTES, a_rd, b_tr, sw, half, f);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + ST - 1 < nk) stage_issue<NL, BKE, true>(src, kt + ST - 1, sm, (kt + ST - 1) % ST, wave);
+    } else {
+      frag_read<NACT, NJ, BKE>(sm + (kt % ST) * C::STAGE_BYTES, a_rd, b_rd, sw, half, f);
+    }
     // every fragment read of the slice ahead of its MFMAs: one LDS latency per slice
     __builtin_amdgcn_sched_barrier(0);
     frag_mfma<MI, NJ, NACT, C::KSTEPS>(f, acc);
@@ -256,9 +314,10 @@ __device__ __forceinline__ void k_loop(const StageSrc<NL>& src, uint8_t* sm, int
 
 // Computes one workgroup tile: rows tc.r0 .. tc.r0 + tc.rows - 1 of group tc.grp, n-tile tc.nt,
 // K slices [k0, k0 + 32 nk) (times two with a.two_pass). smem holds kGemmSmemElems bf16.
-template <int EPI, bool KG, int WN, int WAVES_N, int BKE>
+template <int EPI, bool KG, int WN, int WAVES_N, int BKE, bool BT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc, int k0, int nk, int ntn,
                                           uint16_t* smem, int tid_in = -1) {
+  static_assert(!BT || ((EPI == EPI_STORE || EPI == EPI_DGRAD) && !KG), "k-major B: grouped dgrad GEMMs");
   using C = SliceCfg<BKE>;
   constexpr int WM = 128, BN = WAVES_N * WN;
   constexpr int NWAVES = 2 * WAVES_N, NL = BM / (C::RPI * NWAVES);   // wavefronts; loads per operand per slice
@@ -280,6 +339,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   src.bbase[1] = (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU)
                      ? (const uint16_t*)a.B2 + (int64_t)tc.grp * a.b_group_stride + k0
                      : src.bbase[0];
+  if (BT) {
+    // k-major B: K rows of the group's matrix (rows >= b_split from the second one)
+    src.bbase[0] = (const uint16_t*)a.B + (int64_t)tc.grp * a.b_group_stride;
+    src.bbase[1] = a.B2 ? (const uint16_t*)a.B2 + (int64_t)tc.grp * a.b_group_stride : src.bbase[0];
+    src.bk_stride = a.ldb;
+    src.b_split = a.b_split;
+  }
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;
@@ -299,6 +365,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
     }
     wrow = wrow < a.N ? wrow : a.N - 1;          // partial last n-tile: clamp, results unused
     src.boff[j] = (uint32_t)(wrow * a.ldb + ch * 8);
+    if (BT) {
+      // K row kr of the slice, position lane % 32 of its 32 chunks holding chunk c = position ^ swz
+      // (N columns 8 c .. 8 c + 7 of the tile; past N clamped, results unused)
+      const int kr = 2 * (NL * wave + j) + (lane >> 5);
+      const int c = (lane & 31) ^ bt_swz(kr);
+      int64_t n = (int64_t)tc.nt * BN + 8 * c;
+      n = n < a.N - 8 ? n : a.N - 8;
+      src.boff[j] = (uint32_t)(kr * a.ldb + n);
+    }
   }
   // K slice kt < nk1 reads the first pass, kt >= nk1 the second (operands shifted by the split offsets)
   src.nk1 = nk;
@@ -328,6 +403,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   const int a_rd = (wm * WM + (lane & 31)) * C::ROWB;
   const int b_rd = (wn * WN + (lane & 31)) * C::ROWB;
   const int sw = C::swz(lane & 31), half = lane >> 5;
+  // k-major B: this lane's transposing-read offsets per column block (16-lane group g reads K rows
+  // 8 (g / 2) + (lane % 16) / 4 and columns 16 (g % 2) + 4 (lane % 4) of the block)
+  int b_tr[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int g = (lane >> 4) & 3, sl = lane & 15;
+    const int kr = 8 * (g >> 1) + (sl >> 2);
+    const int ncol = wn * WN + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
+    b_tr[j] = BT ? kr * 512 + ((((ncol >> 3) ^ bt_swz(kr))) << 4) + (ncol & 7) * 2 : 0;
+  }
 
   static_assert(4 * NL <= 63, "vmcnt range");
   // wave-uniform count of this wave's row blocks that hold a valid row
@@ -335,11 +420,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
   const int nact = wrows_u <= 0 ? 0 : min(MI, (wrows_u + 31) / 32);
   static_assert(MI == 4, "row-block dispatch below assumes 4 row blocks per wave");
   switch (nact) {
-    case 0: k_loop<MI, NJ, 0, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 1: k_loop<MI, NJ, 1, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 2: k_loop<MI, NJ, 2, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    case 3: k_loop<MI, NJ, 3, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
-    default: k_loop<MI, NJ, 4, NL, BKE>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc); break;
+    case 0: k_loop<MI, NJ, 0, NL, BKE, BT>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc, b_tr); break;
+    case 1: k_loop<MI, NJ, 1, NL, BKE, BT>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc, b_tr); break;
+    case 2: k_loop<MI, NJ, 2, NL, BKE, BT>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc, b_tr); break;
+    case 3: k_loop<MI, NJ, 3, NL, BKE, BT>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc, b_tr); break;
+    default: k_loop<MI, NJ, 4, NL, BKE, BT>(src, sm, nk, wave, a_rd, b_rd, sw, half, acc, b_tr); break;
   }
   __syncthreads();
 
