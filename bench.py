@@ -121,6 +121,9 @@ def main():
     ap.add_argument('--no-extra', action='store_true',
                     help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
+    ap.add_argument('--ring-stages', type=int, default=0, help='ring depth of the chunked path (0: 3)')
+    ap.add_argument('--lanes', type=int, default=0,
+                    help='extra streams for the chunked forward (moe_forward_lanes); 0: moe_forward')
     ap.add_argument('--flags', type=int, default=0)
     ap.add_argument('--keep-activations', action='store_true',
                     help='ep_share workloads: hand a, u from the forward to the backward instead of replaying')
@@ -146,15 +149,22 @@ def main():
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
-    F = make_forward(cfg, args.chunk_rows, args.flags)
+    F = make_forward(cfg, args.chunk_rows, args.flags, args.ring_stages)
     L, p, weights, routing_t, routing, out, ws = F['L'], F['p'], F['weights'], F['routing_t'], F['routing'], F['out'], F['ws']
     T, D, K = cfg.T, cfg.D, cfg.K
     dev = 'cuda'
     stream = torch.cuda.current_stream()
     nst = len(moe.STAGES)
 
+    lane_streams = [torch.cuda.Stream() for _ in range(args.lanes)]
+    lane_events = [torch.cuda.Event() for _ in range(moe.lane_event_count(p, args.lanes) if args.lanes else 0)]
+    for e in lane_events:
+        e.record(stream)          # creates the HIP event
+
     def step(events=None):
-        if events is None:
+        if events is None and args.lanes:
+            moe.forward_lanes(p, L.x, L.logits, weights, out, routing, ws, lane_streams, lane_events, stream=stream)
+        elif events is None:
             moe.forward(p, L.x, L.logits, weights, out, routing, ws, stream=stream)
         else:
             moe.forward_stages(p, L.x, L.logits, weights, out, routing, ws, events, stream=stream)
@@ -289,7 +299,7 @@ def main():
         'data': 'synthetic',
         'config': {'workload': f'{cfg.name} forward', 'T': T, 'D': cfg.D, 'I': cfg.I, 'E': cfg.E, 'K': K,
                    'I_shared': cfg.I_shared, 'router': cfg.router, 'chunk_rows': args.chunk_rows,
-                   'flags': args.flags},
+                   'ring_stages': args.ring_stages, 'lanes': args.lanes, 'flags': args.flags},
         'tflops': tflops,
         'mfma_peak_frac': tflops / peak,
         'stages_ms': stage_ms,
@@ -678,7 +688,7 @@ def calib_copy():
     del src, dst
 
 
-def make_forward(cfg, chunk_rows=0, flags=0):
+def make_forward(cfg, chunk_rows=0, flags=0, ring_stages=0):
     """Inputs of one moe_forward of configuration `cfg` generated on the device (seeded), with the
     routing state, output and workspace buffers; under MXFP8 the routed weights quantised on the
     device (E4M3 + E8M0 per 32 along K; the shared expert stays BF16)."""
@@ -699,7 +709,7 @@ def make_forward(cfg, chunk_rows=0, flags=0):
             moe.quantize_mx(wbf, q, sc)
             mx[k] = (q, sc)
         torch.cuda.synchronize()
-    p = moe.problem(T, D, cfg.I, E, K, cfg.I_shared, cfg.dtype, chunk_rows, 0, flags)
+    p = moe.problem(T, D, cfg.I, E, K, cfg.I_shared, cfg.dtype, chunk_rows, ring_stages, flags)
     routing_t = dict(topk_idx=torch.empty((T, K), dtype=torch.int32, device=dev),
                      topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
                      counts=torch.empty((E,), dtype=torch.int32, device=dev),

@@ -306,6 +306,39 @@ int moe_forward(const moe_problem *p, const void *x, const float *logits, const 
                 void *out, const moe_routing *routing, void *y_routes, void *shared_out,
                 void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Concurrent chunk lanes for the chunked forward (Notes "Mixture-of-Kittens: MoE Megakernel for
+ * NVL72s", section "Granularity as a tunable": small chunks stay cheap only when the work of
+ * several chunks is in flight at once). Lane 0 is the call's `stream`; lanes 1 .. count are the
+ * caller's `streams[0 .. count-1]` (streams of the current device at the default priority; the
+ * library creates none). `events` holds S + 1 + count events created by the caller on the current
+ * device (hipEventCreateWithFlags with hipEventDisableTiming suggested), where S is the
+ * problem's ring depth (ring_stages, 0 meaning 3): events[0 .. S-1] mark ring stages free again,
+ * events[S] forks the lanes from `stream`, events[S+1 ..] join them back. */
+#define MOE_MAX_LANES 4
+typedef struct moe_lanes {
+  int32_t count;          /* extra lanes, 1 .. MOE_MAX_LANES - 1 */
+  hipStream_t *streams;   /* [count] */
+  hipEvent_t *events;     /* [S + 1 + count] */
+} moe_lanes;
+
+/* moe_forward whose routed chunks run on several streams at once. After the routing, the
+ * schedule and the chunk tables (on `stream`), the lanes fork from `stream`; chunk c (dispatch,
+ * up/gate, down) runs on lane c mod (count + 1), and the shared expert first on lane 0. Chunk c
+ * reuses the ring stage of chunk c - S: when that chunk ran on another lane, chunk c's dispatch
+ * waits (hipStreamWaitEvent) for the event recorded after that chunk's down GEMM. The lanes join
+ * `stream` before the combine, so `stream` orders the whole call as for moe_forward: the caller
+ * may synchronise or capture `stream` alone (a graph captured from `stream` takes in the lanes'
+ * work through the fork and join events). Each lane's persistent GEMMs take tiles from ticket
+ * counters of their own in the workspace's first 256 bytes. Outputs are bitwise those of
+ * moe_forward for the same problem: every output tile is the same workgroup sum. With one chunk
+ * (chunk_rows == 0) the lanes only fork and join. Requirements as moe_forward (chunk_rows > 0
+ * under MOE_F32 or MOE_FLAG_FUSED_GATHER: MOE_ERR_UNSUPPORTED); lanes NULL, count outside
+ * [1, MOE_MAX_LANES - 1], or a NULL stream or event: MOE_ERR_INVALID_ARG. Overlapping calls on
+ * the same events or workspace race. */
+int moe_forward_lanes(const moe_problem *p, const void *x, const float *logits, const moe_weights *w,
+                      void *out, const moe_routing *routing, void *y_routes, void *shared_out,
+                      void *ws, size_t ws_bytes, hipStream_t stream, const moe_lanes *lanes);
+
 /* Stage boundaries of the forward, for moe_forward_stages. Event i is recorded on `stream`
  * just before stage i; event MOE_STAGE_COUNT just after the last stage. */
 enum moe_stage {

@@ -32,6 +32,7 @@ MOE_FLAG_BWD_WGRAD_LO_MXFP8 = 0x80
 MOE_FLAG_PERSISTENT_GEMM = 0x10000
 MOE_FLAG_CU_BUDGET = 0x20000
 MOE_WS_CU_BUDGET_OFFSET = 4
+MOE_MAX_LANES = 4
 STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3: 'MOE_ERR_WORKSPACE',
           -4: 'MOE_ERR_MISALIGNED', -5: 'MOE_ERR_HIP'}
 DTYPES = {'f32': MOE_F32, 'bf16': MOE_BF16, 'mxfp8': MOE_MXFP8}
@@ -42,7 +43,8 @@ EXPORTED = ('moe_status_string', 'moe_workspace_size', 'moe_route_topk', 'moe_sc
             'moe_experts_forward_keep', 'moe_experts_backward_kept', 'moe_forward_keep', 'moe_backward_kept',
             'moe_quantize_mx', 'moe_forward_stages', 'moe_backward_workspace_size', 'moe_pull_schedule',
             'moe_pull_schedule_workspace_size', 'moe_route_gemm', 'moe_route_gemm_workspace_size',
-            'moe_backward_kept_workspace_size', 'moe_schedule_noalloc', 'moe_route_gemm_backward')
+            'moe_backward_kept_workspace_size', 'moe_schedule_noalloc', 'moe_route_gemm_backward',
+            'moe_forward_lanes')
 STAGES = ('route', 'schedule', 'shared', 'dispatch', 'up_gate', 'down', 'combine')
 
 
@@ -65,6 +67,11 @@ class Weights(ctypes.Structure):
 
 class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm')]
+
+
+class Lanes(ctypes.Structure):
+    _fields_ = [('count', ctypes.c_int32), ('streams', ctypes.POINTER(ctypes.c_void_p)),
+                ('events', ctypes.POINTER(ctypes.c_void_p))]
 
 
 class Grads(ctypes.Structure):
@@ -110,6 +117,8 @@ _sig = {
     'moe_pull_schedule_workspace_size': (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     'moe_forward_stages': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P,
                                           _P, _P, _sz, _P, _P]),
+    'moe_forward_lanes': (ctypes.c_int, [_PP, _P, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Routing), _P,
+                                         _P, _P, _sz, _P, ctypes.POINTER(Lanes)]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -224,6 +233,31 @@ def forward_stages(p, x, logits, weights: Weights, out, routing: Routing, ws, ev
     _check(_lib.moe_forward_stages(ctypes.byref(p), _ptr(x), _ptr(logits), ctypes.byref(weights), _ptr(out),
                                    ctypes.byref(routing), _ptr(y_routes), _ptr(shared_out), _ptr(ws),
                                    ws.numel() * ws.element_size(), arr, _stream(stream)), 'moe_forward_stages')
+
+
+def lane_event_count(p, lanes):
+    """Events moe_forward_lanes needs with `lanes` extra streams: ring depth + 1 + lanes."""
+    return (p.ring_stages or 3) + 1 + lanes
+
+
+def forward_lanes(p, x, logits, weights: Weights, out, routing: Routing, ws, streams, events, y_routes=None,
+                  shared_out=None, stream=None):
+    """moe_forward with the routed chunks spread over `stream` and the torch streams `streams`
+    (1 .. MOE_MAX_LANES - 1 of them); `events` holds lane_event_count(p, len(streams))
+    torch.cuda.Event objects, each recorded once so that it exists."""
+    sh = [s.cuda_stream for s in streams]
+    ev = [e.cuda_event for e in events]
+    if not all(sh) or not all(ev):
+        raise ValueError('forward_lanes needs created streams and events (record each event once first)')
+    sarr = (ctypes.c_void_p * max(1, len(sh)))(*sh)
+    earr = (ctypes.c_void_p * max(1, len(ev)))(*ev)
+    if len(ev) < lane_event_count(p, len(sh)):
+        raise ValueError(f'forward_lanes needs {lane_event_count(p, len(sh))} events')
+    lanes = Lanes(len(sh), ctypes.cast(sarr, ctypes.POINTER(ctypes.c_void_p)), ctypes.cast(earr, ctypes.POINTER(ctypes.c_void_p)))
+    _check(_lib.moe_forward_lanes(ctypes.byref(p), _ptr(x), _ptr(logits), ctypes.byref(weights), _ptr(out),
+                                  ctypes.byref(routing), _ptr(y_routes), _ptr(shared_out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream), ctypes.byref(lanes)),
+           'moe_forward_lanes')
 
 
 def backward(p, dout, x, logits, weights: Weights, routing: Routing, dx, grads: Grads, d_topk_w, d_logits, ws,

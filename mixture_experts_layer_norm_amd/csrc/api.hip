@@ -277,9 +277,18 @@ static int expert_ffn(int dtype, const Grouped& grp, const void* A, int64_t lda,
 static int forward_impl(const moe_problem* p, const void* x, const float* logits, const moe_weights* w,
                         void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                         size_t ws_bytes, hipEvent_t* ev, hipStream_t stream, float* act_a = nullptr,
-                        float* act_u = nullptr) {
+                        float* act_u = nullptr, const moe_lanes* lanes = nullptr) {
   int st = validate_routing(p);
   if (st) return st;
+  static_assert(kTicketsOffset + 32 * MOE_MAX_LANES <= 256, "per-lane ticket counters in the error word's block");
+  if (lanes) {
+    if (lanes->count < 1 || lanes->count >= MOE_MAX_LANES || !lanes->streams || !lanes->events) return MOE_ERR_INVALID_ARG;
+    const int S = p->ring_stages ? p->ring_stages : 3;
+    for (int l = 0; l < lanes->count; ++l)
+      if (!lanes->streams[l]) return MOE_ERR_INVALID_ARG;
+    for (int e = 0; e < S + 1 + lanes->count; ++e)
+      if (!lanes->events[e]) return MOE_ERR_INVALID_ARG;
+  }
   const bool keep = act_a || act_u;
   if (keep && (!act_a || !act_u)) return MOE_ERR_INVALID_ARG;
   if (keep && (p->dtype == MOE_F32 || p->chunk_rows > 0)) return MOE_ERR_UNSUPPORTED;
@@ -323,15 +332,17 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   st = schedule_into(p, r->topk_idx, r->counts, r->offsets, r->perm, r->inv_perm, wsb, stream);
   if (st) return st;
 
-  // shared expert first: it does not depend on the schedule
+  // shared expert first: it does not depend on the schedule (with lanes: on lane 0 after the fork)
   MOE_MARK(MOE_STAGE_SHARED);
-  if (p->I_shared > 0) {
+  auto shared_expert = [&](hipStream_t s_, const Persist* pc_) -> int {
+    if (p->I_shared <= 0) return MOE_OK;
     Grouped gs;
     gs.M = p->T;
-    st = expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
-                    0, 0, wsb + L.sh_h, sho, nullptr, stream, nullptr, pc);
-    if (st) return st;
-  }
+    return expert_ffn(p->dtype, gs, x, p->D, nullptr, 1, w->ws_gate, w->ws_up, w->ws_down, p->D, p->I_shared,
+                      0, 0, wsb + L.sh_h, sho, nullptr, s_, nullptr, pc_);
+  };
+  const bool laned = lanes && L.chunked;
+  if (!laned && (st = shared_expert(stream, pc))) return st;
 
   Grouped gr;
   gr.row_off = r->offsets;
@@ -351,6 +362,24 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     int32_t* crow = (int32_t*)(wsb + L.chunk_rowoff);
     st = launch_chunk_tables(r->offsets, p->E, (int)n, (int)b, C, ctile, crow, stream);
     if (st) return st;
+    // Lanes: chunk c on lane c % NLn (lane 0 = `stream`), each lane with ticket counters of its
+    // own; events[0 .. S-1] hand a ring stage from the lane that used it last to the next one,
+    // events[S] forks the lanes, events[S + l] (l >= 1) joins lane l back.
+    const int NLn = laned ? lanes->count + 1 : 1;
+    hipStream_t ls[MOE_MAX_LANES];
+    Persist lpc[MOE_MAX_LANES];
+    ls[0] = stream;
+    for (int l = 0; l < NLn; ++l) {
+      if (l > 0) ls[l] = lanes->streams[l - 1];
+      lpc[l] = pcs;
+      if (pcs.tickets) lpc[l].tickets = pcs.tickets + 8 * l;
+    }
+    if (NLn > 1) {
+      if (hipEventRecord(lanes->events[S], stream) != hipSuccess) return MOE_ERR_HIP;
+      for (int l = 1; l < NLn; ++l)
+        if (hipStreamWaitEvent(ls[l], lanes->events[S], 0) != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (laned && (st = shared_expert(stream, pc))) return st;
     MOE_MARK(MOE_STAGE_DISPATCH);
     const int64_t xrow = mx ? p->D : (int64_t)p->D * 2, hrow = mx ? p->I : (int64_t)p->I * 2;   // bytes per row
     uint8_t* xr = (uint8_t*)(wsb + L.x_slot);
@@ -360,8 +389,14 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     for (int c = 0; c < C; ++c) {
       const int64_t c0 = c * b, rows = (n - c0) < b ? (n - c0) : b;
       const int64_t stage = (int64_t)(c % S) * b, shift = stage - c0;   // slot index -> ring row
+      const int lane = c % NLn;
+      hipStream_t cs = ls[lane];
+      const Persist* cpc = pc ? &lpc[lane] : nullptr;
+      // ring stage c % S was last read by chunk c - S (its up/gate and down): on another lane, wait
+      if (NLn > 1 && c >= S && (c - S) % NLn != lane && hipStreamWaitEvent(cs, lanes->events[c % S], 0) != hipSuccess)
+        return MOE_ERR_HIP;
       st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + stage * xrow,
-                           mx ? xs + stage * (p->D / 32) : nullptr, stream);
+                           mx ? xs + stage * (p->D / 32) : nullptr, cs);
       if (st) return st;
       Grouped gc;
       gc.row_off = crow + (int64_t)c * (p->E + 1);
@@ -373,20 +408,26 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
         g1.A = xr + shift * xrow; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
         g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hr + shift * hrow; g1.ldc = p->I;
         st = launch_gemm_mx(g1, xs + shift * (p->D / 32), w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32),
-                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, stream);
+                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, cs);
         if (st) return st;
         GemmArgs g2;
         g2.A = hr + shift * hrow; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I;
         g2.b_group_stride = (int64_t)p->D * p->I; g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D;
         g2.c_scatter = r->perm;
         st = launch_gemm_mx(g2, hs + shift * (p->I / 32), w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr,
-                            gc, EPI_STORE, stream);
+                            gc, EPI_STORE, cs);
       } else {
         st = expert_ffn(p->dtype, gc, xr + shift * xrow, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
-                        p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, stream,
-                        nullptr, pc);
+                        p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, cs,
+                        nullptr, cpc);
       }
       if (st) return st;
+      if (NLn > 1 && c + S < C && (c + S) % NLn != lane && hipEventRecord(lanes->events[c % S], cs) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+    for (int l = 1; l < NLn; ++l) {
+      if (hipEventRecord(lanes->events[S + l], ls[l]) != hipSuccess) return MOE_ERR_HIP;
+      if (hipStreamWaitEvent(stream, lanes->events[S + l], 0) != hipSuccess) return MOE_ERR_HIP;
     }
     MOE_MARK(MOE_STAGE_UP_GATE);
     MOE_MARK(MOE_STAGE_DOWN);
@@ -482,6 +523,14 @@ int moe_forward_stages(const moe_problem* p, const void* x, const float* logits,
                        void* out, const moe_routing* r, void* y_routes, void* shared_out, void* ws,
                        size_t ws_bytes, hipEvent_t* ev, hipStream_t stream) {
   return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, ev, stream);
+}
+
+int moe_forward_lanes(const moe_problem* p, const void* x, const float* logits, const moe_weights* w, void* out,
+                      const moe_routing* r, void* y_routes, void* shared_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream, const moe_lanes* lanes) {
+  if (!lanes) return MOE_ERR_INVALID_ARG;
+  return forward_impl(p, x, logits, w, out, r, y_routes, shared_out, ws, ws_bytes, nullptr, stream, nullptr,
+                      nullptr, lanes);
 }
 
 }  // extern "C"

@@ -119,3 +119,9 @@ class ForwardRun:
         self.m.forward(self.p, self.L.x, self.L.logits, self.weights, self.out, self.routing, self.ws,
                        self.y_routes, self.shared_out)
         return self
+
+    def lanes(self, streams, events):
+        """moe_forward_lanes on the current stream plus `streams`."""
+        self.m.forward_lanes(self.p, self.L.x, self.L.logits, self.weights, self.out, self.routing, self.ws,
+                             streams, events, self.y_routes, self.shared_out)
+        return self

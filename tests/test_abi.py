@@ -260,3 +260,43 @@ def test_schedule_noalloc_rejects_without_gpu():
     assert lib.moe_schedule_noalloc(ctypes.byref(p), None, fake, fake, fake, fake, fake, None) == -1
     big = m.problem(1 << 18, 128, 128, 1024, 8, 0, 'bf16')        # 2^21 routes, 1024 experts
     assert lib.moe_schedule_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None) == -2
+
+
+def test_forward_lanes_rejects_without_gpu():
+    """moe_forward_lanes validates its lanes on the host before any HIP call: NULL lanes, a lane
+    count outside [1, MOE_MAX_LANES - 1], a NULL stream or any NULL among the S + 1 + count
+    events is MOE_ERR_INVALID_ARG; the chunked path's own refusals (fp32, fused gather) stay."""
+    import mixture_experts_layer_norm_amd as m
+    lib = m._lib
+    fake = 1 << 20
+    w, r = m.Weights(), m.Routing()
+    for f in ('w_gate', 'w_up', 'w_down'):
+        setattr(w, f, fake)
+    for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
+        setattr(r, f, fake)
+
+    def call(p, count, streams, events):
+        sarr = (ctypes.c_void_p * max(1, len(streams)))(*streams)
+        earr = (ctypes.c_void_p * max(1, len(events)))(*events)
+        lanes = m.Lanes(count, ctypes.cast(sarr, ctypes.POINTER(ctypes.c_void_p)),
+                        ctypes.cast(earr, ctypes.POINTER(ctypes.c_void_p)))
+        return lib.moe_forward_lanes(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None,
+                                     fake, 1 << 40, None, ctypes.byref(lanes))
+
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 256, 3)
+    assert lib.moe_forward_lanes(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None,
+                                 fake, 1 << 40, None, None) == -1
+    ev = [fake] * m.lane_event_count(p, 3)
+    assert m.lane_event_count(p, 1) == 5
+    for count in (0, -1, m.MOE_MAX_LANES):
+        assert call(p, count, [fake] * 4, ev + [fake]) == -1, count
+    assert call(p, 2, [fake, None], ev) == -1
+    for hole in range(m.lane_event_count(p, 2)):
+        e = list(ev)
+        e[hole] = None
+        assert call(p, 2, [fake, fake], e) == -1, hole
+    p5 = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 256, 5)   # S = 5: 5 + 1 + 1 events
+    assert call(p5, 1, [fake], [fake] * 6 + [None]) == -1
+    for dt, flags in (('bf16', m.MOE_FLAG_FUSED_GATHER), ('f32', 0)):
+        q = m.problem(64, 128, 128, 8, 2, 0, dt, 256, 3, flags)
+        assert call(q, 1, [fake], [fake] * 5) == -2, (dt, flags)

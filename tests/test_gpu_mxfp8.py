@@ -56,8 +56,9 @@ def mx_layer(cfg):
     return H, q
 
 
-def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0):
-    """moe_forward in MXFP8; with act = [a, u] buffers, moe_forward_keep."""
+def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0, lanes=None):
+    """moe_forward in MXFP8; with act = [a, u] buffers, moe_forward_keep; with lanes = (streams,
+    events), moe_forward_lanes."""
     cfg = H.cfg
     T, K, D, E = cfg.T, cfg.K, cfg.D, cfg.E
     p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8', chunk_rows, ring_stages)
@@ -72,7 +73,9 @@ def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0):
     out = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
     yr = torch.empty((T * K, D), dtype=torch.bfloat16, device='cuda')
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
-    if act is None:
+    if lanes is not None:
+        m.forward_lanes(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, *lanes, y_routes=yr)
+    elif act is None:
         m.forward(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, y_routes=yr)
     else:
         m.forward_keep(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), *act, ws, y_routes=yr)
