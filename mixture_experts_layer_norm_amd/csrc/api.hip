@@ -391,7 +391,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       const int64_t stage = (int64_t)(c % S) * b, shift = stage - c0;   // slot index -> ring row
       const int lane = c % NLn;
       hipStream_t cs = ls[lane];
-      const Persist* cpc = pc ? &lpc[lane] : nullptr;
+      // A chunk's tile bound counts a partial tile per expert, so with many experts every chunk
+      // passes the persistent rule; below 4 full m-tiles per chunk the per-tile form measured
+      // faster (DSV3 shape with 3 extra lanes, b = 512: 12.7 vs 13.6 ms; from b = 2048 on the
+      // persistent form is faster, 9.84 vs 10.47 ms at b = 32768).
+      const Persist* cpc = (pc && (pcs.force || b >= 4 * kGemmBM)) ? &lpc[lane] : nullptr;
       // ring stage c % S was last read by chunk c - S (its up/gate and down): on another lane, wait
       if (NLn > 1 && c >= S && (c - S) % NLn != lane && hipStreamWaitEvent(cs, lanes->events[c % S], 0) != hipSuccess)
         return MOE_ERR_HIP;
