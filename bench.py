@@ -149,6 +149,7 @@ def main():
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
+    lane_streams_first()
     F = make_forward(cfg, args.chunk_rows, args.flags, args.ring_stages)
     L, p, weights, routing_t, routing, out, ws = F['L'], F['p'], F['weights'], F['routing_t'], F['routing'], F['out'], F['ws']
     T, D, K = cfg.T, cfg.D, cfg.K
@@ -156,7 +157,7 @@ def main():
     stream = torch.cuda.current_stream()
     nst = len(moe.STAGES)
 
-    lane_streams = [torch.cuda.Stream() for _ in range(args.lanes)]
+    lane_streams = LANE_STREAMS[:args.lanes]
     lane_events = [torch.cuda.Event() for _ in range(moe.lane_event_count(p, args.lanes) if args.lanes else 0)]
     for e in lane_events:
         e.record(stream)          # creates the HIP event
@@ -261,13 +262,14 @@ def main():
     extra = None
     if not args.no_extra and args.workload == 'dsv3':
         rg = bench_route_gemm(moe, cfg, L.x, stream)
+        chunks = chunk_leg(moe, cfg, L, weights, routing, stream, ms_per_step)
         del weights, ws, out, F
         torch.cuda.empty_cache()
         layer = {'layer_fwd_bwd': layer_fwd_bwd_leg(cfg, L, keep=False),
                  'layer_fwd_bwd_keep_activations': layer_fwd_bwd_leg(cfg, L, keep=True)}
         del L
         torch.cuda.empty_cache()
-        extra = {'second_stream_latency': yl, **layer,
+        extra = {'second_stream_latency': yl, 'chunked_forward': chunks, **layer,
                  'mid_forward': forward_leg(synth.MID, 20), 'mxfp8_forward': forward_leg(synth.MXFP8, 5),
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
                  'ep_share_fwd_bwd_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
@@ -739,6 +741,52 @@ def time_calls(fn, steps, warmup, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+LANE_STREAMS = []
+
+
+def lane_streams_first():
+    """The lanes of moe_forward_lanes: the first three streams this process creates. HIP binds
+    each stream to one of its GPU_MAX_HW_QUEUES hardware queues (4 by default); measured with
+    rocprofv3's queue ids, the default stream and the first three streams created hold the four
+    queues and later streams share them, and two lanes on one queue run one after the other."""
+    import torch
+    if not LANE_STREAMS:
+        LANE_STREAMS.extend(torch.cuda.Stream() for _ in range(3))
+
+
+def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, warmup=2):
+    """The same DSV3 forward through the chunked ring at several chunk sizes b: in order on one
+    stream (moe_forward, S = 3) and with the chunks spread over the stream and 3 more
+    (moe_forward_lanes, S = 4); device time per step and its ratio to the unchunked forward."""
+    import torch
+    T, D, K = cfg.T, cfg.D, cfg.K
+    out = torch.empty((T, D), dtype=L.x.dtype, device='cuda')
+    main, lane_streams = stream, LANE_STREAMS[:3]
+    res = {'unchunked_ms': unchunked_ms, 'lanes': 3, 'rows': []}
+    for b in (512, 2048, 4096, 32768):
+        row = {'b': b}
+        for name, S, lanes in (('in_order', 3, 0), ('lanes', 4, 3)):
+            p = moe.problem(T, D, cfg.I, cfg.E, K, cfg.I_shared, cfg.dtype, b, S, 0)
+            ws = torch.empty((moe.workspace_size(p),), dtype=torch.uint8, device='cuda')
+            if lanes:
+                ev = [torch.cuda.Event() for _ in range(moe.lane_event_count(p, lanes))]
+                for e in ev:
+                    e.record(main)
+                fn = lambda: moe.forward_lanes(p, L.x, L.logits, weights, out, routing, ws, lane_streams, ev,
+                                               stream=main)
+                ms = time_calls(fn, steps, warmup, main)
+            else:
+                fn = lambda: moe.forward(p, L.x, L.logits, weights, out, routing, ws, stream=stream)
+                ms = time_calls(fn, steps, warmup, stream)
+            row[f'{name}_ms'] = ms
+            row[f'{name}_vs_unchunked'] = ms / unchunked_ms
+            del ws
+        res['rows'].append(row)
+        print(f'[bench] chunked b={b}: {json.dumps(row)}', file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    return res
 
 
 def forward_leg(cfg, steps, warmup=3):
