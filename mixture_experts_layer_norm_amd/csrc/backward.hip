@@ -11,9 +11,10 @@
 //   * "Pull dispatch, push combine": the backward reverse-combine gathers the output gradient
 //     into slots (dy_slot[j] = dout[perm[j] / K]) and the reverse-dispatch sums each token's
 //     slot gradients back (fixed order, no atomics).
-// Steps per group of rows: weight transposes; replay (a, u in fp32); dgrad-down with the SwiGLU
-// backward in its epilogue (da, du and per-tile <h, dh'> partials); dgrad-up over [da | du] with
-// K = 2I; padded transposes of x, dy, g*h and [da | du]; K-grouped weight-gradient GEMMs.
+// Steps per group of rows: replay (a, u in fp32); dgrad-down with the SwiGLU backward in its
+// epilogue (da, du and per-tile <h, dh'> partials); dgrad-up over [da | du] with K = 2I (both
+// read the weights in place, k-major); padded transposes of x, dy, g*h and [da | du]; K-grouped
+// weight-gradient GEMMs.
 // The weight-gradient operands that are not exact inputs (da, du, g*h) are carried as pairs of
 // bf16 values hi + lo (lo = v - bf16(v)) and contracted in two K passes, so they lose ~2^-17
 // relative instead of 2^-9: a weight gradient of an expert with a single slot is an outer
@@ -33,8 +34,8 @@ static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct BwdLayout {
   size_t err, offs, tile_off, poff, order, offs_s, tile_off_s, poff_s;
   size_t g_slot, dg_slot, x_slot, dy_slot, dx_slot, dx_sh;
-  size_t act_a, act_u, dau, part, wdT, wguT, xT, dyT, ghT, dauT;
-  size_t s_a, s_u, s_dau, s_part, s_wdT, s_wguT, s_xT, s_dyT, s_hT, s_dauT;
+  size_t act_a, act_u, dau, part, xT, dyT, ghT, dauT;
+  size_t s_a, s_u, s_dau, s_part, s_xT, s_dyT, s_hT, s_dauT;
   // MXFP8 routed experts: E4M3 codes (q) and E8M0 scales (s) of every backward GEMM operand
   size_t mq_x, ms_x, mq_dy, ms_dy, m_dhp, mq_dau, ms_dau, mq_wdT, ms_wdT, mq_wguT, ms_wguT;
   size_t mq_xT, ms_xT, mq_gdyT, ms_gdyT, mq_hT, ms_hT, mq_dauT, ms_dauT;
@@ -105,7 +106,6 @@ static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
     // [da | du | da_lo | du_lo] bf16; transposed padded x, dy, [g*h | lo], [da|du|lo]
     L.dau = take(n * 4 * I * 2);
     L.part = take(n * ((I + 127) / 128) * 4);
-    L.wdT = take(0); L.wguT = take(0);   // the dgrad GEMMs read the weights k-major, in place
     L.xT = take(D * L.Spad * 2); L.dyT = take(D * L.Spad * 2); L.ghT = take(2 * I * L.Spad * 2);
     L.dauT = take(4 * I * L.Spad * 2);
     const int64_t S = L.Spad;
@@ -117,7 +117,6 @@ static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
   if (Is > 0) {
     L.s_a = take(T * Is * 4); L.s_u = take(T * Is * 4); L.s_dau = take(T * 4 * Is * 2);
     L.s_part = take(T * ((Is + 127) / 128) * 4);
-    L.s_wdT = take(0); L.s_wguT = take(0);
     L.s_xT = take(D * L.Tpad * 2); L.s_dyT = take(D * L.Tpad * 2); L.s_hT = take(2 * Is * L.Tpad * 2);
     L.s_dauT = take(4 * Is * L.Tpad * 2);
     const int64_t S = L.Tpad;
@@ -132,7 +131,7 @@ static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
 }
 
 struct CoreBufs {
-  void *act_a, *act_u, *dau, *wdT, *wguT, *xT, *dyT, *ghT, *dauT;
+  void *act_a, *act_u, *dau, *xT, *dyT, *ghT, *dauT;   // the dgrad GEMMs read the weights in place, k-major
   float* part;
   int64_t Spad;
   int32_t* order;   // [G] dealing order of the K-grouped GEMMs (null for one group)
@@ -326,13 +325,13 @@ static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 static CoreBufs routed_bufs(char* ws, const BwdLayout& L) {
   auto u = [&](size_t o) { return L.lo_mx ? (uint8_t*)(ws + o) : nullptr; };
-  return CoreBufs{ws + L.act_a, ws + L.act_u, ws + L.dau, ws + L.wdT, ws + L.wguT, ws + L.xT, ws + L.dyT,
+  return CoreBufs{ws + L.act_a, ws + L.act_u, ws + L.dau, ws + L.xT, ws + L.dyT,
                   ws + L.ghT, ws + L.dauT, (float*)(ws + L.part), L.Spad, (int32_t*)(ws + L.order),
                   u(L.lq_dau), u(L.ls_dau), u(L.lq_gh), u(L.ls_gh), u(L.lq_x), u(L.ls_x), u(L.lq_dy), u(L.ls_dy)};
 }
 static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
   auto u = [&](size_t o) { return L.lo_mx_s ? (uint8_t*)(ws + o) : nullptr; };
-  return CoreBufs{ws + L.s_a, ws + L.s_u, ws + L.s_dau, ws + L.s_wdT, ws + L.s_wguT, ws + L.s_xT, ws + L.s_dyT,
+  return CoreBufs{ws + L.s_a, ws + L.s_u, ws + L.s_dau, ws + L.s_xT, ws + L.s_dyT,
                   ws + L.s_hT, ws + L.s_dauT, (float*)(ws + L.s_part), L.Tpad, nullptr,
                   u(L.slq_dau), u(L.sls_dau), u(L.slq_gh), u(L.sls_gh), u(L.slq_x), u(L.sls_x), u(L.slq_dy),
                   u(L.sls_dy)};

@@ -208,75 +208,6 @@ int launch_transpose_pad(int mode, const void* src, const void* src2, const floa
   return MOE_OK;
 }
 
-// Batched transpose of weights: in [B][R][C] -> out[b][c][col0 + r] with row pitch ldo.
-__global__ __launch_bounds__(256) void transpose_batched_kernel(const uint16_t* __restrict__ in, int R, int C,
-                                                                uint16_t* __restrict__ out, int64_t ldo,
-                                                                int64_t out_batch_stride, int col0) {
-  __shared__ uint16_t tile[64][66];
-  const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, cc0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const uint16_t* src = in + (int64_t)b * R * C;
-  for (int r = ty; r < 64; r += 4)
-    tile[r][tx] = (r0 + r < R && cc0 + tx < C) ? src[(int64_t)(r0 + r) * C + cc0 + tx] : (uint16_t)0;
-  __syncthreads();
-  uint16_t* dst = out + (int64_t)b * out_batch_stride;
-  for (int c = ty; c < 64; c += 4)
-    if (cc0 + c < C && r0 + tx < R) dst[(int64_t)(cc0 + c) * ldo + col0 + r0 + tx] = tile[tx][c];
-}
-
-// The same transpose with 16-byte global accesses on both sides, for R and C multiples of 64 and
-// 16-byte aligned output rows. A 64 x 64 tile: each thread loads two 16-byte chunks of input rows
-// into LDS (row pitch 66 elements), then gathers eight elements of one LDS column into a 16-byte
-// chunk of an output row; 8 consecutive threads write one output row's 128 contiguous bytes.
-// Column reads touch 8 rows (8 apart) and 8 columns per instruction: at most 2-way bank
-// conflicts with the pitch of 66.
-__global__ __launch_bounds__(256) void transpose_batched16_kernel(const uint16_t* __restrict__ in, int R, int C,
-                                                                  uint16_t* __restrict__ out, int64_t ldo,
-                                                                  int64_t out_batch_stride, int col0) {
-  constexpr int P = 66;
-  __shared__ uint16_t tile[64 * P];
-  const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int t = threadIdx.x;
-  const uint16_t* src = in + (int64_t)b * R * C + (int64_t)r0 * C + c0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = (t >> 3) + 32 * h, ch = t & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)row * C + ch * 8);
-    uint32_t* d = reinterpret_cast<uint32_t*>(tile + row * P + ch * 8);   // 4-byte aligned (P even)
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-  __syncthreads();
-  uint16_t* dst = out + (int64_t)b * out_batch_stride + col0 + r0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rg = t & 7, c = (t >> 3) + 32 * h;   // output row c0 + c, its input rows 8 rg .. 8 rg + 7
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)tile[(8 * rg + 2 * q) * P + c] | ((uint32_t)tile[(8 * rg + 2 * q + 1) * P + c] << 16);
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + c) * ldo + 8 * rg) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-int launch_transpose_batched(const void* in, int B, int R, int C, void* out, int64_t ldo, int64_t out_batch_stride,
-                             int col0, hipStream_t s) {
-  if (B == 0) return MOE_OK;
-  if (R % 64 == 0 && C % 64 == 0 && col0 % 8 == 0 && ldo % 8 == 0 && out_batch_stride % 8 == 0 &&
-      ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0) {
-    dim3 grid((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)B), block(256);
-    hipLaunchKernelGGL(transpose_batched16_kernel, grid, block, 0, s, (const uint16_t*)in, R, C, (uint16_t*)out, ldo,
-                       out_batch_stride, col0);
-    MOE_LAUNCH_CHECK();
-    return MOE_OK;
-  }
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)B), block(256);
-  hipLaunchKernelGGL(transpose_batched_kernel, grid, block, 0, s, (const uint16_t*)in, R, C, (uint16_t*)out, ldo,
-                     out_batch_stride, col0);
-  MOE_LAUNCH_CHECK();
-  return MOE_OK;
-}
 
 // dg[j] = sum over n-tiles of the per-tile partial <h, dh'> (fixed order)
 __global__ __launch_bounds__(256) void row_sum_kernel(const float* __restrict__ part, int64_t rows, int ntn,
