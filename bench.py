@@ -378,8 +378,8 @@ def bench_route_gemm(moe, cfg, x, stream, reps=20):
     ms = e0.elapsed_time(e1) / reps
     flops = 2.0 * T * D * E
     res = {'workload': f'router GEMM + top-{K}, T={T} D={D} E={E}', 'ms': ms, 'tflops': flops / (ms * 1e-3) / 1e12}
-    # its backward: dW_r = d_logits^T x and dx += d_logits W_r (fp32 FMA, 4*T*D*E FLOP), with
-    # d_logits nonzero on each token's K chosen experts as the layer backward writes it
+    # its backward: dW_r = d_logits^T x and dx += d_logits W_r, with d_logits nonzero on each
+    # token's K chosen experts as the layer backward writes it
     dl = torch.zeros((T, E), dtype=torch.float32, device='cuda')
     dl.scatter_(1, idx.long(), torch.randn((T, K), generator=g, device='cuda'))
     dw = torch.empty((E, D), dtype=torch.float32, device='cuda')
@@ -395,9 +395,17 @@ def bench_route_gemm(moe, cfg, x, stream, reps=20):
     e1.record(stream)
     torch.cuda.synchronize()
     mb = e0.elapsed_time(e1) / (reps // 2)
-    res['backward'] = {'ms': mb, 'tflops': 2 * flops / (mb * 1e-3) / 1e12,
-                       'fp32_peak_frac': 2 * flops / (mb * 1e-3) / 1e12 / PEAK_F32_TFLOPS,
-                       'note': 'dW_r = d_logits^T x and dx += d_logits W_r, fp32 FMA; fraction of the 157.3 TFLOP/s fp32 peak'}
+    # the kernels skip the zero entries of d_logits: T K nonzeros, 2 D FMAs each; algorithmic bytes
+    # read d_logits, x and W_r once, read and write dx, write dW_r
+    nnz_flops = 2 * 2.0 * T * K * D
+    alg_bytes = T * E * 4 + T * D * 2 + E * D * 2 + 2 * T * D * 2 + E * D * 4
+    res['backward'] = {'ms': mb, 'dense_equivalent_tflops': 2 * flops / (mb * 1e-3) / 1e12,
+                       'nonzero_tflops': nnz_flops / (mb * 1e-3) / 1e12,
+                       'algorithmic_bytes': alg_bytes,
+                       'hbm_frac': alg_bytes / (mb * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       'note': 'dW_r = d_logits^T x and dx += d_logits W_r with d_logits nonzero on K of E entries '
+                               'per token; fp32 FMA over the nonzero entries only (bitwise the dense sums); '
+                               'dense_equivalent_tflops counts the 4 T D E FLOP of the dense products'}
     return res
 
 

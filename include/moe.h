@@ -140,6 +140,11 @@ typedef struct moe_problem {
  * workgroup per block, and do not read the word. */
 #define MOE_FLAG_CU_BUDGET 0x20000
 #define MOE_WS_CU_BUDGET_OFFSET 4
+/* moe_route_gemm_backward: d_logits has dense terms (e.g. from an auxiliary loss on the router),
+ * so both products run on the dense kernel instead of skipping zero entries. The results are the
+ * same bits either way; only the speed differs (DSV3 shape: 0.48 ms skipping zeros at K = 8 of 256
+ * nonzero per row and 2.4 ms dense; a fully dense d_logits takes 8.8 ms skipping zeros). */
+#define MOE_FLAG_ROUTER_BWD_DENSE 0x80000
 
 /* Expert weights (device pointers). Routed: w_gate, w_up [E][I][D]; w_down [E][D][I].
  * Shared: ws_gate, ws_up [I_shared][D]; ws_down [D][I_shared] (always bf16 under MOE_MXFP8).
@@ -220,7 +225,11 @@ int moe_route_gemm_workspace_size(const moe_problem *p, size_t *bytes);
  * not NULL, dx [T][D] (BF16, the experts' input gradient from moe_backward) += d_logits W_r,
  * summed in fp32 onto the stored value and rounded once. x [T][D], w_router [E][D] BF16.
  * Products are exact in fp32; each output is one thread's fp32 sum in ascending token (dw) or
- * expert (dx) order: deterministic. BF16 and MXFP8 problems (x is BF16 under both);
+ * expert (dx) order: deterministic. Zero entries of d_logits are skipped: their products are
+ * exact zeros, so the sums are those over every entry (up to the sign of an all-zero sum), at
+ * about K/E of the work; a NaN or infinite x or W_r element meets only the nonzero entries. With
+ * x 4-byte, dw_router 8-byte and w_router and dx 16-byte aligned the zero-skipping kernels run
+ * (unless MOE_FLAG_ROUTER_BWD_DENSE), otherwise a dense kernel with the same sums. BF16 and MXFP8 problems (x is BF16 under both);
  * MOE_F32: MOE_ERR_UNSUPPORTED. No workspace. */
 int moe_route_gemm_backward(const moe_problem *p, const void *x, const void *w_router, const float *d_logits,
                             float *dw_router, void *dx, hipStream_t stream);

@@ -13,7 +13,8 @@ size_t elt_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static constexpr uint32_t kKnownFlags = MOE_FLAG_FUSED_GATHER | MOE_FLAG_PERSISTENT | MOE_FLAG_BWD_DGRAD_ONE_PASS |
-                                        MOE_FLAG_BWD_WGRAD_LO_MXFP8 | MOE_FLAG_PERSISTENT_GEMM | MOE_FLAG_CU_BUDGET;
+                                        MOE_FLAG_BWD_WGRAD_LO_MXFP8 | MOE_FLAG_PERSISTENT_GEMM | MOE_FLAG_CU_BUDGET |
+                                        MOE_FLAG_ROUTER_BWD_DENSE;
 
 // Extra checks of the entry points that route tokens (top-k over the E experts).
 int validate_routing(const moe_problem* p) {

@@ -184,6 +184,8 @@ def test_persistent_gemm_flags_without_gpu():
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1
     p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET)
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value >= 256
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_ROUTER_BWD_DENSE)   # a known bit
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert 4 <= m.MOE_WS_CU_BUDGET_OFFSET and m.MOE_WS_CU_BUDGET_OFFSET + 4 <= 64
     fake = 1 << 20
     w, r = m.Weights(), m.Routing()

@@ -138,3 +138,44 @@ def test_layer_backward_through_the_router(m):
     m.route_gemm_backward(p, xt, wrt, dlg, dwr2, dx2)
     torch.cuda.synchronize()
     assert torch.equal(dwr, dwr2) and torch.equal(dx, dx2)
+
+
+@pytest.mark.parametrize('T,D,E,density', [(1000, 1024, 64, 0.1), (300, 256, 300, 1.0), (2048, 7168, 256, 8 / 256)])
+def test_router_backward_sparse_kernels_equal_dense_bitwise(m, T, D, E, density):
+    """Aligned operands take the kernels that skip zero d_logits entries; the same values stored at
+    misaligned addresses, or MOE_FLAG_ROUTER_BWD_DENSE, take the dense FMA kernel. Skipping exact-zero products leaves every fp32
+    sum unchanged, so both give the same bits: sparse, dense (every entry nonzero) and signed-zero
+    d_logits, E a multiple of 4 or not."""
+    print(f'[router bwd] sparse = dense T={T} D={D} E={E} density={density:.3f}', flush=True)
+    g = torch.Generator(device='cuda')
+    g.manual_seed(T + E)
+    x = torch.randn((T, D), device='cuda', generator=g).to(torch.bfloat16)
+    w = (torch.randn((E, D), device='cuda', generator=g) / np.sqrt(D)).to(torch.bfloat16)
+    keep = torch.rand((T, E), device='cuda', generator=g) < density
+    dl = torch.where(keep, torch.randn((T, E), device='cuda', generator=g), torch.zeros((T, E), device='cuda'))
+    dl[::7, ::5] = -0.0                       # negative zeros are zeros too
+    dx0 = (torch.randn((T, D), device='cuda', generator=g) * 0.05).to(torch.bfloat16)
+    p = m.problem(T, D, 128, E, 1, 0, 'bf16')
+
+    def shifted(t, elems):
+        """A copy of t whose data starts `elems` elements past an aligned allocation."""
+        buf = torch.empty(t.numel() + elems, dtype=t.dtype, device='cuda')
+        v = buf[elems:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    dw1 = torch.full((E, D), float('nan'), device='cuda')
+    dx1 = dx0.clone()
+    m.route_gemm_backward(p, x, w, dl, dw1, dx1)
+    xs, ws_, dxs = shifted(x, 1), shifted(w, 1), shifted(dx0, 1)
+    dw2 = shifted(torch.full((E, D), float('nan'), device='cuda'), 1)
+    assert xs.data_ptr() % 4 and ws_.data_ptr() % 16 and dxs.data_ptr() % 16 and dw2.data_ptr() % 8
+    m.route_gemm_backward(p, xs, ws_, dl, dw2, dxs)
+    # MOE_FLAG_ROUTER_BWD_DENSE selects the dense kernel on aligned operands too
+    pd = m.problem(T, D, 128, E, 1, 0, 'bf16', flags=m.MOE_FLAG_ROUTER_BWD_DENSE)
+    dw3 = torch.full((E, D), float('nan'), device='cuda')
+    dx3 = dx0.clone()
+    m.route_gemm_backward(pd, x, w, dl, dw3, dx3)
+    torch.cuda.synchronize()
+    assert torch.equal(dw1, dw2) and torch.equal(dw1, dw3)
+    assert torch.equal(dx1, dxs) and torch.equal(dx1, dx3)
