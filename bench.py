@@ -270,7 +270,8 @@ def main():
         del L
         torch.cuda.empty_cache()
         extra = {'second_stream_latency': yl, 'chunked_forward': chunks, **layer,
-                 'mid_forward': forward_leg(synth.MID, 20), 'mxfp8_forward': forward_leg(synth.MXFP8, 5),
+                 'mid_forward': forward_leg(synth.MID, 20), 'mid_chunked_forward': mid_chunk_leg(),
+                 'mxfp8_forward': forward_leg(synth.MXFP8, 5),
                  'ep_share_fwd_bwd': bench_share(max(5, args.steps // 5), 2, args.flags),
                  'ep_share_fwd_bwd_keep_activations': bench_share(max(5, args.steps // 5), 2, args.flags,
                                                                   keep=True),
@@ -764,7 +765,7 @@ def lane_streams_first():
         LANE_STREAMS.extend(torch.cuda.Stream() for _ in range(3))
 
 
-def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, warmup=2):
+def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, warmup=2, bs=(512, 2048, 4096, 32768)):
     """The same DSV3 forward through the chunked ring at several chunk sizes b: in order on one
     stream (moe_forward, S = 3) and with the chunks spread over the stream and 3 more
     (moe_forward_lanes, S = 4); device time per step and its ratio to the unchunked forward."""
@@ -773,7 +774,7 @@ def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, war
     out = torch.empty((T, D), dtype=L.x.dtype, device='cuda')
     main, lane_streams = stream, LANE_STREAMS[:3]
     res = {'unchunked_ms': unchunked_ms, 'lanes': 3, 'rows': []}
-    for b in (512, 2048, 4096, 32768):
+    for b in bs:
         row = {'b': b}
         for name, S, lanes in (('in_order', 3, 0), ('lanes', 4, 3)):
             p = moe.problem(T, D, cfg.I, cfg.E, K, cfg.I_shared, cfg.dtype, b, S, 0)
@@ -792,7 +793,25 @@ def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, war
             row[f'{name}_vs_unchunked'] = ms / unchunked_ms
             del ws
         res['rows'].append(row)
-        print(f'[bench] chunked b={b}: {json.dumps(row)}', file=sys.stderr, flush=True)
+        print(f'[bench] chunked {cfg.name} b={b}: {json.dumps(row)}', file=sys.stderr, flush=True)
+    best = min(res['rows'], key=lambda r: r['lanes_ms'])
+    res['best_b'] = {'b': best['b'], 'lanes_ms': best['lanes_ms']}
+    torch.cuda.empty_cache()
+    return res
+
+
+def mid_chunk_leg(steps=10):
+    """The mid forward (T=4096, E=128) unchunked and chunked at b = 512 ... 4096."""
+    import torch
+    import synth
+    import mixture_experts_layer_norm_amd as moe
+    cfg = synth.MID
+    F = make_forward(cfg)
+    stream = torch.cuda.current_stream()
+    ms = time_calls(lambda: moe.forward(F['p'], F['L'].x, F['L'].logits, F['weights'], F['out'], F['routing'],
+                                        F['ws'], stream=stream), 20, 3, stream)
+    res = chunk_leg(moe, cfg, F['L'], F['weights'], F['routing'], stream, ms, steps, bs=(512, 1024, 2048, 4096))
+    del F
     torch.cuda.empty_cache()
     return res
 
