@@ -38,7 +38,9 @@ METRIC = 'MoE layer tokens/s (fwd, fwd+bwd) on 1 MI355X; % of MFMA peak'
 
 # HBM traffic of the dominant kernel is read from its rocprofv3 counter summary, and only while the
 # kernel sources are the ones the counters were taken on (hash recorded in the summary).
-GEMM_SOURCES = ('mixture_experts_layer_norm_amd/csrc/gemm_tile.h', 'mixture_experts_layer_norm_amd/csrc/gemm.hip')
+# the GEMM kernels and the host code that chooses their operands (gathered or copied rows) and forms
+GEMM_SOURCES = ('mixture_experts_layer_norm_amd/csrc/gemm_tile.h', 'mixture_experts_layer_norm_amd/csrc/gemm.hip',
+                'mixture_experts_layer_norm_amd/csrc/api.hip')
 TRAFFIC_SUMMARY = {'up_gate': 'profiles/gemm_swiglu_routed_dsv3_T8192_hbm_traffic.md',
                    'down': 'profiles/gemm_down_routed_dsv3_T8192_hbm_traffic.md'}
 
@@ -89,7 +91,7 @@ def stage_work(cfg, flags):
     T, D, I, E, K, Is = cfg.T, cfg.D, cfg.I, cfg.E, cfg.K, cfg.I_shared
     n = T * K
     b = 4 if cfg.dtype == 'f32' else 2
-    fused = bool(flags & 1)
+    fused = not (flags & 0x100000)   # GEMM1 reads x through the schedule unless the slot copy is asked for
     w = {}
     if cfg.dtype == 'mxfp8':
         # routed operands E4M3 (1 byte) + one E8M0 byte per 32; activations in, outputs BF16
@@ -210,7 +212,7 @@ def main():
     peak = {'f32': PEAK_F32_TFLOPS, 'mxfp8': PEAK_MXFP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    work = stage_work(cfg, args.flags)
+    work = stage_work(cfg, args.flags | (0x100000 if args.chunk_rows else 0))   # the ring holds slot copies
     dom = max(stage_ms, key=stage_ms.get)
     f_dom, b_dom = work[dom]
     t_dom = stage_ms[dom] * 1e-3

@@ -86,8 +86,15 @@ typedef struct moe_problem {
   int32_t flags;
 } moe_problem;
 
-/* Routed GEMM1 reads x rows through the schedule (gather) instead of a dispatched copy. */
+/* The unchunked BF16 and fp32 forwards (moe_forward, moe_forward_stages, moe_forward_keep) read
+ * the x rows of the routed up/gate GEMM through the schedule (row j of expert-slot order is
+ * x[perm[j] / K]) instead of a dispatched copy: the pages' pull dispatch done by the GEMM's own
+ * operand loads, with no copy pass (DSV3 shape: 9.41 against 9.66 ms per forward). This is the
+ * default; MOE_FLAG_FUSED_GATHER names it and is accepted. MOE_FLAG_DISPATCH_COPY instead writes
+ * the expert-contiguous slot copy first (as the chunked ring and MXFP8 always do) and runs the
+ * GEMM on it; the outputs are the same bits. Both flags together: MOE_ERR_INVALID_ARG. */
 #define MOE_FLAG_FUSED_GATHER 0x1
+#define MOE_FLAG_DISPATCH_COPY 0x100000
 /* Bits 0x2, 0x8, 0x10, 0x20 and 0xff00 are reserved (they selected tuning variants that measured
  * no faster and were removed); a problem that sets one, or any bit not defined here, is rejected. */
 /* moe_backward / moe_experts_backward under MOE_BF16: contract dgrad-up (dx = [da | du] [W_gate |
@@ -180,8 +187,9 @@ typedef struct moe_grads {
 /* Human-readable name of a status code (static string). */
 const char *moe_status_string(int status);
 
-/* Bytes of device workspace that moe_schedule / moe_forward / moe_backward need for `p`
- * (the largest of the three). Writes *bytes; returns MOE_OK or MOE_ERR_INVALID_ARG.
+/* Bytes of device workspace that moe_schedule and the forwards (moe_forward, moe_forward_stages,
+ * moe_forward_keep, moe_forward_lanes) need for `p` (moe_backward: moe_backward_workspace_size).
+ * Writes *bytes; returns MOE_OK or MOE_ERR_INVALID_ARG.
  * The first 256 bytes hold the sticky error word (offset 0, int32). */
 int moe_workspace_size(const moe_problem *p, size_t *bytes);
 

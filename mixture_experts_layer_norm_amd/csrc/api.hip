@@ -14,7 +14,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static constexpr uint32_t kKnownFlags = MOE_FLAG_FUSED_GATHER | MOE_FLAG_PERSISTENT | MOE_FLAG_BWD_DGRAD_ONE_PASS |
                                         MOE_FLAG_BWD_WGRAD_LO_MXFP8 | MOE_FLAG_PERSISTENT_GEMM | MOE_FLAG_CU_BUDGET |
-                                        MOE_FLAG_ROUTER_BWD_DENSE;
+                                        MOE_FLAG_ROUTER_BWD_DENSE | MOE_FLAG_DISPATCH_COPY;
 
 // Extra checks of the entry points that route tokens (top-k over the E experts).
 int validate_routing(const moe_problem* p) {
@@ -32,6 +32,7 @@ int validate_problem(const moe_problem* p) {
   if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
   if ((uint32_t)p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
   if ((p->flags & MOE_FLAG_CU_BUDGET) && !(p->flags & MOE_FLAG_PERSISTENT_GEMM)) return MOE_ERR_INVALID_ARG;
+  if ((p->flags & MOE_FLAG_FUSED_GATHER) && (p->flags & MOE_FLAG_DISPATCH_COPY)) return MOE_ERR_INVALID_ARG;
   if (p->E > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (p->dtype == MOE_F32) {
@@ -72,7 +73,10 @@ WsLayout ws_layout(const moe_problem& p) {
   L.tile_off = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_clean = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_poff = o; o = align256(o + (size_t)(p.E + 1) * 4);
-  L.x_slot = o; o = align256(o + (size_t)L.ring_rows * p.D * (mx ? 1 : act));
+  // dispatched slot rows: the chunked ring, MXFP8 (quantised in dispatch) and MOE_FLAG_DISPATCH_COPY;
+  // otherwise GEMM1 reads x through the schedule and no copy is made
+  const bool copy = L.chunked || mx || (p.flags & MOE_FLAG_DISPATCH_COPY);
+  L.x_slot = o; o = align256(o + (copy ? (size_t)L.ring_rows * p.D * (mx ? 1 : act) : 0));
   L.x_slot_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.D / 32) : 0));
   L.h = o; o = align256(o + (size_t)L.ring_rows * p.I * (mx ? 1 : act));
   L.h_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.I / 32) : 0));
@@ -473,9 +477,10 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     st = launch_gemm_mx(g2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream);
     if (st) return st;
   } else {
+    // GEMM1 reads x rows through the schedule (row j = x[perm[j] / K]) unless the slot copy is asked for
     const void* A = x;
     const int32_t* gather = r->perm;
-    if (!(p->flags & MOE_FLAG_FUSED_GATHER)) {
+    if (p->flags & MOE_FLAG_DISPATCH_COPY) {
       st = launch_dispatch_tokens(x, p->dtype, r->inv_perm, p->T, p->K, p->D, wsb + L.x_slot, nullptr, stream);
       if (st) return st;
       A = wsb + L.x_slot;

@@ -186,6 +186,14 @@ def test_persistent_gemm_flags_without_gpu():
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value >= 256
     p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_ROUTER_BWD_DENSE)   # a known bit
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    # the forward gathers x through the schedule by default; the slot copy is asked for, and needs
+    # the slot buffer; asking for both is invalid
+    p = m.problem(8192, 7168, 2048, 256, 8, 2048, 'bf16')
+    gather = m.workspace_size(p)
+    p = m.problem(8192, 7168, 2048, 256, 8, 2048, 'bf16', 0, 0, m.MOE_FLAG_DISPATCH_COPY)
+    assert m.workspace_size(p) >= gather + 8192 * 8 * 7168 * 2
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_DISPATCH_COPY | m.MOE_FLAG_FUSED_GATHER)
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1
     assert 4 <= m.MOE_WS_CU_BUDGET_OFFSET and m.MOE_WS_CU_BUDGET_OFFSET + 4 <= 64
     fake = 1 << 20
     w, r = m.Weights(), m.Routing()

@@ -403,7 +403,7 @@ def test_experts_backward_dgrad_one_pass(m, counts):
         assert torch.equal(r[k], base[k]), k
 
 
-@pytest.mark.parametrize('flags', [0, 0x1, 0x40], ids=['dispatched', 'fused_gather', 'one_pass'])
+@pytest.mark.parametrize('flags', [0, 0x100000, 0x40], ids=['gather', 'dispatch_copy', 'one_pass'])
 def test_layer_keep_activations_bitwise(m, flags):
     """moe_forward_keep + moe_backward_kept: the routed a, u handed from the layer forward to the
     layer backward instead of replayed; every output bitwise that of moe_forward + moe_backward."""

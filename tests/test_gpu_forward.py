@@ -72,13 +72,19 @@ def test_forward_mid(m):
     check_forward(m, synth.MID)
 
 
-def test_forward_fused_gather_matches_dispatch_bitwise(m):
-    H = synth.host_layer(SMALL_BF16)
+@pytest.mark.parametrize('cfg', [SMALL_BF16, DENSE_F32], ids=lambda c: c.name)
+def test_forward_gather_matches_dispatch_copy_bitwise(m, cfg):
+    """The default forward reads x through the schedule; MOE_FLAG_DISPATCH_COPY writes the slot copy
+    first. Same rows, same GEMM tiles: the same bits (MOE_FLAG_FUSED_GATHER names the default)."""
+    H = synth.host_layer(cfg)
     L = synth.to_device(H)
     a = ForwardRun(m, L)()
-    b = ForwardRun(m, L, flags=m.MOE_FLAG_FUSED_GATHER)()
+    b = ForwardRun(m, L, flags=m.MOE_FLAG_DISPATCH_COPY)()
+    c = ForwardRun(m, L, flags=m.MOE_FLAG_FUSED_GATHER)()
     torch.cuda.synchronize()
-    assert torch.equal(a.out, b.out) and torch.equal(a.y_routes, b.y_routes)
+    assert b.ws.numel() > a.ws.numel()      # the copy needs the slot buffer
+    for r in (b, c):
+        assert torch.equal(a.out, r.out) and torch.equal(a.y_routes, r.y_routes)
 
 
 def test_forward_bitwise_deterministic(m):
