@@ -18,8 +18,8 @@
 // accumulator slot and the epilogue needs no data exchange. 256-row m-tiles read each expert's
 // weights once for up to 256 routed rows; row blocks past an expert's last row skip their MFMAs.
 //
-// Workgroup -> tile mapping: tiles are numbered group by group (inside a group in pairs of
-// m-tiles, n-tile major inside a pair, see decode_grouped_tile) and dealt out so that each XCD
+// Workgroup -> tile mapping: tiles are numbered group by group (inside a group in blocks of 4
+// m-tiles, n-tile major inside a block, see decode_grouped_tile) and dealt out so that each XCD
 // (workgroups are placed round-robin over the 8 XCDs) gets a contiguous range, which keeps an
 // expert's activation rows and weight tiles in that XCD's L2. The split is over the tiles that
 // exist (read on the device), not over the launched upper bound, so that every XCD gets an
