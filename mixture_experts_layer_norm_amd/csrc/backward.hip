@@ -78,7 +78,10 @@ static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
   L.offs_s = take(8); L.tile_off_s = take(8); L.poff_s = take(8);
   const int64_t eb = p.dtype == MOE_F32 ? 4 : 2;   // bytes per activation element
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
-  L.x_slot = take(n * D * eb); L.dy_slot = take(n * D * eb); L.dx_slot = take(n * D * eb);
+  // slot copies of x and dout: the BF16 layer backward reads both through the schedule instead
+  // (unless MOE_FLAG_DISPATCH_COPY); fp32 and MXFP8 copy them
+  const bool copy = p.dtype != MOE_BF16 || (p.flags & MOE_FLAG_DISPATCH_COPY);
+  L.x_slot = take(copy ? n * D * eb : 0); L.dy_slot = take(copy ? n * D * eb : 0); L.dx_slot = take(n * D * eb);
   L.dx_sh = take(T * D * eb);
   // replayed a, u; left out when the caller keeps them (offsets then unused)
   L.act_a = take(kept ? 0 : n * I * 4); L.act_u = take(kept ? 0 : n * I * 4);
@@ -143,13 +146,15 @@ struct CoreBufs {
 
 // Backward of one set of groups (routed experts, or the shared expert as one group).
 // rows: x_rows/dy_rows [n][D] grouped by offs (sanitised, device) with m-tile prefix tile_off
-// and padded offsets poff. g_rows may be null (weight 1). Outputs dx_rows [n][D] bf16, dg_rows
-// [n] fp32 (nullable), dW (fp32).
+// and padded offsets poff; with row_map, row j of either is row row_map[j] / row_div of x_rows /
+// dy_rows (the layer backward reads x and dout through the schedule, no slot copies). g_rows may
+// be null (weight 1). Outputs dx_rows [n][D] bf16, dg_rows [n] fp32 (nullable), dW (fp32).
 static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
                          const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                          const void* wg, const void* wu, const void* wd, void* dx_rows, float* dg_rows,
                          float* dw_gate, float* dw_up, float* dw_down, const CoreBufs& b, hipStream_t s,
-                         bool dgrad_one_pass, bool replay = true) {
+                         bool dgrad_one_pass, bool replay = true, const int32_t* row_map = nullptr,
+                         int row_div = 1) {
   int st;
   // The dgrad GEMMs contract the weights along their row axis (dh' = dy W_down over D, dx =
   // [da | du] [W_gate; W_up] over I): they read them in place, k-major, through transposing LDS
@@ -165,14 +170,16 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   // replay: a = x W_gate^T, u = x W_up^T (kept in fp32); skipped when the forward kept them
   if (replay) {
     GemmArgs r;
-    r.A = x_rows; r.lda = D; r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
+    r.A = x_rows; r.lda = D; r.a_gather = row_map; r.a_div = row_div;
+    r.B = wg; r.B2 = wu; r.ldb = D; r.b_group_stride = (int64_t)I * D;
     r.N = I; r.K = D; r.C = b.act_a; r.C2 = b.act_u; r.ldc = I;
     if ((st = launch_gemm_bf16(r, grp, EPI_SAVE_AU, s, b.pc))) return st;
   }
 
   // dgrad-down + SwiGLU backward: dh' = dy W_down; da, du (as bf16 hi/lo pairs); partial <h, dh'>
   GemmArgs d;
-  d.A = dy_rows; d.lda = D; d.B = wd; d.ldb = I; d.b_group_stride = (int64_t)D * I; d.b_kmajor = 1;
+  d.A = dy_rows; d.lda = D; d.a_gather = row_map; d.a_div = row_div;
+  d.B = wd; d.ldb = I; d.b_group_stride = (int64_t)D * I; d.b_kmajor = 1;
   d.N = I; d.K = D; d.C = b.dau; d.C2 = (uint16_t*)b.dau + I; d.ldc = 4 * I; d.lo_off = 2 * I;
   d.ea = (const float*)b.act_a; d.eu = (const float*)b.act_u; d.lde = I;
   d.row_scale = g_rows; d.row_partial = b.part;
@@ -190,8 +197,12 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
 
   // padded transposes for the weight gradients: x and dy exact; g*h and [da|du] as hi/lo rows
   const int64_t Sp = b.Spad;
-  if ((st = launch_transpose_pad(TR_COPY, x_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.xT, Sp, s))) return st;
-  if ((st = launch_transpose_pad(TR_COPY, dy_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.dyT, Sp, s))) return st;
+  if ((st = launch_transpose_pad(TR_COPY, x_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.xT, Sp, s, 0, row_map,
+                                 row_div)))
+    return st;
+  if ((st = launch_transpose_pad(TR_COPY, dy_rows, nullptr, nullptr, D, D, offs, poff, G, Sp, b.dyT, Sp, s, 0, row_map,
+                                 row_div)))
+    return st;
   if ((st = launch_transpose_pad(TR_SWIGLU, b.act_a, b.act_u, g_rows, I, I, offs, poff, G, Sp, b.ghT, Sp, s, 1)))
     return st;
   if ((st = launch_transpose_pad(TR_COPY, b.dau, nullptr, nullptr, 4 * I, 4 * I, offs, poff, G, Sp, b.dauT, Sp, s)))
@@ -718,10 +729,15 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
   if (kept && (!al16(act_a) || !al16(act_u))) return MOE_ERR_MISALIGNED;
   char* wsb = (char*)ws;
   const int64_t n = L.n;
-  // reverse-combine (pull dout into slots), replayed dispatch of x, slot weights
+  // reverse-combine (pull dout into slots) and replayed dispatch of x: copies for fp32, MXFP8 (quantised
+  // from them) and MOE_FLAG_DISPATCH_COPY; the BF16 GEMMs and transposes otherwise read slot row j
+  // from dout / x row perm[j] / K directly
+  const bool copy = p->dtype != MOE_BF16 || (p->flags & MOE_FLAG_DISPATCH_COPY);
   const int adt = f32 ? MOE_F32 : MOE_BF16;   // activations stay bf16 under MXFP8 until quantised
-  if ((st = launch_dispatch(dout, adt, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
-  if ((st = launch_dispatch(x, adt, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream))) return st;
+  if (copy) {
+    if ((st = launch_dispatch(dout, adt, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
+    if ((st = launch_dispatch(x, adt, r->perm, p->K, p->D, 0, n, wsb + L.x_slot, nullptr, stream))) return st;
+  }
   if ((st = launch_gather_f32(r->topk_w, r->perm, n, (float*)(wsb + L.g_slot), stream))) return st;
   int32_t* offs = (int32_t*)(wsb + L.offs);
   if ((st = launch_group_prefix(r->offsets, p->E, (int)n, offs, (int32_t*)(wsb + L.tile_off),
@@ -748,10 +764,12 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
       cb.act_a = const_cast<float*>(act_a);   // read only from here on
       cb.act_u = const_cast<float*>(act_u);
     }
-    if ((st = core_backward(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+    if ((st = core_backward(p->E, n, p->D, p->I, copy ? (const void*)(wsb + L.x_slot) : x,
+                            copy ? (const void*)(wsb + L.dy_slot) : dout, (float*)(wsb + L.g_slot), offs,
                             (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w->w_gate, w->w_up, w->w_down,
                             wsb + L.dx_slot, (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, cb,
-                            stream, (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0, !kept)))
+                            stream, (p->flags & MOE_FLAG_BWD_DGRAD_ONE_PASS) != 0, !kept,
+                            copy ? nullptr : r->perm, p->K)))
       return st;
   }
   if ((st = launch_router_backward((float*)(wsb + L.dg_slot), r->inv_perm, r->topk_idx, r->topk_w, p->T, p->E, p->K,

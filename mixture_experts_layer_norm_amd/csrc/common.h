@@ -94,7 +94,7 @@ int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean,
                         int32_t* err, hipStream_t s, int pad = 64);
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
                          const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
-                         int64_t ldo, hipStream_t s, int split_lo = 0);
+                         int64_t ldo, hipStream_t s, int split_lo = 0, const int32_t* rmap = nullptr, int rdiv = 1);
 int launch_row_sum(const float* part, int64_t rows, int ntn, float* out, hipStream_t s);
 int launch_gather_f32(const float* src, const int32_t* idx, int64_t n, float* out, hipStream_t s);
 int launch_router_backward(const float* dg_slot, const int32_t* inv_perm, const int32_t* topk_idx,

@@ -94,6 +94,8 @@ int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean,
 //   TR_SCALE:  out = src[j][c] * scale[j]           (fp32 product, rounded once)
 //   TR_SWIGLU: out = scale[j] * SiLU(src[j][c]) * src2[j][c]  (gated activation from fp32 a, u;
 //              scale optional); with split_lo the remainder v - bf16(v) goes to rows W..2W-1
+// TR_COPY may read its rows through a row map: source row rmap[j] / rdiv instead of j (the
+// layer backward reads x and dout rows through the schedule instead of slot copies).
 // 64 x 64 tiles through LDS; each tile lies inside one group (poff is 64-aligned).
 template <int MODE>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
                                                             const float* __restrict__ scale, int64_t lds,
                                                             int W, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ poff, int G,
-                                                            uint16_t* __restrict__ out, int64_t ldo, int split_lo) {
+                                                            uint16_t* __restrict__ out, int64_t ldo, int split_lo,
+                                                            const int32_t* __restrict__ rmap, int rdiv) {
   __shared__ uint16_t tile[64][66];
   __shared__ uint16_t tile_lo[64][66];
   const int p0 = blockIdx.x * 64;          // padded column block
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
     uint16_t v = 0, vlo = 0;
     if (r < valid && c0 + tx < W) {
       const int64_t j = jbase + r;
-      if (MODE == TR_COPY) v = src[j * lds + c0 + tx];
+      if (MODE == TR_COPY) v = src[(rmap ? (int64_t)(rmap[j] / rdiv) : j) * lds + c0 + tx];
       if (MODE == TR_SCALE) v = f2bf(bf2f(src[j * lds + c0 + tx]) * scale[j]);
       if (MODE == TR_SWIGLU) {
         const float* fa = reinterpret_cast<const float*>(src);
@@ -152,7 +155,8 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
 __global__ __launch_bounds__(256) void transpose_pad_copy16_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                                    int W, const int32_t* __restrict__ offsets,
                                                                    const int32_t* __restrict__ poff, int G,
-                                                                   uint16_t* __restrict__ out, int64_t ldo) {
+                                                                   uint16_t* __restrict__ out, int64_t ldo,
+                                                                   const int32_t* __restrict__ rmap, int rdiv) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
   const int p0 = blockIdx.x * 64;          // padded column block
   const int c0 = blockIdx.y * 64;          // feature block
@@ -170,7 +174,10 @@ __global__ __launch_bounds__(256) void transpose_pad_copy16_kernel(const uint16_
   for (int pass = 0; pass < 2; ++pass) {
     const int r = rr + 32 * pass;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < valid && c0 + q * 8 < W) v = *reinterpret_cast<const u32x4*>(src + (int64_t)(jbase + r) * lds + c0 + q * 8);
+    if (r < valid && c0 + q * 8 < W) {
+      const int64_t j = rmap ? (int64_t)(rmap[jbase + r] / rdiv) : (int64_t)(jbase + r);
+      v = *reinterpret_cast<const u32x4*>(src + j * lds + c0 + q * 8);
+    }
     *reinterpret_cast<u32x4*>(&tile[r][q * 8]) = v;
   }
   __syncthreads();
@@ -189,7 +196,8 @@ __global__ __launch_bounds__(256) void transpose_pad_copy16_kernel(const uint16_
 
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
                          const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
-                         int64_t ldo, hipStream_t s, int split_lo) {
+                         int64_t ldo, hipStream_t s, int split_lo, const int32_t* rmap, int rdiv) {
+  if (rmap && mode != TR_COPY) return MOE_ERR_UNSUPPORTED;
   dim3 grid((unsigned)((max_padded + 63) / 64), (unsigned)((W + 63) / 64)), block(256);
   const uint16_t* a = (const uint16_t*)src;
   const uint16_t* b = (const uint16_t*)src2;
@@ -197,13 +205,13 @@ int launch_transpose_pad(int mode, const void* src, const void* src2, const floa
   const bool v16 = mode == TR_COPY && !split_lo && W % 8 == 0 && lds % 8 == 0 && ldo % 8 == 0 &&
                    ((uintptr_t)src & 15) == 0 && ((uintptr_t)out & 15) == 0;
   if (v16)
-    hipLaunchKernelGGL(transpose_pad_copy16_kernel, grid, block, 0, s, a, lds, W, offsets, poff, G, o, ldo);
+    hipLaunchKernelGGL(transpose_pad_copy16_kernel, grid, block, 0, s, a, lds, W, offsets, poff, G, o, ldo, rmap, rdiv);
   else if (mode == TR_COPY)
-    hipLaunchKernelGGL(transpose_pad_kernel<TR_COPY>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo);
+    hipLaunchKernelGGL(transpose_pad_kernel<TR_COPY>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, rmap, rdiv);
   else if (mode == TR_SCALE)
-    hipLaunchKernelGGL(transpose_pad_kernel<TR_SCALE>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo);
+    hipLaunchKernelGGL(transpose_pad_kernel<TR_SCALE>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, nullptr, 1);
   else
-    hipLaunchKernelGGL(transpose_pad_kernel<TR_SWIGLU>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo);
+    hipLaunchKernelGGL(transpose_pad_kernel<TR_SWIGLU>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, nullptr, 1);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -403,38 +403,57 @@ def test_experts_backward_dgrad_one_pass(m, counts):
         assert torch.equal(r[k], base[k]), k
 
 
-@pytest.mark.parametrize('flags', [0, 0x100000, 0x40], ids=['gather', 'dispatch_copy', 'one_pass'])
-def test_layer_keep_activations_bitwise(m, flags):
-    """moe_forward_keep + moe_backward_kept: the routed a, u handed from the layer forward to the
-    layer backward instead of replayed; every output bitwise that of moe_forward + moe_backward."""
-    cfg = LAYER_BWD
-    print(f'[backward] layer keep {cfg.name} flags={flags:#x}', flush=True)
+def layer_fwd_bwd(m, cfg, flags, keep):
+    """One layer forward (moe_forward, or moe_forward_keep) and backward (moe_backward, or
+    moe_backward_kept) on `cfg`; every output."""
     H = synth.host_layer(cfg)
     L = synth.to_device(H)
     E, I, D, Is, T, K = cfg.E, cfg.I, cfg.D, cfg.I_shared, cfg.T, cfg.K
     dout = bf(synth.host_dout(cfg, T))
-    res = []
-    for keep in (False, True):
-        run = ForwardRun(m, L, flags=flags, want_parts=False)
-        act = [torch.full((T * K, I), float('nan'), device='cuda') for _ in range(2)]
-        if keep:
-            m.forward_keep(run.p, L.x, L.logits, run.weights, run.out, run.routing, *act, run.ws)
-        else:
-            run()
-        gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
-                  dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
-                  dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
-        G = m.make_grads(**gr)
-        dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
-        dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
-        dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
-        wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(run.p),),
-                          dtype=torch.uint8, device='cuda')
-        if keep:
-            m.backward_kept(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, *act, wsb)
-        else:
-            m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, wsb)
-        torch.cuda.synchronize()
-        res.append(dict(out=run.out.clone(), perm=run.perm.clone(), dx=dx, dtw=dtw, dlg=dlg, **gr))
+    run = ForwardRun(m, L, flags=flags, want_parts=False)
+    act = [torch.full((T * K, I), float('nan'), device='cuda') for _ in range(2)]
+    if keep:
+        m.forward_keep(run.p, L.x, L.logits, run.weights, run.out, run.routing, *act, run.ws)
+    else:
+        run()
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    G = m.make_grads(**gr)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(run.p),),
+                      dtype=torch.uint8, device='cuda')
+    if keep:
+        m.backward_kept(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, *act, wsb)
+    else:
+        m.backward(run.p, dout, L.x, L.logits, run.weights, run.routing, dx, G, dtw, dlg, wsb)
+    torch.cuda.synchronize()
+    return dict(out=run.out.clone(), perm=run.perm.clone(), dx=dx, dtw=dtw, dlg=dlg, **gr), wsb.numel()
+
+
+@pytest.mark.parametrize('flags', [0, 0x100000, 0x40], ids=['gather', 'dispatch_copy', 'one_pass'])
+def test_layer_keep_activations_bitwise(m, flags):
+    """moe_forward_keep + moe_backward_kept: the routed a, u handed from the layer forward to the
+    layer backward instead of replayed; every output bitwise that of moe_forward + moe_backward."""
+    print(f'[backward] layer keep {LAYER_BWD.name} flags={flags:#x}', flush=True)
+    res = [layer_fwd_bwd(m, LAYER_BWD, flags, keep)[0] for keep in (False, True)]
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k
+
+
+@pytest.mark.parametrize('keep', [False, True], ids=['replay', 'kept'])
+@pytest.mark.parametrize('extra', [0, 0x40 | 0x80], ids=['default', 'one_pass_lo_mxfp8'])
+def test_layer_gather_equals_dispatch_copy_bitwise(m, keep, extra):
+    """The BF16 layer forward and backward read x and dout rows through the schedule (GEMM operand
+    loads and the weight gradients' transposes); MOE_FLAG_DISPATCH_COPY makes the slot copies
+    first. Same rows in the same order: every output is the same bits, and the gathering
+    backward needs no slot buffers."""
+    print(f'[backward] layer gather vs copy keep={keep} flags={extra:#x}', flush=True)
+    a, wa = layer_fwd_bwd(m, LAYER_BWD, extra, keep)
+    b, wb = layer_fwd_bwd(m, LAYER_BWD, extra | 0x100000, keep)
+    n = LAYER_BWD.T * LAYER_BWD.K
+    assert wb - wa >= 2 * n * LAYER_BWD.D * 2
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
