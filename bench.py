@@ -758,13 +758,19 @@ LANE_STREAMS = []
 
 
 def lane_streams_first():
-    """The lanes of moe_forward_lanes: the first three streams this process creates. HIP binds
-    each stream to one of its GPU_MAX_HW_QUEUES hardware queues (4 by default); measured with
-    rocprofv3's queue ids, the default stream and the first three streams created hold the four
-    queues and later streams share them, and two lanes on one queue run one after the other."""
+    """The lanes of moe_forward_lanes: three streams that receive work before any other stream
+    but the default one. HIP binds a stream to one of its GPU_MAX_HW_QUEUES hardware queues (4 by
+    default) when the stream first receives work, and later streams share those queues; two lanes
+    on one queue run one after the other (measured: rocprofv3's queue ids, and b = 512 at the DSV3
+    shape taking 18.8 instead of 12.8 ms when another stream was used first)."""
     import torch
     if not LANE_STREAMS:
+        torch.zeros(1, device='cuda')                 # the default stream takes its queue first
         LANE_STREAMS.extend(torch.cuda.Stream() for _ in range(3))
+        for s in LANE_STREAMS:
+            with torch.cuda.stream(s):
+                torch.zeros(1, device='cuda')         # first work: binds the stream to its queue
+        torch.cuda.synchronize()
 
 
 def chunk_leg(moe, cfg, L, weights, routing, stream, unchunked_ms, steps=10, warmup=2, bs=(512, 2048, 4096, 32768)):

@@ -355,11 +355,11 @@ typedef struct moe_lanes {
  * under MOE_F32 or MOE_FLAG_FUSED_GATHER: MOE_ERR_UNSUPPORTED); lanes NULL, count outside
  * [1, MOE_MAX_LANES - 1], or a NULL stream or event: MOE_ERR_INVALID_ARG. Overlapping calls on
  * the same events or workspace race. The lanes overlap only where `stream` and the lane streams
- * sit on distinct hardware queues. HIP binds each stream to one of GPU_MAX_HW_QUEUES queues (4
- * by default); as measured through rocprofv3's queue ids, the default stream and the first three
- * streams a process creates hold the four queues and later streams share them, so lanes on
- * later streams may run one after the other (same outputs, less overlap). Give the first streams
- * the process creates as lanes, or raise GPU_MAX_HW_QUEUES. */
+ * sit on distinct hardware queues. HIP binds a stream to one of GPU_MAX_HW_QUEUES queues (4 by
+ * default) when the stream first receives work, and streams beyond that share queues (measured
+ * through rocprofv3's queue ids and the run times), so lanes may run one after the other (same
+ * outputs, less overlap). Give lanes streams that received work before any other stream but
+ * `stream`, e.g. one small kernel each at start-up, or raise GPU_MAX_HW_QUEUES. */
 int moe_forward_lanes(const moe_problem *p, const void *x, const float *logits, const moe_weights *w,
                       void *out, const moe_routing *routing, void *y_routes, void *shared_out,
                       void *ws, size_t ws_bytes, hipStream_t stream, const moe_lanes *lanes);
