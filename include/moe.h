@@ -69,10 +69,11 @@ typedef enum moe_dtype {
  *   dispatch and the whole expert FFN before the next (Notes "Mixture-of-Kittens: MoE Megakernel
  *   for NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
  *   values are rounded up to a multiple of 256 and clamped to [max(256, T*K/1024), T*K]. With
- *   chunks, the dispatched rows and h live in a ring of ring_stages chunk stages (BF16 and
- *   MXFP8). moe_forward / moe_forward_stages return MOE_ERR_UNSUPPORTED for chunk_rows > 0 under
- *   MOE_F32 or MOE_FLAG_FUSED_GATHER (no dispatched copies to hold), as do moe_forward_keep and
- *   the expert-level forwards (their slots are not dispatched through a ring). The backward entry
+ *   chunks, h lives in a ring of ring_stages chunk stages (BF16 and MXFP8), and so do the
+ *   dispatched rows where there are any (MXFP8, or BF16 under MOE_FLAG_DISPATCH_COPY; BF16 chunks
+ *   otherwise read x through the schedule). moe_forward / moe_forward_stages return
+ *   MOE_ERR_UNSUPPORTED for chunk_rows > 0 under MOE_F32, as do moe_forward_keep and the
+ *   expert-level forwards (their slots are not carried through a ring). The backward entry
  *   points do not chunk: they accept the forward's problem descriptor and ignore chunk_rows and
  *   ring_stages.
  * ring_stages: macrobatch ring depth (Notes, section "A ring buffer instead of a host
@@ -86,11 +87,12 @@ typedef struct moe_problem {
   int32_t flags;
 } moe_problem;
 
-/* The unchunked BF16 and fp32 forwards (moe_forward, moe_forward_stages, moe_forward_keep) read
- * the x rows of the routed up/gate GEMM through the schedule (row j of expert-slot order is
- * x[perm[j] / K]) instead of a dispatched copy: the pages' pull dispatch done by the GEMM's own
- * operand loads, with no copy pass (DSV3 shape: 9.41 against 9.66 ms per forward). This is the
- * default; MOE_FLAG_FUSED_GATHER names it and is accepted. The BF16 layer backward (moe_backward,
+/* The BF16 and fp32 forwards (moe_forward, moe_forward_stages, moe_forward_keep, moe_forward_lanes;
+ * BF16 chunks too) read the x rows of the routed up/gate GEMM through the schedule (row j of
+ * expert-slot order is x[perm[j] / K]) instead of a dispatched copy: the pages' pull dispatch done
+ * by the GEMM's own operand loads, with no copy pass (DSV3 shape: 9.41 against 9.66 ms per
+ * forward). This is the default; MOE_FLAG_FUSED_GATHER names it and is accepted (under MOE_MXFP8,
+ * which quantises x while dispatching it: MOE_ERR_UNSUPPORTED). The BF16 layer backward (moe_backward,
  * moe_backward_kept) reads x and dout the same way in its GEMMs and transposes (DSV3 shape: 45.3
  * against 45.7 ms, and no 2 T K D-element slot buffers in its workspace). MOE_FLAG_DISPATCH_COPY
  * instead writes the expert-contiguous slot copies first (as the chunked ring, MXFP8 and fp32
@@ -352,7 +354,7 @@ typedef struct moe_lanes {
  * counters of their own in the workspace's first 256 bytes. Outputs are bitwise those of
  * moe_forward for the same problem: every output tile is the same workgroup sum. With one chunk
  * (chunk_rows == 0) the lanes only fork and join. Requirements as moe_forward (chunk_rows > 0
- * under MOE_F32 or MOE_FLAG_FUSED_GATHER: MOE_ERR_UNSUPPORTED); lanes NULL, count outside
+ * under MOE_F32: MOE_ERR_UNSUPPORTED); lanes NULL, count outside
  * [1, MOE_MAX_LANES - 1], or a NULL stream or event: MOE_ERR_INVALID_ARG. Overlapping calls on
  * the same events or workspace race. The lanes overlap only where `stream` and the lane streams
  * sit on distinct hardware queues. HIP binds a stream to one of GPU_MAX_HW_QUEUES queues (4 by

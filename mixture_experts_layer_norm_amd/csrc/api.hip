@@ -73,9 +73,9 @@ WsLayout ws_layout(const moe_problem& p) {
   L.tile_off = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_clean = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_poff = o; o = align256(o + (size_t)(p.E + 1) * 4);
-  // dispatched slot rows: the chunked ring, MXFP8 (quantised in dispatch) and MOE_FLAG_DISPATCH_COPY;
-  // otherwise GEMM1 reads x through the schedule and no copy is made
-  const bool copy = L.chunked || mx || (p.flags & MOE_FLAG_DISPATCH_COPY);
+  // dispatched slot rows (all of them, or a ring of chunk stages): MXFP8 (quantised in dispatch) and
+  // MOE_FLAG_DISPATCH_COPY; otherwise GEMM1 reads x through the schedule and no copy is made
+  const bool copy = mx || (p.flags & MOE_FLAG_DISPATCH_COPY);
   L.x_slot = o; o = align256(o + (copy ? (size_t)L.ring_rows * p.D * (mx ? 1 : act) : 0));
   L.x_slot_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.D / 32) : 0));
   L.h = o; o = align256(o + (size_t)L.ring_rows * p.I * (mx ? 1 : act));
@@ -306,8 +306,9 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
   if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  // the chunked ring holds dispatched copies; with the gather fused into GEMM1 there are none
-  if (p->chunk_rows > 0 && ((p->flags & MOE_FLAG_FUSED_GATHER) || p->dtype == MOE_F32)) return MOE_ERR_UNSUPPORTED;
+  // MXFP8 quantises x while dispatching it: there is no gathered form
+  if (mx && (p->flags & MOE_FLAG_FUSED_GATHER)) return MOE_ERR_UNSUPPORTED;
+  if (p->chunk_rows > 0 && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || (y_routes && !aligned16(y_routes)) ||
@@ -386,6 +387,9 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     }
     if (laned && (st = shared_expert(stream, pc))) return st;
     MOE_MARK(MOE_STAGE_DISPATCH);
+    // BF16 chunks read x through the schedule (the ring then holds only h); MXFP8 dispatches
+    // (quantising) into the ring, as does BF16 under MOE_FLAG_DISPATCH_COPY
+    const bool gather_x = !mx && !(p->flags & MOE_FLAG_DISPATCH_COPY);
     const int64_t xrow = mx ? p->D : (int64_t)p->D * 2, hrow = mx ? p->I : (int64_t)p->I * 2;   // bytes per row
     uint8_t* xr = (uint8_t*)(wsb + L.x_slot);
     uint8_t* hr = (uint8_t*)(wsb + L.h);
@@ -404,9 +408,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       // ring stage c % S was last read by chunk c - S (its up/gate and down): on another lane, wait
       if (NLn > 1 && c >= S && (c - S) % NLn != lane && hipStreamWaitEvent(cs, lanes->events[c % S], 0) != hipSuccess)
         return MOE_ERR_HIP;
-      st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + stage * xrow,
-                           mx ? xs + stage * (p->D / 32) : nullptr, cs);
-      if (st) return st;
+      if (!gather_x) {
+        st = launch_dispatch(x, p->dtype, r->perm, p->K, p->D, c0, rows, xr + stage * xrow,
+                             mx ? xs + stage * (p->D / 32) : nullptr, cs);
+        if (st) return st;
+      }
       Grouped gc;
       gc.row_off = crow + (int64_t)c * (p->E + 1);
       gc.tile_off = ctile + (int64_t)c * (p->E + 1);
@@ -426,7 +432,8 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
         st = launch_gemm_mx(g2, hs + shift * (p->I / 32), w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr,
                             gc, EPI_STORE, cs);
       } else {
-        st = expert_ffn(p->dtype, gc, xr + shift * xrow, p->D, nullptr, 1, w->w_gate, w->w_up, w->w_down, p->D,
+        st = expert_ffn(p->dtype, gc, gather_x ? x : (const void*)(xr + shift * xrow), p->D,
+                        gather_x ? r->perm : nullptr, gather_x ? p->K : 1, w->w_gate, w->w_up, w->w_down, p->D,
                         p->I, (int64_t)p->I * p->D, (int64_t)p->D * p->I, hr + shift * hrow, yr, r->perm, cs,
                         nullptr, cpc);
       }

@@ -212,6 +212,13 @@ def test_chunked_ring_bitwise_equals_unchunked(m, chunk, stages):
     chunked_equals_unchunked(m, chunk, stages)
 
 
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (768, 5)])
+def test_chunked_ring_dispatch_copy_bitwise_equals_unchunked(m, chunk, stages):
+    """The same with MOE_FLAG_DISPATCH_COPY: each chunk's x rows dispatched into its ring stage
+    instead of read through the schedule."""
+    chunked_equals_unchunked(m, chunk, stages, flags=m.MOE_FLAG_DISPATCH_COPY)
+
+
 @pytest.mark.skip(reason='the persistent work-queue chunk kernel hung on MI355X twice (second time after '
                          'bounding its waits); its cause is not yet shown, so the path is switched off and '
                          'MOE_FLAG_PERSISTENT returns MOE_ERR_UNSUPPORTED')

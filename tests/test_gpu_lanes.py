@@ -55,6 +55,20 @@ def test_lanes_bitwise_equal_unchunked(m, chunk, stages, count):
         assert_same(a, b, f'rep {rep}')
 
 
+def test_lanes_dispatch_copy(m):
+    """Lanes with each chunk's x rows dispatched into the ring (MOE_FLAG_DISPATCH_COPY): stage
+    events then guard x copies as well as h."""
+    print(f'[lanes] {SMALL_BF16.name} dispatch copy', flush=True)
+    L = synth.to_device(synth.host_layer(SMALL_BF16))
+    a = ForwardRun(m, L)()
+    b = ForwardRun(m, L, chunk_rows=256, ring_stages=3, flags=m.MOE_FLAG_DISPATCH_COPY)
+    streams, events = make_lanes(m, b.p, 3)
+    for rep in range(3):
+        b.lanes(streams, events)
+        torch.cuda.synchronize()
+        assert_same(a, b, f'rep {rep}')
+
+
 def test_lanes_with_persistent_gemms(m):
     """Every GEMM forced persistent: the lanes' launches run at once, each on its own counters."""
     print(f'[lanes] {SMALL_BF16.name} persistent', flush=True)
