@@ -102,7 +102,7 @@ int launch_router_backward(const float* dg_slot, const int32_t* inv_perm, const 
                            hipStream_t s);
 int launch_reverse_dispatch(const void* dx_slot, const int32_t* inv_perm, const void* dx_shared, void* dx, int T,
                             int K, int D, hipStream_t s);
-enum { TR_COPY = 0, TR_SCALE = 1, TR_SWIGLU = 2 };   // TR_SWIGLU reads fp32 a and u
+enum { TR_COPY = 0, TR_SWIGLU = 2 };   // TR_SWIGLU reads fp32 a and u
 int launch_quantize_mx(const uint16_t* src, int64_t rows, int cols, uint8_t* q, uint8_t* sc,
                        hipStream_t s);
 // MXFP8 backward operands (mx_backward.hip)

@@ -91,7 +91,6 @@ int launch_group_prefix(const int32_t* offsets, int G, int rows, int32_t* clean,
 // offsets[e+1]) become columns poff[e] + (j - offsets[e]) of out [W][ldo]; columns in a group's
 // padding become 0. Modes:
 //   TR_COPY:   out = src[j][c]
-//   TR_SCALE:  out = src[j][c] * scale[j]           (fp32 product, rounded once)
 //   TR_SWIGLU: out = scale[j] * SiLU(src[j][c]) * src2[j][c]  (gated activation from fp32 a, u;
 //              scale optional); with split_lo the remainder v - bf16(v) goes to rows W..2W-1
 // TR_COPY may read its rows through a row map: source row rmap[j] / rdiv instead of j (the
@@ -126,7 +125,6 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
     if (r < valid && c0 + tx < W) {
       const int64_t j = jbase + r;
       if (MODE == TR_COPY) v = src[(rmap ? (int64_t)(rmap[j] / rdiv) : j) * lds + c0 + tx];
-      if (MODE == TR_SCALE) v = f2bf(bf2f(src[j * lds + c0 + tx]) * scale[j]);
       if (MODE == TR_SWIGLU) {
         const float* fa = reinterpret_cast<const float*>(src);
         const float* fu = reinterpret_cast<const float*>(src2);
@@ -197,6 +195,7 @@ __global__ __launch_bounds__(256) void transpose_pad_copy16_kernel(const uint16_
 int launch_transpose_pad(int mode, const void* src, const void* src2, const float* scale, int64_t lds, int W,
                          const int32_t* offsets, const int32_t* poff, int G, int64_t max_padded, void* out,
                          int64_t ldo, hipStream_t s, int split_lo, const int32_t* rmap, int rdiv) {
+  if (mode != TR_COPY && mode != TR_SWIGLU) return MOE_ERR_INVALID_ARG;
   if (rmap && mode != TR_COPY) return MOE_ERR_UNSUPPORTED;
   dim3 grid((unsigned)((max_padded + 63) / 64), (unsigned)((W + 63) / 64)), block(256);
   const uint16_t* a = (const uint16_t*)src;
@@ -208,8 +207,6 @@ int launch_transpose_pad(int mode, const void* src, const void* src2, const floa
     hipLaunchKernelGGL(transpose_pad_copy16_kernel, grid, block, 0, s, a, lds, W, offsets, poff, G, o, ldo, rmap, rdiv);
   else if (mode == TR_COPY)
     hipLaunchKernelGGL(transpose_pad_kernel<TR_COPY>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, rmap, rdiv);
-  else if (mode == TR_SCALE)
-    hipLaunchKernelGGL(transpose_pad_kernel<TR_SCALE>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, nullptr, 1);
   else
     hipLaunchKernelGGL(transpose_pad_kernel<TR_SWIGLU>, grid, block, 0, s, a, b, scale, lds, W, offsets, poff, G, o, ldo, split_lo, nullptr, 1);
   MOE_LAUNCH_CHECK();
