@@ -121,19 +121,19 @@ typedef struct moe_problem {
 /* Run the chunked path (chunk_rows > 0) as one persistent work-queue kernel instead of three
  * launches per chunk. Currently disabled: a call with this flag returns MOE_ERR_UNSUPPORTED. */
 #define MOE_FLAG_PERSISTENT 0x4
-/* Persistent grouped GEMMs (MOE_BF16; the sparsenotes page "Mixture-of-Kittens: MoE Megakernel for
- * NVL72s", sections "Granularity as a tunable" and "The production details"): the up/gate and down
- * GEMMs of the forward entry points (moe_forward, moe_forward_stages, moe_forward_keep, and the
+/* Persistent grouped GEMMs (MOE_BF16 and MOE_MXFP8; the sparsenotes page "Mixture-of-Kittens: MoE
+ * Megakernel for NVL72s", sections "Granularity as a tunable" and "The production details"): the
+ * up/gate and down GEMMs (BF16 or block-scaled) of the forward entry points (moe_forward, moe_forward_stages, moe_forward_keep, and the
  * expert-level moe_experts_forward, moe_experts_forward_keep; routed and shared expert) can run as
  * persistent kernels, one workgroup per CU taking 256 x 256 tiles from ticket counters kept in
  * the first 256 bytes of the workspace, instead of one workgroup per tile. Without this flag a
  * GEMM runs persistent where it has at least 12 tiles per workgroup (e.g. the routed GEMMs at
  * T = 8192, 256 experts, K = 8), per tile otherwise; with it, always. Each tile is computed by one
  * workgroup in the same order either way, so every output is bitwise the same. Workgroups never
- * wait for each other. MOE_F32 and MOE_MXFP8 forwards with the flag: MOE_ERR_UNSUPPORTED. The
- * backward entry points apply the same rule to their BF16 GEMMs (replay, dgrad-down, dgrad-up,
- * K-grouped weight gradients; under MOE_MXFP8 the shared expert's), with the counters in their own
- * workspace's first 256 bytes. */
+ * wait for each other. MOE_F32 forwards with the flag: MOE_ERR_UNSUPPORTED. The backward entry
+ * points apply the same rule to their GEMMs (replay, dgrad-down, dgrad-up, K-grouped weight
+ * gradients; BF16, and block-scaled under MOE_MXFP8), with the counters in their own workspace's
+ * first 256 bytes. */
 #define MOE_FLAG_PERSISTENT_GEMM 0x10000
 /* With MOE_FLAG_PERSISTENT_GEMM (alone: MOE_ERR_INVALID_ARG): between tiles, the persistent GEMMs
  * read the int32 workgroup budget at byte offset MOE_WS_CU_BUDGET_OFFSET of the workspace the call

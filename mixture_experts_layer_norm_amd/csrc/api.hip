@@ -305,7 +305,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   const bool mx = p->dtype == MOE_MXFP8;
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
-  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   // MXFP8 quantises x while dispatching it: there is no gathered form
   if (mx && (p->flags & MOE_FLAG_FUSED_GATHER)) return MOE_ERR_UNSUPPORTED;
   if (p->chunk_rows > 0 && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
@@ -318,11 +318,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   const int64_t n = (int64_t)p->T * p->K;
   void* yr = y_routes ? y_routes : (void*)(wsb + L.y_routes);
   void* sho = p->I_shared > 0 ? (shared_out ? shared_out : (void*)(wsb + L.sh_out)) : nullptr;
-  // persistent GEMMs (BF16): ticket counters and the workgroup budget word in the error word's
-  // block; taken where a launch has enough tiles per workgroup, always with the flag
+  // persistent GEMMs (BF16 and MXFP8): ticket counters and the workgroup budget word in the error
+  // word's block; taken where a launch has enough tiles per workgroup, always with the flag
   Persist pcs;
   const Persist* pc = nullptr;
-  if (p->dtype == MOE_BF16) {
+  if (p->dtype != MOE_F32) {
     pcs.tickets = (int32_t*)(wsb + L.err + kTicketsOffset);
     pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
     pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)(wsb + L.err + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
@@ -423,14 +423,14 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
         g1.A = xr + shift * xrow; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
         g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hr + shift * hrow; g1.ldc = p->I;
         st = launch_gemm_mx(g1, xs + shift * (p->D / 32), w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32),
-                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, cs);
+                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, cs, cpc);
         if (st) return st;
         GemmArgs g2;
         g2.A = hr + shift * hrow; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I;
         g2.b_group_stride = (int64_t)p->D * p->I; g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D;
         g2.c_scatter = r->perm;
         st = launch_gemm_mx(g2, hs + shift * (p->I / 32), w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr,
-                            gc, EPI_STORE, cs);
+                            gc, EPI_STORE, cs, cpc);
       } else {
         st = expert_ffn(p->dtype, gc, gather_x ? x : (const void*)(xr + shift * xrow), p->D,
                         gather_x ? r->perm : nullptr, gather_x ? p->K : 1, w->w_gate, w->w_up, w->w_down, p->D,
@@ -470,18 +470,18 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     if (keep) {
       // a, u to the caller in fp32 (the backward's replay GEMM), h quantised from them
       g1.C = act_a; g1.C2 = act_u;
-      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), nullptr, gr, EPI_SAVE_AU, stream);
+      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), nullptr, gr, EPI_SAVE_AU, stream, pc);
       if (st) return st;
       st = launch_swiglu_rows_mx(act_a, act_u, n * (p->I / 32), hq, hs, stream);
     } else {
-      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream);
+      st = launch_gemm_mx(g1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU, stream, pc);
     }
     if (st) return st;
     MOE_MARK(MOE_STAGE_DOWN);
     GemmArgs g2;
     g2.A = hq; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I; g2.b_group_stride = (int64_t)p->D * p->I;
     g2.N = p->D; g2.K = p->I; g2.C = yr; g2.ldc = p->D; g2.c_scatter = r->perm;
-    st = launch_gemm_mx(g2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream);
+    st = launch_gemm_mx(g2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream, pc);
     if (st) return st;
   } else {
     // GEMM1 reads x rows through the schedule (row j = x[perm[j] / K]) unless the slot copy is asked for

@@ -141,7 +141,7 @@ struct CoreBufs {
   // MXFP8 codes and scales of the weight gradients' second pass: [da | du] and g*h low halves,
   // x and dy, each [features][Spad] along the slots (all null: both passes in BF16)
   uint8_t *q_dau, *s_dau, *q_gh, *s_gh, *q_x, *s_x, *q_dy, *s_dy;
-  const Persist* pc = nullptr;   // persistent GEMM control (BF16), see launch_gemm_bf16
+  const Persist* pc = nullptr;   // persistent GEMM control, see launch_gemm_bf16
 };
 
 // Backward of one set of groups (routed experts, or the shared expert as one group).
@@ -240,7 +240,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   if ((st = launch_gemm_bf16_kgroup(w1, G, s, b.pc))) return st;
   GemmArgs m1 = w1;
   m1.A = b.q_dy; m1.B = b.q_gh; m1.c_accumulate = 1;
-  if ((st = launch_gemm_mx_kgroup(m1, b.s_dy, b.s_gh, G, s))) return st;
+  if ((st = launch_gemm_mx_kgroup(m1, b.s_dy, b.s_gh, G, s, b.pc))) return st;
   // [dW_gate; dW_up][g] = sum_j [da_j; du_j] x_j^T -> rows < I: dW_gate, rows >= I: dW_up
   GemmArgs w2;
   w2.A = b.dauT; w2.lda = Sp; w2.B = b.xT; w2.ldb = Sp; w2.k_off = poff; w2.M = 2 * I; w2.N = D;
@@ -248,7 +248,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
   if ((st = launch_gemm_bf16_kgroup(w2, G, s, b.pc))) return st;
   GemmArgs m2 = w2;
   m2.A = b.q_dau; m2.B = b.q_x; m2.c_accumulate = 1;
-  return launch_gemm_mx_kgroup(m2, b.s_dau, b.s_x, G, s);
+  return launch_gemm_mx_kgroup(m2, b.s_dau, b.s_x, G, s, b.pc);
 }
 
 // MXFP8 backward of the routed groups (the shared expert stays BF16). Weights are the forward's
@@ -263,7 +263,7 @@ static int core_backward(int G, int64_t n_cap, int D, int I, const void* x_rows,
 static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_rows, const void* dy_rows,
                             const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                             const moe_weights* w, void* dx_rows, float* dg_rows, float* dw_gate, float* dw_up,
-                            float* dw_down, char* ws, const BwdLayout& L, hipStream_t s,
+                            float* dw_down, char* ws, const BwdLayout& L, hipStream_t s, const Persist* pc,
                             const float* kept_a = nullptr, const float* kept_u = nullptr) {
   int st;
   auto B = [&](size_t off) { return (uint8_t*)(ws + off); };
@@ -296,12 +296,12 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
     GemmArgs r;   // replay
     r.A = B(L.mq_x); r.lda = D; r.B = w->w_gate; r.B2 = w->w_up; r.ldb = D; r.b_group_stride = ID;
     r.N = I; r.K = D; r.C = act_a; r.C2 = act_u; r.ldc = I;
-    if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s))) return st;
+    if ((st = launch_gemm_mx(r, B(L.ms_x), w->sc_gate, w->sc_up, ID / 32, nullptr, grp, EPI_SAVE_AU, s, pc))) return st;
   }
   GemmArgs d;   // dgrad-down
   d.A = B(L.mq_dy); d.lda = D; d.B = B(L.mq_wdT); d.ldb = D; d.b_group_stride = ID;
   d.N = I; d.K = D; d.C = F(L.m_dhp); d.ldc = I; d.c_f32 = 1;
-  if ((st = launch_gemm_mx(d, B(L.ms_dy), B(L.ms_wdT), nullptr, ID / 32, nullptr, grp, EPI_STORE, s))) return st;
+  if ((st = launch_gemm_mx(d, B(L.ms_dy), B(L.ms_wdT), nullptr, ID / 32, nullptr, grp, EPI_STORE, s, pc))) return st;
   // SwiGLU backward: [da | du] quantised along I (dgrad-up), h and [da | du] along the slots
   // (weight gradients), dg from per-tile partial sums
   if ((st = launch_mx_swiglu_bwd_t(act_a, act_u, F(L.m_dhp), g_rows, I, offs, poff, G, S, B(L.mq_dau),
@@ -311,18 +311,19 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   GemmArgs u;   // dgrad-up, K = 2I
   u.A = B(L.mq_dau); u.lda = 2 * I; u.B = B(L.mq_wguT); u.ldb = 2 * I; u.b_group_stride = 2 * ID;
   u.N = D; u.K = 2 * I; u.C = dx_rows; u.ldc = D;
-  if ((st = launch_gemm_mx(u, B(L.ms_dau), B(L.ms_wguT), nullptr, 2 * ID / 32, nullptr, grp, EPI_STORE, s))) return st;
+  if ((st = launch_gemm_mx(u, B(L.ms_dau), B(L.ms_wguT), nullptr, 2 * ID / 32, nullptr, grp, EPI_STORE, s, pc)))
+    return st;
 
   int32_t* order = G > 1 ? (int32_t*)(ws + L.order) : nullptr;
   if (order && (st = launch_group_order(poff, G, order, s))) return st;
   GemmArgs w1;  // dW_down [G][D][I]
   w1.A = B(L.mq_gdyT); w1.lda = S; w1.B = B(L.mq_hT); w1.ldb = S; w1.k_off = poff; w1.k_order = order;
   w1.M = D; w1.N = I; w1.C = dw_down; w1.ldc = I; w1.c_group_stride = ID;
-  if ((st = launch_gemm_mx_kgroup(w1, B(L.ms_gdyT), B(L.ms_hT), G, s))) return st;
+  if ((st = launch_gemm_mx_kgroup(w1, B(L.ms_gdyT), B(L.ms_hT), G, s, pc))) return st;
   GemmArgs w2;  // [dW_gate; dW_up] [G][I][D] each
   w2.A = B(L.mq_dauT); w2.lda = S; w2.B = B(L.mq_xT); w2.ldb = S; w2.k_off = poff; w2.k_order = order;
   w2.M = 2 * I; w2.N = D; w2.C = dw_gate; w2.C2 = dw_up; w2.m_split = I; w2.ldc = D; w2.c_group_stride = ID;
-  return launch_gemm_mx_kgroup(w2, B(L.ms_dauT), B(L.ms_xT), G, s);
+  return launch_gemm_mx_kgroup(w2, B(L.ms_dauT), B(L.ms_xT), G, s, pc);
 }
 
 int core_backward_f32(int G, int64_t n_cap, int64_t max_rows, int D, int I, const float* x_rows, const float* dy_rows,
@@ -348,7 +349,7 @@ static CoreBufs shared_bufs(char* ws, const BwdLayout& L) {
                   u(L.sls_dy)};
 }
 
-// Persistent GEMM control of a backward call (BF16 GEMMs): the ticket counters and the budget word
+// Persistent GEMM control of a backward call: the ticket counters and the budget word
 // sit in the first block of the backward workspace, as in the forward's.
 static Persist bwd_persist(const moe_problem* p, char* wsb, const BwdLayout& L) {
   Persist pc;
@@ -492,12 +493,12 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
   const bool mx = p->dtype == MOE_MXFP8;
   // the non-MX path runs the bf16 MFMA GEMMs, or the fp32 FMA GEMMs under MOE_F32
   const bool f32 = p->dtype == MOE_F32;
-  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  // BF16: the up/gate and down GEMMs run persistent where they have enough tiles per workgroup
+  if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  // BF16 and MXFP8: the up/gate and down GEMMs run persistent where they have enough tiles per workgroup
   // (always with MOE_FLAG_PERSISTENT_GEMM), their ticket counters in the workspace's first block
   Persist pcs;
   const Persist* pc = nullptr;
-  if (p->dtype == MOE_BF16 && ws) {
+  if (p->dtype != MOE_F32 && ws) {
     pcs.tickets = (int32_t*)((char*)ws + kTicketsOffset);
     pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
     pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)((char*)ws + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
@@ -541,7 +542,7 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
       // a, u to the caller in fp32 (the backward's replay GEMM), then h quantised from them
       m1.C = act_a; m1.C2 = act_u;
       if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), nullptr, gr, EPI_SAVE_AU,
-                               stream)))
+                               stream, pc)))
         return st;
       const int64_t nblk = slots * (p->I / 32);
       if (nblk > 0) {
@@ -550,13 +551,14 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
         MOE_LAUNCH_CHECK();
       }
     } else if ((st = launch_gemm_mx(m1, xs, w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32), hs, gr, EPI_SWIGLU,
-                                    stream))) {
+                                    stream, pc))) {
       return st;
     }
     GemmArgs m2;
     m2.A = hq; m2.lda = p->I; m2.B = w->w_down; m2.ldb = p->I; m2.b_group_stride = (int64_t)p->D * p->I;
     m2.N = p->D; m2.K = p->I; m2.C = y_slot; m2.ldc = p->D;
-    if ((st = launch_gemm_mx(m2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream)))
+    if ((st = launch_gemm_mx(m2, hs, w->sc_down, nullptr, (int64_t)p->D * (p->I / 32), nullptr, gr, EPI_STORE, stream,
+                             pc)))
       return st;
   } else {
   GemmArgs g1;
@@ -646,9 +648,10 @@ static int experts_backward_impl(const moe_problem* p, int64_t slots, const void
                                 F(L.f_dh), F(L.f_h), F(L.f_da), F(L.f_du), stream)))
       return st;
   } else if (mx) {
+    const Persist pc = bwd_persist(p, wsb, L);
     if ((st = core_backward_mx(p->E, slots, p->D, p->I, x_slot, dy_slot, g_slot, offs, (int32_t*)(wsb + L.tile_off),
                                (int32_t*)(wsb + L.poff), w, dx_slot, dg_slot, dw->dw_gate, dw->dw_up, dw->dw_down, wsb,
-                               L, stream, act_a, act_u)))
+                               L, stream, &pc, act_a, act_u)))
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);
@@ -751,9 +754,10 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
                                 F(L.f_h), F(L.f_da), F(L.f_du), stream)))
       return st;
   } else if (mx) {
+    const Persist pc = bwd_persist(p, wsb, L);
     if ((st = core_backward_mx(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
                                (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
-                               (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream,
+                               (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream, &pc,
                                act_a, act_u)))
       return st;
   } else {

@@ -171,7 +171,7 @@ struct GemmArgs {
   int32_t c_accumulate = 0;           // fp32 outputs of the MXFP8 GEMM: C += product
 };
 
-// Persistent launch of the forward grouped GEMMs (gemm.hip): tickets, 8 int32 counters in device
+// Persistent launch of the grouped GEMMs (gemm.hip, gemm_mx.hip): tickets, 8 int32 counters in device
 // memory (zeroed by the launch); budget, the workgroup budget word (nullable, read only); force:
 // always persistent, otherwise only where the launch holds at least kPersistMinTilesPerWg tiles
 // per workgroup (its upper bound of tiles, known on the host).
@@ -181,18 +181,25 @@ struct Persist {
   bool force = false;
 };
 constexpr int kPersistMinTilesPerWg = 12;
+// Grid of the persistent form for a launch of at most nb tiles: nw workgroups, or nw = 0 for the
+// per-tile form (pc null, or too few tiles per workgroup and not forced).
+int persistent_grid(int64_t nb, const Persist* pc, int64_t& nw);
+int launch_zero_tickets(int32_t* tickets, hipStream_t s);
 // pc: may run as the persistent kernel (see Persist).
 int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s, const Persist* pc = nullptr);
 int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s, const Persist* pc = nullptr);
 int gemm_tile_cols(Epi epi);
 int launch_chunk_tables(const int32_t* offsets, int E, int n, int b, int C, int32_t* ctile, int32_t* crow,
                         hipStream_t s);
+// pc: may run as the persistent kernel, as launch_gemm_bf16.
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
-                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s);
+                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s,
+                   const Persist* pc = nullptr);
 // K-grouped MXFP8 weight gradients: A [M][lda] and B [N][ldb] E4M3 along K with scales
 // [M][lda / 32], [N][ldb / 32]; group g contracts k in [k_off[g], k_off[g+1]) (multiples of 128);
 // fp32 output as launch_gemm_bf16_kgroup.
-int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s);
+int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s,
+                         const Persist* pc = nullptr);
 // h [n4 * 4] bf16 = SiLU(a) u from fp32 a, u, with the SwiGLU GEMM epilogue's arithmetic.
 int launch_swiglu_rows(const float* a, const float* u, int64_t n4, uint16_t* h, hipStream_t s);
 // The same under MXFP8: nblk blocks of 32 along I -> E4M3 codes q and E8M0 scales sc, as the

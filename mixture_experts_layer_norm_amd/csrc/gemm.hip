@@ -70,77 +70,26 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
 }
 
 // Persistent form of the grouped GEMMs (every epilogue; grouped, dense and K-grouped tiles): one
-// workgroup per CU loops over tiles instead of one workgroup per tile. The tiles and their order
-// are those of gemm_bf16_kernel, but a workgroup takes them from ticket counters: for grouped and
-// dense tiles one per XCD range, starting with its own XCD's range (workgroups are placed
-// round-robin over the 8 XCDs) and moving on to the other ranges once that one is used up, so the
-// XCDs that finish early take over the rest; for K-grouped tiles one counter over the dealing
-// order (longest groups first). Workgroups never wait for one another: the only
-// shared state is the counters, and each tile is computed by exactly one workgroup with the
-// same summation order as the per-tile launch, so the results are bitwise those of
-// gemm_bf16_kernel whatever the grid and the timing.
-// budget (nullable): a word polled between tiles (the sharing of the sparsenotes page
-// "Mixture-of-Kittens: MoE Megakernel for NVL72s", section "The production details": the
-// persistent kernel hands processors back to another stream's work). While it holds v > 0,
-// workgroups with index >= v take no further tile and exit once their current tile is done;
-// the others go on until every tile is taken. The library reads the word and never writes it.
+// workgroup per CU loops over tiles (persistent_tiles) instead of one workgroup per tile. The
+// tiles and their order are those of gemm_bf16_kernel: for grouped and dense tiles one ticket
+// counter per XCD range, a workgroup starting with its own XCD's range (workgroups are placed
+// round-robin over the 8 XCDs); for K-grouped tiles one counter over the dealing order (longest
+// groups first). Each tile is computed by exactly one workgroup with the same summation order as
+// the per-tile launch, so the results are bitwise those of gemm_bf16_kernel whatever the grid and
+// the timing. budget: the workgroup budget word (nullable), see persistent_tiles.
 template <int EPI, bool KG, int WN, int WAVES_N, int BKE, bool BT = false>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(GemmArgs a, Grouped g, int ntn,
                                                                                   int mtn, int32_t* tickets,
                                                                                   const int32_t* budget) {
   static_assert(!(KG && EPI != EPI_STORE), "K-grouped tiles store fp32 weight gradients");
   constexpr int BK = SliceCfg<BKE>::BK;
-  // The two control words live past the operand staging (and EPI_DGRAD's row partials) in the
-  // same LDS array: as separate __shared__ objects their presence made the compiler guard every
-  // fragment read with a wait for all outstanding LDS-direct copies (it could not tell them
-  // apart), which serialised each K slice's loads with its MFMAs.
-  constexpr int kExtra = EPI == EPI_DGRAD ? 2 * BM * WAVES_N : 0;
+  constexpr int kExtra = EPI == EPI_DGRAD ? 2 * BM * WAVES_N : 0;   // EPI_DGRAD's row partials
   __shared__ __attribute__((aligned(16))) uint16_t smem[kGemmSmemElems + kExtra + 8];
-  int& s_next = *reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra);
-  int& s_probe = *reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra + 2);
   // K-grouped: every (group, m-tile, n-tile) in launch order (longest groups first), one counter;
   // grouped / dense: the XCD ranges of gemm_bf16_kernel, one counter each
   const int valid = KG ? g.groups * mtn * ntn : (g.row_off ? g.tile_off[g.groups] : mtn) * ntn;
-  const int per_xcd = KG ? valid : (valid + 7) >> 3;
-  const int nrange = KG ? 1 : 8;
-  const int home = KG ? 0 : (int)(blockIdx.x & 7);
-  // The loop keeps no per-lane value live across a tile (the tile itself uses the whole register
-  // budget): the thread index is rebuilt per tile from the lane count and the wavefront's scalar
-  // index, and thread 0's position in the ranges (home, home + 1, ... found used up) is kept in
-  // LDS.
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  auto thread_index = [&]() -> int {
-    int t = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    asm volatile("" : "+v"(t));   // opaque per tile: the tile's lane-dependent addressing stays inside the loop
-    return t;
-  };
-  auto take = [&]() -> int {   // thread 0 only
-    if (budget) {
-      const int v = __hip_atomic_load(budget, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      if (v > 0 && (int)blockIdx.x >= v) return -1;
-    }
-    int probe = s_probe;
-    int got = -1;
-    for (; probe < nrange; ++probe) {
-      const int x = (home + probe) & 7;
-      const int lo = x * per_xcd, cnt = min(per_xcd, valid - lo);
-      if (cnt <= 0) continue;
-      const int i = __hip_atomic_fetch_add(tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (i < cnt) {
-        got = lo + i;
-        break;
-      }
-    }
-    s_probe = probe;
-    return got;
-  };
-  if (threadIdx.x == 0) {
-    s_probe = 0;
-    s_next = take();
-  }
-  __syncthreads();
-  int cur = __builtin_amdgcn_readfirstlane(s_next);   // uniform: the tile's coordinates stay scalar
-  while (cur >= 0) {
+  persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
+                   reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra), [&](int cur, auto& ti) {
     // A per-tile copy of the arguments the tile reads, opaque like the thread index, so that
     // nothing the tile derives from them is hoisted out of the loop and held across the K loop.
     GemmArgs la = a;
@@ -166,20 +115,20 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
     } else {
       ok = decode_grouped_tile(g, cur, ntn, mtn, tc);
     }
-    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(la, tc, k0, nk, ntn, smem, thread_index());
-    // every thread is past its read of s_next (the tile's barriers) and, after the barrier
-    // below, past the epilogue's LDS reads that the next tile's copies overwrite
-    if (thread_index() == 0) s_next = take();
-    __syncthreads();
-    cur = __builtin_amdgcn_readfirstlane(s_next);
-    __syncthreads();
-  }
+    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(la, tc, k0, nk, ntn, smem, ti());
+  });
 }
 
 // Zeroes the 8 ticket counters of a persistent launch (a kernel, not a memset, so that the
 // launch sequence can be captured into a graph).
 __global__ void zero_tickets_kernel(int32_t* t) {
   if (threadIdx.x < 8) t[threadIdx.x] = 0;
+}
+
+int launch_zero_tickets(int32_t* tickets, hipStream_t s) {
+  hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, tickets);
+  MOE_LAUNCH_CHECK();
+  return MOE_OK;
 }
 
 static int64_t grid_blocks(int64_t mtiles, int ntn) {
@@ -202,7 +151,7 @@ int gemm_tile_cols(Epi epi) { return (epi == EPI_SWIGLU || epi == EPI_SAVE_AU) ?
 // expert-parallel rank's share (14 and 25) faster too; at the mid shape (6 and 8) 3% slower, the
 // counters' zeroing launch and each tile's ticket costing more than the workgroup launches they
 // replace.
-static int persistent_grid(int64_t nb, const Persist* pc, int64_t& nw) {
+int persistent_grid(int64_t nb, const Persist* pc, int64_t& nw) {
   nw = 0;
   if (!pc || !pc->tickets) return MOE_OK;
   int dev = 0, ncu = 0;
@@ -229,8 +178,7 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
   int st;
   if ((st = persistent_grid(nb, pc, nw))) return st;
   if (nw > 0) {
-    hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
-    MOE_LAUNCH_CHECK();
+    if ((st = launch_zero_tickets(pc->tickets, s))) return st;
     const dim3 pg((unsigned)nw), pb(512);
     if (a.b_kmajor) {
       if (epi == EPI_STORE)
@@ -279,8 +227,7 @@ int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s, const 
   int st;
   if ((st = persistent_grid(nb, pc, nw))) return st;
   if (nw > 0) {
-    hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(64), 0, s, pc->tickets);
-    MOE_LAUNCH_CHECK();
+    if ((st = launch_zero_tickets(pc->tickets, s))) return st;
     hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, true, kWN, 4, 64>), dim3((unsigned)nw), dim3(512), 0, s,
                        a, g, ntn, mtn, pc->tickets, pc->budget);
     MOE_LAUNCH_CHECK();

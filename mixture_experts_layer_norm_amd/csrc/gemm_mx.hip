@@ -85,51 +85,58 @@ __device__ __forceinline__ void mx_k_loop(const StageSrc<NL>& src, uint8_t* sm, 
   }
 }
 
-// KG (weight gradients): tile `blockIdx.x` in launch order is n-tile fastest, then m-tile, then
-// group (groups in k_order, longest K first); group grp contracts k in [k_off[grp], k_off[grp+1]).
+// An output tile of the MX GEMMs: n-tile nt of group grp, tile rows [r0, r0 + rows), nk K slices
+// of 128 from k0; kbl scale bytes per A row (and per B row unless KG).
+struct MxTile {
+  int nt, grp, r0, rows, k0, nk;
+  int64_t kbl;
+};
+
+// Tile `logical` of a launch: KG (weight gradients) in launch order n-tile fastest, then m-tile,
+// then group (groups in k_order, longest K first), group grp contracting k in [k_off[grp],
+// k_off[grp+1]); otherwise the grouped (or dense) tiles of decode_grouped_tile. False: no tile.
+template <bool KG>
+__device__ __forceinline__ bool mx_decode(const GemmArgs& a, const Grouped& g, int ntn, int logical, MxTile& t) {
+  if (KG) {
+    const int mtn = (a.M + BM - 1) / BM;
+    if (logical >= g.groups * mtn * ntn) return false;
+    const int gi = logical / (mtn * ntn), rem = logical - gi * mtn * ntn;
+    t.grp = a.k_order ? a.k_order[gi] : gi;
+    const int mt = rem / ntn;
+    t.nt = rem - mt * ntn;
+    t.r0 = mt * BM;
+    t.rows = min(BM, a.M - t.r0);
+    t.k0 = a.k_off[t.grp];
+    t.nk = (a.k_off[t.grp + 1] - t.k0) / 128;
+    t.kbl = a.lda / 32;
+  } else {
+    TileCoord tc;
+    if (!decode_grouped_tile(g, logical, ntn, (g.M + BM - 1) / BM, tc)) return false;
+    t.nt = tc.nt; t.grp = tc.grp; t.r0 = tc.r0; t.rows = tc.rows;
+    t.k0 = 0;
+    t.nk = a.K / 128;                            // 128-wide K slices
+    t.kbl = a.K / 32;
+  }
+  return true;
+}
+
+// LDS of an MX tile: the two operand stages, then 2 x 512 scale words
+constexpr int kMxSmemElems = kGemmSmemElems + 2048;
+
+// One tile; tid: the thread index (the persistent kernel passes one rebuilt per tile).
 template <int EPI, bool KG>
-__global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
-                                                         const uint8_t* __restrict__ b_sc,
-                                                         const uint8_t* __restrict__ b2_sc, int64_t sc_group_stride,
-                                                         uint8_t* __restrict__ h_sc, Grouped g, int ntn) {
+__device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __restrict__ a_sc,
+                                        const uint8_t* __restrict__ b_sc, const uint8_t* __restrict__ b2_sc,
+                                        int64_t sc_group_stride, uint8_t* __restrict__ h_sc, const MxTile& t,
+                                        uint8_t* sm, int tid) {
   using C = SliceCfg<64>;
   constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int NL = BM / (C::RPI * 8);   // loads per operand per slice per wavefront
   constexpr bool PAIRED = EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU;   // gate and up rows in one tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kGemmSmemElems + 2048];
-  uint8_t* sm = reinterpret_cast<uint8_t*>(smem_u16);
-  int nt, grp, r0, rows, nk, k0 = 0;
-  int64_t kbl;                                   // scale bytes per A / B row
-  if (KG) {
-    const int mtn = (a.M + BM - 1) / BM;
-    const int logical = blockIdx.x;
-    if (logical >= g.groups * mtn * ntn) return;
-    const int gi = logical / (mtn * ntn), rem = logical - gi * mtn * ntn;
-    grp = a.k_order ? a.k_order[gi] : gi;
-    const int mt = rem / ntn;
-    nt = rem - mt * ntn;
-    r0 = mt * BM;
-    rows = min(BM, a.M - r0);
-    k0 = a.k_off[grp];
-    nk = (a.k_off[grp + 1] - k0) / 128;
-    kbl = a.lda / 32;
-  } else {
-    // tiles that exist (known on the device) split evenly over the 8 XCDs, contiguous per XCD
-    const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
-    const int per_xcd = (valid + 7) >> 3;
-    const int bid = blockIdx.x;
-    if ((bid >> 3) >= per_xcd) return;
-    const int logical = (bid & 7) * per_xcd + (bid >> 3);
-    if (logical >= valid) return;
-    TileCoord tc;
-    if (!decode_grouped_tile(g, logical, ntn, (g.M + BM - 1) / BM, tc)) return;
-    nt = tc.nt; grp = tc.grp; r0 = tc.r0; rows = tc.rows;
-    nk = a.K / 128;                              // 128-wide K slices
-    kbl = a.K / 32;
-  }
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nt = t.nt, grp = t.grp, r0 = t.r0, rows = t.rows, nk = t.nk, k0 = t.k0;
+  const int64_t kbl = t.kbl;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   // Copies as 16-bit units (2 fp8 each): row offsets in units of lda / 2.
   StageSrc<NL> src;
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   }
 
   const int ccol = lane & 31;
-  const int tid512 = threadIdx.x;
+  const int tid512 = tid;
   if (KG || EPI == EPI_SAVE_AU || (EPI == EPI_STORE && a.c_f32)) {
     // fp32 outputs, element stores (the 32 lanes of a lane group cover 32 consecutive columns).
     // Accumulator slot r of lane l: tile row (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
@@ -315,9 +322,63 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
   }
 }
 
-// a_sc / b_sc / b2_sc: E8M0 scales of A [rows][K/32] and of the weights [G][N][K/32].
+// One workgroup per tile: tile `blockIdx.x` in launch order (KG), or the tiles that exist
+// (known on the device) split evenly over the 8 XCDs, contiguous per XCD.
+template <int EPI, bool KG>
+__global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
+                                                         const uint8_t* __restrict__ b_sc,
+                                                         const uint8_t* __restrict__ b2_sc, int64_t sc_group_stride,
+                                                         uint8_t* __restrict__ h_sc, Grouped g, int ntn) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kMxSmemElems];
+  int logical = blockIdx.x;
+  if (!KG) {
+    const int valid = (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
+    const int per_xcd = (valid + 7) >> 3;
+    const int bid = blockIdx.x;
+    if ((bid >> 3) >= per_xcd) return;
+    logical = (bid & 7) * per_xcd + (bid >> 3);
+    if (logical >= valid) return;
+  }
+  MxTile t;
+  if (!mx_decode<KG>(a, g, ntn, logical, t)) return;
+  mx_tile<EPI, KG>(a, a_sc, b_sc, b2_sc, sc_group_stride, h_sc, t, reinterpret_cast<uint8_t*>(smem_u16),
+                   (int)threadIdx.x);
+}
+
+// Persistent form (persistent_tiles): the tiles and their dealing order of gemm_mx_kernel, one
+// workgroup per CU; each tile is the same workgroup sum, so the results are bitwise those of the
+// per-tile launch. budget: the workgroup budget word (nullable).
+template <int EPI, bool KG>
+__global__ __launch_bounds__(512, 1) void gemm_mx_persistent_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
+                                                                    const uint8_t* __restrict__ b_sc,
+                                                                    const uint8_t* __restrict__ b2_sc,
+                                                                    int64_t sc_group_stride,
+                                                                    uint8_t* __restrict__ h_sc, Grouped g, int ntn,
+                                                                    int32_t* tickets, const int32_t* budget) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kMxSmemElems + 4];
+  const int valid = KG ? g.groups * ((a.M + BM - 1) / BM) * ntn
+                       : (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
+  persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
+                   reinterpret_cast<int*>(smem_u16 + kMxSmemElems), [&](int cur, auto& ti) {
+    // per-tile opaque copies of the arguments (nothing derived from them is held across tiles)
+    GemmArgs la = a;
+    const uint8_t *la_sc = a_sc, *lb_sc = b_sc, *lb2_sc = b2_sc;
+    uint8_t* lh_sc = h_sc;
+    int64_t lsgs = sc_group_stride;
+    asm volatile("" : "+s"(la.A), "+s"(la.B), "+s"(la.B2), "+s"(la.C), "+s"(la.C2), "+s"(la.c_scatter));
+    asm volatile("" : "+s"(la_sc), "+s"(lb_sc), "+s"(lb2_sc), "+s"(lh_sc), "+s"(lsgs));
+    asm volatile("" : "+s"(la.lda), "+s"(la.ldb), "+s"(la.ldc), "+s"(la.b_group_stride), "+s"(la.N), "+s"(la.K));
+    MxTile t;
+    if (mx_decode<KG>(la, g, ntn, cur, t))
+      mx_tile<EPI, KG>(la, la_sc, lb_sc, lb2_sc, lsgs, lh_sc, t, reinterpret_cast<uint8_t*>(smem_u16), ti());
+  });
+}
+
+// a_sc / b_sc / b2_sc: E8M0 scales of A [rows][K/32] and of the weights [G][N][K/32]. pc: may
+// run as the persistent kernel (see Persist).
 int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, const uint8_t* b2_sc,
-                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s) {
+                   int64_t sc_group_stride, uint8_t* h_sc, const Grouped& g, Epi epi, hipStream_t s,
+                   const Persist* pc) {
   if (epi != EPI_SWIGLU && epi != EPI_STORE && epi != EPI_SAVE_AU) return MOE_ERR_UNSUPPORTED;
   const bool paired = epi == EPI_SWIGLU || epi == EPI_SAVE_AU;
   const int tcols = paired ? 128 : 256;
@@ -330,6 +391,24 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
   // the bf16 / E4M3 epilogues write whole 16-byte chunks of output rows; fp32 ones single words
   const int64_t rowb = epi == EPI_SWIGLU ? 1 : (epi == EPI_SAVE_AU || a.c_f32) ? 4 : 2;
   if ((reinterpret_cast<uintptr_t>(a.C) | (a.ldc * rowb) | (a.N * rowb)) & 15) return MOE_ERR_MISALIGNED;
+  int64_t nw = 0;
+  int st;
+  if ((st = persistent_grid(nb, pc, nw))) return st;
+  if (nw > 0) {
+    if ((st = launch_zero_tickets(pc->tickets, s))) return st;
+    const dim3 pg((unsigned)nw), pb(512);
+    if (epi == EPI_SWIGLU)
+      hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_SWIGLU, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+    else if (epi == EPI_SAVE_AU)
+      hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_SAVE_AU, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+    else
+      hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_STORE, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   if (epi == EPI_SWIGLU)
     hipLaunchKernelGGL((gemm_mx_kernel<EPI_SWIGLU, false>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b2_sc,
                        sc_group_stride, h_sc, g, ntn);
@@ -343,7 +422,8 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
   return MOE_OK;
 }
 
-int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s) {
+int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, int groups, hipStream_t s,
+                          const Persist* pc) {
   if (groups <= 0 || a.M <= 0 || a.N <= 0) return MOE_OK;
   if ((a.lda | a.ldb) % 128 || a.ldc % 4 || (reinterpret_cast<uintptr_t>(a.C) & 15) ||
       (a.C2 && (reinterpret_cast<uintptr_t>(a.C2) & 15)))
@@ -353,6 +433,16 @@ int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t*
   if (nb > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   Grouped g;
   g.groups = groups;
+  int64_t nw = 0;
+  int st;
+  if ((st = persistent_grid(nb, pc, nw))) return st;
+  if (nw > 0) {
+    if ((st = launch_zero_tickets(pc->tickets, s))) return st;
+    hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_STORE, true>), dim3((unsigned)nw), dim3(512), 0, s, a, a_sc,
+                       b_sc, b_sc, (int64_t)0, (uint8_t*)nullptr, g, ntn, pc->tickets, pc->budget);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+  }
   hipLaunchKernelGGL((gemm_mx_kernel<EPI_STORE, true>), dim3((unsigned)nb), dim3(512), 0, s, a, a_sc, b_sc, b_sc,
                      (int64_t)0, (uint8_t*)nullptr, g, ntn);
   MOE_LAUNCH_CHECK();

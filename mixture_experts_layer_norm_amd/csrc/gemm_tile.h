@@ -691,4 +691,69 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 }
 
 
+// The tile loop of the persistent GEMMs (one workgroup per CU, looping over tiles instead of one
+// workgroup per tile). Tiles are dealt from ticket counters, one per range of per_range
+// consecutive tiles (nrange ranges, counters tickets[0 .. nrange-1]): a workgroup starts with
+// range `home` and moves on to the following ones once it finds a range used up, so workgroups
+// that finish early take over the rest. body(tile, ti) computes tile `tile`, calling ti() for the
+// thread index. Workgroups never wait for one another; the only shared state is the counters.
+// The loop keeps no per-lane value live across a tile (the tile itself uses the whole register
+// budget): the thread index is rebuilt per tile from the lane count and the wavefront's scalar
+// index, and thread 0's position in the ranges is kept in LDS, in the two ints at ctl (past the
+// tile's own LDS use, in the same array: as separate __shared__ objects the compiler could not
+// tell them from the staging buffers and guarded every fragment read with a wait for all
+// outstanding LDS-direct copies).
+// budget (nullable): a word polled between tiles (the sharing of the sparsenotes page
+// "Mixture-of-Kittens: MoE Megakernel for NVL72s", section "The production details": the
+// persistent kernel hands processors back to another stream's work). While it holds v > 0,
+// workgroups with index >= v take no further tile and exit once their current tile is done;
+// the others go on until every tile is taken. The word is read, never written.
+template <class Body>
+__device__ __forceinline__ void persistent_tiles(int valid, int per_range, int nrange, int home, int32_t* tickets,
+                                                 const int32_t* budget, int* ctl, Body&& body) {
+  int& s_next = ctl[0];
+  int& s_probe = ctl[1];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  auto thread_index = [&]() -> int {
+    int t = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(t));   // opaque per tile: the tile's lane-dependent addressing stays inside the loop
+    return t;
+  };
+  auto take = [&]() -> int {   // thread 0 only
+    if (budget) {
+      const int v = __hip_atomic_load(budget, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (v > 0 && (int)blockIdx.x >= v) return -1;
+    }
+    int probe = s_probe;
+    int got = -1;
+    for (; probe < nrange; ++probe) {
+      const int x = (home + probe) % nrange;
+      const int lo = x * per_range, cnt = min(per_range, valid - lo);
+      if (cnt <= 0) continue;
+      const int i = __hip_atomic_fetch_add(tickets + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (i < cnt) {
+        got = lo + i;
+        break;
+      }
+    }
+    s_probe = probe;
+    return got;
+  };
+  if (threadIdx.x == 0) {
+    s_probe = 0;
+    s_next = take();
+  }
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_next);   // uniform: the tile's coordinates stay scalar
+  while (cur >= 0) {
+    body(cur, thread_index);
+    // every thread is past its read of s_next (the tile's barriers) and, after the barrier
+    // below, past the epilogue's LDS reads that the next tile's copies overwrite
+    if (thread_index() == 0) s_next = take();
+    __syncthreads();
+    cur = __builtin_amdgcn_readfirstlane(s_next);
+    __syncthreads();
+  }
+}
+
 }  // namespace moe

@@ -177,8 +177,8 @@ def test_removed_flag_bits_and_chunk_refusals_without_gpu():
 
 def test_persistent_gemm_flags_without_gpu():
     """MOE_FLAG_CU_BUDGET needs MOE_FLAG_PERSISTENT_GEMM (invalid alone); the persistent GEMMs are
-    BF16 only (MOE_F32, MOE_MXFP8: unsupported); checked on the host before any launch. The
-    budget word sits inside the first 256 bytes of the forward workspace, with the error word."""
+    BF16 and MXFP8 (MOE_F32: unsupported); checked on the host before any launch. The budget word
+    sits inside the first 256 bytes of the forward workspace, with the error word."""
     import mixture_experts_layer_norm_amd as m
     lib = m._lib
     n = ctypes.c_size_t()
@@ -203,12 +203,11 @@ def test_persistent_gemm_flags_without_gpu():
         setattr(w, f, fake)
     for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
         setattr(r, f, fake)
-    for dt in ('f32', 'mxfp8'):
-        p = m.problem(64, 128, 128, 8, 2, 0, dt, 0, 0, m.MOE_FLAG_PERSISTENT_GEMM)
-        assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
-                               1 << 40, None) == -2, dt
-        assert lib.moe_experts_forward(ctypes.byref(p), 64, fake, fake, ctypes.byref(w), fake, None, None, fake,
-                                       1 << 40, None) == -2, dt
+    p = m.problem(64, 128, 128, 8, 2, 0, 'f32', 0, 0, m.MOE_FLAG_PERSISTENT_GEMM)
+    assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
+                           1 << 40, None) == -2
+    assert lib.moe_experts_forward(ctypes.byref(p), 64, fake, fake, ctypes.byref(w), fake, None, None, fake,
+                                   1 << 40, None) == -2
 
 
 def test_layer_keep_entry_points_reject_without_gpu():

@@ -56,12 +56,12 @@ def mx_layer(cfg):
     return H, q
 
 
-def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0, lanes=None):
+def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0, lanes=None, flags=0, budget=None):
     """moe_forward in MXFP8; with act = [a, u] buffers, moe_forward_keep; with lanes = (streams,
-    events), moe_forward_lanes."""
+    events), moe_forward_lanes; budget: the workgroup budget word's value."""
     cfg = H.cfg
     T, K, D, E = cfg.T, cfg.K, cfg.D, cfg.E
-    p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8', chunk_rows, ring_stages)
+    p = m.problem(T, D, cfg.I, E, K, cfg.I_shared, 'mxfp8', chunk_rows, ring_stages, flags)
     tensors = dict(x=bf(H.x), logits=torch.from_numpy(H.logits).cuda(),
                    wq=[u8(q[k][0]) for k in ('w_gate', 'w_up', 'w_down')],
                    ws=[bf(H.ws_gate), bf(H.ws_up), bf(H.ws_down)],
@@ -73,6 +73,8 @@ def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0, lanes=None):
     out = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
     yr = torch.empty((T * K, D), dtype=torch.bfloat16, device='cuda')
     ws = torch.zeros((m.workspace_size(p),), dtype=torch.uint8, device='cuda')
+    if budget is not None:
+        ws[m.MOE_WS_CU_BUDGET_OFFSET:m.MOE_WS_CU_BUDGET_OFFSET + 4].view(torch.int32).fill_(budget)
     if lanes is not None:
         m.forward_lanes(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), ws, *lanes, y_routes=yr)
     elif act is None:
@@ -80,6 +82,7 @@ def run_mx_forward(m, H, q, act=None, chunk_rows=0, ring_stages=0, lanes=None):
     else:
         m.forward_keep(p, tensors['x'], tensors['logits'], W, out, m.make_routing(*rt), *act, ws, y_routes=yr)
     torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0
     return out, yr, rt, p, tensors
 
 

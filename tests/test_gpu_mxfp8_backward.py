@@ -336,34 +336,42 @@ def test_mx_layer_backward(m):
         assert_close_rms(t2np(gr[k.replace('dW', 'dws')]), rs[k], TOL['bf16'], 'mx layer shared ' + k)
 
 
+def run_mx_layer(m, H, q, keep=False, flags=0, budget=None):
+    """moe_forward + moe_backward in MXFP8 (keep: moe_forward_keep + moe_backward_kept), every
+    output; budget: the workgroup budget word's value in both workspaces."""
+    from test_gpu_mxfp8 import run_mx_forward
+    cfg = H.cfg
+    T, K, D, E, I, Is = cfg.T, cfg.K, cfg.D, cfg.E, cfg.I, cfg.I_shared
+    dout = bf(synth.host_dout(cfg, T))
+    act = [torch.full((T * K, I), float('nan'), device='cuda') for _ in range(2)] if keep else None
+    out, yr, rt, p, tensors = run_mx_forward(m, H, q, act, flags=flags, budget=budget)
+    W = m.make_weights(*tensors['wq'], *tensors['ws'], *tensors['sc'])
+    gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
+              dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
+              dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
+    dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
+    dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
+    wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(p),),
+                      dtype=torch.uint8, device='cuda')
+    if budget is not None:
+        wsb[m.MOE_WS_CU_BUDGET_OFFSET:m.MOE_WS_CU_BUDGET_OFFSET + 4].view(torch.int32).fill_(budget)
+    args = (p, dout, tensors['x'], tensors['logits'], W, m.make_routing(*rt), dx, m.make_grads(**gr), dtw, dlg)
+    if keep:
+        m.backward_kept(*args, *act, wsb)
+    else:
+        m.backward(*args, wsb)
+    torch.cuda.synchronize()
+    assert int(wsb[:4].view(torch.int32).item()) == 0
+    return dict(out=out, yr=yr, dx=dx, dtw=dtw, dlg=dlg, **gr)
+
+
 def test_mx_layer_keep_activations_bitwise(m):
     """moe_forward_keep + moe_backward_kept in MXFP8: the routed a, u of the block-scaled GEMM
     handed to the layer backward instead of replayed; every output bitwise that of moe_forward +
     moe_backward."""
-    from test_gpu_mxfp8 import MX_SMALL, mx_layer, run_mx_forward
-    cfg = MX_SMALL
-    H, q = mx_layer(cfg)
-    T, K, D, E, I, Is = cfg.T, cfg.K, cfg.D, cfg.E, cfg.I, cfg.I_shared
-    dout = bf(synth.host_dout(cfg, T))
-    res = []
-    for keep in (False, True):
-        act = [torch.full((T * K, I), float('nan'), device='cuda') for _ in range(2)] if keep else None
-        out, yr, rt, p, tensors = run_mx_forward(m, H, q, act)
-        W = m.make_weights(*tensors['wq'], *tensors['ws'], *tensors['sc'])
-        gr = dict(dw_gate=torch.empty((E, I, D), device='cuda'), dw_up=torch.empty((E, I, D), device='cuda'),
-                  dw_down=torch.empty((E, D, I), device='cuda'), dws_gate=torch.empty((Is, D), device='cuda'),
-                  dws_up=torch.empty((Is, D), device='cuda'), dws_down=torch.empty((D, Is), device='cuda'))
-        dx = torch.empty((T, D), dtype=torch.bfloat16, device='cuda')
-        dtw = torch.empty((T, K), dtype=torch.float32, device='cuda')
-        dlg = torch.empty((T, E), dtype=torch.float32, device='cuda')
-        wsb = torch.zeros(((m.backward_kept_workspace_size if keep else m.backward_workspace_size)(p),),
-                          dtype=torch.uint8, device='cuda')
-        args = (p, dout, tensors['x'], tensors['logits'], W, m.make_routing(*rt), dx, m.make_grads(**gr), dtw, dlg)
-        if keep:
-            m.backward_kept(*args, *act, wsb)
-        else:
-            m.backward(*args, wsb)
-        torch.cuda.synchronize()
-        res.append(dict(out=out, yr=yr, dx=dx, dtw=dtw, dlg=dlg, **gr))
+    from test_gpu_mxfp8 import MX_SMALL, mx_layer
+    H, q = mx_layer(MX_SMALL)
+    res = [run_mx_layer(m, H, q, keep) for keep in (False, True)]
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k

@@ -200,3 +200,44 @@ def test_persistent_gemm_layer_backward(m, cfg, budget):
         res.append([dx, dtw, dlg] + gr)
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+# MXFP8: the block-scaled GEMMs (forward, replay, dgrad, K-grouped weight gradients) have the same
+# persistent form; forced, with or without a budget, every output equals the per-tile launch's.
+@pytest.mark.parametrize('budget', [None, 3])
+def test_persistent_mx_layer_forward_backward(m, budget):
+    from test_gpu_mxfp8 import MX_SMALL, mx_layer
+    from test_gpu_mxfp8_backward import run_mx_layer
+    print(f'[persistent] mxfp8 layer forward + backward budget={budget}', flush=True)
+    H, q = mx_layer(MX_SMALL)
+    a = run_mx_layer(m, H, q)
+    flags = m.MOE_FLAG_PERSISTENT_GEMM | (m.MOE_FLAG_CU_BUDGET if budget else 0)
+    for keep in (False, True):
+        b = run_mx_layer(m, H, q, keep, flags, budget)
+        for k in a:
+            assert torch.equal(a[k], b[k]), (keep, k)
+
+
+@pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 4)])
+def test_persistent_mx_chunked_ring(m, chunk, stages):
+    from test_gpu_mxfp8 import MX_SMALL, mx_layer, run_mx_forward
+    print(f'[persistent] mxfp8 chunked {chunk} {stages}', flush=True)
+    H, q = mx_layer(MX_SMALL)
+    a, ya, *_ = run_mx_forward(m, H, q)
+    b, yb, *_ = run_mx_forward(m, H, q, chunk_rows=chunk, ring_stages=stages, flags=m.MOE_FLAG_PERSISTENT_GEMM)
+    assert torch.equal(a, b) and torch.equal(ya, yb)
+
+
+@pytest.mark.parametrize('counts', [[300, 0, 157], [1, 257, 242]], ids=['empty_mid', 'ragged_single'])
+def test_persistent_mx_experts(m, counts):
+    """moe_experts_forward + moe_experts_backward in MXFP8 (one expert-parallel rank's share)."""
+    import oracle
+    from test_gpu_mxfp8_backward import SMALL, run_share_mx
+    print(f'[persistent] mxfp8 experts {counts}', flush=True)
+    H = synth.host_share(SMALL)
+    q = {k: oracle.mx_quantize(getattr(H, k).astype(np.float64)) for k in ('w_gate', 'w_up', 'w_down')}
+    a = run_share_mx(m, H, q, counts)
+    b = run_share_mx(m, H, q, counts, flags=m.MOE_FLAG_PERSISTENT_GEMM)
+    assert a['err'] == 0 and b['err'] == 0
+    for k in ('y', 'sh', 'dx_slot', 'dg', 'dw_gate', 'dw_up', 'dw_down', 'dws_gate', 'dws_up', 'dws_down', 'dx_local'):
+        assert torch.equal(a[k], b[k]), k
