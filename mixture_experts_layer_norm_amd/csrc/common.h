@@ -21,7 +21,16 @@ typedef uint16_t bf16_t;   // raw bf16 bits in memory
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint16_t f2bf(float f) {
+// float -> bf16 bits, round to nearest even; a NaN keeps its sign and top payload bits with the
+// quiet bit set. gfx950's conversion instruction (v_cvt_pk_bf16_f32); over all 2^32 inputs it
+// gives the bits of f2bf_split below.
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// The same rounding in integer arithmetic, for the high half of a split v = hi + lo with
+// lo = v - hi: given the conversion instruction, the compiler sees hi as a float truncation of v
+// and may fuse the product that forms v into the subtraction (lo then comes from the unrounded
+// product); from integer operations it cannot, and lo is the residual of the fp32 v.
+__device__ __forceinline__ uint16_t f2bf_split(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);

@@ -547,7 +547,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
           const float dh = gj * dhp;
           const float da = dh * uv * sg * (1.f + av * (1.f - sg));
           const float du = dh * sl;
-          const uint16_t dah = f2bf(da), duh = f2bf(du);
+          const uint16_t dah = f2bf_split(da), duh = f2bf_split(du);
           *reinterpret_cast<uint32_t*>(la + pos) = (uint32_t)dah | ((uint32_t)duh << 16);
           *reinterpret_cast<uint32_t*>(lu + pos) =
               (uint32_t)f2bf(da - bf2f(dah)) | ((uint32_t)f2bf(du - bf2f(duh)) << 16);
@@ -636,7 +636,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
             const float dh = gj * dhp;
             const float da = dh * uv * sg * (1.f + av * (1.f - sg));
             const float du = dh * sl;
-            const uint16_t dah = f2bf(da), duh = f2bf(du);
+            const uint16_t dah = f2bf_split(da), duh = f2bf_split(du);
             uint16_t* c1 = (uint16_t*)a.C + (int64_t)row * a.ldc + col;
             uint16_t* c2 = (uint16_t*)a.C2 + (int64_t)row * a.ldc + col;
             *c1 = dah;

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
         const float* fu = reinterpret_cast<const float*>(src2);
         float f = silu_f(fa[j * lds + c0 + tx]) * fu[j * lds + c0 + tx];
         if (scale) f *= scale[j];
-        v = f2bf(f);
+        v = f2bf_split(f);
         vlo = f2bf(f - bf2f(v));
       }
     }
