@@ -231,8 +231,8 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
         if (EPI == EPI_SAVE_AU && !KG) {
           const int64_t col = (int64_t)nt * (BN / 2) + wn * (WN / 2) + ccol;
           if (col < a.N) {
-            ((float*)a.C)[row * a.ldc + col] = acc[i][0][r];
-            ((float*)a.C2)[row * a.ldc + col] = acc[i][1][r];
+            *gmem((float*)a.C + row * a.ldc + col) = acc[i][0][r];
+            *gmem((float*)a.C2 + row * a.ldc + col) = acc[i][1][r];
           }
         } else {
           float* out = (float*)a.C;
@@ -247,7 +247,10 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int64_t col = (int64_t)nt * BN + wn * WN + j * 32 + ccol;
-            if (col < a.N) out[orow * a.ldc + col] = acc[i][j][r] + (a.c_accumulate ? out[orow * a.ldc + col] : 0.f);
+            if (col < a.N) {
+              auto o = gmem(out + orow * a.ldc + col);
+              *o = acc[i][j][r] + (a.c_accumulate ? *o : 0.f);
+            }
           }
         }
       }
@@ -280,7 +283,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
         }
         sm[lr * 128 + (((c >> 4) ^ (((lr >> 2) & 3) << 1)) << 4) + (c & 15)] = (uint8_t)code;
         const int64_t col = (int64_t)nt * (BN / 2) + c;
-        if (ccol == 0 && lr < rows && col < a.N) h_sc[(int64_t)row * (a.ldc / 32) + col / 32] = (uint8_t)sbyte;
+        if (ccol == 0 && lr < rows && col < a.N) *gmem(h_sc + (int64_t)row * (a.ldc / 32) + col / 32) = (uint8_t)sbyte;
       }
     __syncthreads();
 #pragma unroll 4
@@ -289,12 +292,20 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
       if (lr >= rows) break;
       const int64_t col = (int64_t)nt * (BN / 2) + c * 16;
       if (col >= a.N) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 128 + ((c ^ (((lr >> 2) & 3) << 1)) << 4));
-      *reinterpret_cast<uint4*>((uint8_t*)a.C + (int64_t)(r0 + lr) * a.ldc + col) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm + lr * 128 + ((c ^ (((lr >> 2) & 3) << 1)) << 4));
+      *gmem(reinterpret_cast<u32x4*>((uint8_t*)a.C + (int64_t)(r0 + lr) * a.ldc + col)) = v;
     }
   } else {
     // BF16 output tile through LDS (512-byte rows, chunk c of row r at c ^ (4 ((r >> 2) & 3))),
-    // then 16-byte stores to the (scattered) output rows
+    // then 16-byte stores to the (scattered) output rows, whose indices are loaded first (a load
+    // between two stores would make the second wait for every earlier one)
+    constexpr int NS = BM * 32 / 512;
+    int32_t orow[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int row = r0 + min((tid512 >> 5) + k * 16, rows - 1);
+      orow[k] = a.c_scatter ? *gmem(a.c_scatter + row) : row;
+    }
 #pragma clang loop unroll(full)
     for (int i = 0; i < MI; ++i)
 #pragma clang loop unroll(full)
@@ -308,16 +319,15 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
         }
       }
     __syncthreads();
-#pragma unroll 4
-    for (int qq = tid512; qq < BM * 32; qq += 512) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int qq = tid512 + k * 512;
       const int lr = qq >> 5, c = qq & 31;
       if (lr >= rows) break;
       const int64_t col = (int64_t)nt * BN + c * 8;
       if (col >= a.N) continue;
-      const int row = r0 + lr;
-      const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
-      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
-      *reinterpret_cast<uint4*>((uint16_t*)a.C + orow * a.ldc + col) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C + (int64_t)orow[k] * a.ldc + col)) = v;
     }
   }
 }

@@ -126,6 +126,16 @@ __device__ __forceinline__ bool decode_grouped_tile(const Grouped& g, int logica
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The global-memory view of a pointer. The persistent kernels pass their arguments through an
+// empty asm (so that nothing derived from them is held across tiles), which hides where the
+// pointers came from; their accesses then compile to flat instructions, which count against the
+// LDS counter as well as the vector-memory one, so that every LDS wait of an epilogue also waits
+// for the stores in flight. Every output and index the GEMMs access is in global memory.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (expcnt, lgkmcnt left at maximum)
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
@@ -354,7 +364,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
     const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;
     const int ch = (lane % C::CPR) ^ C::swz(rr);
     const int r = tc.r0 + min(rr, tc.rows - 1);
-    const int64_t srow = (!KG && a.a_gather) ? (int64_t)(a.a_gather[r] / a.a_div) : (int64_t)r;
+    const int64_t srow = (!KG && a.a_gather) ? (int64_t)(*gmem(a.a_gather + r) / a.a_div) : (int64_t)r;
     src.aoff[j] = (uint32_t)(srow * a.lda + ch * 8);
     int64_t wrow;
     if (EPI == EPI_SWIGLU || EPI == EPI_SAVE_AU) {
@@ -438,6 +448,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
     // aligned rows and N a multiple of 8): 16 stores per thread instead of 128 two-byte ones. Chunk c of tile row r sits at c ^ (4 ((r >> 2) & 3))
     // so the two rows one store instruction writes (r and r + 4) use different banks.
     static_assert(BN * 2 == 512, "one tile row is 32 chunks of 16 bytes");
+    // Output rows of this thread's NS chunk stores (tile rows tid / 32 + k NT / 32), loaded before
+    // the tile goes through LDS: a scatter load between two stores would make the second store
+    // wait for every earlier one (vector-memory waits count stores too).
+    constexpr int NT = NWAVES * 64, NS = BM * 32 / NT;
+    int32_t orow[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int row = tc.r0 + min((tid >> 5) + k * (NT / 32), tc.rows - 1);
+      orow[k] = a.c_scatter ? *gmem(a.c_scatter + row) : row;
+    }
 #pragma clang loop unroll(full)
     for (int i = 0; i < MI; ++i)
 #pragma clang loop unroll(full)
@@ -451,17 +471,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
         }
       }
     __syncthreads();
-    constexpr int NT = NWAVES * 64;
-#pragma unroll 4
-    for (int q = tid; q < BM * 32; q += NT) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int q = tid + k * NT;
       const int lr = q >> 5, c = q & 31;
       if (lr >= tc.rows) break;           // rows grow with q
       const int64_t col = (int64_t)tc.nt * BN + c * 8;
       if (col >= a.N) continue;
-      const int row = tc.r0 + lr;
-      const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
-      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
-      *reinterpret_cast<uint4*>((uint16_t*)a.C + orow * a.ldc + col) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm + lr * 512 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C + (int64_t)orow[k] * a.ldc + col)) = v;
     }
     return;
   }
@@ -489,8 +507,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
       if (lr >= tc.rows) break;
       const int64_t col = (int64_t)tc.nt * (BN / 2) + c * 8;
       if (col >= a.N) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(sm + lr * 256 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
-      *reinterpret_cast<uint4*>((uint16_t*)a.C + (int64_t)(tc.r0 + lr) * a.ldc + col) = v;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm + lr * 256 + ((c ^ (((lr >> 2) & 3) << 2)) << 4));
+      *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C + (int64_t)(tc.r0 + lr) * a.ldc + col)) = v;
     }
     return;
   }
@@ -532,7 +550,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
         const int rl = wm * 32 + rsub, lr = wm * WM + i * 32 + rsub;
         const bool ok = lr < tc.rows;
         const int row = tc.r0 + lr;
-        const float gj = (ok && a.row_scale) ? a.row_scale[row] : 1.f;
+        const float gj = (ok && a.row_scale) ? *gmem(a.row_scale + row) : 1.f;
         float p = 0.f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -568,20 +586,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
         const uint4 h0 = *reinterpret_cast<const uint4*>(la + p0), h1 = *reinterpret_cast<const uint4*>(la + p1);
         const int64_t o = (int64_t)(tc.r0 + lr) * a.ldc + col;
         // element e of the 8 holds (da | du << 16): the low halves are da, the high halves du
-        *reinterpret_cast<uint4*>((uint16_t*)a.C + o) =
-            make_uint4((h0.x & 0xffffu) | (h0.y << 16), (h0.z & 0xffffu) | (h0.w << 16),
-                       (h1.x & 0xffffu) | (h1.y << 16), (h1.z & 0xffffu) | (h1.w << 16));
-        *reinterpret_cast<uint4*>((uint16_t*)a.C2 + o) =
-            make_uint4((h0.x >> 16) | (h0.y & 0xffff0000u), (h0.z >> 16) | (h0.w & 0xffff0000u),
-                       (h1.x >> 16) | (h1.y & 0xffff0000u), (h1.z >> 16) | (h1.w & 0xffff0000u));
+        *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C + o)) =
+            u32x4{(h0.x & 0xffffu) | (h0.y << 16), (h0.z & 0xffffu) | (h0.w << 16),
+                  (h1.x & 0xffffu) | (h1.y << 16), (h1.z & 0xffffu) | (h1.w << 16)};
+        *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C2 + o)) =
+            u32x4{(h0.x >> 16) | (h0.y & 0xffff0000u), (h0.z >> 16) | (h0.w & 0xffff0000u),
+                  (h1.x >> 16) | (h1.y & 0xffff0000u), (h1.z >> 16) | (h1.w & 0xffff0000u)};
         if (a.lo_off) {
           const uint4 l0 = *reinterpret_cast<const uint4*>(lu + p0), l1 = *reinterpret_cast<const uint4*>(lu + p1);
-          *reinterpret_cast<uint4*>((uint16_t*)a.C + o + a.lo_off) =
-              make_uint4((l0.x & 0xffffu) | (l0.y << 16), (l0.z & 0xffffu) | (l0.w << 16),
-                         (l1.x & 0xffffu) | (l1.y << 16), (l1.z & 0xffffu) | (l1.w << 16));
-          *reinterpret_cast<uint4*>((uint16_t*)a.C2 + o + a.lo_off) =
-              make_uint4((l0.x >> 16) | (l0.y & 0xffff0000u), (l0.z >> 16) | (l0.w & 0xffff0000u),
-                         (l1.x >> 16) | (l1.y & 0xffff0000u), (l1.z >> 16) | (l1.w & 0xffff0000u));
+          *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C + o + a.lo_off)) =
+              u32x4{(l0.x & 0xffffu) | (l0.y << 16), (l0.z & 0xffffu) | (l0.w << 16),
+                    (l1.x & 0xffffu) | (l1.y << 16), (l1.z & 0xffffu) | (l1.w << 16)};
+          *gmem(reinterpret_cast<u32x4*>((uint16_t*)a.C2 + o + a.lo_off)) =
+              u32x4{(l0.x >> 16) | (l0.y & 0xffff0000u), (l0.z >> 16) | (l0.w & 0xffff0000u),
+                    (l1.x >> 16) | (l1.y & 0xffff0000u), (l1.z >> 16) | (l1.w & 0xffff0000u)};
         }
       }
     }
@@ -590,7 +608,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES_N; ++w) sum += part[tid * WAVES_N + w];
-      a.row_partial[(int64_t)(tc.r0 + tid) * ntn + tc.nt] = sum;
+      *gmem(a.row_partial + (int64_t)(tc.r0 + tid) * ntn + tc.nt) = sum;
     }
     return;
   }
@@ -612,11 +630,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
           const float gt = acc[i][j][r], up = acc[i][j + NJ / 2][r];
           if (EPI == EPI_SWIGLU) {
             const float h = silu_f(gt) * up;
-            if (a.c_f32) ((float*)a.C)[(int64_t)row * a.ldc + col] = h;
-            else ((uint16_t*)a.C)[(int64_t)row * a.ldc + col] = f2bf(h);
+            if (a.c_f32) *gmem(((float*)a.C) + (int64_t)row * a.ldc + col) = h;
+            else *gmem(((uint16_t*)a.C) + (int64_t)row * a.ldc + col) = f2bf(h);
           } else {
-            ((float*)a.C)[(int64_t)row * a.ldc + col] = gt;
-            ((float*)a.C2)[(int64_t)row * a.ldc + col] = up;
+            *gmem(((float*)a.C) + (int64_t)row * a.ldc + col) = gt;
+            *gmem(((float*)a.C2) + (int64_t)row * a.ldc + col) = up;
           }
         }
       } else if (EPI == EPI_DGRAD) {
@@ -664,7 +682,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
             const int64_t col = (int64_t)tc.nt * BN + wn * WN + j * 32 + ccol;
             // nontemporal: nothing reads dW again in this call (layer backward 57.95 -> 57.03 ms at
             // the DSV3 shape; staging the tile through LDS for 16-byte stores measured no faster)
-            if (col < a.N) __builtin_nontemporal_store(acc[i][j][r], cb + orow * a.ldc + col);
+            if (col < a.N) __builtin_nontemporal_store(acc[i][j][r], gmem(cb + orow * a.ldc + col));
           }
         } else {
           const int64_t orow = a.c_scatter ? (int64_t)a.c_scatter[row] : (int64_t)row;
@@ -672,8 +690,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
           for (int j = 0; j < NJ; ++j) {
             const int64_t col = (int64_t)tc.nt * BN + wn * WN + j * 32 + ccol;
             if (col >= a.N) continue;
-            if (a.c_f32) ((float*)a.C)[orow * a.ldc + col] = acc[i][j][r];
-            else ((uint16_t*)a.C)[orow * a.ldc + col] = f2bf(acc[i][j][r]);
+            if (a.c_f32) *gmem(((float*)a.C) + orow * a.ldc + col) = acc[i][j][r];
+            else *gmem(((uint16_t*)a.C) + orow * a.ldc + col) = f2bf(acc[i][j][r]);
           }
         }
       }
@@ -685,7 +703,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES_N; ++w) s += part[tid * WAVES_N + w];
-      a.row_partial[(int64_t)(tc.r0 + tid) * ntn + tc.nt] = s;
+      *gmem(a.row_partial + (int64_t)(tc.r0 + tid) * ntn + tc.nt) = s;
     }
   }
 }
