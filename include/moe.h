@@ -70,8 +70,8 @@ typedef enum moe_dtype {
  *   for NVL72s", section "Granularity as a tunable"). 0 means one chunk of all T*K rows; other
  *   values are rounded up to a multiple of 256 and clamped to [max(256, T*K/1024), T*K]. With
  *   chunks, h lives in a ring of ring_stages chunk stages (BF16 and MXFP8), and so do the
- *   dispatched rows where there are any (MXFP8, or BF16 under MOE_FLAG_DISPATCH_COPY; BF16 chunks
- *   otherwise read x through the schedule). moe_forward / moe_forward_stages return
+ *   dispatched rows under MOE_FLAG_DISPATCH_COPY (otherwise chunks read x through the schedule:
+ *   BF16 x itself, MXFP8 its token rows quantised once). moe_forward / moe_forward_stages return
  *   MOE_ERR_UNSUPPORTED for chunk_rows > 0 under MOE_F32, as do moe_forward_keep and the
  *   expert-level forwards (their slots are not carried through a ring). The backward entry
  *   points do not chunk: they accept the forward's problem descriptor and ignore chunk_rows and
@@ -87,17 +87,18 @@ typedef struct moe_problem {
   int32_t flags;
 } moe_problem;
 
-/* The BF16 and fp32 forwards (moe_forward, moe_forward_stages, moe_forward_keep, moe_forward_lanes;
- * BF16 chunks too) read the x rows of the routed up/gate GEMM through the schedule (row j of
- * expert-slot order is x[perm[j] / K]) instead of a dispatched copy: the pages' pull dispatch done
- * by the GEMM's own operand loads, with no copy pass (DSV3 shape: 9.41 against 9.66 ms per
- * forward). This is the default; MOE_FLAG_FUSED_GATHER names it and is accepted (under MOE_MXFP8,
- * which quantises x while dispatching it: MOE_ERR_UNSUPPORTED). The BF16 layer backward (moe_backward,
- * moe_backward_kept) reads x and dout the same way in its GEMMs and transposes (DSV3 shape: 45.3
- * against 45.7 ms, and no 2 T K D-element slot buffers in its workspace). MOE_FLAG_DISPATCH_COPY
- * instead writes the expert-contiguous slot copies first (as the chunked ring, MXFP8 and fp32
- * backward always do) and runs on them; the outputs are the same bits. Both flags together:
- * MOE_ERR_INVALID_ARG. */
+/* The forwards (moe_forward, moe_forward_stages, moe_forward_keep, moe_forward_lanes; chunks too)
+ * read the x rows of the routed up/gate GEMM through the schedule (row j of expert-slot order is
+ * x[perm[j] / K]) instead of a dispatched copy: the pages' pull dispatch done by the GEMM's own
+ * operand loads, with no copy pass (DSV3 shape: 9.41 against 9.66 ms per forward). Under
+ * MOE_MXFP8 the T token rows are quantised once (E4M3 codes and E8M0 scales per 32) and the
+ * block-scaled GEMM reads codes and scales the same way (T = 32768: the dispatch stage 0.50 ->
+ * 0.11 ms). This is the default; MOE_FLAG_FUSED_GATHER names it and is accepted. The BF16 layer
+ * backward (moe_backward, moe_backward_kept) reads x and dout the same way in its GEMMs and
+ * transposes (DSV3 shape: 45.3 against 45.7 ms, and no 2 T K D-element slot buffers in its
+ * workspace). MOE_FLAG_DISPATCH_COPY instead writes the expert-contiguous slot copies first (as the
+ * MXFP8 and fp32 backwards always do) and runs on them; the outputs are the same bits. Both flags
+ * together: MOE_ERR_INVALID_ARG. */
 #define MOE_FLAG_FUSED_GATHER 0x1
 #define MOE_FLAG_DISPATCH_COPY 0x100000
 /* Bits 0x2, 0x8, 0x10, 0x20 and 0xff00 are reserved (they selected tuning variants that measured

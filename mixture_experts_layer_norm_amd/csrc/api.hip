@@ -73,11 +73,14 @@ WsLayout ws_layout(const moe_problem& p) {
   L.tile_off = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_clean = o; o = align256(o + (size_t)(p.E + 1) * 4);
   L.grp_poff = o; o = align256(o + (size_t)(p.E + 1) * 4);
-  // dispatched slot rows (all of them, or a ring of chunk stages): MXFP8 (quantised in dispatch) and
-  // MOE_FLAG_DISPATCH_COPY; otherwise GEMM1 reads x through the schedule and no copy is made
+  // x rows for GEMM1: under MOE_FLAG_DISPATCH_COPY the dispatched slot rows (all of them, or a
+  // ring of chunk stages); otherwise BF16 GEMM1 reads x itself through the schedule (no buffer) and
+  // MXFP8 reads its T token rows quantised once. The MXFP8 expert-level forward quantises its
+  // slot rows here too (up to T K of them).
   const bool copy = mx || (p.flags & MOE_FLAG_DISPATCH_COPY);
-  L.x_slot = o; o = align256(o + (copy ? (size_t)L.ring_rows * p.D * (mx ? 1 : act) : 0));
-  L.x_slot_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.D / 32) : 0));
+  const int64_t xrows = mx && L.ring_rows < p.T ? p.T : L.ring_rows;
+  L.x_slot = o; o = align256(o + (copy ? (size_t)xrows * p.D * (mx ? 1 : act) : 0));
+  L.x_slot_sc = o; o = align256(o + (mx ? (size_t)xrows * (p.D / 32) : 0));
   L.h = o; o = align256(o + (size_t)L.ring_rows * p.I * (mx ? 1 : act));
   L.h_sc = o; o = align256(o + (mx ? (size_t)L.ring_rows * (p.I / 32) : 0));
   L.y_routes = o; o = align256(o + (size_t)n * p.D * act);
@@ -307,7 +310,6 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
   if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   // MXFP8 quantises x while dispatching it: there is no gathered form
-  if (mx && (p->flags & MOE_FLAG_FUSED_GATHER)) return MOE_ERR_UNSUPPORTED;
   if (p->chunk_rows > 0 && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -380,21 +382,27 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       lpc[l] = pcs;
       if (pcs.tickets) lpc[l].tickets = pcs.tickets + 8 * l;
     }
+    // Chunks read x through the schedule (the ring then holds only h): BF16 x as it is, MXFP8 its
+    // T token rows quantised once up front (on `stream`, before the lanes fork). Under
+    // MOE_FLAG_DISPATCH_COPY each chunk's rows are dispatched (MXFP8: quantising) into the ring.
+    const bool gather_x = !(p->flags & MOE_FLAG_DISPATCH_COPY);
+    const int64_t xrow = mx ? p->D : (int64_t)p->D * 2, hrow = mx ? p->I : (int64_t)p->I * 2;   // bytes per row
+    uint8_t* xr = (uint8_t*)(wsb + L.x_slot);
+    uint8_t* hr = (uint8_t*)(wsb + L.h);
+    uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
+    uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
+    auto quantize_tokens = [&]() -> int {
+      return (mx && gather_x) ? launch_quantize_mx((const uint16_t*)x, p->T, p->D, xr, xs, stream) : MOE_OK;
+    };
     if (NLn > 1) {
+      if ((st = quantize_tokens())) return st;
       if (hipEventRecord(lanes->events[S], stream) != hipSuccess) return MOE_ERR_HIP;
       for (int l = 1; l < NLn; ++l)
         if (hipStreamWaitEvent(ls[l], lanes->events[S], 0) != hipSuccess) return MOE_ERR_HIP;
     }
     if (laned && (st = shared_expert(stream, pc))) return st;
     MOE_MARK(MOE_STAGE_DISPATCH);
-    // BF16 chunks read x through the schedule (the ring then holds only h); MXFP8 dispatches
-    // (quantising) into the ring, as does BF16 under MOE_FLAG_DISPATCH_COPY
-    const bool gather_x = !mx && !(p->flags & MOE_FLAG_DISPATCH_COPY);
-    const int64_t xrow = mx ? p->D : (int64_t)p->D * 2, hrow = mx ? p->I : (int64_t)p->I * 2;   // bytes per row
-    uint8_t* xr = (uint8_t*)(wsb + L.x_slot);
-    uint8_t* hr = (uint8_t*)(wsb + L.h);
-    uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
-    uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
+    if (NLn == 1 && (st = quantize_tokens())) return st;
     for (int c = 0; c < C; ++c) {
       const int64_t c0 = c * b, rows = (n - c0) < b ? (n - c0) : b;
       const int64_t stage = (int64_t)(c % S) * b, shift = stage - c0;   // slot index -> ring row
@@ -420,10 +428,11 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
       gc.max_mtiles = (rows + kGemmBM - 1) / kGemmBM + p->E;
       if (mx) {
         GemmArgs g1;
-        g1.A = xr + shift * xrow; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
+        g1.A = gather_x ? xr : xr + shift * xrow; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
         g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hr + shift * hrow; g1.ldc = p->I;
-        st = launch_gemm_mx(g1, xs + shift * (p->D / 32), w->sc_gate, w->sc_up, (int64_t)p->I * (p->D / 32),
-                            hs + shift * (p->I / 32), gc, EPI_SWIGLU, cs, cpc);
+        if (gather_x) { g1.a_gather = r->perm; g1.a_div = p->K; }
+        st = launch_gemm_mx(g1, gather_x ? xs : xs + shift * (p->D / 32), w->sc_gate, w->sc_up,
+                            (int64_t)p->I * (p->D / 32), hs + shift * (p->I / 32), gc, EPI_SWIGLU, cs, cpc);
         if (st) return st;
         GemmArgs g2;
         g2.A = hr + shift * hrow; g2.lda = p->I; g2.B = w->w_down; g2.ldb = p->I;
@@ -461,11 +470,16 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
     uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
     uint8_t* hq = (uint8_t*)(wsb + L.h);
     uint8_t* hs = (uint8_t*)(wsb + L.h_sc);
-    st = launch_dispatch_tokens(x, MOE_MXFP8, r->inv_perm, p->T, p->K, p->D, xq, xs, stream);
+    // the T token rows quantised once, read by GEMM1 through the schedule (row j = token
+    // perm[j] / K); under MOE_FLAG_DISPATCH_COPY quantised into per-slot copies instead
+    const bool gather = !(p->flags & MOE_FLAG_DISPATCH_COPY);
+    st = gather ? launch_quantize_mx((const uint16_t*)x, p->T, p->D, xq, xs, stream)
+                : launch_dispatch_tokens(x, MOE_MXFP8, r->inv_perm, p->T, p->K, p->D, xq, xs, stream);
     if (st) return st;
     MOE_MARK(MOE_STAGE_UP_GATE);
     GemmArgs g1;
     g1.A = xq; g1.lda = p->D; g1.B = w->w_gate; g1.B2 = w->w_up; g1.ldb = p->D;
+    if (gather) { g1.a_gather = r->perm; g1.a_div = p->K; }
     g1.b_group_stride = (int64_t)p->I * p->D; g1.N = p->I; g1.K = p->D; g1.C = hq; g1.ldc = p->I;
     if (keep) {
       // a, u to the caller in fp32 (the backward's replay GEMM), h quantised from them

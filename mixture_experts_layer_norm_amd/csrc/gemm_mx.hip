@@ -7,6 +7,8 @@
 //
 //   up/gate:  h = SiLU(X W_gate^T) (*) (X W_up^T), quantised to MXFP8 along I in the epilogue
 //   down:     y = h W_down^T (bf16), row j stored at c_scatter[j]
+// With a_gather, A row j (codes and scales) is row a_gather[j] / a_div: the up/gate GEMM reads the
+// E4M3 token rows through the schedule instead of per-slot copies.
 //
 // Tiling matches the BF16 kernel byte for byte: 256 rows x 256 weight rows, 8 wavefronts of
 // 128 x 64, and the same LDS staging (gemm_tile.h): a K slice of 128 fp8 values is a 128-byte row,
@@ -155,7 +157,8 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
     const int rr = C::RPI * (NL * wave + j) + lane / C::CPR;
     const int ch = (lane % C::CPR) ^ C::swz(rr);
     const int r = r0 + min(rr, rows - 1);
-    src.aoff[j] = (uint32_t)((int64_t)r * (a.lda / 2) + ch * 8);
+    const int64_t sr = (!KG && a.a_gather) ? (int64_t)(*gmem(a.a_gather + r) / a.a_div) : (int64_t)r;
+    src.aoff[j] = (uint32_t)(sr * (a.lda / 2) + ch * 8);
     int64_t wrow;
     if (PAIRED) {
       const int wc = rr / WN, qq = (rr % WN) / 32;
@@ -176,7 +179,8 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
     const int tr = 64 * (wave & 3) + lane;   // tile row whose words this lane copies
     if (wave < 4) {
       const int r = r0 + min(tr, rows - 1);
-      sc_src = reinterpret_cast<const uint32_t*>(a_sc + (int64_t)r * kbl + k0 / 32);
+      const int64_t sr = (!KG && a.a_gather) ? (int64_t)(*gmem(a.a_gather + r) / a.a_div) : (int64_t)r;
+      sc_src = reinterpret_cast<const uint32_t*>(a_sc + sr * kbl + k0 / 32);
     } else {
       int64_t wrow;
       bool up = false;
@@ -375,7 +379,8 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_persistent_kernel(GemmArgs a, 
     const uint8_t *la_sc = a_sc, *lb_sc = b_sc, *lb2_sc = b2_sc;
     uint8_t* lh_sc = h_sc;
     int64_t lsgs = sc_group_stride;
-    asm volatile("" : "+s"(la.A), "+s"(la.B), "+s"(la.B2), "+s"(la.C), "+s"(la.C2), "+s"(la.c_scatter));
+    asm volatile("" : "+s"(la.A), "+s"(la.B), "+s"(la.B2), "+s"(la.C), "+s"(la.C2), "+s"(la.c_scatter),
+                 "+s"(la.a_gather), "+s"(la.a_div));
     asm volatile("" : "+s"(la_sc), "+s"(lb_sc), "+s"(lb2_sc), "+s"(lh_sc), "+s"(lsgs));
     asm volatile("" : "+s"(la.lda), "+s"(la.ldb), "+s"(la.ldc), "+s"(la.b_group_stride), "+s"(la.N), "+s"(la.K));
     MxTile t;

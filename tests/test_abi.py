@@ -146,9 +146,8 @@ def test_keep_activation_entry_points_reject_without_gpu():
 
 def test_removed_flag_bits_and_chunk_refusals_without_gpu():
     """Flag bits the library does not define are refused; chunk_rows is refused where no ring can
-    hold the rows (fp32, the expert-level forward, the keep forward) and the gathered form where
-    x must be quantised while dispatched (MXFP8), instead of being ignored. Every call returns
-    before any HIP call."""
+    hold the rows (fp32, the expert-level forward, the keep forward) instead of being ignored.
+    Every call returns before any HIP call."""
     import mixture_experts_layer_norm_amd as m
     lib = m._lib
     n = ctypes.c_size_t()
@@ -161,11 +160,9 @@ def test_removed_flag_bits_and_chunk_refusals_without_gpu():
         setattr(w, f, fake)
     for f in ('topk_idx', 'topk_w', 'counts', 'offsets', 'perm', 'inv_perm'):
         setattr(r, f, fake)
-    for dt, chunk, flags in (('mxfp8', 0, m.MOE_FLAG_FUSED_GATHER), ('mxfp8', 256, m.MOE_FLAG_FUSED_GATHER),
-                             ('f32', 256, 0)):
-        p = m.problem(64, 128, 128, 8, 2, 0, dt, chunk, 3, flags)
-        assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
-                               1 << 40, None) == -2, (dt, chunk, flags)
+    p = m.problem(64, 128, 128, 8, 2, 0, 'f32', 256, 3)
+    assert lib.moe_forward(ctypes.byref(p), fake, fake, ctypes.byref(w), fake, ctypes.byref(r), None, None, fake,
+                           1 << 40, None) == -2
     for dt in ('bf16', 'mxfp8', 'f32'):
         p = m.problem(64, 128, 128, 8, 2, 0, dt, 512, 3)
         assert lib.moe_experts_forward(ctypes.byref(p), 64, fake, fake, ctypes.byref(w), fake, None, None, fake,
@@ -310,6 +307,5 @@ def test_forward_lanes_rejects_without_gpu():
     assert call(p5, 1, [fake], [fake] * 6 + [None]) == -1
     for f in ('sc_gate', 'sc_up', 'sc_down'):
         setattr(w, f, fake)
-    for dt, flags in (('mxfp8', m.MOE_FLAG_FUSED_GATHER), ('f32', 0)):
-        q = m.problem(64, 128, 128, 8, 2, 0, dt, 256, 3, flags)
-        assert call(q, 1, [fake], [fake] * 5) == -2, (dt, flags)
+    q = m.problem(64, 128, 128, 8, 2, 0, 'f32', 256, 3)
+    assert call(q, 1, [fake], [fake] * 5) == -2

@@ -118,7 +118,7 @@ def test_mx_dispatch_bit_exact(m):
     torch.cuda.synchronize()
     rq, rs = oracle.mx_quantize(H.x[perm // cfg.K].astype(np.float64))
     assert np.array_equal(xs.cpu().numpy(), rs) and np.array_equal(xq.cpu().numpy(), rq)
-    # token-major form (the one the forward uses): same bytes
+    # token-major form (the forward's slot copies under MOE_FLAG_DISPATCH_COPY): same bytes
     xq.fill_(0xAA)
     xs.fill_(0xAA)
     m.dispatch_tokens(p, bf(H.x), torch.from_numpy(inv).cuda(), xq, xs)
@@ -161,14 +161,39 @@ def test_mx_forward_small(m):
         assert fb < MAX_FRAC_BEYOND, (name, fb)
 
 
+@pytest.mark.parametrize('flags', [0, 0x100000], ids=['gather', 'dispatch_copy'])
 @pytest.mark.parametrize('chunk,stages', [(256, 3), (512, 4), (768, 5), (1 << 20, 3)])
-def test_mx_chunked_ring_bitwise_equals_unchunked(m, chunk, stages):
-    """The MXFP8 forward through the chunked ring (dispatch quantises each chunk into ring stage
-    c mod S, the two block-scaled GEMMs read it there) gives the unchunked path's bits."""
+def test_mx_chunked_ring_bitwise_equals_unchunked(m, chunk, stages, flags):
+    """The MXFP8 forward through the chunked ring (the up/gate GEMM reads the token rows quantised
+    once through the schedule, h goes through ring stage c mod S; with MOE_FLAG_DISPATCH_COPY each
+    chunk's rows are quantised into its ring stage first) gives the unchunked path's bits."""
     H, q = mx_layer(MX_SMALL)
     a, ya, *_ = run_mx_forward(m, H, q)
-    b, yb, _, p, _ = run_mx_forward(m, H, q, chunk_rows=chunk, ring_stages=stages)
+    b, yb, _, p, _ = run_mx_forward(m, H, q, chunk_rows=chunk, ring_stages=stages, flags=flags)
     assert torch.equal(a, b) and torch.equal(ya, yb)
+
+
+def test_mx_gather_matches_dispatch_copy_bitwise(m):
+    """The default MXFP8 forward quantises the T token rows once and the block-scaled up/gate GEMM
+    reads codes and scales through the schedule; MOE_FLAG_DISPATCH_COPY quantises per-slot copies
+    first (the same codes: a slot's row is its token's row). Same bits, also with a, u kept
+    (moe_forward_keep); MOE_FLAG_FUSED_GATHER names the default."""
+    H, q = mx_layer(MX_SMALL)
+    cfg = H.cfg
+    n = cfg.T * cfg.K
+    runs = {}
+    for name, flags in (('gather', 0), ('copy', m.MOE_FLAG_DISPATCH_COPY), ('named', m.MOE_FLAG_FUSED_GATHER)):
+        runs[name] = run_mx_forward(m, H, q, flags=flags)
+    for name in ('copy', 'named'):
+        assert torch.equal(runs['gather'][0], runs[name][0]) and torch.equal(runs['gather'][1], runs[name][1]), name
+    kept = []
+    for flags in (0, m.MOE_FLAG_DISPATCH_COPY):
+        act = [torch.full((n, cfg.I), float('nan'), device='cuda') for _ in range(2)]
+        out, yr, *_ = run_mx_forward(m, H, q, act, flags=flags)
+        kept.append((out, yr, act))
+    assert torch.equal(kept[0][0], runs['gather'][0]) and torch.equal(kept[1][0], runs['gather'][0])
+    for u, v in zip(kept[0][2], kept[1][2]):
+        assert torch.equal(u, v)
 
 
 def test_mx_forward_deterministic(m):
