@@ -99,8 +99,9 @@ def stage_work(cfg, flags):
         w['route'] = (0.0, T * cfg.E * 4 + T * K * 8)
         w['schedule'] = (0.0, n * 4 * 3)
         w['shared'] = (6.0 * T * D * Is, 3 * Is * D * 2 + 2 * T * D * 2 + 2 * T * Is * 2) if Is else (0.0, 0)
-        w['dispatch'] = (0.0, T * D * 2 + n * D * q + n * 4)
-        w['up_gate'] = (4.0 * n * D * I, 2 * E * I * D * q + n * D * q + n * I * q)
+        # gathered (default): the T token rows quantised once, read by GEMM1 through the schedule
+        w['dispatch'] = (0.0, T * D * 2 + (T * D * q if fused else n * D * q + n * 4))
+        w['up_gate'] = (4.0 * n * D * I, 2 * E * I * D * q + (T if fused else n) * D * q + n * I * q)
         w['down'] = (2.0 * n * I * D, E * D * I * q + n * I * q + n * D * 2 + n * 4)
         w['combine'] = (0.0, n * D * 2 + (2 if Is else 1) * T * D * 2 + n * 4)
         return w
@@ -212,7 +213,7 @@ def main():
     peak = {'f32': PEAK_F32_TFLOPS, 'mxfp8': PEAK_MXFP8_TFLOPS}.get(cfg.dtype, PEAK_BF16_TFLOPS)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    work = stage_work(cfg, args.flags | (0x100000 if args.chunk_rows else 0))   # the ring holds slot copies
+    work = stage_work(cfg, args.flags)   # chunks too read x through the schedule unless copies are asked for
     dom = max(stage_ms, key=stage_ms.get)
     f_dom, b_dom = work[dom]
     t_dom = stage_ms[dom] * 1e-3
