@@ -120,7 +120,9 @@ def main():
     ap.add_argument('--gpus', type=int, default=1)
     ap.add_argument('--steps', type=int, default=50)
     ap.add_argument('--warmup', type=int, default=10)
-    ap.add_argument('--workload', default='dsv3', choices=['dsv3', 'mid', 'tiny', 'mxfp8', 'ep_share', 'ep_share_mxfp8'])
+    ap.add_argument('--workload', default='dsv3',
+                    choices=['dsv3', 'mid', 'tiny', 'mxfp8', 'ep_share', 'ep_share_mxfp8', 'dsv3_layer'],
+                    help='dsv3_layer: the DSV3-shape layer forward + backward as the step')
     ap.add_argument('--no-extra', action='store_true',
                     help='skip the expert-parallel share forward+backward reported under "extra"')
     ap.add_argument('--chunk-rows', type=int, default=0)
@@ -149,6 +151,12 @@ def main():
         if args.calib_copy:
             calib_copy()
         print(json.dumps(bench_share(args.steps, args.warmup, args.flags, dt, keep=args.keep_activations)), flush=True)
+        return
+    if args.workload == 'dsv3_layer':
+        torch.cuda.set_device(0)
+        r = layer_fwd_bwd_leg(synth.DSV3, synth.device_layer(synth.DSV3), args.keep_activations, args.steps, args.warmup)
+        print(json.dumps({'metric': METRIC, 'n_gpus': 1, 'higher_is_better': True, 'scaling': 'weak', 'dtype': 'bf16',
+                          'data': 'synthetic', 'config': {'workload': r.pop('workload')}, **r}), flush=True)
         return
     cfg = {'dsv3': synth.DSV3, 'mid': synth.MID, 'tiny': synth.TINY, 'mxfp8': synth.MXFP8}[args.workload]
     torch.cuda.set_device(0)
