@@ -309,7 +309,6 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   if (mx && (!w->sc_gate || !w->sc_up || !w->sc_down)) return MOE_ERR_INVALID_ARG;
   if (p->flags & MOE_FLAG_PERSISTENT) return MOE_ERR_UNSUPPORTED;   // persistent chunk kernel is switched off
   if ((p->flags & MOE_FLAG_PERSISTENT_GEMM) && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
-  // MXFP8 quantises x while dispatching it: there is no gathered form
   if (p->chunk_rows > 0 && p->dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   WsLayout L = ws_layout(*p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -464,8 +463,8 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   }
   MOE_MARK(MOE_STAGE_DISPATCH);
   if (mx) {
-    // quantise while dispatching, then the two block-scaled grouped GEMMs (h quantised in the
-    // SwiGLU epilogue)
+    // x quantised (its token rows once, or per-slot copies under MOE_FLAG_DISPATCH_COPY), then the
+    // two block-scaled grouped GEMMs (h quantised in the SwiGLU epilogue)
     uint8_t* xq = (uint8_t*)(wsb + L.x_slot);
     uint8_t* xs = (uint8_t*)(wsb + L.x_slot_sc);
     uint8_t* hq = (uint8_t*)(wsb + L.h);
