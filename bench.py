@@ -261,7 +261,26 @@ def main():
 
         def step_b():
             moe.forward(pb, L.x, L.logits, weights, out, routing, wsb, stream=stream)
-        yl = second_stream_latency(step, stream, budget=(step_b, word, 224))
+        # and with the budget word in coherent pinned host memory, stored to by the host
+        hip = hip_runtime()
+        hw = pinned_host_word(hip)
+        host_budget = None
+        if hw is not None:
+            ph = moe.problem(T, D, cfg.I, cfg.E, K, cfg.I_shared, cfg.dtype, args.chunk_rows, 0,
+                             args.flags | moe.MOE_FLAG_PERSISTENT_GEMM | moe.MOE_FLAG_CU_BUDGET |
+                             moe.MOE_FLAG_CU_BUDGET_INDIRECT)
+            wsh = torch.zeros((moe.workspace_size(ph),), dtype=torch.uint8, device=dev)
+            o = moe.MOE_WS_CU_BUDGET_PTR_OFFSET
+            wsh[o:o + 8].view(torch.int64).fill_(hw[1])
+
+            def step_h():
+                moe.forward(ph, L.x, L.logits, weights, out, routing, wsh, stream=stream)
+            host_budget = (step_h, hw[0], 224)
+        yl = second_stream_latency(step, stream, budget=(step_b, word, 224), host_budget=host_budget)
+        torch.cuda.synchronize()
+        if hw is not None:
+            del wsh
+            hip.hipHostFree(hw[2])
         del wsb
 
     # per-step spread from the in-order run (sum of its stage events)
@@ -545,7 +564,7 @@ def bench_share(steps, warmup, flags, dtype='bf16', keep=False):
             'fwd_tflops': flops_f / (f_ms * 1e-3) / 1e12, 'bwd_tflops': 2 * flops_f / (b_ms * 1e-3) / 1e12}
 
 
-def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10, budget=None):
+def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10, budget=None, host_budget=None):
     """Latency of a small kernel (an in-place add over 4 MB) enqueued on a second default-priority
     stream while moe_forward runs on the library's stream, `delay` ms after the forward was
     enqueued. Probes that did not start inside the forward are dropped.
@@ -553,7 +572,11 @@ def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10, bu
     MOE_FLAG_CU_BUDGET, and the second stream first copies `value` into its workgroup budget word
     `word` (a host-to-device copy, which needs no CU), then runs the probe; the latency counts from
     the copy. Workgroups at or above `value` end after their current tile and leave their CUs to
-    the probe; the word is reset to 0 after each trial."""
+    the probe; the word is reset to 0 after each trial.
+    host_budget = (step_h, host_word, value): the forward `step_h` runs with MOE_FLAG_CU_BUDGET_INDIRECT,
+    its budget word in coherent pinned host memory (`host_word`, a ctypes c_int32); the host stores
+    `value` into it right before enqueueing the probe (no GPU work at all) and resets it after each
+    trial."""
     import torch
     other = torch.cuda.Stream()
     small = torch.zeros(1 << 20, device='cuda')
@@ -620,7 +643,36 @@ def second_stream_latency(step, stream, delays_ms=(1.0, 3.0, 8.0), trials=10, bu
             res['cu_budget_dynamic'] = {'value': value, 'note': 'budget written by hipStreamWriteValue32 on the '
                                                                 'second stream; latency from that write to the end '
                                                                 'of the probe', **sweep(step_b, pre, reset)}
+    if host_budget is not None:
+        step_h, host_word, value = host_budget
+
+        def pre_h():
+            host_word.value = value
+
+        def reset_h():
+            host_word.value = 0
+        reset_h()
+        res['cu_budget_host'] = {'value': value, 'note': 'MOE_FLAG_CU_BUDGET_INDIRECT: budget word in coherent pinned '
+                                                         'host memory, stored by the host right before the probe is '
+                                                         'enqueued; latency from the probe stream\'s start event to '
+                                                         'the end of the probe', **sweep(step_h, pre_h, reset_h)}
     return res
+
+
+def pinned_host_word(hip):
+    """A coherent pinned host int32 (hipHostMalloc with hipHostMallocCoherent), as (c_int32 view, device
+    address, host pointer), or None."""
+    if hip is None:
+        return None
+    ptr, dptr = ctypes.c_void_p(), ctypes.c_void_p()
+    if hip.hipHostMalloc(ctypes.byref(ptr), ctypes.c_size_t(64), ctypes.c_uint(0x40000000)) != 0:
+        return None
+    if hip.hipHostGetDevicePointer(ctypes.byref(dptr), ptr, ctypes.c_uint(0)) != 0:
+        hip.hipHostFree(ptr)
+        return None
+    word = ctypes.c_int32.from_address(ptr.value)
+    word.value = 0
+    return word, dptr.value, ptr
 
 
 def hip_runtime():

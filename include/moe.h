@@ -153,6 +153,17 @@ typedef struct moe_problem {
  * workgroup per block, and do not read the word. */
 #define MOE_FLAG_CU_BUDGET 0x20000
 #define MOE_WS_CU_BUDGET_OFFSET 4
+/* With MOE_FLAG_CU_BUDGET (alone: MOE_ERR_INVALID_ARG): the budget word is not the one in the
+ * workspace but the one whose address the 8 bytes at byte offset MOE_WS_CU_BUDGET_PTR_OFFSET of the
+ * workspace hold (8-byte aligned; a null address: no limit). It may live in any memory the GPU
+ * reads, e.g. pinned host memory allocated coherent (hipHostMalloc with hipHostMallocCoherent),
+ * which the host can store to while the call runs: the persistent GEMMs read the word with
+ * system-scope loads between tiles, so the store takes effect at each workgroup's next tile
+ * boundary with no GPU work of its own (a copy or write-value on another stream would itself wait
+ * for a free CU). The caller writes the address into the workspace before the call and keeps the
+ * word alive until the call's work is done; the library only reads both. */
+#define MOE_FLAG_CU_BUDGET_INDIRECT 0x200000
+#define MOE_WS_CU_BUDGET_PTR_OFFSET 8
 /* moe_route_gemm_backward: d_logits has dense terms (e.g. from an auxiliary loss on the router),
  * so both products run on the dense kernel instead of skipping zero entries. The results are the
  * same bits either way; only the speed differs (DSV3 shape: 0.48 ms skipping zeros at K = 8 of 256

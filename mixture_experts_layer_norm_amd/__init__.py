@@ -34,6 +34,8 @@ MOE_FLAG_CU_BUDGET = 0x20000
 MOE_FLAG_ROUTER_BWD_DENSE = 0x80000
 MOE_FLAG_DISPATCH_COPY = 0x100000
 MOE_WS_CU_BUDGET_OFFSET = 4
+MOE_FLAG_CU_BUDGET_INDIRECT = 0x200000
+MOE_WS_CU_BUDGET_PTR_OFFSET = 8
 MOE_MAX_LANES = 4
 STATUS = {0: 'MOE_OK', -1: 'MOE_ERR_INVALID_ARG', -2: 'MOE_ERR_UNSUPPORTED', -3: 'MOE_ERR_WORKSPACE',
           -4: 'MOE_ERR_MISALIGNED', -5: 'MOE_ERR_HIP'}

@@ -14,7 +14,8 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 static constexpr uint32_t kKnownFlags = MOE_FLAG_FUSED_GATHER | MOE_FLAG_PERSISTENT | MOE_FLAG_BWD_DGRAD_ONE_PASS |
                                         MOE_FLAG_BWD_WGRAD_LO_MXFP8 | MOE_FLAG_PERSISTENT_GEMM | MOE_FLAG_CU_BUDGET |
-                                        MOE_FLAG_ROUTER_BWD_DENSE | MOE_FLAG_DISPATCH_COPY;
+                                        MOE_FLAG_ROUTER_BWD_DENSE | MOE_FLAG_DISPATCH_COPY |
+                                        MOE_FLAG_CU_BUDGET_INDIRECT;
 
 // Extra checks of the entry points that route tokens (top-k over the E experts).
 int validate_routing(const moe_problem* p) {
@@ -32,6 +33,7 @@ int validate_problem(const moe_problem* p) {
   if (p->chunk_rows < 0 || p->ring_stages < 0 || p->ring_stages == 1 || p->ring_stages == 2) return MOE_ERR_INVALID_ARG;
   if ((uint32_t)p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
   if ((p->flags & MOE_FLAG_CU_BUDGET) && !(p->flags & MOE_FLAG_PERSISTENT_GEMM)) return MOE_ERR_INVALID_ARG;
+  if ((p->flags & MOE_FLAG_CU_BUDGET_INDIRECT) && !(p->flags & MOE_FLAG_CU_BUDGET)) return MOE_ERR_INVALID_ARG;
   if ((p->flags & MOE_FLAG_FUSED_GATHER) && (p->flags & MOE_FLAG_DISPATCH_COPY)) return MOE_ERR_INVALID_ARG;
   if (p->E > 1024) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
@@ -326,7 +328,7 @@ static int forward_impl(const moe_problem* p, const void* x, const float* logits
   if (p->dtype != MOE_F32) {
     pcs.tickets = (int32_t*)(wsb + L.err + kTicketsOffset);
     pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
-    pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)(wsb + L.err + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+    set_budget(pcs, p->flags, wsb + L.err);
     pc = &pcs;
   }
 

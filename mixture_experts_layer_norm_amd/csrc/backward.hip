@@ -355,7 +355,7 @@ static Persist bwd_persist(const moe_problem* p, char* wsb, const BwdLayout& L) 
   Persist pc;
   pc.tickets = (int32_t*)(wsb + L.err + kTicketsOffset);
   pc.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
-  pc.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)(wsb + L.err + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+  set_budget(pc, p->flags, wsb + L.err);
   return pc;
 }
 
@@ -501,7 +501,7 @@ static int experts_forward_impl(const moe_problem* p, int64_t slots, const void*
   if (p->dtype != MOE_F32 && ws) {
     pcs.tickets = (int32_t*)((char*)ws + kTicketsOffset);
     pcs.force = (p->flags & MOE_FLAG_PERSISTENT_GEMM) != 0;
-    pcs.budget = (p->flags & MOE_FLAG_CU_BUDGET) ? (const int32_t*)((char*)ws + MOE_WS_CU_BUDGET_OFFSET) : nullptr;
+    set_budget(pcs, p->flags, (char*)ws);
     pc = &pcs;
   }
   auto gemm = [f32, pc](const GemmArgs& a, const Grouped& g, Epi e, hipStream_t s) {

@@ -188,7 +188,17 @@ struct Persist {
   int32_t* tickets = nullptr;
   const int32_t* budget = nullptr;
   bool force = false;
+  bool budget_indirect = false;   // budget points at the address of the word (MOE_FLAG_CU_BUDGET_INDIRECT)
 };
+// The persistent GEMMs' budget control of a call: the workspace's budget word, or with
+// MOE_FLAG_CU_BUDGET_INDIRECT its address slot; none without MOE_FLAG_CU_BUDGET. wsblock: the
+// workspace's first (error-word) block.
+inline void set_budget(Persist& pc, int32_t flags, char* wsblock) {
+  pc.budget = nullptr;
+  pc.budget_indirect = (flags & MOE_FLAG_CU_BUDGET_INDIRECT) != 0;
+  if (flags & MOE_FLAG_CU_BUDGET)
+    pc.budget = (const int32_t*)(wsblock + (pc.budget_indirect ? MOE_WS_CU_BUDGET_PTR_OFFSET : MOE_WS_CU_BUDGET_OFFSET));
+}
 constexpr int kPersistMinTilesPerWg = 12;
 // Grid of the persistent form for a launch of at most nb tiles: nw workgroups, or nw = 0 for the
 // per-tile form (pc null, or too few tiles per workgroup and not forced).

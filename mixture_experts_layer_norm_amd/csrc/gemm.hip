@@ -76,11 +76,12 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_kernel(GemmArgs a,
 // round-robin over the 8 XCDs); for K-grouped tiles one counter over the dealing order (longest
 // groups first). Each tile is computed by exactly one workgroup with the same summation order as
 // the per-tile launch, so the results are bitwise those of gemm_bf16_kernel whatever the grid and
-// the timing. budget: the workgroup budget word (nullable), see persistent_tiles.
+// the timing. budget, budget_ind: the workgroup budget word (nullable), see persistent_tiles.
 template <int EPI, bool KG, int WN, int WAVES_N, int BKE, bool BT = false>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(GemmArgs a, Grouped g, int ntn,
                                                                                   int mtn, int32_t* tickets,
-                                                                                  const int32_t* budget) {
+                                                                                  const int32_t* budget,
+                                                                                  int budget_ind) {
   static_assert(!(KG && EPI != EPI_STORE), "K-grouped tiles store fp32 weight gradients");
   constexpr int BK = SliceCfg<BKE>::BK;
   constexpr int kExtra = EPI == EPI_DGRAD ? 2 * BM * WAVES_N : 0;   // EPI_DGRAD's row partials
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
   // grouped / dense: the XCD ranges of gemm_bf16_kernel, one counter each
   const int valid = KG ? g.groups * mtn * ntn : (g.row_off ? g.tile_off[g.groups] : mtn) * ntn;
   persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
-                   reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra), [&](int cur, auto& ti) {
+                   budget_ind, reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra), [&](int cur, auto& ti) {
     // A per-tile copy of the arguments the tile reads, opaque like the thread index, so that
     // nothing the tile derives from them is hoisted out of the loop and held across the K loop.
     GemmArgs la = a;
@@ -182,15 +183,15 @@ int launch_gemm_bf16(const GemmArgs& a, const Grouped& g, Epi epi, hipStream_t s
     const dim3 pg((unsigned)nw), pb(512);
     if (a.b_kmajor) {
       if (epi == EPI_STORE)
-        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget);
+        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect);
       else
-        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget);
+        hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64, true>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     } else {
       switch (epi) {
-        case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-        case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-        case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
-        case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SWIGLU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect); break;
+        case EPI_STORE: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect); break;
+        case EPI_SAVE_AU: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_SAVE_AU, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect); break;
+        case EPI_DGRAD: hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_DGRAD, false, kWN, 4, 64>), pg, pb, 0, s, a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect); break;
       }
     }
     MOE_LAUNCH_CHECK();
@@ -229,7 +230,7 @@ int launch_gemm_bf16_kgroup(const GemmArgs& a, int groups, hipStream_t s, const 
   if (nw > 0) {
     if ((st = launch_zero_tickets(pc->tickets, s))) return st;
     hipLaunchKernelGGL((gemm_bf16_persistent_kernel<EPI_STORE, true, kWN, 4, 64>), dim3((unsigned)nw), dim3(512), 0, s,
-                       a, g, ntn, mtn, pc->tickets, pc->budget);
+                       a, g, ntn, mtn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }

@@ -361,19 +361,20 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a, const uint8
 
 // Persistent form (persistent_tiles): the tiles and their dealing order of gemm_mx_kernel, one
 // workgroup per CU; each tile is the same workgroup sum, so the results are bitwise those of the
-// per-tile launch. budget: the workgroup budget word (nullable).
+// per-tile launch. budget, budget_ind: the workgroup budget word (nullable), see persistent_tiles.
 template <int EPI, bool KG>
 __global__ __launch_bounds__(512, 1) void gemm_mx_persistent_kernel(GemmArgs a, const uint8_t* __restrict__ a_sc,
                                                                     const uint8_t* __restrict__ b_sc,
                                                                     const uint8_t* __restrict__ b2_sc,
                                                                     int64_t sc_group_stride,
                                                                     uint8_t* __restrict__ h_sc, Grouped g, int ntn,
-                                                                    int32_t* tickets, const int32_t* budget) {
+                                                                    int32_t* tickets, const int32_t* budget,
+                                                                    int budget_ind) {
   __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kMxSmemElems + 4];
   const int valid = KG ? g.groups * ((a.M + BM - 1) / BM) * ntn
                        : (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
   persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
-                   reinterpret_cast<int*>(smem_u16 + kMxSmemElems), [&](int cur, auto& ti) {
+                   budget_ind, reinterpret_cast<int*>(smem_u16 + kMxSmemElems), [&](int cur, auto& ti) {
     // per-tile opaque copies of the arguments (nothing derived from them is held across tiles)
     GemmArgs la = a;
     const uint8_t *la_sc = a_sc, *lb_sc = b_sc, *lb2_sc = b2_sc;
@@ -414,13 +415,13 @@ int launch_gemm_mx(const GemmArgs& a, const uint8_t* a_sc, const uint8_t* b_sc, 
     const dim3 pg((unsigned)nw), pb(512);
     if (epi == EPI_SWIGLU)
       hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_SWIGLU, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
-                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     else if (epi == EPI_SAVE_AU)
       hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_SAVE_AU, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
-                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     else
       hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_STORE, false>), pg, pb, 0, s, a, a_sc, b_sc, b2_sc,
-                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget);
+                         sc_group_stride, h_sc, g, ntn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }
@@ -454,7 +455,7 @@ int launch_gemm_mx_kgroup(const GemmArgs& a, const uint8_t* a_sc, const uint8_t*
   if (nw > 0) {
     if ((st = launch_zero_tickets(pc->tickets, s))) return st;
     hipLaunchKernelGGL((gemm_mx_persistent_kernel<EPI_STORE, true>), dim3((unsigned)nw), dim3(512), 0, s, a, a_sc,
-                       b_sc, b_sc, (int64_t)0, (uint8_t*)nullptr, g, ntn, pc->tickets, pc->budget);
+                       b_sc, b_sc, (int64_t)0, (uint8_t*)nullptr, g, ntn, pc->tickets, pc->budget, (int)pc->budget_indirect);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
   }

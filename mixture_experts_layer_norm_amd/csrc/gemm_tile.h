@@ -725,10 +725,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 // "Mixture-of-Kittens: MoE Megakernel for NVL72s", section "The production details": the
 // persistent kernel hands processors back to another stream's work). While it holds v > 0,
 // workgroups with index >= v take no further tile and exit once their current tile is done;
-// the others go on until every tile is taken. The word is read, never written.
+// the others go on until every tile is taken. The word is read, never written. budget_ind: budget
+// points at the word's address (8 bytes; null: no limit) instead of the word.
 template <class Body>
 __device__ __forceinline__ void persistent_tiles(int valid, int per_range, int nrange, int home, int32_t* tickets,
-                                                 const int32_t* budget, int* ctl, Body&& body) {
+                                                 const int32_t* budget, int budget_ind, int* ctl, Body&& body) {
   int& s_next = ctl[0];
   int& s_probe = ctl[1];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -739,7 +740,8 @@ __device__ __forceinline__ void persistent_tiles(int valid, int per_range, int n
   };
   auto take = [&]() -> int {   // thread 0 only
     if (budget) {
-      const int v = __hip_atomic_load(budget, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const int32_t* word = budget_ind ? *reinterpret_cast<const int32_t* const volatile*>(budget) : budget;
+      const int v = word ? __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0;
       if (v > 0 && (int)blockIdx.x >= v) return -1;
     }
     int probe = s_probe;

@@ -125,3 +125,35 @@ class ForwardRun:
         self.m.forward_lanes(self.p, self.L.x, self.L.logits, self.weights, self.out, self.routing, self.ws,
                              streams, events, self.y_routes, self.shared_out)
         return self
+
+
+class PinnedWord:
+    """A coherent pinned host int32 (hipHostMalloc with hipHostMallocCoherent, through the HIP runtime
+    torch has loaded): `value` reads and stores it from the host, `device_address` is what a kernel
+    reads. Free with close() once no queued work reads it."""
+
+    def __init__(self):
+        import ctypes
+        with open('/proc/self/maps') as f:
+            paths = sorted({line.split()[-1] for line in f if 'libamdhip64' in line})
+        assert paths, 'HIP runtime not loaded'
+        self._hip = ctypes.CDLL(paths[0])
+        self._ptr, dptr = ctypes.c_void_p(), ctypes.c_void_p()
+        assert self._hip.hipHostMalloc(ctypes.byref(self._ptr), ctypes.c_size_t(64), ctypes.c_uint(0x40000000)) == 0
+        assert self._hip.hipHostGetDevicePointer(ctypes.byref(dptr), self._ptr, ctypes.c_uint(0)) == 0
+        self.device_address = dptr.value
+        self._word = ctypes.c_int32.from_address(self._ptr.value)
+        self._word.value = 0
+
+    @property
+    def value(self):
+        return self._word.value
+
+    @value.setter
+    def value(self, v):
+        self._word.value = v
+
+    def close(self):
+        if self._ptr is not None:
+            self._hip.hipHostFree(self._ptr)
+            self._ptr = None

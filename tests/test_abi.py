@@ -183,6 +183,15 @@ def test_persistent_gemm_flags_without_gpu():
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1
     p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET)
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value >= 256
+    # the indirect budget word needs the budget; its address slot is 8-byte aligned, clear of the
+    # error word and the budget word, and before the ticket counters (offset 64)
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET_INDIRECT)
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == -1
+    p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0,
+                  m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET | m.MOE_FLAG_CU_BUDGET_INDIRECT)
+    assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert m.MOE_WS_CU_BUDGET_PTR_OFFSET % 8 == 0 and m.MOE_WS_CU_BUDGET_PTR_OFFSET >= m.MOE_WS_CU_BUDGET_OFFSET + 4
+    assert m.MOE_WS_CU_BUDGET_PTR_OFFSET + 8 <= 64
     p = m.problem(64, 128, 128, 8, 2, 0, 'bf16', 0, 0, m.MOE_FLAG_ROUTER_BWD_DENSE)   # a known bit
     assert lib.moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     # the forward gathers x through the schedule by default; the slot copy is asked for, and needs

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import ForwardRun
+from gpu_util import ForwardRun, PinnedWord
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,40 @@ def test_cu_budget_changed_from_another_stream(m):
         assert int(word.item()) == v
         set_budget(b, m, 0)
         torch.cuda.synchronize()
+
+
+def test_cu_budget_host_word(m):
+    """MOE_FLAG_CU_BUDGET_INDIRECT: the budget word in coherent pinned host memory, its address in the
+    workspace. Set before the call (0: no limit, 2, 1) and stored by the host while the call runs
+    (after the launch, before the synchronisation): the outputs equal the per-tile forward's; a
+    null address means no limit. The word is only read."""
+    print('[budget] host word', flush=True)
+    L = synth.to_device(synth.host_layer(synth.MID))
+    a = ForwardRun(m, L)()
+    b = ForwardRun(m, L, flags=m.MOE_FLAG_PERSISTENT_GEMM | m.MOE_FLAG_CU_BUDGET | m.MOE_FLAG_CU_BUDGET_INDIRECT)
+    slot = b.ws[m.MOE_WS_CU_BUDGET_PTR_OFFSET:m.MOE_WS_CU_BUDGET_PTR_OFFSET + 8].view(torch.int64)
+    hw = PinnedWord()
+    try:
+        slot.fill_(0)                       # null address: no limit
+        b()
+        torch.cuda.synchronize()
+        same(a, b)
+        slot.fill_(hw.device_address)
+        for v in (0, 2, 1):
+            hw.value = v
+            b()
+            torch.cuda.synchronize()
+            same(a, b)
+            assert hw.value == v
+        for v in (1, 5, 0):
+            hw.value = 0
+            b()
+            hw.value = v                    # stored while the forward may still run
+            torch.cuda.synchronize()
+            same(a, b)
+        torch.cuda.synchronize()
+    finally:
+        hw.close()
 
 
 def test_persistent_gemm_full_size_dsv3(m):
