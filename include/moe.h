@@ -96,8 +96,8 @@ typedef struct moe_problem {
  * 0.11 ms). This is the default; MOE_FLAG_FUSED_GATHER names it and is accepted. The BF16 layer
  * backward (moe_backward, moe_backward_kept) reads x and dout the same way in its GEMMs and
  * transposes (DSV3 shape: 45.3 against 45.7 ms, and no 2 T K D-element slot buffers in its
- * workspace). MOE_FLAG_DISPATCH_COPY instead writes the expert-contiguous slot copies first (as the
- * MXFP8 and fp32 backwards always do) and runs on them; the outputs are the same bits. Both flags
+ * workspace), the MXFP8 layer backward in its quantisers. MOE_FLAG_DISPATCH_COPY instead writes the expert-contiguous slot copies first (as the
+ * fp32 backward always does) and runs on them; the outputs are the same bits. Both flags
  * together: MOE_ERR_INVALID_ARG. */
 #define MOE_FLAG_FUSED_GATHER 0x1
 #define MOE_FLAG_DISPATCH_COPY 0x100000

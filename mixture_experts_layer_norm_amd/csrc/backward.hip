@@ -78,9 +78,9 @@ static BwdLayout bwd_layout(const moe_problem& p, bool kept = false) {
   L.offs_s = take(8); L.tile_off_s = take(8); L.poff_s = take(8);
   const int64_t eb = p.dtype == MOE_F32 ? 4 : 2;   // bytes per activation element
   L.g_slot = take(n * 4); L.dg_slot = take(n * 4);
-  // slot copies of x and dout: the BF16 layer backward reads both through the schedule instead
-  // (unless MOE_FLAG_DISPATCH_COPY); fp32 and MXFP8 copy them
-  const bool copy = p.dtype != MOE_BF16 || (p.flags & MOE_FLAG_DISPATCH_COPY);
+  // slot copies of x and dout: the BF16 and MXFP8 layer backwards read both through the schedule
+  // instead (unless MOE_FLAG_DISPATCH_COPY); fp32 copies them
+  const bool copy = p.dtype == MOE_F32 || (p.flags & MOE_FLAG_DISPATCH_COPY);
   L.x_slot = take(copy ? n * D * eb : 0); L.dy_slot = take(copy ? n * D * eb : 0); L.dx_slot = take(n * D * eb);
   L.dx_sh = take(T * D * eb);
   // replayed a, u; left out when the caller keeps them (offsets then unused)
@@ -264,7 +264,8 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
                             const float* g_rows, const int32_t* offs, const int32_t* tile_off, const int32_t* poff,
                             const moe_weights* w, void* dx_rows, float* dg_rows, float* dw_gate, float* dw_up,
                             float* dw_down, char* ws, const BwdLayout& L, hipStream_t s, const Persist* pc,
-                            const float* kept_a = nullptr, const float* kept_u = nullptr) {
+                            const float* kept_a = nullptr, const float* kept_u = nullptr,
+                            const int32_t* row_map = nullptr, int row_div = 1) {
   int st;
   auto B = [&](size_t off) { return (uint8_t*)(ws + off); };
   auto F = [&](size_t off) { return (float*)(ws + off); };
@@ -281,10 +282,10 @@ static int core_backward_mx(int G, int64_t n_cap, int D, int I, const void* x_ro
   // x and dy: along D (dgrad operands) and, in the same pass, x and g dy along the slots
   // (weight-gradient operands)
   if ((st = launch_mx_quant_t((const uint16_t*)x_rows, nullptr, D, D, offs, poff, G, S, B(L.mq_xT), B(L.ms_xT), S,
-                              B(L.mq_x), B(L.ms_x), s)))
+                              B(L.mq_x), B(L.ms_x), s, row_map, row_div)))
     return st;
   if ((st = launch_mx_quant_t((const uint16_t*)dy_rows, g_rows, D, D, offs, poff, G, S, B(L.mq_gdyT), B(L.ms_gdyT), S,
-                              B(L.mq_dy), B(L.ms_dy), s)))
+                              B(L.mq_dy), B(L.ms_dy), s, row_map, row_div)))
     return st;
 
   Grouped grp;
@@ -732,10 +733,10 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
   if (kept && (!al16(act_a) || !al16(act_u))) return MOE_ERR_MISALIGNED;
   char* wsb = (char*)ws;
   const int64_t n = L.n;
-  // reverse-combine (pull dout into slots) and replayed dispatch of x: copies for fp32, MXFP8 (quantised
-  // from them) and MOE_FLAG_DISPATCH_COPY; the BF16 GEMMs and transposes otherwise read slot row j
-  // from dout / x row perm[j] / K directly
-  const bool copy = p->dtype != MOE_BF16 || (p->flags & MOE_FLAG_DISPATCH_COPY);
+  // reverse-combine (pull dout into slots) and replayed dispatch of x: copies for fp32 and under
+  // MOE_FLAG_DISPATCH_COPY; otherwise the BF16 GEMMs and transposes, and the MXFP8 quantisers, read
+  // slot row j from dout / x row perm[j] / K directly
+  const bool copy = p->dtype == MOE_F32 || (p->flags & MOE_FLAG_DISPATCH_COPY);
   const int adt = f32 ? MOE_F32 : MOE_BF16;   // activations stay bf16 under MXFP8 until quantised
   if (copy) {
     if ((st = launch_dispatch(dout, adt, r->perm, p->K, p->D, 0, n, wsb + L.dy_slot, nullptr, stream))) return st;
@@ -755,10 +756,11 @@ static int backward_impl(const moe_problem* p, const void* dout, const void* x, 
       return st;
   } else if (mx) {
     const Persist pc = bwd_persist(p, wsb, L);
-    if ((st = core_backward_mx(p->E, n, p->D, p->I, wsb + L.x_slot, wsb + L.dy_slot, (float*)(wsb + L.g_slot), offs,
+    if ((st = core_backward_mx(p->E, n, p->D, p->I, copy ? (const void*)(wsb + L.x_slot) : x,
+                               copy ? (const void*)(wsb + L.dy_slot) : dout, (float*)(wsb + L.g_slot), offs,
                                (int32_t*)(wsb + L.tile_off), (int32_t*)(wsb + L.poff), w, wsb + L.dx_slot,
                                (float*)(wsb + L.dg_slot), dw->dw_gate, dw->dw_up, dw->dw_down, wsb, L, stream, &pc,
-                               act_a, act_u)))
+                               act_a, act_u, copy ? nullptr : r->perm, p->K)))
       return st;
   } else {
     CoreBufs cb = routed_bufs(wsb, L);

@@ -119,7 +119,7 @@ int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, in
                         int64_t ldo, int64_t col0, int64_t out_bstride, int64_t osc_bstride, hipStream_t s);
 int launch_mx_quant_t(const uint16_t* src, const float* rscale, int64_t lds, int W, const int32_t* offs,
                       const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc, int64_t ldo, uint8_t* rq,
-                      uint8_t* rsc, hipStream_t s);
+                      uint8_t* rsc, hipStream_t s, const int32_t* rmap = nullptr, int rdiv = 1);
 int launch_mx_swiglu_bwd_t(const float* a, const float* u, const float* dhp, const float* g, int I, const int32_t* offs,
                            const int32_t* poff, int G, int64_t max_padded, uint8_t* dq, uint8_t* dsc, uint8_t* hq,
                            uint8_t* hsc, uint8_t* daq, uint8_t* dasc, int64_t ldo, float* part, hipStream_t s);

@@ -90,6 +90,8 @@ __global__ __launch_bounds__(256) void mx_requant_t_kernel(const uint8_t* __rest
 //     neighbouring threads write one 128-byte line of an output row;
 //   * along the features (rq != nullptr): each valid row's two 32-feature blocks -> rq + row * W +
 //     c0 (codes) and rsc + row * (W / 32) + c0 / 32 (scales), from the unscaled source.
+// With rmap, slot row r is read from source row rmap[r] / rdiv (the layer backward reads x and
+// dout through the schedule instead of slot copies); outputs stay indexed by slot.
 // The tile stays bf16 in LDS (18.5 KB, so 8 workgroups share a CU and their loads overlap): row r
 // at halfword r * 72 + (r / 32) * 16, which puts the four 32-slot blocks a column read touches on
 // different banks.
@@ -97,7 +99,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
                                                          int64_t lds, int W, const int32_t* __restrict__ offs,
                                                          const int32_t* __restrict__ poff, int G, uint8_t* __restrict__ q,
                                                          uint8_t* __restrict__ sc, int64_t ldo, uint8_t* __restrict__ rq,
-                                                         uint8_t* __restrict__ rsc, int nsb, int ntiles) {
+                                                         uint8_t* __restrict__ rsc, int nsb, int ntiles,
+                                                         const int32_t* __restrict__ rmap, int rdiv) {
   constexpr int P = 72;       // halfwords per tile row (64 + 8)
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * P + 64];
   __shared__ float rs[128];   // row scales of the block (1 without rscale or past the group's end)
@@ -121,7 +124,10 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     const int qd = tid + 256 * k, i = qd >> 3, cc = (qd & 7) * 8;
     const int64_t r = rbase + i;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (r < rend && c0 + cc < W) w = *reinterpret_cast<const u32x4*>(src + r * lds + c0 + cc);
+    if (r < rend && c0 + cc < W) {
+      const int64_t sr = rmap ? (int64_t)(rmap[r] / rdiv) : r;   // source row of slot r
+      w = *reinterpret_cast<const u32x4*>(src + sr * lds + c0 + cc);
+    }
     *reinterpret_cast<u32x4*>(&tile[at(i, cc)]) = w;
   }
   __syncthreads();
@@ -300,12 +306,12 @@ int launch_mx_requant_t(const uint8_t* src, const uint8_t* ssc, int G, int R, in
 
 int launch_mx_quant_t(const uint16_t* src, const float* rscale, int64_t lds, int W, const int32_t* offs,
                       const int32_t* poff, int G, int64_t max_padded, uint8_t* q, uint8_t* sc, int64_t ldo, uint8_t* rq,
-                      uint8_t* rsc, hipStream_t s) {
+                      uint8_t* rsc, hipStream_t s, const int32_t* rmap, int rdiv) {
   if (max_padded <= 0 || W <= 0) return MOE_OK;
   if (max_padded % 128 || ldo % 128 || W % 32 || lds % 8) return MOE_ERR_UNSUPPORTED;
   const int nsb = (int)(max_padded / 128), ntiles = nsb * ((W + 63) / 64);
   hipLaunchKernelGGL(mx_quant_t_kernel, dim3(xcd_grid(ntiles)), dim3(256), 0, s, src, rscale, lds, W, offs, poff, G, q,
-                     sc, ldo, rq, rsc, nsb, ntiles);
+                     sc, ldo, rq, rsc, nsb, ntiles, rmap, rdiv);
   MOE_LAUNCH_CHECK();
   return MOE_OK;
 }

@@ -375,3 +375,16 @@ def test_mx_layer_keep_activations_bitwise(m):
     res = [run_mx_layer(m, H, q, keep) for keep in (False, True)]
     for k in res[0]:
         assert torch.equal(res[0][k], res[1][k]), k
+
+
+def test_mx_layer_gather_equals_dispatch_copy_bitwise(m):
+    """The MXFP8 layer backward quantises x and g dout straight from the token rows through the
+    schedule; MOE_FLAG_DISPATCH_COPY dispatches slot copies first. Same bits in every output, with
+    a, u replayed or kept."""
+    from test_gpu_mxfp8 import MX_SMALL, mx_layer
+    H, q = mx_layer(MX_SMALL)
+    for keep in (False, True):
+        a = run_mx_layer(m, H, q, keep)
+        b = run_mx_layer(m, H, q, keep, m.MOE_FLAG_DISPATCH_COPY)
+        for k in a:
+            assert torch.equal(a[k], b[k]), (keep, k)
