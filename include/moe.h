@@ -96,9 +96,9 @@ typedef struct moe_problem {
  * 0.11 ms). This is the default; MOE_FLAG_FUSED_GATHER names it and is accepted. The BF16 layer
  * backward (moe_backward, moe_backward_kept) reads x and dout the same way in its GEMMs and
  * transposes (DSV3 shape: 45.3 against 45.7 ms, and no 2 T K D-element slot buffers in its
- * workspace), the MXFP8 layer backward in its quantisers. MOE_FLAG_DISPATCH_COPY instead writes the expert-contiguous slot copies first (as the
- * fp32 backward always does) and runs on them; the outputs are the same bits. Both flags
- * together: MOE_ERR_INVALID_ARG. */
+ * workspace), the MXFP8 layer backward in its quantisers. MOE_FLAG_DISPATCH_COPY instead writes
+ * the expert-contiguous slot copies first (as the fp32 backward always does) and runs on them; the
+ * outputs are the same bits. Both flags together: MOE_ERR_INVALID_ARG. */
 #define MOE_FLAG_FUSED_GATHER 0x1
 #define MOE_FLAG_DISPATCH_COPY 0x100000
 /* Bits 0x2, 0x8, 0x10, 0x20 and 0xff00 are reserved (they selected tuning variants that measured
