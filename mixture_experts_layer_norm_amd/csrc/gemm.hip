@@ -89,8 +89,11 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
   // K-grouped: every (group, m-tile, n-tile) in launch order (longest groups first), one counter;
   // grouped / dense: the XCD ranges of gemm_bf16_kernel, one counter each
   const int valid = KG ? g.groups * mtn * ntn : (g.row_off ? g.tile_off[g.groups] : mtn) * ntn;
-  persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
-                   budget_ind, reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra), [&](int cur, auto& ti) {
+  // the next ticket fetched during the epilogue: the forward's GEMMs (see persistent_tiles)
+  constexpr bool kEarly = !KG && !BT && (EPI == EPI_SWIGLU || EPI == EPI_STORE);
+  persistent_tiles<kEarly>(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets,
+                           budget, budget_ind, reinterpret_cast<int*>(smem + kGemmSmemElems + kExtra),
+                           [&](int cur, auto& ti, auto& hook) {
     // A per-tile copy of the arguments the tile reads, opaque like the thread index, so that
     // nothing the tile derives from them is hoisted out of the loop and held across the K loop.
     GemmArgs la = a;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_persistent_kernel(
     } else {
       ok = decode_grouped_tile(g, cur, ntn, mtn, tc);
     }
-    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(la, tc, k0, nk, ntn, smem, ti());
+    if (ok) gemm_tile<EPI, KG, WN, WAVES_N, BKE, BT>(la, tc, k0, nk, ntn, smem, ti(), hook);
   });
 }
 

@@ -125,12 +125,13 @@ __device__ __forceinline__ bool mx_decode(const GemmArgs& a, const Grouped& g, i
 // LDS of an MX tile: the two operand stages, then 2 x 512 scale words
 constexpr int kMxSmemElems = kGemmSmemElems + 2048;
 
-// One tile; tid: the thread index (the persistent kernel passes one rebuilt per tile).
-template <int EPI, bool KG>
+// One tile; tid: the thread index (the persistent kernel passes one rebuilt per tile); hook() runs
+// between the K loop and the epilogue (see gemm_tile).
+template <int EPI, bool KG, class Hook = NoHook>
 __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __restrict__ a_sc,
                                         const uint8_t* __restrict__ b_sc, const uint8_t* __restrict__ b2_sc,
                                         int64_t sc_group_stride, uint8_t* __restrict__ h_sc, const MxTile& t,
-                                        uint8_t* sm, int tid) {
+                                        uint8_t* sm, int tid, Hook hook = Hook{}) {
   using C = SliceCfg<64>;
   constexpr int WAVES_N = 4, WM = 128, WN = 64, BN = WAVES_N * WN;
   constexpr int MI = WM / 32, NJ = WN / 32;
@@ -219,6 +220,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& a, const uint8_t* __rest
     case 3: mx_k_loop<EPI, 3, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
     default: mx_k_loop<EPI, 4, NL>(src, sm, scl, nk, wave, a_rd, b_rd, sw, q, sc_src, a_srow, b_srow, acc); break;
   }
+  hook();
 
   const int ccol = lane & 31;
   const int tid512 = tid;
@@ -373,8 +375,9 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_persistent_kernel(GemmArgs a, 
   __shared__ __attribute__((aligned(16))) uint16_t smem_u16[kMxSmemElems + 4];
   const int valid = KG ? g.groups * ((a.M + BM - 1) / BM) * ntn
                        : (g.row_off ? g.tile_off[g.groups] : (g.M + BM - 1) / BM) * ntn;
-  persistent_tiles(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets, budget,
-                   budget_ind, reinterpret_cast<int*>(smem_u16 + kMxSmemElems), [&](int cur, auto& ti) {
+  persistent_tiles<!KG>(valid, KG ? valid : (valid + 7) >> 3, KG ? 1 : 8, KG ? 0 : (int)(blockIdx.x & 7), tickets,
+                        budget, budget_ind, reinterpret_cast<int*>(smem_u16 + kMxSmemElems),
+                        [&](int cur, auto& ti, auto& hook) {
     // per-tile opaque copies of the arguments (nothing derived from them is held across tiles)
     GemmArgs la = a;
     const uint8_t *la_sc = a_sc, *lb_sc = b_sc, *lb2_sc = b2_sc;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_persistent_kernel(GemmArgs a, 
     asm volatile("" : "+s"(la.lda), "+s"(la.ldb), "+s"(la.ldc), "+s"(la.b_group_stride), "+s"(la.N), "+s"(la.K));
     MxTile t;
     if (mx_decode<KG>(la, g, ntn, cur, t))
-      mx_tile<EPI, KG>(la, la_sc, lb_sc, lb2_sc, lsgs, lh_sc, t, reinterpret_cast<uint8_t*>(smem_u16), ti());
+      mx_tile<EPI, KG>(la, la_sc, lb_sc, lb2_sc, lsgs, lh_sc, t, reinterpret_cast<uint8_t*>(smem_u16), ti(), hook);
   });
 }
 
