@@ -722,8 +722,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const TileCoord& tc
 // consecutive tiles (nrange ranges, counters tickets[0 .. nrange-1]): a workgroup starts with
 // range `home` and moves on to the following ones once it finds a range used up, so workgroups
 // that finish early take over the rest. body(tile, ti, hook) computes tile `tile`, calling ti() for
-// the thread index and hook() between its K loop and its epilogue. Workgroups never wait for one another; the only shared state is the counters.
-// The loop keeps no per-lane value live across a tile (the tile itself uses the whole register
+// the thread index and hook() between its K loop and its epilogue (with EARLY the hook fetches the
+// next ticket, below). Workgroups never wait for one another; the only shared state is the
+// counters. The loop keeps no per-lane value live across a tile (the tile itself uses the whole register
 // budget): the thread index is rebuilt per tile from the lane count and the wavefront's scalar
 // index, and thread 0's position in the ranges is kept in LDS, in the two ints at ctl (past the
 // tile's own LDS use, in the same array: as separate __shared__ objects the compiler could not
