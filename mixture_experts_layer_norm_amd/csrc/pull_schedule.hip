@@ -16,8 +16,9 @@
 //   1. per block of routes, a histogram over the R L (source rank, local expert) keys;
 //   2. one block: per-key prefix over blocks (each block's first ordinal per key), M, the region
 //      sizes T[l] and their exclusive scan S;
-//   3. per block, the stable rank of each route among equal keys (ballots inside a wavefront,
-//      per-wavefront counts across), hence its ordinal and its position by the formula above.
+//   3. per block, the stable rank of each route among equal keys (a comparison with every lane's
+//      key inside a wavefront, per-wavefront counts across), hence its ordinal and its position
+//      by the formula above.
 #include "common.h"
 
 namespace moe {
@@ -129,28 +130,23 @@ __global__ __launch_bounds__(256) void pull_place_kernel(const int32_t* __restri
   for (int l = tid; l < L; l += 256) s[l] = offsets[l];
   const int64_t base = (int64_t)blockIdx.x * kPullBlock;
   const int64_t end = min(n, base + kPullBlock);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t rb = base; rb < end; rb += 256) {
     for (int i = tid; i < 4 * RL; i += 256) wcnt[i] = 0;
     __syncthreads();
     const int64_t j = rb + tid;
     const bool valid = j < end;
     const int key = valid ? pull_key(routing, j, NK, L, RL, rank, err) : -1;
-    bool pending = key >= 0;
-    int rank_in_wave = 0;
-    while (true) {
-      const uint64_t act = __ballot(pending);
-      if (act == 0ull) break;
-      const int leader = __ffsll((unsigned long long)act) - 1;
-      const int lk = __shfl(key, leader, 64);
-      const bool mine = pending && key == lk;
-      const uint64_t same = __ballot(mine);
-      if (mine) {
-        rank_in_wave = __popcll(same & lt_mask);
-        pending = false;
-      }
-      if (lane == leader) wcnt[w * RL + lk] = __popcll(same);
+    // rank among earlier lanes of this wave with the same key, read lane by lane with readlane
+    // (a fixed 64 steps); the last lane of a key records the wave's count for it
+    int rank_in_wave = 0, later = 0;
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+      const int kq = __builtin_amdgcn_readlane(key, q);
+      const int same = kq == key ? 1 : 0;
+      rank_in_wave += q < lane ? same : 0;
+      later += q > lane ? same : 0;
     }
+    if (key >= 0 && later == 0) wcnt[w * RL + key] = rank_in_wave + 1;
     __syncthreads();
     if (key >= 0) {
       int o = cnt[key] + rank_in_wave;

@@ -202,12 +202,20 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ 
                                                           int32_t* __restrict__ tile_off) {
   __shared__ int sbuf[1024];
   const int e = threadIdx.x;
+  // the per-block counts are read kScanBatch at a time, so that their loads are in flight
+  // together instead of one after another
+  constexpr int kScanBatch = 16;
   int running = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      int v = blk_hist[(size_t)b * E + e];
-      blk_hist[(size_t)b * E + e] = running;
-      running += v;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = b0 + j < nblk ? blk_hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) blk_hist[(size_t)(b0 + j) * E + e] = running;
+        running += v[j];
+      }
     }
   }
   int total;
@@ -219,7 +227,14 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ 
     counts[e] = running;
     offsets[e] = off;
     tile_off[e] = toff;
-    for (int b = 0; b < nblk; ++b) blk_hist[(size_t)b * E + e] += off;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = b0 + j < nblk ? blk_hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        if (b0 + j < nblk) blk_hist[(size_t)(b0 + j) * E + e] = v[j] + off;
+    }
   }
   if (e == 0) {
     offsets[E] = total;
@@ -228,7 +243,8 @@ __global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ 
 }
 
 // pass 3: stable placement. Each block walks its routes in order, 256 at a time; inside a
-// wave the rank among equal experts comes from ballots, across waves from per-wave counts.
+// wave the rank among equal experts comes from comparing all 64 lanes' experts, across waves
+// from per-wave counts.
 __global__ __launch_bounds__(256) void sched_place_kernel(const int32_t* __restrict__ idx, int n, int E,
                                                           const int32_t* __restrict__ blk_start,
                                                           int32_t* __restrict__ perm,
@@ -241,28 +257,24 @@ __global__ __launch_bounds__(256) void sched_place_kernel(const int32_t* __restr
   for (int e = tid; e < E; e += 256) cnt[e] = blk_start[(size_t)blockIdx.x * E + e];
   const int base = blockIdx.x * kRouteRowsPerBlock;
   const int end = min(n, base + kRouteRowsPerBlock);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int rb = base; rb < end; rb += 256) {
     for (int i = tid; i < 4 * E; i += 256) wcnt[i] = 0;
     __syncthreads();
     const int r = rb + tid;
     const bool valid = r < end;
     const int e = valid ? checked_expert(idx[r], E, err) : -1;
-    bool pending = valid;
-    int rank = 0;
-    while (true) {
-      const uint64_t act = __ballot(pending);
-      if (act == 0ull) break;
-      const int leader = __ffsll((unsigned long long)act) - 1;
-      const int le = __shfl(e, leader, 64);
-      const bool mine = pending && e == le;
-      const uint64_t same = __ballot(mine);
-      if (mine) {
-        rank = __popcll(same & lt_mask);
-        pending = false;
-      }
-      if (lane == leader) wcnt[w * E + le] = __popcll(same);
+    // rank = earlier lanes of this wave with the same expert; the last such lane also records
+    // the wave's count for that expert. Every lane reads every other lane's expert (readlane
+    // with a constant lane index), so the cost is fixed whatever the mix of experts.
+    int rank = 0, later = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const int same = ej == e ? 1 : 0;
+      rank += j < lane ? same : 0;
+      later += j > lane ? same : 0;
     }
+    if (valid && later == 0) wcnt[w * E + e] = rank + 1;
     __syncthreads();
     if (valid) {
       int pos = cnt[e] + rank;
